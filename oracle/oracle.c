@@ -1,0 +1,267 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the gated fine-grained sparse attention
+ * layer: indexer scoring -> Top-K selection -> exact softmax attention over the
+ * selected keys/values -> elementwise sigmoid output gate.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library. The GPU path never calls it,
+ * shares no source, header, table or helper with it, and does not fall back to it.
+ *
+ * Each step is the plain definition written out, one query row at a time:
+ *
+ *   scoring  "Hybrid Sparse Attention for Long-Context LLMs", section "Indexer +
+ *            Top-K: How Fine-Grained Sparse Attention Works", step 1 (a light
+ *            scorer over low-dimensional projections of every history position).
+ *            The pages give no formula; the reading taken is
+ *              S[s] = sum_h w_h * max(0, sum_j qI[h][j] * kI[s][j])
+ *            over int8 inputs, accumulated exactly (int64 here), for every
+ *            candidate s in 0..p (causal, own position included).
+ *   Top-K    same section, step 2 and its pseudocode (keep the K best positions
+ *            per query); "Optimizing LLM Long-Context Inference with Indexed
+ *            Top-K Sparse Attention", section "Interface Design" (topk over the
+ *            score row). Order: higher score first, lower position on equal
+ *            scores. Output: the selected positions in ascending order, padded
+ *            with -1 when fewer than K candidates exist.
+ *   attention same page, step 3 (standard softmax attention over the selected
+ *            positions only, scaled by 1/sqrt(d)), in fp64 from the exact values
+ *            of the bf16 inputs; query head h reads KV head h / (Hq/Hkv).
+ *   gate     same page, step 4, and "From Linear Attention to Gated Sparse
+ *            Attention", section 2 pseudocode (the gate multiplies the attention
+ *            output): y = o * sigmoid(G), elementwise per head and feature.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_OVERFLOW 1
+
+/* ---------------------------------------------------------------- scoring */
+
+/* Scores of one query row against history rows 0..n-1.
+ * qI [H_I][d_I], kI [n][d_I], w [H_I]; writes S[0..n-1].
+ * Returns ORC_OVERFLOW if any score leaves the int32 range (S is then clamped). */
+int orc_score_row(int H_I, int d_I, const int8_t *qI, const int8_t *kI, const int8_t *w,
+                  int64_t n, int32_t *S)
+{
+    int rc = ORC_OK;
+    for (int64_t s = 0; s < n; ++s) {
+        int64_t acc = 0;
+        for (int h = 0; h < H_I; ++h) {
+            int64_t dot = 0;
+            for (int j = 0; j < d_I; ++j)
+                dot += (int64_t)qI[h * d_I + j] * (int64_t)kI[s * d_I + j];
+            if (dot < 0) dot = 0;                 /* ReLU */
+            acc += (int64_t)w[h] * dot;
+        }
+        if (acc > INT32_MAX) { acc = INT32_MAX; rc = ORC_OVERFLOW; }
+        if (acc < INT32_MIN) { acc = INT32_MIN; rc = ORC_OVERFLOW; }
+        S[s] = (int32_t)acc;
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------------ Top-K */
+
+typedef struct { int32_t score; int32_t pos; } orc_pair;
+
+/* a before b  <=>  a.score > b.score, or equal scores and a.pos < b.pos */
+static int orc_cmp_rank(const void *pa, const void *pb)
+{
+    const orc_pair *a = (const orc_pair *)pa, *b = (const orc_pair *)pb;
+    if (a->score != b->score) return a->score > b->score ? -1 : 1;
+    return (a->pos > b->pos) - (a->pos < b->pos);
+}
+
+static int orc_cmp_pos(const void *pa, const void *pb)
+{
+    const orc_pair *a = (const orc_pair *)pa, *b = (const orc_pair *)pb;
+    return (a->pos > b->pos) - (a->pos < b->pos);
+}
+
+/* The min(K, n) best of S[0..n-1]; idx[0..K-1] ascending, -1 padded; sel (nullable)
+ * holds the score of each selected position, INT32_MIN in the padding. */
+void orc_topk_row(const int32_t *S, int64_t n, int K, int32_t *idx, int32_t *sel)
+{
+    int64_t m = n < K ? n : K;
+    orc_pair *pr = (orc_pair *)malloc((size_t)(n > 0 ? n : 1) * sizeof(orc_pair));
+    for (int64_t s = 0; s < n; ++s) { pr[s].score = S[s]; pr[s].pos = (int32_t)s; }
+    qsort(pr, (size_t)n, sizeof(orc_pair), orc_cmp_rank);   /* full sort: rank order */
+    qsort(pr, (size_t)m, sizeof(orc_pair), orc_cmp_pos);    /* the first m, by position */
+    for (int64_t j = 0; j < K; ++j) {
+        idx[j] = j < m ? pr[j].pos : -1;
+        if (sel) sel[j] = j < m ? pr[j].score : INT32_MIN;
+    }
+    free(pr);
+}
+
+/* -------------------------------------------------------------- attention */
+
+static double orc_bf16(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Gated attention of one query row over the listed positions.
+ * q, gate [Hq][d]; k, v [kv_rows][Hkv][d] (one sequence); idx [K].
+ * Entries outside 0..kv_len-1 (the -1 padding) are skipped. gate may be NULL
+ * (ungated). out [Hq][d], lse [Hq] (natural log of the softmax denominator,
+ * including the running max); a row with no valid entry gives out = 0 and
+ * lse = -inf. */
+void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
+                  const uint16_t *v, int64_t kv_len, const int32_t *idx, int K,
+                  const uint16_t *gate, double scale, double *out, double *lse)
+{
+    int G = Hq / Hkv;
+    double *logit = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    for (int h = 0; h < Hq; ++h) {
+        int g = h / G;
+        double m = -INFINITY;
+        for (int t = 0; t < K; ++t) {
+            int64_t s = idx[t];
+            if (s < 0 || s >= kv_len) { logit[t] = -INFINITY; continue; }
+            double dot = 0.0;
+            for (int j = 0; j < d; ++j)
+                dot += orc_bf16(q[h * d + j]) * orc_bf16(k[(s * Hkv + g) * d + j]);
+            logit[t] = scale * dot;
+            if (logit[t] > m) m = logit[t];
+        }
+        double *o = out + (size_t)h * d;
+        for (int j = 0; j < d; ++j) o[j] = 0.0;
+        if (m == -INFINITY) {
+            if (lse) lse[h] = -INFINITY;
+            continue;
+        }
+        double Z = 0.0;
+        for (int t = 0; t < K; ++t) {
+            int64_t s = idx[t];
+            if (s < 0 || s >= kv_len) continue;
+            double e = exp(logit[t] - m);
+            Z += e;
+            for (int j = 0; j < d; ++j) o[j] += e * orc_bf16(v[(s * Hkv + g) * d + j]);
+        }
+        for (int j = 0; j < d; ++j) {
+            o[j] /= Z;
+            if (gate) o[j] /= 1.0 + exp(-orc_bf16(gate[h * d + j]));
+        }
+        if (lse) lse[h] = m + log(Z);
+    }
+    free(logit);
+}
+
+/* ----------------------------------------------------------- whole rows */
+
+/* Scores for a list of (sequence, query row) pairs; rows [nrows][Tk], only
+ * positions 0..p written (p = q_offset[b] + i). Returns ORC_OVERFLOW if any
+ * score overflowed int32; invalid rows (p outside 0..kv_len-1) are left untouched. */
+int orc_scores_rows(int Tq, int Tk, int H_I, int d_I, const int32_t *q_offset,
+                    const int32_t *kv_len, const int8_t *q_idx, const int8_t *k_idx,
+                    const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
+                    int64_t nrows, const int32_t *row_b, const int32_t *row_i, int32_t *S)
+{
+    int rc = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : rc)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int b = row_b[r], i = row_i[r];
+        int64_t p = (int64_t)q_offset[b] + i;
+        if (p < 0 || p >= kv_len[b] || kv_len[b] > Tk) continue;
+        const int8_t *qI = q_idx + ((int64_t)b * Tq + i) * H_I * d_I;
+        const int8_t *kI = k_idx + (int64_t)b * Tk * d_I;
+        const int8_t *wr = w + b * w_stride_b + (int64_t)i * w_stride_q;
+        rc |= orc_score_row(H_I, d_I, qI, kI, wr, p + 1, S + r * (int64_t)Tk);
+    }
+    return rc;
+}
+
+/* Top-K over given score rows: row r has n[r] candidates (positions 0..n[r]-1)
+ * stored at S + r*stride. n[r] <= 0 gives an all -1 row. */
+void orc_topk_rows(int64_t nrows, const int32_t *S, int64_t stride, const int64_t *n, int K,
+                   int32_t *idx, int32_t *sel)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r)
+        orc_topk_row(S + r * stride, n[r] > 0 ? n[r] : 0, K, idx + r * (int64_t)K,
+                     sel ? sel + r * (int64_t)K : NULL);
+}
+
+/* Attention + gate for a list of rows with the given index rows idx [nrows][K]. */
+void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t *kv_len,
+                   const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   const uint16_t *gate, double scale, int64_t nrows, const int32_t *row_b,
+                   const int32_t *row_i, const int32_t *idx, double *out, double *lse)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int b = row_b[r], i = row_i[r];
+        int64_t qrow = (int64_t)b * Tq + i;
+        int64_t kvl = kv_len[b] < Tk ? kv_len[b] : Tk;
+        orc_attn_row(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
+                     v + (int64_t)b * Tk * Hkv * d, kvl, idx + r * (int64_t)K, K,
+                     gate ? gate + qrow * Hq * d : NULL, scale, out + r * (int64_t)Hq * d,
+                     lse ? lse + r * (int64_t)Hq : NULL);
+    }
+}
+
+/* The whole layer for a list of rows: score -> Top-K -> attention -> gate.
+ * idx/sel [nrows][K], out [nrows][Hq][d], lse [nrows][Hq]. Invalid rows give
+ * idx = -1, sel = INT32_MIN, out = 0, lse = -inf. Returns ORC_OVERFLOW if a
+ * score overflowed int32. */
+int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int K,
+                   const int32_t *q_offset, const int32_t *kv_len, const int8_t *q_idx,
+                   const int8_t *k_idx, const int8_t *w, int64_t w_stride_b,
+                   int64_t w_stride_q, const uint16_t *q, const uint16_t *k,
+                   const uint16_t *v, const uint16_t *gate, double scale, int64_t nrows,
+                   const int32_t *row_b, const int32_t *row_i, int32_t *idx, int32_t *sel,
+                   double *out, double *lse)
+{
+    int rc = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : rc)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int b = row_b[r], i = row_i[r];
+        int64_t p = (int64_t)q_offset[b] + i;
+        int32_t *ir = idx + r * (int64_t)K;
+        int32_t *sr = sel ? sel + r * (int64_t)K : NULL;
+        double *orow = out + r * (int64_t)Hq * d;
+        double *lrow = lse ? lse + r * (int64_t)Hq : NULL;
+        if (p < 0 || p >= kv_len[b] || kv_len[b] > Tk) {
+            for (int j = 0; j < K; ++j) { ir[j] = -1; if (sr) sr[j] = INT32_MIN; }
+            for (int64_t j = 0; j < (int64_t)Hq * d; ++j) orow[j] = 0.0;
+            if (lrow) for (int h = 0; h < Hq; ++h) lrow[h] = -INFINITY;
+            continue;
+        }
+        int32_t *S = (int32_t *)malloc((size_t)(p + 1) * sizeof(int32_t));
+        const int8_t *qI = q_idx + ((int64_t)b * Tq + i) * H_I * d_I;
+        const int8_t *kI = k_idx + (int64_t)b * Tk * d_I;
+        const int8_t *wr = w + b * w_stride_b + (int64_t)i * w_stride_q;
+        rc |= orc_score_row(H_I, d_I, qI, kI, wr, p + 1, S);
+        orc_topk_row(S, p + 1, K, ir, sr);
+        free(S);
+        int64_t qrow = (int64_t)b * Tq + i;
+        orc_attn_row(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
+                     v + (int64_t)b * Tk * Hkv * d, kv_len[b], ir, K,
+                     gate ? gate + qrow * Hq * d : NULL, scale, orow, lrow);
+    }
+    return rc;
+}
+
+int orc_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

@@ -1,0 +1,441 @@
+"""Pins for the CPU oracle: facts fixed by the pages and by mathematics, each
+checked against an oracle build (the real one, or a deliberately mutated copy).
+
+Every pin raises AssertionError when the oracle disagrees. None of them retypes
+the oracle's general formula: they use hand-worked values (tests/golden/),
+closed forms of special cases, library routines (torch's SDPA, numpy matmul,
+scipy's expit / logsumexp) and brute-force definitions that differ from the
+oracle's own algorithm (the O(n^2) rank definition of Top-K, the masked dense
+formulation of attention).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+from synth import bf16_bits, bf16_to_f32
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+I32_MIN = np.iinfo(np.int32).min
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bf(x):
+    return bf16_bits(np.asarray(x, np.float32))
+
+
+# ------------------------------------------------------------------ indexer
+
+def pin_indexer_hand(orc):
+    g = _golden("indexer_hand.json")
+    S, ovf = orc.score_row(np.array(g["q_idx"]), np.array(g["k_idx"]), np.array(g["w"]), 5)
+    assert not ovf
+    assert S.tolist() == g["scores"], (S.tolist(), g["scores"])
+
+
+def pin_indexer_unit_keys(orc):
+    """k_s = c_s * e_{j_s} reduces each head's dot to c_s * q[h, j_s]."""
+    r = np.random.default_rng(11)
+    H_I, d_I = 4, 8
+    q = r.integers(-8, 9, size=(H_I, d_I))
+    w = np.array([1, 2, 3, 5])
+    n = 40
+    js = r.integers(0, d_I, size=n)
+    cs = r.integers(-5, 6, size=n)
+    k = np.zeros((n, d_I), np.int64)
+    k[np.arange(n), js] = cs
+    S, _ = orc.score_row(q, k, w, n)
+    want = [(w * np.maximum(0, cs[s] * q[:, js[s]])).sum() for s in range(n)]
+    assert S.tolist() == want
+
+
+def pin_indexer_zero_query(orc):
+    r = np.random.default_rng(12)
+    k = r.integers(-8, 9, size=(30, 16))
+    S, _ = orc.score_row(np.zeros((3, 16), np.int8), k, np.array([1, -2, 4]), 30)
+    assert (S == 0).all()
+
+
+def pin_indexer_one_hot_weights(orc):
+    """With w = e_h the score is ReLU of a textbook dot product (numpy matmul),
+    and doubling w doubles the score exactly."""
+    r = np.random.default_rng(13)
+    H_I, d_I, n = 3, 32, 50
+    q = r.integers(-8, 9, size=(H_I, d_I))
+    k = r.integers(-8, 9, size=(n, d_I))
+    dots = k.astype(np.int64) @ q.T.astype(np.int64)        # [n, H_I]
+    for h in range(H_I):
+        w = np.zeros(H_I, np.int64)
+        w[h] = 1
+        S, _ = orc.score_row(q, k, w, n)
+        assert S.tolist() == np.maximum(dots[:, h], 0).tolist()
+    w = np.array([3, 1, 4])
+    S1, _ = orc.score_row(q, k, w, n)
+    S2, _ = orc.score_row(q, k, 2 * w, n)
+    assert (S2 == 2 * S1.astype(np.int64)).all()
+    assert (S1 >= 0).all()
+
+
+def pin_indexer_head_permutation(orc):
+    r = np.random.default_rng(14)
+    q = r.integers(-8, 9, size=(8, 16))
+    w = r.integers(1, 5, size=8)
+    k = r.integers(-8, 9, size=(25, 16))
+    perm = r.permutation(8)
+    S1, _ = orc.score_row(q, k, w, 25)
+    S2, _ = orc.score_row(q[perm], k, w[perm], 25)
+    assert (S1 == S2).all()
+
+
+def pin_indexer_causal_rows(orc):
+    """Row i of sequence b covers positions 0..q_offset[b]+i (its own included)
+    and leaves the rest undefined; ragged sequences."""
+    r = np.random.default_rng(15)
+    B, Tq, Tk, H_I, d_I = 2, 5, 12, 2, 8
+    q_idx = r.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.int8)
+    k_idx = r.integers(-8, 9, size=(B, Tk, d_I)).astype(np.int8)
+    w = np.array([1, 2], np.int8)
+    q_offset = np.array([0, 6], np.int32)
+    kv_len = np.array([5, 11], np.int32)
+    S = orc.scores(q_idx, k_idx, w, q_offset, kv_len)
+    for b in range(B):
+        for i in range(Tq):
+            p = q_offset[b] + i
+            row = S[b * Tq + i]
+            if p < kv_len[b]:
+                assert (row[p + 1:] == I32_MIN).all()
+                ref, _ = orc.score_row(q_idx[b, i], k_idx[b], w, p + 1)
+                assert (row[:p + 1] == ref).all()
+            else:
+                assert (row == I32_MIN).all()
+    # the row's own key: put a needle at position p and nowhere else
+    q1 = np.zeros((1, 3, 1, 4), np.int8)
+    q1[0, :, 0, 0] = 1
+    k1 = np.zeros((1, 3, 4), np.int8)
+    k1[0, 2, 0] = 7
+    S = orc.scores(q1, k1, np.array([1], np.int8), np.array([0], np.int32),
+                   np.array([3], np.int32))
+    assert S[2, 2] == 7 and S[1, :2].tolist() == [0, 0]
+
+
+def pin_indexer_overflow(orc):
+    """H_I*d_I <= 1024 never leaves int32: the extreme value fits exactly; twice
+    as many heads overflow and are reported."""
+    q = np.full((16, 64), -128, np.int8)
+    k = np.full((2, 64), -128, np.int8)
+    S, ovf = orc.score_row(q, k, np.full(16, 127, np.int8), 2)
+    assert not ovf and S.tolist() == [16 * 127 * 64 * 128 * 128] * 2
+    q = np.full((32, 64), -128, np.int8)
+    _, ovf = orc.score_row(q, k, np.full(32, 127, np.int8), 2)
+    assert ovf
+
+
+# ------------------------------------------------------------------- Top-K
+
+def _rank_topk(S, K):
+    """O(n^2) definition: s is kept iff fewer than K positions rank ahead of it."""
+    n = len(S)
+    keep = [s for s in range(n)
+            if sum(1 for t in range(n) if S[t] > S[s] or (S[t] == S[s] and t < s)) < K]
+    return keep + [-1] * (K - len(keep))
+
+
+def pin_topk_hand(orc):
+    g = _golden("indexer_hand.json")
+    S = np.array(g["scores"], np.int32)
+    for K, want in g["topk"].items():
+        K = int(K)
+        idx, sel = orc.topk(S, 5, K)
+        if K == 1:
+            assert idx[0, 0] == want[0]
+        else:
+            assert idx[0].tolist() == want, (K, idx[0].tolist(), want)
+
+
+def pin_topk_rank_definition(orc):
+    r = np.random.default_rng(21)
+    for trial in range(60):
+        n = int(r.integers(1, 60))
+        hi = int(r.choice([2, 4, 1000]))
+        S = r.integers(-hi, hi, size=n).astype(np.int32)
+        for K in sorted({1, max(1, n // 3), n, n + 5}):
+            idx, sel = orc.topk(S, n, K)
+            want = _rank_topk(S.tolist(), K)
+            assert idx[0].tolist() == want, (S.tolist(), K)
+            m = min(K, n)
+            assert sel[0, :m].tolist() == S[idx[0, :m]].tolist()
+            assert (sel[0, m:] == I32_MIN).all()
+
+
+def pin_topk_closed_forms(orc):
+    n, K = 100, 17
+    idx, _ = orc.topk(np.arange(n, dtype=np.int32), n, K)
+    assert idx[0].tolist() == list(range(n - K, n))
+    idx, _ = orc.topk(-np.arange(n, dtype=np.int32), n, K)
+    assert idx[0].tolist() == list(range(K))
+    idx, _ = orc.topk(np.full(n, 5, np.int32), n, K)
+    assert idx[0].tolist() == list(range(K))
+    S = np.full(n, I32_MIN, np.int32)
+    S[[3, 50, 99]] = np.iinfo(np.int32).max
+    idx, _ = orc.topk(S, n, 5)
+    assert idx[0].tolist() == [0, 1, 3, 50, 99]
+    # only the first n entries of a row are candidates
+    idx, _ = orc.topk(np.arange(n, dtype=np.int32), 10, 4)
+    assert idx[0].tolist() == [6, 7, 8, 9]
+
+
+def pin_topk_invariants(orc):
+    r = np.random.default_rng(22)
+    n, K = 5000, 300
+    S = (r.integers(0, 400, size=n) * r.integers(0, 2, size=n)).astype(np.int32)
+    idx, sel = orc.topk(S, n, K)
+    idx = idx[0]
+    assert (np.diff(idx) > 0).all() and idx[0] >= 0 and idx[-1] < n
+    mask = np.zeros(n, bool)
+    mask[idx] = True
+    v = S[mask].min()
+    assert v >= S[~mask].max()
+    ties_in = np.flatnonzero(mask & (S == v))
+    ties_out = np.flatnonzero(~mask & (S == v))
+    if len(ties_out):
+        assert ties_in.max() < ties_out.min()
+
+
+def pin_topk_split_merge(orc):
+    """Exact two-level selection (used by history-split decode): the Top-K of the
+    union of each chunk's Top-K equals the Top-K of the whole row."""
+    r = np.random.default_rng(23)
+    n, K = 3000, 64
+    S = r.integers(0, 50, size=n).astype(np.int32)
+    want, _ = orc.topk(S, n, K)
+    for chunks in (1, 2, 7, 32):
+        bounds = np.linspace(0, n, chunks + 1).astype(int)
+        cand = []
+        for c in range(chunks):
+            lo, hi = bounds[c], bounds[c + 1]
+            loc, _ = orc.topk(S[lo:hi], hi - lo, K)
+            cand += [lo + s for s in loc[0] if s >= 0]
+        cand = np.array(sorted(cand))
+        sub, _ = orc.topk(S[cand], len(cand), K)
+        got = cand[sub[0][sub[0] >= 0]]
+        assert got.tolist() == want[0].tolist()
+
+
+# --------------------------------------------------------------- attention
+
+def _rand_bf16(r, shape):
+    return _bf(r.standard_normal(shape).astype(np.float32))
+
+
+def _sdpa_dense(q, k, v, scale):
+    """Dense causal attention from torch's SDPA in fp64 (library routine); GQA
+    by repeating each KV head over its group of query heads."""
+    import torch
+    qf = torch.from_numpy(bf16_to_f32(q).astype(np.float64)).permute(0, 2, 1, 3)
+    kf = torch.from_numpy(bf16_to_f32(k).astype(np.float64)).permute(0, 2, 1, 3)
+    vf = torch.from_numpy(bf16_to_f32(v).astype(np.float64)).permute(0, 2, 1, 3)
+    G = qf.shape[1] // kf.shape[1]
+    kf = kf.repeat_interleave(G, dim=1)
+    vf = vf.repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, is_causal=True,
+                                                         scale=scale)
+    logits = (qf @ kf.transpose(-1, -2)) * scale
+    T = qf.shape[2]
+    logits = logits.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), float("-inf"))
+    lse = torch.logsumexp(logits, dim=-1)
+    return o.permute(0, 2, 1, 3).numpy(), lse.permute(0, 2, 1).numpy()
+
+
+def pin_attn_hand(orc):
+    g = _golden("attention_hand.json")
+    q = _bf(g["q"])[None, None]
+    k = _bf(g["k"])[None, :, None]
+    v = _bf(g["v"])[None, :, None]
+    gate = _bf(g["gate"])[None, None]
+    idx = np.array([g["idx"]], np.int32)
+    out, lse = orc.attention(q, k, v, gate, idx, np.array([3]), g["scale"], rows=[[0, 0]])
+    assert np.allclose(out[0], g["out"], rtol=0, atol=1e-14)
+    assert np.allclose(lse[0], g["lse"], rtol=0, atol=1e-14)
+    out, _ = orc.attention(q, k, v, None, idx, np.array([3]), g["scale"], rows=[[0, 0]])
+    assert np.allclose(out[0], g["out_ungated"], rtol=0, atol=1e-14)
+
+
+def pin_attn_dense_equivalence(orc):
+    """K >= p+1 selects every causal position, so the layer is dense causal attention."""
+    r = np.random.default_rng(31)
+    B, T, Hq, Hkv, d = 2, 24, 4, 2, 16
+    q = _rand_bf16(r, (B, T, Hq, d))
+    k = _rand_bf16(r, (B, T, Hkv, d))
+    v = _rand_bf16(r, (B, T, Hkv, d))
+    scale = float(np.float32(0.3))
+    K = T + 3
+    idx = np.full((B * T, K), -1, np.int32)
+    for b in range(B):
+        for i in range(T):
+            idx[b * T + i, :i + 1] = np.arange(i + 1)
+    out, lse = orc.attention(q, k, v, None, idx, np.array([T, T]), scale)
+    ref, ref_lse = _sdpa_dense(q, k, v, scale)
+    assert np.abs(out.reshape(B, T, Hq, d) - ref).max() < 1e-12
+    assert np.abs(lse.reshape(B, T, Hq) - ref_lse).max() < 1e-12
+
+
+def pin_attn_single_key(orc):
+    """K = 1: softmax of one logit is 1, so y = sigmoid(G) * V[s] (scipy expit)."""
+    from scipy.special import expit
+    r = np.random.default_rng(32)
+    Tk, Hq, Hkv, d = 9, 4, 2, 8
+    q = _rand_bf16(r, (1, 1, Hq, d))
+    k = _rand_bf16(r, (1, Tk, Hkv, d))
+    v = _rand_bf16(r, (1, Tk, Hkv, d))
+    gate = _rand_bf16(r, (1, 1, Hq, d))
+    out, _ = orc.attention(q, k, v, gate, np.array([[5]], np.int32), np.array([Tk]), 0.7)
+    vv = bf16_to_f32(v[0, 5]).astype(np.float64)
+    want = np.stack([vv[h // 2] for h in range(Hq)]) * expit(bf16_to_f32(gate[0, 0]).astype(
+        np.float64))
+    assert np.abs(out[0] - want).max() < 1e-14
+
+
+def pin_attn_constant_values(orc):
+    """Every selected V row of KV head g equal to c_g gives o = c_g for its query heads."""
+    r = np.random.default_rng(33)
+    Tk, Hq, Hkv, d = 40, 6, 3, 8
+    q = _rand_bf16(r, (1, 1, Hq, d))
+    k = _rand_bf16(r, (1, Tk, Hkv, d))
+    c = _rand_bf16(r, (Hkv, d))
+    v = np.broadcast_to(c, (1, Tk, Hkv, d)).copy()
+    idx = np.array([r.choice(Tk, 15, replace=False)], np.int32)
+    out, _ = orc.attention(q, k, v, None, idx, np.array([Tk]), 0.25)
+    cf = bf16_to_f32(c).astype(np.float64)
+    for h in range(Hq):
+        assert np.abs(out[0, h] - cf[h // 2]).max() < 1e-14
+
+
+def pin_attn_two_keys(orc):
+    """Two selected keys: the weights are the logistic function of the logit gap."""
+    r = np.random.default_rng(34)
+    d = 8
+    q = _rand_bf16(r, (1, 1, 1, d))
+    k = _rand_bf16(r, (1, 2, 1, d))
+    v = _rand_bf16(r, (1, 2, 1, d))
+    scale = 0.5
+    out, _ = orc.attention(q, k, v, None, np.array([[0, 1]], np.int32), np.array([2]), scale)
+    qf, kf, vf = (bf16_to_f32(x).astype(np.float64) for x in (q, k, v))
+    gap = scale * (float(qf[0, 0, 0] @ kf[0, 0, 0]) - float(qf[0, 0, 0] @ kf[0, 1, 0]))
+    a0 = 1.0 / (1.0 + np.exp(-gap))
+    want = a0 * vf[0, 0, 0] + (1 - a0) * vf[0, 1, 0]
+    assert np.abs(out[0, 0] - want).max() < 1e-14
+
+
+def pin_attn_permutation_and_padding(orc):
+    r = np.random.default_rng(35)
+    Tk, Hq, Hkv, d = 64, 4, 1, 16
+    q = _rand_bf16(r, (1, 1, Hq, d))
+    k = _rand_bf16(r, (1, Tk, Hkv, d))
+    v = _rand_bf16(r, (1, Tk, Hkv, d))
+    sel = np.sort(r.choice(Tk, 20, replace=False)).astype(np.int32)
+    o1, l1 = orc.attention(q, k, v, None, sel[None], np.array([Tk]), 0.25)
+    o2, l2 = orc.attention(q, k, v, None, r.permutation(sel)[None], np.array([Tk]), 0.25)
+    padded = np.concatenate([sel, np.full(7, -1, np.int32)])
+    o3, l3 = orc.attention(q, k, v, None, r.permutation(padded)[None], np.array([Tk]), 0.25)
+    assert np.abs(o1 - o2).max() < 1e-14 and np.abs(o1 - o3).max() < 1e-14
+    assert np.abs(l1 - l3).max() < 1e-14
+
+
+def pin_attn_mask_formulation(orc):
+    """Page 5's form (scores over the whole cache, a sparse mask, masked softmax via
+    torch) equals attention over the gathered rows."""
+    import torch
+    r = np.random.default_rng(36)
+    Tk, Hq, Hkv, d = 50, 4, 2, 16
+    q = _rand_bf16(r, (1, 1, Hq, d))
+    k = _rand_bf16(r, (1, Tk, Hkv, d))
+    v = _rand_bf16(r, (1, Tk, Hkv, d))
+    gate = _rand_bf16(r, (1, 1, Hq, d))
+    sel = np.sort(r.choice(Tk, 12, replace=False)).astype(np.int32)
+    out, lse = orc.attention(q, k, v, gate, sel[None], np.array([Tk]), 0.3)
+    qt = torch.from_numpy(bf16_to_f32(q[0, 0]).astype(np.float64))
+    kt = torch.from_numpy(bf16_to_f32(k[0]).astype(np.float64))
+    vt = torch.from_numpy(bf16_to_f32(v[0]).astype(np.float64))
+    gt = torch.from_numpy(bf16_to_f32(gate[0, 0]).astype(np.float64))
+    mask = torch.full((Tk,), float("-inf"), dtype=torch.float64)
+    mask[torch.from_numpy(sel).long()] = 0.0
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        logits = (kt[:, g] @ qt[h]) * 0.3 + mask
+        a = torch.softmax(logits, dim=0)
+        o = (a[:, None] * vt[:, g]).sum(0) * torch.sigmoid(gt[h])
+        assert (o.numpy() - out[0, h]).__abs__().max() < 1e-13
+        assert abs(torch.logsumexp(logits, 0).item() - lse[0, h]) < 1e-13
+
+
+# -------------------------------------------------------------------- gate
+
+def pin_gate_limits(orc):
+    """G = 0 halves the output; G = +30 leaves it (to 1e-13 relative); the
+    gated/ungated ratio is scipy's expit of G."""
+    from scipy.special import expit
+    r = np.random.default_rng(41)
+    Tk, Hq, Hkv, d = 30, 2, 1, 8
+    q = _rand_bf16(r, (1, 1, Hq, d))
+    k = _rand_bf16(r, (1, Tk, Hkv, d))
+    v = _rand_bf16(r, (1, Tk, Hkv, d))
+    idx = np.arange(Tk, dtype=np.int32)[None]
+    o, _ = orc.attention(q, k, v, None, idx, np.array([Tk]), 0.3)
+    z, _ = orc.attention(q, k, v, _bf(np.zeros((1, 1, Hq, d))), idx, np.array([Tk]), 0.3)
+    assert np.abs(z - o / 2).max() < 1e-15
+    big, _ = orc.attention(q, k, v, _bf(np.full((1, 1, Hq, d), 30.0)), idx, np.array([Tk]), 0.3)
+    assert np.abs(big - o).max() <= 1e-12 * np.abs(o).max()
+    G = _rand_bf16(r, (1, 1, Hq, d))
+    y, _ = orc.attention(q, k, v, G, idx, np.array([Tk]), 0.3)
+    ratio = expit(bf16_to_f32(G[0, 0]).astype(np.float64))
+    assert np.abs(y[0] - o[0] * ratio).max() < 1e-14
+
+
+# ------------------------------------------------------------------- layer
+
+def pin_layer_dense_rows(orc):
+    """Through the whole layer, rows with K >= p+1 equal gated dense causal attention."""
+    from scipy.special import expit
+    import synth
+    cfg = synth.CONFIGS["tiny"].replace(Tq=40, Tk=40)
+    inp = synth.host_inputs(cfg, seed=3)
+    res = orc.layer(inp, K=64)
+    ref, ref_lse = _sdpa_dense(inp["q"], inp["k"], inp["v"], inp["scale"])
+    gate = expit(bf16_to_f32(inp["gate"]).astype(np.float64))
+    want = ref * gate
+    got = res["out"].reshape(want.shape)
+    assert np.abs(got - want).max() < 1e-12
+    assert np.abs(res["lse"].reshape(ref_lse.shape) - ref_lse).max() < 1e-12
+    for i in range(cfg.Tq):
+        assert res["idx"][i].tolist() == list(range(i + 1)) + [-1] * (64 - i - 1)
+
+
+def pin_layer_composition(orc):
+    """The whole-layer entry equals score -> Top-K -> attention run step by step,
+    including an invalid row (position beyond the history) and ragged sequences."""
+    import synth
+    cfg = synth.CONFIGS["tiny"].replace(B=2, Tq=6, Tk=70, K=9, decode=False)
+    inp = synth.host_inputs(cfg, seed=5)
+    inp["q_offset"] = np.array([10, 63], np.int32)
+    inp["kv_len"] = np.array([40, 68], np.int32)
+    res = orc.layer(inp, K=9)
+    S = orc.scores(inp["q_idx"], inp["k_idx"], inp["w"], inp["q_offset"], inp["kv_len"])
+    n = np.array([inp["q_offset"][b] + i + 1 for b in range(2) for i in range(6)])
+    valid = np.array([inp["q_offset"][b] + i < inp["kv_len"][b] for b in range(2)
+                      for i in range(6)])
+    idx, sel = orc.topk(S, np.where(valid, n, 0), 9)
+    out, lse = orc.attention(inp["q"], inp["k"], inp["v"], inp["gate"], idx, inp["kv_len"],
+                             inp["scale"])
+    assert (res["idx"] == idx).all() and (res["sel"] == sel).all()
+    assert np.abs(res["out"] - out).max() == 0.0
+    assert (~valid).sum() == 1 and (res["idx"][~valid] == -1).all()
+    assert (res["out"][~valid] == 0).all() and np.isneginf(res["lse"][~valid]).all()
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,63 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of oracle/oracle.c (on the CPU, in a
+temporary directory), builds it, runs every pin against it and expects at
+least one pin to fail. The real oracle passes all of them (test_oracle_pins.py).
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement); every occurrence of the text is replaced
+MUTANTS = [
+    ("relu_dropped", "if (dot < 0) dot = 0;", ""),
+    ("relu_wrong_side", "if (dot < 0) dot = 0;", "if (dot > 0) dot = 0;"),
+    ("weight_of_head0", "acc += (int64_t)w[h] * dot;", "acc += (int64_t)w[0] * dot;"),
+    ("key_row_shift", "(int64_t)kI[s * d_I + j]", "(int64_t)kI[(s > 0 ? s - 1 : 0) * d_I + j]"),
+    ("query_head_fixed", "(int64_t)qI[h * d_I + j]", "(int64_t)qI[j]"),
+    ("smallest_first", "return a->score > b->score ? -1 : 1;",
+     "return a->score < b->score ? -1 : 1;"),
+    ("tie_higher_index", "    return (a->pos > b->pos) - (a->pos < b->pos);\n}\n\nstatic int orc_cmp_pos",
+     "    return (a->pos < b->pos) - (a->pos > b->pos);\n}\n\nstatic int orc_cmp_pos"),
+    ("output_in_rank_order", "qsort(pr, (size_t)m, sizeof(orc_pair), orc_cmp_pos);", ""),
+    ("causal_excludes_self", "orc_topk_row(S, p + 1, K, ir, sr);", "orc_topk_row(S, p, K, ir, sr);"),
+    ("causal_scores_exclude_self", "rc |= orc_score_row(H_I, d_I, qI, kI, wr, p + 1, S + r * (int64_t)Tk);",
+     "rc |= orc_score_row(H_I, d_I, qI, kI, wr, p, S + r * (int64_t)Tk);"),
+    ("no_softmax_scale", "logit[t] = scale * dot;", "logit[t] = dot;"),
+    ("gqa_modulo", "int g = h / G;", "int g = h % Hkv;"),
+    ("keys_as_values", "o[j] += e * orc_bf16(v[", "o[j] += e * orc_bf16(k["),
+    ("no_normalisation", "o[j] /= Z;", ""),
+    ("gate_sign", "o[j] /= 1.0 + exp(-orc_bf16(", "o[j] /= 1.0 + exp(orc_bf16("),
+    ("gate_dropped", "if (gate) o[j] /= 1.0 + exp(-orc_bf16(gate[h * d + j]));", ""),
+    ("lse_without_max", "lse[h] = m + log(Z);", "lse[h] = log(Z);"),
+    ("padding_read_as_position0", "if (s < 0 || s >= kv_len)", "if (s < 0) s = 0; if (s >= kv_len)"),
+    ("overflow_unchecked", "if (acc > INT32_MAX) { acc = INT32_MAX; rc = ORC_OVERFLOW; }", ""),
+]
+
+
+def test_mutant_table_applies():
+    text = open(SRC).read()
+    for name, old, _ in MUTANTS:
+        assert text.count(old) >= 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) >= 1
+    src = tmp_path / f"oracle_{name}.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.compile_source(str(src), str(tmp_path / f"liboracle_{name}.so"))
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(mutant)
+        except Exception:          # a failing assertion, or a crash of the mutant's output
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name!r}"
