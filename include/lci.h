@@ -1,0 +1,193 @@
+/*
+ * lci.h -- C ABI of the MI355X (gfx950) gated fine-grained sparse attention library.
+ *
+ * The layer, as the pages describe it ("Hybrid Sparse Attention for Long-Context
+ * LLMs", section "Indexer + Top-K: How Fine-Grained Sparse Attention Works",
+ * steps 1-4; "Optimizing LLM Long-Context Inference with Indexed Top-K Sparse
+ * Attention", section "Interface Design for Practical Implementation"; "From
+ * Linear Attention to Gated Sparse Attention", section 2):
+ *   1. a light indexer scores every causal history position for each query,
+ *   2. Top-K keeps the K best positions,
+ *   3. exact softmax attention runs over those K keys/values only,
+ *   4. a sigmoid gate multiplies the output elementwise.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. Tensors are
+ *     dense and row-major in the shapes written next to each argument; the
+ *     library never frees, keeps or retains them after the call returns.
+ *   - Inputs are never written. Outputs are fully overwritten over their whole
+ *     documented extent (scores: see lci_idx_score).
+ *   - Every call is asynchronous: it validates its arguments on the host,
+ *     enqueues kernels on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and returns. There is no host synchronisation, no device
+ *     memory allocation and no global mutable state except the per-thread last
+ *     HIP error. Calls are reentrant; calls that share output or workspace
+ *     buffers must be ordered by the caller.
+ *   - An invalid argument returns an error code synchronously and enqueues
+ *     nothing. The contents of device arrays (q_offset, kv_len, idx) cannot be
+ *     checked on the host; the kernels treat out-of-range values as documented
+ *     below and never read or write outside the buffers described here.
+ *   - bf16 tensors hold bfloat16 bit patterns (lci_bf16 = uint16_t storage).
+ *   - Results are deterministic: repeated calls on the same inputs give
+ *     bit-identical outputs (no floating-point atomics anywhere).
+ *
+ * Positions. Query row i of sequence b sits at absolute position
+ * p = q_offset[b] + i. Its candidate set is every history position 0..p, its
+ * own position included (the key/value cache is kept whole so any past
+ * position can be selected: "Hybrid Sparse Attention ...", section "Why Keep
+ * Linear Attention ...", item 3). A row is VALID when 0 <= p < kv_len[b] <= Tk;
+ * an invalid row produces idx = -1, out = 0 and lse = -inf.
+ *
+ * Indexer arithmetic (the pages give no formula; reading taken):
+ *   S[b,i,s] = sum_{h < H_I} w[b,i,h] * max(0, sum_{j < d_I} qI[b,i,h,j] * kI[b,s,j])
+ * with int8 qI, kI, w and exact int32 accumulation. |S| <= H_I*d_I*128*128*128,
+ * which fits int32 whenever H_I*d_I <= 1024 (checked: LCI_ERR_OVERFLOW_RISK).
+ *
+ * Top-K order: higher score first; on equal scores the lower position wins.
+ * The selected positions are written in ascending position order, followed by
+ * -1 padding when the row has fewer than K candidates (then all are selected,
+ * and the layer equals dense causal attention for that row).
+ *
+ * Supported shapes: d in {64, 128}; Hkv in {1, 2, 4, 8}; G = Hq/Hkv in
+ * {1, 2, 4, 8, 16}; H_I in {1, 2, 4, 8, 16}; d_I in {32, 64, 128} with
+ * H_I*d_I <= 1024; 1 <= K <= 4096; B, Tq, Tk >= 1; Tk < 2^31 / max(4, d_I).
+ */
+#ifndef LCI_H
+#define LCI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCI_ABI_VERSION 1
+
+typedef uint16_t lci_bf16;
+
+typedef enum lci_status {
+    LCI_OK = 0,
+    LCI_ERR_NULL = -1,          /* a required pointer is NULL                           */
+    LCI_ERR_SHAPE = -2,         /* a size is out of range or sizes are inconsistent     */
+    LCI_ERR_UNSUPPORTED = -3,   /* a valid shape that no kernel here implements         */
+    LCI_ERR_OVERFLOW_RISK = -4, /* H_I*d_I > 1024: an int32 score could overflow        */
+    LCI_ERR_WORKSPACE = -5,     /* workspace NULL or smaller than lci_workspace_bytes() */
+    LCI_ERR_HIP = -6,           /* a HIP call failed; see lci_last_hip_error()          */
+    LCI_ERR_ALIGN = -7          /* a pointer is not 16-byte aligned                     */
+} lci_status;
+
+/* Geometry shared by every entry point. */
+typedef struct lci_geom {
+    int32_t B;                 /* sequences                                              */
+    int32_t Tq;                /* query rows per sequence                                */
+    int32_t Tk;                /* history rows allocated per sequence (row stride)       */
+    int32_t Hq, Hkv, d;        /* query heads, key/value heads, head dim                 */
+    int32_t H_I, d_I;          /* indexer heads, indexer dim                             */
+    int32_t K;                 /* positions kept per query row                           */
+    const int32_t *q_offset;   /* device [B]: position of query row 0 of each sequence   */
+    const int32_t *kv_len;     /* device [B]: valid history rows of each sequence        */
+} lci_geom;
+
+/* Entry ids for lci_workspace_bytes. */
+enum {
+    LCI_ENTRY_IDX_SCORE = 0,
+    LCI_ENTRY_TOPK_SELECT = 1,
+    LCI_ENTRY_SPARSE_ATTN = 2,
+    LCI_ENTRY_PREFILL = 3,
+    LCI_ENTRY_DECODE = 4
+};
+
+/* Indexer scoring (step 1). "Hybrid Sparse Attention ...", section "Indexer +
+ * Top-K ...", step 1 and pseudocode line "indexer_score(q, k)"; "Optimizing ...",
+ * section "Two Engineering Considerations", item 1 (a light scorer over
+ * low-dimensional projections).
+ *   q_idx  int8 [B, Tq, H_I, d_I]
+ *   k_idx  int8 [B, Tk, d_I]
+ *   w      int8, element (b, i, h) at w[b*w_stride_b + i*w_stride_q + h];
+ *          strides in elements, 0 broadcasts (a [H_I] vector uses 0, 0)
+ *   scores int32 [B, Tq, Tk] out: S[b,i,s] for s <= p of every valid row; all
+ *          other elements are left unwritten.
+ * Errors: NULL, SHAPE, UNSUPPORTED, OVERFLOW_RISK, HIP. Workspace: none. */
+lci_status lci_idx_score(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
+                         const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
+                         int32_t *scores, void *stream);
+
+/* Top-K selection (step 2). "Hybrid Sparse Attention ...", step 2 and pseudocode
+ * line "topk(s, top_k)"; "Optimizing ...", section "Interface Design", line
+ * "topk(index_score, k=top_k, dim=-1)".
+ *   scores     int32 [B, Tq, Tk]: only s <= p of each row is read
+ *   idx        int32 [B, Tq, K] out: selected positions ascending, -1 padded
+ *   sel_scores int32 [B, Tq, K] out, nullable: the score of each idx entry,
+ *              INT32_MIN in the padding
+ *   workspace  device scratch of at least lci_workspace_bytes(LCI_ENTRY_TOPK_SELECT)
+ * Errors: NULL, SHAPE, WORKSPACE, HIP. */
+lci_status lci_topk_select(const lci_geom *g, const int32_t *scores, int32_t *idx,
+                           int32_t *sel_scores, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/* Sparse exact attention + sigmoid gate (steps 3-4). "Hybrid Sparse Attention
+ * ...", steps 3-4 and pseudocode lines "softmax(q @ k_sel^T / d**0.5) @ v_sel",
+ * "g * o_sparse"; "From Linear Attention ...", section 2, "gate(q) * out".
+ *   q, gate  bf16 [B, Tq, Hq, d]; gate nullable (ungated)
+ *   k, v     bf16 [B, Tk, Hkv, d]; query head h reads key/value head h / (Hq/Hkv)
+ *   idx      int32 [B, Tq, K]: positions to attend; entries outside 0..kv_len[b]-1
+ *            (the -1 padding) are skipped; duplicates count once each; order is free
+ *   out      bf16 [B, Tq, Hq, d] out: sigmoid(gate) * softmax(scale*q.k) v,
+ *            fp32 accumulation, rounded to nearest even; 0 for a row without entries
+ *   lse      fp32 [B, Tq, Hq] out, nullable: natural log of the softmax
+ *            denominator of scale*q.k (-inf for a row without entries)
+ *   workspace scratch of at least lci_workspace_bytes(LCI_ENTRY_SPARSE_ATTN)
+ * Errors: NULL, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN, HIP. */
+lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_bf16 *k,
+                               const lci_bf16 *v, const int32_t *idx, const lci_bf16 *gate,
+                               float softmax_scale, lci_bf16 *out, float *lse,
+                               void *workspace, size_t ws_bytes, void *stream);
+
+/* Fused prefill: steps 1-4 for many query rows per sequence in one call
+ * ("Hybrid Sparse Attention ...", section "Engineering and Evaluation
+ * Recommendations": Top-K and gather need fused kernels; chunked long prefill).
+ * Arguments as in the three calls above; idx_out (int32 [B, Tq, K]) and lse are
+ * nullable. Results equal lci_idx_score -> lci_topk_select ->
+ * lci_sparse_attn_fwd on the same inputs (idx bit-exact).
+ * Errors: NULL, SHAPE, UNSUPPORTED, OVERFLOW_RISK, WORKSPACE, ALIGN, HIP. */
+lci_status lci_prefill_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
+                           const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
+                           const lci_bf16 *q, const lci_bf16 *k, const lci_bf16 *v,
+                           const lci_bf16 *gate, float softmax_scale, lci_bf16 *out,
+                           float *lse, int32_t *idx_out, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/* Fused decode: one query row per sequence (Tq == 1) over a long history, with
+ * the history split across workgroups for scoring, an exact two-level Top-K
+ * and split-K attention combined in a fixed order ("How Fine-Grained Sparse
+ * Attention Reshapes ...", section "Engineering Practices": per-step decode
+ * work decoupled from context length). Same arguments and results as
+ * lci_prefill_fwd.
+ * Errors: NULL, SHAPE (Tq != 1 included), UNSUPPORTED, OVERFLOW_RISK,
+ * WORKSPACE, ALIGN, HIP. */
+lci_status lci_decode_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
+                          const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
+                          const lci_bf16 *q, const lci_bf16 *k, const lci_bf16 *v,
+                          const lci_bf16 *gate, float softmax_scale, lci_bf16 *out,
+                          float *lse, int32_t *idx_out, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/* Workspace bytes an entry needs for this geometry (host only, reads no device
+ * memory). Returns 0 for an invalid geometry or entry id. */
+size_t lci_workspace_bytes(int entry, const lci_geom *g);
+
+/* Static text for a status code. */
+const char *lci_status_str(int status);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int lci_last_hip_error(void);
+
+/* LCI_ABI_VERSION of the loaded library. */
+int lci_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCI_H */

@@ -1,0 +1,276 @@
+"""Gated fine-grained sparse attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over liblci.so, the HIP library whose C ABI is declared in
+include/lci.h. Every step of the layer (indexer scoring, Top-K selection, sparse
+attention, sigmoid gate) runs in the library's kernels; this module only checks
+tensor dtypes/shapes/contiguity, passes device pointers and the current HIP
+stream, and turns status codes into exceptions. PyTorch supplies device memory
+and streams. There is no CPU fallback: without the built library every call
+raises.
+
+Entry points (same names as the C ABI, without the ``lci_`` prefix):
+    idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd,
+    workspace_bytes
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblci.so")
+
+ENTRY_IDX_SCORE, ENTRY_TOPK_SELECT, ENTRY_SPARSE_ATTN, ENTRY_PREFILL, ENTRY_DECODE = range(5)
+
+EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
+           "lci_decode_fwd", "lci_workspace_bytes", "lci_status_str", "lci_last_hip_error",
+           "lci_abi_version")
+
+
+class LciError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class lci_geom(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("Tk", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("H_I", ctypes.c_int32), ("d_I", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("q_offset", ctypes.c_void_p), ("kv_len", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load liblci.so and declare its signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m long_context_indexer_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    G = ctypes.POINTER(lci_geom)
+    lib.lci_idx_score.argtypes = [G, P, P, P, i64, i64, P, P]
+    lib.lci_topk_select.argtypes = [G, P, P, P, P, sz, P]
+    lib.lci_sparse_attn_fwd.argtypes = [G, P, P, P, P, P, ctypes.c_float, P, P, P, sz, P]
+    fused = [G, P, P, P, i64, i64, P, P, P, P, ctypes.c_float, P, P, P, P, sz, P]
+    lib.lci_prefill_fwd.argtypes = fused
+    lib.lci_decode_fwd.argtypes = fused
+    lib.lci_workspace_bytes.argtypes = [ctypes.c_int, G]
+    lib.lci_workspace_bytes.restype = sz
+    lib.lci_status_str.argtypes = [ctypes.c_int]
+    lib.lci_status_str.restype = ctypes.c_char_p
+    lib.lci_last_hip_error.restype = ctypes.c_int
+    lib.lci_abi_version.restype = ctypes.c_int
+    for fn in ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
+               "lci_decode_fwd"):
+        getattr(lib, fn).restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load_library()
+        msg = lib.lci_status_str(rc).decode()
+        if rc == -6:
+            msg += f" (hipError {lib.lci_last_hip_error()})"
+        raise LciError(rc, msg)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t, dtype, name, ndim=None):
+    import torch
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=0, Hkv=0, d=0, H_I=0, d_I=0) -> lci_geom:
+    import torch
+    _dev(q_offset, torch.int32, "q_offset", 1)
+    _dev(kv_len, torch.int32, "kv_len", 1)
+    if q_offset.numel() != B or kv_len.numel() != B:
+        raise ValueError("q_offset and kv_len need one entry per sequence")
+    g = lci_geom(B, Tq, Tk, Hq, Hkv, d, H_I, d_I, K, q_offset.data_ptr(), kv_len.data_ptr())
+    g._keep = (q_offset, kv_len)
+    return g
+
+
+def _w_strides(w, B, Tq, H_I):
+    """Element strides (sequence, row) of indexer weights shaped [H_I], [Tq,H_I] or [B,Tq,H_I]."""
+    if w.dim() == 1 and w.shape[0] == H_I:
+        return 0, 0
+    if w.dim() == 2 and tuple(w.shape) == (Tq, H_I):
+        return 0, H_I
+    if w.dim() == 3 and tuple(w.shape) == (B, Tq, H_I):
+        return Tq * H_I, H_I
+    raise ValueError(f"indexer weights must be [H_I], [Tq,H_I] or [B,Tq,H_I]; got {tuple(w.shape)}")
+
+
+def workspace_bytes(entry: int, geom: lci_geom) -> int:
+    return int(load_library().lci_workspace_bytes(entry, ctypes.byref(geom)))
+
+
+def _workspace(entry, geom, workspace, device):
+    import torch
+    need = workspace_bytes(entry, geom)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def idx_score(q_idx, k_idx, w, q_offset, kv_len, scores=None, stream=None):
+    """Indexer scores int32 [B,Tq,Tk]; only s <= p of each valid row is written."""
+    import torch
+    _dev(q_idx, torch.int8, "q_idx", 4)
+    _dev(k_idx, torch.int8, "k_idx", 3)
+    _dev(w, torch.int8, "w")
+    B, Tq, H_I, d_I = q_idx.shape
+    Tk = k_idx.shape[1]
+    if k_idx.shape[0] != B or k_idx.shape[2] != d_I:
+        raise ValueError("k_idx must be [B,Tk,d_I]")
+    wsb, wsq = _w_strides(w, B, Tq, H_I)
+    g = make_geom(B, Tq, Tk, 1, q_offset, kv_len, H_I=H_I, d_I=d_I)
+    if scores is None:
+        scores = torch.empty((B, Tq, Tk), dtype=torch.int32, device=q_idx.device)
+    _dev(scores, torch.int32, "scores", 3)
+    lib = load_library()
+    _check(lib.lci_idx_score(ctypes.byref(g), _ptr(q_idx), _ptr(k_idx), _ptr(w), wsb, wsq,
+                             _ptr(scores), _stream(stream)))
+    return scores
+
+
+def topk_select(scores, K, q_offset, kv_len, idx=None, sel_scores=None, want_scores=False,
+                workspace=None, stream=None):
+    """Top-K positions int32 [B,Tq,K] (ascending, -1 padded) and optional scores."""
+    import torch
+    _dev(scores, torch.int32, "scores", 3)
+    B, Tq, Tk = scores.shape
+    g = make_geom(B, Tq, Tk, K, q_offset, kv_len)
+    if idx is None:
+        idx = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+    if want_scores and sel_scores is None:
+        sel_scores = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+    _dev(idx, torch.int32, "idx", 3)
+    _dev(sel_scores, torch.int32, "sel_scores", 3)
+    ws, nb = _workspace(ENTRY_TOPK_SELECT, g, workspace, scores.device)
+    lib = load_library()
+    _check(lib.lci_topk_select(ctypes.byref(g), _ptr(scores), _ptr(idx), _ptr(sel_scores),
+                               _ptr(ws), nb, _stream(stream)))
+    return (idx, sel_scores) if want_scores or sel_scores is not None else idx
+
+
+def sparse_attn_fwd(q, k, v, idx, gate, scale, kv_len, q_offset=None, out=None, lse=None,
+                    want_lse=False, workspace=None, stream=None):
+    """Gated attention over the listed positions: out bf16 [B,Tq,Hq,d] (and lse)."""
+    import torch
+    _dev(q, torch.bfloat16, "q", 4)
+    _dev(k, torch.bfloat16, "k", 4)
+    _dev(v, torch.bfloat16, "v", 4)
+    _dev(idx, torch.int32, "idx", 3)
+    _dev(gate, torch.bfloat16, "gate", 4)
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Tk, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k, v must be [B,Tk,Hkv,d]")
+    if idx.shape[:2] != (B, Tq):
+        raise ValueError("idx must be [B,Tq,K]")
+    if gate is not None and tuple(gate.shape) != tuple(q.shape):
+        raise ValueError("gate must match q")
+    if q_offset is None:
+        q_offset = torch.zeros(B, dtype=torch.int32, device=q.device)
+    g = make_geom(B, Tq, Tk, idx.shape[2], q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    _dev(out, torch.bfloat16, "out", 4)
+    _dev(lse, torch.float32, "lse", 3)
+    ws, nb = _workspace(ENTRY_SPARSE_ATTN, g, workspace, q.device)
+    lib = load_library()
+    _check(lib.lci_sparse_attn_fwd(ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                   _ptr(gate), float(scale), _ptr(out), _ptr(lse), _ptr(ws), nb,
+                                   _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K,
+           out, lse, idx_out, want_lse, want_idx, workspace, stream):
+    import torch
+    _dev(q_idx, torch.int8, "q_idx", 4)
+    _dev(k_idx, torch.int8, "k_idx", 3)
+    _dev(w, torch.int8, "w")
+    _dev(q, torch.bfloat16, "q", 4)
+    _dev(k, torch.bfloat16, "k", 4)
+    _dev(v, torch.bfloat16, "v", 4)
+    _dev(gate, torch.bfloat16, "gate", 4)
+    B, Tq, H_I, d_I = q_idx.shape
+    Tk = k_idx.shape[1]
+    _, _, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(q.shape[:2]) != (B, Tq) or tuple(k.shape) != (B, Tk, Hkv, d) or \
+            tuple(v.shape) != tuple(k.shape) or tuple(k_idx.shape) != (B, Tk, d_I):
+        raise ValueError("inconsistent shapes")
+    if gate is not None and tuple(gate.shape) != tuple(q.shape):
+        raise ValueError("gate must match q")
+    wsb, wsq = _w_strides(w, B, Tq, H_I)
+    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d, H_I=H_I, d_I=d_I)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    if want_idx and idx_out is None:
+        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=q.device)
+    _dev(out, torch.bfloat16, "out", 4)
+    _dev(lse, torch.float32, "lse", 3)
+    _dev(idx_out, torch.int32, "idx_out", 3)
+    ws, nb = _workspace(entry, g, workspace, q.device)
+    lib = load_library()
+    _check(getattr(lib, fn_name)(ctypes.byref(g), _ptr(q_idx), _ptr(k_idx), _ptr(w), wsb, wsq,
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(gate), float(scale), _ptr(out),
+                                 _ptr(lse), _ptr(idx_out), _ptr(ws), nb, _stream(stream)))
+    res = [out]
+    if idx_out is not None:
+        res.append(idx_out)
+    if lse is not None:
+        res.append(lse)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def prefill_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None, lse=None,
+                idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None):
+    """Fused layer for many query rows: returns out (and idx, lse when asked)."""
+    return _fused("lci_prefill_fwd", ENTRY_PREFILL, q_idx, k_idx, w, q, k, v, gate, scale,
+                  q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream)
+
+
+def decode_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None, lse=None,
+               idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None):
+    """Fused layer for one query row per sequence (Tq == 1) over a long history."""
+    return _fused("lci_decode_fwd", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, scale,
+                  q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream)

@@ -1,0 +1,162 @@
+// Indexer scoring on gfx950: int8 MFMA over low-dimensional indexer heads.
+//
+// "Hybrid Sparse Attention for Long-Context LLMs", section "Indexer + Top-K: How
+// Fine-Grained Sparse Attention Works", step 1: a light scorer over
+// low-dimensional projections rates every history position for each query. The
+// arithmetic (a reading; the pages give no formula) is
+//   S[b,i,s] = sum_h w[b,i,h] * max(0, qI[b,i,h,:] . kI[b,s,:])   (int8 in, int32 exact)
+//
+// The contraction over d_I is a dense GEMM: rows = (query, indexer head) pairs,
+// columns = history positions. It runs on v_mfma_i32_32x32x32_i8. The 32 MFMA
+// rows of one tile hold 32/H_I queries x H_I heads, placed so that every lane's
+// 16 accumulators are complete head groups of its column's queries: the ReLU
+// and the weighted head sum then run in-lane with no cross-lane traffic.
+//
+// MFMA row r = 8*i + 4*hf + j (i, j in 0..3, hf in 0..1) is "slot" 4*i + j of
+// lane half hf; slot k holds query hf*(16/H_I) + k/H_I, head k%H_I. The output
+// element v of lane l is row 8*(v/4) + 4*(l/32) + v%4, i.e. slot v of half l/32,
+// for column (history position) l%32.
+#include "common.h"
+#include "internal.h"
+
+namespace lci {
+
+template <int H_I, int D_I, int WQ>
+__global__ __launch_bounds__(256) void idx_score_kernel(
+    int Tq, int Tk, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
+    const int8_t* __restrict__ w, int64_t wsb, int64_t wsq, int32_t* __restrict__ scores,
+    int64_t row_stride, int row_begin, int row_count, int keys_per_wg) {
+  constexpr int QW = 32 / H_I;   // query rows per wave tile
+  constexpr int QH = 16 / H_I;   // query rows per lane half
+  constexpr int NCH = D_I / 32;  // 32-deep MFMA steps over d_I
+  constexpr int WK = 4 / WQ;     // waves along the history axis
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int wq = wid % WQ, wk = wid / WQ;
+  const int b = blockIdx.z;
+  const int r0 = (blockIdx.y * WQ + wq) * QW;  // first local row of this wave
+  if (r0 >= row_count) return;
+  const int qoff = q_offset[b];
+  const int kvl = kv_len[b];
+  if (kvl > Tk || kvl <= 0) return;  // invalid sequence: nothing is written
+  const int row0 = row_begin + r0;
+  // last history position any row of this wave may read
+  const int pmax = static_cast<int>(min(static_cast<int64_t>(qoff) + row0 + QW - 1,
+                                        static_cast<int64_t>(kvl) - 1));
+  const int k_begin = blockIdx.x * keys_per_wg;
+  const int k_end = min(k_begin + keys_per_wg, pmax + 1);
+  if (k_begin >= k_end) return;
+
+  // A operand: lane supplies MFMA row l%32
+  v4i a[NCH];
+  {
+    const int r = lane & 31;
+    const int slot = 4 * (r >> 3) + (r & 3);
+    const int hf = (r >> 2) & 1;
+    const int qa = hf * QH + slot / H_I;
+    const int ha = slot % H_I;
+    const int lr = r0 + qa;
+    const bool ok = lr < row_count && row_begin + lr < Tq;
+    const int8_t* src = q_idx + ((static_cast<int64_t>(b) * Tq + row_begin + lr) * H_I + ha) * D_I +
+                        16 * (lane >> 5);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      v4i z = {0, 0, 0, 0};
+      a[c] = ok ? *reinterpret_cast<const v4i*>(src + 32 * c) : z;
+    }
+  }
+  // weights and positions of this lane's output rows (lane half l/32)
+  int wv[16];
+  int prow[QH];      // absolute position of each of the lane's rows (-1: no row)
+  int64_t orow[QH];  // output row offsets
+#pragma unroll
+  for (int qq = 0; qq < QH; ++qq) {
+    const int lr = r0 + (lane >> 5) * QH + qq;
+    const int row = row_begin + lr;
+    const bool ok = lr < row_count && row < Tq;
+    const int64_t p = static_cast<int64_t>(qoff) + row;
+    prow[qq] = (ok && p >= 0 && p < kvl) ? static_cast<int>(p) : -1;
+    orow[qq] = (static_cast<int64_t>(b) * row_count + lr) * row_stride;
+#pragma unroll
+    for (int h = 0; h < H_I; ++h)
+      wv[qq * H_I + h] = ok ? static_cast<int>(w[b * wsb + static_cast<int64_t>(row) * wsq + h]) : 0;
+  }
+
+  const int8_t* kbase = k_idx + static_cast<int64_t>(b) * Tk * D_I + 16 * (lane >> 5);
+  for (int kt = k_begin + wk * 32; kt < k_end; kt += 32 * WK) {
+    const int key = kt + (lane & 31);
+    v4i bf[NCH];
+    const bool kok = key < kvl;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      v4i z = {0, 0, 0, 0};
+      bf[c] = kok ? *reinterpret_cast<const v4i*>(kbase + static_cast<int64_t>(key) * D_I + 32 * c) : z;
+    }
+    v16i acc = {};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c], bf[c], acc, 0, 0, 0);
+#pragma unroll
+    for (int qq = 0; qq < QH; ++qq) {
+      if (key <= prow[qq]) {  // causal: s <= p (also false for rows without a position)
+        int s = 0;
+#pragma unroll
+        for (int h = 0; h < H_I; ++h) s += __mul24(wv[qq * H_I + h], max(acc[qq * H_I + h], 0));
+        scores[orow[qq] + key] = s;
+      }
+    }
+  }
+}
+
+template <int H_I, int D_I>
+static hipError_t launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
+                            const int8_t* w, int64_t wsb, int64_t wsq, int32_t* scores,
+                            int64_t stride, int row_begin, int row_count, hipStream_t st) {
+  constexpr int QW = 32 / H_I;
+  if (row_count >= 4 * QW) {
+    // many query rows: 4 waves on 4 row tiles share each key tile
+    const int keys = 256;
+    dim3 grid((g.Tk + keys - 1) / keys, (row_count + 4 * QW - 1) / (4 * QW), g.B);
+    hipLaunchKernelGGL((idx_score_kernel<H_I, D_I, 4>), grid, dim3(256), 0, st, g.Tq, g.Tk,
+                       g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, wsq, scores, stride,
+                       row_begin, row_count, keys);
+  } else {
+    // few query rows (decode): the 4 waves split the history
+    const int keys = 1024;
+    dim3 grid((g.Tk + keys - 1) / keys, (row_count + QW - 1) / QW, g.B);
+    hipLaunchKernelGGL((idx_score_kernel<H_I, D_I, 1>), grid, dim3(256), 0, st, g.Tq, g.Tk,
+                       g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, wsq, scores, stride,
+                       row_begin, row_count, keys);
+  }
+  return hipGetLastError();
+}
+
+template <int H_I>
+static hipError_t launch_h(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
+                           const int8_t* w, int64_t wsb, int64_t wsq, int32_t* scores,
+                           int64_t stride, int row_begin, int row_count, hipStream_t st) {
+  switch (g.d_I) {
+    case 32: return launch_hd<H_I, 32>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    case 64: return launch_hd<H_I, 64>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    case 128:
+      if constexpr (H_I * 128 <= 1024)
+        return launch_hd<H_I, 128>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_idx_score(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
+                            const int8_t* w, int64_t wsb, int64_t wsq, int32_t* scores,
+                            int64_t stride, int row_begin, int row_count, hipStream_t st) {
+  switch (g.H_I) {
+    case 1: return launch_h<1>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    case 2: return launch_h<2>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    case 4: return launch_h<4>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    case 8: return launch_h<8>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    case 16: return launch_h<16>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lci

@@ -1,0 +1,38 @@
+// Host-side declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lci {
+
+struct Geom {
+  int B, Tq, Tk, Hq, Hkv, d, H_I, d_I, K;
+  const int32_t* q_offset;
+  const int32_t* kv_len;
+};
+
+// ---- indexer scoring
+hipError_t launch_idx_score(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
+                            const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
+                            int32_t* scores, int64_t score_row_stride, int row_begin,
+                            int row_count, hipStream_t stream);
+
+// ---- Top-K over materialised score rows.
+// Both launchers work on query rows [row_begin, row_begin+row_count) of every
+// sequence; the score row of (b, row_begin + r) is at scores + (b*row_count + r)*stride.
+// idx/sel are always the full [B, Tq, K] arrays.
+hipError_t launch_topk_rows(const Geom& g, const int32_t* scores, int64_t score_row_stride,
+                            int row_begin, int row_count, int32_t* idx, int32_t* sel,
+                            hipStream_t stream);
+
+// ---- sparse attention over index rows
+size_t sparse_attn_workspace(const Geom& g, int splits);
+int sparse_attn_pick_splits(const Geom& g);
+hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                              float scale, uint16_t* out, float* lse, int splits,
+                              void* workspace, hipStream_t stream);
+
+}  // namespace lci

@@ -1,0 +1,240 @@
+// C ABI of the library: argument validation on the host, workspace carving and
+// kernel dispatch on the caller's stream. See include/lci.h for the contract.
+#include "../../include/lci.h"
+
+#include <algorithm>
+
+#include "internal.h"
+
+using lci::Geom;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+lci_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return LCI_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return LCI_ERR_HIP;
+}
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int kMaxK = 4096;
+
+// Sizes common to every entry.
+lci_status check_base(const lci_geom* g) {
+  if (!g) return LCI_ERR_NULL;
+  if (!g->q_offset || !g->kv_len) return LCI_ERR_NULL;
+  if (g->B < 1 || g->Tq < 1 || g->Tk < 1 || g->K < 1 || g->K > kMaxK) return LCI_ERR_SHAPE;
+  if (!aligned4(g->q_offset) || !aligned4(g->kv_len)) return LCI_ERR_ALIGN;
+  return LCI_OK;
+}
+
+lci_status check_indexer(const lci_geom* g) {
+  if (g->H_I < 1 || g->d_I < 1) return LCI_ERR_SHAPE;
+  if (static_cast<int64_t>(g->H_I) * g->d_I > 1024) return LCI_ERR_OVERFLOW_RISK;
+  if (!pow2_in(g->H_I, 1, 16) || !(g->d_I == 32 || g->d_I == 64 || g->d_I == 128))
+    return LCI_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(g->Tk) * g->d_I >= (int64_t(1) << 31)) return LCI_ERR_SHAPE;
+  return LCI_OK;
+}
+
+lci_status check_attention(const lci_geom* g) {
+  if (g->Hq < 1 || g->Hkv < 1 || g->d < 1 || g->Hq % g->Hkv != 0) return LCI_ERR_SHAPE;
+  if (!(g->d == 64 || g->d == 128) || !pow2_in(g->Hkv, 1, 8) || !pow2_in(g->Hq / g->Hkv, 1, 16))
+    return LCI_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(g->Tk) * g->Hkv * g->d >= (int64_t(1) << 31)) return LCI_ERR_SHAPE;
+  return LCI_OK;
+}
+
+Geom to_geom(const lci_geom* g) {
+  return Geom{g->B, g->Tq, g->Tk, g->Hq, g->Hkv, g->d, g->H_I, g->d_I, g->K, g->q_offset,
+              g->kv_len};
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Fused prefill: query rows are scored and selected in chunks whose int32 score
+// block stays within kScoreBudget (it then largely stays in the 256 MiB
+// last-level cache between the scoring and selection kernels).
+constexpr size_t kScoreBudget = size_t(128) << 20;
+
+int prefill_chunk_rows(const lci_geom* g) {
+  const size_t per_row = static_cast<size_t>(g->B) * g->Tk * sizeof(int32_t);
+  size_t rows = std::max<size_t>(1, kScoreBudget / per_row);
+  if (rows >= 64) rows = rows / 64 * 64;
+  return static_cast<int>(std::min<size_t>(rows, static_cast<size_t>(g->Tq)));
+}
+
+struct PrefillLayout {
+  size_t idx_off, idx_bytes, score_off, score_bytes, attn_off, attn_bytes, total;
+  int chunk_rows, splits;
+};
+
+PrefillLayout prefill_layout(const lci_geom* g) {
+  PrefillLayout L{};
+  const Geom gg = to_geom(g);
+  L.chunk_rows = prefill_chunk_rows(g);
+  L.splits = lci::sparse_attn_pick_splits(gg);
+  L.idx_off = 0;
+  L.idx_bytes = align_up(static_cast<size_t>(g->B) * g->Tq * g->K * sizeof(int32_t));
+  L.score_off = L.idx_off + L.idx_bytes;
+  L.score_bytes = align_up(static_cast<size_t>(g->B) * L.chunk_rows * g->Tk * sizeof(int32_t));
+  L.attn_off = L.score_off + L.score_bytes;
+  L.attn_bytes = align_up(lci::sparse_attn_workspace(gg, L.splits));
+  L.total = L.attn_off + L.attn_bytes;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lci_abi_version(void) { return LCI_ABI_VERSION; }
+
+int lci_last_hip_error(void) { return g_last_hip_error; }
+
+const char* lci_status_str(int s) {
+  switch (s) {
+    case LCI_OK: return "LCI_OK";
+    case LCI_ERR_NULL: return "LCI_ERR_NULL: a required pointer is NULL";
+    case LCI_ERR_SHAPE: return "LCI_ERR_SHAPE: a size is out of range or inconsistent";
+    case LCI_ERR_UNSUPPORTED: return "LCI_ERR_UNSUPPORTED: no kernel for this shape";
+    case LCI_ERR_OVERFLOW_RISK: return "LCI_ERR_OVERFLOW_RISK: H_I*d_I > 1024 could overflow int32 scores";
+    case LCI_ERR_WORKSPACE: return "LCI_ERR_WORKSPACE: workspace missing or too small";
+    case LCI_ERR_HIP: return "LCI_ERR_HIP: a HIP call failed";
+    case LCI_ERR_ALIGN: return "LCI_ERR_ALIGN: a pointer is not 16-byte aligned";
+    default: return "unknown lci status";
+  }
+}
+
+size_t lci_workspace_bytes(int entry, const lci_geom* g) {
+  if (check_base(g) != LCI_OK) return 0;
+  switch (entry) {
+    case LCI_ENTRY_IDX_SCORE:
+    case LCI_ENTRY_TOPK_SELECT:
+      return 0;
+    case LCI_ENTRY_SPARSE_ATTN: {
+      if (check_attention(g) != LCI_OK) return 0;
+      const Geom gg = to_geom(g);
+      return lci::sparse_attn_workspace(gg, lci::sparse_attn_pick_splits(gg));
+    }
+    case LCI_ENTRY_PREFILL:
+    case LCI_ENTRY_DECODE:
+      if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK) return 0;
+      return prefill_layout(g).total;
+    default:
+      return 0;
+  }
+}
+
+lci_status lci_idx_score(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
+                         const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
+                         int32_t* scores, void* stream) {
+  lci_status s = check_base(g);
+  if (s != LCI_OK) return s;
+  if ((s = check_indexer(g)) != LCI_OK) return s;
+  if (!q_idx || !k_idx || !w || !scores) return LCI_ERR_NULL;
+  if (w_stride_b < 0 || w_stride_q < 0) return LCI_ERR_SHAPE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(scores)) return LCI_ERR_ALIGN;
+  const Geom gg = to_geom(g);
+  return hip_status(lci::launch_idx_score(gg, q_idx, k_idx, w, w_stride_b, w_stride_q, scores,
+                                          g->Tk, 0, g->Tq, static_cast<hipStream_t>(stream)));
+}
+
+lci_status lci_topk_select(const lci_geom* g, const int32_t* scores, int32_t* idx,
+                           int32_t* sel_scores, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  lci_status s = check_base(g);
+  if (s != LCI_OK) return s;
+  if (!scores || !idx) return LCI_ERR_NULL;
+  if (!aligned4(scores) || !aligned4(idx) || (sel_scores && !aligned4(sel_scores)))
+    return LCI_ERR_ALIGN;
+  const Geom gg = to_geom(g);
+  return hip_status(lci::launch_topk_rows(gg, scores, g->Tk, 0, g->Tq, idx, sel_scores,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+lci_status lci_sparse_attn_fwd(const lci_geom* g, const lci_bf16* q, const lci_bf16* k,
+                               const lci_bf16* v, const int32_t* idx, const lci_bf16* gate,
+                               float softmax_scale, lci_bf16* out, float* lse,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  lci_status s = check_base(g);
+  if (s != LCI_OK) return s;
+  if ((s = check_attention(g)) != LCI_OK) return s;
+  if (!q || !k || !v || !idx || !out) return LCI_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (gate && !aligned16(gate)) || !aligned4(idx) || (lse && !aligned4(lse)))
+    return LCI_ERR_ALIGN;
+  const Geom gg = to_geom(g);
+  const int splits = lci::sparse_attn_pick_splits(gg);
+  const size_t need = lci::sparse_attn_workspace(gg, splits);
+  if (need > 0 && (!workspace || ws_bytes < need)) return LCI_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return LCI_ERR_ALIGN;
+  return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, softmax_scale, out, lse,
+                                            splits, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
+                                const int8_t* w, int64_t wsb, int64_t wsq, const lci_bf16* q,
+                                const lci_bf16* k, const lci_bf16* v, const lci_bf16* gate,
+                                float scale, lci_bf16* out, float* lse, int32_t* idx_out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  lci_status s = check_base(g);
+  if (s != LCI_OK) return s;
+  if ((s = check_indexer(g)) != LCI_OK) return s;
+  if ((s = check_attention(g)) != LCI_OK) return s;
+  if (!q_idx || !k_idx || !w || !q || !k || !v || !out) return LCI_ERR_NULL;
+  if (wsb < 0 || wsq < 0) return LCI_ERR_SHAPE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(v) || !aligned16(out) || (gate && !aligned16(gate)) ||
+      (lse && !aligned4(lse)) || (idx_out && !aligned4(idx_out)))
+    return LCI_ERR_ALIGN;
+  const PrefillLayout L = prefill_layout(g);
+  if (!workspace || ws_bytes < L.total) return LCI_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LCI_ERR_ALIGN;
+  const Geom gg = to_geom(g);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx_off);
+  int32_t* sc = reinterpret_cast<int32_t*>(ws + L.score_off);
+  for (int r0 = 0; r0 < g->Tq; r0 += L.chunk_rows) {
+    const int rc = std::min(L.chunk_rows, g->Tq - r0);
+    hipError_t e = lci::launch_idx_score(gg, q_idx, k_idx, w, wsb, wsq, sc, g->Tk, r0, rc, st);
+    if (e != hipSuccess) return hip_status(e);
+    e = lci::launch_topk_rows(gg, sc, g->Tk, r0, rc, idx, nullptr, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, scale, out, lse, L.splits,
+                                            ws + L.attn_off, st));
+}
+
+lci_status lci_prefill_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
+                           const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
+                           const lci_bf16* q, const lci_bf16* k, const lci_bf16* v,
+                           const lci_bf16* gate, float softmax_scale, lci_bf16* out,
+                           float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  return fused_forward(g, q_idx, k_idx, w, w_stride_b, w_stride_q, q, k, v, gate,
+                       softmax_scale, out, lse, idx_out, workspace, ws_bytes, stream);
+}
+
+lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
+                          const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
+                          const lci_bf16* q, const lci_bf16* k, const lci_bf16* v,
+                          const lci_bf16* gate, float softmax_scale, lci_bf16* out,
+                          float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  if (g && g->Tq != 1) return LCI_ERR_SHAPE;
+  return fused_forward(g, q_idx, k_idx, w, w_stride_b, w_stride_q, q, k, v, gate,
+                       softmax_scale, out, lse, idx_out, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"

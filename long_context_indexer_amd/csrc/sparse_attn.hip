@@ -1,0 +1,275 @@
+// Sparse exact attention over gathered key/value rows + sigmoid output gate (gfx950).
+//
+// "Hybrid Sparse Attention for Long-Context LLMs", section "Indexer + Top-K: How
+// Fine-Grained Sparse Attention Works", steps 3-4: standard softmax attention
+// over the selected positions only (scaled by 1/sqrt(d)), then a sigmoid gate
+// that modulates the output per head and feature; "From Linear Attention to
+// Gated Sparse Attention", section 2 (the gate multiplies the attention output).
+//
+// One workgroup per (query row, split of its index list); one wave per key/value
+// head g, which serves that head's G = Hq/Hkv query heads (grouped-query
+// attention). Per chunk of 16 listed positions a wave
+//   - gathers the 16 key rows of head g straight into MFMA A-operand registers
+//     (each lane loads 16 contiguous bytes of one row),
+//   - computes S^T = K_sel . Q^T on v_mfma_f32_16x16x32_bf16 (rows = keys,
+//     columns = the G query heads), so lane l holds keys 4*(l/16)+i of head l%16,
+//   - updates an online softmax in base 2 (logits pre-scaled by scale*log2 e),
+//   - rounds P to bf16; its register layout is already the B operand of
+//     O^T += V^T . P on v_mfma_f32_16x16x16bf16_1k,
+//   - stages the 16 value rows in LDS (per-wave region, row pitch padded to
+//     avoid bank conflicts) and reads them transposed as the A operand.
+// Every per-head statistic lives in the lane that owns that head's column, so
+// rescaling needs no cross-lane traffic; the softmax denominator is kept per
+// lane and reduced once at the end. With one split the epilogue applies
+// sigmoid(gate) and stores bf16; with several splits each writes (m, l, O) and
+// a combine kernel merges the splits in a fixed order (deterministic).
+#include "common.h"
+#include "internal.h"
+
+namespace lci {
+
+template <int D>
+struct AttnCfg {
+  static constexpr int NCH = D / 32;          // 32-deep steps for Q.K
+  static constexpr int NJB = D / 16;          // 16-wide blocks of the value dim
+  static constexpr int PITCH = D + 4;         // LDS row pitch in bf16 (8-byte aligned rows)
+  static constexpr int PART = D + 4;          // floats per split partial: O[D], m, l, l_exact, pad
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void sparse_attn_kernel(
+    int Tq, int Tk, int K, int Hq, int Hkv, int G, const int32_t* __restrict__ kv_len,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ gate, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int splits, int per_split, float* __restrict__ part) {
+  using C = AttnCfg<D>;
+  extern __shared__ uint16_t vstage[];  // [Hkv][16][PITCH]
+  const int lane = threadIdx.x & 63;
+  const int g = threadIdx.x >> 6;
+  // blockIdx.x = (b*Tq + row)*splits + split
+  const int split = static_cast<int>(blockIdx.x % splits);
+  const int64_t qrow = blockIdx.x / splits;
+  const int b = static_cast<int>(qrow / Tq);
+  const int kvl0 = kv_len[b];
+  const int kvl = kvl0 <= Tk ? kvl0 : 0;  // a history longer than its allocation: no entry is read
+  const int e_begin = split * per_split;
+  const int nent = max(0, min(per_split, K - e_begin));
+  const int32_t* ip = idx + qrow * K + e_begin;
+  uint16_t* vs = vstage + g * 16 * C::PITCH;
+
+  const int hl = lane & 15;     // this lane's query-head column
+  const int grp = lane >> 4;    // lane group 0..3
+  const bool hok = hl < G;
+  const int h = g * G + hl;
+
+  v8bf qf[C::NCH];
+  {
+    const uint16_t* qp = q + (qrow * Hq + (hok ? h : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) {
+      v4i z = {0, 0, 0, 0};
+      v4i t = hok ? *reinterpret_cast<const v4i*>(qp + 32 * c) : z;
+      qf[c] = __builtin_bit_cast(v8bf, t);
+    }
+  }
+
+  float m = -INFINITY;  // running max (base-2 units) of head hl
+  float lsum = 0.f;     // this lane's share of the denominator, from the bf16-rounded P
+  float lex = 0.f;      // the same from the unrounded P (for lse only)
+  v4f o[C::NJB];
+#pragma unroll
+  for (int jb = 0; jb < C::NJB; ++jb) o[jb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kbase = k + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
+  const uint16_t* vbase = v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
+  const int64_t rowstep = static_cast<int64_t>(Hkv) * D;
+
+  for (int e0 = 0; e0 < nent; e0 += 16) {
+    // position of listed entry e0 + (lane % 16); invalid entries read row 0 and are masked
+    const int ea = e0 + hl;
+    const int sa = ea < nent ? ip[ea] : -1;
+    const bool va = sa >= 0 && sa < kvl;
+    const int ss = va ? sa : 0;
+    v8bf kf[C::NCH];
+    {
+      const uint16_t* kp = kbase + ss * rowstep + 8 * grp;
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c)
+        kf[c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kp + 32 * c));
+    }
+    // stage the 16 value rows: piece t covers 8 bf16 of row (piece / (D/8))
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const int piece = t * 64 + lane;
+      const int r = piece / (D / 8);
+      const int c8 = piece % (D / 8);
+      const int sr = __shfl(ss, r, 64);
+      const v4i x = *reinterpret_cast<const v4i*>(vbase + sr * rowstep + 8 * c8);
+      uint16_t* dst = vs + r * C::PITCH + 8 * c8;
+      reinterpret_cast<int2*>(dst)[0] = make_int2(x[0], x[1]);
+      reinterpret_cast<int2*>(dst)[1] = make_int2(x[2], x[3]);
+    }
+    v4f st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[c], st, 0, 0, 0);
+
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool vi = __shfl(static_cast<int>(va), 4 * grp + i, 64) != 0;
+      x[i] = vi ? st[i] * scale_log2 : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
+    v4s pb;
+    float psum = 0.f, pex = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pi = (x[i] == -INFINITY) ? 0.f : fast_exp2(x[i] - m_new);
+      const uint16_t hb = f32_to_bf16(pi);
+      pb[i] = static_cast<short>(hb);
+      psum += bf16_to_f32(hb);
+      pex += pi;
+    }
+    // normalising by the sum of the rounded P keeps the weights a convex combination
+    lsum = lsum * alpha + psum;
+    lex = lex * alpha + pex;
+    m = m_new;
+#pragma unroll
+    for (int jb = 0; jb < C::NJB; ++jb) {
+      o[jb] *= alpha;
+      v4s va4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) va4[i] = static_cast<short>(vs[(4 * grp + i) * C::PITCH + 16 * jb + hl]);
+      o[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, pb, o[jb], 0, 0, 0);
+    }
+  }
+
+  lsum += shfl_xor(lsum, 16);
+  lsum += shfl_xor(lsum, 32);
+  lex += shfl_xor(lex, 16);
+  lex += shfl_xor(lex, 32);
+  if (!hok) return;
+  if (splits == 1) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int64_t obase = (qrow * Hq + h) * D + 4 * grp;
+#pragma unroll
+    for (int jb = 0; jb < C::NJB; ++jb) {
+      float gv[4] = {1.f, 1.f, 1.f, 1.f};
+      if (gate) {
+        const int2 graw = *reinterpret_cast<const int2*>(gate + obase + 16 * jb);
+        const uint32_t g01 = static_cast<uint32_t>(graw.x), g23 = static_cast<uint32_t>(graw.y);
+        gv[0] = sigmoidf(bf16_to_f32(g01 & 0xffff));
+        gv[1] = sigmoidf(bf16_to_f32(g01 >> 16));
+        gv[2] = sigmoidf(bf16_to_f32(g23 & 0xffff));
+        gv[3] = sigmoidf(bf16_to_f32(g23 >> 16));
+      }
+      uint32_t w0 = f32_to_bf16(o[jb][0] * inv * gv[0]) | (static_cast<uint32_t>(f32_to_bf16(o[jb][1] * inv * gv[1])) << 16);
+      uint32_t w1 = f32_to_bf16(o[jb][2] * inv * gv[2]) | (static_cast<uint32_t>(f32_to_bf16(o[jb][3] * inv * gv[3])) << 16);
+      *reinterpret_cast<int2*>(out + obase + 16 * jb) = make_int2(static_cast<int>(w0), static_cast<int>(w1));
+    }
+    if (lse && grp == 0) lse[qrow * Hq + h] = lex > 0.f ? (m + fast_log2(lex)) * LN2 : -INFINITY;
+  } else {
+    float* pp = part + ((qrow * Hq + h) * splits + split) * C::PART;
+#pragma unroll
+    for (int jb = 0; jb < C::NJB; ++jb)
+      *reinterpret_cast<v4f*>(pp + 16 * jb + 4 * grp) = o[jb];
+    if (grp == 0) {
+      pp[D] = m;
+      pp[D + 1] = lsum;
+      pp[D + 2] = lex;
+    }
+  }
+}
+
+// Merge the splits of one (row, head) in split order, apply the gate, store.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(
+    int Tq, int Hq, int splits, const float* __restrict__ part,
+    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  using C = AttnCfg<D>;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (h >= Hq) return;
+  const int64_t qrow = blockIdx.x;  // b*Tq + row
+  const float* pp = part + (qrow * Hq + h) * splits * C::PART;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, pp[s * C::PART + D]);
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float L = 0.f, Lex = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float ms = pp[s * C::PART + D];
+    const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+    L += wgt * pp[s * C::PART + D + 1];
+    Lex += wgt * pp[s * C::PART + D + 2];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += wgt * pp[s * C::PART + lane * PER + e];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int64_t obase = (qrow * Hq + h) * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    float y = acc[e] * inv;
+    if (gate) y *= sigmoidf(bf16_to_f32(gate[obase + e]));
+    out[obase + e] = f32_to_bf16(y);
+  }
+  if (lse && lane == 0) lse[qrow * Hq + h] = Lex > 0.f ? (M + fast_log2(Lex)) * LN2 : -INFINITY;
+}
+
+int sparse_attn_pick_splits(const Geom& g) {
+  // enough workgroups to cover the chip several times over; each split keeps
+  // at least 64 listed positions so the per-split partial stays small against
+  // the gathered rows
+  const int64_t rows = static_cast<int64_t>(g.B) * g.Tq;
+  int splits = 1;
+  while (rows * splits < 2048 && g.K / (splits * 2) >= 64) splits *= 2;
+  return splits;
+}
+
+size_t sparse_attn_workspace(const Geom& g, int splits) {
+  if (splits <= 1) return 0;
+  return static_cast<size_t>(g.B) * g.Tq * g.Hq * splits * (g.d + 4) * sizeof(float);
+}
+
+template <int D>
+static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                           float scale, uint16_t* out, float* lse, int splits, void* ws,
+                           hipStream_t st) {
+  using C = AttnCfg<D>;
+  const int G = g.Hq / g.Hkv;
+  int per_split = (g.K + splits - 1) / splits;
+  per_split = (per_split + 15) / 16 * 16;
+  dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq * splits));
+  const size_t lds = static_cast<size_t>(g.Hkv) * 16 * C::PITCH * sizeof(uint16_t);
+  hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * g.Hkv), lds, st, g.Tq, g.Tk, g.K,
+                     g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, scale * LOG2E, out, lse,
+                     splits, per_split, static_cast<float*>(ws));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int hpb = g.Hq < 4 ? g.Hq : 4;  // heads (waves) per combine workgroup
+  dim3 cgrid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq), (g.Hq + hpb - 1) / hpb);
+  hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(64 * hpb), 0, st, g.Tq, g.Hq, splits,
+                     static_cast<const float*>(ws), gate, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                              float scale, uint16_t* out, float* lse, int splits, void* ws,
+                              hipStream_t st) {
+  switch (g.d) {
+    case 64: return launch_d<64>(g, q, k, v, idx, gate, scale, out, lse, splits, ws, st);
+    case 128: return launch_d<128>(g, q, k, v, idx, gate, scale, out, lse, splits, ws, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lci

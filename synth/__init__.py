@@ -115,12 +115,16 @@ def needle_plan(cfg: Config, seed: int, b: int):
     if cfg.needles == "none" or cfg.n_needles == 0:
         return []
     r = _rng(seed, cfg, T_NEEDLE, b)
+    if cfg.needles in ("random", "stride4096"):
+        # prefill: query row t sits at position t, so a needle key at p < t is causal
+        T = min(cfg.Tq, cfg.Tk)
+        if cfg.needles == "random":
+            n = min(cfg.n_needles, T - 1)
+            ps = r.choice(T - 1, size=n, replace=False) if n > 0 else []
+            return [(int(p), int(r.integers(p + 1, T))) for p in ps]
+        return [(4096 * j, int(r.integers(4096 * j + 1, T))) for j in range(cfg.n_needles)
+                if 4096 * j + 1 < T]
     T = cfg.Tk
-    if cfg.needles == "random":
-        ps = r.choice(T - 1, size=cfg.n_needles, replace=False)
-        return [(int(p), int(r.integers(p + 1, T))) for p in ps]
-    if cfg.needles == "stride4096":
-        return [(4096 * j, int(r.integers(4096 * j + 1, T))) for j in range(cfg.n_needles)]
     if cfg.needles == "decode":
         ps = r.choice(T, size=cfg.n_needles, replace=False)
         return [(int(p), 0) for p in ps]

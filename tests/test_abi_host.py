@@ -1,0 +1,154 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/lci.h
+declares, and rejects invalid arguments before touching a device. No kernel is
+launched here (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_indexer_amd as lci
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lci.h")
+
+OK, NULL, SHAPE, UNSUP, OVF, WS, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lci.LIB_PATH):
+        from long_context_indexer_amd import build
+        build.build()
+    return lci.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(lci_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
+              "lci_decode_fwd", "lci_workspace_bytes"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(lci.EXPORTS) <= set(declared_functions())
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.lci_abi_version() == 1
+    for code in (OK, NULL, SHAPE, UNSUP, OVF, WS, HIP, ALIGN):
+        assert lib.lci_status_str(code).decode().startswith("LCI_")
+    assert b"unknown" in lib.lci_status_str(123)
+    assert lib.lci_last_hip_error() == 0
+
+
+def geom(**kw):
+    base = dict(B=1, Tq=16, Tk=64, Hq=8, Hkv=2, d=128, H_I=8, d_I=64, K=8,
+                q_offset=FAKE, kv_len=FAKE)
+    base.update(kw)
+    return lci.lci_geom(base["B"], base["Tq"], base["Tk"], base["Hq"], base["Hkv"], base["d"],
+                        base["H_I"], base["d_I"], base["K"], base["q_offset"], base["kv_len"])
+
+
+def score(lib, g, q=FAKE, k=FAKE, w=FAKE, out=FAKE, wsb=0, wsq=0):
+    return lib.lci_idx_score(ctypes.byref(g) if g is not None else None, q, k, w, wsb, wsq, out,
+                             None)
+
+
+def attn(lib, g, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, gate=None, out=FAKE, ws=None, nb=0):
+    return lib.lci_sparse_attn_fwd(ctypes.byref(g), q, k, v, idx, gate, 0.1, out, None, ws, nb,
+                                   None)
+
+
+def fused(lib, g, fn="lci_prefill_fwd", ws=FAKE, nb=None, **ptrs):
+    p = dict(qi=FAKE, ki=FAKE, w=FAKE, q=FAKE, k=FAKE, v=FAKE, out=FAKE)
+    p.update(ptrs)
+    if nb is None:
+        nb = lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g))
+    return getattr(lib, fn)(ctypes.byref(g), p["qi"], p["ki"], p["w"], 0, 0, p["q"], p["k"], p["v"],
+                            None, 0.1, p["out"], None, None, ws, nb, None)
+
+
+def test_null_arguments(lib):
+    assert score(lib, None) == NULL
+    assert score(lib, geom(q_offset=None)) == NULL
+    assert score(lib, geom(kv_len=None)) == NULL
+    assert score(lib, geom(), q=None) == NULL
+    assert score(lib, geom(), out=None) == NULL
+    assert attn(lib, geom(), idx=None) == NULL
+    assert fused(lib, geom(), v=None) == NULL
+    assert lib.lci_topk_select(ctypes.byref(geom()), None, FAKE, None, None, 0, None) == NULL
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("Tq", 0), ("Tk", 0), ("K", 0), ("K", 4097),
+                                         ("Tq", -3)])
+def test_shape_errors(lib, field, value):
+    assert score(lib, geom(**{field: value})) == SHAPE
+
+
+def test_indexer_limits(lib):
+    assert score(lib, geom(H_I=16, d_I=128)) == OVF          # 2048 > 1024
+    assert score(lib, geom(H_I=32, d_I=64)) == OVF
+    assert score(lib, geom(H_I=3, d_I=64)) == UNSUP
+    assert score(lib, geom(H_I=8, d_I=48)) == UNSUP
+    assert score(lib, geom(H_I=0)) == SHAPE
+    assert score(lib, geom(), wsb=-1) == SHAPE
+    assert score(lib, geom(Tk=1 << 30, d_I=64)) == SHAPE     # Tk*d_I >= 2^31
+
+
+def test_attention_limits(lib):
+    assert attn(lib, geom(d=96)) == UNSUP
+    assert attn(lib, geom(Hq=12, Hkv=8)) == SHAPE            # not a multiple
+    assert attn(lib, geom(Hq=48, Hkv=16)) == UNSUP           # Hkv > 8
+    assert attn(lib, geom(Hq=64, Hkv=2)) == UNSUP            # group of 32 query heads
+    assert attn(lib, geom(Hq=6, Hkv=2)) == UNSUP             # group of 3
+
+
+def test_alignment(lib):
+    assert attn(lib, geom(), q=FAKE + 2) == ALIGN
+    assert attn(lib, geom(), gate=FAKE + 8) == ALIGN
+    assert score(lib, geom(), q=FAKE + 4) == ALIGN
+    assert score(lib, geom(), out=FAKE + 2) == ALIGN
+    assert score(lib, geom(q_offset=FAKE + 2)) == ALIGN
+
+
+def test_workspace_checks(lib):
+    g = geom(B=2, Tq=64, Tk=4096, K=64)
+    need = lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g))
+    assert need >= 2 * 64 * 64 * 4          # at least the index rows
+    assert fused(lib, g, nb=need - 1) == WS
+    assert fused(lib, g, ws=None) == WS
+    assert fused(lib, g, ws=FAKE + 8, nb=need) == ALIGN
+    gd = geom(B=4, Tq=1, Tk=1 << 16, K=2048)
+    needd = lib.lci_workspace_bytes(lci.ENTRY_DECODE, ctypes.byref(gd))
+    assert needd > 0
+    assert fused(lib, gd, fn="lci_decode_fwd", nb=needd - 1) == WS
+    # split-K attention of few long rows needs partials
+    need_a = lib.lci_workspace_bytes(lci.ENTRY_SPARSE_ATTN, ctypes.byref(gd))
+    assert need_a > 0
+    assert attn(lib, gd, ws=None) == WS
+    assert attn(lib, gd, ws=FAKE, nb=need_a - 4) == WS
+    assert lib.lci_workspace_bytes(99, ctypes.byref(g)) == 0
+    assert lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(geom(K=0))) == 0
+    assert lib.lci_workspace_bytes(lci.ENTRY_IDX_SCORE, ctypes.byref(g)) == 0
+
+
+def test_decode_needs_one_row(lib):
+    g = geom(Tq=2, Tk=1024)
+    assert fused(lib, g, fn="lci_decode_fwd") == SHAPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    z = torch.zeros(1, 4, 2, 32, dtype=torch.int8)
+    with pytest.raises((ValueError, RuntimeError)):
+        lci.idx_score(z, torch.zeros(1, 4, 32, dtype=torch.int8), torch.ones(2, dtype=torch.int8),
+                      torch.zeros(1, dtype=torch.int32), torch.ones(1, dtype=torch.int32))
