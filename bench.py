@@ -167,17 +167,21 @@ def main():
         log(f"prefill8k fused: {ms_step:.3f} ms/step ({ev_ms:.3f} ms by events), "
             f"{tok_s / 1e6:.2f} M tok/s")
 
-        # per-stage breakdown through the unfused entries (same kernels)
+        # per-stage breakdown through the unfused entries (the same kernels), every
+        # buffer preallocated so the events time GPU work, not host allocation
         scores = torch.empty((cfg.B, cfg.Tq, cfg.Tk), dtype=torch.int32, device="cuda")
         idx = torch.empty((cfg.B, cfg.Tq, cfg.K), dtype=torch.int32, device="cuda")
-        it = max(3, args.steps // 2)
+        ws_attn = torch.empty(max(1, lci.workspace_bytes(lci.ENTRY_SPARSE_ATTN, geom)),
+                              dtype=torch.uint8, device="cuda")
+        it = max(5, args.steps)
         st_ms = timer.time(lambda: lci.idx_score(d["q_idx"], d["k_idx"], d["w"], d["q_offset"],
                                                  d["kv_len"], scores=scores, stream=stream), it)
         tk_ms = timer.time(lambda: lci.topk_select(scores, cfg.K, d["q_offset"], d["kv_len"],
                                                    idx=idx, stream=stream), it)
         at_ms = timer.time(lambda: lci.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, d["gate"],
-                                                       cfg.scale, d["kv_len"], out=out,
-                                                       stream=stream), it)
+                                                       cfg.scale, d["kv_len"],
+                                                       q_offset=d["q_offset"], out=out,
+                                                       workspace=ws_attn, stream=stream), it)
         del scores
         flops = attn_flops(cfg)
         iops = idx_ops(cfg)
@@ -217,9 +221,13 @@ def main():
         dwall = time.perf_counter() - t0
         dms = dwall * 1e3 / args.steps
         qps = dcfg.B * args.steps / dwall
+        dws_attn = torch.empty(max(1, lci.workspace_bytes(lci.ENTRY_SPARSE_ATTN, dgeom)),
+                               dtype=torch.uint8, device="cuda")
         a_ms = timer.time(lambda: lci.sparse_attn_fwd(dd["q"], dd["k"], dd["v"], didx, dd["gate"],
-                                                      dcfg.scale, dd["kv_len"], out=dout,
-                                                      stream=stream), max(3, args.steps))
+                                                      dcfg.scale, dd["kv_len"],
+                                                      q_offset=dd["q_offset"], out=dout,
+                                                      workspace=dws_attn, stream=stream),
+                          max(5, args.steps))
         abytes = decode_attn_bytes(dcfg)
         sbytes = decode_step_bytes(dcfg)
         res["decode"] = dict(workload="decode128k", ms_per_step=dms, event_ms_per_step=dev_ms,

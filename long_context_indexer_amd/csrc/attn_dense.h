@@ -1,0 +1,26 @@
+// Dense-tile path of sparse attention (see attn_dense.hip).
+#pragma once
+
+#include <algorithm>
+
+#include "internal.h"
+
+namespace lci {
+
+// A query row takes the tile path when its causal history is at most
+// kDenseFactor * K positions long (it then keeps at least 1/kDenseFactor of it).
+constexpr int kDenseFactor = 4;
+constexpr int kDenseMaxWords = (kDenseFactor * 4096 + 31) / 32;
+
+int dense_block_rows(int G);
+int dense_mask_words(const Geom& g);
+size_t dense_workspace(const Geom& g);
+// Builds masks/flags in `ws` (dense_workspace bytes), runs the tile kernel on
+// every token block whose rows all qualify, and returns the row flags so the
+// gather kernel can skip those blocks.
+hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                             float scale, uint16_t* out, float* lse, void* ws, uint8_t** flag_out,
+                             hipStream_t st);
+
+}  // namespace lci

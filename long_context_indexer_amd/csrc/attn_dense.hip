@@ -1,0 +1,384 @@
+// Dense-tile path of sparse attention for prefill rows whose selected set is a
+// large fraction of their causal history (gfx950).
+//
+// The pages' own formulation ("From Linear Attention to Gated Sparse
+// Attention", section 2 pseudocode: build a sparse mask from the Top-K
+// positions, then run attention under that mask) computes the same thing as
+// gathering the selected rows ("Hybrid Sparse Attention for Long-Context LLMs",
+// section "Indexer + Top-K ...", step 3). When a query row keeps a quarter or
+// more of its causal positions (always so for rows with p < K, where every
+// position is kept), streaming contiguous key/value tiles through LDS and
+// masking is much cheaper than gathering 2 KiB per selected position: each key
+// tile is loaded once for 4*32 query rows instead of once per row.
+//
+// Two kernels:
+//   idx_mask_kernel  turns each index row into a bit mask over positions and a
+//                    row flag: 2 = the row keeps exactly 0..p (no mask needed),
+//                    1 = masked tile path, 0 = leave the row to the gather
+//                    kernel (index rows that are not strictly increasing
+//                    positions in 0..p, or rows too sparse for tiles).
+//   attn_dense_kernel one workgroup = 4 waves = 4*32 (token, query head) rows of
+//                    one key/value head g; waves own 32/G tokens x G heads.
+//                    Per 64-key tile: K and V tiles go to LDS (register
+//                    prefetch of the next tile overlaps the MFMAs), then
+//                      S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (lane l owns
+//                            query row l%32, keys 8i+4*(l/32)+j of each 32-key half),
+//                      mask + online softmax in base 2, all lane-local except
+//                            one exchange with lane l^32 for the row max,
+//                      O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, with V^T read
+//                            by ds_read_b64_tr_b16 (each 16-lane group reads a
+//                            4-key x 16-feature block transposed into registers).
+//                    The epilogue applies sigmoid(gate) and stores bf16.
+// Workgroups are placed so that each XCD (its own L2) serves one key/value head
+// (blockIdx.x % 8 picks the XCD), and the longest causal tiles start first.
+#include "attn_dense.h"
+#include "common.h"
+
+namespace lci {
+
+#define LDS_AS __attribute__((address_space(3)))
+
+// ------------------------------------------------------------------ masks
+
+__global__ __launch_bounds__(256) void idx_mask_kernel(
+    int Tq, int Tk, int K, const int32_t* __restrict__ q_offset,
+    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ idx, int lim, int Wm,
+    uint32_t* __restrict__ mask, uint8_t* __restrict__ flag) {
+  __shared__ uint32_t bits[kDenseMaxWords];
+  __shared__ uint32_t red[8];
+  const int64_t row = blockIdx.x;
+  const int b = static_cast<int>(row / Tq);
+  const int i = static_cast<int>(row % Tq);
+  const int kvl = kv_len[b];
+  const int64_t p = static_cast<int64_t>(q_offset[b]) + i;
+  const bool eligible = kvl <= Tk && p >= 0 && p < kvl && p + 1 <= lim;
+  if (!eligible) {
+    if (threadIdx.x == 0) flag[row] = 0;
+    return;
+  }
+  for (int w = threadIdx.x; w < Wm; w += blockDim.x) bits[w] = 0u;
+  __syncthreads();
+  const int32_t* ir = idx + row * K;
+  int bad = 0;
+  uint32_t cnt = 0;
+  for (int j = threadIdx.x; j < K; j += blockDim.x) {
+    const int s = ir[j];
+    if (s == -1) {
+      // padding may only follow padding
+      if (j + 1 < K && ir[j + 1] != -1) bad = 1;
+      continue;
+    }
+    if (s < 0 || s > p) {
+      bad = 1;
+      continue;
+    }
+    if (j > 0 && !(ir[j - 1] >= 0 && ir[j - 1] < s)) bad = 1;
+    atomicOr(&bits[s >> 5], 1u << (s & 31));
+    ++cnt;
+  }
+  bad = __syncthreads_or(bad);
+  cnt = wave_sum(cnt);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  uint32_t tot = 0;
+  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) tot += red[w];
+  const uint8_t f = bad ? 0 : (tot == static_cast<uint32_t>(p + 1) ? 2 : 1);
+  if (threadIdx.x == 0) flag[row] = f;
+  if (f == 1)
+    for (int w = threadIdx.x; w < Wm; w += blockDim.x) mask[row * Wm + w] = bits[w];
+}
+
+// ------------------------------------------------------------ tile kernel
+
+template <int D, int G>
+struct DenseCfg {
+  static constexpr int TW = 32 / G;   // tokens per wave
+  static constexpr int BQ = 4 * TW;   // tokens per workgroup
+  static constexpr int BK = 64;       // keys per tile
+  static constexpr int KP = D + 8;    // LDS row pitch (bf16): 16-byte aligned rows
+  static constexpr int NKK = D / 16;  // 16-deep MFMA steps over d for S^T
+  static constexpr int NDT = D / 32;  // 32-wide d tiles of O^T
+  static constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
+  static constexpr int LPT = BK * CPR / 256;  // 16-byte loads per thread per tile (K and V each)
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void attn_dense_kernel(
+    int Tq, int Tk, int Hq, int Hkv, const int32_t* __restrict__ q_offset,
+    const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ gate, const uint32_t* __restrict__ mask, int Wm,
+    const uint8_t* __restrict__ flag, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int nbps, int nblk) {
+  using C = DenseCfg<D, G>;
+  __shared__ __align__(16) uint16_t ks[C::BK * C::KP];
+  __shared__ __align__(16) uint16_t vsh[C::BK * C::KP];
+
+  // XCD-aware placement: XCD x = blockIdx.x % 8 serves key/value head x / (8/Hkv)
+  const int per = 8 / Hkv;
+  const int xcd = blockIdx.x & 7;
+  const int g = xcd / per;
+  const int blk = (blockIdx.x >> 3) * per + xcd % per;
+  if (blk >= nblk) return;
+  const int b = blk / nbps;
+  const int tb = nbps - 1 - blk % nbps;  // longest causal range first
+  const int i0 = tb * C::BQ;
+  const int iend = min(i0 + C::BQ, Tq);
+
+  // the whole token block must be on this path
+  int ok = 1;
+  if (threadIdx.x < C::BQ && i0 + static_cast<int>(threadIdx.x) < Tq)
+    ok = flag[static_cast<int64_t>(b) * Tq + i0 + threadIdx.x] != 0;
+  if (__syncthreads_and(ok) == 0) return;
+
+  const int qo = q_offset[b];
+  const int kvl = kv_len[b];
+  const int p_last = qo + iend - 1;
+  const int nkb = p_last / C::BK + 1;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int r = lane & 31;
+  const int hf = lane >> 5;
+  const int i = i0 + wv * C::TW + r / G;
+  const int h = g * G + r % G;
+  const bool rv = i < Tq;
+  const int64_t qrow = static_cast<int64_t>(b) * Tq + (rv ? i : 0);
+  const int p = qo + i;
+  const int fl = rv ? flag[qrow] : 0;
+  const uint32_t* mrow = mask + qrow * Wm;
+
+  // Q^T as the B operand: lane holds Q[row][16*kk + 8*hf .. +7]
+  v8bf qf[C::NKK];
+  {
+    const uint16_t* qp = q + (qrow * Hq + h) * D + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      v4i z = {0, 0, 0, 0};
+      v4i t = rv ? *reinterpret_cast<const v4i*>(qp + 16 * kk) : z;
+      qf[kk] = __builtin_bit_cast(v8bf, t);
+    }
+  }
+
+  const int64_t rowstep = static_cast<int64_t>(Hkv) * D;
+  const uint16_t* kbase = k + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
+  const uint16_t* vbase = v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
+
+  // register prefetch of one K/V tile: thread t loads chunks t + 256*c
+  v4i pk[C::LPT], pv[C::LPT];
+  auto prefetch = [&](int kb) {
+#pragma unroll
+    for (int c = 0; c < C::LPT; ++c) {
+      const int chunk = c * 256 + static_cast<int>(threadIdx.x);
+      const int row = chunk / C::CPR;
+      const int col = chunk % C::CPR;
+      const int key = kb * C::BK + row;
+      v4i z = {0, 0, 0, 0};
+      const bool in = key < kvl;
+      pk[c] = in ? *reinterpret_cast<const v4i*>(kbase + key * rowstep + 8 * col) : z;
+      pv[c] = in ? *reinterpret_cast<const v4i*>(vbase + key * rowstep + 8 * col) : z;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int c = 0; c < C::LPT; ++c) {
+      const int chunk = c * 256 + static_cast<int>(threadIdx.x);
+      const int row = chunk / C::CPR;
+      const int col = chunk % C::CPR;
+      *reinterpret_cast<v4i*>(ks + row * C::KP + 8 * col) = pk[c];
+      *reinterpret_cast<v4i*>(vsh + row * C::KP + 8 * col) = pv[c];
+    }
+  };
+
+  float m = -INFINITY, lsum = 0.f, lex = 0.f;
+  v16f o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+
+  prefetch(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();  // previous tile fully consumed
+    stage();
+    __syncthreads();
+    if (kb + 1 < nkb) prefetch(kb + 1);
+
+    // S^T for two 32-key halves
+    v16f st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
+      const uint16_t* ka = ks + (32 * kt + r) * C::KP + 8 * hf;
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        const v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(ka + 16 * kk));
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st[kt], 0, 0, 0);
+      }
+    }
+    // selection bits of this lane's row for the two halves
+    uint32_t mw[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key0 = kb * C::BK + 32 * kt;
+      if (fl == 2) {
+        const int n = p - key0 + 1;  // keys key0..p are kept
+        mw[kt] = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
+      } else if (fl == 1) {
+        const int wi = 2 * kb + kt;
+        mw[kt] = wi < Wm ? mrow[wi] : 0u;
+      } else {
+        mw[kt] = 0u;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kofs = 8 * (e >> 2) + 4 * hf + (e & 3);
+        const bool keep = (mw[kt] >> kofs) & 1u;
+        const float x = keep ? st[kt][e] * scale_log2 : -INFINITY;
+        st[kt][e] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
+    m = m_new;
+    // P^T as the B operand of the PV step s: e<4 -> half-row i=2(s%2), e>=4 -> i=2(s%2)+1
+    v8bf pb[4];
+    float psum = 0.f, pex = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float x = st[kt][e];
+        const float pe = (x == -INFINITY) ? 0.f : fast_exp2(x - m_new);
+        const __bf16 hb = static_cast<__bf16>(pe);
+        pex += pe;
+        psum += static_cast<float>(hb);
+        const int s = 2 * kt + (e >> 3);
+        pb[s][e & 7] = hb;
+      }
+    lsum = lsum * alpha + psum;
+    lex = lex * alpha + pex;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+
+    // O^T += V^T P^T over the 64 keys, four 16-key steps
+    const int gi = lane & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
+        const int k0 = 16 * s + 4 * hf;
+        LDS_AS uint16_t* vl = (LDS_AS uint16_t*)(vsh);
+        LDS_AS v4bf* a0 = (LDS_AS v4bf*)(vl + (k0 + gi / 4) * C::KP + d0 + 4 * (gi % 4));
+        LDS_AS v4bf* a1 = (LDS_AS v4bf*)(vl + (k0 + 8 + gi / 4) * C::KP + d0 + 4 * (gi % 4));
+        const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0);
+        const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1);
+        const v8bf a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  lsum += shfl_xor(lsum, 32);
+  lex += shfl_xor(lex, 32);
+  if (!rv || fl == 0) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int64_t obase = (qrow * Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int d = 32 * dt + 8 * ii + 4 * hf;
+      float gv[4] = {1.f, 1.f, 1.f, 1.f};
+      if (gate) {
+        const int2 graw = *reinterpret_cast<const int2*>(gate + obase + d);
+        gv[0] = sigmoidf(bf16_to_f32(static_cast<uint32_t>(graw.x) & 0xffff));
+        gv[1] = sigmoidf(bf16_to_f32(static_cast<uint32_t>(graw.x) >> 16));
+        gv[2] = sigmoidf(bf16_to_f32(static_cast<uint32_t>(graw.y) & 0xffff));
+        gv[3] = sigmoidf(bf16_to_f32(static_cast<uint32_t>(graw.y) >> 16));
+      }
+      const uint32_t w0 = f32_to_bf16(o[dt][4 * ii] * inv * gv[0]) |
+                          (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * ii + 1] * inv * gv[1])) << 16);
+      const uint32_t w1 = f32_to_bf16(o[dt][4 * ii + 2] * inv * gv[2]) |
+                          (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * ii + 3] * inv * gv[3])) << 16);
+      *reinterpret_cast<int2*>(out + obase + d) = make_int2(static_cast<int>(w0), static_cast<int>(w1));
+    }
+  if (lse && hf == 0) lse[qrow * Hq + h] = lex > 0.f ? (m + fast_log2(lex)) * LN2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------- host side
+
+int dense_block_rows(int G) { return 4 * (32 / G); }
+
+int dense_mask_words(const Geom& g) {
+  const int64_t lim = std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk);
+  return static_cast<int>((lim + 31) / 32);
+}
+
+size_t dense_workspace(const Geom& g) {
+  const size_t rows = static_cast<size_t>(g.B) * g.Tq;
+  const size_t mbytes = (rows * dense_mask_words(g) * sizeof(uint32_t) + 255) & ~size_t(255);
+  return mbytes + ((rows + 255) & ~size_t(255));
+}
+
+template <int D, int G>
+static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const uint16_t* gate, float scale,
+                                  uint16_t* out, float* lse, const uint32_t* mask, int Wm,
+                                  const uint8_t* flag, hipStream_t st) {
+  using C = DenseCfg<D, G>;
+  const int nbps = (g.Tq + C::BQ - 1) / C::BQ;
+  const int nblk = g.B * nbps;
+  const int per = 8 / g.Hkv;
+  const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
+  hipLaunchKernelGGL((attn_dense_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, st,
+                     g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, mask, Wm, flag,
+                     scale * LOG2E, out, lse, nbps, nblk);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dense_d(const Geom& g, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const uint16_t* gate, float scale,
+                                 uint16_t* out, float* lse, const uint32_t* mask, int Wm,
+                                 const uint8_t* flag, hipStream_t st) {
+  switch (g.Hq / g.Hkv) {
+    case 1: return launch_dense_dg<D, 1>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    case 2: return launch_dense_dg<D, 2>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    case 4: return launch_dense_dg<D, 4>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    case 8: return launch_dense_dg<D, 8>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    case 16: return launch_dense_dg<D, 16>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                             float scale, uint16_t* out, float* lse, void* ws, uint8_t** flag_out,
+                             hipStream_t st) {
+  const int Wm = dense_mask_words(g);
+  const size_t rows = static_cast<size_t>(g.B) * g.Tq;
+  uint32_t* mask = static_cast<uint32_t*>(ws);
+  uint8_t* flag = reinterpret_cast<uint8_t*>(static_cast<char*>(ws) +
+                                             ((rows * Wm * sizeof(uint32_t) + 255) & ~size_t(255)));
+  const int lim = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
+  hipLaunchKernelGGL(idx_mask_kernel, dim3(static_cast<uint32_t>(rows)), dim3(256), 0, st, g.Tq,
+                     g.Tk, g.K, g.q_offset, g.kv_len, idx, lim, Wm, mask, flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  *flag_out = flag;
+  switch (g.d) {
+    case 64: return launch_dense_d<64>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    case 128: return launch_dense_d<128>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lci

@@ -23,6 +23,7 @@
 // lane and reduced once at the end. With one split the epilogue applies
 // sigmoid(gate) and stores bf16; with several splits each writes (m, l, O) and
 // a combine kernel merges the splits in a fixed order (deterministic).
+#include "attn_dense.h"
 #include "common.h"
 #include "internal.h"
 
@@ -42,7 +43,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ gate, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int splits, int per_split, float* __restrict__ part) {
+    float* __restrict__ lse, int splits, int per_split, float* __restrict__ part,
+    const uint8_t* __restrict__ dflag, int dbq) {
   using C = AttnCfg<D>;
   extern __shared__ uint16_t vstage[];  // [Hkv][16][PITCH]
   const int lane = threadIdx.x & 63;
@@ -51,6 +53,14 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   const int split = static_cast<int>(blockIdx.x % splits);
   const int64_t qrow = blockIdx.x / splits;
   const int b = static_cast<int>(qrow / Tq);
+  if (dflag) {
+    // rows of a token block that the tile kernel took are done already
+    const int i = static_cast<int>(qrow % Tq);
+    const int r0 = i / dbq * dbq, r1 = min(r0 + dbq, Tq);
+    bool all = true;
+    for (int rr = r0; rr < r1; ++rr) all = all && dflag[static_cast<int64_t>(b) * Tq + rr] != 0;
+    if (all) return;
+  }
   const int kvl0 = kv_len[b];
   const int kvl = kvl0 <= Tk ? kvl0 : 0;  // a history longer than its allocation: no entry is read
   const int e_begin = split * per_split;
@@ -234,7 +244,7 @@ int sparse_attn_pick_splits(const Geom& g) {
 }
 
 size_t sparse_attn_workspace(const Geom& g, int splits) {
-  if (splits <= 1) return 0;
+  if (splits <= 1) return dense_workspace(g);
   return static_cast<size_t>(g.B) * g.Tq * g.Hq * splits * (g.d + 4) * sizeof(float);
 }
 
@@ -247,11 +257,16 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   const int G = g.Hq / g.Hkv;
   int per_split = (g.K + splits - 1) / splits;
   per_split = (per_split + 15) / 16 * 16;
+  uint8_t* dflag = nullptr;
+  if (splits == 1) {
+    hipError_t e0 = launch_dense_attn(g, q, k, v, idx, gate, scale, out, lse, ws, &dflag, st);
+    if (e0 != hipSuccess) return e0;
+  }
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq * splits));
   const size_t lds = static_cast<size_t>(g.Hkv) * 16 * C::PITCH * sizeof(uint16_t);
   hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * g.Hkv), lds, st, g.Tq, g.Tk, g.K,
                      g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, scale * LOG2E, out, lse,
-                     splits, per_split, static_cast<float*>(ws));
+                     splits, per_split, static_cast<float*>(ws), dflag, dense_block_rows(G));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int hpb = g.Hq < 4 ? g.Hq : 4;  // heads (waves) per combine workgroup

@@ -126,17 +126,21 @@ ATTN_CASES = {
 }
 
 
+@pytest.mark.parametrize("order", ["sorted", "scrambled"])
 @pytest.mark.parametrize("name", list(ATTN_CASES))
-def test_sparse_attn_on_oracle_idx(lci, orc, name):
+def test_sparse_attn_on_oracle_idx(lci, orc, name, order):
+    """Sorted index rows (the Top-K output form) may take the dense-tile path;
+    scrambled rows must take the gather path; both must match the oracle."""
     import torch
     cfg, K, gated = ATTN_CASES[name]
     inp = make(cfg.replace(K=K), seed=3)
     log(f"sparse_attn {name}: B={cfg.B} Tq={cfg.Tq} Tk={cfg.Tk} Hq={cfg.Hq} Hkv={cfg.Hkv} "
         f"d={cfg.d} K={K}")
     res = orc.layer(inp, K, gated=gated)
-    # scramble the order of each index row (the kernel must not depend on it)
-    r = np.random.default_rng(0)
-    idx = np.stack([r.permutation(row) for row in res["idx"]]).astype(np.int32)
+    idx = res["idx"]
+    if order == "scrambled":
+        r = np.random.default_rng(0)
+        idx = np.stack([r.permutation(row) for row in idx]).astype(np.int32)
     d = to_device(inp)
     out, lse = lci.sparse_attn_fwd(d["q"], d["k"], d["v"], dev(idx.reshape(cfg.B, cfg.Tq, K)),
                                    d["gate"] if gated else None, inp["scale"], d["kv_len"],
