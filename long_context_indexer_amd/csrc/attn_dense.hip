@@ -179,14 +179,16 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
       pv[c] = in ? *reinterpret_cast<const v4i*>(vbase + key * rowstep + 8 * col) : z;
     }
   };
+  LDS_AS uint16_t* ksl = (LDS_AS uint16_t*)(ks);
+  LDS_AS uint16_t* vsl = (LDS_AS uint16_t*)(vsh);
   auto stage = [&]() {
 #pragma unroll
     for (int c = 0; c < C::LPT; ++c) {
       const int chunk = c * 256 + static_cast<int>(threadIdx.x);
       const int row = chunk / C::CPR;
       const int col = chunk % C::CPR;
-      *reinterpret_cast<v4i*>(ks + row * C::KP + 8 * col) = pk[c];
-      *reinterpret_cast<v4i*>(vsh + row * C::KP + 8 * col) = pv[c];
+      *(LDS_AS v4i*)(ksl + row * C::KP + 8 * col) = pk[c];
+      *(LDS_AS v4i*)(vsl + row * C::KP + 8 * col) = pv[c];
     }
   };
 
@@ -210,10 +212,10 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
-      const uint16_t* ka = ks + (32 * kt + r) * C::KP + 8 * hf;
+      const LDS_AS uint16_t* ka = ksl + (32 * kt + r) * C::KP + 8 * hf;
 #pragma unroll
       for (int kk = 0; kk < C::NKK; ++kk) {
-        const v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(ka + 16 * kk));
+        const v8bf a = __builtin_bit_cast(v8bf, *(const LDS_AS v4i*)(ka + 16 * kk));
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st[kt], 0, 0, 0);
       }
     }
@@ -275,9 +277,8 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
       for (int dt = 0; dt < C::NDT; ++dt) {
         const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
         const int k0 = 16 * s + 4 * hf;
-        LDS_AS uint16_t* vl = (LDS_AS uint16_t*)(vsh);
-        LDS_AS v4bf* a0 = (LDS_AS v4bf*)(vl + (k0 + gi / 4) * C::KP + d0 + 4 * (gi % 4));
-        LDS_AS v4bf* a1 = (LDS_AS v4bf*)(vl + (k0 + 8 + gi / 4) * C::KP + d0 + 4 * (gi % 4));
+        LDS_AS v4bf* a0 = (LDS_AS v4bf*)(vsl + (k0 + gi / 4) * C::KP + d0 + 4 * (gi % 4));
+        LDS_AS v4bf* a1 = (LDS_AS v4bf*)(vsl + (k0 + 8 + gi / 4) * C::KP + d0 + 4 * (gi % 4));
         const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0);
         const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1);
         const v8bf a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   lsum += shfl_xor(lsum, 32);
   lex += shfl_xor(lex, 32);
   if (!rv || fl == 0) return;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
   const int64_t obase = (qrow * Hq + h) * D;
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)

@@ -6,6 +6,7 @@
 
 namespace lci {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -36,9 +37,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Reciprocal by v_rcp_f32 (about 1 ulp) instead of the correctly rounded
+// division sequence.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // Sigmoid from 2^x: 1 / (1 + 2^(-x*log2 e)).
 __device__ __forceinline__ float sigmoidf(float x) {
-  return 1.0f / (1.0f + fast_exp2(-x * LOG2E));
+  return fast_rcp(1.0f + fast_exp2(-x * LOG2E));
 }
 
 // Order-preserving map of int32 scores to uint32 keys (sign bit flipped).

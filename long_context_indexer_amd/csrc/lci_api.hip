@@ -4,6 +4,7 @@
 
 #include <algorithm>
 
+#include "decode.h"
 #include "internal.h"
 
 using lci::Geom;
@@ -124,9 +125,11 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
       return lci::sparse_attn_workspace(gg, lci::sparse_attn_pick_splits(gg));
     }
     case LCI_ENTRY_PREFILL:
-    case LCI_ENTRY_DECODE:
       if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK) return 0;
       return prefill_layout(g).total;
+    case LCI_ENTRY_DECODE:
+      if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK || g->Tq != 1) return 0;
+      return lci::decode_layout(to_geom(g)).total;
     default:
       return 0;
   }
@@ -232,9 +235,26 @@ lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* 
                           const lci_bf16* gate, float softmax_scale, lci_bf16* out,
                           float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
                           void* stream) {
-  if (g && g->Tq != 1) return LCI_ERR_SHAPE;
-  return fused_forward(g, q_idx, k_idx, w, w_stride_b, w_stride_q, q, k, v, gate,
-                       softmax_scale, out, lse, idx_out, workspace, ws_bytes, stream);
+  lci_status s = check_base(g);
+  if (s != LCI_OK) return s;
+  if (g->Tq != 1) return LCI_ERR_SHAPE;
+  if ((s = check_indexer(g)) != LCI_OK) return s;
+  if ((s = check_attention(g)) != LCI_OK) return s;
+  if (static_cast<int64_t>(g->Tk) > static_cast<int64_t>(lci::kDecChunk) * lci::kDecMaxChunks)
+    return LCI_ERR_SHAPE;
+  if (!q_idx || !k_idx || !w || !q || !k || !v || !out) return LCI_ERR_NULL;
+  if (w_stride_b < 0 || w_stride_q < 0) return LCI_ERR_SHAPE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(v) || !aligned16(out) || (gate && !aligned16(gate)) ||
+      (lse && !aligned4(lse)) || (idx_out && !aligned4(idx_out)))
+    return LCI_ERR_ALIGN;
+  const Geom gg = to_geom(g);
+  const lci::DecLayout L = lci::decode_layout(gg);
+  if (!workspace || ws_bytes < L.total) return LCI_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LCI_ERR_ALIGN;
+  return hip_status(lci::launch_decode(gg, q_idx, k_idx, w, w_stride_b, q, k, v, gate,
+                                       softmax_scale, out, lse, idx_out, workspace,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -22,20 +22,71 @@
 // rescaling needs no cross-lane traffic; the softmax denominator is kept per
 // lane and reduced once at the end. With one split the epilogue applies
 // sigmoid(gate) and stores bf16; with several splits each writes (m, l, O) and
-// a combine kernel merges the splits in a fixed order (deterministic).
+// a combine kernel merges them in split order (deterministic).
 #include "attn_dense.h"
 #include "common.h"
 #include "internal.h"
 
 namespace lci {
 
+#define LDS_AS __attribute__((address_space(3)))
+
 template <int D>
 struct AttnCfg {
   static constexpr int NCH = D / 32;          // 32-deep steps for Q.K
   static constexpr int NJB = D / 16;          // 16-wide blocks of the value dim
-  static constexpr int PITCH = D + 4;         // LDS row pitch in bf16 (8-byte aligned rows)
+  static constexpr int PITCH = D + 8;         // LDS row pitch in bf16: rows 16-byte aligned, as the
+                                              // transposed LDS read (ds_read_b64_tr_b16) needs
   static constexpr int PART = D + 4;          // floats per split partial: O[D], m, l, l_exact, pad
 };
+
+// Merge the splits of one query row in split order (fixed, so deterministic),
+// apply the gate and store. A kernel of its own: on a multi-XCD part, handing
+// partials from workgroup to workgroup inside one kernel needs an L2 write-back
+// per workgroup, a kernel boundary needs one. Thread t owns 4 consecutive
+// features of one (row, head) and reads every split's (m, l) and its 4 partial
+// features; the loads of different splits are independent, so they overlap.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(int Hq, int splits,
+                                                           const float* __restrict__ part,
+                                                           const uint16_t* __restrict__ gate,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  using C = AttnCfg<D>;
+  constexpr int QPH = D / 4;  // threads per head
+  const int64_t qrow = blockIdx.x;
+  const int t = blockIdx.y * blockDim.x + threadIdx.x;
+  if (t >= Hq * QPH) return;
+  const int h = t / QPH;
+  const int j0 = 4 * (t % QPH);
+  const float* pp = part + (qrow * Hq + h) * splits * C::PART;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, pp[s * C::PART + D]);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f, Lex = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    const float* ps = pp + s * C::PART;
+    const float ms = ps[D];
+    const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+    L += wgt * ps[D + 1];
+    Lex += wgt * ps[D + 2];
+    acc += wgt * *reinterpret_cast<const v4f*>(ps + j0);
+  }
+  const float inv = L > 0.f ? fast_rcp(L) : 0.f;
+  const int64_t obase = (qrow * Hq + h) * D + j0;
+  uint16_t ys[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float y = acc[e] * inv;
+    if (gate) y *= sigmoidf(bf16_to_f32(gate[obase + e]));
+    ys[e] = f32_to_bf16(y);
+  }
+  *reinterpret_cast<int2*>(out + obase) =
+      make_int2(static_cast<int>(ys[0] | (static_cast<uint32_t>(ys[1]) << 16)),
+                static_cast<int>(ys[2] | (static_cast<uint32_t>(ys[3]) << 16)));
+  if (lse && j0 == 0) lse[qrow * Hq + h] = Lex > 0.f ? (M + fast_log2(Lex)) * LN2 : -INFINITY;
+}
 
 template <int D>
 __global__ __launch_bounds__(512) void sparse_attn_kernel(
@@ -46,7 +97,9 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
     float* __restrict__ lse, int splits, int per_split, float* __restrict__ part,
     const uint8_t* __restrict__ dflag, int dbq) {
   using C = AttnCfg<D>;
-  extern __shared__ uint16_t vstage[];  // [Hkv][16][PITCH]
+  // [Hkv][16][PITCH]; 16-byte aligned wherever the dynamic LDS region starts:
+  // its 8-byte writes and transposed reads need aligned rows
+  extern __shared__ __align__(16) uint16_t vstage[];
   const int lane = threadIdx.x & 63;
   const int g = threadIdx.x >> 6;
   // blockIdx.x = (b*Tq + row)*splits + split
@@ -95,30 +148,43 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   const uint16_t* vbase = v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
   const int64_t rowstep = static_cast<int64_t>(Hkv) * D;
 
-  for (int e0 = 0; e0 < nent; e0 += 16) {
-    // position of listed entry e0 + (lane % 16); invalid entries read row 0 and are masked
-    const int ea = e0 + hl;
-    const int sa = ea < nent ? ip[ea] : -1;
+  // listed position of entry e0 + (lane % 16), read unconditionally (clamped)
+  // so every load in the loop is straight-line and the compiler can wait for
+  // exactly the loads a step needs; -1 past the end of the list
+  const int last = max(nent - 1, 0);
+  auto entry = [&](int e0) {
+    const int e = e0 + hl;
+    const int v0 = ip[min(e, last)];
+    return e < nent ? v0 : -1;
+  };
+  // issue the key fragment and value-row loads of one 16-entry chunk
+  auto issue = [&](int sa, v8bf (&kf)[C::NCH], v4i (&vx)[D / 32]) {
     const bool va = sa >= 0 && sa < kvl;
-    const int ss = va ? sa : 0;
-    v8bf kf[C::NCH];
-    {
-      const uint16_t* kp = kbase + ss * rowstep + 8 * grp;
+    const int ss = va ? sa : 0;  // invalid entries read row 0 and are masked
+    const uint16_t* kp = kbase + ss * rowstep + 8 * grp;
 #pragma unroll
-      for (int c = 0; c < C::NCH; ++c)
-        kf[c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kp + 32 * c));
-    }
-    // stage the 16 value rows: piece t covers 8 bf16 of row (piece / (D/8))
+    for (int c = 0; c < C::NCH; ++c)
+      kf[c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kp + 32 * c));
+    // value piece t of this lane: row (t*64 + lane) / (D/8) of the chunk
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
       const int piece = t * 64 + lane;
-      const int r = piece / (D / 8);
-      const int c8 = piece % (D / 8);
-      const int sr = __shfl(ss, r, 64);
-      const v4i x = *reinterpret_cast<const v4i*>(vbase + sr * rowstep + 8 * c8);
-      uint16_t* dst = vs + r * C::PITCH + 8 * c8;
-      reinterpret_cast<int2*>(dst)[0] = make_int2(x[0], x[1]);
-      reinterpret_cast<int2*>(dst)[1] = make_int2(x[2], x[3]);
+      const int sr = __shfl(ss, piece / (D / 8), 64);
+      vx[t] = *reinterpret_cast<const v4i*>(vbase + sr * rowstep + 8 * (piece % (D / 8)));
+    }
+  };
+
+  LDS_AS uint16_t* vl = (LDS_AS uint16_t*)(vs);
+  // one 16-entry chunk: stage V, S^T, online softmax, O^T += V^T P^T
+  auto compute = [&](const v8bf (&kf)[C::NCH], const v4i (&vx)[D / 32], bool va) {
+    // stage the 16 value rows (row-major, padded pitch); stores and the
+    // transposed reads below are DS operations of this wave, in program order
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const int piece = t * 64 + lane;
+      LDS_AS v2i* dst = (LDS_AS v2i*)(vl + (piece / (D / 8)) * C::PITCH + 8 * (piece % (D / 8)));
+      dst[0] = v2i{vx[t][0], vx[t][1]};
+      dst[1] = v2i{vx[t][2], vx[t][3]};
     }
     v4f st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -149,13 +215,40 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
     lsum = lsum * alpha + psum;
     lex = lex * alpha + pex;
     m = m_new;
+    // V^T by transposed LDS reads: the 16 lanes of group grp read keys 4*grp..4*grp+3,
+    // lane hl receives feature 16*jb + hl of those four keys
+    const int vr = 4 * grp + hl / 4;
 #pragma unroll
     for (int jb = 0; jb < C::NJB; ++jb) {
       o[jb] *= alpha;
-      v4s va4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) va4[i] = static_cast<short>(vs[(4 * grp + i) * C::PITCH + 16 * jb + hl]);
+      LDS_AS v4bf* ap = (LDS_AS v4bf*)(vl + vr * C::PITCH + 16 * jb + 4 * (hl % 4));
+      const v4s va4 = __builtin_bit_cast(v4s, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(ap));
       o[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, pb, o[jb], 0, 0, 0);
+    }
+  };
+
+  // two named buffers (X for even chunks, Y for odd ones) and two entry
+  // registers, so no register with a load in flight is ever copied: the loads
+  // of chunk c+1 stay in flight while chunk c is computed
+  if (nent > 0) {
+    v8bf kx[C::NCH], ky[C::NCH];
+    v4i vxx[D / 32], vxy[D / 32];
+    int ex = entry(0);
+    int ey = entry(16);
+    issue(ex, kx, vxx);
+    for (int e0 = 0; e0 < nent; e0 += 32) {
+      issue(ey, ky, vxy);                     // chunk e0+16 (clamped reads if past the end)
+      const bool vx_ok = ex >= 0 && ex < kvl;
+      ex = entry(e0 + 32);
+      // keep the scheduler from sinking these loads to their use
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kx, vxx, vx_ok);
+      if (e0 + 16 >= nent) break;
+      issue(ex, kx, vxx);                     // chunk e0+32
+      const bool vy_ok = ey >= 0 && ey < kvl;
+      ey = entry(e0 + 48);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ky, vxy, vy_ok);
     }
   }
 
@@ -164,8 +257,20 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   lex += shfl_xor(lex, 16);
   lex += shfl_xor(lex, 32);
   if (!hok) return;
-  if (splits == 1) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  if (splits > 1) {
+    float* pp = part + ((qrow * Hq + h) * splits + split) * C::PART;
+#pragma unroll
+    for (int jb = 0; jb < C::NJB; ++jb)
+      *reinterpret_cast<v4f*>(pp + 16 * jb + 4 * grp) = o[jb];
+    if (grp == 0) {
+      pp[D] = m;
+      pp[D + 1] = lsum;
+      pp[D + 2] = lex;
+    }
+    return;
+  }
+  {
+    const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
     const int64_t obase = (qrow * Hq + h) * D + 4 * grp;
 #pragma unroll
     for (int jb = 0; jb < C::NJB; ++jb) {
@@ -183,54 +288,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
       *reinterpret_cast<int2*>(out + obase + 16 * jb) = make_int2(static_cast<int>(w0), static_cast<int>(w1));
     }
     if (lse && grp == 0) lse[qrow * Hq + h] = lex > 0.f ? (m + fast_log2(lex)) * LN2 : -INFINITY;
-  } else {
-    float* pp = part + ((qrow * Hq + h) * splits + split) * C::PART;
-#pragma unroll
-    for (int jb = 0; jb < C::NJB; ++jb)
-      *reinterpret_cast<v4f*>(pp + 16 * jb + 4 * grp) = o[jb];
-    if (grp == 0) {
-      pp[D] = m;
-      pp[D + 1] = lsum;
-      pp[D + 2] = lex;
-    }
   }
-}
-
-// Merge the splits of one (row, head) in split order, apply the gate, store.
-template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(
-    int Tq, int Hq, int splits, const float* __restrict__ part,
-    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  using C = AttnCfg<D>;
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.y * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (h >= Hq) return;
-  const int64_t qrow = blockIdx.x;  // b*Tq + row
-  const float* pp = part + (qrow * Hq + h) * splits * C::PART;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pp[s * C::PART + D]);
-  constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float L = 0.f, Lex = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float ms = pp[s * C::PART + D];
-    const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    L += wgt * pp[s * C::PART + D + 1];
-    Lex += wgt * pp[s * C::PART + D + 2];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += wgt * pp[s * C::PART + lane * PER + e];
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const int64_t obase = (qrow * Hq + h) * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    float y = acc[e] * inv;
-    if (gate) y *= sigmoidf(bf16_to_f32(gate[obase + e]));
-    out[obase + e] = f32_to_bf16(y);
-  }
-  if (lse && lane == 0) lse[qrow * Hq + h] = Lex > 0.f ? (M + fast_log2(Lex)) * LN2 : -INFINITY;
 }
 
 int sparse_attn_pick_splits(const Geom& g) {
@@ -269,9 +327,8 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
                      splits, per_split, static_cast<float*>(ws), dflag, dense_block_rows(G));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  const int hpb = g.Hq < 4 ? g.Hq : 4;  // heads (waves) per combine workgroup
-  dim3 cgrid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq), (g.Hq + hpb - 1) / hpb);
-  hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(64 * hpb), 0, st, g.Tq, g.Hq, splits,
+  dim3 cgrid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq), (g.Hq * (D / 4) + 255) / 256);
+  hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(256), 0, st, g.Hq, splits,
                      static_cast<const float*>(ws), gate, out, lse);
   return hipGetLastError();
 }

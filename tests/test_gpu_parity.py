@@ -196,6 +196,27 @@ def test_decode_fused(lci, orc):
     _fused_check(lci, orc, cfg, inp, cfg.K, entry="decode")
 
 
+DECODE_EDGE = {
+    # every score equal: one histogram bin holds the whole history (capacity fallback)
+    "all_equal": (dict(q_range=0), 12000),
+    # scores in a narrow range: many ties inside the threshold bin
+    "heavy_ties": (dict(q_range=1), 30000),
+    # another indexer shape, K larger than some histories
+    "h2d32": (dict(H_I=2, d_I=32, K=300), 9000),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_EDGE))
+def test_decode_fused_edges(lci, orc, name):
+    kw, L = DECODE_EDGE[name]
+    q_range = kw.pop("q_range", None)
+    cfg = MED.replace(B=3, Tq=1, Tk=L, decode=True, K=kw.pop("K", 2048), needles="none", **kw)
+    inp = make(cfg, seed=8, q_range=q_range, kv_len=[L, L - 77, 250],
+               q_offset=[L - 1, L - 78, 249])
+    log(f"decode edge {name}: L={L} K={cfg.K} H_I={cfg.H_I} d_I={cfg.d_I}")
+    _fused_check(lci, orc, cfg, inp, cfg.K, entry="decode")
+
+
 def test_deterministic(lci):
     import torch
     cfg = MED.replace(Tq=256, Tk=256, K=64)
