@@ -137,6 +137,7 @@ lci_status lci_topk_select(const lci_geom *g, const int32_t *scores, int32_t *id
  *            fp32 accumulation, rounded to nearest even; 0 for a row without entries
  *   lse      fp32 [B, Tq, Hq] out, nullable: natural log of the softmax
  *            denominator of scale*q.k (-inf for a row without entries)
+ *   softmax_scale  positive and finite (1/sqrt(d) in the pages), else SHAPE
  *   workspace scratch of at least lci_workspace_bytes(LCI_ENTRY_SPARSE_ATTN)
  * Errors: NULL, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN, HIP. */
 lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_bf16 *k,

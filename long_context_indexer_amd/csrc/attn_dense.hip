@@ -19,17 +19,21 @@
 //                    positions in 0..p, or rows too sparse for tiles).
 //   attn_dense_kernel one workgroup = 4 waves = 4*32 (token, query head) rows of
 //                    one key/value head g; waves own 32/G tokens x G heads.
-//                    Per 64-key tile: K and V tiles go to LDS (register
-//                    prefetch of the next tile overlaps the MFMAs), then
+//                    Per 64-key tile: K and V tiles go to LDS (double
+//                    buffered; the next tile is prefetched into registers
+//                    while this one is computed; one barrier per tile), then
 //                      S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (lane l owns
 //                            query row l%32, keys 8i+4*(l/32)+j of each 32-key half),
-//                      mask + online softmax in base 2, all lane-local except
-//                            one exchange with lane l^32 for the row max,
+//                      mask + online softmax in base 2 (max on raw scores,
+//                            the scale folded into one FMA per exponent, the
+//                            offset moved only when a row's max grows by 2^8),
+//                            all lane-local except one exchange with lane l^32,
 //                      O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, with V^T read
 //                            by ds_read_b64_tr_b16 (each 16-lane group reads a
 //                            4-key x 16-feature block transposed into registers).
 //                    The epilogue applies sigmoid(gate) and stores bf16.
-// Workgroups are placed so that each XCD (its own L2) serves one key/value head
+// K and V tiles use an XOR-swizzled LDS layout that keeps every access pattern
+// free of bank conflicts. Workgroups are placed so that each XCD (its own L2) serves one key/value head
 // (blockIdx.x % 8 picks the XCD), and the longest causal tiles start first.
 #include "attn_dense.h"
 #include "common.h"
@@ -95,12 +99,33 @@ struct DenseCfg {
   static constexpr int TW = 32 / G;   // tokens per wave
   static constexpr int BQ = 4 * TW;   // tokens per workgroup
   static constexpr int BK = 64;       // keys per tile
-  static constexpr int KP = D + 8;    // LDS row pitch (bf16): 16-byte aligned rows
+  static constexpr int KP = D;        // LDS row pitch (bf16); 16-byte units are XOR-swizzled
   static constexpr int NKK = D / 16;  // 16-deep MFMA steps over d for S^T
   static constexpr int NDT = D / 32;  // 32-wide d tiles of O^T
   static constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
   static constexpr int LPT = BK * CPR / 256;  // 16-byte loads per thread per tile (K and V each)
 };
+
+// Bank-conflict-free placement of the 16-byte unit u of tile row r: unit
+// u ^ swz(r). With this, the 16-row key reads (ds_read_b128, one unit of 16
+// consecutive rows), the transposed value reads (4 consecutive rows x 4 units
+// per 32-lane phase) and the row stores all touch 16 distinct 16-byte bank
+// groups of the 64-bank LDS.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+// element offset of (row, col) in a swizzled tile
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+// Rows whose running max grows by less than this (log2 units) keep their
+// softmax offset: P stays <= 2^8, far from overflow, and the O and l rescale
+// is skipped for the whole wave unless some row needs it.
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
@@ -111,8 +136,9 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     const uint8_t* __restrict__ flag, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nbps, int nblk) {
   using C = DenseCfg<D, G>;
-  __shared__ __align__(16) uint16_t ks[C::BK * C::KP];
-  __shared__ __align__(16) uint16_t vsh[C::BK * C::KP];
+  // two K/V tile buffers: the tile for step kb+1 is written while step kb is read
+  __shared__ __align__(16) uint16_t ks[2][C::BK * C::KP];
+  __shared__ __align__(16) uint16_t vsh[2][C::BK * C::KP];
 
   // XCD-aware placement: XCD x = blockIdx.x % 8 serves key/value head x / (8/Hkv)
   const int per = 8 / Hkv;
@@ -147,6 +173,11 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   const int p = qo + i;
   const int fl = rv ? flag[qrow] : 0;
   const uint32_t* mrow = mask + qrow * Wm;
+  // every row of this wave keeps all of 0..p (flag 2): tiles entirely at or
+  // below the wave's first position need no mask at all
+  const int iw0 = i0 + wv * C::TW;
+  const int p_wave_min = qo + iw0;
+  const bool wave_all = __all(!rv || fl == 2) && iw0 < Tq;
 
   // Q^T as the B operand: lane holds Q[row][16*kk + 8*hf .. +7]
   v8bf qf[C::NKK];
@@ -164,7 +195,8 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   const uint16_t* kbase = k + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
   const uint16_t* vbase = v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
 
-  // register prefetch of one K/V tile: thread t loads chunks t + 256*c
+  // register prefetch of one K/V tile: thread t loads chunks t + 256*c; rows
+  // past the history are clamped to row 0 (finite values, masked out later)
   v4i pk[C::LPT], pv[C::LPT];
   auto prefetch = [&](int kb) {
 #pragma unroll
@@ -172,27 +204,28 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
       const int chunk = c * 256 + static_cast<int>(threadIdx.x);
       const int row = chunk / C::CPR;
       const int col = chunk % C::CPR;
-      const int key = kb * C::BK + row;
-      v4i z = {0, 0, 0, 0};
-      const bool in = key < kvl;
-      pk[c] = in ? *reinterpret_cast<const v4i*>(kbase + key * rowstep + 8 * col) : z;
-      pv[c] = in ? *reinterpret_cast<const v4i*>(vbase + key * rowstep + 8 * col) : z;
+      int key = kb * C::BK + row;
+      key = key < kvl ? key : 0;
+      pk[c] = *reinterpret_cast<const v4i*>(kbase + key * rowstep + 8 * col);
+      pv[c] = *reinterpret_cast<const v4i*>(vbase + key * rowstep + 8 * col);
     }
   };
-  LDS_AS uint16_t* ksl = (LDS_AS uint16_t*)(ks);
-  LDS_AS uint16_t* vsl = (LDS_AS uint16_t*)(vsh);
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
+    LDS_AS uint16_t* ksl = (LDS_AS uint16_t*)(ks[buf]);
+    LDS_AS uint16_t* vsl = (LDS_AS uint16_t*)(vsh[buf]);
 #pragma unroll
     for (int c = 0; c < C::LPT; ++c) {
       const int chunk = c * 256 + static_cast<int>(threadIdx.x);
       const int row = chunk / C::CPR;
       const int col = chunk % C::CPR;
-      *(LDS_AS v4i*)(ksl + row * C::KP + 8 * col) = pk[c];
-      *(LDS_AS v4i*)(vsl + row * C::KP + 8 * col) = pv[c];
+      const int off = row * C::KP + ((col ^ swz<D>(row)) << 3);
+      *(LDS_AS v4i*)(ksl + off) = pk[c];
+      *(LDS_AS v4i*)(vsl + off) = pv[c];
     }
   };
 
-  float m = -INFINITY, lsum = 0.f, lex = 0.f;
+  float m = -INFINITY;  // softmax offset of this row, raw score units (a running max)
+  float lsum = 0.f;     // this lane's share of the softmax denominator
   v16f o[C::NDT];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)
@@ -200,11 +233,14 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
 
   prefetch(0);
+  stage(0);
+  __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // previous tile fully consumed
-    stage();
-    __syncthreads();
+    const int buf = kb & 1;
     if (kb + 1 < nkb) prefetch(kb + 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next tile's loads ahead of the MFMAs
+    const LDS_AS uint16_t* ksl = (const LDS_AS uint16_t*)(ks[buf]);
+    LDS_AS uint16_t* vsl = (LDS_AS uint16_t*)(vsh[buf]);
 
     // S^T for two 32-key halves
     v16f st[2];
@@ -212,83 +248,94 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
-      const LDS_AS uint16_t* ka = ksl + (32 * kt + r) * C::KP + 8 * hf;
+      const int krow = 32 * kt + r;
 #pragma unroll
       for (int kk = 0; kk < C::NKK; ++kk) {
-        const v8bf a = __builtin_bit_cast(v8bf, *(const LDS_AS v4i*)(ka + 16 * kk));
+        const v8bf a = __builtin_bit_cast(
+            v8bf, *(const LDS_AS v4i*)(ksl + tile_off<D>(krow, 16 * kk + 8 * hf)));
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st[kt], 0, 0, 0);
       }
     }
-    // selection bits of this lane's row for the two halves
-    uint32_t mw[2];
+    // mask (selection bits, or causal for rows that keep everything)
+    const int key0 = kb * C::BK;
+    if (!(wave_all && key0 + C::BK - 1 <= p_wave_min)) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key0 = kb * C::BK + 32 * kt;
-      if (fl == 2) {
-        const int n = p - key0 + 1;  // keys key0..p are kept
-        mw[kt] = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
-      } else if (fl == 1) {
-        const int wi = 2 * kb + kt;
-        mw[kt] = wi < Wm ? mrow[wi] : 0u;
-      } else {
-        mw[kt] = 0u;
+      for (int kt = 0; kt < 2; ++kt) {
+        uint32_t mw;
+        if (fl == 2) {
+          const int n = p - (key0 + 32 * kt) + 1;  // keys key0+32kt .. p are kept
+          mw = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
+        } else if (fl == 1) {
+          const int wi = 2 * kb + kt;
+          mw = wi < Wm ? mrow[wi] : 0u;
+        } else {
+          mw = 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kofs = 8 * (e >> 2) + 4 * hf + (e & 3);
+          st[kt][e] = ((mw >> kofs) & 1u) ? st[kt][e] : -INFINITY;
+        }
       }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kofs = 8 * (e >> 2) + 4 * hf + (e & 3);
-        const bool keep = (mw[kt] >> kofs) & 1u;
-        const float x = keep ? st[kt][e] * scale_log2 : -INFINITY;
-        st[kt][e] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(st[kt][e], st[kt][e + 1]));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
-    m = m_new;
+    // lazy offset update: only rows whose max grew by kRescaleLog2 or more move
+    // their offset (all rows start at -inf, so every row moves on its first
+    // kept score); the rescale of O and l runs only if some row of the wave moved
+    const bool grow = mx * scale_log2 > m * scale_log2 + kRescaleLog2;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m;
+      // a row with nothing kept yet has O = l = 0: alpha = 2^-inf = 0, never 0*inf
+      const float moff_new = (m_new == -INFINITY) ? 0.f : m_new * scale_log2;
+      const float alpha = fast_exp2(m * scale_log2 - moff_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+    }
+    // a row with nothing kept so far has m = -inf: offset 0 (every p is 0)
+    const float moff = (m == -INFINITY) ? 0.f : m * scale_log2;
     // P^T as the B operand of the PV step s: e<4 -> half-row i=2(s%2), e>=4 -> i=2(s%2)+1
     v8bf pb[4];
-    float psum = 0.f, pex = 0.f;
+    float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float x = st[kt][e];
-        const float pe = (x == -INFINITY) ? 0.f : fast_exp2(x - m_new);
-        const __bf16 hb = static_cast<__bf16>(pe);
-        pex += pe;
-        psum += static_cast<float>(hb);
-        const int s = 2 * kt + (e >> 3);
-        pb[s][e & 7] = hb;
+        const float pe = fast_exp2(__builtin_fmaf(st[kt][e], scale_log2, -moff));
+        psum += pe;
+        pb[2 * kt + (e >> 3)][e & 7] = static_cast<__bf16>(pe);
       }
-    lsum = lsum * alpha + psum;
-    lex = lex * alpha + pex;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+    lsum += psum;
 
     // O^T += V^T P^T over the 64 keys, four 16-key steps
     const int gi = lane & 15;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt) {
         const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
-        const int k0 = 16 * s + 4 * hf;
-        LDS_AS v4bf* a0 = (LDS_AS v4bf*)(vsl + (k0 + gi / 4) * C::KP + d0 + 4 * (gi % 4));
-        LDS_AS v4bf* a1 = (LDS_AS v4bf*)(vsl + (k0 + 8 + gi / 4) * C::KP + d0 + 4 * (gi % 4));
+        const int k0 = 16 * s2 + 4 * hf;
+        LDS_AS v4bf* a0 = (LDS_AS v4bf*)(vsl + tile_off<D>(k0 + gi / 4, d0 + 4 * (gi % 4)));
+        LDS_AS v4bf* a1 = (LDS_AS v4bf*)(vsl + tile_off<D>(k0 + 8 + gi / 4, d0 + 4 * (gi % 4)));
         const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0);
         const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1);
         const v8bf a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], o[dt], 0, 0, 0);
       }
     }
+    // the prefetched tile goes to the other buffer; one barrier per step makes
+    // it visible and guarantees nobody still reads the buffer written next
+    if (kb + 1 < nkb) stage(buf ^ 1);
+    __syncthreads();
   }
 
   lsum += shfl_xor(lsum, 32);
-  lex += shfl_xor(lex, 32);
   if (!rv || fl == 0) return;
   const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
   const int64_t obase = (qrow * Hq + h) * D;
@@ -311,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
                           (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * ii + 3] * inv * gv[3])) << 16);
       *reinterpret_cast<int2*>(out + obase + d) = make_int2(static_cast<int>(w0), static_cast<int>(w1));
     }
-  if (lse && hf == 0) lse[qrow * Hq + h] = lex > 0.f ? (m + fast_log2(lex)) * LN2 : -INFINITY;
+  if (lse && hf == 0) lse[qrow * Hq + h] = lsum > 0.f ? (m * scale_log2 + fast_log2(lsum)) * LN2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- host side

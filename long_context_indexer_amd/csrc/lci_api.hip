@@ -52,6 +52,10 @@ lci_status check_attention(const lci_geom* g) {
   return LCI_OK;
 }
 
+// The kernels track running maxima of the raw dot products, which are the
+// maxima of scale*q.k only for a positive scale.
+bool scale_ok(float scale) { return scale > 0.f && scale < INFINITY; }
+
 Geom to_geom(const lci_geom* g) {
   return Geom{g->B, g->Tq, g->Tk, g->Hq, g->Hkv, g->d, g->H_I, g->d_I, g->K, g->q_offset,
               g->kv_len};
@@ -172,6 +176,7 @@ lci_status lci_sparse_attn_fwd(const lci_geom* g, const lci_bf16* q, const lci_b
   if (s != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
   if (!q || !k || !v || !idx || !out) return LCI_ERR_NULL;
+  if (!scale_ok(softmax_scale)) return LCI_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       (gate && !aligned16(gate)) || !aligned4(idx) || (lse && !aligned4(lse)))
     return LCI_ERR_ALIGN;
@@ -195,7 +200,7 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   if ((s = check_indexer(g)) != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
   if (!q_idx || !k_idx || !w || !q || !k || !v || !out) return LCI_ERR_NULL;
-  if (wsb < 0 || wsq < 0) return LCI_ERR_SHAPE;
+  if (wsb < 0 || wsq < 0 || !scale_ok(scale)) return LCI_ERR_SHAPE;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(k) ||
       !aligned16(v) || !aligned16(out) || (gate && !aligned16(gate)) ||
       (lse && !aligned4(lse)) || (idx_out && !aligned4(idx_out)))

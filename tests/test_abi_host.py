@@ -63,18 +63,19 @@ def score(lib, g, q=FAKE, k=FAKE, w=FAKE, out=FAKE, wsb=0, wsq=0):
                              None)
 
 
-def attn(lib, g, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, gate=None, out=FAKE, ws=None, nb=0):
-    return lib.lci_sparse_attn_fwd(ctypes.byref(g), q, k, v, idx, gate, 0.1, out, None, ws, nb,
+def attn(lib, g, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, gate=None, out=FAKE, ws=None, nb=0,
+         scale=0.1):
+    return lib.lci_sparse_attn_fwd(ctypes.byref(g), q, k, v, idx, gate, scale, out, None, ws, nb,
                                    None)
 
 
-def fused(lib, g, fn="lci_prefill_fwd", ws=FAKE, nb=None, **ptrs):
+def fused(lib, g, fn="lci_prefill_fwd", ws=FAKE, nb=None, scale=0.1, **ptrs):
     p = dict(qi=FAKE, ki=FAKE, w=FAKE, q=FAKE, k=FAKE, v=FAKE, out=FAKE)
     p.update(ptrs)
     if nb is None:
         nb = lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g))
     return getattr(lib, fn)(ctypes.byref(g), p["qi"], p["ki"], p["w"], 0, 0, p["q"], p["k"], p["v"],
-                            None, 0.1, p["out"], None, None, ws, nb, None)
+                            None, scale, p["out"], None, None, ws, nb, None)
 
 
 def test_null_arguments(lib):
@@ -110,6 +111,13 @@ def test_attention_limits(lib):
     assert attn(lib, geom(Hq=48, Hkv=16)) == UNSUP           # Hkv > 8
     assert attn(lib, geom(Hq=64, Hkv=2)) == UNSUP            # group of 32 query heads
     assert attn(lib, geom(Hq=6, Hkv=2)) == UNSUP             # group of 3
+
+
+def test_softmax_scale_must_be_positive(lib):
+    # running maxima are taken on raw dot products: only a positive scale keeps them maxima
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert attn(lib, geom(), scale=bad) == SHAPE
+        assert fused(lib, geom(), scale=bad) == SHAPE
 
 
 def test_alignment(lib):
