@@ -102,8 +102,6 @@ struct DenseCfg {
   static constexpr int KP = D;        // LDS row pitch (bf16); 16-byte units are XOR-swizzled
   static constexpr int NKK = D / 16;  // 16-deep MFMA steps over d for S^T
   static constexpr int NDT = D / 32;  // 32-wide d tiles of O^T
-  static constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
-  static constexpr int LPT = BK * CPR / 256;  // 16-byte loads per thread per tile (K and V each)
 };
 
 // Bank-conflict-free placement of the 16-byte unit u of tile row r: unit
@@ -122,6 +120,30 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
 }
 
+// dword 3 of a raw buffer resource on gfx9-class parts: 32-bit data format
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kNegInfBits = static_cast<int>(0xff800000u);
+
+// A workgroup-uniform pointer, moved to scalar registers (buffer resources must
+// live there; without this the compiler may loop over lanes to build them).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// dst + 16 l (dst is wave-uniform); offsets outside the buffer read as zero.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rs, LDS_AS void* dst,
+                                              int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 // Rows whose running max grows by less than this (log2 units) keep their
 // softmax offset: P stays <= 2^8, far from overflow, and the O and l rescale
 // is skipped for the whole wave unless some row needs it.
@@ -136,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     const uint8_t* __restrict__ flag, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nbps, int nblk) {
   using C = DenseCfg<D, G>;
-  // two K/V tile buffers: the tile for step kb+1 is written while step kb is read
+  // two K and two V tile buffers (see the pipeline below)
   __shared__ __align__(16) uint16_t ks[2][C::BK * C::KP];
   __shared__ __align__(16) uint16_t vsh[2][C::BK * C::KP];
 
@@ -191,59 +213,42 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     }
   }
 
-  const int64_t rowstep = static_cast<int64_t>(Hkv) * D;
+  // K/V tiles go from HBM straight into LDS (buffer_load ... lds: lane l of a
+  // wave writes 16 bytes at the instruction's LDS base + 16 l). Wave wv's c-th
+  // load fills LDS bytes [1024 (4c + wv), +1024) of the tile, i.e. RPI whole
+  // rows; each lane fetches the logical 16-byte unit that the XOR swizzle puts
+  // at its physical slot. The buffer resource starts at the tile's first key and
+  // ends at the last valid one: keys past kv_len read as zero (finite, masked).
+  constexpr int UPR = D / 8;             // 16-byte units per row
+  constexpr int RPI = 64 / UPR;          // rows per wave load
+  constexpr int NI = C::BK * UPR / 256;  // loads per wave per tile (K and V each)
+  const int rowstep = Hkv * D;           // elements between consecutive keys
   const uint16_t* kbase = k + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
   const uint16_t* vbase = v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
-
-  // register prefetch of one K/V tile: thread t loads chunks t + 256*c; rows
-  // past the history are clamped to row 0 (finite values, masked out later)
-  v4i pk[C::LPT], pv[C::LPT];
-  auto prefetch = [&](int kb) {
+  int voff[NI];
 #pragma unroll
-    for (int c = 0; c < C::LPT; ++c) {
-      const int chunk = c * 256 + static_cast<int>(threadIdx.x);
-      const int row = chunk / C::CPR;
-      const int col = chunk % C::CPR;
-      int key = kb * C::BK + row;
-      key = key < kvl ? key : 0;
-      pk[c] = *reinterpret_cast<const v4i*>(kbase + key * rowstep + 8 * col);
-      pv[c] = *reinterpret_cast<const v4i*>(vbase + key * rowstep + 8 * col);
-    }
+  for (int c = 0; c < NI; ++c) {
+    const int row = (4 * c + wv) * RPI + lane / UPR;
+    const int lu = (lane % UPR) ^ swz<D>(row);
+    voff[c] = (row * rowstep + 8 * lu) * 2;
+  }
+  auto tile_rsrc = [&](const uint16_t* base, int kb) {
+    const int key0 = kb * C::BK;
+    const int nvalid = max(0, min(kvl - key0, C::BK));
+    const int nbytes = __builtin_amdgcn_readfirstlane(nvalid * rowstep * 2);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(base + static_cast<int64_t>(key0) * rowstep), 0, nbytes, kBufferFlags);
   };
-  auto stage = [&](int buf) {
-    LDS_AS uint16_t* ksl = (LDS_AS uint16_t*)(ks[buf]);
-    LDS_AS uint16_t* vsl = (LDS_AS uint16_t*)(vsh[buf]);
+  auto load_tile = [&](const uint16_t* base, int kb, uint16_t* dst) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base, kb);
 #pragma unroll
-    for (int c = 0; c < C::LPT; ++c) {
-      const int chunk = c * 256 + static_cast<int>(threadIdx.x);
-      const int row = chunk / C::CPR;
-      const int col = chunk % C::CPR;
-      const int off = row * C::KP + ((col ^ swz<D>(row)) << 3);
-      *(LDS_AS v4i*)(ksl + off) = pk[c];
-      *(LDS_AS v4i*)(vsl + off) = pv[c];
-    }
+    for (int c = 0; c < NI; ++c)
+      load16_to_lds(rs, (LDS_AS uint16_t*)dst + (4 * c + wv) * 512, voff[c]);
   };
 
-  float m = -INFINITY;  // softmax offset of this row, raw score units (a running max)
-  float lsum = 0.f;     // this lane's share of the softmax denominator
-  v16f o[C::NDT];
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-
-  prefetch(0);
-  stage(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) prefetch(kb + 1);
-    __builtin_amdgcn_sched_barrier(0);  // keep the next tile's loads ahead of the MFMAs
-    const LDS_AS uint16_t* ksl = (const LDS_AS uint16_t*)(ks[buf]);
-    LDS_AS uint16_t* vsl = (LDS_AS uint16_t*)(vsh[buf]);
-
-    // S^T for two 32-key halves
-    v16f st[2];
+  // S^T of one 64-key tile (two 32-key halves) from the K tile in LDS
+  auto tile_scores = [&](const uint16_t* kt_lds, v16f* st) {
+    const LDS_AS uint16_t* ksl = (const LDS_AS uint16_t*)kt_lds;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -256,34 +261,72 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st[kt], 0, 0, 0);
       }
     }
+  };
+
+  // selection words of the next tile, loaded one tile ahead (rows not on the
+  // mask path read a valid but unused word)
+  const int wlast = Wm - 1;
+  auto mask_words = [&](int kb, uint32_t* w) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint32_t x = mrow[min(2 * kb + kt, wlast)];
+      w[kt] = 2 * kb + kt <= wlast ? x : 0u;  // past the mask row: nothing kept
+    }
+  };
+
+  float m = -INFINITY;  // softmax offset of this row, raw score units (a running max)
+  float lsum = 0.f;     // this lane's share of the softmax denominator
+  v16f o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+
+  // pipeline: while tile kb is in softmax, the scores of tile kb+1 are computed
+  // (their K is already in LDS) and V of kb+1 and K of kb+2 are in flight
+  load_tile(kbase, 0, ks[0]);
+  load_tile(vbase, 0, vsh[0]);
+  if (nkb > 1) load_tile(kbase, 1, ks[1]);
+  uint32_t mwc[2];
+  mask_words(0, mwc);
+  __syncthreads();
+  v16f sc[2];
+  tile_scores(ks[0], sc);
+  __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nkb) load_tile(vbase, kb + 1, vsh[buf ^ 1]);
+    if (kb + 2 < nkb) load_tile(kbase, kb + 2, ks[buf]);
+    uint32_t mwn[2];
+    mask_words(kb + 1, mwn);
+
     // mask (selection bits, or causal for rows that keep everything)
     const int key0 = kb * C::BK;
     if (!(wave_all && key0 + C::BK - 1 <= p_wave_min)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        uint32_t mw;
-        if (fl == 2) {
-          const int n = p - (key0 + 32 * kt) + 1;  // keys key0+32kt .. p are kept
-          mw = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
-        } else if (fl == 1) {
-          const int wi = 2 * kb + kt;
-          mw = wi < Wm ? mrow[wi] : 0u;
-        } else {
-          mw = 0u;
-        }
+        const int n = p - (key0 + 32 * kt) + 1;  // flag 2: keys key0+32kt .. p are kept
+        const uint32_t causal = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
+        uint32_t mw = fl == 2 ? causal : (fl == 1 ? mwc[kt] : 0u);
+        // bit kofs(e) = 8(e/4) + 4hf + e%4 of mw keeps element e: a one-bit
+        // signed extract gives an all-ones/all-zeros select mask
+        mw >>= 4 * hf;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int kofs = 8 * (e >> 2) + 4 * hf + (e & 3);
-          st[kt][e] = ((mw >> kofs) & 1u) ? st[kt][e] : -INFINITY;
+          const int sel = __builtin_amdgcn_sbfe(static_cast<int>(mw), 8 * (e >> 2) + (e & 3), 1);
+          const int sb = __float_as_int(sc[kt][e]);
+          sc[kt][e] = __int_as_float((sb & sel) | (~sel & kNegInfBits));
         }
       }
     }
+    // scores are finite or -inf: IEEE maximum (no NaN quieting) folds into v_maximum3
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(st[kt][e], st[kt][e + 1]));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+      for (int e = 0; e < 16; e += 2) mx = max3f(mx, sc[kt][e], sc[kt][e + 1]);
+    mx = __builtin_elementwise_maximum(mx, shfl_xor(mx, 32));
     // lazy offset update: only rows whose max grew by kRescaleLog2 or more move
     // their offset (all rows start at -inf, so every row moves on its first
     // kept score); the rescale of O and l runs only if some row of the wave moved
@@ -300,6 +343,12 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     }
     // a row with nothing kept so far has m = -inf: offset 0 (every p is 0)
     const float moff = (m == -INFINITY) ? 0.f : m * scale_log2;
+
+    // scores of the next tile (independent MFMA work beside the exponentials;
+    // past the last tile the result is unused)
+    v16f sn[2];
+    tile_scores(ks[buf ^ 1], sn);
+
     // P^T as the B operand of the PV step s: e<4 -> half-row i=2(s%2), e>=4 -> i=2(s%2)+1
     v8bf pb[4];
     float psum = 0.f;
@@ -307,13 +356,14 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(__builtin_fmaf(st[kt][e], scale_log2, -moff));
+        const float pe = fast_exp2(__builtin_fmaf(sc[kt][e], scale_log2, -moff));
         psum += pe;
         pb[2 * kt + (e >> 3)][e & 7] = static_cast<__bf16>(pe);
       }
     lsum += psum;
 
     // O^T += V^T P^T over the 64 keys, four 16-key steps
+    const LDS_AS uint16_t* vsl = (const LDS_AS uint16_t*)(vsh[buf]);
     const int gi = lane & 15;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
@@ -329,9 +379,13 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], o[dt], 0, 0, 0);
       }
     }
-    // the prefetched tile goes to the other buffer; one barrier per step makes
-    // it visible and guarantees nobody still reads the buffer written next
-    if (kb + 1 < nkb) stage(buf ^ 1);
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+    mwc[0] = mwn[0];
+    mwc[1] = mwn[1];
+    // the barrier waits for this step's tile loads (vmcnt) and makes them
+    // visible; it also guarantees every wave is done with the buffers the
+    // next step's loads overwrite
     __syncthreads();
   }
 
