@@ -30,6 +30,39 @@ PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+# HBM traffic of the dominant kernel from rocprofv3 counter passes (one pass
+# for FETCH_SIZE, one for WRITE_SIZE, KiB per dispatch, Prefill-8K step), each
+# scaled by what the same counter reads for a plain 2 GiB device copy kernel
+# (FETCH_SIZE reads 1 GiB for its 2 GiB of reads: x2.0; WRITE_SIZE reads
+# 2 GiB for its 2 GiB of writes: x1.0). Valid only for the kernel sources the
+# counters were taken on: any change to them turns the figure into null.
+TRAFFIC = {
+    "attn_dense": dict(fetch_kib=131944.1, fetch_scale=2.0, write_kib=115312.1, write_scale=1.0,
+                       sources=("long_context_indexer_amd/csrc/attn_dense.hip",
+                                "long_context_indexer_amd/csrc/attn_dense.h",
+                                "long_context_indexer_amd/csrc/common.h"),
+                       sha256="12838301b9b6f8addb90df84dc6fcb3dfd2864153497d6536ac76439d7cb2f2d"),
+}
+
+
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(kernel):
+    """HBM bytes per launch from the recorded counters, or None when the kernel's
+    sources changed since they were taken (or none were taken)."""
+    t = TRAFFIC.get(kernel)
+    if t is None or sources_sha256(t["sources"]) != t["sha256"]:
+        return None
+    return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -86,6 +119,61 @@ class Timer:
         e.record(self.stream)
         e.synchronize()
         return s.elapsed_time(e) / iters
+
+
+def timed_region(timer, step, steps, lci):
+    """Time `steps` steps (wall clock and stream events around the whole region),
+    then run `steps` more with the library's per-kernel event log switched on
+    (events around every launch, on the launch stream). The log's events add a
+    few microseconds per launch, so the headline step time comes from the first
+    region and only the per-kernel durations from the second."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev_ms = timer.time(step, steps)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    lci.kernel_timing(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern = {}
+    for name in lci.KERNELS:
+        tot, n = lci.kernel_timing_read(name)
+        if n:
+            kern[name] = dict(launches_per_step=n / steps, ms_per_step=tot / steps,
+                              avg_launch_ms=tot / n)
+    lci.kernel_timing(False)
+    return wall_ms, ev_ms, kern
+
+
+def roofline(cfg, kern):
+    """Roofline of the kernel that takes the most time per prefill step.
+    achieved = the algorithmic work that kernel does per step / its summed launch
+    durations per step (its event-timed average launch time x launches/step)."""
+    dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
+    ms = kern[dom]["ms_per_step"]
+    if dom in ("attn_dense", "attn_gather"):
+        # every Prefill-8K row keeps at least a quarter of its history, so all rows
+        # take the dense-tile kernel: its work is the whole layer's attention
+        ach = attn_flops(cfg) / ms / 1e9
+        r = dict(kernel=dom, bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS,
+                 unit="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS, traffic=None)
+    elif dom == "idx_score":
+        ach = idx_ops(cfg) / ms / 1e9
+        r = dict(kernel=dom, bound="mfma", achieved=ach, peak=PEAK_INT8_TOPS, unit="TOP/s",
+                 frac=ach / PEAK_INT8_TOPS, traffic=None)
+    else:
+        nbytes = 4.0 * scored_pairs(cfg) + 4.0 * cfg.B * cfg.Tq * cfg.K
+        ach = nbytes / ms / 1e6
+        r = dict(kernel=dom, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                 frac=ach / PEAK_HBM_GBS, traffic=None)
+    r["traffic"] = traffic_bytes(dom)
+    r.update(traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                          "copy-calibrated)",
+             launches_per_step=kern[dom]["launches_per_step"],
+             avg_launch_ms=kern[dom]["avg_launch_ms"])
+    return r
 
 
 def cpu_baseline(cfg, inp_host, budget_s):
@@ -157,44 +245,15 @@ def main():
         for _ in range(args.warmup):
             prefill_step()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev_ms = timer.time(prefill_step, args.steps)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms_step = wall * 1e3 / args.steps
-        tok_s = cfg.B * cfg.Tq * args.steps / wall
-        res["prefill"] = dict(ms_per_step=ms_step, event_ms_per_step=ev_ms, tok_s=tok_s)
+        ms_step, ev_ms, kern = timed_region(timer, prefill_step, args.steps, lci)
+        tok_s = cfg.B * cfg.Tq / (ms_step * 1e-3)
+        res["prefill"] = dict(ms_per_step=ms_step, event_ms_per_step=ev_ms, tok_s=tok_s,
+                              kernels=kern)
         log(f"prefill8k fused: {ms_step:.3f} ms/step ({ev_ms:.3f} ms by events), "
             f"{tok_s / 1e6:.2f} M tok/s")
-
-        # per-stage breakdown through the unfused entries (the same kernels), every
-        # buffer preallocated so the events time GPU work, not host allocation
-        scores = torch.empty((cfg.B, cfg.Tq, cfg.Tk), dtype=torch.int32, device="cuda")
-        idx = torch.empty((cfg.B, cfg.Tq, cfg.K), dtype=torch.int32, device="cuda")
-        ws_attn = torch.empty(max(1, lci.workspace_bytes(lci.ENTRY_SPARSE_ATTN, geom)),
-                              dtype=torch.uint8, device="cuda")
-        it = max(5, args.steps)
-        st_ms = timer.time(lambda: lci.idx_score(d["q_idx"], d["k_idx"], d["w"], d["q_offset"],
-                                                 d["kv_len"], scores=scores, stream=stream), it)
-        tk_ms = timer.time(lambda: lci.topk_select(scores, cfg.K, d["q_offset"], d["kv_len"],
-                                                   idx=idx, stream=stream), it)
-        at_ms = timer.time(lambda: lci.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, d["gate"],
-                                                       cfg.scale, d["kv_len"],
-                                                       q_offset=d["q_offset"], out=out,
-                                                       workspace=ws_attn, stream=stream), it)
-        del scores
-        flops = attn_flops(cfg)
-        iops = idx_ops(cfg)
-        stages = {
-            "idx_score": dict(ms=st_ms, tops=iops / st_ms / 1e9,
-                              frac_int8_peak=iops / st_ms / 1e9 / PEAK_INT8_TOPS),
-            "topk_select": dict(ms=tk_ms),
-            "sparse_attn": dict(ms=at_ms, tflops=flops / at_ms / 1e9,
-                                frac_bf16_peak=flops / at_ms / 1e9 / PEAK_BF16_TFLOPS),
-        }
-        res["prefill"]["stages"] = stages
-        log(f"  idx_score {st_ms:.3f} ms ({iops / st_ms / 1e9:.1f} TOPS), topk {tk_ms:.3f} ms, "
-            f"sparse_attn {at_ms:.3f} ms ({flops / at_ms / 1e9:.1f} TFLOP/s)")
+        for name, kv in kern.items():
+            log(f"  {name:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
+                f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
 
     # --------------------------------------------------------------- decode 128K
     if not args.no_decode and args.only in (None, "decode"):
@@ -215,30 +274,24 @@ def main():
         for _ in range(args.warmup):
             decode_step()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        dev_ms = timer.time(decode_step, args.steps)
-        torch.cuda.synchronize()
-        dwall = time.perf_counter() - t0
-        dms = dwall * 1e3 / args.steps
-        qps = dcfg.B * args.steps / dwall
-        dws_attn = torch.empty(max(1, lci.workspace_bytes(lci.ENTRY_SPARSE_ATTN, dgeom)),
-                               dtype=torch.uint8, device="cuda")
-        a_ms = timer.time(lambda: lci.sparse_attn_fwd(dd["q"], dd["k"], dd["v"], didx, dd["gate"],
-                                                      dcfg.scale, dd["kv_len"],
-                                                      q_offset=dd["q_offset"], out=dout,
-                                                      workspace=dws_attn, stream=stream),
-                          max(5, args.steps))
+        dms, dev_ms, dkern = timed_region(timer, decode_step, args.steps, lci)
+        qps = dcfg.B / (dms * 1e-3)
         abytes = decode_attn_bytes(dcfg)
         sbytes = decode_step_bytes(dcfg)
+        a_ms = sum(dkern[k]["ms_per_step"] for k in ("attn_gather", "attn_combine") if k in dkern)
         res["decode"] = dict(workload="decode128k", ms_per_step=dms, event_ms_per_step=dev_ms,
                              queries_s=qps,
                              step_hbm_gbs=sbytes / dms / 1e6,
                              step_frac_hbm=sbytes / dms / 1e6 / PEAK_HBM_GBS,
                              sparse_attn_ms=a_ms, sparse_attn_gbs=abytes / a_ms / 1e6,
-                             sparse_attn_frac_hbm=abytes / a_ms / 1e6 / PEAK_HBM_GBS)
+                             sparse_attn_frac_hbm=abytes / a_ms / 1e6 / PEAK_HBM_GBS,
+                             kernels=dkern)
         log(f"decode128k fused: {dms:.3f} ms/step, {qps:.0f} queries/s, whole step "
-            f"{sbytes / dms / 1e6:.0f} GB/s; sparse_attn {a_ms:.3f} ms = "
+            f"{sbytes / dms / 1e6:.0f} GB/s; attention kernels {a_ms * 1e3:.1f} us = "
             f"{abytes / a_ms / 1e6:.0f} GB/s")
+        for name, kv in dkern.items():
+            log(f"  {name:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
+                f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
 
     if args.only is not None:
         print(json.dumps(res))
@@ -246,23 +299,7 @@ def main():
 
     # ------------------------------------------------------------------ report
     pre = res["prefill"]
-    stages = pre["stages"]
-    dom = max(stages, key=lambda k: stages[k]["ms"])
-    if dom == "sparse_attn":
-        ach = attn_flops(cfg) / stages[dom]["ms"] / 1e9
-        roof = dict(kernel="sparse_attn_kernel<128>", bound="mfma", achieved=ach,
-                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS,
-                    traffic=None, ms=stages[dom]["ms"])
-    elif dom == "idx_score":
-        ach = idx_ops(cfg) / stages[dom]["ms"] / 1e9
-        roof = dict(kernel="idx_score_kernel<8,64,4>", bound="mfma", achieved=ach,
-                    peak=PEAK_INT8_TOPS, unit="TOP/s", frac=ach / PEAK_INT8_TOPS, traffic=None,
-                    ms=stages[dom]["ms"])
-    else:
-        nbytes = 4.0 * scored_pairs(cfg)
-        ach = nbytes / stages[dom]["ms"] / 1e6
-        roof = dict(kernel="topk_rows_kernel", bound="hbm", achieved=ach, peak=PEAK_HBM_GBS,
-                    unit="GB/s", frac=ach / PEAK_HBM_GBS, traffic=None, ms=stages[dom]["ms"])
+    roof = roofline(cfg, pre["kernels"])
 
     cpu = None
     if not args.no_cpu:
@@ -288,7 +325,8 @@ def main():
                    "Hkv": cfg.Hkv, "head_dim": cfg.d, "H_I": cfg.H_I, "d_I": cfg.d_I,
                    "top_k": cfg.K, "parallelism": "none (1 GPU)"},
         "roofline": roof,
-        "stages_ms": {k: v["ms"] for k, v in stages.items()},
+        "kernels_us_per_step": {k: round(v["ms_per_step"] * 1e3, 2)
+                                for k, v in pre["kernels"].items()},
         "cpu_baseline": cpu,
     }
     if "decode" in res:

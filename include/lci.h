@@ -21,7 +21,7 @@
  *     enqueues kernels on `stream` (a hipStream_t passed as void*; NULL is the
  *     default stream) and returns. There is no host synchronisation, no device
  *     memory allocation and no global mutable state except the per-thread last
- *     HIP error. Calls are reentrant; calls that share output or workspace
+ *     HIP error (and the kernel timing log, while timing is switched on). Calls are reentrant; calls that share output or workspace
  *     buffers must be ordered by the caller.
  *   - An invalid argument returns an error code synchronously and enqueues
  *     nothing. The contents of device arrays (q_offset, kv_len, idx) cannot be
@@ -186,6 +186,38 @@ int lci_last_hip_error(void);
 
 /* LCI_ABI_VERSION of the loaded library. */
 int lci_abi_version(void);
+
+/* Kernel timing (instrumentation for profiling and roofline reports; not part
+ * of the computation). While switched on, every kernel the library launches is
+ * bracketed by two HIP events recorded on its launch stream, and the pairs are
+ * kept in a process-wide log (the one piece of global mutable state besides the
+ * per-thread last HIP error; it is guarded by a mutex). Off by default.
+ *   lci_kernel_timing(1) clears the log and switches timing on; (0) switches it
+ *     off and clears the log. Returns LCI_OK, or LCI_ERR_HIP.
+ *   lci_kernel_timing_read(kernel, &total_ms, &launches) waits for the logged
+ *     events of that kernel kind (host synchronisation on those events only)
+ *     and returns the summed event-to-event time and the launch count since the
+ *     log was cleared. Errors: NULL, SHAPE (unknown kernel id), HIP.
+ *   lci_kernel_name(kernel) is the kernel kind's name, NULL for an unknown id.
+ * Recording events costs a few microseconds per launch: use it for per-kernel
+ * figures, not for the end-to-end latency of a call. */
+enum {
+  LCI_KERNEL_IDX_SCORE = 0,   /* indexer scores, prefill layout                     */
+  LCI_KERNEL_TOPK = 1,        /* Top-K over materialised score rows                 */
+  LCI_KERNEL_IDX_MASK = 2,    /* index rows -> position bit masks for dense tiles    */
+  LCI_KERNEL_ATTN_DENSE = 3,  /* masked attention over contiguous key tiles          */
+  LCI_KERNEL_ATTN_GATHER = 4, /* attention over gathered selected keys              */
+  LCI_KERNEL_ATTN_COMBINE = 5,/* fixed-order merge of split-K partial results        */
+  LCI_KERNEL_DEC_INIT = 6,    /* decode: clear histograms and counters              */
+  LCI_KERNEL_DEC_SCORE = 7,   /* decode: scores + score histogram per history chunk */
+  LCI_KERNEL_DEC_CAND = 8,    /* decode: candidates at or above the threshold bin   */
+  LCI_KERNEL_DEC_RESOLVE = 9, /* decode: exact K-th score among the candidates      */
+  LCI_KERNEL_DEC_COMPACT = 10,/* decode: ordered compaction of the selected positions*/
+  LCI_KERNEL_COUNT = 11
+};
+int lci_kernel_timing(int enable);
+int lci_kernel_timing_read(int kernel, double *total_ms, int64_t *launches);
+const char *lci_kernel_name(int kernel);
 
 #ifdef __cplusplus
 }

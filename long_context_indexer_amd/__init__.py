@@ -10,7 +10,7 @@ raises.
 
 Entry points (same names as the C ABI, without the ``lci_`` prefix):
     idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd,
-    workspace_bytes
+    workspace_bytes, kernel_timing, kernel_timing_read, kernel_name
 """
 from __future__ import annotations
 
@@ -25,7 +25,11 @@ ENTRY_IDX_SCORE, ENTRY_TOPK_SELECT, ENTRY_SPARSE_ATTN, ENTRY_PREFILL, ENTRY_DECO
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
            "lci_decode_fwd", "lci_workspace_bytes", "lci_status_str", "lci_last_hip_error",
-           "lci_abi_version")
+           "lci_abi_version", "lci_kernel_timing", "lci_kernel_timing_read", "lci_kernel_name")
+
+# kernel kinds of the timing log (LCI_KERNEL_* in lci.h)
+KERNELS = ("idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
+           "dec_init", "dec_score", "dec_cand", "dec_resolve", "dec_compact")
 
 
 class LciError(RuntimeError):
@@ -67,8 +71,13 @@ def load_library(path: str = LIB_PATH):
     lib.lci_status_str.restype = ctypes.c_char_p
     lib.lci_last_hip_error.restype = ctypes.c_int
     lib.lci_abi_version.restype = ctypes.c_int
+    lib.lci_kernel_timing.argtypes = [ctypes.c_int]
+    lib.lci_kernel_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_int64)]
+    lib.lci_kernel_name.argtypes = [ctypes.c_int]
+    lib.lci_kernel_name.restype = ctypes.c_char_p
     for fn in ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
-               "lci_decode_fwd"):
+               "lci_decode_fwd", "lci_kernel_timing", "lci_kernel_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -132,6 +141,24 @@ def _w_strides(w, B, Tq, H_I):
 
 def workspace_bytes(entry: int, geom: lci_geom) -> int:
     return int(load_library().lci_workspace_bytes(entry, ctypes.byref(geom)))
+
+
+def kernel_timing(enable: bool) -> None:
+    """Switch the library's per-kernel event log on (cleared) or off."""
+    _check(load_library().lci_kernel_timing(1 if enable else 0))
+
+
+def kernel_timing_read(kernel) -> tuple:
+    """(total_ms, launches) of one kernel kind (index or name) since timing was switched on."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(load_library().lci_kernel_timing_read(k, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def kernel_name(kernel: int) -> Optional[str]:
+    r = load_library().lci_kernel_name(int(kernel))
+    return None if r is None else r.decode()
 
 
 def _workspace(entry, geom, workspace, device):

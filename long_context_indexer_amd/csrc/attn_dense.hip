@@ -37,6 +37,8 @@
 // (blockIdx.x % 8 picks the XCD), and the longest causal tiles start first.
 #include "attn_dense.h"
 #include "common.h"
+#include "../../include/lci.h"
+#include "internal.h"
 
 namespace lci {
 
@@ -440,9 +442,12 @@ static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16
   const int nblk = g.B * nbps;
   const int per = 8 / g.Hkv;
   const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
-  hipLaunchKernelGGL((attn_dense_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, st,
-                     g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, mask, Wm, flag,
-                     scale * LOG2E, out, lse, nbps, nblk);
+  {
+    KernelTimer timer(LCI_KERNEL_ATTN_DENSE, st);
+    hipLaunchKernelGGL((attn_dense_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, st,
+                       g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, mask, Wm, flag,
+                       scale * LOG2E, out, lse, nbps, nblk);
+  }
   return hipGetLastError();
 }
 
@@ -471,8 +476,11 @@ hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k
   uint8_t* flag = reinterpret_cast<uint8_t*>(static_cast<char*>(ws) +
                                              ((rows * Wm * sizeof(uint32_t) + 255) & ~size_t(255)));
   const int lim = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
-  hipLaunchKernelGGL(idx_mask_kernel, dim3(static_cast<uint32_t>(rows)), dim3(256), 0, st, g.Tq,
-                     g.Tk, g.K, g.q_offset, g.kv_len, idx, lim, Wm, mask, flag);
+  {
+    KernelTimer timer(LCI_KERNEL_IDX_MASK, st);
+    hipLaunchKernelGGL(idx_mask_kernel, dim3(static_cast<uint32_t>(rows)), dim3(256), 0, st, g.Tq,
+                       g.Tk, g.K, g.q_offset, g.kv_len, idx, lim, Wm, mask, flag);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   *flag_out = flag;

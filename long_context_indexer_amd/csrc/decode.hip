@@ -30,6 +30,8 @@
 // asc): every position in a higher bin is kept, every position in a lower bin
 // dropped, and the split inside b* is resolved exactly.
 #include "common.h"
+#include "../../include/lci.h"
+#include "internal.h"
 #include "decode.h"
 #include "select_row.h"
 
@@ -502,8 +504,11 @@ template <int H_I, int D_I>
 static hipError_t launch_score_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                                   const int8_t* w, int64_t wsb, int32_t* S, uint32_t* hist,
                                   int nchunks, hipStream_t st) {
-  hipLaunchKernelGGL((dec_score_kernel<H_I, D_I>), dim3(nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk,
-                     g.K, g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, S, hist);
+  {
+    KernelTimer timer(LCI_KERNEL_DEC_SCORE, st);
+    hipLaunchKernelGGL((dec_score_kernel<H_I, D_I>), dim3(nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk,
+                       g.K, g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, S, hist);
+  }
   return hipGetLastError();
 }
 
@@ -537,7 +542,10 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
   int32_t* thr = reinterpret_cast<int32_t*>(ws + L.thr);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
 
-  hipLaunchKernelGGL(dec_init_kernel, dim3(g.B), dim3(256), 0, st, g.B, hist, ncand);
+  {
+    KernelTimer timer(LCI_KERNEL_DEC_INIT, st);
+    hipLaunchKernelGGL(dec_init_kernel, dim3(g.B), dim3(256), 0, st, g.B, hist, ncand);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (g.H_I) {
@@ -549,14 +557,23 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
     default: e = hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dec_cand_kernel, dim3(L.nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk, g.K,
-                     g.q_offset, g.kv_len, S, hist, ncand, cand, ngt, L.nchunks);
+  {
+    KernelTimer timer(LCI_KERNEL_DEC_CAND, st);
+    hipLaunchKernelGGL(dec_cand_kernel, dim3(L.nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk, g.K,
+                       g.q_offset, g.kv_len, S, hist, ncand, cand, ngt, L.nchunks);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(dec_resolve_kernel, dim3(g.B), dim3(TOPK_NT), 0, st, g.Tk, g.K, g.q_offset,
-                     g.kv_len, S, hist, ncand, cand, ngt, off, L.nchunks, thr, idx);
+  {
+    KernelTimer timer(LCI_KERNEL_DEC_RESOLVE, st);
+    hipLaunchKernelGGL(dec_resolve_kernel, dim3(g.B), dim3(TOPK_NT), 0, st, g.Tk, g.K, g.q_offset,
+                       g.kv_len, S, hist, ncand, cand, ngt, off, L.nchunks, thr, idx);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(dec_compact_kernel, dim3(L.nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk,
-                     g.q_offset, g.kv_len, S, thr, off, L.nchunks, g.K, idx);
+  {
+    KernelTimer timer(LCI_KERNEL_DEC_COMPACT, st);
+    hipLaunchKernelGGL(dec_compact_kernel, dim3(L.nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk,
+                       g.q_offset, g.kv_len, S, thr, off, L.nchunks, g.K, idx);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_sparse_attn(g, q, k, v, idx, gate, scale, out, lse, L.splits, ws + L.attn, st);
 }

@@ -17,6 +17,7 @@
 // element v of lane l is row 8*(v/4) + 4*(l/32) + v%4, i.e. slot v of half l/32,
 // for column (history position) l%32.
 #include "common.h"
+#include "../../include/lci.h"
 #include "internal.h"
 
 namespace lci {
@@ -117,16 +118,22 @@ static hipError_t launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_
     // many query rows: 4 waves on 4 row tiles share each key tile
     const int keys = 256;
     dim3 grid((g.Tk + keys - 1) / keys, (row_count + 4 * QW - 1) / (4 * QW), g.B);
-    hipLaunchKernelGGL((idx_score_kernel<H_I, D_I, 4>), grid, dim3(256), 0, st, g.Tq, g.Tk,
-                       g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, wsq, scores, stride,
-                       row_begin, row_count, keys);
+    {
+      KernelTimer timer(LCI_KERNEL_IDX_SCORE, st);
+      hipLaunchKernelGGL((idx_score_kernel<H_I, D_I, 4>), grid, dim3(256), 0, st, g.Tq, g.Tk,
+                         g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, wsq, scores, stride,
+                         row_begin, row_count, keys);
+    }
   } else {
     // few query rows (decode): the 4 waves split the history
     const int keys = 1024;
     dim3 grid((g.Tk + keys - 1) / keys, (row_count + QW - 1) / QW, g.B);
-    hipLaunchKernelGGL((idx_score_kernel<H_I, D_I, 1>), grid, dim3(256), 0, st, g.Tq, g.Tk,
-                       g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, wsq, scores, stride,
-                       row_begin, row_count, keys);
+    {
+      KernelTimer timer(LCI_KERNEL_IDX_SCORE, st);
+      hipLaunchKernelGGL((idx_score_kernel<H_I, D_I, 1>), grid, dim3(256), 0, st, g.Tq, g.Tk,
+                         g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, wsq, scores, stride,
+                         row_begin, row_count, keys);
+    }
   }
   return hipGetLastError();
 }

@@ -7,6 +7,21 @@
 
 namespace lci {
 
+// Brackets one kernel launch with timing events on its stream while kernel
+// timing is on (lci_kernel_timing); does nothing otherwise.
+class KernelTimer {
+ public:
+  KernelTimer(int kind, hipStream_t stream);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  int kind_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
+};
+
 struct Geom {
   int B, Tq, Tk, Hq, Hkv, d, H_I, d_I, K;
   const int32_t* q_offset;

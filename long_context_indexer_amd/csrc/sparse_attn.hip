@@ -25,6 +25,7 @@
 // a combine kernel merges them in split order (deterministic).
 #include "attn_dense.h"
 #include "common.h"
+#include "../../include/lci.h"
 #include "internal.h"
 
 namespace lci {
@@ -322,14 +323,20 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   }
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq * splits));
   const size_t lds = static_cast<size_t>(g.Hkv) * 16 * C::PITCH * sizeof(uint16_t);
-  hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * g.Hkv), lds, st, g.Tq, g.Tk, g.K,
-                     g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, scale * LOG2E, out, lse,
-                     splits, per_split, static_cast<float*>(ws), dflag, dense_block_rows(G));
+  {
+    KernelTimer timer(LCI_KERNEL_ATTN_GATHER, st);
+    hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * g.Hkv), lds, st, g.Tq, g.Tk, g.K,
+                       g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, scale * LOG2E, out, lse,
+                       splits, per_split, static_cast<float*>(ws), dflag, dense_block_rows(G));
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   dim3 cgrid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq), (g.Hq * (D / 4) + 255) / 256);
-  hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(256), 0, st, g.Hq, splits,
-                     static_cast<const float*>(ws), gate, out, lse);
+  {
+    KernelTimer timer(LCI_KERNEL_ATTN_COMBINE, st);
+    hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(256), 0, st, g.Hq, splits,
+                       static_cast<const float*>(ws), gate, out, lse);
+  }
   return hipGetLastError();
 }
 

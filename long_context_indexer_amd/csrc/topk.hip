@@ -17,6 +17,7 @@
 //      first r keys == v*: one block-wide prefix scan per chunk of the packed
 //      (count greater, count equal) pair gives each thread its output slot.
 #include "common.h"
+#include "../../include/lci.h"
 #include "internal.h"
 #include "select_row.h"
 
@@ -53,8 +54,11 @@ hipError_t launch_topk_rows(const Geom& g, const int32_t* scores, int64_t stride
                             int row_begin, int row_count, int32_t* idx, int32_t* sel,
                             hipStream_t st) {
   dim3 grid(row_count, g.B);
-  hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(TOPK_NT), 0, st, g.Tq, g.Tk, g.K,
-                     g.q_offset, g.kv_len, scores, stride, row_begin, row_count, idx, sel);
+  {
+    KernelTimer timer(LCI_KERNEL_TOPK, st);
+    hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(TOPK_NT), 0, st, g.Tq, g.Tk, g.K,
+                       g.q_offset, g.kv_len, scores, stride, row_begin, row_count, idx, sel);
+  }
   return hipGetLastError();
 }
 

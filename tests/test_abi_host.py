@@ -154,6 +154,18 @@ def test_decode_needs_one_row(lib):
     assert fused(lib, g, fn="lci_decode_fwd") == SHAPE
 
 
+def test_kernel_timing_log_on_the_host(lib):
+    # switching the log on and off touches no device; reads validate their arguments
+    assert [lci.kernel_name(k) for k in range(len(lci.KERNELS))] == list(lci.KERNELS)
+    assert lib.lci_kernel_name(len(lci.KERNELS)) is None
+    assert lib.lci_kernel_timing(1) == OK
+    assert lci.kernel_timing_read("attn_dense") == (0.0, 0)
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.lci_kernel_timing_read(99, ctypes.byref(ms), ctypes.byref(n)) == SHAPE
+    assert lib.lci_kernel_timing_read(0, None, ctypes.byref(n)) == NULL
+    assert lib.lci_kernel_timing(0) == OK
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     z = torch.zeros(1, 4, 2, 32, dtype=torch.int8)
