@@ -15,12 +15,12 @@ constexpr int kDenseMaxWords = (kDenseFactor * 4096 + 31) / 32;
 int dense_block_rows(int G);
 int dense_mask_words(const Geom& g);
 size_t dense_workspace(const Geom& g);
-// Builds masks/flags in `ws` (dense_workspace bytes), runs the tile kernel on
-// every token block whose rows all qualify, and returns the row flags so the
-// gather kernel can skip those blocks.
+// Builds masks/flags in `ws` (dense_workspace bytes; skipped when the Top-K
+// kernel wrote them already), runs the tile kernel on every token block whose
+// rows all qualify and marks those blocks done for the gather kernel.
 hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const int32_t* idx, const uint16_t* gate,
-                             float scale, uint16_t* out, float* lse, void* ws, uint8_t** flag_out,
+                             float scale, uint16_t* out, float* lse, void* ws, bool masks_ready,
                              hipStream_t st);
 
 }  // namespace lci

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ gate, const uint32_t* __restrict__ mask, int Wm,
     const uint8_t* __restrict__ flag, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int nbps, int nblk) {
+    float* __restrict__ lse, uint8_t* __restrict__ done, int nbps, int nblk) {
   using C = DenseCfg<D, G>;
   // two K and two V tile buffers (see the pipeline below)
   __shared__ __align__(16) uint16_t ks[2][C::BK * C::KP];
@@ -179,7 +179,10 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   int ok = 1;
   if (threadIdx.x < C::BQ && i0 + static_cast<int>(threadIdx.x) < Tq)
     ok = flag[static_cast<int64_t>(b) * Tq + i0 + threadIdx.x] != 0;
-  if (__syncthreads_and(ok) == 0) return;
+  const int all_ok = __syncthreads_and(ok);
+  // the gather kernel skips the token blocks this kernel takes
+  if (threadIdx.x == 0) done[static_cast<int64_t>(b) * nbps + tb] = all_ok ? 1 : 0;
+  if (all_ok == 0) return;
 
   const int qo = q_offset[b];
   const int kvl = kv_len[b];
@@ -426,17 +429,32 @@ int dense_mask_words(const Geom& g) {
   return static_cast<int>((lim + 31) / 32);
 }
 
+// [mask: rows x Wm words][flag: rows bytes][done: one byte per token block
+// (at most one block per row)], each part 256-byte aligned
 size_t dense_workspace(const Geom& g) {
   const size_t rows = static_cast<size_t>(g.B) * g.Tq;
   const size_t mbytes = (rows * dense_mask_words(g) * sizeof(uint32_t) + 255) & ~size_t(255);
-  return mbytes + ((rows + 255) & ~size_t(255));
+  return mbytes + 2 * ((rows + 255) & ~size_t(255));
+}
+
+DenseMasks dense_masks(const Geom& g, void* ws) {
+  const size_t rows = static_cast<size_t>(g.B) * g.Tq;
+  DenseMasks d;
+  d.Wm = dense_mask_words(g);
+  d.lim = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
+  char* base = static_cast<char*>(ws);
+  const size_t mbytes = (rows * d.Wm * sizeof(uint32_t) + 255) & ~size_t(255);
+  d.mask = reinterpret_cast<uint32_t*>(base);
+  d.flag = reinterpret_cast<uint8_t*>(base + mbytes);
+  d.done = reinterpret_cast<uint8_t*>(base + mbytes + ((rows + 255) & ~size_t(255)));
+  return d;
 }
 
 template <int D, int G>
 static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const uint16_t* gate, float scale,
-                                  uint16_t* out, float* lse, const uint32_t* mask, int Wm,
-                                  const uint8_t* flag, hipStream_t st) {
+                                  uint16_t* out, float* lse, const DenseMasks& dm,
+                                  hipStream_t st) {
   using C = DenseCfg<D, G>;
   const int nbps = (g.Tq + C::BQ - 1) / C::BQ;
   const int nblk = g.B * nbps;
@@ -445,8 +463,8 @@ static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16
   {
     KernelTimer timer(LCI_KERNEL_ATTN_DENSE, st);
     hipLaunchKernelGGL((attn_dense_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, st,
-                       g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, mask, Wm, flag,
-                       scale * LOG2E, out, lse, nbps, nblk);
+                       g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, dm.mask,
+                       dm.Wm, dm.flag, scale * LOG2E, out, lse, dm.done, nbps, nblk);
   }
   return hipGetLastError();
 }
@@ -454,39 +472,33 @@ static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16
 template <int D>
 static hipError_t launch_dense_d(const Geom& g, const uint16_t* q, const uint16_t* k,
                                  const uint16_t* v, const uint16_t* gate, float scale,
-                                 uint16_t* out, float* lse, const uint32_t* mask, int Wm,
-                                 const uint8_t* flag, hipStream_t st) {
+                                 uint16_t* out, float* lse, const DenseMasks& dm, hipStream_t st) {
   switch (g.Hq / g.Hkv) {
-    case 1: return launch_dense_dg<D, 1>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
-    case 2: return launch_dense_dg<D, 2>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
-    case 4: return launch_dense_dg<D, 4>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
-    case 8: return launch_dense_dg<D, 8>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
-    case 16: return launch_dense_dg<D, 16>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    case 1: return launch_dense_dg<D, 1>(g, q, k, v, gate, scale, out, lse, dm, st);
+    case 2: return launch_dense_dg<D, 2>(g, q, k, v, gate, scale, out, lse, dm, st);
+    case 4: return launch_dense_dg<D, 4>(g, q, k, v, gate, scale, out, lse, dm, st);
+    case 8: return launch_dense_dg<D, 8>(g, q, k, v, gate, scale, out, lse, dm, st);
+    case 16: return launch_dense_dg<D, 16>(g, q, k, v, gate, scale, out, lse, dm, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const int32_t* idx, const uint16_t* gate,
-                             float scale, uint16_t* out, float* lse, void* ws, uint8_t** flag_out,
+                             float scale, uint16_t* out, float* lse, void* ws, bool masks_ready,
                              hipStream_t st) {
-  const int Wm = dense_mask_words(g);
+  const DenseMasks dm = dense_masks(g, ws);
   const size_t rows = static_cast<size_t>(g.B) * g.Tq;
-  uint32_t* mask = static_cast<uint32_t*>(ws);
-  uint8_t* flag = reinterpret_cast<uint8_t*>(static_cast<char*>(ws) +
-                                             ((rows * Wm * sizeof(uint32_t) + 255) & ~size_t(255)));
-  const int lim = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
-  {
+  if (!masks_ready) {
     KernelTimer timer(LCI_KERNEL_IDX_MASK, st);
     hipLaunchKernelGGL(idx_mask_kernel, dim3(static_cast<uint32_t>(rows)), dim3(256), 0, st, g.Tq,
-                       g.Tk, g.K, g.q_offset, g.kv_len, idx, lim, Wm, mask, flag);
+                       g.Tk, g.K, g.q_offset, g.kv_len, idx, dm.lim, dm.Wm, dm.mask, dm.flag);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  *flag_out = flag;
   switch (g.d) {
-    case 64: return launch_dense_d<64>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
-    case 128: return launch_dense_d<128>(g, q, k, v, gate, scale, out, lse, mask, Wm, flag, st);
+    case 64: return launch_dense_d<64>(g, q, k, v, gate, scale, out, lse, dm, st);
+    case 128: return launch_dense_d<128>(g, q, k, v, gate, scale, out, lse, dm, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -575,7 +575,8 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
                        g.q_offset, g.kv_len, S, thr, off, L.nchunks, g.K, idx);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_sparse_attn(g, q, k, v, idx, gate, scale, out, lse, L.splits, ws + L.attn, st);
+  return launch_sparse_attn(g, q, k, v, idx, gate, scale, out, lse, L.splits, ws + L.attn, false,
+                            st);
 }
 
 }  // namespace lci

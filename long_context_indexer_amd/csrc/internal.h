@@ -38,16 +38,37 @@ hipError_t launch_idx_score(const Geom& g, const int8_t* q_idx, const int8_t* k_
 // Both launchers work on query rows [row_begin, row_begin+row_count) of every
 // sequence; the score row of (b, row_begin + r) is at scores + (b*row_count + r)*stride.
 // idx/sel are always the full [B, Tq, K] arrays.
+// Rows of histories up to kWaveTopkMax positions (Tk <= kWaveTopkMax) run one
+// wave per row with the row in registers; longer ones one workgroup per row.
+constexpr int kWaveTopkMax = 8192;
+
+// Inputs of the dense-tile attention kernel, inside the sparse-attention
+// workspace: per-row bit masks over positions (Wm words a row), row flags
+// (2: keeps all of 0..p, 1: masked tiles, 0: gathered) and per-token-block
+// "done by the tile kernel" bytes. Rows qualify when p + 1 <= lim.
+struct DenseMasks {
+  uint32_t* mask;
+  uint8_t* flag;
+  uint8_t* done;
+  int Wm, lim;
+};
+DenseMasks dense_masks(const Geom& g, void* workspace);
+
+// With dm (only when Tk <= kWaveTopkMax), the Top-K kernel also writes the
+// dense-path flags and masks of its rows.
 hipError_t launch_topk_rows(const Geom& g, const int32_t* scores, int64_t score_row_stride,
                             int row_begin, int row_count, int32_t* idx, int32_t* sel,
-                            hipStream_t stream);
+                            const DenseMasks* dm, hipStream_t stream);
 
 // ---- sparse attention over index rows
 size_t sparse_attn_workspace(const Geom& g, int splits);
 int sparse_attn_pick_splits(const Geom& g);
+// masks_ready: the dense-path masks and flags in the workspace were written by
+// the Top-K kernel (valid index rows by construction), so the index rows are
+// not scanned again.
 hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* idx, const uint16_t* gate,
                               float scale, uint16_t* out, float* lse, int splits,
-                              void* workspace, hipStream_t stream);
+                              void* workspace, bool masks_ready, hipStream_t stream);
 
 }  // namespace lci

@@ -164,7 +164,7 @@ lci_status lci_topk_select(const lci_geom* g, const int32_t* scores, int32_t* id
   if (!aligned4(scores) || !aligned4(idx) || (sel_scores && !aligned4(sel_scores)))
     return LCI_ERR_ALIGN;
   const Geom gg = to_geom(g);
-  return hip_status(lci::launch_topk_rows(gg, scores, g->Tk, 0, g->Tq, idx, sel_scores,
+  return hip_status(lci::launch_topk_rows(gg, scores, g->Tk, 0, g->Tq, idx, sel_scores, nullptr,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -186,7 +186,7 @@ lci_status lci_sparse_attn_fwd(const lci_geom* g, const lci_bf16* q, const lci_b
   if (need > 0 && (!workspace || ws_bytes < need)) return LCI_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return LCI_ERR_ALIGN;
   return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, softmax_scale, out, lse,
-                                            splits, workspace,
+                                            splits, workspace, false,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -213,15 +213,19 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   char* ws = static_cast<char*>(workspace);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx_off);
   int32_t* sc = reinterpret_cast<int32_t*>(ws + L.score_off);
+  // with the dense-tile path on (one split) and rows short enough for the
+  // one-wave Top-K kernel, that kernel writes the tile path's masks and flags
+  const bool masks = L.splits == 1 && g->Tk <= lci::kWaveTopkMax;
+  const lci::DenseMasks dm = masks ? lci::dense_masks(gg, ws + L.attn_off) : lci::DenseMasks{};
   for (int r0 = 0; r0 < g->Tq; r0 += L.chunk_rows) {
     const int rc = std::min(L.chunk_rows, g->Tq - r0);
     hipError_t e = lci::launch_idx_score(gg, q_idx, k_idx, w, wsb, wsq, sc, g->Tk, r0, rc, st);
     if (e != hipSuccess) return hip_status(e);
-    e = lci::launch_topk_rows(gg, sc, g->Tk, r0, rc, idx, nullptr, st);
+    e = lci::launch_topk_rows(gg, sc, g->Tk, r0, rc, idx, nullptr, masks ? &dm : nullptr, st);
     if (e != hipSuccess) return hip_status(e);
   }
   return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, scale, out, lse, L.splits,
-                                            ws + L.attn_off, st));
+                                            ws + L.attn_off, masks, st));
 }
 
 lci_status lci_prefill_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,

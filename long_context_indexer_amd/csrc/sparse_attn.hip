@@ -96,24 +96,25 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ gate, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int splits, int per_split, float* __restrict__ part,
-    const uint8_t* __restrict__ dflag, int dbq) {
+    const uint8_t* __restrict__ done, int dbq, int64_t nitems) {
   using C = AttnCfg<D>;
   // [Hkv][16][PITCH]; 16-byte aligned wherever the dynamic LDS region starts:
   // its 8-byte writes and transposed reads need aligned rows
   extern __shared__ __align__(16) uint16_t vstage[];
   const int lane = threadIdx.x & 63;
   const int g = threadIdx.x >> 6;
-  // blockIdx.x = (b*Tq + row)*splits + split
-  const int split = static_cast<int>(blockIdx.x % splits);
-  const int64_t qrow = blockIdx.x / splits;
+  // work items (b*Tq + row)*splits + split, strided over the grid; the waves
+  // of a workgroup share no LDS and no barrier, so an item ends by returning
+  // from the per-item body
+  for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) [&] {
+  const int split = static_cast<int>(item % splits);
+  const int64_t qrow = item / splits;
   const int b = static_cast<int>(qrow / Tq);
-  if (dflag) {
-    // rows of a token block that the tile kernel took are done already
+  if (done) {
+    // token blocks the tile kernel took are finished already
     const int i = static_cast<int>(qrow % Tq);
-    const int r0 = i / dbq * dbq, r1 = min(r0 + dbq, Tq);
-    bool all = true;
-    for (int rr = r0; rr < r1; ++rr) all = all && dflag[static_cast<int64_t>(b) * Tq + rr] != 0;
-    if (all) return;
+    const int nbps = (Tq + dbq - 1) / dbq;
+    if (done[static_cast<int64_t>(b) * nbps + i / dbq]) return;
   }
   const int kvl0 = kv_len[b];
   const int kvl = kvl0 <= Tk ? kvl0 : 0;  // a history longer than its allocation: no entry is read
@@ -290,6 +291,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
     }
     if (lse && grp == 0) lse[qrow * Hq + h] = lex > 0.f ? (m + fast_log2(lex)) * LN2 : -INFINITY;
   }
+  }();
 }
 
 int sparse_attn_pick_splits(const Geom& g) {
@@ -311,23 +313,28 @@ template <int D>
 static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const int32_t* idx, const uint16_t* gate,
                            float scale, uint16_t* out, float* lse, int splits, void* ws,
-                           hipStream_t st) {
+                           bool masks_ready, hipStream_t st) {
   using C = AttnCfg<D>;
   const int G = g.Hq / g.Hkv;
   int per_split = (g.K + splits - 1) / splits;
   per_split = (per_split + 15) / 16 * 16;
-  uint8_t* dflag = nullptr;
+  const uint8_t* done = nullptr;
   if (splits == 1) {
-    hipError_t e0 = launch_dense_attn(g, q, k, v, idx, gate, scale, out, lse, ws, &dflag, st);
+    hipError_t e0 = launch_dense_attn(g, q, k, v, idx, gate, scale, out, lse, ws, masks_ready, st);
     if (e0 != hipSuccess) return e0;
+    done = dense_masks(g, ws).done;
   }
-  dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq * splits));
+  // a grid of up to 8192 waves strides over the items (rows x splits), so
+  // items the tile kernel finished cost one byte read each
+  const int64_t nitems = static_cast<int64_t>(g.B) * g.Tq * splits;
+  dim3 grid(static_cast<uint32_t>(std::min<int64_t>(nitems, 8192 / g.Hkv)));
   const size_t lds = static_cast<size_t>(g.Hkv) * 16 * C::PITCH * sizeof(uint16_t);
   {
     KernelTimer timer(LCI_KERNEL_ATTN_GATHER, st);
     hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * g.Hkv), lds, st, g.Tq, g.Tk, g.K,
                        g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, scale * LOG2E, out, lse,
-                       splits, per_split, static_cast<float*>(ws), dflag, dense_block_rows(G));
+                       splits, per_split, static_cast<float*>(ws), done, dense_block_rows(G),
+                       nitems);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
@@ -343,10 +350,10 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
 hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* idx, const uint16_t* gate,
                               float scale, uint16_t* out, float* lse, int splits, void* ws,
-                              hipStream_t st) {
+                              bool masks_ready, hipStream_t st) {
   switch (g.d) {
-    case 64: return launch_d<64>(g, q, k, v, idx, gate, scale, out, lse, splits, ws, st);
-    case 128: return launch_d<128>(g, q, k, v, idx, gate, scale, out, lse, splits, ws, st);
+    case 64: return launch_d<64>(g, q, k, v, idx, gate, scale, out, lse, splits, ws, masks_ready, st);
+    case 128: return launch_d<128>(g, q, k, v, idx, gate, scale, out, lse, splits, ws, masks_ready, st);
     default: return hipErrorInvalidValue;
   }
 }

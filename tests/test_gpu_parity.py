@@ -94,6 +94,11 @@ TOPK_CASES = {
     "ragged_invalid": (MED.replace(B=3, Tq=40, Tk=900), 100,
                        dict(q_offset=[0, 850, 400], kv_len=[900, 870, 420])),
     "long_rows": (MED.replace(B=2, Tq=1, Tk=40000, decode=True), 2048, {}),
+    # one-wave kernel at its limit: rows of 8184..8191 positions, row starts not
+    # 16-byte aligned (Tk % 4 == 3), a partial last chunk
+    "wave_unaligned": (MED.replace(Tq=8, Tk=8191), 2048, dict(q_offset=[8183])),
+    # rows of exactly 8192 positions (every chunk full) and a few shorter ones
+    "wave_full": (MED.replace(Tq=12, Tk=8192), 3000, dict(q_offset=[8180])),
 }
 
 
@@ -177,6 +182,9 @@ FUSED_CASES = {
                             dict(q_offset=[604, 300], kv_len=[700, 396])),
     "invalid_rows": (TINY.replace(B=2, Tq=20, Tk=100, K=8), dict(q_offset=[90, 0],
                                                                   kv_len=[100, 10])),
+    # one split: the Top-K kernel writes the tile path's flags and masks; rows
+    # p < 256 keep everything, 256 <= p < 1024 take masked tiles, the rest gather
+    "tile_masks_from_topk": (MED.replace(Tq=2048, Tk=2048, K=256), {}),
 }
 
 
