@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void idx_mask_kernel(
   const int64_t p = static_cast<int64_t>(q_offset[b]) + i;
   const bool eligible = kvl <= Tk && p >= 0 && p < kvl && p + 1 <= lim;
   if (!eligible) {
-    if (threadIdx.x == 0) flag[row] = 0;
+    if (threadIdx.x == 0) flag[row] = kRowGather;
     return;
   }
   for (int w = threadIdx.x; w < Wm; w += blockDim.x) bits[w] = 0u;
@@ -88,9 +88,9 @@ __global__ __launch_bounds__(256) void idx_mask_kernel(
   __syncthreads();
   uint32_t tot = 0;
   for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) tot += red[w];
-  const uint8_t f = bad ? 0 : (tot == static_cast<uint32_t>(p + 1) ? 2 : 1);
+  const uint8_t f = bad ? kRowGather : (tot == static_cast<uint32_t>(p + 1) ? kRowAll : kRowMasked);
   if (threadIdx.x == 0) flag[row] = f;
-  if (f == 1)
+  if (f == kRowMasked)
     for (int w = threadIdx.x; w < Wm; w += blockDim.x) mask[row * Wm + w] = bits[w];
 }
 
@@ -186,8 +186,9 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
 
   const int qo = q_offset[b];
   const int kvl = kv_len[b];
-  const int p_last = qo + iend - 1;
-  const int nkb = p_last / C::BK + 1;
+  // last key any row of the block reads (rows past the history read none)
+  const int64_t p_last = min(static_cast<int64_t>(qo) + iend - 1, static_cast<int64_t>(kvl) - 1);
+  const int nkb = p_last < 0 ? 0 : static_cast<int>(p_last / C::BK) + 1;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   // below the wave's first position need no mask at all
   const int iw0 = i0 + wv * C::TW;
   const int p_wave_min = qo + iw0;
-  const bool wave_all = __all(!rv || fl == 2) && iw0 < Tq;
+  const bool wave_all = __all(!rv || fl == kRowAll) && iw0 < Tq;
 
   // Q^T as the B operand: lane holds Q[row][16*kk + 8*hf .. +7]
   v8bf qf[C::NKK];
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
       for (int kt = 0; kt < 2; ++kt) {
         const int n = p - (key0 + 32 * kt) + 1;  // flag 2: keys key0+32kt .. p are kept
         const uint32_t causal = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
-        uint32_t mw = fl == 2 ? causal : (fl == 1 ? mwc[kt] : 0u);
+        uint32_t mw = fl == kRowAll ? causal : (fl == kRowMasked ? mwc[kt] : 0u);
         // bit kofs(e) = 8(e/4) + 4hf + e%4 of mw keeps element e: a one-bit
         // signed extract gives an all-ones/all-zeros select mask
         mw >>= 4 * hf;
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   }
 
   lsum += shfl_xor(lsum, 32);
-  if (!rv || fl == 0) return;
+  if (!rv || fl == kRowGather) return;  // an empty row (nothing kept) writes 0 and -inf
   const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
   const int64_t obase = (qrow * Hq + h) * D;
 #pragma unroll

@@ -42,10 +42,18 @@ hipError_t launch_idx_score(const Geom& g, const int8_t* q_idx, const int8_t* k_
 // wave per row with the row in registers; longer ones one workgroup per row.
 constexpr int kWaveTopkMax = 8192;
 
+// Row flags of the dense-tile attention path.
+enum : uint8_t {
+  kRowGather = 0,  // left to the gather kernel
+  kRowMasked = 1,  // tile kernel, keys given by the row's bit mask
+  kRowAll = 2,     // tile kernel, the row keeps every position 0..p
+  kRowEmpty = 3,   // tile kernel writes the empty-row result (no valid position)
+};
+
 // Inputs of the dense-tile attention kernel, inside the sparse-attention
 // workspace: per-row bit masks over positions (Wm words a row), row flags
-// (2: keeps all of 0..p, 1: masked tiles, 0: gathered) and per-token-block
-// "done by the tile kernel" bytes. Rows qualify when p + 1 <= lim.
+// (kRow*) and per-token-block "done by the tile kernel" bytes. Rows qualify
+// when p + 1 <= lim.
 struct DenseMasks {
   uint32_t* mask;
   uint8_t* flag;

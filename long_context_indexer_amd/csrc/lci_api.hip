@@ -66,7 +66,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 // Fused prefill: query rows are scored and selected in chunks whose int32 score
 // block stays within kScoreBudget (it then largely stays in the 256 MiB
 // last-level cache between the scoring and selection kernels).
-constexpr size_t kScoreBudget = size_t(128) << 20;
+constexpr size_t kScoreBudget = size_t(256) << 20;
 
 int prefill_chunk_rows(const lci_geom* g) {
   const size_t per_row = static_cast<size_t>(g->B) * g->Tk * sizeof(int32_t);

@@ -322,7 +322,11 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   if (splits == 1) {
     hipError_t e0 = launch_dense_attn(g, q, k, v, idx, gate, scale, out, lse, ws, masks_ready, st);
     if (e0 != hipSuccess) return e0;
-    done = dense_masks(g, ws).done;
+    const DenseMasks dm = dense_masks(g, ws);
+    // masks from the Top-K kernel and histories no longer than lim: every row
+    // is a tile-kernel row (valid ones qualify, empty ones are written there)
+    if (masks_ready && g.Tk <= dm.lim) return hipSuccess;
+    done = dm.done;
   }
   // a grid of up to 8192 waves strides over the items (rows x splits), so
   // items the tile kernel finished cost one byte read each

@@ -72,8 +72,8 @@ __global__ __launch_bounds__(TOPK_NT) void topk_rows_kernel(
 //      position its slot in an LDS copy of the output row, written out
 //      coalesced at the end.
 // With dense-path outputs, the kernel also writes the row flag of the
-// dense-tile attention kernel (2: the row keeps all of 0..p; 1: masked tiles;
-// 0: gathered) and, for flag-1 rows, the bit mask of the kept positions.
+// dense-tile attention kernel (kRow* in internal.h) and, for masked rows, the
+// bit mask of the kept positions.
 
 namespace {
 
@@ -137,11 +137,11 @@ __global__ __launch_bounds__(B4_NT) void topk_b4_kernel(
       out[j] = j < n ? j : -1;
       if (outs) outs[j] = j < n ? S[j] : INT32_MIN;
     }
-    if (dflag && t == 0) dflag[grow] = valid ? 2 : 0;
+    if (dflag && t == 0) dflag[grow] = valid ? kRowAll : kRowEmpty;
     return;
   }
   const bool want_mask = dmask != nullptr && n <= lim;
-  if (dflag && t == 0) dflag[grow] = want_mask ? 1 : 0;
+  if (dflag && t == 0) dflag[grow] = want_mask ? kRowMasked : kRowGather;
   const int m = 256 * ((n + 1023) >> 10);  // positions per wave segment
   const int nch = m >> 8;                   // chunks per lane, 1..B4_CH
   const int seg = wv * m;

@@ -185,6 +185,10 @@ FUSED_CASES = {
     # one split: the Top-K kernel writes the tile path's flags and masks; rows
     # p < 256 keep everything, 256 <= p < 1024 take masked tiles, the rest gather
     "tile_masks_from_topk": (MED.replace(Tq=2048, Tk=2048, K=256), {}),
+    # histories no longer than 4K: every row, the empty ones included, is written
+    # by the tile kernel and the gather kernel is not launched
+    "tile_only_with_empty_rows": (MED.replace(B=2, Tq=64, Tk=128, K=32),
+                                  dict(q_offset=[64, 0], kv_len=[100, 50])),
 }
 
 
