@@ -208,7 +208,7 @@ enum {
   LCI_KERNEL_ATTN_DENSE = 3,  /* masked attention over contiguous key tiles          */
   LCI_KERNEL_ATTN_GATHER = 4, /* attention over gathered selected keys              */
   LCI_KERNEL_ATTN_COMBINE = 5,/* fixed-order merge of split-K partial results        */
-  LCI_KERNEL_DEC_INIT = 6,    /* decode: clear histograms and counters              */
+  LCI_KERNEL_DEC_THRESH = 6,  /* decode: histogram bin of the K-th largest score    */
   LCI_KERNEL_DEC_SCORE = 7,   /* decode: scores + score histogram per history chunk */
   LCI_KERNEL_DEC_CAND = 8,    /* decode: candidates at or above the threshold bin   */
   LCI_KERNEL_DEC_RESOLVE = 9, /* decode: exact K-th score among the candidates      */

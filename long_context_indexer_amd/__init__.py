@@ -29,7 +29,7 @@ EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefi
 
 # kernel kinds of the timing log (LCI_KERNEL_* in lci.h)
 KERNELS = ("idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
-           "dec_init", "dec_score", "dec_cand", "dec_resolve", "dec_compact")
+           "dec_thresh", "dec_score", "dec_cand", "dec_resolve", "dec_compact")
 
 
 class LciError(RuntimeError):

@@ -9,17 +9,16 @@
 // keys and values per query.
 //
 // With one query per sequence the parallelism comes from splitting the history:
-//   dec_init     zero the per-sequence histograms and counters;
 //   dec_score    (chunks x B) int8-MFMA scores of 4096 positions per workgroup,
-//                written to workspace, and a 2048-bin histogram over a monotone
-//                float-like binning of the int32 score (exponent + 5 mantissa
-//                bits, both signs), built in LDS and added to the sequence's
-//                global histogram with integer atomics (order-free: exact);
-//   dec_cand     (chunks x B) every workgroup finds the bin b* holding the K-th
-//                largest score from the histogram, counts its positions above b*
-//                and appends the (score, position) pairs inside b* to a
-//                per-sequence candidate list;
-//   dec_resolve  (B) selects inside the candidates the exact K-th score v* and
+//                written to workspace, and the chunk's 2048-bin histogram over a
+//                monotone float-like binning of the int32 score (exponent + 5
+//                mantissa bits, both signs), built in LDS and stored whole;
+//   dec_thresh   (B) sums the chunk histograms, then finds the bin b* holding
+//                the K-th largest score and the count of positions above it;
+//   dec_cand     (chunks x B) every workgroup counts its positions above b*
+//                and writes the (score, position) pairs inside b* to its own
+//                slice of the sequence's candidate list;
+//   dec_resolve  (B) gathers the candidate slices, selects the exact K-th score v* and
 //                the position cut s* that keeps the lowest-position ties, then
 //                turns per-chunk counts into output offsets (a candidate list
 //                that overflows its capacity falls back to the exact one-workgroup
@@ -94,10 +93,48 @@ __device__ __forceinline__ int find_bin(const uint32_t* __restrict__ hist, uint3
   return bstar;
 }
 
-__global__ void dec_init_kernel(int B, uint32_t* __restrict__ hist, uint32_t* __restrict__ ncand) {
+// One workgroup per sequence: sums the per-chunk histograms, then finds the
+// bin b* holding the K-th largest score and the count of positions in higher
+// bins, read by the candidate and resolve kernels.
+__global__ __launch_bounds__(DEC_NT) void dec_thresh_kernel(
+    int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
+    const uint32_t* __restrict__ chist, int nchunks, uint32_t* __restrict__ bsel) {
+  __shared__ uint32_t h[DEC_BINS];
+  __shared__ uint32_t scratch[DEC_NT / 64 + 2];
+  __shared__ uint32_t found[2];
   const int b = blockIdx.x;
-  for (int j = threadIdx.x; j < DEC_BINS; j += blockDim.x) hist[b * DEC_BINS + j] = 0u;
-  if (threadIdx.x == 0) ncand[b] = 0u;
+  const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
+  if (rw.n <= K) return;
+  const int nc = static_cast<int>((rw.n + kDecChunk - 1) / kDecChunk);  // chunks with positions
+  const uint32_t* hb = chist + static_cast<int64_t>(b) * nchunks * DEC_BINS + threadIdx.x;
+  // thread t sums bins t + 256 i over the chunks, four chunks per round so
+  // 32 independent loads are in flight
+  constexpr int BPT = DEC_BINS / DEC_NT;
+  uint32_t acc[BPT] = {};
+  int c = 0;
+  for (; c + 4 <= nc; c += 4) {
+    uint32_t v[4][BPT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) v[u][i] = hb[static_cast<int64_t>(c + u) * DEC_BINS + i * DEC_NT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) acc[i] += v[u][i];
+  }
+  for (; c < nc; ++c)
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) acc[i] += hb[static_cast<int64_t>(c) * DEC_BINS + i * DEC_NT];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) h[threadIdx.x + i * DEC_NT] = acc[i];
+  __syncthreads();
+  uint32_t above;
+  const int bstar = find_bin(h, K, scratch, found, &above);
+  if (threadIdx.x == 0) {
+    bsel[2 * b] = static_cast<uint32_t>(bstar);
+    bsel[2 * b + 1] = above;
+  }
 }
 
 // Scoring uses v_mfma_i32_16x16x64_i8 with the history positions as the 16
@@ -115,7 +152,7 @@ __global__ __launch_bounds__(DEC_NT) void dec_score_kernel(
     int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
     const int8_t* __restrict__ w, int64_t wsb, int32_t* __restrict__ S,
-    uint32_t* __restrict__ hist) {
+    uint32_t* __restrict__ chist) {
   constexpr int NCH = D_I / 64 > 0 ? D_I / 64 : 1;  // 64-deep MFMA steps
   constexpr int U = 4;                             // 16-position tiles per step
   constexpr int STEP = 16 * U;
@@ -200,28 +237,29 @@ __global__ __launch_bounds__(DEC_NT) void dec_score_kernel(
     atomicAdd(&lh[score_bin(sv)], 1u);
   }
   __syncthreads();
-  uint32_t* hb = hist + static_cast<int64_t>(b) * DEC_BINS;
-  for (int j = threadIdx.x; j < DEC_BINS; j += DEC_NT)
-    if (lh[j]) atomicAdd(&hb[j], lh[j]);
+  // this chunk's histogram, stored whole (no cross-workgroup atomics)
+  uint32_t* hb = chist + (static_cast<int64_t>(b) * gridDim.x + blockIdx.x) * DEC_BINS;
+  for (int j = threadIdx.x; j < DEC_BINS; j += DEC_NT) hb[j] = lh[j];
 }
 
 __global__ __launch_bounds__(DEC_NT) void dec_cand_kernel(
     int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ S, const uint32_t* __restrict__ hist, uint32_t* __restrict__ ncand,
+    const int32_t* __restrict__ S, const uint32_t* __restrict__ bsel, uint32_t* __restrict__ ncand,
     int2* __restrict__ cand, uint32_t* __restrict__ ngt, int nchunks) {
   constexpr int E = kDecChunk / DEC_NT;
   __shared__ uint32_t scratch[DEC_NT / 64 + 2];
-  __shared__ uint32_t found[2];
-  __shared__ uint32_t slot_base;
   const int b = blockIdx.y;
   const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kDecChunk;
+  const int64_t ci = static_cast<int64_t>(b) * nchunks + blockIdx.x;
   if (rw.n <= K || base >= rw.n) {
-    if (threadIdx.x == 0) ngt[static_cast<int64_t>(b) * nchunks + blockIdx.x] = 0u;
+    if (threadIdx.x == 0) {
+      ngt[ci] = 0u;
+      ncand[ci] = 0u;
+    }
     return;
   }
-  uint32_t above;
-  const int bstar = find_bin(hist + static_cast<int64_t>(b) * DEC_BINS, K, scratch, found, &above);
+  const int bstar = static_cast<int>(bsel[2 * b]);
   const int64_t nend = min(base + kDecChunk, rw.n);
   const int32_t* Sb = S + static_cast<int64_t>(b) * Tk;
   // element e of this thread: position base + e*DEC_NT + tid (coalesced)
@@ -243,17 +281,16 @@ __global__ __launch_bounds__(DEC_NT) void dec_cand_kernel(
   uint32_t tot_g;
   block_excl_scan(gt, scratch, &tot_g);
   if (threadIdx.x == 0) {
-    slot_base = tot_c ? atomicAdd(&ncand[b], tot_c) : 0u;
-    ngt[static_cast<int64_t>(b) * nchunks + blockIdx.x] = tot_g;
+    ncand[ci] = tot_c;
+    ngt[ci] = tot_g;
   }
-  __syncthreads();
-  uint32_t slot = slot_base + ex;
-  int2* cb = cand + static_cast<int64_t>(b) * kDecCap;
+  // this chunk's candidates, in its own slice of the list (at most kDecChunk)
+  uint32_t slot = ex;
+  int2* cb = cand + ci * kDecChunk;
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (cmask & (1u << e)) {
-      if (slot < static_cast<uint32_t>(kDecCap))
-        cb[slot] = make_int2(val[e], static_cast<int>(base + e * DEC_NT + threadIdx.x));
+      cb[slot] = make_int2(val[e], static_cast<int>(base + e * DEC_NT + threadIdx.x));
       ++slot;
     }
 }
@@ -321,7 +358,7 @@ __device__ uint32_t lds_kth_largest(int n, uint32_t k, F keyf, uint32_t* hist, u
 
 __global__ __launch_bounds__(TOPK_NT) void dec_resolve_kernel(
     int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ S, const uint32_t* __restrict__ hist,
+    const int32_t* __restrict__ S, const uint32_t* __restrict__ bsel,
     const uint32_t* __restrict__ ncand, const int2* __restrict__ cand,
     const uint32_t* __restrict__ ngt, uint32_t* __restrict__ off, int nchunks,
     int32_t* __restrict__ thr, int32_t* __restrict__ idx) {
@@ -329,7 +366,6 @@ __global__ __launch_bounds__(TOPK_NT) void dec_resolve_kernel(
   __shared__ int cval[kDecCap];
   __shared__ int cpos[kDecCap];
   __shared__ uint32_t ccount[kDecMaxChunks];
-  __shared__ uint32_t bc[4];
   const int b = blockIdx.x;
   const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
   int32_t* out = idx + static_cast<int64_t>(b) * K;
@@ -339,39 +375,42 @@ __global__ __launch_bounds__(TOPK_NT) void dec_resolve_kernel(
     if (threadIdx.x == 0) th[0] = 0;
     return;
   }
-  const uint32_t nc = ncand[b];
+  // per-chunk candidate counts -> where each chunk's candidates go in LDS
+  const int nch = static_cast<int>((rw.n + kDecChunk - 1) / kDecChunk);
+  const uint32_t* cn = ncand + static_cast<int64_t>(b) * nchunks;
+  for (int c = threadIdx.x; c < nch; c += TOPK_NT) ccount[c] = cn[c];
+  __syncthreads();
+  uint32_t nc = 0;
+  for (int c0 = 0; c0 < nch; c0 += TOPK_NT) {
+    const int c = c0 + threadIdx.x;
+    const uint32_t v = c < nch ? ccount[c] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(v, sm.scratch, &tot);
+    if (c < nch) ccount[c] = nc + ex;  // exclusive start of chunk c
+    nc += tot;
+  }
+  __syncthreads();
   if (nc > static_cast<uint32_t>(kDecCap)) {
     // too many equal-bin candidates for LDS: exact selection over the whole row
     select_row(S + static_cast<int64_t>(b) * Tk, rw.n, K, out, nullptr, sm);
     if (threadIdx.x == 0) th[0] = 0;
     return;
   }
-  // count above the candidate bin (same histogram walk as the candidate kernel)
-  constexpr int BPT = DEC_BINS / TOPK_NT;
-  const uint32_t* hb = hist + static_cast<int64_t>(b) * DEC_BINS;
+  // positions in bins above the candidate bin are all kept
+  const uint32_t krem = static_cast<uint32_t>(K) - bsel[2 * b + 1];
+  // gather the chunks' lists: one wave per chunk at a time
   {
-    uint32_t c[BPT];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int e = 0; e < BPT; ++e) {
-      c[e] = hb[DEC_BINS - 1 - BPT * static_cast<int>(threadIdx.x) - e];
-      sum += c[e];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    for (int c = wv; c < nch; c += TOPK_NT / 64) {
+      const uint32_t start = ccount[c];
+      const uint32_t cnt = (c + 1 < nch ? ccount[c + 1] : nc) - start;
+      const int2* cb = cand + (static_cast<int64_t>(b) * nchunks + c) * kDecChunk;
+      for (uint32_t j = lane; j < cnt; j += 64) {
+        const int2 cv = cb[j];
+        cval[start + j] = cv.x;
+        cpos[start + j] = cv.y;
+      }
     }
-    uint32_t tot;
-    uint32_t above = block_excl_scan(sum, sm.scratch, &tot);
-#pragma unroll
-    for (int e = 0; e < BPT; ++e) {
-      if (above < static_cast<uint32_t>(K) && static_cast<uint32_t>(K) <= above + c[e]) bc[0] = above;
-      above += c[e];
-    }
-    __syncthreads();
-  }
-  const uint32_t krem = static_cast<uint32_t>(K) - bc[0];
-  const int2* cb = cand + static_cast<int64_t>(b) * kDecCap;
-  for (int j = threadIdx.x; j < static_cast<int>(nc); j += TOPK_NT) {
-    const int2 c = cb[j];
-    cval[j] = c.x;
-    cpos[j] = c.y;
   }
   __syncthreads();
   const int n = static_cast<int>(nc);
@@ -486,12 +525,13 @@ DecLayout decode_layout(const Geom& g) {
   L.nchunks = static_cast<int>((static_cast<int64_t>(g.Tk) + kDecChunk - 1) / kDecChunk);
   size_t o = 0;
   L.scores = o;  o += al(static_cast<size_t>(g.B) * g.Tk * sizeof(int32_t));
-  L.hist = o;    o += al(static_cast<size_t>(g.B) * DEC_BINS * sizeof(uint32_t));
-  L.ncand = o;   o += al(static_cast<size_t>(g.B) * sizeof(uint32_t));
-  L.cand = o;    o += al(static_cast<size_t>(g.B) * kDecCap * sizeof(int2));
+  L.hist = o;    o += al(static_cast<size_t>(g.B) * L.nchunks * DEC_BINS * sizeof(uint32_t));
+  L.ncand = o;   o += al(static_cast<size_t>(g.B) * L.nchunks * sizeof(uint32_t));
+  L.cand = o;    o += al(static_cast<size_t>(g.B) * L.nchunks * kDecChunk * sizeof(int2));
   L.ngt = o;     o += al(static_cast<size_t>(g.B) * L.nchunks * sizeof(uint32_t));
   L.off = o;     o += al(static_cast<size_t>(g.B) * L.nchunks * sizeof(uint32_t));
   L.thr = o;     o += al(static_cast<size_t>(g.B) * 4 * sizeof(int32_t));
+  L.bsel = o;    o += al(static_cast<size_t>(g.B) * 2 * sizeof(uint32_t));
   L.idx = o;     o += al(static_cast<size_t>(g.B) * g.K * sizeof(int32_t));
   L.attn = o;
   L.splits = sparse_attn_pick_splits(g);
@@ -540,14 +580,10 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
   uint32_t* ngt = reinterpret_cast<uint32_t*>(ws + L.ngt);
   uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
   int32_t* thr = reinterpret_cast<int32_t*>(ws + L.thr);
+  uint32_t* bsel = reinterpret_cast<uint32_t*>(ws + L.bsel);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
 
-  {
-    KernelTimer timer(LCI_KERNEL_DEC_INIT, st);
-    hipLaunchKernelGGL(dec_init_kernel, dim3(g.B), dim3(256), 0, st, g.B, hist, ncand);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   switch (g.H_I) {
     case 1: e = launch_score_h<1>(g, q_idx, k_idx, w, wsb, S, hist, L.nchunks, st); break;
     case 2: e = launch_score_h<2>(g, q_idx, k_idx, w, wsb, S, hist, L.nchunks, st); break;
@@ -558,15 +594,21 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
   }
   if (e != hipSuccess) return e;
   {
+    KernelTimer timer(LCI_KERNEL_DEC_THRESH, st);
+    hipLaunchKernelGGL(dec_thresh_kernel, dim3(g.B), dim3(DEC_NT), 0, st, g.Tk, g.K, g.q_offset,
+                       g.kv_len, hist, L.nchunks, bsel);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
     KernelTimer timer(LCI_KERNEL_DEC_CAND, st);
     hipLaunchKernelGGL(dec_cand_kernel, dim3(L.nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk, g.K,
-                       g.q_offset, g.kv_len, S, hist, ncand, cand, ngt, L.nchunks);
+                       g.q_offset, g.kv_len, S, bsel, ncand, cand, ngt, L.nchunks);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     KernelTimer timer(LCI_KERNEL_DEC_RESOLVE, st);
     hipLaunchKernelGGL(dec_resolve_kernel, dim3(g.B), dim3(TOPK_NT), 0, st, g.Tk, g.K, g.q_offset,
-                       g.kv_len, S, hist, ncand, cand, ngt, off, L.nchunks, thr, idx);
+                       g.kv_len, S, bsel, ncand, cand, ngt, off, L.nchunks, thr, idx);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {

@@ -44,9 +44,9 @@ struct AttnCfg {
 // Merge the splits of one query row in split order (fixed, so deterministic),
 // apply the gate and store. A kernel of its own: on a multi-XCD part, handing
 // partials from workgroup to workgroup inside one kernel needs an L2 write-back
-// per workgroup, a kernel boundary needs one. Thread t owns 4 consecutive
-// features of one (row, head) and reads every split's (m, l) and its 4 partial
-// features; the loads of different splits are independent, so they overlap.
+// per workgroup, a kernel boundary needs one. Thread t owns 2 consecutive
+// features of one (row, head) and merges the splits in one pass with a running
+// maximum; the loads of different splits are independent, so they overlap.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(int Hq, int splits,
                                                            const float* __restrict__ part,
@@ -54,38 +54,42 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(int Hq, int splits,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ lse) {
   using C = AttnCfg<D>;
-  constexpr int QPH = D / 4;  // threads per head
+  constexpr int QPH = D / 2;  // threads per head
   const int64_t qrow = blockIdx.x;
   const int t = blockIdx.y * blockDim.x + threadIdx.x;
   if (t >= Hq * QPH) return;
   const int h = t / QPH;
-  const int j0 = 4 * (t % QPH);
+  const int j0 = 2 * (t % QPH);
   const float* pp = part + (qrow * Hq + h) * splits * C::PART;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pp[s * C::PART + D]);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f, Lex = 0.f;
+  float M = -INFINITY, L = 0.f, Lex = 0.f;
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll 4
   for (int s = 0; s < splits; ++s) {
     const float* ps = pp + s * C::PART;
     const float ms = ps[D];
-    const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    L += wgt * ps[D + 1];
-    Lex += wgt * ps[D + 2];
-    acc += wgt * *reinterpret_cast<const v4f*>(ps + j0);
+    const float2 os = *reinterpret_cast<const float2*>(ps + j0);
+    const float ls = ps[D + 1], lxs = ps[D + 2];
+    const float Mn = fmaxf(M, ms);
+    // weights relative to the running maximum; a split without entries (-inf)
+    // contributes nothing, and nothing is rescaled while M is still -inf
+    const float fo = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+    const float fs = (ms == -INFINITY) ? 0.f : fast_exp2(ms - Mn);
+    a0 = a0 * fo + fs * os.x;
+    a1 = a1 * fo + fs * os.y;
+    L = L * fo + fs * ls;
+    Lex = Lex * fo + fs * lxs;
+    M = Mn;
   }
   const float inv = L > 0.f ? fast_rcp(L) : 0.f;
   const int64_t obase = (qrow * Hq + h) * D + j0;
-  uint16_t ys[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float y = acc[e] * inv;
-    if (gate) y *= sigmoidf(bf16_to_f32(gate[obase + e]));
-    ys[e] = f32_to_bf16(y);
+  float y0 = a0 * inv, y1 = a1 * inv;
+  if (gate) {
+    const uint32_t g01 = *reinterpret_cast<const uint32_t*>(gate + obase);
+    y0 *= sigmoidf(bf16_to_f32(g01 & 0xffff));
+    y1 *= sigmoidf(bf16_to_f32(g01 >> 16));
   }
-  *reinterpret_cast<int2*>(out + obase) =
-      make_int2(static_cast<int>(ys[0] | (static_cast<uint32_t>(ys[1]) << 16)),
-                static_cast<int>(ys[2] | (static_cast<uint32_t>(ys[3]) << 16)));
+  *reinterpret_cast<uint32_t*>(out + obase) =
+      f32_to_bf16(y0) | (static_cast<uint32_t>(f32_to_bf16(y1)) << 16);
   if (lse && j0 == 0) lse[qrow * Hq + h] = Lex > 0.f ? (M + fast_log2(Lex)) * LN2 : -INFINITY;
 }
 
@@ -342,7 +346,7 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  dim3 cgrid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq), (g.Hq * (D / 4) + 255) / 256);
+  dim3 cgrid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq), (g.Hq * (D / 2) + 255) / 256);
   {
     KernelTimer timer(LCI_KERNEL_ATTN_COMBINE, st);
     hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(256), 0, st, g.Hq, splits,

@@ -75,7 +75,7 @@ void clear(Log& l) {
 
 const char* const kNames[LCI_KERNEL_COUNT] = {
     "idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
-    "dec_init", "dec_score", "dec_cand", "dec_resolve", "dec_compact"};
+    "dec_thresh", "dec_score", "dec_cand", "dec_resolve", "dec_compact"};
 
 }  // namespace
 
