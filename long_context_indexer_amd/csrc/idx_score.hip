@@ -59,12 +59,16 @@ __global__ __launch_bounds__(256) void idx_score_kernel(
     const int ha = slot % H_I;
     const int lr = r0 + qa;
     const bool ok = lr < row_count && row_begin + lr < Tq;
-    const int8_t* src = q_idx + ((static_cast<int64_t>(b) * Tq + row_begin + lr) * H_I + ha) * D_I +
+    // unconditional loads (rows past the end read row begin, then zeroed), so
+    // they are all in flight together
+    const int lrc = ok ? lr : 0;
+    const int8_t* src = q_idx + ((static_cast<int64_t>(b) * Tq + row_begin + lrc) * H_I + ha) * D_I +
                         16 * (lane >> 5);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      v4i z = {0, 0, 0, 0};
-      a[c] = ok ? *reinterpret_cast<const v4i*>(src + 32 * c) : z;
+      const v4i t = *reinterpret_cast<const v4i*>(src + 32 * c);
+      const v4i z = {0, 0, 0, 0};
+      a[c] = ok ? t : z;
     }
   }
   // weights and positions of this lane's output rows (lane half l/32)
@@ -79,21 +83,23 @@ __global__ __launch_bounds__(256) void idx_score_kernel(
     const int64_t p = static_cast<int64_t>(qoff) + row;
     prow[qq] = (ok && p >= 0 && p < kvl) ? static_cast<int>(p) : -1;
     orow[qq] = (static_cast<int64_t>(b) * row_count + lr) * row_stride;
+    const int64_t wrow = b * wsb + static_cast<int64_t>(ok ? row : row_begin) * wsq;
 #pragma unroll
-    for (int h = 0; h < H_I; ++h)
-      wv[qq * H_I + h] = ok ? static_cast<int>(w[b * wsb + static_cast<int64_t>(row) * wsq + h]) : 0;
+    for (int h = 0; h < H_I; ++h) {
+      const int wt = static_cast<int>(w[wrow + h]);
+      wv[qq * H_I + h] = ok ? wt : 0;
+    }
   }
 
   const int8_t* kbase = k_idx + static_cast<int64_t>(b) * Tk * D_I + 16 * (lane >> 5);
   for (int kt = k_begin + wk * 32; kt < k_end; kt += 32 * WK) {
     const int key = kt + (lane & 31);
+    // keys past the history read the last valid row; their scores are never stored
+    const int keyc = min(key, kvl - 1);
     v4i bf[NCH];
-    const bool kok = key < kvl;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      v4i z = {0, 0, 0, 0};
-      bf[c] = kok ? *reinterpret_cast<const v4i*>(kbase + static_cast<int64_t>(key) * D_I + 32 * c) : z;
-    }
+    for (int c = 0; c < NCH; ++c)
+      bf[c] = *reinterpret_cast<const v4i*>(kbase + static_cast<int64_t>(keyc) * D_I + 32 * c);
     v16i acc = {};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c], bf[c], acc, 0, 0, 0);
