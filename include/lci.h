@@ -99,9 +99,9 @@ enum {
 };
 
 /* Indexer scoring (step 1). "Hybrid Sparse Attention ...", section "Indexer +
- * Top-K ...", step 1 and pseudocode line "indexer_score(q, k)"; "Optimizing ...",
- * section "Two Engineering Considerations", item 1 (a light scorer over
- * low-dimensional projections).
+ * Top-K ...", step 1 and the scoring step of its pseudocode; "Optimizing ...",
+ * section "Two Engineering Considerations", item 1 (the scorer must stay cheap:
+ * few heads of low dimension).
  *   q_idx  int8 [B, Tq, H_I, d_I]
  *   k_idx  int8 [B, Tk, d_I]
  *   w      int8, element (b, i, h) at w[b*w_stride_b + i*w_stride_q + h];
@@ -113,9 +113,9 @@ lci_status lci_idx_score(const lci_geom *g, const int8_t *q_idx, const int8_t *k
                          const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
                          int32_t *scores, void *stream);
 
-/* Top-K selection (step 2). "Hybrid Sparse Attention ...", step 2 and pseudocode
- * line "topk(s, top_k)"; "Optimizing ...", section "Interface Design", line
- * "topk(index_score, k=top_k, dim=-1)".
+/* Top-K selection (step 2). "Hybrid Sparse Attention ...", step 2 and the
+ * selection step of its pseudocode; "Optimizing ...", section "Interface
+ * Design" (Top-K over the last, position axis of each score row).
  *   scores     int32 [B, Tq, Tk]: only s <= p of each row is read
  *   idx        int32 [B, Tq, K] out: selected positions ascending, -1 padded
  *   sel_scores int32 [B, Tq, K] out, nullable: the score of each idx entry,
@@ -127,8 +127,10 @@ lci_status lci_topk_select(const lci_geom *g, const int32_t *scores, int32_t *id
                            void *stream);
 
 /* Sparse exact attention + sigmoid gate (steps 3-4). "Hybrid Sparse Attention
- * ...", steps 3-4 and pseudocode lines "softmax(q @ k_sel^T / d**0.5) @ v_sel",
- * "g * o_sparse"; "From Linear Attention ...", section 2, "gate(q) * out".
+ * ...", steps 3-4 and the attention and gating steps of its pseudocode (softmax
+ * of the 1/sqrt(d)-scaled dot products with the selected keys, weighting the
+ * selected values; the gate multiplies the result); "From Linear Attention
+ * ...", section 2 (a query-dependent gate multiplies the attention output).
  *   q, gate  bf16 [B, Tq, Hq, d]; gate nullable (ungated)
  *   k, v     bf16 [B, Tk, Hkv, d]; query head h reads key/value head h / (Hq/Hkv)
  *   idx      int32 [B, Tq, K]: positions to attend; entries outside 0..kv_len[b]-1
