@@ -121,6 +121,20 @@ class Timer:
         return s.elapsed_time(e) / iters
 
 
+def copy_calibration():
+    """A plain device-to-device copy of 2 GiB, five times: under rocprofv3 --pmc
+    FETCH_SIZE / WRITE_SIZE it gives the factor between each counter and the bytes
+    a kernel really reads and writes."""
+    import torch
+    n = 2 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+
+
 def timed_region(timer, step, steps, lci):
     """Time `steps` steps (wall clock and stream events around the whole region),
     then run `steps` more with the library's per-kernel event log switched on
@@ -204,7 +218,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run only one fused step kind (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 2 GiB device buffer 5 times (HBM counter calibration runs)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for {args.gpus}); the "
               "multi-GPU split of the path is a design note, not a runnable mode", file=sys.stderr)
