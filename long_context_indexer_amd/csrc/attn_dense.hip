@@ -399,6 +399,16 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   if (!rv || fl == kRowGather) return;  // an empty row (nothing kept) writes 0 and -inf
   const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
   const int64_t obase = (qrow * Hq + h) * D;
+  // every gate load is issued before any is used (one memory latency, not one
+  // per 8-byte piece); bf16 0 = logit 0 is never read without a gate
+  v2i graw[C::NDT][4] = {};
+  if (gate) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        graw[dt][ii] = *reinterpret_cast<const v2i*>(gate + obase + 32 * dt + 8 * ii + 4 * hf);
+  }
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -406,11 +416,12 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
       const int d = 32 * dt + 8 * ii + 4 * hf;
       float gv[4] = {1.f, 1.f, 1.f, 1.f};
       if (gate) {
-        const int2 graw = *reinterpret_cast<const int2*>(gate + obase + d);
-        gv[0] = sigmoidf(bf16_to_f32(static_cast<uint32_t>(graw.x) & 0xffff));
-        gv[1] = sigmoidf(bf16_to_f32(static_cast<uint32_t>(graw.x) >> 16));
-        gv[2] = sigmoidf(bf16_to_f32(static_cast<uint32_t>(graw.y) & 0xffff));
-        gv[3] = sigmoidf(bf16_to_f32(static_cast<uint32_t>(graw.y) >> 16));
+        const uint32_t g01 = static_cast<uint32_t>(graw[dt][ii].x);
+        const uint32_t g23 = static_cast<uint32_t>(graw[dt][ii].y);
+        gv[0] = sigmoidf(bf16_to_f32(g01 & 0xffff));
+        gv[1] = sigmoidf(bf16_to_f32(g01 >> 16));
+        gv[2] = sigmoidf(bf16_to_f32(g23 & 0xffff));
+        gv[3] = sigmoidf(bf16_to_f32(g23 >> 16));
       }
       const uint32_t w0 = f32_to_bf16(o[dt][4 * ii] * inv * gv[0]) |
                           (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * ii + 1] * inv * gv[1])) << 16);

@@ -278,12 +278,17 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   {
     const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
     const int64_t obase = (qrow * Hq + h) * D + 4 * grp;
+    // all gate loads in flight together (one memory latency)
+    v2i gl[C::NJB] = {};
+    if (gate) {
+#pragma unroll
+      for (int jb = 0; jb < C::NJB; ++jb) gl[jb] = *reinterpret_cast<const v2i*>(gate + obase + 16 * jb);
+    }
 #pragma unroll
     for (int jb = 0; jb < C::NJB; ++jb) {
       float gv[4] = {1.f, 1.f, 1.f, 1.f};
       if (gate) {
-        const int2 graw = *reinterpret_cast<const int2*>(gate + obase + 16 * jb);
-        const uint32_t g01 = static_cast<uint32_t>(graw.x), g23 = static_cast<uint32_t>(graw.y);
+        const uint32_t g01 = static_cast<uint32_t>(gl[jb].x), g23 = static_cast<uint32_t>(gl[jb].y);
         gv[0] = sigmoidf(bf16_to_f32(g01 & 0xffff));
         gv[1] = sigmoidf(bf16_to_f32(g01 >> 16));
         gv[2] = sigmoidf(bf16_to_f32(g23 & 0xffff));
