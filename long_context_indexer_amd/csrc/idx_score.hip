@@ -115,11 +115,130 @@ __global__ __launch_bounds__(256) void idx_score_kernel(
   }
 }
 
+// Per-head weights shared by every row (the workloads' [H_I] vector). MFMA
+// v_mfma_i32_16x16x64_i8 with the 16 history positions of a tile as the A rows
+// and 16 query rows as the B columns, one head per MFMA: lane l's 4
+// accumulators are positions 4(l/16)+i of query row l%16, so the weighted ReLU
+// sum over heads accumulates in place (2 VALU per head per output, no per-row
+// weights) and each lane stores 4 consecutive positions of its row at once.
+// A wave scores 16 query rows against 2 tiles (32 positions) per step; the key
+// fragments of the next step are loaded while this one is scored.
+template <int H_I, int D_I>
+__global__ __launch_bounds__(256, 5) void idx_score_q16_kernel(
+    int Tq, int Tk, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
+    const int8_t* __restrict__ w, int32_t* __restrict__ scores, int64_t row_stride,
+    int row_begin, int row_count, int keys_per_wg) {
+  constexpr int NCH = D_I / 64;  // 64-deep MFMA steps over d_I
+  constexpr int U = 2;           // 16-position tiles per step
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int b = blockIdx.z;
+  const int r0 = (blockIdx.y * 4 + wv) * 16;  // first local row of this wave
+  if (r0 >= row_count) return;
+  const int qoff = q_offset[b];
+  const int kvl = kv_len[b];
+  if (kvl > Tk || kvl <= 0) return;  // invalid sequence: nothing is written
+  // last history position any row of this wave may read
+  const int pmax = static_cast<int>(min(static_cast<int64_t>(qoff) + row_begin + r0 + 15,
+                                        static_cast<int64_t>(kvl) - 1));
+  const int k_begin = blockIdx.x * keys_per_wg;
+  const int k_end = min(k_begin + keys_per_wg, pmax + 1);
+  if (k_begin >= k_end) return;
+
+  // B operands: query row r0 + l%16 of every head, k-bytes 16*(l/16) of each step
+  const int lr = r0 + (lane & 15);
+  const bool rok = lr < row_count && row_begin + lr < Tq;
+  v4i bq[H_I][NCH];
+  {
+    const int lrc = rok ? lr : r0;  // rows past the end read a valid row, then zeroed
+    const int8_t* src = q_idx + (static_cast<int64_t>(b) * Tq + row_begin + lrc) * H_I * D_I +
+                        16 * (lane >> 4);
+#pragma unroll
+    for (int h = 0; h < H_I; ++h)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const v4i t = *reinterpret_cast<const v4i*>(src + h * D_I + 64 * c);
+        const v4i z = {0, 0, 0, 0};
+        bq[h][c] = rok ? t : z;
+      }
+  }
+  int wh[H_I];
+#pragma unroll
+  for (int h = 0; h < H_I; ++h) wh[h] = static_cast<int>(w[h]);
+
+  // this lane's row and its causal limit (-1: the row has no position)
+  const int64_t p64 = static_cast<int64_t>(qoff) + row_begin + lr;
+  const int plim = (rok && p64 >= 0 && p64 < kvl) ? static_cast<int>(p64) : -1;
+  int32_t* orow = scores + (static_cast<int64_t>(b) * row_count + (rok ? lr : r0)) * row_stride;
+  const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && (row_stride & 3) == 0;
+
+  const int8_t* kbase = k_idx + static_cast<int64_t>(b) * Tk * D_I + 16 * (lane >> 4);
+  auto load_keys = [&](int kt, v4i (&dst)[U][NCH]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // past the history: a valid row, whose scores are never stored
+      const int keyc = min(kt + 16 * u + (lane & 15), kvl - 1);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        dst[u][c] = *reinterpret_cast<const v4i*>(kbase + static_cast<int64_t>(keyc) * D_I + 64 * c);
+    }
+  };
+  v4i ka[U][NCH];
+  load_keys(k_begin, ka);
+  for (int kt = k_begin; kt < k_end; kt += 16 * U) {
+    v4i kn[U][NCH];
+    load_keys(kt + 16 * U, kn);  // next step (clamped reads past the end are unused)
+    v4i sacc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) sacc[u] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < H_I; ++h)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[u][c], bq[h][c], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[u][i] += __mul24(wh[h], max(acc[i], 0));
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = kt + 16 * u + 4 * (lane >> 4);  // first of this lane's 4 positions
+      if (vec && key + 3 <= plim) {
+        *reinterpret_cast<v4i*>(orow + key) = sacc[u];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key + i <= plim) orow[key + i] = sacc[u][i];  // causal: s <= p
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) ka[u][c] = kn[u][c];
+  }
+}
+
 template <int H_I, int D_I>
 static hipError_t launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                             const int8_t* w, int64_t wsb, int64_t wsq, int32_t* scores,
                             int64_t stride, int row_begin, int row_count, hipStream_t st) {
   constexpr int QW = 32 / H_I;
+  if constexpr (D_I >= 64 && H_I * D_I <= 512) {
+    if (wsb == 0 && wsq == 0 && row_count >= 64) {
+      // shared head weights, many rows: 4 waves x 16 rows, 128 positions per
+      // workgroup (short workgroups, 5 waves per SIMD: the scoring is latency
+      // bound; on Prefill 8K 128 beat 64, 256 and 512)
+      const int keys = 128;
+      dim3 grid((g.Tk + keys - 1) / keys, (row_count + 63) / 64, g.B);
+      KernelTimer timer(LCI_KERNEL_IDX_SCORE, st);
+      hipLaunchKernelGGL((idx_score_q16_kernel<H_I, D_I>), grid, dim3(256), 0, st, g.Tq, g.Tk,
+                         g.q_offset, g.kv_len, q_idx, k_idx, w, scores, stride, row_begin,
+                         row_count, keys);
+      return hipGetLastError();
+    }
+  }
   if (row_count >= 4 * QW) {
     // many query rows: 4 waves on 4 row tiles share each key tile
     const int keys = 256;
