@@ -90,7 +90,8 @@ __global__ __launch_bounds__(256) void idx_mask_kernel(
   for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) tot += red[w];
   const uint8_t f = bad ? kRowGather : (tot == static_cast<uint32_t>(p + 1) ? kRowAll : kRowMasked);
   if (threadIdx.x == 0) flag[row] = f;
-  if (f == kRowMasked)
+  // a row that keeps all of 0..p has exactly those bits set
+  if (f != kRowGather)
     for (int w = threadIdx.x; w < Wm; w += blockDim.x) mask[row * Wm + w] = bits[w];
 }
 
@@ -146,12 +147,27 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
+// Lanes l and l^32 combined, with no LDS round trip: v_permlane32_swap of a
+// value with itself returns v[l % 32] in one result and v[l % 32 + 32] in the
+// other, on every lane.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Rows whose running max grows by less than this (log2 units) keep their
 // softmax offset: P stays <= 2^8, far from overflow, and the O and l rescale
 // is skipped for the whole wave unless some row needs it.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int G>
+// EXACT_L: the softmax denominator sums the fp32 probabilities (needed for the
+// log-sum-exp output). Otherwise it sums the bf16-rounded ones that enter the
+// PV product, two per dot-product instruction.
+template <int D, int G, bool EXACT_L>
 __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     int Tq, int Tk, int Hq, int Hkv, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
@@ -185,20 +201,21 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   if (all_ok == 0) return;
 
   const int qo = q_offset[b];
-  const int kvl = kv_len[b];
+  // a history longer than its allocation (every row of it is empty) reads no tile
+  const int kvl0 = kv_len[b];
+  const int kvl = __builtin_amdgcn_readfirstlane(kvl0 <= Tk ? max(kvl0, 0) : 0);
   // last key any row of the block reads (rows past the history read none)
   const int64_t p_last = min(static_cast<int64_t>(qo) + iend - 1, static_cast<int64_t>(kvl) - 1);
   const int nkb = p_last < 0 ? 0 : static_cast<int>(p_last / C::BK) + 1;
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int r = lane & 31;
   const int hf = lane >> 5;
   const int i = i0 + wv * C::TW + r / G;
   const int h = g * G + r % G;
   const bool rv = i < Tq;
   const int64_t qrow = static_cast<int64_t>(b) * Tq + (rv ? i : 0);
-  const int p = qo + i;
   const int fl = rv ? flag[qrow] : 0;
   const uint32_t* mrow = mask + qrow * Wm;
   // every row of this wave keeps all of 0..p (flag 2): tiles entirely at or
@@ -229,8 +246,11 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   constexpr int RPI = 64 / UPR;          // rows per wave load
   constexpr int NI = C::BK * UPR / 256;  // loads per wave per tile (K and V each)
   const int rowstep = Hkv * D;           // elements between consecutive keys
-  const uint16_t* kbase = k + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
-  const uint16_t* vbase = v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D;
+  // tile addresses and sizes are workgroup-uniform: kept in scalar registers
+  const uint16_t* kbase =
+      static_cast<const uint16_t*>(uniform_ptr(k + (static_cast<int64_t>(b) * Tk * Hkv + g) * D));
+  const uint16_t* vbase =
+      static_cast<const uint16_t*>(uniform_ptr(v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D));
   int voff[NI];
 #pragma unroll
   for (int c = 0; c < NI; ++c) {
@@ -239,11 +259,11 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     voff[c] = (row * rowstep + 8 * lu) * 2;
   }
   auto tile_rsrc = [&](const uint16_t* base, int kb) {
+    // key0 < kv_len for every tile loaded, so at least one key is valid
     const int key0 = kb * C::BK;
-    const int nvalid = max(0, min(kvl - key0, C::BK));
-    const int nbytes = __builtin_amdgcn_readfirstlane(nvalid * rowstep * 2);
-    return __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(base + static_cast<int64_t>(key0) * rowstep), 0, nbytes, kBufferFlags);
+    const int nvalid = min(kvl - key0, C::BK);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base) + static_cast<int64_t>(key0) * rowstep,
+                                             0, nvalid * rowstep * 2, kBufferFlags);
   };
   auto load_tile = [&](const uint16_t* base, int kb, uint16_t* dst) {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base, kb);
@@ -290,8 +310,10 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
 
   // pipeline: while tile kb is in softmax, the scores of tile kb+1 are computed
   // (their K is already in LDS) and V of kb+1 and K of kb+2 are in flight
-  load_tile(kbase, 0, ks[0]);
-  load_tile(vbase, 0, vsh[0]);
+  if (nkb > 0) {
+    load_tile(kbase, 0, ks[0]);
+    load_tile(vbase, 0, vsh[0]);
+  }
   if (nkb > 1) load_tile(kbase, 1, ks[1]);
   uint32_t mwc[2];
   mask_words(0, mwc);
@@ -307,17 +329,14 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     uint32_t mwn[2];
     mask_words(kb + 1, mwn);
 
-    // mask (selection bits, or causal for rows that keep everything)
+    // mask: the row's selection bits (all of 0..p for rows that keep everything)
     const int key0 = kb * C::BK;
     if (!(wave_all && key0 + C::BK - 1 <= p_wave_min)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int n = p - (key0 + 32 * kt) + 1;  // flag 2: keys key0+32kt .. p are kept
-        const uint32_t causal = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
-        uint32_t mw = fl == kRowAll ? causal : (fl == kRowMasked ? mwc[kt] : 0u);
-        // bit kofs(e) = 8(e/4) + 4hf + e%4 of mw keeps element e: a one-bit
-        // signed extract gives an all-ones/all-zeros select mask
-        mw >>= 4 * hf;
+        // bit kofs(e) = 8(e/4) + 4hf + e%4 of the word keeps element e: a
+        // one-bit signed extract gives an all-ones/all-zeros select mask
+        const uint32_t mw = mwc[kt] >> (4 * hf);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int sel = __builtin_amdgcn_sbfe(static_cast<int>(mw), 8 * (e >> 2) + (e & 3), 1);
@@ -332,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) mx = max3f(mx, sc[kt][e], sc[kt][e + 1]);
-    mx = __builtin_elementwise_maximum(mx, shfl_xor(mx, 32));
+    mx = max_xor32(mx);
     // lazy offset update: only rows whose max grew by kRescaleLog2 or more move
     // their offset (all rows start at -inf, so every row moves on its first
     // kept score); the rescale of O and l runs only if some row of the wave moved
@@ -363,9 +382,22 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pe = fast_exp2(__builtin_fmaf(sc[kt][e], scale_log2, -moff));
-        psum += pe;
+        if constexpr (EXACT_L) psum += pe;
         pb[2 * kt + (e >> 3)][e & 7] = static_cast<__bf16>(pe);
       }
+    if constexpr (!EXACT_L) {
+      const v2bf one2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+      float ps2 = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const v8bf x = pb[qq];
+        psum = __builtin_amdgcn_fdot2_f32_bf16(v2bf{x[0], x[1]}, one2, psum, false);
+        ps2 = __builtin_amdgcn_fdot2_f32_bf16(v2bf{x[2], x[3]}, one2, ps2, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(v2bf{x[4], x[5]}, one2, psum, false);
+        ps2 = __builtin_amdgcn_fdot2_f32_bf16(v2bf{x[6], x[7]}, one2, ps2, false);
+      }
+      psum += ps2;
+    }
     lsum += psum;
 
     // O^T += V^T P^T over the 64 keys, four 16-key steps
@@ -395,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     __syncthreads();
   }
 
-  lsum += shfl_xor(lsum, 32);
+  lsum = sum_xor32(lsum);
   if (!rv || fl == kRowGather) return;  // an empty row (nothing kept) writes 0 and -inf
   const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
   const int64_t obase = (qrow * Hq + h) * D;
@@ -462,8 +494,8 @@ DenseMasks dense_masks(const Geom& g, void* ws) {
   return d;
 }
 
-template <int D, int G>
-static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16_t* k,
+template <int D, int G, bool EXACT_L>
+static hipError_t launch_dense_k(const Geom& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const uint16_t* gate, float scale,
                                   uint16_t* out, float* lse, const DenseMasks& dm,
                                   hipStream_t st) {
@@ -474,11 +506,20 @@ static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16
   const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
   {
     KernelTimer timer(LCI_KERNEL_ATTN_DENSE, st);
-    hipLaunchKernelGGL((attn_dense_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_dense_kernel<D, G, EXACT_L>), dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, st,
                        g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, dm.mask,
                        dm.Wm, dm.flag, scale * LOG2E, out, lse, dm.done, nbps, nblk);
   }
   return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const uint16_t* gate, float scale,
+                                  uint16_t* out, float* lse, const DenseMasks& dm,
+                                  hipStream_t st) {
+  return lse ? launch_dense_k<D, G, true>(g, q, k, v, gate, scale, out, lse, dm, st)
+             : launch_dense_k<D, G, false>(g, q, k, v, gate, scale, out, lse, dm, st);
 }
 
 template <int D>

@@ -51,9 +51,10 @@ enum : uint8_t {
 };
 
 // Inputs of the dense-tile attention kernel, inside the sparse-attention
-// workspace: per-row bit masks over positions (Wm words a row), row flags
-// (kRow*) and per-token-block "done by the tile kernel" bytes. Rows qualify
-// when p + 1 <= lim.
+// workspace: per-row bit masks over positions (Wm words a row, written for
+// every row on the tile path: the selected positions, all of 0..p for kRowAll
+// rows, none for kRowEmpty rows), row flags (kRow*) and per-token-block "done
+// by the tile kernel" bytes. Rows qualify when p + 1 <= lim.
 struct DenseMasks {
   uint32_t* mask;
   uint8_t* flag;

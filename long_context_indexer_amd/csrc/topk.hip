@@ -138,6 +138,13 @@ __global__ __launch_bounds__(B4_NT) void topk_b4_kernel(
       if (outs) outs[j] = j < n ? S[j] : INT32_MIN;
     }
     if (dflag && t == 0) dflag[grow] = valid ? kRowAll : kRowEmpty;
+    if (dmask) {
+      // the tile path's mask: all of 0..n-1
+      for (int w = t; w < Wm; w += B4_NT) {
+        const int nb = n - 32 * w;
+        dmask[grow * Wm + w] = nb >= 32 ? 0xffffffffu : (nb <= 0 ? 0u : (1u << nb) - 1u);
+      }
+    }
     return;
   }
   const bool want_mask = dmask != nullptr && n <= lim;
