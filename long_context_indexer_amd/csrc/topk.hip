@@ -106,7 +106,27 @@ constexpr int B4_CH = kWaveTopkMax / 1024;  // chunks per lane
 constexpr int B4_NT = 256;
 constexpr int B4_STAGE = 4096;              // output row staging (K <= 4096)
 
-__global__ __launch_bounds__(B4_NT) void topk_b4_kernel(
+// Exclusive prefix sum over the four waves of a B4_NT-thread workgroup with a
+// single barrier; *total receives the workgroup sum. `red` (4 words) must not
+// be written again before a later barrier.
+__device__ __forceinline__ uint32_t scan_b4(uint32_t v, int wv, uint32_t* red, uint32_t* total) {
+  const uint32_t incl = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) red[wv] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = red[w];
+    before += w < wv ? x : 0u;
+    tot += x;
+  }
+  *total = tot;
+  return before + incl - v;
+}
+
+// Six workgroups per CU (80 VGPRs, 26 KiB of LDS each): latency of the
+// row's barriers and loads is hidden by the other rows on the CU.
+__global__ __launch_bounds__(B4_NT, 6) void topk_b4_kernel(
     int Tq, int Tk, int K, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ scores, int64_t stride,
     int row_begin, int row_count, int32_t* __restrict__ idx, int32_t* __restrict__ sel,
@@ -149,6 +169,8 @@ __global__ __launch_bounds__(B4_NT) void topk_b4_kernel(
   }
   const bool want_mask = dmask != nullptr && n <= lim;
   if (dflag && t == 0) dflag[grow] = want_mask ? kRowMasked : kRowGather;
+  // the histogram starts at zero; each radix pass leaves it zero again
+  for (int j = t; j < TOPK_BINS; j += B4_NT) hist[j] = 0u;
   const int m = 256 * ((n + 1023) >> 10);  // positions per wave segment
   const int nch = m >> 8;                   // chunks per lane, 1..B4_CH
   const int seg = wv * m;
@@ -214,8 +236,6 @@ __global__ __launch_bounds__(B4_NT) void topk_b4_kernel(
       shift -= nb;
       const uint32_t bmask = low_mask(nb);
       const int nbins = 1 << nb;
-      for (int j = t; j < nbins; j += B4_NT) hist[j] = 0u;
-      __syncthreads();
 #pragma unroll
       for (int c = 0; c < B4_CH; ++c)
         if (c < nch)
@@ -225,17 +245,22 @@ __global__ __launch_bounds__(B4_NT) void topk_b4_kernel(
             atomicAdd(&hist[hit ? static_cast<int>((u[c][e] >> shift) & bmask) : dummy], 1u);
           }
       __syncthreads();
-      // thread t owns the 8 bins nbins-1-8t-7 .. nbins-1-8t (from the top)
+      // thread t owns the 8 bins nbins-1-8t-7 .. nbins-1-8t (from the top); it
+      // reads them and sets them back to zero for the next pass
       const int bhi = nbins - 1 - 8 * t;
       uint32_t cnt[8];
       uint32_t sum = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        cnt[e] = bhi - e >= 0 ? hist[bhi - e] : 0u;
+        cnt[e] = 0u;
+        if (bhi - e >= 0) {
+          cnt[e] = hist[bhi - e];
+          hist[bhi - e] = 0u;
+        }
         sum += cnt[e];
       }
       uint32_t tot;
-      uint32_t above = block_excl_scan(sum, red, &tot);
+      uint32_t above = scan_b4(sum, wv, red, &tot);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (above < krem && krem <= above + cnt[e]) {
@@ -245,11 +270,12 @@ __global__ __launch_bounds__(B4_NT) void topk_b4_kernel(
         above += cnt[e];
       }
       __syncthreads();
+      // bc is read before this thread's next barrier; it is rewritten only
+      // after two more barriers
       const uint32_t bin = bc[0];
       krem -= bc[1];
       prefix |= bin << shift;
       mask |= bmask << shift;
-      __syncthreads();
     }
     vstar = prefix;
     r = krem;
