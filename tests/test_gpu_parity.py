@@ -215,6 +215,10 @@ DECODE_EDGE = {
     "heavy_ties": (dict(q_range=1), 30000),
     # another indexer shape, K larger than some histories
     "h2d32": (dict(H_I=2, d_I=32, K=300), 9000),
+    # a long history (66 chunks, a ragged last chunk)
+    "long_history": (dict(), 270000),
+    # the same with every score equal: the whole-row fallback over a long row
+    "long_history_all_equal": (dict(q_range=0), 270000),
 }
 
 
