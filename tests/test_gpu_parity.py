@@ -55,6 +55,12 @@ SCORE_CASES = {
     "h16d64_rowweights": (TINY.replace(H_I=16, d_I=64, B=2, Tq=70, Tk=333),
                           dict(q_offset=[0, 263], kv_len=[333, 333])),
     "decode_shape": (MED.replace(B=3, Tq=1, Tk=5000, decode=True), {}),
+    # int32 extremes: every int8 input at -128 and every weight at 127, at the
+    # largest indexer size (H_I*d_I = 1024: S = 16*127*64*128^2 = 2 130 706 432)
+    # and on the shared-weight MFMA layout (H_I*d_I = 512, 64+ rows)
+    "extreme_h16d64": (TINY.replace(H_I=16, d_I=64, Tq=64, Tk=200), {}),
+    "extreme_h8d128": (TINY.replace(H_I=8, d_I=128, Tq=40, Tk=100), {}),
+    "extreme_q16": (MED.replace(Tq=128, Tk=300), {}),
 }
 
 
@@ -68,6 +74,10 @@ def test_idx_score_bit_exact(lci, orc, name):
         inp["w"] = r.integers(-128, 128, size=(cfg.B, cfg.Tq, cfg.H_I)).astype(np.int8)
         inp["q_idx"] = r.integers(-128, 128, size=inp["q_idx"].shape).astype(np.int8)
         inp["k_idx"] = r.integers(-128, 128, size=inp["k_idx"].shape).astype(np.int8)
+    if name.startswith("extreme"):
+        inp["q_idx"][:] = -128
+        inp["k_idx"][:] = -128
+        inp["w"] = np.full(cfg.H_I, 127, np.int8)
     log(f"idx_score {name}: B={cfg.B} Tq={cfg.Tq} Tk={cfg.Tk} H_I={cfg.H_I} d_I={cfg.d_I}")
     d = to_device(inp)
     sentinel = torch.full((cfg.B, cfg.Tq, cfg.Tk), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
@@ -187,6 +197,8 @@ FUSED_CASES = {
     "tile_masks_from_topk": (MED.replace(Tq=2048, Tk=2048, K=256), {}),
     # histories no longer than 4K: every row, the empty ones included, is written
     # by the tile kernel and the gather kernel is not launched
+    # the largest K, on rows that keep 68-72% of their history (tile path)
+    "k_max": (MED.replace(Tq=300, Tk=6000, K=4096), dict(q_offset=[5700])),
     "tile_only_with_empty_rows": (MED.replace(B=2, Tq=64, Tk=128, K=32),
                                   dict(q_offset=[64, 0], kv_len=[100, 50])),
 }
@@ -215,6 +227,8 @@ DECODE_EDGE = {
     "heavy_ties": (dict(q_range=1), 30000),
     # another indexer shape, K larger than some histories
     "h2d32": (dict(H_I=2, d_I=32, K=300), 9000),
+    # the largest K
+    "k_max": (dict(K=4096), 20000),
     # a long history (66 chunks, a ragged last chunk)
     "long_history": (dict(), 270000),
     # the same with every score equal: the whole-row fallback over a long row
