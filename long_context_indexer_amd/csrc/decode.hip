@@ -39,16 +39,6 @@ namespace lci {
 constexpr int DEC_BINS = 2048;
 constexpr int DEC_NT = 256;
 
-// Monotone map int32 -> [0, 2048): 1024 + f(s) for s >= 0, 1023 - f(~s) for s < 0,
-// f(t) = 32*bitlength(t) + the 5 bits after the leading one (exact below 64).
-__device__ __forceinline__ int score_bin(int32_t s) {
-  const uint32_t t = s >= 0 ? static_cast<uint32_t>(s) : ~static_cast<uint32_t>(s);
-  const int e = 32 - __clz(t);
-  const uint32_t m = e > 5 ? (t >> (e - 6)) & 31u : (t << (6 - e)) & 31u;
-  const int f = e * 32 + static_cast<int>(m);
-  return s >= 0 ? 1024 + f : 1023 - f;
-}
-
 struct DecRow {
   int valid;
   int64_t n;  // candidates 0..n-1

@@ -8,7 +8,11 @@
 // selected positions in ascending order, -1 padded when the row has fewer than
 // K candidates (positions 0..p).
 //
-// One workgroup per query row:
+// Rows longer than 8192 positions, one workgroup per query row: two passes
+// over the row with the keep mask in LDS (select_row_2pass: log-bin histogram
+// and threshold bin, then keep bits above it and candidates inside it, exact
+// rank among the candidates, ordered compaction of the mask). When the
+// threshold bin holds too many candidates (heavy ties), the radix select:
 //   1. min/max of the order-preserving uint32 keys fixes the varying low bits;
 //   2. radix select, up to 11 bits per pass, with an LDS histogram (integer
 //      atomics: order-independent, so the result is deterministic) finds the
@@ -29,7 +33,10 @@ __global__ __launch_bounds__(TOPK_NT) void topk_rows_kernel(
     int Tq, int Tk, int K, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ scores, int64_t stride,
     int row_begin, int row_count, int32_t* __restrict__ idx, int32_t* __restrict__ sel) {
-  __shared__ SelectLds sm;
+  __shared__ union {
+    SelectLds radix;
+    Select2Lds mask2;
+  } sm;
   const int rr = blockIdx.x;
   const int b = blockIdx.y;
   const int row = row_begin + rr;
@@ -49,7 +56,13 @@ __global__ __launch_bounds__(TOPK_NT) void topk_rows_kernel(
     }
     return;
   }
-  select_row(S, n, K, out, outs, sm);
+  // two passes with the keep mask in LDS; the radix select when the row is
+  // longer or the threshold bin holds too many candidates
+  const bool vec = (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+  if (vec && n <= kSel2MaxN && select_row_2pass(S, static_cast<int>(n), K, out, outs, sm.mask2))
+    return;
+  __syncthreads();  // the radix select reuses the LDS
+  select_row(S, n, K, out, outs, sm.radix);
 }
 
 // ---------------------------------------- four waves per row, row in registers
