@@ -10,7 +10,7 @@ constexpr int kDecCap = 8192;        // candidates per sequence resolved in LDS
 constexpr int kDecMaxChunks = 8192;  // history of at most 2^25 positions
 
 struct DecLayout {
-  size_t scores, hist, ncand, cand, ngt, off, thr, bsel, idx, attn, total;
+  size_t scores, hist, chist, ncand, cand, ngt, off, thr, bsel, idx, attn, total;
   int nchunks, splits;
 };
 

@@ -37,6 +37,7 @@
 namespace lci {
 
 constexpr int DEC_BINS = 2048;
+constexpr int DEC_CBINS = DEC_BINS / 32;  // coarse bins: fine bin / 32 (sign and exponent)
 constexpr int DEC_NT = 256;
 
 struct DecRow {
@@ -54,76 +55,76 @@ __device__ __forceinline__ DecRow dec_row(int Tk, const int32_t* q_offset, const
   return r;
 }
 
-// b* = the bin holding the K-th largest score; *above = count in bins > b*.
-// All threads of the block get the result (uses LDS scratch).
-__device__ __forceinline__ int find_bin(const uint32_t* __restrict__ hist, uint32_t K,
-                                        uint32_t* scratch, uint32_t* found, uint32_t* above_out) {
-  constexpr int BPT = DEC_BINS / DEC_NT;
-  uint32_t c[BPT];
-  uint32_t sum = 0;
+// Sum of p[c * stride] over c = c0, c0 + step, ... < nc, eight loads in flight.
+__device__ __forceinline__ uint32_t strided_sum(const uint32_t* __restrict__ p, int c0, int nc,
+                                                int step, int64_t stride) {
+  uint32_t acc = 0;
+  int c = c0;
+  for (; c + 7 * step < nc; c += 8 * step) {
+    uint32_t v[8];
 #pragma unroll
-  for (int e = 0; e < BPT; ++e) {
-    c[e] = hist[DEC_BINS - 1 - BPT * static_cast<int>(threadIdx.x) - e];
-    sum += c[e];
-  }
-  uint32_t tot;
-  uint32_t above = block_excl_scan(sum, scratch, &tot);
+    for (int u = 0; u < 8; ++u) v[u] = p[static_cast<int64_t>(c + u * step) * stride];
 #pragma unroll
-  for (int e = 0; e < BPT; ++e) {
-    if (above < K && K <= above + c[e]) {
-      found[0] = static_cast<uint32_t>(DEC_BINS - 1 - BPT * static_cast<int>(threadIdx.x) - e);
-      found[1] = above;
-    }
-    above += c[e];
+    for (int u = 0; u < 8; ++u) acc += v[u];
   }
-  __syncthreads();
-  const int bstar = static_cast<int>(found[0]);
-  *above_out = found[1];
-  __syncthreads();
-  return bstar;
+  for (; c < nc; c += step) acc += p[static_cast<int64_t>(c) * stride];
+  return acc;
 }
 
-// One workgroup per sequence: sums the per-chunk histograms, then finds the
-// bin b* holding the K-th largest score and the count of positions in higher
-// bins, read by the candidate and resolve kernels.
+// One workgroup per sequence: the bin b* holding the K-th largest score and
+// the count of positions in higher bins, read by the candidate and resolve
+// kernels. Two levels over the stored chunk histograms: the 64 coarse bins
+// (sign and exponent) summed over the chunks give the coarse bin holding the
+// K-th score, then only its 32 fine bins are summed (96 words per chunk read
+// instead of 2048).
 __global__ __launch_bounds__(DEC_NT) void dec_thresh_kernel(
     int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
-    const uint32_t* __restrict__ chist, int nchunks, uint32_t* __restrict__ bsel) {
-  __shared__ uint32_t h[DEC_BINS];
-  __shared__ uint32_t scratch[DEC_NT / 64 + 2];
-  __shared__ uint32_t found[2];
+    const uint32_t* __restrict__ fhist, const uint32_t* __restrict__ chist, int nchunks,
+    uint32_t* __restrict__ bsel) {
+  __shared__ uint32_t red[DEC_NT];
+  __shared__ uint32_t res[2];
   const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
   const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
   if (rw.n <= K) return;
   const int nc = static_cast<int>((rw.n + kDecChunk - 1) / kDecChunk);  // chunks with positions
-  const uint32_t* hb = chist + static_cast<int64_t>(b) * nchunks * DEC_BINS + threadIdx.x;
-  // thread t sums bins t + 256 i over the chunks, four chunks per round so
-  // 32 independent loads are in flight
-  constexpr int BPT = DEC_BINS / DEC_NT;
-  uint32_t acc[BPT] = {};
-  int c = 0;
-  for (; c + 4 <= nc; c += 4) {
-    uint32_t v[4][BPT];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < BPT; ++i) v[u][i] = hb[static_cast<int64_t>(c + u) * DEC_BINS + i * DEC_NT];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < BPT; ++i) acc[i] += v[u][i];
-  }
-  for (; c < nc; ++c)
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) acc[i] += hb[static_cast<int64_t>(c) * DEC_BINS + i * DEC_NT];
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) h[threadIdx.x + i * DEC_NT] = acc[i];
+  const uint32_t uK = static_cast<uint32_t>(K);
+  // coarse: thread t sums coarse bin t % 64 over chunks t / 64, t / 64 + 4, ...
+  red[t] = strided_sum(chist + static_cast<int64_t>(b) * nchunks * DEC_CBINS + lane, t >> 6, nc,
+                       DEC_NT / 64, DEC_CBINS);
   __syncthreads();
-  uint32_t above;
-  const int bstar = find_bin(h, K, scratch, found, &above);
-  if (threadIdx.x == 0) {
-    bsel[2 * b] = static_cast<uint32_t>(bstar);
-    bsel[2 * b + 1] = above;
+  if (t < 64) {
+    // lane l takes coarse bin 63 - l: the inclusive scan runs from the top bin down
+    const int cb = DEC_CBINS - 1 - lane;
+    uint32_t v = 0;
+#pragma unroll
+    for (int g = 0; g < DEC_NT / 64; ++g) v += red[g * 64 + cb];
+    const uint32_t incl = wave_incl_scan(v);
+    if (incl - v < uK && uK <= incl) {
+      res[0] = static_cast<uint32_t>(cb);
+      res[1] = incl - v;
+    }
+  }
+  __syncthreads();
+  const int cbin = static_cast<int>(res[0]);
+  const uint32_t abovec = res[1];
+  // fine: thread t sums fine bin 32 cbin + t % 32 over chunks t / 32, t / 32 + 8, ...
+  red[t] = strided_sum(fhist + static_cast<int64_t>(b) * nchunks * DEC_BINS + 32 * cbin + (t & 31),
+                       t >> 5, nc, DEC_NT / 32, DEC_BINS);
+  __syncthreads();
+  if (t < 64) {
+    const int f = 31 - lane;  // lanes 32..63 carry nothing
+    uint32_t v = 0;
+    if (lane < 32)
+#pragma unroll
+      for (int g = 0; g < DEC_NT / 32; ++g) v += red[g * 32 + f];
+    const uint32_t incl = wave_incl_scan(v);
+    const uint32_t krem = uK - abovec;
+    if (lane < 32 && incl - v < krem && krem <= incl) {
+      bsel[2 * b] = static_cast<uint32_t>(32 * cbin + f);
+      bsel[2 * b + 1] = abovec + incl - v;
+    }
   }
 }
 
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(DEC_NT) void dec_score_kernel(
     int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
     const int8_t* __restrict__ w, int64_t wsb, int32_t* __restrict__ S,
-    uint32_t* __restrict__ chist) {
+    uint32_t* __restrict__ fhist, uint32_t* __restrict__ chist) {
   constexpr int NCH = D_I / 64 > 0 ? D_I / 64 : 1;  // 64-deep MFMA steps
   constexpr int U = 4;                             // 16-position tiles per step
   constexpr int STEP = 16 * U;
@@ -227,9 +228,17 @@ __global__ __launch_bounds__(DEC_NT) void dec_score_kernel(
     atomicAdd(&lh[score_bin(sv)], 1u);
   }
   __syncthreads();
-  // this chunk's histogram, stored whole (no cross-workgroup atomics)
-  uint32_t* hb = chist + (static_cast<int64_t>(b) * gridDim.x + blockIdx.x) * DEC_BINS;
+  // this chunk's histogram, stored whole (no cross-workgroup atomics), and
+  // its coarse form (32 fine bins per coarse bin)
+  const int64_t ci = static_cast<int64_t>(b) * gridDim.x + blockIdx.x;
+  uint32_t* hb = fhist + ci * DEC_BINS;
   for (int j = threadIdx.x; j < DEC_BINS; j += DEC_NT) hb[j] = lh[j];
+  if (threadIdx.x < DEC_CBINS) {
+    uint32_t cs = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) cs += lh[32 * threadIdx.x + ((j + threadIdx.x) & 31)];
+    chist[ci * DEC_CBINS + threadIdx.x] = cs;
+  }
 }
 
 __global__ __launch_bounds__(DEC_NT) void dec_cand_kernel(
@@ -388,17 +397,33 @@ __global__ __launch_bounds__(TOPK_NT) void dec_resolve_kernel(
   }
   // positions in bins above the candidate bin are all kept
   const uint32_t krem = static_cast<uint32_t>(K) - bsel[2 * b + 1];
-  // gather the chunks' lists: one wave per chunk at a time
+  // gather the chunks' lists: entry j of the merged list comes from the last
+  // chunk whose start is <= j (empty chunks share their successor's start);
+  // eight loads in flight per thread
   {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    for (int c = wv; c < nch; c += TOPK_NT / 64) {
-      const uint32_t start = ccount[c];
-      const uint32_t cnt = (c + 1 < nch ? ccount[c + 1] : nc) - start;
-      const int2* cb = cand + (static_cast<int64_t>(b) * nchunks + c) * kDecChunk;
-      for (uint32_t j = lane; j < cnt; j += 64) {
-        const int2 cv = cb[j];
-        cval[start + j] = cv.x;
-        cpos[start + j] = cv.y;
+    const int2* cbase = cand + static_cast<int64_t>(b) * nchunks * kDecChunk;
+    for (uint32_t j0 = 0; j0 < nc; j0 += 8 * TOPK_NT) {
+      int2 cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        // nc >= 1 here (at least K - (count above b*) candidates); entries
+        // past nc read the last one and are not stored
+        const uint32_t j = min(j0 + u * TOPK_NT + threadIdx.x, nc - 1);
+        int lo = 0, hi = nch - 1;  // largest c with ccount[c] <= j
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (ccount[mid] <= j) lo = mid;
+          else hi = mid - 1;
+        }
+        cv[u] = cbase[static_cast<int64_t>(lo) * kDecChunk + (j - ccount[lo])];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t j = j0 + u * TOPK_NT + threadIdx.x;
+        if (j < nc) {
+          cval[j] = cv[u].x;
+          cpos[j] = cv[u].y;
+        }
       }
     }
   }
@@ -526,6 +551,7 @@ DecLayout decode_layout(const Geom& g) {
   L.attn = o;
   L.splits = sparse_attn_pick_splits(g);
   o += al(sparse_attn_workspace(g, L.splits));
+  L.chist = o;   o += al(static_cast<size_t>(g.B) * L.nchunks * DEC_CBINS * sizeof(uint32_t));
   L.total = o;
   return L;
 }
@@ -533,11 +559,11 @@ DecLayout decode_layout(const Geom& g) {
 template <int H_I, int D_I>
 static hipError_t launch_score_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                                   const int8_t* w, int64_t wsb, int32_t* S, uint32_t* hist,
-                                  int nchunks, hipStream_t st) {
+                                  uint32_t* chist, int nchunks, hipStream_t st) {
   {
     KernelTimer timer(LCI_KERNEL_DEC_SCORE, st);
     hipLaunchKernelGGL((dec_score_kernel<H_I, D_I>), dim3(nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk,
-                       g.K, g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, S, hist);
+                       g.K, g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, S, hist, chist);
   }
   return hipGetLastError();
 }
@@ -545,13 +571,13 @@ static hipError_t launch_score_hd(const Geom& g, const int8_t* q_idx, const int8
 template <int H_I>
 static hipError_t launch_score_h(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                                  const int8_t* w, int64_t wsb, int32_t* S, uint32_t* hist,
-                                 int nchunks, hipStream_t st) {
+                                 uint32_t* chist, int nchunks, hipStream_t st) {
   switch (g.d_I) {
-    case 32: return launch_score_hd<H_I, 32>(g, q_idx, k_idx, w, wsb, S, hist, nchunks, st);
-    case 64: return launch_score_hd<H_I, 64>(g, q_idx, k_idx, w, wsb, S, hist, nchunks, st);
+    case 32: return launch_score_hd<H_I, 32>(g, q_idx, k_idx, w, wsb, S, hist, chist, nchunks, st);
+    case 64: return launch_score_hd<H_I, 64>(g, q_idx, k_idx, w, wsb, S, hist, chist, nchunks, st);
     case 128:
       if constexpr (H_I * 128 <= 1024)
-        return launch_score_hd<H_I, 128>(g, q_idx, k_idx, w, wsb, S, hist, nchunks, st);
+        return launch_score_hd<H_I, 128>(g, q_idx, k_idx, w, wsb, S, hist, chist, nchunks, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -565,6 +591,7 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
   char* ws = static_cast<char*>(workspace);
   int32_t* S = reinterpret_cast<int32_t*>(ws + L.scores);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+  uint32_t* chist = reinterpret_cast<uint32_t*>(ws + L.chist);
   uint32_t* ncand = reinterpret_cast<uint32_t*>(ws + L.ncand);
   int2* cand = reinterpret_cast<int2*>(ws + L.cand);
   uint32_t* ngt = reinterpret_cast<uint32_t*>(ws + L.ngt);
@@ -575,18 +602,18 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
 
   hipError_t e = hipSuccess;
   switch (g.H_I) {
-    case 1: e = launch_score_h<1>(g, q_idx, k_idx, w, wsb, S, hist, L.nchunks, st); break;
-    case 2: e = launch_score_h<2>(g, q_idx, k_idx, w, wsb, S, hist, L.nchunks, st); break;
-    case 4: e = launch_score_h<4>(g, q_idx, k_idx, w, wsb, S, hist, L.nchunks, st); break;
-    case 8: e = launch_score_h<8>(g, q_idx, k_idx, w, wsb, S, hist, L.nchunks, st); break;
-    case 16: e = launch_score_h<16>(g, q_idx, k_idx, w, wsb, S, hist, L.nchunks, st); break;
+    case 1: e = launch_score_h<1>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
+    case 2: e = launch_score_h<2>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
+    case 4: e = launch_score_h<4>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
+    case 8: e = launch_score_h<8>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
+    case 16: e = launch_score_h<16>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
     default: e = hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   {
     KernelTimer timer(LCI_KERNEL_DEC_THRESH, st);
     hipLaunchKernelGGL(dec_thresh_kernel, dim3(g.B), dim3(DEC_NT), 0, st, g.Tk, g.K, g.q_offset,
-                       g.kv_len, hist, L.nchunks, bsel);
+                       g.kv_len, hist, chist, L.nchunks, bsel);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
