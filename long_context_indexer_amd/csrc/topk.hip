@@ -188,27 +188,29 @@ __global__ __launch_bounds__(B4_NT, 6) void topk_b4_kernel(
   const int nch = m >> 8;                   // chunks per lane, 1..B4_CH
   const int seg = wv * m;
 
-  // 0. the row into registers
-  const bool vec = (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+  // 0. the row into registers: every load issued before any is used (one
+  // memory round trip per row, not one per chunk); with 16-byte aligned rows,
+  // 16-byte loads clamped to the last aligned group of the row
+  const bool vec = (reinterpret_cast<uintptr_t>(S) & 15) == 0 && (stride & 3) == 0;
   uint32_t u[B4_CH][4];
+  if (vec) {
+    const int last4 = (n - 1) & ~3;
+    int4 v4[B4_CH];
 #pragma unroll
-  for (int c = 0; c < B4_CH; ++c) {
-    const int s0 = seg + 256 * c + 4 * lane;
-    if (c < nch) {
-      if (vec && s0 + 3 < n) {
-        const int4 v4 = *reinterpret_cast<const int4*>(S + s0);
-        u[c][0] = score_key(v4.x);
-        u[c][1] = score_key(v4.y);
-        u[c][2] = score_key(v4.z);
-        u[c][3] = score_key(v4.w);
-      } else {
+    for (int c = 0; c < B4_CH; ++c)
+      v4[c] = *reinterpret_cast<const int4*>(S + min(seg + 256 * c + 4 * lane, last4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[c][e] = score_key(S[min(s0 + e, n - 1)]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[c][e] = 0u;
+    for (int c = 0; c < B4_CH; ++c) {
+      u[c][0] = score_key(v4[c].x);
+      u[c][1] = score_key(v4[c].y);
+      u[c][2] = score_key(v4[c].z);
+      u[c][3] = score_key(v4[c].w);
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < B4_CH; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[c][e] = score_key(S[min(seg + 256 * c + 4 * lane + e, n - 1)]);
   }
 
   // 1. range of the keys, then positions >= n take the minimum
