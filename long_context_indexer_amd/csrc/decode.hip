@@ -264,10 +264,12 @@ __global__ __launch_bounds__(DEC_NT) void dec_cand_kernel(
   // element e of this thread: position base + e*DEC_NT + tid (coalesced)
   int32_t val[E];
   uint32_t gt = 0, nc = 0, cmask = 0;
+  // every load issued before any is used (clamped to the chunk's last position)
+#pragma unroll
+  for (int e = 0; e < E; ++e) val[e] = Sb[min(base + e * DEC_NT + threadIdx.x, nend - 1)];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int64_t s = base + e * DEC_NT + threadIdx.x;
-    val[e] = s < nend ? Sb[s] : 0;
     const int bin = s < nend ? score_bin(val[e]) : -1;
     gt += bin > bstar ? 1u : 0u;
     if (bin == bstar) {
@@ -501,14 +503,14 @@ __global__ __launch_bounds__(DEC_NT) void dec_compact_kernel(
   // position of element e of this thread: base + e*DEC_NT + tid, i.e. position
   // order is (e, wave, lane): a ballot per e ranks lanes, LDS counts rank (e, wave)
   uint64_t km[E];
+  int32_t vals[E];  // every load issued before any is used
+#pragma unroll
+  for (int e = 0; e < E; ++e) vals[e] = Sb[min(base + e * DEC_NT + threadIdx.x, rw.n - 1)];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int64_t s = base + e * DEC_NT + threadIdx.x;
-    bool keep = false;
-    if (s < rw.n) {
-      const int32_t v = Sb[s];
-      keep = v > vstar || (v == vstar && s <= scut);
-    }
+    const int32_t v = vals[e];
+    const bool keep = s < rw.n && (v > vstar || (v == vstar && s <= scut));
     km[e] = __ballot(keep);
     if (lane == 0) cnt[e * NW + wv] = __popcll(km[e]);
   }
