@@ -41,7 +41,7 @@ TRAFFIC = {
                        sources=("long_context_indexer_amd/csrc/attn_dense.hip",
                                 "long_context_indexer_amd/csrc/attn_dense.h",
                                 "long_context_indexer_amd/csrc/common.h"),
-                       sha256="130d715a264c49fc21cdfec2faab7379bada036f44c22be397b7317e11c4bf79"),
+                       sha256="fc7bdeb3beeadd5c87044c081959582edd69348680ead44eb6634096436b4c2f"),
 }
 
 

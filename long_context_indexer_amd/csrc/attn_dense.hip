@@ -13,15 +13,17 @@
 //
 // Two kernels:
 //   idx_mask_kernel  turns each index row into a bit mask over positions and a
-//                    row flag: 2 = the row keeps exactly 0..p (no mask needed),
-//                    1 = masked tile path, 0 = leave the row to the gather
-//                    kernel (index rows that are not strictly increasing
-//                    positions in 0..p, or rows too sparse for tiles).
+//                    row flag: 2 = the row keeps exactly 0..p, 1 = masked tile
+//                    path, 0 = leave the row to the gather kernel (index rows
+//                    that are not strictly increasing positions in 0..p, or
+//                    rows too sparse for tiles). Every tile-path row gets its
+//                    mask (all of 0..p for flag 2).
 //   attn_dense_kernel one workgroup = 4 waves = 4*32 (token, query head) rows of
 //                    one key/value head g; waves own 32/G tokens x G heads.
-//                    Per 64-key tile: K and V tiles go to LDS (double
-//                    buffered; the next tile is prefetched into registers
-//                    while this one is computed; one barrier per tile), then
+//                    Per 64-key tile: K and V tiles go from HBM straight into
+//                    LDS (double buffered: V of the next tile and K of the one
+//                    after are in flight while this one is computed; one
+//                    barrier per tile), then
 //                      S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (lane l owns
 //                            query row l%32, keys 8i+4*(l/32)+j of each 32-key half),
 //                      mask + online softmax in base 2 (max on raw scores,
@@ -33,8 +35,9 @@
 //                            4-key x 16-feature block transposed into registers).
 //                    The epilogue applies sigmoid(gate) and stores bf16.
 // K and V tiles use an XOR-swizzled LDS layout that keeps every access pattern
-// free of bank conflicts. Workgroups are placed so that each XCD (its own L2) serves one key/value head
-// (blockIdx.x % 8 picks the XCD), and the longest causal tiles start first.
+// free of bank conflicts. Workgroups are placed so that each XCD (its own L2)
+// serves one key/value head (blockIdx.x % 8 picks the XCD), and the longest
+// causal tiles start first.
 #include "attn_dense.h"
 #include "common.h"
 #include "../../include/lci.h"
