@@ -216,8 +216,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="run only one fused step kind (for profiler runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "prefill64k", "decode1m"], default=None,
+                    help="run only one fused step (profiler runs; prefill64k and decode1m are "
+                         "the long-context workloads, outside the default run)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 2 GiB device buffer 5 times (HBM counter calibration runs)")
     args = ap.parse_args()
@@ -239,44 +240,40 @@ def main():
     timer = Timer(stream)
     res = {}
 
-    # ---------------------------------------------------------------- prefill 8K
-    cfg = synth.CONFIGS["prefill8k"]
-    inp_host = synth.host_inputs(cfg, seed=0)
-
     def dev(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    d = {k: dev(v) for k, v in inp_host.items() if isinstance(v, np.ndarray)}
-    geom = lci.make_geom(cfg.B, cfg.Tq, cfg.Tk, cfg.K, d["q_offset"], d["kv_len"], Hq=cfg.Hq,
-                         Hkv=cfg.Hkv, d=cfg.d, H_I=cfg.H_I, d_I=cfg.d_I)
-    ws = torch.empty(lci.workspace_bytes(lci.ENTRY_PREFILL, geom), dtype=torch.uint8,
-                     device="cuda")
-    out = torch.empty_like(d["q"])
+    def run_prefill(name, inp_host):
+        cfg = synth.CONFIGS[name]
+        d = {k: dev(v) for k, v in inp_host.items() if isinstance(v, np.ndarray)}
+        geom = lci.make_geom(cfg.B, cfg.Tq, cfg.Tk, cfg.K, d["q_offset"], d["kv_len"], Hq=cfg.Hq,
+                             Hkv=cfg.Hkv, d=cfg.d, H_I=cfg.H_I, d_I=cfg.d_I)
+        ws = torch.empty(lci.workspace_bytes(lci.ENTRY_PREFILL, geom), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty_like(d["q"])
 
-    def prefill_step():
-        lci.prefill_fwd(d["q_idx"], d["k_idx"], d["w"], d["q"], d["k"], d["v"], d["gate"],
-                        cfg.scale, d["q_offset"], d["kv_len"], cfg.K, out=out, workspace=ws,
-                        stream=stream)
+        def prefill_step():
+            lci.prefill_fwd(d["q_idx"], d["k_idx"], d["w"], d["q"], d["k"], d["v"], d["gate"],
+                            cfg.scale, d["q_offset"], d["kv_len"], cfg.K, out=out, workspace=ws,
+                            stream=stream)
 
-    if args.only in (None, "prefill"):
         for _ in range(args.warmup):
             prefill_step()
         torch.cuda.synchronize()
         ms_step, ev_ms, kern = timed_region(timer, prefill_step, args.steps, lci)
         tok_s = cfg.B * cfg.Tq / (ms_step * 1e-3)
-        res["prefill"] = dict(ms_per_step=ms_step, event_ms_per_step=ev_ms, tok_s=tok_s,
-                              kernels=kern)
-        log(f"prefill8k fused: {ms_step:.3f} ms/step ({ev_ms:.3f} ms by events), "
+        log(f"{name} fused: {ms_step:.3f} ms/step ({ev_ms:.3f} ms by events), "
             f"{tok_s / 1e6:.2f} M tok/s")
-        for name, kv in kern.items():
-            log(f"  {name:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
+        for kname, kv in kern.items():
+            log(f"  {kname:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
                 f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
+        return dict(workload=name, ms_per_step=ms_step, event_ms_per_step=ev_ms, tok_s=tok_s,
+                    kernels=kern)
 
-    # --------------------------------------------------------------- decode 128K
-    if not args.no_decode and args.only in (None, "decode"):
-        dcfg = synth.CONFIGS["decode128k"]
+    def run_decode(name):
+        dcfg = synth.CONFIGS[name]
         dd = synth.device_inputs(dcfg, seed=0)
         dgeom = lci.make_geom(dcfg.B, dcfg.Tq, dcfg.Tk, dcfg.K, dd["q_offset"], dd["kv_len"],
                               Hq=dcfg.Hq, Hkv=dcfg.Hkv, d=dcfg.d, H_I=dcfg.H_I, d_I=dcfg.d_I)
@@ -298,19 +295,37 @@ def main():
         abytes = decode_attn_bytes(dcfg)
         sbytes = decode_step_bytes(dcfg)
         a_ms = sum(dkern[k]["ms_per_step"] for k in ("attn_gather", "attn_combine") if k in dkern)
-        res["decode"] = dict(workload="decode128k", ms_per_step=dms, event_ms_per_step=dev_ms,
-                             queries_s=qps,
-                             step_hbm_gbs=sbytes / dms / 1e6,
-                             step_frac_hbm=sbytes / dms / 1e6 / PEAK_HBM_GBS,
-                             sparse_attn_ms=a_ms, sparse_attn_gbs=abytes / a_ms / 1e6,
-                             sparse_attn_frac_hbm=abytes / a_ms / 1e6 / PEAK_HBM_GBS,
-                             kernels=dkern)
-        log(f"decode128k fused: {dms:.3f} ms/step, {qps:.0f} queries/s, whole step "
+        log(f"{name} fused: {dms:.3f} ms/step, {qps:.0f} queries/s, whole step "
             f"{sbytes / dms / 1e6:.0f} GB/s; attention kernels {a_ms * 1e3:.1f} us = "
             f"{abytes / a_ms / 1e6:.0f} GB/s")
-        for name, kv in dkern.items():
-            log(f"  {name:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
+        for kname, kv in dkern.items():
+            log(f"  {kname:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
                 f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
+        return dict(workload=name, ms_per_step=dms, event_ms_per_step=dev_ms, queries_s=qps,
+                    step_hbm_gbs=sbytes / dms / 1e6,
+                    step_frac_hbm=sbytes / dms / 1e6 / PEAK_HBM_GBS,
+                    sparse_attn_ms=a_ms, sparse_attn_gbs=abytes / a_ms / 1e6,
+                    sparse_attn_frac_hbm=abytes / a_ms / 1e6 / PEAK_HBM_GBS,
+                    kernels=dkern)
+
+    if args.only in ("prefill64k", "decode1m"):
+        if args.only == "prefill64k":
+            res["prefill64k"] = run_prefill("prefill64k", synth.host_inputs(
+                synth.CONFIGS["prefill64k"], seed=0))
+        else:
+            res["decode1m"] = run_decode("decode1m")
+        print(json.dumps(res))
+        return
+
+    # ---------------------------------------------------------------- prefill 8K
+    cfg = synth.CONFIGS["prefill8k"]
+    inp_host = synth.host_inputs(cfg, seed=0)
+    if args.only in (None, "prefill"):
+        res["prefill"] = run_prefill("prefill8k", inp_host)
+
+    # --------------------------------------------------------------- decode 128K
+    if not args.no_decode and args.only in (None, "decode"):
+        res["decode"] = run_decode("decode128k")
 
     if args.only is not None:
         print(json.dumps(res))
