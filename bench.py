@@ -121,6 +121,27 @@ class Timer:
         return s.elapsed_time(e) / iters
 
 
+def cold_steps(step, steps, stream):
+    """Each step timed alone (events on the launch stream) after the
+    last-level cache has been flushed by streaming a 1 GiB buffer outside the
+    timed span: inputs are in HBM but no longer in any cache. Median ms."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    times = []
+    for _ in range(steps):
+        flush.add_(1.0)  # reads and writes 1 GiB on the same stream
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        step()
+        e.record(stream)
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    del flush
+    times.sort()
+    return times[len(times) // 2]
+
+
 def copy_calibration():
     """A plain device-to-device copy of 2 GiB, five times: under rocprofv3 --pmc
     FETCH_SIZE / WRITE_SIZE it gives the factor between each counter and the bytes
@@ -264,12 +285,14 @@ def main():
         torch.cuda.synchronize()
         ms_step, ev_ms, kern = timed_region(timer, prefill_step, args.steps, lci)
         tok_s = cfg.B * cfg.Tq / (ms_step * 1e-3)
+        cold_ms = cold_steps(prefill_step, args.steps, stream)
         log(f"{name} fused: {ms_step:.3f} ms/step ({ev_ms:.3f} ms by events), "
-            f"{tok_s / 1e6:.2f} M tok/s")
+            f"{tok_s / 1e6:.2f} M tok/s; cold cache {cold_ms:.3f} ms/step")
         for kname, kv in kern.items():
             log(f"  {kname:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
                 f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
         return dict(workload=name, ms_per_step=ms_step, event_ms_per_step=ev_ms, tok_s=tok_s,
+                    cold_ms_per_step=cold_ms, cold_tok_s=cfg.B * cfg.Tq / (cold_ms * 1e-3),
                     kernels=kern)
 
     def run_decode(name):
@@ -361,6 +384,8 @@ def main():
         "roofline": roof,
         "kernels_us_per_step": {k: round(v["ms_per_step"] * 1e3, 2)
                                 for k, v in pre["kernels"].items()},
+        "cold_cache": {"ms_per_step": pre["cold_ms_per_step"], "tok_s": pre["cold_tok_s"],
+                       "note": "median of single steps, each after a 1 GiB cache flush"},
         "cpu_baseline": cpu,
     }
     if "decode" in res:
