@@ -55,14 +55,14 @@ def open_library(path: str):
     lib.orc_score_row.argtypes = [i32, i32, P, P, P, i64, P]
     lib.orc_score_row.restype = i32
     lib.orc_topk_row.argtypes = [P, i64, i32, P, P]
-    lib.orc_attn_row.argtypes = [i32, i32, i32, P, P, P, i64, P, i32, P, f64, P, P]
+    lib.orc_attn_row.argtypes = [i32, i32, i32, P, P, P, i64, P, i32, P, P, f64, P, P]
     lib.orc_scores_rows.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i64, i64, i64, P, P, P]
     lib.orc_scores_rows.restype = i32
     lib.orc_topk_rows.argtypes = [i64, P, i64, P, i32, P, P]
-    lib.orc_attn_rows.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, f64, i64, P,
-                                  P, P, P, P]
+    lib.orc_attn_rows.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, i64,
+                                  P, P, P, P, P]
     lib.orc_layer_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
-                                   i64, i64, P, P, P, P, f64, i64, P, P, P, P, P, P]
+                                   i64, i64, P, P, P, P, P, f64, i64, P, P, P, P, P, P]
     lib.orc_layer_rows.restype = i32
     lib.orc_num_threads.restype = i32
     return lib
@@ -148,29 +148,35 @@ class Oracle:
         self.lib.orc_topk_rows(S.shape[0], _p(S), S.shape[1], _p(n), K, _p(idx), _p(sel))
         return idx, sel
 
-    def attention(self, q, k, v, gate, idx, kv_len, scale, rows=None):
-        """Gated attention over given index rows. q, gate uint16 [B,Tq,Hq,d] (gate may
-        be None); k, v uint16 [B,Tk,Hkv,d]; idx int32 [nrows, K] for the listed rows.
-        Returns (out float64 [nrows,Hq,d], lse float64 [nrows,Hq])."""
+    def attention(self, q, k, v, gate, idx, kv_len, scale, rows=None, mix=None):
+        """Gated attention over given index rows. q, gate, mix uint16 [B,Tq,Hq,d] (gate
+        may be None: ungated; mix may be None: the gate only scales, else
+        out = s*o + (1-s)*mix); k, v uint16 [B,Tk,Hkv,d]; idx int32 [nrows, K] for the
+        listed rows. Returns (out float64 [nrows,Hq,d], lse float64 [nrows,Hq])."""
         q = _c(q, np.uint16)
         k = _c(k, np.uint16)
         v = _c(v, np.uint16)
         B, Tq, Hq, d = q.shape
         Tk, Hkv = k.shape[1], k.shape[2]
         gate = None if gate is None else _c(gate, np.uint16)
+        mix = None if mix is None else _c(mix, np.uint16)
+        for t in (gate, mix):
+            if t is not None and t.shape != q.shape:
+                raise ValueError("gate and mix have the shape of q")
         rb, ri = _rows(rows, B, Tq)
         idx = _c(idx, np.int32).reshape(len(rb), -1)
         K = idx.shape[1]
         out = np.empty((len(rb), Hq, d), np.float64)
         lse = np.empty((len(rb), Hq), np.float64)
         self.lib.orc_attn_rows(Tq, Tk, Hq, Hkv, d, K, _p(_c(kv_len, np.int32)), _p(q), _p(k),
-                              _p(v), _p(gate), float(scale), len(rb), _p(rb), _p(ri), _p(idx),
-                              _p(out), _p(lse))
+                              _p(v), _p(gate), _p(mix), float(scale), len(rb), _p(rb), _p(ri),
+                              _p(idx), _p(out), _p(lse))
         return out, lse
 
     def layer(self, inp, K, rows=None, gated=True):
         """The whole layer (score -> Top-K -> attention -> gate) for the listed rows
-        of an input dict as produced by ``synth.host_inputs``.
+        of an input dict as produced by ``synth.host_inputs``; an entry "mix" (the
+        other branch's output, uint16 [B,Tq,Hq,d]) is mixed in by the gate.
         Returns dict(idx, sel, out, lse) with out float64 [nrows,Hq,d]."""
         q_idx = _c(inp["q_idx"], np.int8)
         k_idx = _c(inp["k_idx"], np.int8)
@@ -182,6 +188,9 @@ class Oracle:
         Hq, d = q.shape[2], q.shape[3]
         Hkv = k.shape[2]
         gate = _c(inp["gate"], np.uint16) if gated and inp.get("gate") is not None else None
+        mix = _c(inp["mix"], np.uint16) if gate is not None and inp.get("mix") is not None else None
+        if mix is not None and mix.shape != q.shape:
+            raise ValueError("mix has the shape of q")
         w = _c(inp["w"], np.int8)
         wsb, wsq = _w_strides(w, B, Tq, H_I)
         rb, ri = _rows(rows, B, Tq)
@@ -193,7 +202,7 @@ class Oracle:
         rc = self.lib.orc_layer_rows(Tq, Tk, Hq, Hkv, d, H_I, d_I, K,
                                     _p(_c(inp["q_offset"], np.int32)), _p(_c(inp["kv_len"], np.int32)),
                                     _p(q_idx), _p(k_idx), _p(w), wsb, wsq, _p(q), _p(k), _p(v),
-                                    _p(gate), float(inp["scale"]), nr, _p(rb), _p(ri), _p(idx),
+                                    _p(gate), _p(mix), float(inp["scale"]), nr, _p(rb), _p(ri), _p(idx),
                                     _p(sel), _p(out), _p(lse))
         if rc == OVERFLOW:
             raise OverflowError("indexer score outside the int32 range")

@@ -108,15 +108,30 @@ static double orc_bf16(uint16_t h)
     return (double)f;
 }
 
+/* The gate on one attention output o: y = s*o with s = sigmoid(G), or, with
+ * the output x of another branch to mix with, y = s*o + (1 - s)*x: the gate
+ * weighs the sparse branch against the linear or compressed one ("Hybrid
+ * Sparse Attention for Long-Context LLMs", section "Indexer + Top-K: How
+ * Fine-Grained Sparse Attention Works", step 4 and its pseudocode; "How
+ * Fine-Grained Sparse Attention Reshapes Long-Context Architecture in Large
+ * Models", section "How Indexer + Top-K Works at Runtime", its pseudocode). */
+static double orc_gate(double o, double G, const uint16_t *mix, int64_t j)
+{
+    double s = 1.0 / (1.0 + exp(-G));
+    return s * o + (mix ? (1.0 - s) * orc_bf16(mix[j]) : 0.0);
+}
+
 /* Gated attention of one query row over the listed positions.
- * q, gate [Hq][d]; k, v [kv_rows][Hkv][d] (one sequence); idx [K].
+ * q, gate, mix [Hq][d]; k, v [kv_rows][Hkv][d] (one sequence); idx [K].
  * Entries outside 0..kv_len-1 (the -1 padding) are skipped. gate may be NULL
- * (ungated). out [Hq][d], lse [Hq] (natural log of the softmax denominator,
- * including the running max); a row with no valid entry gives out = 0 and
+ * (ungated; then mix is ignored), mix may be NULL (no mixing). out [Hq][d],
+ * lse [Hq] (natural log of the softmax denominator, including the running
+ * max); a row with no valid entry has o = 0 (so out = 0 without mixing) and
  * lse = -inf. */
 void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
                   const uint16_t *v, int64_t kv_len, const int32_t *idx, int K,
-                  const uint16_t *gate, double scale, double *out, double *lse)
+                  const uint16_t *gate, const uint16_t *mix, double scale, double *out,
+                  double *lse)
 {
     int G = Hq / Hkv;
     double *logit = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
@@ -136,21 +151,21 @@ void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
         for (int j = 0; j < d; ++j) o[j] = 0.0;
         if (m == -INFINITY) {
             if (lse) lse[h] = -INFINITY;
-            continue;
+        } else {
+            double Z = 0.0;
+            for (int t = 0; t < K; ++t) {
+                int64_t s = idx[t];
+                if (s < 0 || s >= kv_len) continue;
+                double e = exp(logit[t] - m);
+                Z += e;
+                for (int j = 0; j < d; ++j) o[j] += e * orc_bf16(v[(s * Hkv + g) * d + j]);
+            }
+            for (int j = 0; j < d; ++j) o[j] /= Z;
+            if (lse) lse[h] = m + log(Z);
         }
-        double Z = 0.0;
-        for (int t = 0; t < K; ++t) {
-            int64_t s = idx[t];
-            if (s < 0 || s >= kv_len) continue;
-            double e = exp(logit[t] - m);
-            Z += e;
-            for (int j = 0; j < d; ++j) o[j] += e * orc_bf16(v[(s * Hkv + g) * d + j]);
-        }
-        for (int j = 0; j < d; ++j) {
-            o[j] /= Z;
-            if (gate) o[j] /= 1.0 + exp(-orc_bf16(gate[h * d + j]));
-        }
-        if (lse) lse[h] = m + log(Z);
+        if (gate)
+            for (int j = 0; j < d; ++j)
+                o[j] = orc_gate(o[j], orc_bf16(gate[h * d + j]), mix ? mix + (size_t)h * d : NULL, j);
     }
     free(logit);
 }
@@ -193,7 +208,8 @@ void orc_topk_rows(int64_t nrows, const int32_t *S, int64_t stride, const int64_
 /* Attention + gate for a list of rows with the given index rows idx [nrows][K]. */
 void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t *kv_len,
                    const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                   const uint16_t *gate, double scale, int64_t nrows, const int32_t *row_b,
+                   const uint16_t *gate, const uint16_t *mix, double scale, int64_t nrows,
+                   const int32_t *row_b,
                    const int32_t *row_i, const int32_t *idx, double *out, double *lse)
 {
 #pragma omp parallel for schedule(dynamic, 1)
@@ -203,22 +219,22 @@ void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t 
         int64_t kvl = kv_len[b] < Tk ? kv_len[b] : Tk;
         orc_attn_row(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
                      v + (int64_t)b * Tk * Hkv * d, kvl, idx + r * (int64_t)K, K,
-                     gate ? gate + qrow * Hq * d : NULL, scale, out + r * (int64_t)Hq * d,
-                     lse ? lse + r * (int64_t)Hq : NULL);
+                     gate ? gate + qrow * Hq * d : NULL, mix ? mix + qrow * Hq * d : NULL, scale,
+                     out + r * (int64_t)Hq * d, lse ? lse + r * (int64_t)Hq : NULL);
     }
 }
 
 /* The whole layer for a list of rows: score -> Top-K -> attention -> gate.
  * idx/sel [nrows][K], out [nrows][Hq][d], lse [nrows][Hq]. Invalid rows give
- * idx = -1, sel = INT32_MIN, out = 0, lse = -inf. Returns ORC_OVERFLOW if a
- * score overflowed int32. */
+ * idx = -1, sel = INT32_MIN, an attention output of 0 (out = 0 unless mixed)
+ * and lse = -inf. Returns ORC_OVERFLOW if a score overflowed int32. */
 int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int K,
                    const int32_t *q_offset, const int32_t *kv_len, const int8_t *q_idx,
                    const int8_t *k_idx, const int8_t *w, int64_t w_stride_b,
                    int64_t w_stride_q, const uint16_t *q, const uint16_t *k,
-                   const uint16_t *v, const uint16_t *gate, double scale, int64_t nrows,
-                   const int32_t *row_b, const int32_t *row_i, int32_t *idx, int32_t *sel,
-                   double *out, double *lse)
+                   const uint16_t *v, const uint16_t *gate, const uint16_t *mix, double scale,
+                   int64_t nrows, const int32_t *row_b, const int32_t *row_i, int32_t *idx,
+                   int32_t *sel, double *out, double *lse)
 {
     int rc = ORC_OK;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : rc)
@@ -230,8 +246,12 @@ int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int
         double *orow = out + r * (int64_t)Hq * d;
         double *lrow = lse ? lse + r * (int64_t)Hq : NULL;
         if (p < 0 || p >= kv_len[b] || kv_len[b] > Tk) {
+            int64_t qrow = (int64_t)b * Tq + i;
             for (int j = 0; j < K; ++j) { ir[j] = -1; if (sr) sr[j] = INT32_MIN; }
-            for (int64_t j = 0; j < (int64_t)Hq * d; ++j) orow[j] = 0.0;
+            for (int64_t j = 0; j < (int64_t)Hq * d; ++j)
+                orow[j] = gate ? orc_gate(0.0, orc_bf16(gate[qrow * Hq * d + j]),
+                                          mix ? mix + qrow * Hq * d : NULL, j)
+                               : 0.0;
             if (lrow) for (int h = 0; h < Hq; ++h) lrow[h] = -INFINITY;
             continue;
         }
@@ -245,7 +265,8 @@ int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int
         int64_t qrow = (int64_t)b * Tq + i;
         orc_attn_row(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
                      v + (int64_t)b * Tk * Hkv * d, kv_len[b], ir, K,
-                     gate ? gate + qrow * Hq * d : NULL, scale, orow, lrow);
+                     gate ? gate + qrow * Hq * d : NULL, mix ? mix + qrow * Hq * d : NULL, scale,
+                     orow, lrow);
     }
     return rc;
 }

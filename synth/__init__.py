@@ -28,7 +28,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-T_Q, T_K, T_V, T_G, T_QI, T_KI, T_W, T_NEEDLE = range(8)
+T_Q, T_K, T_V, T_G, T_QI, T_KI, T_W, T_NEEDLE, T_MIX = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -173,6 +173,16 @@ def host_inputs(cfg: Config, seed: int = 0) -> dict:
     if cfg.fp32_source:
         out.update(q_f32=qf, k_f32=kf, v_f32=vf, gate_f32=gf)
     return out
+
+
+def host_mix(cfg: Config, seed: int = 0) -> np.ndarray:
+    """The other branch's output for the gate to mix with (the linear or
+    compressed attention the pages pair the sparse branch with): uint16 (bf16
+    bits) [B,Tq,Hq,d] of standard normals, its own stream per sequence."""
+    m = np.empty((cfg.B, cfg.Tq, cfg.Hq, cfg.d), np.float32)
+    for b in range(cfg.B):
+        m[b] = _rng(seed, cfg, T_MIX, b).standard_normal(m.shape[1:], dtype=np.float32)
+    return bf16_bits(m)
 
 
 def device_inputs(cfg: Config, seed: int = 0, device: str = "cuda") -> dict:

@@ -264,6 +264,10 @@ def pin_attn_hand(orc):
     assert np.allclose(lse[0], g["lse"], rtol=0, atol=1e-14)
     out, _ = orc.attention(q, k, v, None, idx, np.array([3]), g["scale"], rows=[[0, 0]])
     assert np.allclose(out[0], g["out_ungated"], rtol=0, atol=1e-14)
+    out, lse = orc.attention(q, k, v, gate, idx, np.array([3]), g["scale"], rows=[[0, 0]],
+                             mix=_bf(g["mix"])[None, None])
+    assert np.allclose(out[0], g["out_mixed"], rtol=0, atol=1e-14)
+    assert np.allclose(lse[0], g["lse"], rtol=0, atol=1e-14)
 
 
 def pin_attn_dense_equivalence(orc):
@@ -397,6 +401,47 @@ def pin_gate_limits(orc):
     assert np.abs(y[0] - o[0] * ratio).max() < 1e-14
 
 
+def pin_gate_mix(orc):
+    """Mixing with another branch's output x: G = 0 gives (o + x)/2, G = +30
+    gives o and G = -30 gives x (to 1e-12 relative), x = o gives o for any G,
+    a row with no selected entry gives sigmoid(-G) * x, and the random-G case
+    weighs the ungated output by scipy's expit(G) and x by expit(-G)."""
+    from scipy.special import expit
+    r = np.random.default_rng(43)
+    Tk, Hq, Hkv, d = 30, 4, 2, 8
+    q = _rand_bf16(r, (1, 1, Hq, d))
+    k = _rand_bf16(r, (1, Tk, Hkv, d))
+    v = _rand_bf16(r, (1, Tk, Hkv, d))
+    x = _rand_bf16(r, (1, 1, Hq, d))
+    xf = bf16_to_f32(x[0]).astype(np.float64)
+    idx = np.arange(Tk, dtype=np.int32)[None]
+    kv = np.array([Tk])
+    o, lse0 = orc.attention(q, k, v, None, idx, kv, 0.3)
+
+    def run(G, mix=x, sel=idx):
+        return orc.attention(q, k, v, G, sel, kv, 0.3, mix=mix)
+
+    z, lse = run(_bf(np.zeros((1, 1, Hq, d))))
+    assert np.abs(z - (o + xf) / 2).max() < 1e-15
+    assert (lse == lse0).all()
+    big, _ = run(_bf(np.full((1, 1, Hq, d), 30.0)))
+    assert np.abs(big - o).max() <= 1e-12 * np.abs(o).max()
+    small, _ = run(_bf(np.full((1, 1, Hq, d), -30.0)))
+    assert np.abs(small - xf).max() <= 1e-12 * np.abs(xf).max()
+    G = _rand_bf16(r, (1, 1, Hq, d))
+    s = expit(bf16_to_f32(G[0]).astype(np.float64))
+    y, _ = run(G)
+    assert np.abs(y - (s * o + expit(-bf16_to_f32(G[0]).astype(np.float64)) * xf)).max() < 1e-14
+    # x equal to the (bf16-exact) sparse output itself leaves it unchanged
+    k1 = np.array([[7]], np.int32)
+    o1, _ = orc.attention(q, k, v, None, k1, kv, 0.3)
+    same, _ = run(G, mix=bf16_bits(o1.astype(np.float32))[None], sel=k1)
+    assert np.abs(same - o1).max() < 1e-14
+    empty, lse_e = run(G, sel=np.full((1, 5), -1, np.int32))
+    assert np.abs(empty - (1 - s) * xf).max() < 1e-15
+    assert np.isneginf(lse_e).all()
+
+
 # ------------------------------------------------------------------- layer
 
 def pin_layer_dense_rows(orc):
@@ -436,6 +481,31 @@ def pin_layer_composition(orc):
     assert np.abs(res["out"] - out).max() == 0.0
     assert (~valid).sum() == 1 and (res["idx"][~valid] == -1).all()
     assert (res["out"][~valid] == 0).all() and np.isneginf(res["lse"][~valid]).all()
+
+
+def pin_layer_mix(orc):
+    """With another branch's output x in the input, the whole layer equals the
+    unmixed layer's selection followed by the mixed attention step, and an
+    invalid row (no history to select from) gives sigmoid(-G) * x."""
+    from scipy.special import expit
+    import synth
+    cfg = synth.CONFIGS["tiny"].replace(B=2, Tq=6, Tk=70, K=9, decode=False)
+    inp = synth.host_inputs(cfg, seed=6)
+    inp["q_offset"] = np.array([10, 63], np.int32)
+    inp["kv_len"] = np.array([40, 68], np.int32)
+    base = orc.layer(inp, K=9)
+    inp["mix"] = synth.host_mix(cfg, seed=6)
+    res = orc.layer(inp, K=9)
+    assert (res["idx"] == base["idx"]).all() and (res["sel"] == base["sel"]).all()
+    assert np.array_equal(res["lse"], base["lse"])
+    out, _ = orc.attention(inp["q"], inp["k"], inp["v"], inp["gate"], base["idx"],
+                           inp["kv_len"], inp["scale"], mix=inp["mix"])
+    valid = ~np.isneginf(base["lse"][:, 0])
+    assert (~valid).sum() == 1
+    assert np.abs(res["out"][valid] - out[valid]).max() == 0.0
+    G = bf16_to_f32(inp["gate"]).astype(np.float64).reshape(res["out"].shape)
+    x = bf16_to_f32(inp["mix"]).astype(np.float64).reshape(res["out"].shape)
+    assert np.abs(res["out"][~valid] - expit(-G[~valid]) * x[~valid]).max() < 1e-15
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

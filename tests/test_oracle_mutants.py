@@ -32,8 +32,15 @@ MUTANTS = [
     ("gqa_modulo", "int g = h / G;", "int g = h % Hkv;"),
     ("keys_as_values", "o[j] += e * orc_bf16(v[", "o[j] += e * orc_bf16(k["),
     ("no_normalisation", "o[j] /= Z;", ""),
-    ("gate_sign", "o[j] /= 1.0 + exp(-orc_bf16(", "o[j] /= 1.0 + exp(orc_bf16("),
-    ("gate_dropped", "if (gate) o[j] /= 1.0 + exp(-orc_bf16(gate[h * d + j]));", ""),
+    ("gate_sign", "exp(-G)", "exp(G)"),
+    ("gate_dropped", "return s * o + ", "return o + "),
+    ("mix_weight_swapped", "(1.0 - s) * orc_bf16(mix[j])", "s * orc_bf16(mix[j])"),
+    ("mix_of_head0", "mix ? mix + (size_t)h * d : NULL", "mix"),
+    ("empty_row_not_mixed", "            if (lse) lse[h] = -INFINITY;\n        } else {",
+     "            if (lse) lse[h] = -INFINITY;\n            continue;\n        } else {"),
+    ("invalid_row_not_mixed", "mix ? mix + qrow * Hq * d : NULL, j)", "NULL, j)"),
+    ("layer_drops_mix", "NULL, mix ? mix + qrow * Hq * d : NULL, scale,\n                     orow",
+     "NULL, NULL, scale,\n                     orow"),
     ("lse_without_max", "lse[h] = m + log(Z);", "lse[h] = log(Z);"),
     ("padding_read_as_position0", "if (s < 0 || s >= kv_len)", "if (s < 0) s = 0; if (s >= kv_len)"),
     ("overflow_unchecked", "if (acc > INT32_MAX) { acc = INT32_MAX; rc = ORC_OVERFLOW; }", ""),
