@@ -9,7 +9,8 @@
  *   1. a light indexer scores every causal history position for each query,
  *   2. Top-K keeps the K best positions,
  *   3. exact softmax attention runs over those K keys/values only,
- *   4. a sigmoid gate multiplies the output elementwise.
+ *   4. a sigmoid gate multiplies the output elementwise, or weighs it against
+ *      the output of the layer's other (linear or compressed) branch.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. Tensors are
@@ -62,7 +63,7 @@
 extern "C" {
 #endif
 
-#define LCI_ABI_VERSION 1
+#define LCI_ABI_VERSION 2
 
 typedef uint16_t lci_bf16;
 
@@ -129,14 +130,20 @@ lci_status lci_topk_select(const lci_geom *g, const int32_t *scores, int32_t *id
 /* Sparse exact attention + sigmoid gate (steps 3-4). "Hybrid Sparse Attention
  * ...", steps 3-4 and the attention and gating steps of its pseudocode (softmax
  * of the 1/sqrt(d)-scaled dot products with the selected keys, weighting the
- * selected values; the gate multiplies the result); "From Linear Attention
- * ...", section 2 (a query-dependent gate multiplies the attention output).
+ * selected values; the gate multiplies the result, or mixes it with the linear
+ * branch's output); "From Linear Attention ...", section 2 (a query-dependent
+ * gate multiplies the attention output); "How Fine-Grained Sparse Attention
+ * Reshapes ...", section "How Indexer + Top-K Works at Runtime" (the gate
+ * mixes the exact result with a compressed global summary).
  *   q, gate  bf16 [B, Tq, Hq, d]; gate nullable (ungated)
+ *   mix      bf16 [B, Tq, Hq, d], nullable: the other branch's output x to mix
+ *            with; requires gate (NULL error otherwise)
  *   k, v     bf16 [B, Tk, Hkv, d]; query head h reads key/value head h / (Hq/Hkv)
  *   idx      int32 [B, Tq, K]: positions to attend; entries outside 0..kv_len[b]-1
  *            (the -1 padding) are skipped; duplicates count once each; order is free
- *   out      bf16 [B, Tq, Hq, d] out: sigmoid(gate) * softmax(scale*q.k) v,
- *            fp32 accumulation, rounded to nearest even; 0 for a row without entries
+ *   out      bf16 [B, Tq, Hq, d] out: s*o, or s*o + (1-s)*x with mix, where
+ *            s = sigmoid(gate) (1 ungated) and o = softmax(scale*q.k) v (0 for
+ *            a row without entries); fp32 arithmetic, rounded to nearest even
  *   lse      fp32 [B, Tq, Hq] out, nullable: natural log of the softmax
  *            denominator of scale*q.k (-inf for a row without entries)
  *   softmax_scale  positive and finite (1/sqrt(d) in the pages), else SHAPE
@@ -144,8 +151,8 @@ lci_status lci_topk_select(const lci_geom *g, const int32_t *scores, int32_t *id
  * Errors: NULL, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN, HIP. */
 lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_bf16 *k,
                                const lci_bf16 *v, const int32_t *idx, const lci_bf16 *gate,
-                               float softmax_scale, lci_bf16 *out, float *lse,
-                               void *workspace, size_t ws_bytes, void *stream);
+                               const lci_bf16 *mix, float softmax_scale, lci_bf16 *out,
+                               float *lse, void *workspace, size_t ws_bytes, void *stream);
 
 /* Fused prefill: steps 1-4 for many query rows per sequence in one call
  * ("Hybrid Sparse Attention ...", section "Engineering and Evaluation
@@ -157,9 +164,9 @@ lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_b
 lci_status lci_prefill_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
                            const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
                            const lci_bf16 *q, const lci_bf16 *k, const lci_bf16 *v,
-                           const lci_bf16 *gate, float softmax_scale, lci_bf16 *out,
-                           float *lse, int32_t *idx_out, void *workspace, size_t ws_bytes,
-                           void *stream);
+                           const lci_bf16 *gate, const lci_bf16 *mix, float softmax_scale,
+                           lci_bf16 *out, float *lse, int32_t *idx_out, void *workspace,
+                           size_t ws_bytes, void *stream);
 
 /* Fused decode: one query row per sequence (Tq == 1) over a long history, with
  * the history split across workgroups for scoring, an exact two-level Top-K
@@ -172,9 +179,9 @@ lci_status lci_prefill_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t 
 lci_status lci_decode_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
                           const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
                           const lci_bf16 *q, const lci_bf16 *k, const lci_bf16 *v,
-                          const lci_bf16 *gate, float softmax_scale, lci_bf16 *out,
-                          float *lse, int32_t *idx_out, void *workspace, size_t ws_bytes,
-                          void *stream);
+                          const lci_bf16 *gate, const lci_bf16 *mix, float softmax_scale,
+                          lci_bf16 *out, float *lse, int32_t *idx_out, void *workspace,
+                          size_t ws_bytes, void *stream);
 
 /* Workspace bytes an entry needs for this geometry (host only, reads no device
  * memory). Returns 0 for an invalid geometry or entry id. */

@@ -2,11 +2,11 @@
 
 A thin ctypes binding over liblci.so, the HIP library whose C ABI is declared in
 include/lci.h. Every step of the layer (indexer scoring, Top-K selection, sparse
-attention, sigmoid gate) runs in the library's kernels; this module only checks
-tensor dtypes/shapes/contiguity, passes device pointers and the current HIP
-stream, and turns status codes into exceptions. PyTorch supplies device memory
-and streams. There is no CPU fallback: without the built library every call
-raises.
+attention, sigmoid gate and its mix with another branch) runs in the library's
+kernels; this module only checks tensor dtypes/shapes/contiguity, passes device
+pointers and the current HIP stream, and turns status codes into exceptions.
+PyTorch supplies device memory and streams. There is no CPU fallback: without
+the built library every call raises.
 
 Entry points (same names as the C ABI, without the ``lci_`` prefix):
     idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd,
@@ -22,6 +22,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblci.so")
 
 ENTRY_IDX_SCORE, ENTRY_TOPK_SELECT, ENTRY_SPARSE_ATTN, ENTRY_PREFILL, ENTRY_DECODE = range(5)
+
+# LCI_ABI_VERSION of the signatures declared below
+ABI_VERSION = 2
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
            "lci_decode_fwd", "lci_workspace_bytes", "lci_status_str", "lci_last_hip_error",
@@ -61,8 +64,8 @@ def load_library(path: str = LIB_PATH):
     G = ctypes.POINTER(lci_geom)
     lib.lci_idx_score.argtypes = [G, P, P, P, i64, i64, P, P]
     lib.lci_topk_select.argtypes = [G, P, P, P, P, sz, P]
-    lib.lci_sparse_attn_fwd.argtypes = [G, P, P, P, P, P, ctypes.c_float, P, P, P, sz, P]
-    fused = [G, P, P, P, i64, i64, P, P, P, P, ctypes.c_float, P, P, P, P, sz, P]
+    lib.lci_sparse_attn_fwd.argtypes = [G, P, P, P, P, P, P, ctypes.c_float, P, P, P, sz, P]
+    fused = [G, P, P, P, i64, i64, P, P, P, P, P, ctypes.c_float, P, P, P, P, sz, P]
     lib.lci_prefill_fwd.argtypes = fused
     lib.lci_decode_fwd.argtypes = fused
     lib.lci_workspace_bytes.argtypes = [ctypes.c_int, G]
@@ -71,6 +74,9 @@ def load_library(path: str = LIB_PATH):
     lib.lci_status_str.restype = ctypes.c_char_p
     lib.lci_last_hip_error.restype = ctypes.c_int
     lib.lci_abi_version.restype = ctypes.c_int
+    if lib.lci_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.lci_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild it")
     lib.lci_kernel_timing.argtypes = [ctypes.c_int]
     lib.lci_kernel_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_int64)]
@@ -213,22 +219,23 @@ def topk_select(scores, K, q_offset, kv_len, idx=None, sel_scores=None, want_sco
 
 
 def sparse_attn_fwd(q, k, v, idx, gate, scale, kv_len, q_offset=None, out=None, lse=None,
-                    want_lse=False, workspace=None, stream=None):
-    """Gated attention over the listed positions: out bf16 [B,Tq,Hq,d] (and lse)."""
+                    want_lse=False, workspace=None, stream=None, mix=None):
+    """Gated attention over the listed positions: out bf16 [B,Tq,Hq,d] (and lse).
+    With ``mix`` (bf16, the shape of q) the gate mixes: s*o + (1-s)*mix."""
     import torch
     _dev(q, torch.bfloat16, "q", 4)
     _dev(k, torch.bfloat16, "k", 4)
     _dev(v, torch.bfloat16, "v", 4)
     _dev(idx, torch.int32, "idx", 3)
     _dev(gate, torch.bfloat16, "gate", 4)
+    _dev(mix, torch.bfloat16, "mix", 4)
     B, Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, Tk, Hkv, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k, v must be [B,Tk,Hkv,d]")
     if idx.shape[:2] != (B, Tq):
         raise ValueError("idx must be [B,Tq,K]")
-    if gate is not None and tuple(gate.shape) != tuple(q.shape):
-        raise ValueError("gate must match q")
+    _gate_args(q, gate, mix)
     if q_offset is None:
         q_offset = torch.zeros(B, dtype=torch.int32, device=q.device)
     g = make_geom(B, Tq, Tk, idx.shape[2], q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d)
@@ -241,12 +248,21 @@ def sparse_attn_fwd(q, k, v, idx, gate, scale, kv_len, q_offset=None, out=None, 
     ws, nb = _workspace(ENTRY_SPARSE_ATTN, g, workspace, q.device)
     lib = load_library()
     _check(lib.lci_sparse_attn_fwd(ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
-                                   _ptr(gate), float(scale), _ptr(out), _ptr(lse), _ptr(ws), nb,
-                                   _stream(stream)))
+                                   _ptr(gate), _ptr(mix), float(scale), _ptr(out), _ptr(lse),
+                                   _ptr(ws), nb, _stream(stream)))
     return (out, lse) if lse is not None else out
 
 
-def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K,
+def _gate_args(q, gate, mix):
+    if gate is not None and tuple(gate.shape) != tuple(q.shape):
+        raise ValueError("gate must match q")
+    if mix is not None and tuple(mix.shape) != tuple(q.shape):
+        raise ValueError("mix must match q")
+    if mix is not None and gate is None:
+        raise ValueError("mix needs a gate")
+
+
+def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset, kv_len, K,
            out, lse, idx_out, want_lse, want_idx, workspace, stream):
     import torch
     _dev(q_idx, torch.int8, "q_idx", 4)
@@ -256,6 +272,7 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_l
     _dev(k, torch.bfloat16, "k", 4)
     _dev(v, torch.bfloat16, "v", 4)
     _dev(gate, torch.bfloat16, "gate", 4)
+    _dev(mix, torch.bfloat16, "mix", 4)
     B, Tq, H_I, d_I = q_idx.shape
     Tk = k_idx.shape[1]
     _, _, Hq, d = q.shape
@@ -263,8 +280,7 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_l
     if tuple(q.shape[:2]) != (B, Tq) or tuple(k.shape) != (B, Tk, Hkv, d) or \
             tuple(v.shape) != tuple(k.shape) or tuple(k_idx.shape) != (B, Tk, d_I):
         raise ValueError("inconsistent shapes")
-    if gate is not None and tuple(gate.shape) != tuple(q.shape):
-        raise ValueError("gate must match q")
+    _gate_args(q, gate, mix)
     wsb, wsq = _w_strides(w, B, Tq, H_I)
     g = make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d, H_I=H_I, d_I=d_I)
     if out is None:
@@ -279,8 +295,9 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_l
     ws, nb = _workspace(entry, g, workspace, q.device)
     lib = load_library()
     _check(getattr(lib, fn_name)(ctypes.byref(g), _ptr(q_idx), _ptr(k_idx), _ptr(w), wsb, wsq,
-                                 _ptr(q), _ptr(k), _ptr(v), _ptr(gate), float(scale), _ptr(out),
-                                 _ptr(lse), _ptr(idx_out), _ptr(ws), nb, _stream(stream)))
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(mix), float(scale),
+                                 _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), nb,
+                                 _stream(stream)))
     res = [out]
     if idx_out is not None:
         res.append(idx_out)
@@ -290,14 +307,18 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_l
 
 
 def prefill_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None, lse=None,
-                idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None):
-    """Fused layer for many query rows: returns out (and idx, lse when asked)."""
-    return _fused("lci_prefill_fwd", ENTRY_PREFILL, q_idx, k_idx, w, q, k, v, gate, scale,
+                idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None,
+                mix=None):
+    """Fused layer for many query rows: returns out (and idx, lse when asked).
+    ``mix`` as in ``sparse_attn_fwd``."""
+    return _fused("lci_prefill_fwd", ENTRY_PREFILL, q_idx, k_idx, w, q, k, v, gate, mix, scale,
                   q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream)
 
 
 def decode_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None, lse=None,
-               idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None):
-    """Fused layer for one query row per sequence (Tq == 1) over a long history."""
-    return _fused("lci_decode_fwd", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, scale,
+               idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None,
+               mix=None):
+    """Fused layer for one query row per sequence (Tq == 1) over a long history.
+    ``mix`` as in ``sparse_attn_fwd``."""
+    return _fused("lci_decode_fwd", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, mix, scale,
                   q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream)

@@ -20,6 +20,7 @@ size_t dense_workspace(const Geom& g);
 // rows all qualify and marks those blocks done for the gather kernel.
 hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                             const uint16_t* mix,
                              float scale, uint16_t* out, float* lse, void* ws, bool masks_ready,
                              hipStream_t st);
 

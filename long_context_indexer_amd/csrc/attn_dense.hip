@@ -33,7 +33,8 @@
 //                      O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, with V^T read
 //                            by ds_read_b64_tr_b16 (each 16-lane group reads a
 //                            4-key x 16-feature block transposed into registers).
-//                    The epilogue applies sigmoid(gate) and stores bf16.
+//                    The epilogue applies the gate (sigmoid(gate) * o, or
+//                    mixed with the other branch's output) and stores bf16.
 // K and V tiles use an XOR-swizzled LDS layout that keeps every access pattern
 // free of bank conflicts. Workgroups are placed so that each XCD (its own L2)
 // serves one key/value head (blockIdx.x % 8 picks the XCD), and the longest
@@ -170,12 +171,16 @@ constexpr float kRescaleLog2 = 8.0f;
 // EXACT_L: the softmax denominator sums the fp32 probabilities (needed for the
 // log-sum-exp output). Otherwise it sums the bf16-rounded ones that enter the
 // PV product, two per dot-product instruction.
-template <int D, int G, bool EXACT_L>
+// MIX: the gate mixes the output with the other branch's (mix non-null). A
+// template flag, not a runtime test: the extra epilogue registers change the
+// allocation of the main loop, which costs the unmixed kernel about 4%.
+template <int D, int G, bool EXACT_L, bool MIX>
 __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     int Tq, int Tk, int Hq, int Hkv, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ gate, const uint32_t* __restrict__ mask, int Wm,
+    const uint16_t* __restrict__ gate, const uint16_t* __restrict__ mix,
+    const uint32_t* __restrict__ mask, int Wm,
     const uint8_t* __restrict__ flag, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, uint8_t* __restrict__ done, int nbps, int nblk) {
   using C = DenseCfg<D, G>;
@@ -434,8 +439,9 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   if (!rv || fl == kRowGather) return;  // an empty row (nothing kept) writes 0 and -inf
   const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
   const int64_t obase = (qrow * Hq + h) * D;
-  // every gate load is issued before any is used (one memory latency, not one
-  // per 8-byte piece); bf16 0 = logit 0 is never read without a gate
+  // every gate (and mix) load is issued before any is used (one memory
+  // latency, not one per 8-byte piece); bf16 0 = logit 0 is never read
+  // without a gate
   v2i graw[C::NDT][4] = {};
   if (gate) {
 #pragma unroll
@@ -443,6 +449,14 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
         graw[dt][ii] = *reinterpret_cast<const v2i*>(gate + obase + 32 * dt + 8 * ii + 4 * hf);
+  }
+  v2i xraw[MIX ? C::NDT : 1][4] = {};
+  if constexpr (MIX) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        xraw[dt][ii] = *reinterpret_cast<const v2i*>(mix + obase + 32 * dt + 8 * ii + 4 * hf);
   }
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)
@@ -458,11 +472,24 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
         gv[2] = sigmoidf(bf16_to_f32(g23 & 0xffff));
         gv[3] = sigmoidf(bf16_to_f32(g23 >> 16));
       }
-      const uint32_t w0 = f32_to_bf16(o[dt][4 * ii] * inv * gv[0]) |
-                          (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * ii + 1] * inv * gv[1])) << 16);
-      const uint32_t w1 = f32_to_bf16(o[dt][4 * ii + 2] * inv * gv[2]) |
-                          (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * ii + 3] * inv * gv[3])) << 16);
-      *reinterpret_cast<int2*>(out + obase + d) = make_int2(static_cast<int>(w0), static_cast<int>(w1));
+      if constexpr (MIX) {
+        const uint32_t x01 = static_cast<uint32_t>(xraw[dt][ii].x);
+        const uint32_t x23 = static_cast<uint32_t>(xraw[dt][ii].y);
+        const uint16_t xs[4] = {static_cast<uint16_t>(x01), static_cast<uint16_t>(x01 >> 16),
+                                static_cast<uint16_t>(x23), static_cast<uint16_t>(x23 >> 16)};
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = gate_mix(o[dt][4 * ii + e] * inv, gv[e], xs[e]);
+        const uint32_t w0 = f32_to_bf16(y[0]) | (static_cast<uint32_t>(f32_to_bf16(y[1])) << 16);
+        const uint32_t w1 = f32_to_bf16(y[2]) | (static_cast<uint32_t>(f32_to_bf16(y[3])) << 16);
+        *reinterpret_cast<int2*>(out + obase + d) = make_int2(static_cast<int>(w0), static_cast<int>(w1));
+      } else {
+        const uint32_t w0 = f32_to_bf16(o[dt][4 * ii] * inv * gv[0]) |
+                            (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * ii + 1] * inv * gv[1])) << 16);
+        const uint32_t w1 = f32_to_bf16(o[dt][4 * ii + 2] * inv * gv[2]) |
+                            (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * ii + 3] * inv * gv[3])) << 16);
+        *reinterpret_cast<int2*>(out + obase + d) = make_int2(static_cast<int>(w0), static_cast<int>(w1));
+      }
     }
   if (lse && hf == 0) lse[qrow * Hq + h] = lsum > 0.f ? (m * scale_log2 + fast_log2(lsum)) * LN2 : -INFINITY;
 }
@@ -497,9 +524,10 @@ DenseMasks dense_masks(const Geom& g, void* ws) {
   return d;
 }
 
-template <int D, int G, bool EXACT_L>
+template <int D, int G, bool EXACT_L, bool MIX>
 static hipError_t launch_dense_k(const Geom& g, const uint16_t* q, const uint16_t* k,
-                                  const uint16_t* v, const uint16_t* gate, float scale,
+                                  const uint16_t* v, const uint16_t* gate,
+                                  const uint16_t* mix, float scale,
                                   uint16_t* out, float* lse, const DenseMasks& dm,
                                   hipStream_t st) {
   using C = DenseCfg<D, G>;
@@ -509,8 +537,9 @@ static hipError_t launch_dense_k(const Geom& g, const uint16_t* q, const uint16_
   const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
   {
     KernelTimer timer(LCI_KERNEL_ATTN_DENSE, st);
-    hipLaunchKernelGGL((attn_dense_kernel<D, G, EXACT_L>), dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, st,
-                       g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, dm.mask,
+    hipLaunchKernelGGL((attn_dense_kernel<D, G, EXACT_L, MIX>), dim3(static_cast<uint32_t>(nwg)),
+                       dim3(256), 0, st,
+                       g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, mix, dm.mask,
                        dm.Wm, dm.flag, scale * LOG2E, out, lse, dm.done, nbps, nblk);
   }
   return hipGetLastError();
@@ -518,29 +547,35 @@ static hipError_t launch_dense_k(const Geom& g, const uint16_t* q, const uint16_
 
 template <int D, int G>
 static hipError_t launch_dense_dg(const Geom& g, const uint16_t* q, const uint16_t* k,
-                                  const uint16_t* v, const uint16_t* gate, float scale,
+                                  const uint16_t* v, const uint16_t* gate,
+                                  const uint16_t* mix, float scale,
                                   uint16_t* out, float* lse, const DenseMasks& dm,
                                   hipStream_t st) {
-  return lse ? launch_dense_k<D, G, true>(g, q, k, v, gate, scale, out, lse, dm, st)
-             : launch_dense_k<D, G, false>(g, q, k, v, gate, scale, out, lse, dm, st);
+  if (gate && mix)
+    return lse ? launch_dense_k<D, G, true, true>(g, q, k, v, gate, mix, scale, out, lse, dm, st)
+               : launch_dense_k<D, G, false, true>(g, q, k, v, gate, mix, scale, out, lse, dm, st);
+  return lse ? launch_dense_k<D, G, true, false>(g, q, k, v, gate, nullptr, scale, out, lse, dm, st)
+             : launch_dense_k<D, G, false, false>(g, q, k, v, gate, nullptr, scale, out, lse, dm, st);
 }
 
 template <int D>
 static hipError_t launch_dense_d(const Geom& g, const uint16_t* q, const uint16_t* k,
-                                 const uint16_t* v, const uint16_t* gate, float scale,
+                                 const uint16_t* v, const uint16_t* gate,
+                                 const uint16_t* mix, float scale,
                                  uint16_t* out, float* lse, const DenseMasks& dm, hipStream_t st) {
   switch (g.Hq / g.Hkv) {
-    case 1: return launch_dense_dg<D, 1>(g, q, k, v, gate, scale, out, lse, dm, st);
-    case 2: return launch_dense_dg<D, 2>(g, q, k, v, gate, scale, out, lse, dm, st);
-    case 4: return launch_dense_dg<D, 4>(g, q, k, v, gate, scale, out, lse, dm, st);
-    case 8: return launch_dense_dg<D, 8>(g, q, k, v, gate, scale, out, lse, dm, st);
-    case 16: return launch_dense_dg<D, 16>(g, q, k, v, gate, scale, out, lse, dm, st);
+    case 1: return launch_dense_dg<D, 1>(g, q, k, v, gate, mix, scale, out, lse, dm, st);
+    case 2: return launch_dense_dg<D, 2>(g, q, k, v, gate, mix, scale, out, lse, dm, st);
+    case 4: return launch_dense_dg<D, 4>(g, q, k, v, gate, mix, scale, out, lse, dm, st);
+    case 8: return launch_dense_dg<D, 8>(g, q, k, v, gate, mix, scale, out, lse, dm, st);
+    case 16: return launch_dense_dg<D, 16>(g, q, k, v, gate, mix, scale, out, lse, dm, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                             const uint16_t* mix,
                              float scale, uint16_t* out, float* lse, void* ws, bool masks_ready,
                              hipStream_t st) {
   const DenseMasks dm = dense_masks(g, ws);
@@ -553,8 +588,8 @@ hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (g.d) {
-    case 64: return launch_dense_d<64>(g, q, k, v, gate, scale, out, lse, dm, st);
-    case 128: return launch_dense_d<128>(g, q, k, v, gate, scale, out, lse, dm, st);
+    case 64: return launch_dense_d<64>(g, q, k, v, gate, mix, scale, out, lse, dm, st);
+    case 128: return launch_dense_d<128>(g, q, k, v, gate, mix, scale, out, lse, dm, st);
     default: return hipErrorInvalidValue;
   }
 }

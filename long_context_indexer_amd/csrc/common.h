@@ -47,6 +47,13 @@ __device__ __forceinline__ float sigmoidf(float x) {
   return fast_rcp(1.0f + fast_exp2(-x * LOG2E));
 }
 
+// The gate mixing an attention output o with the other branch's output x
+// (bf16) by s = sigmoid(G): s*o + (1 - s)*x, computed as x + s*(o - x).
+__device__ __forceinline__ float gate_mix(float o, float s, uint16_t x) {
+  const float xf = bf16_to_f32(x);
+  return fmaf(s, o - xf, xf);
+}
+
 // Order-preserving map of int32 scores to uint32 keys (sign bit flipped).
 __device__ __forceinline__ uint32_t score_key(int32_t s) {
   return static_cast<uint32_t>(s) ^ 0x80000000u;

@@ -17,7 +17,8 @@ struct DecLayout {
 DecLayout decode_layout(const Geom& g);
 hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                          const int8_t* w, int64_t wsb, const uint16_t* q, const uint16_t* k,
-                         const uint16_t* v, const uint16_t* gate, float scale, uint16_t* out,
+                         const uint16_t* v, const uint16_t* gate,
+                         const uint16_t* mix, float scale, uint16_t* out,
                          float* lse, int32_t* idx_out, void* workspace, hipStream_t stream);
 
 }  // namespace lci

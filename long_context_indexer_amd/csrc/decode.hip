@@ -587,7 +587,8 @@ static hipError_t launch_score_h(const Geom& g, const int8_t* q_idx, const int8_
 
 hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                          const int8_t* w, int64_t wsb, const uint16_t* q, const uint16_t* k,
-                         const uint16_t* v, const uint16_t* gate, float scale, uint16_t* out,
+                         const uint16_t* v, const uint16_t* gate,
+                         const uint16_t* mix, float scale, uint16_t* out,
                          float* lse, int32_t* idx_out, void* workspace, hipStream_t st) {
   const DecLayout L = decode_layout(g);
   char* ws = static_cast<char*>(workspace);
@@ -636,7 +637,8 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
                        g.q_offset, g.kv_len, S, thr, off, L.nchunks, g.K, idx);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_sparse_attn(g, q, k, v, idx, gate, scale, out, lse, L.splits, ws + L.attn, false,
+  return launch_sparse_attn(g, q, k, v, idx, gate, mix, scale, out, lse, L.splits, ws + L.attn,
+                            false,
                             st);
 }
 

@@ -77,6 +77,7 @@ int sparse_attn_pick_splits(const Geom& g);
 // not scanned again.
 hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                              const uint16_t* mix,
                               float scale, uint16_t* out, float* lse, int splits,
                               void* workspace, bool masks_ready, hipStream_t stream);
 

@@ -173,40 +173,42 @@ lci_status lci_topk_select(const lci_geom* g, const int32_t* scores, int32_t* id
 
 lci_status lci_sparse_attn_fwd(const lci_geom* g, const lci_bf16* q, const lci_bf16* k,
                                const lci_bf16* v, const int32_t* idx, const lci_bf16* gate,
-                               float softmax_scale, lci_bf16* out, float* lse,
-                               void* workspace, size_t ws_bytes, void* stream) {
+                               const lci_bf16* mix, float softmax_scale, lci_bf16* out,
+                               float* lse, void* workspace, size_t ws_bytes, void* stream) {
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
-  if (!q || !k || !v || !idx || !out) return LCI_ERR_NULL;
+  if (!q || !k || !v || !idx || !out || (mix && !gate)) return LCI_ERR_NULL;
   if (!scale_ok(softmax_scale)) return LCI_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-      (gate && !aligned16(gate)) || !aligned4(idx) || (lse && !aligned4(lse)))
+      (gate && !aligned16(gate)) || (mix && !aligned16(mix)) || !aligned4(idx) ||
+      (lse && !aligned4(lse)))
     return LCI_ERR_ALIGN;
   const Geom gg = to_geom(g);
   const int splits = lci::sparse_attn_pick_splits(gg);
   const size_t need = lci::sparse_attn_workspace(gg, splits);
   if (need > 0 && (!workspace || ws_bytes < need)) return LCI_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return LCI_ERR_ALIGN;
-  return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, softmax_scale, out, lse,
-                                            splits, workspace, false,
+  return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, mix, softmax_scale, out,
+                                            lse, splits, workspace, false,
                                             static_cast<hipStream_t>(stream)));
 }
 
 static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
                                 const int8_t* w, int64_t wsb, int64_t wsq, const lci_bf16* q,
                                 const lci_bf16* k, const lci_bf16* v, const lci_bf16* gate,
-                                float scale, lci_bf16* out, float* lse, int32_t* idx_out,
-                                void* workspace, size_t ws_bytes, void* stream) {
+                                const lci_bf16* mix, float scale, lci_bf16* out, float* lse,
+                                int32_t* idx_out, void* workspace, size_t ws_bytes,
+                                void* stream) {
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if ((s = check_indexer(g)) != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
-  if (!q_idx || !k_idx || !w || !q || !k || !v || !out) return LCI_ERR_NULL;
+  if (!q_idx || !k_idx || !w || !q || !k || !v || !out || (mix && !gate)) return LCI_ERR_NULL;
   if (wsb < 0 || wsq < 0 || !scale_ok(scale)) return LCI_ERR_SHAPE;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(k) ||
       !aligned16(v) || !aligned16(out) || (gate && !aligned16(gate)) ||
-      (lse && !aligned4(lse)) || (idx_out && !aligned4(idx_out)))
+      (mix && !aligned16(mix)) || (lse && !aligned4(lse)) || (idx_out && !aligned4(idx_out)))
     return LCI_ERR_ALIGN;
   const PrefillLayout L = prefill_layout(g);
   if (!workspace || ws_bytes < L.total) return LCI_ERR_WORKSPACE;
@@ -227,26 +229,26 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
     e = lci::launch_topk_rows(gg, sc, g->Tk, r0, rc, idx, nullptr, masks ? &dm : nullptr, st);
     if (e != hipSuccess) return hip_status(e);
   }
-  return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, scale, out, lse, L.splits,
-                                            ws + L.attn_off, masks, st));
+  return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, mix, scale, out, lse,
+                                            L.splits, ws + L.attn_off, masks, st));
 }
 
 lci_status lci_prefill_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
                            const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
                            const lci_bf16* q, const lci_bf16* k, const lci_bf16* v,
-                           const lci_bf16* gate, float softmax_scale, lci_bf16* out,
-                           float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
-                           void* stream) {
-  return fused_forward(g, q_idx, k_idx, w, w_stride_b, w_stride_q, q, k, v, gate,
+                           const lci_bf16* gate, const lci_bf16* mix, float softmax_scale,
+                           lci_bf16* out, float* lse, int32_t* idx_out, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  return fused_forward(g, q_idx, k_idx, w, w_stride_b, w_stride_q, q, k, v, gate, mix,
                        softmax_scale, out, lse, idx_out, workspace, ws_bytes, stream);
 }
 
 lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
                           const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
                           const lci_bf16* q, const lci_bf16* k, const lci_bf16* v,
-                          const lci_bf16* gate, float softmax_scale, lci_bf16* out,
-                          float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
-                          void* stream) {
+                          const lci_bf16* gate, const lci_bf16* mix, float softmax_scale,
+                          lci_bf16* out, float* lse, int32_t* idx_out, void* workspace,
+                          size_t ws_bytes, void* stream) {
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if (g->Tq != 1) return LCI_ERR_SHAPE;
@@ -254,17 +256,17 @@ lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* 
   if ((s = check_attention(g)) != LCI_OK) return s;
   if (static_cast<int64_t>(g->Tk) > static_cast<int64_t>(lci::kDecChunk) * lci::kDecMaxChunks)
     return LCI_ERR_SHAPE;
-  if (!q_idx || !k_idx || !w || !q || !k || !v || !out) return LCI_ERR_NULL;
+  if (!q_idx || !k_idx || !w || !q || !k || !v || !out || (mix && !gate)) return LCI_ERR_NULL;
   if (w_stride_b < 0 || w_stride_q < 0) return LCI_ERR_SHAPE;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(k) ||
       !aligned16(v) || !aligned16(out) || (gate && !aligned16(gate)) ||
-      (lse && !aligned4(lse)) || (idx_out && !aligned4(idx_out)))
+      (mix && !aligned16(mix)) || (lse && !aligned4(lse)) || (idx_out && !aligned4(idx_out)))
     return LCI_ERR_ALIGN;
   const Geom gg = to_geom(g);
   const lci::DecLayout L = lci::decode_layout(gg);
   if (!workspace || ws_bytes < L.total) return LCI_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LCI_ERR_ALIGN;
-  return hip_status(lci::launch_decode(gg, q_idx, k_idx, w, w_stride_b, q, k, v, gate,
+  return hip_status(lci::launch_decode(gg, q_idx, k_idx, w, w_stride_b, q, k, v, gate, mix,
                                        softmax_scale, out, lse, idx_out, workspace,
                                        static_cast<hipStream_t>(stream)));
 }

@@ -20,9 +20,11 @@
 //     avoid bank conflicts) and reads them transposed as the A operand.
 // Every per-head statistic lives in the lane that owns that head's column, so
 // rescaling needs no cross-lane traffic; the softmax denominator is kept per
-// lane and reduced once at the end. With one split the epilogue applies
-// sigmoid(gate) and stores bf16; with several splits each writes (m, l, O) and
-// a combine kernel merges them in split order (deterministic).
+// lane and reduced once at the end. With one split the epilogue applies the
+// gate (sigmoid(gate) * o, or s*o + (1-s)*x mixed with the other branch's
+// output x: the fusion step and pseudocode of the same section) and stores
+// bf16; with several splits each writes (m, l, O) and a combine kernel merges
+// them in split order (deterministic) and applies the gate.
 #include "attn_dense.h"
 #include "common.h"
 #include "../../include/lci.h"
@@ -51,6 +53,7 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(int Hq, int splits,
                                                            const float* __restrict__ part,
                                                            const uint16_t* __restrict__ gate,
+                                                           const uint16_t* __restrict__ mix,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ lse) {
   using C = AttnCfg<D>;
@@ -85,8 +88,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(int Hq, int splits,
   float y0 = a0 * inv, y1 = a1 * inv;
   if (gate) {
     const uint32_t g01 = *reinterpret_cast<const uint32_t*>(gate + obase);
-    y0 *= sigmoidf(bf16_to_f32(g01 & 0xffff));
-    y1 *= sigmoidf(bf16_to_f32(g01 >> 16));
+    const float s0 = sigmoidf(bf16_to_f32(g01 & 0xffff));
+    const float s1 = sigmoidf(bf16_to_f32(g01 >> 16));
+    if (mix) {
+      const uint32_t x01 = *reinterpret_cast<const uint32_t*>(mix + obase);
+      y0 = gate_mix(y0, s0, x01 & 0xffff);
+      y1 = gate_mix(y1, s1, x01 >> 16);
+    } else {
+      y0 *= s0;
+      y1 *= s1;
+    }
   }
   *reinterpret_cast<uint32_t*>(out + obase) =
       f32_to_bf16(y0) | (static_cast<uint32_t>(f32_to_bf16(y1)) << 16);
@@ -98,7 +109,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
     int Tq, int Tk, int K, int Hq, int Hkv, int G, const int32_t* __restrict__ kv_len,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
-    const uint16_t* __restrict__ gate, float scale_log2, uint16_t* __restrict__ out,
+    const uint16_t* __restrict__ gate, const uint16_t* __restrict__ mix, float scale_log2,
+    uint16_t* __restrict__ out,
     float* __restrict__ lse, int splits, int per_split, float* __restrict__ part,
     const uint8_t* __restrict__ done, int dbq, int64_t nitems) {
   using C = AttnCfg<D>;
@@ -278,11 +290,16 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   {
     const float inv = lsum > 0.f ? fast_rcp(lsum) : 0.f;
     const int64_t obase = (qrow * Hq + h) * D + 4 * grp;
-    // all gate loads in flight together (one memory latency)
-    v2i gl[C::NJB] = {};
+    // all gate (and mix) loads in flight together (one memory latency)
+    v2i gl[C::NJB] = {}, xl[C::NJB] = {};
     if (gate) {
 #pragma unroll
       for (int jb = 0; jb < C::NJB; ++jb) gl[jb] = *reinterpret_cast<const v2i*>(gate + obase + 16 * jb);
+      if (mix) {
+#pragma unroll
+        for (int jb = 0; jb < C::NJB; ++jb)
+          xl[jb] = *reinterpret_cast<const v2i*>(mix + obase + 16 * jb);
+      }
     }
 #pragma unroll
     for (int jb = 0; jb < C::NJB; ++jb) {
@@ -294,8 +311,19 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
         gv[2] = sigmoidf(bf16_to_f32(g23 & 0xffff));
         gv[3] = sigmoidf(bf16_to_f32(g23 >> 16));
       }
-      uint32_t w0 = f32_to_bf16(o[jb][0] * inv * gv[0]) | (static_cast<uint32_t>(f32_to_bf16(o[jb][1] * inv * gv[1])) << 16);
-      uint32_t w1 = f32_to_bf16(o[jb][2] * inv * gv[2]) | (static_cast<uint32_t>(f32_to_bf16(o[jb][3] * inv * gv[3])) << 16);
+      float y[4];
+      if (mix) {
+        const uint32_t x01 = static_cast<uint32_t>(xl[jb].x), x23 = static_cast<uint32_t>(xl[jb].y);
+        const uint16_t xs[4] = {static_cast<uint16_t>(x01), static_cast<uint16_t>(x01 >> 16),
+                                static_cast<uint16_t>(x23), static_cast<uint16_t>(x23 >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = gate_mix(o[jb][e] * inv, gv[e], xs[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = o[jb][e] * inv * gv[e];
+      }
+      uint32_t w0 = f32_to_bf16(y[0]) | (static_cast<uint32_t>(f32_to_bf16(y[1])) << 16);
+      uint32_t w1 = f32_to_bf16(y[2]) | (static_cast<uint32_t>(f32_to_bf16(y[3])) << 16);
       *reinterpret_cast<int2*>(out + obase + 16 * jb) = make_int2(static_cast<int>(w0), static_cast<int>(w1));
     }
     if (lse && grp == 0) lse[qrow * Hq + h] = lex > 0.f ? (m + fast_log2(lex)) * LN2 : -INFINITY;
@@ -322,6 +350,7 @@ size_t sparse_attn_workspace(const Geom& g, int splits) {
 template <int D>
 static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                           const uint16_t* mix,
                            float scale, uint16_t* out, float* lse, int splits, void* ws,
                            bool masks_ready, hipStream_t st) {
   using C = AttnCfg<D>;
@@ -330,7 +359,8 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   per_split = (per_split + 15) / 16 * 16;
   const uint8_t* done = nullptr;
   if (splits == 1) {
-    hipError_t e0 = launch_dense_attn(g, q, k, v, idx, gate, scale, out, lse, ws, masks_ready, st);
+    hipError_t e0 =
+        launch_dense_attn(g, q, k, v, idx, gate, mix, scale, out, lse, ws, masks_ready, st);
     if (e0 != hipSuccess) return e0;
     const DenseMasks dm = dense_masks(g, ws);
     // masks from the Top-K kernel and histories no longer than lim: every row
@@ -346,7 +376,7 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   {
     KernelTimer timer(LCI_KERNEL_ATTN_GATHER, st);
     hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * g.Hkv), lds, st, g.Tq, g.Tk, g.K,
-                       g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, scale * LOG2E, out, lse,
+                       g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, mix, scale * LOG2E, out, lse,
                        splits, per_split, static_cast<float*>(ws), done, dense_block_rows(G),
                        nitems);
   }
@@ -356,18 +386,21 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   {
     KernelTimer timer(LCI_KERNEL_ATTN_COMBINE, st);
     hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(256), 0, st, g.Hq, splits,
-                       static_cast<const float*>(ws), gate, out, lse);
+                       static_cast<const float*>(ws), gate, mix, out, lse);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                              const uint16_t* mix,
                               float scale, uint16_t* out, float* lse, int splits, void* ws,
                               bool masks_ready, hipStream_t st) {
   switch (g.d) {
-    case 64: return launch_d<64>(g, q, k, v, idx, gate, scale, out, lse, splits, ws, masks_ready, st);
-    case 128: return launch_d<128>(g, q, k, v, idx, gate, scale, out, lse, splits, ws, masks_ready, st);
+    case 64:
+      return launch_d<64>(g, q, k, v, idx, gate, mix, scale, out, lse, splits, ws, masks_ready, st);
+    case 128:
+      return launch_d<128>(g, q, k, v, idx, gate, mix, scale, out, lse, splits, ws, masks_ready, st);
     default: return hipErrorInvalidValue;
   }
 }

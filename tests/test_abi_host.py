@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.lci_abi_version() == 1
+    assert lib.lci_abi_version() == lci.ABI_VERSION == 2
     for code in (OK, NULL, SHAPE, UNSUP, OVF, WS, HIP, ALIGN):
         assert lib.lci_status_str(code).decode().startswith("LCI_")
     assert b"unknown" in lib.lci_status_str(123)
@@ -63,19 +63,19 @@ def score(lib, g, q=FAKE, k=FAKE, w=FAKE, out=FAKE, wsb=0, wsq=0):
                              None)
 
 
-def attn(lib, g, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, gate=None, out=FAKE, ws=None, nb=0,
+def attn(lib, g, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, gate=None, mix=None, out=FAKE, ws=None, nb=0,
          scale=0.1):
-    return lib.lci_sparse_attn_fwd(ctypes.byref(g), q, k, v, idx, gate, scale, out, None, ws, nb,
-                                   None)
+    return lib.lci_sparse_attn_fwd(ctypes.byref(g), q, k, v, idx, gate, mix, scale, out, None, ws,
+                                   nb, None)
 
 
 def fused(lib, g, fn="lci_prefill_fwd", ws=FAKE, nb=None, scale=0.1, **ptrs):
-    p = dict(qi=FAKE, ki=FAKE, w=FAKE, q=FAKE, k=FAKE, v=FAKE, out=FAKE)
+    p = dict(qi=FAKE, ki=FAKE, w=FAKE, q=FAKE, k=FAKE, v=FAKE, gate=None, mix=None, out=FAKE)
     p.update(ptrs)
     if nb is None:
         nb = lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g))
     return getattr(lib, fn)(ctypes.byref(g), p["qi"], p["ki"], p["w"], 0, 0, p["q"], p["k"], p["v"],
-                            None, scale, p["out"], None, None, ws, nb, None)
+                            p["gate"], p["mix"], scale, p["out"], None, None, ws, nb, None)
 
 
 def test_null_arguments(lib):
@@ -87,6 +87,10 @@ def test_null_arguments(lib):
     assert attn(lib, geom(), idx=None) == NULL
     assert fused(lib, geom(), v=None) == NULL
     assert lib.lci_topk_select(ctypes.byref(geom()), None, FAKE, None, None, 0, None) == NULL
+    # the other branch's output is mixed in by the gate: without a gate it has no weight
+    assert attn(lib, geom(), mix=FAKE) == NULL
+    assert fused(lib, geom(), mix=FAKE) == NULL
+    assert fused(lib, geom(Tq=1, Tk=1024), fn="lci_decode_fwd", mix=FAKE) == NULL
 
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("Tq", 0), ("Tk", 0), ("K", 0), ("K", 4097),
@@ -123,6 +127,8 @@ def test_softmax_scale_must_be_positive(lib):
 def test_alignment(lib):
     assert attn(lib, geom(), q=FAKE + 2) == ALIGN
     assert attn(lib, geom(), gate=FAKE + 8) == ALIGN
+    assert attn(lib, geom(), gate=FAKE, mix=FAKE + 8) == ALIGN
+    assert fused(lib, geom(), gate=FAKE, mix=FAKE + 2) == ALIGN
     assert score(lib, geom(), q=FAKE + 4) == ALIGN
     assert score(lib, geom(), out=FAKE + 2) == ALIGN
     assert score(lib, geom(q_offset=FAKE + 2)) == ALIGN

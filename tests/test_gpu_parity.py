@@ -5,7 +5,9 @@ attention outputs within max-abs 2e-2 and relative L2 5e-3 (bf16).
 Small cases cover every row; they span several tiles of every kernel and end in
 ragged tails. Edge cases: ragged sequences, continuation rows (q_offset > 0),
 invalid rows, K = 1, K larger than the history, heavy ties, all-zero scores,
-negative per-row weights, a null gate, every supported indexer shape."""
+negative per-row weights, a null gate, every supported indexer shape, and the
+gate mixing the output with another branch's (tile, gather and split-K
+epilogues, empty and invalid rows)."""
 import numpy as np
 import pytest
 
@@ -171,7 +173,8 @@ def _fused_check(lci, orc, cfg, inp, K, rows=None, entry="prefill"):
     d = to_device(inp)
     fn = lci.prefill_fwd if entry == "prefill" else lci.decode_fwd
     out, idx, lse = fn(d["q_idx"], d["k_idx"], d["w"], d["q"], d["k"], d["v"], d["gate"],
-                       inp["scale"], d["q_offset"], d["kv_len"], K, want_idx=True, want_lse=True)
+                       inp["scale"], d["q_offset"], d["kv_len"], K, want_idx=True, want_lse=True,
+                       mix=d.get("mix"))
     torch.cuda.synchronize()
     res = orc.layer(inp, K, rows=rows)
     out = host(out).reshape(cfg.B * cfg.Tq, cfg.Hq, cfg.d)
@@ -258,3 +261,67 @@ def test_deterministic(lci):
         outs.append((host(o).copy(), host(i).copy()))
     torch.cuda.synchronize()
     assert (outs[0][0] == outs[1][0]).all() and (outs[0][1] == outs[1][1]).all()
+
+
+# ---- the gate mixing the sparse output o with another branch's output x:
+# s*o + (1-s)*x, s = sigmoid(gate); rows without entries give (1-s)*x
+
+MIX_ATTN_CASES = {
+    # sorted rows: dense-tile epilogue; scrambled rows: gather epilogue
+    "tile": (MED.replace(Tq=300, Tk=300), 96, "sorted"),
+    "gather": (MED.replace(Tq=300, Tk=300), 96, "scrambled"),
+    "gather_d64": (TINY.replace(Hq=4, Hkv=2, Tq=77, Tk=200), 40, "scrambled"),
+    # few long rows: split-K, the combine kernel applies the gate
+    "split": (MED.replace(B=3, Tq=1, Tk=9000, decode=True), 2048, "sorted"),
+}
+
+
+@pytest.mark.parametrize("name", list(MIX_ATTN_CASES))
+def test_sparse_attn_mix(lci, orc, name):
+    import torch
+    cfg, K, order = MIX_ATTN_CASES[name]
+    cfg = cfg.replace(K=K)
+    inp = make(cfg, seed=9)
+    inp["mix"] = synth.host_mix(cfg, seed=9)
+    log(f"sparse_attn mix {name}: B={cfg.B} Tq={cfg.Tq} Tk={cfg.Tk} Hq={cfg.Hq} K={K} {order}")
+    res = orc.layer(inp, K)
+    idx = res["idx"]
+    if order == "scrambled":
+        r = np.random.default_rng(1)
+        idx = np.stack([r.permutation(row) for row in idx]).astype(np.int32)
+    d = to_device(inp)
+    out, lse = lci.sparse_attn_fwd(d["q"], d["k"], d["v"], dev(idx.reshape(cfg.B, cfg.Tq, K)),
+                                   d["gate"], inp["scale"], d["kv_len"], want_lse=True,
+                                   mix=d["mix"])
+    torch.cuda.synchronize()
+    assert_attn_close(host(out), res["out"].reshape(cfg.B, cfg.Tq, cfg.Hq, cfg.d), name)
+    assert np.abs(host(lse).reshape(-1, cfg.Hq) - res["lse"]).max() < LSE_TOL
+
+
+MIX_FUSED_CASES = {
+    # invalid rows (positions past the history) on the gather path
+    "invalid_rows": (TINY.replace(B=2, Tq=20, Tk=100, K=8), dict(q_offset=[90, 0],
+                                                                  kv_len=[100, 10])),
+    # empty rows written by the tile kernel
+    "tile_only_with_empty_rows": (MED.replace(B=2, Tq=64, Tk=128, K=32),
+                                  dict(q_offset=[64, 0], kv_len=[100, 50])),
+    "tile_masks_from_topk": (MED.replace(Tq=2048, Tk=2048, K=256), {}),
+}
+
+
+@pytest.mark.parametrize("name", list(MIX_FUSED_CASES))
+def test_prefill_fused_mix(lci, orc, name):
+    cfg, kw = MIX_FUSED_CASES[name]
+    inp = make(cfg, seed=10, **kw)
+    inp["mix"] = synth.host_mix(cfg, seed=10)
+    log(f"prefill mix {name}: B={cfg.B} Tq={cfg.Tq} Tk={cfg.Tk} K={cfg.K}")
+    _fused_check(lci, orc, cfg, inp, cfg.K)
+
+
+def test_decode_fused_mix(lci, orc):
+    # sequence 1 is invalid (its position is past its history): its output is (1-s)*x
+    cfg = MED.replace(B=3, Tq=1, Tk=20000, decode=True, K=2048, needles="none")
+    inp = make(cfg, seed=11, kv_len=[20000, 3000, 5000], q_offset=[19999, 3000, 4999])
+    inp["mix"] = synth.host_mix(cfg, seed=11)
+    log("decode mix B=3 with an invalid sequence")
+    _fused_check(lci, orc, cfg, inp, cfg.K, entry="decode")
