@@ -64,6 +64,7 @@ def open_library(path: str):
     lib.orc_layer_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                    i64, i64, P, P, P, P, P, f64, i64, P, P, P, P, P, P]
     lib.orc_layer_rows.restype = i32
+    lib.orc_kv_append.argtypes = [i32, i32, i32, i64, P, P, P, P, P, P]
     lib.orc_num_threads.restype = i32
     return lib
 
@@ -209,6 +210,27 @@ class Oracle:
         return dict(idx=idx, sel=sel, out=out, lse=lse)
 
 
+    def kv_append(self, new, cache, kv_len, n_new=None):
+        """Append rows to a cache: new [B, Tn, ...], cache [B, Tk, ...] (same trailing
+        shape and dtype), kv_len int32 [B], n_new int32 [B] or None (all Tn rows).
+        Returns (cache', q_offset_out, kv_len_out); the input cache is not modified."""
+        new = np.ascontiguousarray(new)
+        out = np.array(cache, copy=True, order="C")
+        if new.dtype != out.dtype or new.shape[0] != out.shape[0] or new.shape[2:] != out.shape[2:]:
+            raise ValueError("new and cache must agree in dtype, batch and row shape")
+        B, Tn, Tk = new.shape[0], new.shape[1], out.shape[1]
+        row_bytes = int(np.prod(new.shape[2:], dtype=np.int64)) * new.dtype.itemsize
+        kv = _c(kv_len, np.int32)
+        nn = None if n_new is None else _c(n_new, np.int32)
+        if kv.shape != (B,) or (nn is not None and nn.shape != (B,)):
+            raise ValueError("kv_len and n_new have one entry per sequence")
+        qo = np.empty(B, np.int32)
+        kl = np.empty(B, np.int32)
+        self.lib.orc_kv_append(B, Tn, Tk, row_bytes, _p(new), _p(out), _p(kv), _p(nn), _p(qo),
+                               _p(kl))
+        return out, qo, kl
+
+
 _default = None
 
 
@@ -242,3 +264,7 @@ def attention(*a, **k):
 
 def layer(*a, **k):
     return default().layer(*a, **k)
+
+
+def kv_append(*a, **k):
+    return default().kv_append(*a, **k)

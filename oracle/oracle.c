@@ -27,7 +27,14 @@
  *            of the bf16 inputs; query head h reads KV head h / (Hq/Hkv).
  *   gate     same page, step 4, and "From Linear Attention to Gated Sparse
  *            Attention", section 2 pseudocode (the gate multiplies the attention
- *            output): y = o * sigmoid(G), elementwise per head and feature.
+ *            output): y = o * sigmoid(G), elementwise per head and feature; or,
+ *            mixed with the other branch's output x (step 4 and its pseudocode),
+ *            y = sigmoid(G) * o + (1 - sigmoid(G)) * x.
+ *   append   same page, section "Engineering and Evaluation Recommendations"
+ *            (chunked prefill that reuses the cached scorer inputs): the new
+ *            rows' keys, values and indexer keys go into the caches right after
+ *            each sequence's history, so a later chunk or decode step scores
+ *            against the cache instead of recomputing earlier rows.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
  */
@@ -269,6 +276,34 @@ int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int
                      orow, lrow);
     }
     return rc;
+}
+
+/* Append new rows to a per-sequence cache (the "append" step above).
+ * src [B][Tn][row_bytes], cache [B][Tk][row_bytes]; kv_len [B] the current
+ * history lengths, n_new [B] the rows to append (NULL: Tn for every sequence).
+ * A length outside 0..Tk is taken as the nearest end of that range and a count
+ * outside 0..Tn likewise. Row t of sequence b goes to cache row kv_len[b] + t
+ * for t < n_new[b]; rows that would land at or past Tk are dropped. Writes, when
+ * non-NULL, q_offset_out[b] = the old length (the position of the first new row)
+ * and kv_len_out[b] = the new length, min(old + n, Tk). */
+void orc_kv_append(int B, int Tn, int Tk, int64_t row_bytes, const uint8_t *src,
+                   uint8_t *cache, const int32_t *kv_len, const int32_t *n_new,
+                   int32_t *q_offset_out, int32_t *kv_len_out)
+{
+    for (int b = 0; b < B; ++b) {
+        int64_t old = kv_len[b] < 0 ? 0 : (kv_len[b] > Tk ? Tk : kv_len[b]);
+        int64_t n = n_new ? n_new[b] : Tn;
+        if (n < 0) n = 0;
+        if (n > Tn) n = Tn;
+        for (int64_t t = 0; t < n; ++t) {
+            int64_t dst = old + t;
+            if (dst >= Tk) break;
+            memcpy(cache + ((int64_t)b * Tk + dst) * row_bytes,
+                   src + ((int64_t)b * Tn + t) * row_bytes, (size_t)row_bytes);
+        }
+        if (q_offset_out) q_offset_out[b] = (int32_t)old;
+        if (kv_len_out) kv_len_out[b] = (int32_t)(old + n < Tk ? old + n : Tk);
+    }
 }
 
 int orc_num_threads(void)

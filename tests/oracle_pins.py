@@ -508,4 +508,66 @@ def pin_layer_mix(orc):
     assert np.abs(res["out"][~valid] - expit(-G[~valid]) * x[~valid]).max() < 1e-15
 
 
+# ------------------------------------------------------------------ append
+
+def pin_append_hand(orc):
+    """Hand-worked append: rows go right after each history, the ones past the
+    capacity are dropped, lengths outside 0..Tk are taken at the nearest end."""
+    new = np.arange(1, 2 * 3 * 2 + 1, dtype=np.uint8).reshape(2, 3, 2)  # rows (1,2) (3,4) (5,6) | (7,8) (9,10) (11,12)
+    cache = np.full((2, 5, 2), 0xEE, np.uint8)
+    out, qo, kl = orc.kv_append(new, cache, np.array([1, 4], np.int32), np.array([3, 2], np.int32))
+    E = 0xEE
+    want = np.array([[[E, E], [1, 2], [3, 4], [5, 6], [E, E]],
+                     [[E, E], [E, E], [E, E], [E, E], [7, 8]]], np.uint8)
+    assert (out == want).all()
+    assert qo.tolist() == [1, 4] and kl.tolist() == [4, 5]
+    assert (cache == E).all()                      # the input is not modified
+    out, qo, kl = orc.kv_append(new, cache, np.array([-3, 9], np.int32))
+    assert qo.tolist() == [0, 5] and kl.tolist() == [3, 5]
+    assert (out[0, :3] == new[0]).all() and (out[0, 3:] == E).all() and (out[1] == E).all()
+    out, qo, kl = orc.kv_append(new, cache, np.array([0, 2], np.int32), np.array([0, 9], np.int32))
+    assert (out[0] == E).all() and (out[1, 2:] == new[1]).all() and kl.tolist() == [0, 5]
+
+
+def pin_append_chunked_layer(orc):
+    """Chunked prefill: caches built by appending chunks of 7, 13 and 20 rows
+    (the second sequence appends fewer rows to each chunk) hold the full history,
+    and the layer run on each chunk's rows at the returned q_offset / kv_len
+    equals the same rows of the layer run once on the whole history."""
+    import synth
+    cfg = synth.CONFIGS["tiny"].replace(B=2, Tq=40, Tk=40, K=9)
+    inp = synth.host_inputs(cfg, seed=12)
+    full = orc.layer(inp, K=9)
+    caches = {n: np.zeros_like(inp[n]) for n in ("k", "v", "k_idx")}
+    kv_len = np.zeros(2, np.int32)
+    start = np.zeros(2, np.int64)
+    for c in (7, 13, 20):
+        n_new = np.array([c, c - 3], np.int32)
+        for n in caches:
+            chunk = np.zeros((2, c) + inp[n].shape[2:], inp[n].dtype)
+            for b in range(2):
+                chunk[b, :n_new[b]] = inp[n][b, start[b]:start[b] + n_new[b]]
+            caches[n], qo, kl = orc.kv_append(chunk, caches[n], kv_len, n_new)
+        assert qo.tolist() == kv_len.tolist() and kl.tolist() == (kv_len + n_new).tolist()
+        sub = dict(inp, k=caches["k"], v=caches["v"], k_idx=caches["k_idx"], q_offset=qo,
+                   kv_len=kl)
+        for n in ("q_idx", "q", "gate"):
+            sub[n] = np.zeros((2, c) + inp[n].shape[2:], inp[n].dtype)
+            for b in range(2):
+                sub[n][b, :n_new[b]] = inp[n][b, start[b]:start[b] + n_new[b]]
+        res = orc.layer(sub, K=9)
+        for b in range(2):
+            rows = slice(b * c, b * c + n_new[b])
+            frows = slice(b * 40 + start[b], b * 40 + start[b] + n_new[b])
+            assert (res["idx"][rows] == full["idx"][frows]).all()
+            assert np.array_equal(res["out"][rows], full["out"][frows])
+            # rows past the appended ones lie beyond the history: invalid
+            assert (res["idx"][b * c + n_new[b]:(b + 1) * c] == -1).all()
+        kv_len = kl
+        start += n_new
+    for n in caches:
+        for b in range(2):
+            assert (caches[n][b, :start[b]] == inp[n][b, :start[b]]).all()
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

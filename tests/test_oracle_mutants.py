@@ -43,6 +43,13 @@ MUTANTS = [
      "NULL, NULL, scale,\n                     orow"),
     ("lse_without_max", "lse[h] = m + log(Z);", "lse[h] = log(Z);"),
     ("padding_read_as_position0", "if (s < 0 || s >= kv_len)", "if (s < 0) s = 0; if (s >= kv_len)"),
+    ("append_off_by_one", "int64_t dst = old + t;", "int64_t dst = old + t + 1;"),
+    ("append_ignores_count", "for (int64_t t = 0; t < n; ++t) {", "for (int64_t t = 0; t < Tn; ++t) {"),
+    ("append_length_not_advanced", "kv_len_out[b] = (int32_t)(old + n < Tk ? old + n : Tk);",
+     "kv_len_out[b] = (int32_t)old;"),
+    ("append_offset_is_new_length", "q_offset_out[b] = (int32_t)old;",
+     "q_offset_out[b] = (int32_t)(old + n);"),
+    ("append_no_capacity_clamp", "(int32_t)(old + n < Tk ? old + n : Tk)", "(int32_t)(old + n)"),
     ("overflow_unchecked", "if (acc > INT32_MAX) { acc = INT32_MAX; rc = ORC_OVERFLOW; }", ""),
 ]
 
