@@ -102,6 +102,36 @@ def decode_step_bytes(cfg):
     return cfg.B * (cfg.Tk * cfg.d_I + cfg.H_I * cfg.d_I) + decode_attn_bytes(cfg)
 
 
+def append_bytes(rows, Hkv, d, d_I):
+    """Algorithmic HBM bytes of appending rows to the caches: every new key,
+    value and indexer-key row read once and written once."""
+    return 2 * rows * (2 * Hkv * d * 2 + d_I)
+
+
+def time_append(lci, k_new, v_new, kI_new, k, v, kI, kv_len, reps, stream):
+    """Average event-timed duration (ms) of the cache-append copy kernel and of
+    its length kernel over `reps` calls, with the kernel timing log on."""
+    import torch
+    qo = torch.empty_like(kv_len)
+    kl = torch.empty_like(kv_len)
+
+    def call():
+        lci.kv_append(k_new, v_new, kI_new, k, v, kI, kv_len, q_offset_out=qo, kv_len_out=kl,
+                      stream=stream)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    lci.kernel_timing(True)
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    cp, n_cp = lci.kernel_timing_read("kv_append")
+    ln, n_ln = lci.kernel_timing_read("kv_lengths")
+    lci.kernel_timing(False)
+    return cp / n_cp, ln / n_ln
+
+
 class Timer:
     """HIP events recorded on the stream the library launches on."""
 
@@ -286,14 +316,25 @@ def main():
         ms_step, ev_ms, kern = timed_region(timer, prefill_step, args.steps, lci)
         tok_s = cfg.B * cfg.Tq / (ms_step * 1e-3)
         cold_ms = cold_steps(prefill_step, args.steps, stream)
+        # appending the whole prompt as one chunk to caches of this shape (the
+        # new rows are a copy of the cache contents, so the inputs stay as they are)
+        app_ms, len_ms = time_append(lci, d["k"].clone(), d["v"].clone(), d["k_idx"].clone(),
+                                     d["k"], d["v"], d["k_idx"],
+                                     torch.zeros_like(d["kv_len"]), 20, stream)
+        app_b = append_bytes(cfg.B * cfg.Tk, cfg.Hkv, cfg.d, cfg.d_I)
         log(f"{name} fused: {ms_step:.3f} ms/step ({ev_ms:.3f} ms by events), "
             f"{tok_s / 1e6:.2f} M tok/s; cold cache {cold_ms:.3f} ms/step")
+        log(f"  kv_append of the {cfg.B * cfg.Tk} prompt rows: {app_ms * 1e3:.1f} us "
+            f"({app_b / app_ms / 1e6:.0f} GB/s) + lengths {len_ms * 1e3:.1f} us")
         for kname, kv in kern.items():
             log(f"  {kname:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
                 f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
         return dict(workload=name, ms_per_step=ms_step, event_ms_per_step=ev_ms, tok_s=tok_s,
                     cold_ms_per_step=cold_ms, cold_tok_s=cfg.B * cfg.Tq / (cold_ms * 1e-3),
-                    kernels=kern)
+                    kernels=kern,
+                    kv_append=dict(rows=cfg.B * cfg.Tk, us=app_ms * 1e3, lengths_us=len_ms * 1e3,
+                                   bytes=app_b, gbs=app_b / app_ms / 1e6,
+                                   frac_hbm=app_b / app_ms / 1e6 / PEAK_HBM_GBS))
 
     def run_decode(name):
         dcfg = synth.CONFIGS[name]
@@ -324,9 +365,22 @@ def main():
         for kname, kv in dkern.items():
             log(f"  {kname:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
                 f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
+        # appending one token per sequence: the new rows are each history's last
+        # row, written back where it is (kv_len = Tk - 1), so the inputs stay as they are
+        last = slice(dcfg.Tk - 1, dcfg.Tk)
+        app_ms, len_ms = time_append(lci, dd["k"][:, last].contiguous(),
+                                     dd["v"][:, last].contiguous(),
+                                     dd["k_idx"][:, last].contiguous(), dd["k"], dd["v"],
+                                     dd["k_idx"], torch.full_like(dd["kv_len"], dcfg.Tk - 1),
+                                     20, stream)
+        app_b = append_bytes(dcfg.B, dcfg.Hkv, dcfg.d, dcfg.d_I)
+        log(f"  kv_append of one token per sequence: {app_ms * 1e3:.1f} us + lengths "
+            f"{len_ms * 1e3:.1f} us")
         return dict(workload=name, ms_per_step=dms, event_ms_per_step=dev_ms, queries_s=qps,
                     step_hbm_gbs=sbytes / dms / 1e6,
                     step_frac_hbm=sbytes / dms / 1e6 / PEAK_HBM_GBS,
+                    kv_append=dict(rows=dcfg.B, us=app_ms * 1e3, lengths_us=len_ms * 1e3,
+                                   bytes=app_b),
                     sparse_attn_ms=a_ms, sparse_attn_gbs=abytes / a_ms / 1e6,
                     sparse_attn_frac_hbm=abytes / a_ms / 1e6 / PEAK_HBM_GBS,
                     kernels=dkern)
@@ -387,6 +441,8 @@ def main():
         "cold_cache": {"ms_per_step": pre["cold_ms_per_step"], "tok_s": pre["cold_tok_s"],
                        "note": "median of single steps, each after a 1 GiB cache flush"},
         "cpu_baseline": cpu,
+        "kv_append": dict(pre["kv_append"], note="the whole prompt appended as one chunk to "
+                          "the key/value/indexer-key caches (copy kernel; lengths kernel apart)"),
     }
     if "decode" in res:
         line["decode"] = res["decode"]

@@ -183,6 +183,37 @@ lci_status lci_decode_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *
                           lci_bf16 *out, float *lse, int32_t *idx_out, void *workspace,
                           size_t ws_bytes, void *stream);
 
+/* Append new rows to the key, value and indexer-key caches ("Hybrid Sparse
+ * Attention ...", section "Engineering and Evaluation Recommendations": long
+ * prompts are prefilled in chunks that reuse the cached scorer inputs). The
+ * caches are the k, v and k_idx arguments of the calls above; after an append,
+ * a prefill or decode call with q_offset = q_offset_out and kv_len = kv_len_out
+ * takes the appended rows as its query rows and scores and attends against the
+ * whole cached history, earlier rows included, without recomputing them.
+ *   g        B (at most 65535); Tq = Tn, rows per sequence of the new tensors; Tk, the cache
+ *            capacity (row stride); Hkv, d, d_I; g->kv_len (device [B]) the
+ *            current history lengths. Hq, H_I, K and q_offset are not used
+ *            (q_offset may be NULL).
+ *   k_new, v_new  bf16 [B, Tn, Hkv, d]; kI_new int8 [B, Tn, d_I]
+ *   n_new    int32 device [B], nullable: rows of sequence b to append (NULL:
+ *            all Tn); values outside 0..Tn are taken at the nearest end
+ *   k_cache, v_cache  bf16 [B, Tk, Hkv, d]; kI_cache int8 [B, Tk, d_I]:
+ *            row t < n of sequence b is written at position kv_len[b] + t;
+ *            rows that would land at or past Tk are not written (a length
+ *            outside 0..Tk is taken at the nearest end); nothing else changes
+ *   q_offset_out  int32 device [B] out, nullable: the old length, i.e. the
+ *            position of the first appended row
+ *   kv_len_out    int32 device [B] out, nullable: min(old + n, Tk). It may be
+ *            g->kv_len itself (the lengths are updated after every row is
+ *            copied); q_offset_out and kv_len_out must differ (else SHAPE).
+ * Hkv*d must be a multiple of 8 and d_I of 16 (16-byte rows), else
+ * UNSUPPORTED. Two kernel launches, no workspace.
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, HIP. */
+lci_status lci_kv_append(const lci_geom *g, const lci_bf16 *k_new, const lci_bf16 *v_new,
+                         const int8_t *kI_new, const int32_t *n_new, lci_bf16 *k_cache,
+                         lci_bf16 *v_cache, int8_t *kI_cache, int32_t *q_offset_out,
+                         int32_t *kv_len_out, void *stream);
+
 /* Workspace bytes an entry needs for this geometry (host only, reads no device
  * memory). Returns 0 for an invalid geometry or entry id. */
 size_t lci_workspace_bytes(int entry, const lci_geom *g);
@@ -222,7 +253,9 @@ enum {
   LCI_KERNEL_DEC_CAND = 8,    /* decode: candidates at or above the threshold bin   */
   LCI_KERNEL_DEC_RESOLVE = 9, /* decode: exact K-th score among the candidates      */
   LCI_KERNEL_DEC_COMPACT = 10,/* decode: ordered compaction of the selected positions*/
-  LCI_KERNEL_COUNT = 11
+  LCI_KERNEL_KV_APPEND = 11,  /* new rows into the key/value/indexer-key caches     */
+  LCI_KERNEL_KV_LENGTHS = 12, /* new cache lengths and first positions after append */
+  LCI_KERNEL_COUNT = 13
 };
 int lci_kernel_timing(int enable);
 int lci_kernel_timing_read(int kernel, double *total_ms, int64_t *launches);

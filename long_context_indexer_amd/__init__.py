@@ -9,7 +9,7 @@ PyTorch supplies device memory and streams. There is no CPU fallback: without
 the built library every call raises.
 
 Entry points (same names as the C ABI, without the ``lci_`` prefix):
-    idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd,
+    idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd, kv_append,
     workspace_bytes, kernel_timing, kernel_timing_read, kernel_name
 """
 from __future__ import annotations
@@ -27,12 +27,13 @@ ENTRY_IDX_SCORE, ENTRY_TOPK_SELECT, ENTRY_SPARSE_ATTN, ENTRY_PREFILL, ENTRY_DECO
 ABI_VERSION = 2
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
-           "lci_decode_fwd", "lci_workspace_bytes", "lci_status_str", "lci_last_hip_error",
+           "lci_decode_fwd", "lci_kv_append", "lci_workspace_bytes", "lci_status_str", "lci_last_hip_error",
            "lci_abi_version", "lci_kernel_timing", "lci_kernel_timing_read", "lci_kernel_name")
 
 # kernel kinds of the timing log (LCI_KERNEL_* in lci.h)
 KERNELS = ("idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
-           "dec_thresh", "dec_score", "dec_cand", "dec_resolve", "dec_compact")
+           "dec_thresh", "dec_score", "dec_cand", "dec_resolve", "dec_compact", "kv_append",
+           "kv_lengths")
 
 
 class LciError(RuntimeError):
@@ -68,6 +69,7 @@ def load_library(path: str = LIB_PATH):
     fused = [G, P, P, P, i64, i64, P, P, P, P, P, ctypes.c_float, P, P, P, P, sz, P]
     lib.lci_prefill_fwd.argtypes = fused
     lib.lci_decode_fwd.argtypes = fused
+    lib.lci_kv_append.argtypes = [G, P, P, P, P, P, P, P, P, P, P]
     lib.lci_workspace_bytes.argtypes = [ctypes.c_int, G]
     lib.lci_workspace_bytes.restype = sz
     lib.lci_status_str.argtypes = [ctypes.c_int]
@@ -83,7 +85,7 @@ def load_library(path: str = LIB_PATH):
     lib.lci_kernel_name.argtypes = [ctypes.c_int]
     lib.lci_kernel_name.restype = ctypes.c_char_p
     for fn in ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
-               "lci_decode_fwd", "lci_kernel_timing", "lci_kernel_timing_read"):
+               "lci_decode_fwd", "lci_kv_append", "lci_kernel_timing", "lci_kernel_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -322,3 +324,40 @@ def decode_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=N
     ``mix`` as in ``sparse_attn_fwd``."""
     return _fused("lci_decode_fwd", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, mix, scale,
                   q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream)
+
+
+def kv_append(k_new, v_new, kI_new, k_cache, v_cache, kI_cache, kv_len, n_new=None,
+              q_offset_out=None, kv_len_out=None, stream=None):
+    """Append rows to the key/value/indexer-key caches (in place) after each
+    sequence's kv_len rows. k_new, v_new bf16 [B,Tn,Hkv,d], kI_new int8 [B,Tn,d_I];
+    caches [B,Tk,...]; n_new int32 [B] rows per sequence (None: all Tn).
+    Returns (q_offset_out, kv_len_out): the first appended position and the new
+    length per sequence; kv_len_out may be kv_len itself (updated in place)."""
+    import torch
+    _dev(k_new, torch.bfloat16, "k_new", 4)
+    _dev(v_new, torch.bfloat16, "v_new", 4)
+    _dev(kI_new, torch.int8, "kI_new", 3)
+    _dev(k_cache, torch.bfloat16, "k_cache", 4)
+    _dev(v_cache, torch.bfloat16, "v_cache", 4)
+    _dev(kI_cache, torch.int8, "kI_cache", 3)
+    _dev(kv_len, torch.int32, "kv_len", 1)
+    _dev(n_new, torch.int32, "n_new", 1)
+    B, Tn, Hkv, d = k_new.shape
+    Tk, d_I = k_cache.shape[1], kI_new.shape[2]
+    if tuple(v_new.shape) != tuple(k_new.shape) or tuple(kI_new.shape[:2]) != (B, Tn) or \
+            tuple(k_cache.shape) != (B, Tk, Hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or tuple(kI_cache.shape) != (B, Tk, d_I) or kv_len.numel() != B or \
+            (n_new is not None and n_new.numel() != B):
+        raise ValueError("inconsistent shapes")
+    if q_offset_out is None:
+        q_offset_out = torch.empty_like(kv_len)
+    if kv_len_out is None:
+        kv_len_out = torch.empty_like(kv_len)
+    _dev(q_offset_out, torch.int32, "q_offset_out", 1)
+    _dev(kv_len_out, torch.int32, "kv_len_out", 1)
+    g = lci_geom(B, Tn, Tk, 0, Hkv, d, 0, d_I, 0, None, kv_len.data_ptr())
+    _check(load_library().lci_kv_append(ctypes.byref(g), _ptr(k_new), _ptr(v_new), _ptr(kI_new),
+                                        _ptr(n_new), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(kI_cache), _ptr(q_offset_out), _ptr(kv_len_out),
+                                        _stream(stream)))
+    return q_offset_out, kv_len_out

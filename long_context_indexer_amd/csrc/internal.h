@@ -81,4 +81,12 @@ hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* 
                               float scale, uint16_t* out, float* lse, int splits,
                               void* workspace, bool masks_ready, hipStream_t stream);
 
+// ---- appending rows to the key / value / indexer-key caches
+// Sizes from g: B, Tq (= rows of the new tensors per sequence), Tk (capacity),
+// Hkv, d, d_I; g.kv_len holds the current lengths.
+hipError_t launch_kv_append(const Geom& g, const uint16_t* k_new, const uint16_t* v_new,
+                            const int8_t* kI_new, const int32_t* n_new, uint16_t* k_cache,
+                            uint16_t* v_cache, int8_t* kI_cache, int32_t* q_offset_out,
+                            int32_t* kv_len_out, hipStream_t stream);
+
 }  // namespace lci

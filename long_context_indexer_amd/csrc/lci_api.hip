@@ -271,4 +271,30 @@ lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* 
                                        static_cast<hipStream_t>(stream)));
 }
 
+lci_status lci_kv_append(const lci_geom* g, const lci_bf16* k_new, const lci_bf16* v_new,
+                         const int8_t* kI_new, const int32_t* n_new, lci_bf16* k_cache,
+                         lci_bf16* v_cache, int8_t* kI_cache, int32_t* q_offset_out,
+                         int32_t* kv_len_out, void* stream) {
+  if (!g || !g->kv_len) return LCI_ERR_NULL;
+  if (!k_new || !v_new || !kI_new || !k_cache || !v_cache || !kI_cache) return LCI_ERR_NULL;
+  // one workgroup row per sequence: B within the grid's y limit
+  if (g->B < 1 || g->B > 65535 || g->Tq < 1 || g->Tk < 1 || g->Hkv < 1 || g->d < 1 ||
+      g->d_I < 1)
+    return LCI_ERR_SHAPE;
+  if (q_offset_out && q_offset_out == kv_len_out) return LCI_ERR_SHAPE;
+  if ((static_cast<int64_t>(g->Hkv) * g->d) % 8 != 0 || g->d_I % 16 != 0)
+    return LCI_ERR_UNSUPPORTED;
+  // int32 unit counts inside one workgroup, int64 row offsets
+  if (static_cast<int64_t>(g->Hkv) * g->d > (int64_t(1) << 20) || g->d_I > (1 << 20))
+    return LCI_ERR_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kI_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(kI_cache) || !aligned4(g->kv_len) ||
+      (n_new && !aligned4(n_new)) || (q_offset_out && !aligned4(q_offset_out)) ||
+      (kv_len_out && !aligned4(kv_len_out)))
+    return LCI_ERR_ALIGN;
+  return hip_status(lci::launch_kv_append(to_geom(g), k_new, v_new, kI_new, n_new, k_cache,
+                                          v_cache, kI_cache, q_offset_out, kv_len_out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
-              "lci_decode_fwd", "lci_workspace_bytes"):
+              "lci_decode_fwd", "lci_kv_append", "lci_workspace_bytes"):
         assert n in names
 
 
@@ -153,6 +153,30 @@ def test_workspace_checks(lib):
     assert lib.lci_workspace_bytes(99, ctypes.byref(g)) == 0
     assert lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(geom(K=0))) == 0
     assert lib.lci_workspace_bytes(lci.ENTRY_IDX_SCORE, ctypes.byref(g)) == 0
+
+
+def append(lib, g, n_new=None, qo=FAKE, kl=FAKE + 64, **ptrs):
+    p = dict(kn=FAKE, vn=FAKE, kin=FAKE, kc=FAKE, vc=FAKE, kic=FAKE)
+    p.update(ptrs)
+    return lib.lci_kv_append(ctypes.byref(g) if g is not None else None, p["kn"], p["vn"], p["kin"],
+                             n_new, p["kc"], p["vc"], p["kic"], qo, kl, None)
+
+
+def test_kv_append_arguments(lib):
+    assert append(lib, None) == NULL
+    assert append(lib, geom(kv_len=None)) == NULL
+    assert append(lib, geom(q_offset=None), kc=None) == NULL
+    assert append(lib, geom(q_offset=None), kin=None) == NULL
+    assert append(lib, geom(B=0)) == SHAPE
+    assert append(lib, geom(B=65536)) == SHAPE
+    assert append(lib, geom(Tq=0)) == SHAPE
+    assert append(lib, geom(d_I=0)) == SHAPE
+    assert append(lib, geom(), qo=FAKE, kl=FAKE) == SHAPE      # both outputs in one array
+    assert append(lib, geom(Hkv=1, d=4)) == UNSUP               # 8-byte rows
+    assert append(lib, geom(d_I=40)) == UNSUP
+    assert append(lib, geom(), kc=FAKE + 8) == ALIGN
+    assert append(lib, geom(), n_new=FAKE + 2) == ALIGN
+    assert append(lib, geom(kv_len=FAKE + 2)) == ALIGN
 
 
 def test_decode_needs_one_row(lib):
