@@ -61,7 +61,8 @@ def open_library(path: str):
     lib.orc_topk_rows.argtypes = [i64, P, i64, P, i32, P, P]
     lib.orc_attn_rows.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, i64,
                                   P, P, P, P, P]
-    lib.orc_layer_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
+    lib.orc_block_topk_rows.argtypes = [i64, P, i64, P, i32, i32, P, P, P]
+    lib.orc_layer_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                    i64, i64, P, P, P, P, P, f64, i64, P, P, P, P, P, P]
     lib.orc_layer_rows.restype = i32
     lib.orc_kv_append.argtypes = [i32, i32, i32, i64, P, P, P, P, P, P]
@@ -174,10 +175,30 @@ class Oracle:
                               _p(idx), _p(out), _p(lse))
         return out, lse
 
-    def layer(self, inp, K, rows=None, gated=True):
+    def block_topk(self, S, n, K, block):
+        """Block-granular Top-K of each score row (blocks of `block` positions scored
+        by their best position). Returns (idx int32 [nrows, K*block] positions
+        ascending, -1 padded; blocks int32 [nrows, K] ascending, -1 padded; their
+        scores int32 [nrows, K], INT32_MIN in the padding)."""
+        S = _c(S, np.int32)
+        if S.ndim == 1:
+            S = S[None]
+        n = _c(np.broadcast_to(np.asarray(n, dtype=np.int64), (S.shape[0],)), np.int64)
+        if block < 1 or K < 1:
+            raise ValueError("block and K are positive")
+        idx = np.empty((S.shape[0], K * block), np.int32)
+        blk = np.empty((S.shape[0], K), np.int32)
+        sel = np.empty((S.shape[0], K), np.int32)
+        self.lib.orc_block_topk_rows(S.shape[0], _p(S), S.shape[1], _p(n), block, K, _p(idx),
+                                    _p(blk), _p(sel))
+        return idx, blk, sel
+
+    def layer(self, inp, K, rows=None, gated=True, block=1):
         """The whole layer (score -> Top-K -> attention -> gate) for the listed rows
         of an input dict as produced by ``synth.host_inputs``; an entry "mix" (the
-        other branch's output, uint16 [B,Tq,Hq,d]) is mixed in by the gate.
+        other branch's output, uint16 [B,Tq,Hq,d]) is mixed in by the gate. With
+        block > 1 the selection keeps K blocks of `block` positions: idx holds
+        K*block positions per row and sel the K kept blocks' scores.
         Returns dict(idx, sel, out, lse) with out float64 [nrows,Hq,d]."""
         q_idx = _c(inp["q_idx"], np.int8)
         k_idx = _c(inp["k_idx"], np.int8)
@@ -196,11 +217,12 @@ class Oracle:
         wsb, wsq = _w_strides(w, B, Tq, H_I)
         rb, ri = _rows(rows, B, Tq)
         nr = len(rb)
-        idx = np.empty((nr, K), np.int32)
+        bl = max(int(block), 1)
+        idx = np.empty((nr, K * bl), np.int32)
         sel = np.empty((nr, K), np.int32)
         out = np.empty((nr, Hq, d), np.float64)
         lse = np.empty((nr, Hq), np.float64)
-        rc = self.lib.orc_layer_rows(Tq, Tk, Hq, Hkv, d, H_I, d_I, K,
+        rc = self.lib.orc_layer_rows(Tq, Tk, Hq, Hkv, d, H_I, d_I, K, bl,
                                     _p(_c(inp["q_offset"], np.int32)), _p(_c(inp["kv_len"], np.int32)),
                                     _p(q_idx), _p(k_idx), _p(w), wsb, wsq, _p(q), _p(k), _p(v),
                                     _p(gate), _p(mix), float(inp["scale"]), nr, _p(rb), _p(ri), _p(idx),
@@ -264,6 +286,10 @@ def attention(*a, **k):
 
 def layer(*a, **k):
     return default().layer(*a, **k)
+
+
+def block_topk(*a, **k):
+    return default().block_topk(*a, **k)
 
 
 def kv_append(*a, **k):

@@ -22,6 +22,9 @@
  *            score row). Order: higher score first, lower position on equal
  *            scores. Output: the selected positions in ascending order, padded
  *            with -1 when fewer than K candidates exist.
+ *            Block granularity (same steps: positions or blocks): a block of
+ *            positions scores as its best position, and K blocks are kept under
+ *            the same order; their causal positions form the index row.
  *   attention same page, step 3 (standard softmax attention over the selected
  *            positions only, scaled by 1/sqrt(d)), in fp64 from the exact values
  *            of the bf16 inputs; query head h reads KV head h / (Hq/Hkv).
@@ -201,6 +204,58 @@ int orc_scores_rows(int Tq, int Tk, int H_I, int d_I, const int32_t *q_offset,
     return rc;
 }
 
+/* Block-granular Top-K: the scorer and the selection work on blocks of
+ * positions instead of single positions ("Hybrid Sparse Attention for
+ * Long-Context LLMs", section "Indexer + Top-K: How Fine-Grained Sparse Attention
+ * Works", steps 1-2: scores against positions or blocks, the top K positions or
+ * blocks kept). The pages do not say how a block is scored; the reading taken:
+ * block j holds positions j*block .. j*block + block - 1, and its score is the
+ * largest score among its candidates (positions below n), so a block is as
+ * relevant as its best position. The min(K, nb) best of the nb = ceil(n / block)
+ * blocks are kept under the order of single positions (higher score first,
+ * lower block index on equal scores).
+ * idx [K*block]: the kept blocks' candidate positions, ascending, -1 padded;
+ * blk (nullable) [K]: the kept blocks, ascending, -1 padded; bsel (nullable) [K]:
+ * their scores, INT32_MIN in the padding. block = 1 is orc_topk_row. */
+void orc_block_topk_row(const int32_t *S, int64_t n, int block, int K, int32_t *idx,
+                        int32_t *blk, int32_t *bsel)
+{
+    int64_t nb = n > 0 ? (n + block - 1) / block : 0;
+    int32_t *bs = (int32_t *)malloc((size_t)(nb > 0 ? nb : 1) * sizeof(int32_t));
+    for (int64_t j = 0; j < nb; ++j) {
+        int32_t m = INT32_MIN;
+        for (int64_t s = j * block; s < (j + 1) * block && s < n; ++s)
+            if (S[s] > m) m = S[s];
+        bs[j] = m;
+    }
+    int32_t *bi = (int32_t *)malloc((size_t)K * sizeof(int32_t));
+    int32_t *bv = (int32_t *)malloc((size_t)K * sizeof(int32_t));
+    orc_topk_row(bs, nb, K, bi, bv);
+    for (int kk = 0; kk < K; ++kk) {
+        for (int t = 0; t < block; ++t) {
+            int64_t s = bi[kk] < 0 ? -1 : (int64_t)bi[kk] * block + t;
+            idx[(int64_t)kk * block + t] = (s >= 0 && s < n) ? (int32_t)s : -1;
+        }
+        if (blk) blk[kk] = bi[kk];
+        if (bsel) bsel[kk] = bv[kk];
+    }
+    free(bv);
+    free(bi);
+    free(bs);
+}
+
+/* Block-granular Top-K over given score rows (as orc_topk_rows): idx
+ * [nrows][K*block], blk and bsel [nrows][K], both nullable. */
+void orc_block_topk_rows(int64_t nrows, const int32_t *S, int64_t stride, const int64_t *n,
+                         int block, int K, int32_t *idx, int32_t *blk, int32_t *bsel)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r)
+        orc_block_topk_row(S + r * stride, n[r] > 0 ? n[r] : 0, block, K,
+                           idx + r * (int64_t)K * block, blk ? blk + r * (int64_t)K : NULL,
+                           bsel ? bsel + r * (int64_t)K : NULL);
+}
+
 /* Top-K over given score rows: row r has n[r] candidates (positions 0..n[r]-1)
  * stored at S + r*stride. n[r] <= 0 gives an all -1 row. */
 void orc_topk_rows(int64_t nrows, const int32_t *S, int64_t stride, const int64_t *n, int K,
@@ -232,11 +287,14 @@ void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t 
 }
 
 /* The whole layer for a list of rows: score -> Top-K -> attention -> gate.
- * idx/sel [nrows][K], out [nrows][Hq][d], lse [nrows][Hq]. Invalid rows give
+ * With block > 1 the selection keeps K blocks of that many positions
+ * (orc_block_topk_row): idx [nrows][K*block] positions, sel [nrows][K] the kept
+ * blocks' scores; with block <= 1 single positions, idx and sel [nrows][K].
+ * out [nrows][Hq][d], lse [nrows][Hq]. Invalid rows give
  * idx = -1, sel = INT32_MIN, an attention output of 0 (out = 0 unless mixed)
  * and lse = -inf. Returns ORC_OVERFLOW if a score overflowed int32. */
 int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int K,
-                   const int32_t *q_offset, const int32_t *kv_len, const int8_t *q_idx,
+                   int block, const int32_t *q_offset, const int32_t *kv_len, const int8_t *q_idx,
                    const int8_t *k_idx, const int8_t *w, int64_t w_stride_b,
                    int64_t w_stride_q, const uint16_t *q, const uint16_t *k,
                    const uint16_t *v, const uint16_t *gate, const uint16_t *mix, double scale,
@@ -244,17 +302,20 @@ int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int
                    int32_t *sel, double *out, double *lse)
 {
     int rc = ORC_OK;
+    const int bl = block > 1 ? block : 1;
+    const int KI = K * bl;   /* positions per index row */
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : rc)
     for (int64_t r = 0; r < nrows; ++r) {
         int b = row_b[r], i = row_i[r];
         int64_t p = (int64_t)q_offset[b] + i;
-        int32_t *ir = idx + r * (int64_t)K;
+        int32_t *ir = idx + r * (int64_t)KI;
         int32_t *sr = sel ? sel + r * (int64_t)K : NULL;
         double *orow = out + r * (int64_t)Hq * d;
         double *lrow = lse ? lse + r * (int64_t)Hq : NULL;
         if (p < 0 || p >= kv_len[b] || kv_len[b] > Tk) {
             int64_t qrow = (int64_t)b * Tq + i;
-            for (int j = 0; j < K; ++j) { ir[j] = -1; if (sr) sr[j] = INT32_MIN; }
+            for (int j = 0; j < KI; ++j) ir[j] = -1;
+            for (int j = 0; j < K; ++j) if (sr) sr[j] = INT32_MIN;
             for (int64_t j = 0; j < (int64_t)Hq * d; ++j)
                 orow[j] = gate ? orc_gate(0.0, orc_bf16(gate[qrow * Hq * d + j]),
                                           mix ? mix + qrow * Hq * d : NULL, j)
@@ -267,11 +328,14 @@ int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int
         const int8_t *kI = k_idx + (int64_t)b * Tk * d_I;
         const int8_t *wr = w + b * w_stride_b + (int64_t)i * w_stride_q;
         rc |= orc_score_row(H_I, d_I, qI, kI, wr, p + 1, S);
-        orc_topk_row(S, p + 1, K, ir, sr);
+        if (bl > 1)
+            orc_block_topk_row(S, p + 1, bl, K, ir, NULL, sr);
+        else
+            orc_topk_row(S, p + 1, K, ir, sr);
         free(S);
         int64_t qrow = (int64_t)b * Tq + i;
         orc_attn_row(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
-                     v + (int64_t)b * Tk * Hkv * d, kv_len[b], ir, K,
+                     v + (int64_t)b * Tk * Hkv * d, kv_len[b], ir, KI,
                      gate ? gate + qrow * Hq * d : NULL, mix ? mix + qrow * Hq * d : NULL, scale,
                      orow, lrow);
     }

@@ -570,4 +570,82 @@ def pin_append_chunked_layer(orc):
             assert (caches[n][b, :start[b]] == inp[n][b, :start[b]]).all()
 
 
+# ------------------------------------------------------------ block Top-K
+
+def pin_block_topk_hand(orc):
+    """Hand-worked blocks of 2: scores 5 1 | 9 9 | 2 7 | 3 score 5, 9, 7, 3."""
+    S = np.array([5, 1, 9, 9, 2, 7, 3], np.int32)
+    idx, blk, sel = orc.block_topk(S, 7, 2, 2)
+    assert blk[0].tolist() == [1, 2] and sel[0].tolist() == [9, 7]
+    assert idx[0].tolist() == [2, 3, 4, 5]
+    idx, blk, sel = orc.block_topk(S, 7, 5, 2)   # more blocks asked than exist
+    assert blk[0].tolist() == [0, 1, 2, 3, -1] and sel[0].tolist() == [5, 9, 7, 3, I32_MIN]
+    assert idx[0].tolist() == [0, 1, 2, 3, 4, 5, 6, -1, -1, -1]
+    # only the first 5 candidates: the last block is position 4 alone (score 2)
+    idx, blk, sel = orc.block_topk(S, 5, 2, 2)
+    assert blk[0].tolist() == [0, 1] and idx[0].tolist() == [0, 1, 2, 3]
+    idx, blk, sel = orc.block_topk(S, 5, 3, 2)
+    assert idx[0].tolist() == [0, 1, 2, 3, 4, -1] and sel[0].tolist() == [5, 9, 2]
+    # equal block scores: the lower block wins
+    T = np.array([4, 4, 1, 4, 4], np.int32)
+    idx, blk, sel = orc.block_topk(T, 5, 2, 2)
+    assert blk[0].tolist() == [0, 1] and idx[0].tolist() == [0, 1, 2, 3]
+
+
+def pin_block_topk_definition(orc):
+    """Against a brute-force reading of the definition (numpy block maxima, a
+    Python sort by (score desc, block asc)) on rows with heavy ties; block 1 is
+    the position Top-K."""
+    r = np.random.default_rng(44)
+    for trial in range(40):
+        n = int(r.integers(1, 200))
+        block = int(r.choice([1, 2, 3, 8, 16, 64]))
+        K = int(r.integers(1, 12))
+        S = r.integers(-3, 4, n).astype(np.int32) * 1000
+        idx, blk, sel = orc.block_topk(S, n, K, block)
+        nb = -(-n // block)
+        pad = np.full(nb * block, np.iinfo(np.int32).min, np.int64)
+        pad[:n] = S
+        bs = pad.reshape(nb, block).max(axis=1)
+        keep = sorted(sorted(range(nb), key=lambda j: (-bs[j], j))[:K])
+        want_blk = keep + [-1] * (K - len(keep))
+        assert blk[0].tolist() == want_blk, (trial, n, block, K)
+        assert sel[0].tolist() == [int(bs[j]) for j in keep] + [I32_MIN] * (K - len(keep))
+        pos = [s for j in keep for s in range(j * block, min((j + 1) * block, n))]
+        assert idx[0].tolist() == pos + [-1] * (K * block - len(pos))
+        if block == 1:
+            pidx, psel = orc.topk(S, n, K)
+            assert (pidx == idx).all() and (psel == sel).all()
+
+
+def pin_layer_block_dense_and_composition(orc):
+    """Through the whole layer with blocks of 16: K >= ceil((p+1)/16) keeps every
+    position (gated dense causal attention, torch SDPA); with fewer blocks the
+    layer equals scores -> block Top-K -> attention over the expanded rows."""
+    from scipy.special import expit
+    import synth
+    cfg = synth.CONFIGS["tiny"].replace(Tq=40, Tk=40)
+    inp = synth.host_inputs(cfg, seed=13)
+    res = orc.layer(inp, K=3, block=16)
+    ref, ref_lse = _sdpa_dense(inp["q"], inp["k"], inp["v"], inp["scale"])
+    want = ref * expit(bf16_to_f32(inp["gate"]).astype(np.float64))
+    assert np.abs(res["out"].reshape(want.shape) - want).max() < 1e-12
+    assert np.abs(res["lse"].reshape(ref_lse.shape) - ref_lse).max() < 1e-12
+    for i in range(cfg.Tq):
+        assert res["idx"][i].tolist() == list(range(i + 1)) + [-1] * (48 - i - 1)
+    cfg = synth.CONFIGS["tiny"].replace(B=2, Tq=6, Tk=70, decode=False)
+    inp = synth.host_inputs(cfg, seed=14)
+    inp["q_offset"] = np.array([10, 60], np.int32)
+    inp["kv_len"] = np.array([40, 68], np.int32)
+    res = orc.layer(inp, K=2, block=8)
+    S = orc.scores(inp["q_idx"], inp["k_idx"], inp["w"], inp["q_offset"], inp["kv_len"])
+    n = np.array([inp["q_offset"][b] + i + 1 if inp["q_offset"][b] + i < inp["kv_len"][b] else 0
+                  for b in range(2) for i in range(6)])
+    idx, blk, sel = orc.block_topk(S, n, 2, 8)
+    out, lse = orc.attention(inp["q"], inp["k"], inp["v"], inp["gate"], idx, inp["kv_len"],
+                             inp["scale"])
+    assert (res["idx"] == idx).all() and (res["sel"] == sel).all()
+    assert np.array_equal(res["out"], out) and np.array_equal(res["lse"], lse)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -50,6 +50,10 @@ MUTANTS = [
     ("append_offset_is_new_length", "q_offset_out[b] = (int32_t)old;",
      "q_offset_out[b] = (int32_t)(old + n);"),
     ("append_no_capacity_clamp", "(int32_t)(old + n < Tk ? old + n : Tk)", "(int32_t)(old + n)"),
+    ("block_score_min", "if (S[s] > m) m = S[s];", "if (m == INT32_MIN || S[s] < m) m = S[s];"),
+    ("block_expand_not_causal", "(s >= 0 && s < n) ? (int32_t)s : -1;", "(s >= 0) ? (int32_t)s : -1;"),
+    ("block_index_unscaled", "(int64_t)bi[kk] * block + t", "(int64_t)bi[kk] + t"),
+    ("layer_ignores_blocks", "if (bl > 1)\n            orc_block_topk_row", "if (0)\n            orc_block_topk_row"),
     ("overflow_unchecked", "if (acc > INT32_MAX) { acc = INT32_MAX; rc = ORC_OVERFLOW; }", ""),
 ]
 
