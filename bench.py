@@ -267,7 +267,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "prefill64k", "decode1m"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "prefill64k", "decode1m", "blocks"],
+                    default=None,
                     help="run only one fused step (profiler runs; prefill64k and decode1m are "
                          "the long-context workloads, outside the default run)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -336,6 +337,34 @@ def main():
                                    bytes=app_b, gbs=app_b / app_ms / 1e6,
                                    frac_hbm=app_b / app_ms / 1e6 / PEAK_HBM_GBS))
 
+    def run_blocks(cfg, inp_host, block, kb):
+        d = {k: dev(v) for k, v in inp_host.items() if isinstance(v, np.ndarray)}
+        geom = lci.make_geom(cfg.B, cfg.Tq, cfg.Tk, kb, d["q_offset"], d["kv_len"], Hq=cfg.Hq,
+                             Hkv=cfg.Hkv, d=cfg.d, H_I=cfg.H_I, d_I=cfg.d_I, block=block)
+        ws = torch.empty(lci.workspace_bytes(lci.ENTRY_PREFILL, geom), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty_like(d["q"])
+
+        def step():
+            lci.prefill_fwd(d["q_idx"], d["k_idx"], d["w"], d["q"], d["k"], d["v"], d["gate"],
+                            cfg.scale, d["q_offset"], d["kv_len"], kb, out=out, workspace=ws,
+                            stream=stream, block=block)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ms_step, ev_ms, kern = timed_region(timer, step, args.steps, lci)
+        tok_s = cfg.B * cfg.Tq / (ms_step * 1e-3)
+        log(f"prefill8k, blocks of {block} ({kb} kept): {ms_step:.3f} ms/step, "
+            f"{tok_s / 1e6:.2f} M tok/s")
+        for kname, kv in kern.items():
+            log(f"  {kname:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
+                f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
+        return dict(workload="prefill8k", block=block, blocks_kept=kb, ms_per_step=ms_step,
+                    event_ms_per_step=ev_ms, tok_s=tok_s,
+                    kernels_us_per_step={k: round(v["ms_per_step"] * 1e3, 2)
+                                         for k, v in kern.items()})
+
     def run_decode(name):
         dcfg = synth.CONFIGS[name]
         dd = synth.device_inputs(dcfg, seed=0)
@@ -400,6 +429,12 @@ def main():
     if args.only in (None, "prefill"):
         res["prefill"] = run_prefill("prefill8k", inp_host)
 
+    # ------------------------------------------- Prefill 8K, block-granular selection
+    # blocks of 64 positions, 32 kept: the same 2048 positions per row as the
+    # position Top-K, chosen as whole blocks
+    if args.only in (None, "blocks"):
+        res["blocks"] = run_blocks(cfg, inp_host, 64, 32)
+
     # --------------------------------------------------------------- decode 128K
     if not args.no_decode and args.only in (None, "decode"):
         res["decode"] = run_decode("decode128k")
@@ -444,6 +479,8 @@ def main():
         "kv_append": dict(pre["kv_append"], note="the whole prompt appended as one chunk to "
                           "the key/value/indexer-key caches (copy kernel; lengths kernel apart)"),
     }
+    if "blocks" in res:
+        line["blocks"] = res["blocks"]
     if "decode" in res:
         line["decode"] = res["decode"]
     print(json.dumps(line), flush=True)

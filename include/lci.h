@@ -88,6 +88,9 @@ typedef struct lci_geom {
     int32_t K;                 /* positions kept per query row                           */
     const int32_t *q_offset;   /* device [B]: position of query row 0 of each sequence   */
     const int32_t *kv_len;     /* device [B]: valid history rows of each sequence        */
+    int32_t block;             /* selection granularity: 0 or 1 = single positions; a    */
+                               /* power of two 2..256 = blocks of that many positions,   */
+                               /* K then counts blocks (see lci_topk_select)             */
 } lci_geom;
 
 /* Entry ids for lci_workspace_bytes. */
@@ -121,6 +124,13 @@ lci_status lci_idx_score(const lci_geom *g, const int8_t *q_idx, const int8_t *k
  *   idx        int32 [B, Tq, K] out: selected positions ascending, -1 padded
  *   sel_scores int32 [B, Tq, K] out, nullable: the score of each idx entry,
  *              INT32_MIN in the padding
+ * Block-granular selection (g->block = b > 1; same steps: the scorer rates
+ * positions or blocks and the top K positions or blocks are kept): block j
+ * holds positions j*b .. j*b + b - 1 and rates as its best causal position;
+ * the K best blocks are kept (higher score, then lower block index). idx is
+ * then int32 [B, Tq, K*b]: the kept blocks' causal positions ascending, -1
+ * padded; sel_scores [B, Tq, K] the kept blocks' scores. Requires K*b <= 4096
+ * (SHAPE) and ceil(Tk / b) <= 8192 (UNSUPPORTED).
  *   workspace  device scratch of at least lci_workspace_bytes(LCI_ENTRY_TOPK_SELECT)
  * Errors: NULL, SHAPE, WORKSPACE, HIP. */
 lci_status lci_topk_select(const lci_geom *g, const int32_t *scores, int32_t *idx,
@@ -139,8 +149,9 @@ lci_status lci_topk_select(const lci_geom *g, const int32_t *scores, int32_t *id
  *   mix      bf16 [B, Tq, Hq, d], nullable: the other branch's output x to mix
  *            with; requires gate (NULL error otherwise)
  *   k, v     bf16 [B, Tk, Hkv, d]; query head h reads key/value head h / (Hq/Hkv)
- *   idx      int32 [B, Tq, K]: positions to attend; entries outside 0..kv_len[b]-1
- *            (the -1 padding) are skipped; duplicates count once each; order is free
+ *   idx      int32 [B, Tq, K*max(1, g->block)]: positions to attend; entries
+ *            outside 0..kv_len[b]-1 (the -1 padding) are skipped; duplicates count
+ *            once each; order is free
  *   out      bf16 [B, Tq, Hq, d] out: s*o, or s*o + (1-s)*x with mix, where
  *            s = sigmoid(gate) (1 ungated) and o = softmax(scale*q.k) v (0 for
  *            a row without entries); fp32 arithmetic, rounded to nearest even
@@ -157,9 +168,10 @@ lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_b
 /* Fused prefill: steps 1-4 for many query rows per sequence in one call
  * ("Hybrid Sparse Attention ...", section "Engineering and Evaluation
  * Recommendations": Top-K and gather need fused kernels; chunked long prefill).
- * Arguments as in the three calls above; idx_out (int32 [B, Tq, K]) and lse are
- * nullable. Results equal lci_idx_score -> lci_topk_select ->
- * lci_sparse_attn_fwd on the same inputs (idx bit-exact).
+ * Arguments as in the three calls above; idx_out (int32 [B, Tq, K*max(1,
+ * g->block)]) and lse are nullable. Results equal lci_idx_score ->
+ * lci_topk_select -> lci_sparse_attn_fwd on the same inputs (idx bit-exact),
+ * with single positions or blocks as g->block says.
  * Errors: NULL, SHAPE, UNSUPPORTED, OVERFLOW_RISK, WORKSPACE, ALIGN, HIP. */
 lci_status lci_prefill_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
                            const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
@@ -173,7 +185,8 @@ lci_status lci_prefill_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t 
  * and split-K attention combined in a fixed order ("How Fine-Grained Sparse
  * Attention Reshapes ...", section "Engineering Practices": per-step decode
  * work decoupled from context length). Same arguments and results as
- * lci_prefill_fwd.
+ * lci_prefill_fwd. With block-granular selection (g->block > 1) the one row
+ * runs the prefill path (scores of the whole row, then the block selection).
  * Errors: NULL, SHAPE (Tq != 1 included), UNSUPPORTED, OVERFLOW_RISK,
  * WORKSPACE, ALIGN, HIP. */
 lci_status lci_decode_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,

@@ -46,7 +46,8 @@ class lci_geom(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("Tk", ctypes.c_int32),
                 ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("H_I", ctypes.c_int32), ("d_I", ctypes.c_int32), ("K", ctypes.c_int32),
-                ("q_offset", ctypes.c_void_p), ("kv_len", ctypes.c_void_p)]
+                ("q_offset", ctypes.c_void_p), ("kv_len", ctypes.c_void_p),
+                ("block", ctypes.c_int32)]
 
 
 _lib = None
@@ -125,13 +126,15 @@ def _dev(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
-def make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=0, Hkv=0, d=0, H_I=0, d_I=0) -> lci_geom:
+def make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=0, Hkv=0, d=0, H_I=0, d_I=0,
+              block=1) -> lci_geom:
     import torch
     _dev(q_offset, torch.int32, "q_offset", 1)
     _dev(kv_len, torch.int32, "kv_len", 1)
     if q_offset.numel() != B or kv_len.numel() != B:
         raise ValueError("q_offset and kv_len need one entry per sequence")
-    g = lci_geom(B, Tq, Tk, Hq, Hkv, d, H_I, d_I, K, q_offset.data_ptr(), kv_len.data_ptr())
+    g = lci_geom(B, Tq, Tk, Hq, Hkv, d, H_I, d_I, K, q_offset.data_ptr(), kv_len.data_ptr(),
+                 block)
     g._keep = (q_offset, kv_len)
     return g
 
@@ -201,14 +204,16 @@ def idx_score(q_idx, k_idx, w, q_offset, kv_len, scores=None, stream=None):
 
 
 def topk_select(scores, K, q_offset, kv_len, idx=None, sel_scores=None, want_scores=False,
-                workspace=None, stream=None):
-    """Top-K positions int32 [B,Tq,K] (ascending, -1 padded) and optional scores."""
+                workspace=None, stream=None, block=1):
+    """Top-K positions int32 [B,Tq,K] (ascending, -1 padded) and optional scores.
+    With block > 1, the K best blocks of `block` positions: idx [B,Tq,K*block]
+    holds their positions, sel_scores [B,Tq,K] the blocks' scores."""
     import torch
     _dev(scores, torch.int32, "scores", 3)
     B, Tq, Tk = scores.shape
-    g = make_geom(B, Tq, Tk, K, q_offset, kv_len)
+    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, block=block)
     if idx is None:
-        idx = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+        idx = torch.empty((B, Tq, K * max(block, 1)), dtype=torch.int32, device=scores.device)
     if want_scores and sel_scores is None:
         sel_scores = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
     _dev(idx, torch.int32, "idx", 3)
@@ -265,7 +270,7 @@ def _gate_args(q, gate, mix):
 
 
 def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset, kv_len, K,
-           out, lse, idx_out, want_lse, want_idx, workspace, stream):
+           out, lse, idx_out, want_lse, want_idx, workspace, stream, block=1):
     import torch
     _dev(q_idx, torch.int8, "q_idx", 4)
     _dev(k_idx, torch.int8, "k_idx", 3)
@@ -284,13 +289,14 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset,
         raise ValueError("inconsistent shapes")
     _gate_args(q, gate, mix)
     wsb, wsq = _w_strides(w, B, Tq, H_I)
-    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d, H_I=H_I, d_I=d_I)
+    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d, H_I=H_I, d_I=d_I,
+                  block=block)
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
     if want_idx and idx_out is None:
-        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=q.device)
+        idx_out = torch.empty((B, Tq, K * max(block, 1)), dtype=torch.int32, device=q.device)
     _dev(out, torch.bfloat16, "out", 4)
     _dev(lse, torch.float32, "lse", 3)
     _dev(idx_out, torch.int32, "idx_out", 3)
@@ -310,20 +316,23 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset,
 
 def prefill_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None, lse=None,
                 idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None,
-                mix=None):
+                mix=None, block=1):
     """Fused layer for many query rows: returns out (and idx, lse when asked).
-    ``mix`` as in ``sparse_attn_fwd``."""
+    ``mix`` as in ``sparse_attn_fwd``; with block > 1 the selection keeps K blocks
+    of `block` positions and idx rows hold K*block positions."""
     return _fused("lci_prefill_fwd", ENTRY_PREFILL, q_idx, k_idx, w, q, k, v, gate, mix, scale,
-                  q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream)
+                  q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream,
+                  block)
 
 
 def decode_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None, lse=None,
                idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None,
-               mix=None):
+               mix=None, block=1):
     """Fused layer for one query row per sequence (Tq == 1) over a long history.
-    ``mix`` as in ``sparse_attn_fwd``."""
+    ``mix`` and ``block`` as in ``prefill_fwd``."""
     return _fused("lci_decode_fwd", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, mix, scale,
-                  q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream)
+                  q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream,
+                  block)
 
 
 def kv_append(k_new, v_new, kI_new, k_cache, v_cache, kI_cache, kv_len, n_new=None,

@@ -26,6 +26,7 @@ struct Geom {
   int B, Tq, Tk, Hq, Hkv, d, H_I, d_I, K;
   const int32_t* q_offset;
   const int32_t* kv_len;
+  int block;  // selection granularity: 1 = single positions, else blocks of this many
 };
 
 // ---- indexer scoring
@@ -80,6 +81,17 @@ hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* 
                               const uint16_t* mix,
                               float scale, uint16_t* out, float* lse, int splits,
                               void* workspace, bool masks_ready, hipStream_t stream);
+
+// ---- block-granular Top-K: K blocks of g.block positions (a power of two,
+// at least 2) per row, the row's blocks in LDS. idx rows hold K*block positions,
+// sel (nullable) the K kept blocks' scores. With dm (masks of the attention
+// geometry, K*block positions a row) it also writes the dense-path flags and
+// masks of its rows.
+constexpr int kBlockTopkMaxBlocks = 8192;  // ceil(Tk / block) at most
+constexpr int kBlockTopkMaxKeep = 2048;    // K at most (K*block <= 4096, block >= 2)
+hipError_t launch_block_topk(const Geom& g, const int32_t* scores, int64_t score_row_stride,
+                             int row_begin, int row_count, int32_t* idx, int32_t* sel,
+                             const DenseMasks* dm, hipStream_t stream);
 
 // ---- appending rows to the key / value / indexer-key caches
 // Sizes from g: B, Tq (= rows of the new tensors per sequence), Tk (capacity),

@@ -26,11 +26,22 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 constexpr int kMaxK = 4096;
 
+// Positions per selected unit: 1, or the block size of block-granular selection.
+int sel_block(const lci_geom* g) { return g->block > 1 ? g->block : 1; }
+
 // Sizes common to every entry.
 lci_status check_base(const lci_geom* g) {
   if (!g) return LCI_ERR_NULL;
   if (!g->q_offset || !g->kv_len) return LCI_ERR_NULL;
   if (g->B < 1 || g->Tq < 1 || g->Tk < 1 || g->K < 1 || g->K > kMaxK) return LCI_ERR_SHAPE;
+  if (g->block < 0) return LCI_ERR_SHAPE;
+  const int bl = sel_block(g);
+  if (bl > 1 && (bl > 256 || (bl & (bl - 1)) != 0)) return LCI_ERR_UNSUPPORTED;
+  // index rows hold K*block positions
+  if (static_cast<int64_t>(g->K) * bl > kMaxK) return LCI_ERR_SHAPE;
+  // a row's blocks live in LDS
+  if (bl > 1 && (static_cast<int64_t>(g->Tk) + bl - 1) / bl > lci::kBlockTopkMaxBlocks)
+    return LCI_ERR_UNSUPPORTED;
   if (!aligned4(g->q_offset) || !aligned4(g->kv_len)) return LCI_ERR_ALIGN;
   return LCI_OK;
 }
@@ -58,7 +69,14 @@ bool scale_ok(float scale) { return scale > 0.f && scale < INFINITY; }
 
 Geom to_geom(const lci_geom* g) {
   return Geom{g->B, g->Tq, g->Tk, g->Hq, g->Hkv, g->d, g->H_I, g->d_I, g->K, g->q_offset,
-              g->kv_len};
+              g->kv_len, sel_block(g)};
+}
+
+// The attention kernels' view: index rows of K*block positions.
+Geom attn_geom(const lci_geom* g) {
+  Geom a = to_geom(g);
+  a.K = g->K * a.block;
+  return a;
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -85,11 +103,11 @@ struct PrefillLayout {
 
 PrefillLayout prefill_layout(const lci_geom* g) {
   PrefillLayout L{};
-  const Geom gg = to_geom(g);
+  const Geom gg = attn_geom(g);
   L.chunk_rows = prefill_chunk_rows(g);
   L.splits = lci::sparse_attn_pick_splits(gg);
   L.idx_off = 0;
-  L.idx_bytes = align_up(static_cast<size_t>(g->B) * g->Tq * g->K * sizeof(int32_t));
+  L.idx_bytes = align_up(static_cast<size_t>(g->B) * g->Tq * gg.K * sizeof(int32_t));
   L.score_off = L.idx_off + L.idx_bytes;
   L.score_bytes = align_up(static_cast<size_t>(g->B) * L.chunk_rows * g->Tk * sizeof(int32_t));
   L.attn_off = L.score_off + L.score_bytes;
@@ -128,7 +146,7 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
       return 0;
     case LCI_ENTRY_SPARSE_ATTN: {
       if (check_attention(g) != LCI_OK) return 0;
-      const Geom gg = to_geom(g);
+      const Geom gg = attn_geom(g);
       return lci::sparse_attn_workspace(gg, lci::sparse_attn_pick_splits(gg));
     }
     case LCI_ENTRY_PREFILL:
@@ -136,6 +154,8 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
       return prefill_layout(g).total;
     case LCI_ENTRY_DECODE:
       if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK || g->Tq != 1) return 0;
+      // block-granular decode runs the prefill path on its one row
+      if (sel_block(g) > 1) return prefill_layout(g).total;
       return lci::decode_layout(to_geom(g)).total;
     default:
       return 0;
@@ -167,6 +187,9 @@ lci_status lci_topk_select(const lci_geom* g, const int32_t* scores, int32_t* id
   if (!aligned4(scores) || !aligned4(idx) || (sel_scores && !aligned4(sel_scores)))
     return LCI_ERR_ALIGN;
   const Geom gg = to_geom(g);
+  if (gg.block > 1)
+    return hip_status(lci::launch_block_topk(gg, scores, g->Tk, 0, g->Tq, idx, sel_scores,
+                                             nullptr, static_cast<hipStream_t>(stream)));
   return hip_status(lci::launch_topk_rows(gg, scores, g->Tk, 0, g->Tq, idx, sel_scores, nullptr,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -184,7 +207,7 @@ lci_status lci_sparse_attn_fwd(const lci_geom* g, const lci_bf16* q, const lci_b
       (gate && !aligned16(gate)) || (mix && !aligned16(mix)) || !aligned4(idx) ||
       (lse && !aligned4(lse)))
     return LCI_ERR_ALIGN;
-  const Geom gg = to_geom(g);
+  const Geom gg = attn_geom(g);
   const int splits = lci::sparse_attn_pick_splits(gg);
   const size_t need = lci::sparse_attn_workspace(gg, splits);
   if (need > 0 && (!workspace || ws_bytes < need)) return LCI_ERR_WORKSPACE;
@@ -214,22 +237,26 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   if (!workspace || ws_bytes < L.total) return LCI_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LCI_ERR_ALIGN;
   const Geom gg = to_geom(g);
+  const Geom ga = attn_geom(g);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx_off);
   int32_t* sc = reinterpret_cast<int32_t*>(ws + L.score_off);
-  // with the dense-tile path on (one split) and rows short enough for the
-  // one-wave Top-K kernel, that kernel writes the tile path's masks and flags
-  const bool masks = L.splits == 1 && g->Tk <= lci::kWaveTopkMax;
-  const lci::DenseMasks dm = masks ? lci::dense_masks(gg, ws + L.attn_off) : lci::DenseMasks{};
+  // with the dense-tile path on (one split), the selection kernel writes the
+  // tile path's masks and flags: the block kernel always, the position kernel
+  // for rows short enough for its one-wave form
+  const bool masks = L.splits == 1 && (gg.block > 1 || g->Tk <= lci::kWaveTopkMax);
+  const lci::DenseMasks dm = masks ? lci::dense_masks(ga, ws + L.attn_off) : lci::DenseMasks{};
   for (int r0 = 0; r0 < g->Tq; r0 += L.chunk_rows) {
     const int rc = std::min(L.chunk_rows, g->Tq - r0);
     hipError_t e = lci::launch_idx_score(gg, q_idx, k_idx, w, wsb, wsq, sc, g->Tk, r0, rc, st);
     if (e != hipSuccess) return hip_status(e);
-    e = lci::launch_topk_rows(gg, sc, g->Tk, r0, rc, idx, nullptr, masks ? &dm : nullptr, st);
+    e = gg.block > 1
+            ? lci::launch_block_topk(gg, sc, g->Tk, r0, rc, idx, nullptr, masks ? &dm : nullptr, st)
+            : lci::launch_topk_rows(gg, sc, g->Tk, r0, rc, idx, nullptr, masks ? &dm : nullptr, st);
     if (e != hipSuccess) return hip_status(e);
   }
-  return hip_status(lci::launch_sparse_attn(gg, q, k, v, idx, gate, mix, scale, out, lse,
+  return hip_status(lci::launch_sparse_attn(ga, q, k, v, idx, gate, mix, scale, out, lse,
                                             L.splits, ws + L.attn_off, masks, st));
 }
 
@@ -252,6 +279,11 @@ lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* 
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if (g->Tq != 1) return LCI_ERR_SHAPE;
+  // block-granular selection: the prefill path on the one row (its selection
+  // works on at most kBlockTopkMaxBlocks blocks, which bounds the history)
+  if (sel_block(g) > 1)
+    return fused_forward(g, q_idx, k_idx, w, w_stride_b, w_stride_q, q, k, v, gate, mix,
+                         softmax_scale, out, lse, idx_out, workspace, ws_bytes, stream);
   if ((s = check_indexer(g)) != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
   if (static_cast<int64_t>(g->Tk) > static_cast<int64_t>(lci::kDecChunk) * lci::kDecMaxChunks)

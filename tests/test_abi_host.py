@@ -52,10 +52,11 @@ def test_abi_version_and_status_strings(lib):
 
 def geom(**kw):
     base = dict(B=1, Tq=16, Tk=64, Hq=8, Hkv=2, d=128, H_I=8, d_I=64, K=8,
-                q_offset=FAKE, kv_len=FAKE)
+                q_offset=FAKE, kv_len=FAKE, block=0)
     base.update(kw)
     return lci.lci_geom(base["B"], base["Tq"], base["Tk"], base["Hq"], base["Hkv"], base["d"],
-                        base["H_I"], base["d_I"], base["K"], base["q_offset"], base["kv_len"])
+                        base["H_I"], base["d_I"], base["K"], base["q_offset"], base["kv_len"],
+                        base["block"])
 
 
 def score(lib, g, q=FAKE, k=FAKE, w=FAKE, out=FAKE, wsb=0, wsq=0):
@@ -115,6 +116,18 @@ def test_attention_limits(lib):
     assert attn(lib, geom(Hq=48, Hkv=16)) == UNSUP           # Hkv > 8
     assert attn(lib, geom(Hq=64, Hkv=2)) == UNSUP            # group of 32 query heads
     assert attn(lib, geom(Hq=6, Hkv=2)) == UNSUP             # group of 3
+
+
+def test_block_granularity_limits(lib):
+    assert score(lib, geom(block=-1)) == SHAPE
+    assert score(lib, geom(block=3)) == UNSUP                 # not a power of two
+    assert score(lib, geom(block=512)) == UNSUP
+    assert score(lib, geom(block=64, K=65)) == SHAPE          # 4160 positions per row
+    assert score(lib, geom(block=16, Tk=16 * 8192 + 1)) == UNSUP
+    g = geom(block=64, K=64, Tk=8192)
+    assert lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g)) >= 16 * 4096 * 4
+    gd = geom(Tq=1, block=64, K=32, Tk=1 << 17)
+    assert lib.lci_workspace_bytes(lci.ENTRY_DECODE, ctypes.byref(gd)) > 0
 
 
 def test_softmax_scale_must_be_positive(lib):
