@@ -55,14 +55,14 @@ def open_library(path: str):
     lib.orc_score_row.argtypes = [i32, i32, P, P, P, i64, P]
     lib.orc_score_row.restype = i32
     lib.orc_topk_row.argtypes = [P, i64, i32, P, P]
-    lib.orc_attn_row.argtypes = [i32, i32, i32, P, P, P, i64, P, i32, P, P, f64, P, P]
+    lib.orc_attn_row.argtypes = [i32, i32, i32, P, P, P, i64, P, i32, i32, P, P, f64, P, P]
     lib.orc_scores_rows.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i64, i64, i64, P, P, P]
     lib.orc_scores_rows.restype = i32
     lib.orc_topk_rows.argtypes = [i64, P, i64, P, i32, P, P]
-    lib.orc_attn_rows.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, i64,
+    lib.orc_attn_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, i64,
                                   P, P, P, P, P]
     lib.orc_block_topk_rows.argtypes = [i64, P, i64, P, i32, i32, P, P, P]
-    lib.orc_layer_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
+    lib.orc_layer_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                    i64, i64, P, P, P, P, P, f64, i64, P, P, P, P, P, P]
     lib.orc_layer_rows.restype = i32
     lib.orc_kv_append.argtypes = [i32, i32, i32, i64, P, P, P, P, P, P]
@@ -153,8 +153,9 @@ class Oracle:
     def attention(self, q, k, v, gate, idx, kv_len, scale, rows=None, mix=None):
         """Gated attention over given index rows. q, gate, mix uint16 [B,Tq,Hq,d] (gate
         may be None: ungated; mix may be None: the gate only scales, else
-        out = s*o + (1-s)*mix); k, v uint16 [B,Tk,Hkv,d]; idx int32 [nrows, K] for the
-        listed rows. Returns (out float64 [nrows,Hq,d], lse float64 [nrows,Hq])."""
+        out = s*o + (1-s)*mix); k, v uint16 [B,Tk,Hkv,d]; idx int32 [nrows, K] (one
+        set per row) or [nrows, Hkv, K] (one per key/value head) for the listed
+        rows. Returns (out float64 [nrows,Hq,d], lse float64 [nrows,Hq])."""
         q = _c(q, np.uint16)
         k = _c(k, np.uint16)
         v = _c(v, np.uint16)
@@ -166,11 +167,15 @@ class Oracle:
             if t is not None and t.shape != q.shape:
                 raise ValueError("gate and mix have the shape of q")
         rb, ri = _rows(rows, B, Tq)
-        idx = _c(idx, np.int32).reshape(len(rb), -1)
-        K = idx.shape[1]
+        idx = _c(idx, np.int32)
+        sets = idx.shape[1] if idx.ndim == 3 else 1
+        if sets not in (1, Hkv):
+            raise ValueError("one index set per row or one per key/value head")
+        idx = idx.reshape(len(rb), sets, -1)
+        K = idx.shape[2]
         out = np.empty((len(rb), Hq, d), np.float64)
         lse = np.empty((len(rb), Hq), np.float64)
-        self.lib.orc_attn_rows(Tq, Tk, Hq, Hkv, d, K, _p(_c(kv_len, np.int32)), _p(q), _p(k),
+        self.lib.orc_attn_rows(Tq, Tk, Hq, Hkv, d, K, sets, _p(_c(kv_len, np.int32)), _p(q), _p(k),
                               _p(v), _p(gate), _p(mix), float(scale), len(rb), _p(rb), _p(ri),
                               _p(idx), _p(out), _p(lse))
         return out, lse
@@ -193,12 +198,14 @@ class Oracle:
                                     _p(blk), _p(sel))
         return idx, blk, sel
 
-    def layer(self, inp, K, rows=None, gated=True, block=1):
+    def layer(self, inp, K, rows=None, gated=True, block=1, sets=1):
         """The whole layer (score -> Top-K -> attention -> gate) for the listed rows
         of an input dict as produced by ``synth.host_inputs``; an entry "mix" (the
         other branch's output, uint16 [B,Tq,Hq,d]) is mixed in by the gate. With
         block > 1 the selection keeps K blocks of `block` positions: idx holds
-        K*block positions per row and sel the K kept blocks' scores.
+        K*block positions per row and sel the K kept blocks' scores. With sets =
+        Hkv every key/value head has its own index set, scored by its group of
+        H_I/Hkv indexer heads: idx [nrows, Hkv, K or K*block], sel [nrows, Hkv, K].
         Returns dict(idx, sel, out, lse) with out float64 [nrows,Hq,d]."""
         q_idx = _c(inp["q_idx"], np.int8)
         k_idx = _c(inp["k_idx"], np.int8)
@@ -218,17 +225,22 @@ class Oracle:
         rb, ri = _rows(rows, B, Tq)
         nr = len(rb)
         bl = max(int(block), 1)
-        idx = np.empty((nr, K * bl), np.int32)
-        sel = np.empty((nr, K), np.int32)
+        ns = max(int(sets), 1)
+        if ns not in (1, Hkv) or H_I % ns:
+            raise ValueError("sets is 1 or Hkv, and divides H_I")
+        idx = np.empty((nr, ns, K * bl), np.int32)
+        sel = np.empty((nr, ns, K), np.int32)
         out = np.empty((nr, Hq, d), np.float64)
         lse = np.empty((nr, Hq), np.float64)
-        rc = self.lib.orc_layer_rows(Tq, Tk, Hq, Hkv, d, H_I, d_I, K, bl,
+        rc = self.lib.orc_layer_rows(Tq, Tk, Hq, Hkv, d, H_I, d_I, K, bl, ns,
                                     _p(_c(inp["q_offset"], np.int32)), _p(_c(inp["kv_len"], np.int32)),
                                     _p(q_idx), _p(k_idx), _p(w), wsb, wsq, _p(q), _p(k), _p(v),
                                     _p(gate), _p(mix), float(inp["scale"]), nr, _p(rb), _p(ri), _p(idx),
                                     _p(sel), _p(out), _p(lse))
         if rc == OVERFLOW:
             raise OverflowError("indexer score outside the int32 range")
+        if ns == 1:
+            idx, sel = idx[:, 0], sel[:, 0]
         return dict(idx=idx, sel=sel, out=out, lse=lse)
 
 

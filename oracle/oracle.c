@@ -132,14 +132,16 @@ static double orc_gate(double o, double G, const uint16_t *mix, int64_t j)
 }
 
 /* Gated attention of one query row over the listed positions.
- * q, gate, mix [Hq][d]; k, v [kv_rows][Hkv][d] (one sequence); idx [K].
+ * q, gate, mix [Hq][d]; k, v [kv_rows][Hkv][d] (one sequence); idx [sets][K]:
+ * one index set shared by every head (sets = 1), or one per key/value head
+ * (sets = Hkv: query head h reads the set of its key/value head h / (Hq/Hkv)).
  * Entries outside 0..kv_len-1 (the -1 padding) are skipped. gate may be NULL
  * (ungated; then mix is ignored), mix may be NULL (no mixing). out [Hq][d],
  * lse [Hq] (natural log of the softmax denominator, including the running
  * max); a row with no valid entry has o = 0 (so out = 0 without mixing) and
  * lse = -inf. */
 void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
-                  const uint16_t *v, int64_t kv_len, const int32_t *idx, int K,
+                  const uint16_t *v, int64_t kv_len, const int32_t *idx, int K, int sets,
                   const uint16_t *gate, const uint16_t *mix, double scale, double *out,
                   double *lse)
 {
@@ -147,9 +149,10 @@ void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
     double *logit = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
     for (int h = 0; h < Hq; ++h) {
         int g = h / G;
+        const int32_t *ih = idx + (int64_t)(g * sets / Hkv) * K;   /* this head's index set */
         double m = -INFINITY;
         for (int t = 0; t < K; ++t) {
-            int64_t s = idx[t];
+            int64_t s = ih[t];
             if (s < 0 || s >= kv_len) { logit[t] = -INFINITY; continue; }
             double dot = 0.0;
             for (int j = 0; j < d; ++j)
@@ -164,7 +167,7 @@ void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
         } else {
             double Z = 0.0;
             for (int t = 0; t < K; ++t) {
-                int64_t s = idx[t];
+                int64_t s = ih[t];
                 if (s < 0 || s >= kv_len) continue;
                 double e = exp(logit[t] - m);
                 Z += e;
@@ -267,8 +270,9 @@ void orc_topk_rows(int64_t nrows, const int32_t *S, int64_t stride, const int64_
                      sel ? sel + r * (int64_t)K : NULL);
 }
 
-/* Attention + gate for a list of rows with the given index rows idx [nrows][K]. */
-void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t *kv_len,
+/* Attention + gate for a list of rows with the given index rows idx
+ * [nrows][sets][K] (sets as in orc_attn_row). */
+void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, int sets, const int32_t *kv_len,
                    const uint16_t *q, const uint16_t *k, const uint16_t *v,
                    const uint16_t *gate, const uint16_t *mix, double scale, int64_t nrows,
                    const int32_t *row_b,
@@ -280,7 +284,7 @@ void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t 
         int64_t qrow = (int64_t)b * Tq + i;
         int64_t kvl = kv_len[b] < Tk ? kv_len[b] : Tk;
         orc_attn_row(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
-                     v + (int64_t)b * Tk * Hkv * d, kvl, idx + r * (int64_t)K, K,
+                     v + (int64_t)b * Tk * Hkv * d, kvl, idx + r * (int64_t)sets * K, K, sets,
                      gate ? gate + qrow * Hq * d : NULL, mix ? mix + qrow * Hq * d : NULL, scale,
                      out + r * (int64_t)Hq * d, lse ? lse + r * (int64_t)Hq : NULL);
     }
@@ -288,13 +292,21 @@ void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t 
 
 /* The whole layer for a list of rows: score -> Top-K -> attention -> gate.
  * With block > 1 the selection keeps K blocks of that many positions
- * (orc_block_topk_row): idx [nrows][K*block] positions, sel [nrows][K] the kept
- * blocks' scores; with block <= 1 single positions, idx and sel [nrows][K].
- * out [nrows][Hq][d], lse [nrows][Hq]. Invalid rows give
+ * (orc_block_topk_row): index rows of K*block positions, sel the K kept
+ * blocks' scores; with block <= 1 single positions (K of each).
+ * Index sets: sets = 1, one set per query row shared by every head; sets =
+ * Hkv, one per key/value head ("Hybrid Sparse Attention for Long-Context
+ * LLMs", the pseudocode of the Indexer + Top-K section keeps indices per head;
+ * "How Fine-Grained Sparse Attention Reshapes ...", the runtime section's
+ * pseudocode likewise). Reading taken for the per-set scorer: the H_I indexer
+ * heads are split into sets consecutive groups of H_I/sets heads, and set g is
+ * scored by group g alone (its heads and their weights).
+ * idx [nrows][sets][K or K*block], sel [nrows][sets][K], out [nrows][Hq][d],
+ * lse [nrows][Hq]. Invalid rows give
  * idx = -1, sel = INT32_MIN, an attention output of 0 (out = 0 unless mixed)
  * and lse = -inf. Returns ORC_OVERFLOW if a score overflowed int32. */
 int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int K,
-                   int block, const int32_t *q_offset, const int32_t *kv_len, const int8_t *q_idx,
+                   int block, int sets, const int32_t *q_offset, const int32_t *kv_len, const int8_t *q_idx,
                    const int8_t *k_idx, const int8_t *w, int64_t w_stride_b,
                    int64_t w_stride_q, const uint16_t *q, const uint16_t *k,
                    const uint16_t *v, const uint16_t *gate, const uint16_t *mix, double scale,
@@ -304,18 +316,20 @@ int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int
     int rc = ORC_OK;
     const int bl = block > 1 ? block : 1;
     const int KI = K * bl;   /* positions per index row */
+    const int ns = sets > 1 ? sets : 1;
+    const int Hg = H_I / ns; /* indexer heads per index set */
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : rc)
     for (int64_t r = 0; r < nrows; ++r) {
         int b = row_b[r], i = row_i[r];
         int64_t p = (int64_t)q_offset[b] + i;
-        int32_t *ir = idx + r * (int64_t)KI;
-        int32_t *sr = sel ? sel + r * (int64_t)K : NULL;
+        int32_t *irow = idx + r * (int64_t)ns * KI;
+        int32_t *srow = sel ? sel + r * (int64_t)ns * K : NULL;
         double *orow = out + r * (int64_t)Hq * d;
         double *lrow = lse ? lse + r * (int64_t)Hq : NULL;
         if (p < 0 || p >= kv_len[b] || kv_len[b] > Tk) {
             int64_t qrow = (int64_t)b * Tq + i;
-            for (int j = 0; j < KI; ++j) ir[j] = -1;
-            for (int j = 0; j < K; ++j) if (sr) sr[j] = INT32_MIN;
+            for (int j = 0; j < ns * KI; ++j) irow[j] = -1;
+            for (int j = 0; j < ns * K; ++j) if (srow) srow[j] = INT32_MIN;
             for (int64_t j = 0; j < (int64_t)Hq * d; ++j)
                 orow[j] = gate ? orc_gate(0.0, orc_bf16(gate[qrow * Hq * d + j]),
                                           mix ? mix + qrow * Hq * d : NULL, j)
@@ -324,18 +338,23 @@ int orc_layer_rows(int Tq, int Tk, int Hq, int Hkv, int d, int H_I, int d_I, int
             continue;
         }
         int32_t *S = (int32_t *)malloc((size_t)(p + 1) * sizeof(int32_t));
-        const int8_t *qI = q_idx + ((int64_t)b * Tq + i) * H_I * d_I;
         const int8_t *kI = k_idx + (int64_t)b * Tk * d_I;
         const int8_t *wr = w + b * w_stride_b + (int64_t)i * w_stride_q;
-        rc |= orc_score_row(H_I, d_I, qI, kI, wr, p + 1, S);
-        if (bl > 1)
-            orc_block_topk_row(S, p + 1, bl, K, ir, NULL, sr);
-        else
-            orc_topk_row(S, p + 1, K, ir, sr);
+        for (int gs = 0; gs < ns; ++gs) {
+            /* index set gs: scored by indexer heads gs*Hg .. gs*Hg + Hg - 1 */
+            const int8_t *qI = q_idx + (((int64_t)b * Tq + i) * H_I + (int64_t)gs * Hg) * d_I;
+            int32_t *ir = irow + (int64_t)gs * KI;
+            int32_t *sr = srow ? srow + (int64_t)gs * K : NULL;
+            rc |= orc_score_row(Hg, d_I, qI, kI, wr + gs * Hg, p + 1, S);
+            if (bl > 1)
+                orc_block_topk_row(S, p + 1, bl, K, ir, NULL, sr);
+            else
+                orc_topk_row(S, p + 1, K, ir, sr);
+        }
         free(S);
         int64_t qrow = (int64_t)b * Tq + i;
         orc_attn_row(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
-                     v + (int64_t)b * Tk * Hkv * d, kv_len[b], ir, KI,
+                     v + (int64_t)b * Tk * Hkv * d, kv_len[b], irow, KI, ns,
                      gate ? gate + qrow * Hq * d : NULL, mix ? mix + qrow * Hq * d : NULL, scale,
                      orow, lrow);
     }

@@ -648,4 +648,44 @@ def pin_layer_block_dense_and_composition(orc):
     assert np.array_equal(res["out"], out) and np.array_equal(res["lse"], lse)
 
 
+# ------------------------------------------------------------ index sets
+
+def pin_sets_per_kv_head(orc):
+    """One index set per key/value head equals, head by head, the shared-set
+    layer run on that head's own sub-problem: its group of indexer heads and
+    their weights, its query heads, its keys and values (sliced with numpy).
+    Identical indexer groups give every head the shared-set selection."""
+    import synth
+    cfg = synth.CONFIGS["tiny"].replace(B=2, Tq=12, Tk=60, Hq=4, Hkv=2, H_I=4, K=7, decode=False)
+    inp = synth.host_inputs(cfg, seed=15)
+    inp["w"] = np.array([1, 3, 4, 2], np.int8)
+    inp["q_offset"] = np.array([40, 50], np.int32)
+    inp["kv_len"] = np.array([52, 55], np.int32)   # sequence 1 ends in invalid rows
+    for block in (1, 4):
+        res = orc.layer(inp, K=3 if block > 1 else cfg.K, block=block, sets=2)
+        for g in range(2):
+            sub = dict(inp)
+            sub["q_idx"] = np.ascontiguousarray(inp["q_idx"][:, :, 2 * g:2 * g + 2])
+            sub["w"] = np.ascontiguousarray(inp["w"][2 * g:2 * g + 2])
+            for n in ("q", "gate"):
+                sub[n] = np.ascontiguousarray(inp[n][:, :, 2 * g:2 * g + 2])
+            for n in ("k", "v"):
+                sub[n] = np.ascontiguousarray(inp[n][:, :, g:g + 1])
+            one = orc.layer(sub, K=3 if block > 1 else cfg.K, block=block)
+            assert (res["idx"][:, g] == one["idx"]).all() and (res["sel"][:, g] == one["sel"]).all()
+            assert np.array_equal(res["out"][:, 2 * g:2 * g + 2], one["out"])
+            assert np.array_equal(res["lse"][:, 2 * g:2 * g + 2], one["lse"])
+        assert not (res["idx"][:, 0] == res["idx"][:, 1]).all()
+    # both groups a copy of group 0: every head keeps the shared-set selection
+    dup = dict(inp)
+    dup["q_idx"] = np.ascontiguousarray(np.concatenate([inp["q_idx"][:, :, :2]] * 2, axis=2))
+    dup["w"] = np.array([1, 3, 1, 3], np.int8)
+    res = orc.layer(dup, K=cfg.K, sets=2)
+    base = dict(dup, q_idx=np.ascontiguousarray(inp["q_idx"][:, :, :2]), w=np.array([1, 3], np.int8))
+    shared = orc.layer(base, K=cfg.K)
+    for g in range(2):
+        assert (res["idx"][:, g] == shared["idx"]).all()
+    assert np.array_equal(res["out"], shared["out"])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

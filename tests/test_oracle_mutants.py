@@ -53,7 +53,13 @@ MUTANTS = [
     ("block_score_min", "if (S[s] > m) m = S[s];", "if (m == INT32_MIN || S[s] < m) m = S[s];"),
     ("block_expand_not_causal", "(s >= 0 && s < n) ? (int32_t)s : -1;", "(s >= 0) ? (int32_t)s : -1;"),
     ("block_index_unscaled", "(int64_t)bi[kk] * block + t", "(int64_t)bi[kk] + t"),
-    ("layer_ignores_blocks", "if (bl > 1)\n            orc_block_topk_row", "if (0)\n            orc_block_topk_row"),
+    ("layer_ignores_blocks", "if (bl > 1)\n                orc_block_topk_row",
+     "if (0)\n                orc_block_topk_row"),
+    ("sets_share_group0_heads", "const int8_t *qI = q_idx + (((int64_t)b * Tq + i) * H_I + (int64_t)gs * Hg) * d_I;",
+     "const int8_t *qI = q_idx + ((int64_t)b * Tq + i) * H_I * d_I;"),
+    ("sets_share_group0_weights", "wr + gs * Hg, p + 1, S);", "wr, p + 1, S);"),
+    ("heads_read_set0", "const int32_t *ih = idx + (int64_t)(g * sets / Hkv) * K;",
+     "const int32_t *ih = idx;"),
     ("overflow_unchecked", "if (acc > INT32_MAX) { acc = INT32_MAX; rc = ORC_OVERFLOW; }", ""),
 ]
 
