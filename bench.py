@@ -267,7 +267,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "prefill64k", "decode1m", "blocks"],
+    ap.add_argument("--only", choices=["prefill", "decode", "prefill64k", "decode1m", "blocks",
+                                       "sets"],
                     default=None,
                     help="run only one fused step (profiler runs; prefill64k and decode1m are "
                          "the long-context workloads, outside the default run)")
@@ -337,10 +338,13 @@ def main():
                                    bytes=app_b, gbs=app_b / app_ms / 1e6,
                                    frac_hbm=app_b / app_ms / 1e6 / PEAK_HBM_GBS))
 
-    def run_blocks(cfg, inp_host, block, kb):
+    def run_variant(cfg, inp_host, block, kb, sets):
+        """Prefill-8K with block-granular selection and/or index sets per key/value head."""
+        torch.cuda.empty_cache()   # the buffers of earlier legs go back to the device
         d = {k: dev(v) for k, v in inp_host.items() if isinstance(v, np.ndarray)}
         geom = lci.make_geom(cfg.B, cfg.Tq, cfg.Tk, kb, d["q_offset"], d["kv_len"], Hq=cfg.Hq,
-                             Hkv=cfg.Hkv, d=cfg.d, H_I=cfg.H_I, d_I=cfg.d_I, block=block)
+                             Hkv=cfg.Hkv, d=cfg.d, H_I=cfg.H_I, d_I=cfg.d_I, block=block,
+                             sets=sets)
         ws = torch.empty(lci.workspace_bytes(lci.ENTRY_PREFILL, geom), dtype=torch.uint8,
                          device="cuda")
         out = torch.empty_like(d["q"])
@@ -348,19 +352,19 @@ def main():
         def step():
             lci.prefill_fwd(d["q_idx"], d["k_idx"], d["w"], d["q"], d["k"], d["v"], d["gate"],
                             cfg.scale, d["q_offset"], d["kv_len"], kb, out=out, workspace=ws,
-                            stream=stream, block=block)
+                            stream=stream, block=block, sets=sets)
 
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
         ms_step, ev_ms, kern = timed_region(timer, step, args.steps, lci)
         tok_s = cfg.B * cfg.Tq / (ms_step * 1e-3)
-        log(f"prefill8k, blocks of {block} ({kb} kept): {ms_step:.3f} ms/step, "
-            f"{tok_s / 1e6:.2f} M tok/s")
+        log(f"prefill8k, blocks of {block} ({kb} kept), {sets} index set(s): {ms_step:.3f} "
+            f"ms/step, {tok_s / 1e6:.2f} M tok/s")
         for kname, kv in kern.items():
             log(f"  {kname:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
                 f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
-        return dict(workload="prefill8k", block=block, blocks_kept=kb, ms_per_step=ms_step,
+        return dict(workload="prefill8k", block=block, kept=kb, index_sets=sets, ms_per_step=ms_step,
                     event_ms_per_step=ev_ms, tok_s=tok_s,
                     kernels_us_per_step={k: round(v["ms_per_step"] * 1e3, 2)
                                          for k, v in kern.items()})
@@ -433,7 +437,10 @@ def main():
     # blocks of 64 positions, 32 kept: the same 2048 positions per row as the
     # position Top-K, chosen as whole blocks
     if args.only in (None, "blocks"):
-        res["blocks"] = run_blocks(cfg, inp_host, 64, 32)
+        res["blocks"] = run_variant(cfg, inp_host, 64, 32, 1)
+    # one index set per key/value head (4 sets of 2 indexer heads), K = 2048
+    if args.only in (None, "sets"):
+        res["sets"] = run_variant(cfg, inp_host, 1, cfg.K, cfg.Hkv)
 
     # --------------------------------------------------------------- decode 128K
     if not args.no_decode and args.only in (None, "decode"):
@@ -479,8 +486,9 @@ def main():
         "kv_append": dict(pre["kv_append"], note="the whole prompt appended as one chunk to "
                           "the key/value/indexer-key caches (copy kernel; lengths kernel apart)"),
     }
-    if "blocks" in res:
-        line["blocks"] = res["blocks"]
+    for name in ("blocks", "sets"):
+        if name in res:
+            line[name] = res[name]
     if "decode" in res:
         line["decode"] = res["decode"]
     print(json.dumps(line), flush=True)

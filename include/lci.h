@@ -91,6 +91,9 @@ typedef struct lci_geom {
     int32_t block;             /* selection granularity: 0 or 1 = single positions; a    */
                                /* power of two 2..256 = blocks of that many positions,   */
                                /* K then counts blocks (see lci_topk_select)             */
+    int32_t sets;              /* index sets per query row: 0 or 1 = one set shared by   */
+                               /* every head; Hkv = one per key/value head (fused        */
+                               /* entries and lci_sparse_attn_fwd only; see below)       */
 } lci_geom;
 
 /* Entry ids for lci_workspace_bytes. */
@@ -164,6 +167,18 @@ lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_b
                                const lci_bf16 *v, const int32_t *idx, const lci_bf16 *gate,
                                const lci_bf16 *mix, float softmax_scale, lci_bf16 *out,
                                float *lse, void *workspace, size_t ws_bytes, void *stream);
+
+/* Index sets per key/value head (g->sets = Hkv > 1). The pages' pseudocode keeps
+ * one index row per head ("Hybrid Sparse Attention ...", the pseudocode of the
+ * Indexer + Top-K section; "How Fine-Grained Sparse Attention Reshapes ...",
+ * section "How Indexer + Top-K Works at Runtime"). The H_I indexer heads split
+ * into Hkv consecutive groups of H_I/Hkv heads (H_I must be a multiple of Hkv,
+ * else SHAPE); set g is scored by group g alone, with its heads' weights, and
+ * selected like a shared set; query head h attends over the set of its
+ * key/value head h / (Hq/Hkv). Index rows are then int32 [B, Hkv, Tq, K*max(1,
+ * block)] (idx_out of the fused entries, idx of lci_sparse_attn_fwd). These
+ * rows take the gather attention kernel. lci_idx_score and lci_topk_select work
+ * on one set (sets > 1: UNSUPPORTED). */
 
 /* Fused prefill: steps 1-4 for many query rows per sequence in one call
  * ("Hybrid Sparse Attention ...", section "Engineering and Evaluation

@@ -47,7 +47,7 @@ class lci_geom(ctypes.Structure):
                 ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("H_I", ctypes.c_int32), ("d_I", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("q_offset", ctypes.c_void_p), ("kv_len", ctypes.c_void_p),
-                ("block", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("sets", ctypes.c_int32)]
 
 
 _lib = None
@@ -127,14 +127,14 @@ def _dev(t, dtype, name, ndim=None):
 
 
 def make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=0, Hkv=0, d=0, H_I=0, d_I=0,
-              block=1) -> lci_geom:
+              block=1, sets=1) -> lci_geom:
     import torch
     _dev(q_offset, torch.int32, "q_offset", 1)
     _dev(kv_len, torch.int32, "kv_len", 1)
     if q_offset.numel() != B or kv_len.numel() != B:
         raise ValueError("q_offset and kv_len need one entry per sequence")
     g = lci_geom(B, Tq, Tk, Hq, Hkv, d, H_I, d_I, K, q_offset.data_ptr(), kv_len.data_ptr(),
-                 block)
+                 block, sets)
     g._keep = (q_offset, kv_len)
     return g
 
@@ -228,24 +228,34 @@ def topk_select(scores, K, q_offset, kv_len, idx=None, sel_scores=None, want_sco
 def sparse_attn_fwd(q, k, v, idx, gate, scale, kv_len, q_offset=None, out=None, lse=None,
                     want_lse=False, workspace=None, stream=None, mix=None):
     """Gated attention over the listed positions: out bf16 [B,Tq,Hq,d] (and lse).
-    With ``mix`` (bf16, the shape of q) the gate mixes: s*o + (1-s)*mix."""
+    idx int32 [B,Tq,K] (one index set per row) or [B,Hkv,Tq,K] (one per key/value
+    head). With ``mix`` (bf16, the shape of q) the gate mixes: s*o + (1-s)*mix."""
     import torch
     _dev(q, torch.bfloat16, "q", 4)
     _dev(k, torch.bfloat16, "k", 4)
     _dev(v, torch.bfloat16, "v", 4)
-    _dev(idx, torch.int32, "idx", 3)
+    sets = 1
+    if idx is not None and idx.dim() == 4:
+        sets = idx.shape[1]
+        _dev(idx, torch.int32, "idx", 4)
+        if idx.shape[0] != q.shape[0] or idx.shape[2] != q.shape[1] or sets != k.shape[2]:
+            raise ValueError("per-head index rows must be [B,Hkv,Tq,K]")
+        idx3 = idx.view(idx.shape[0], sets * idx.shape[2], idx.shape[3])
+    else:
+        _dev(idx, torch.int32, "idx", 3)
+        idx3 = idx
     _dev(gate, torch.bfloat16, "gate", 4)
     _dev(mix, torch.bfloat16, "mix", 4)
     B, Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, Tk, Hkv, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k, v must be [B,Tk,Hkv,d]")
-    if idx.shape[:2] != (B, Tq):
+    if sets == 1 and idx.shape[:2] != (B, Tq):
         raise ValueError("idx must be [B,Tq,K]")
     _gate_args(q, gate, mix)
     if q_offset is None:
         q_offset = torch.zeros(B, dtype=torch.int32, device=q.device)
-    g = make_geom(B, Tq, Tk, idx.shape[2], q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d)
+    g = make_geom(B, Tq, Tk, idx3.shape[2], q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d, sets=sets)
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
@@ -270,7 +280,7 @@ def _gate_args(q, gate, mix):
 
 
 def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset, kv_len, K,
-           out, lse, idx_out, want_lse, want_idx, workspace, stream, block=1):
+           out, lse, idx_out, want_lse, want_idx, workspace, stream, block=1, sets=1):
     import torch
     _dev(q_idx, torch.int8, "q_idx", 4)
     _dev(k_idx, torch.int8, "k_idx", 3)
@@ -290,16 +300,17 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset,
     _gate_args(q, gate, mix)
     wsb, wsq = _w_strides(w, B, Tq, H_I)
     g = make_geom(B, Tq, Tk, K, q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d, H_I=H_I, d_I=d_I,
-                  block=block)
+                  block=block, sets=sets)
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
     if want_idx and idx_out is None:
-        idx_out = torch.empty((B, Tq, K * max(block, 1)), dtype=torch.int32, device=q.device)
+        shape = (B, Tq, K * max(block, 1)) if sets <= 1 else (B, sets, Tq, K * max(block, 1))
+        idx_out = torch.empty(shape, dtype=torch.int32, device=q.device)
     _dev(out, torch.bfloat16, "out", 4)
     _dev(lse, torch.float32, "lse", 3)
-    _dev(idx_out, torch.int32, "idx_out", 3)
+    _dev(idx_out, torch.int32, "idx_out", 3 if sets <= 1 else 4)
     ws, nb = _workspace(entry, g, workspace, q.device)
     lib = load_library()
     _check(getattr(lib, fn_name)(ctypes.byref(g), _ptr(q_idx), _ptr(k_idx), _ptr(w), wsb, wsq,
@@ -316,23 +327,24 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset,
 
 def prefill_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None, lse=None,
                 idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None,
-                mix=None, block=1):
+                mix=None, block=1, sets=1):
     """Fused layer for many query rows: returns out (and idx, lse when asked).
     ``mix`` as in ``sparse_attn_fwd``; with block > 1 the selection keeps K blocks
-    of `block` positions and idx rows hold K*block positions."""
+    of `block` positions and idx rows hold K*block positions; with sets = Hkv
+    every key/value head has its own index set (idx [B,Hkv,Tq,K*block])."""
     return _fused("lci_prefill_fwd", ENTRY_PREFILL, q_idx, k_idx, w, q, k, v, gate, mix, scale,
                   q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream,
-                  block)
+                  block, sets)
 
 
 def decode_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None, lse=None,
                idx_out=None, want_lse=False, want_idx=False, workspace=None, stream=None,
-               mix=None, block=1):
+               mix=None, block=1, sets=1):
     """Fused layer for one query row per sequence (Tq == 1) over a long history.
-    ``mix`` and ``block`` as in ``prefill_fwd``."""
+    ``mix``, ``block`` and ``sets`` as in ``prefill_fwd``."""
     return _fused("lci_decode_fwd", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, mix, scale,
                   q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream,
-                  block)
+                  block, sets)
 
 
 def kv_append(k_new, v_new, kI_new, k_cache, v_cache, kI_cache, kv_len, n_new=None,

@@ -51,13 +51,14 @@ namespace lci {
 // ------------------------------------------------------------------ masks
 
 __global__ __launch_bounds__(256) void idx_mask_kernel(
-    int Tq, int Tk, int K, const int32_t* __restrict__ q_offset,
+    int Tq, int Tk, int K, int sets, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ idx, int lim, int Wm,
     uint32_t* __restrict__ mask, uint8_t* __restrict__ flag) {
   __shared__ uint32_t bits[kDenseMaxWords];
   __shared__ uint32_t red[8];
+  // rows [B][sets][Tq], like the index rows
   const int64_t row = blockIdx.x;
-  const int b = static_cast<int>(row / Tq);
+  const int b = static_cast<int>(row / (static_cast<int64_t>(sets) * Tq));
   const int i = static_cast<int>(row % Tq);
   const int kvl = kv_len[b];
   const int64_t p = static_cast<int64_t>(q_offset[b]) + i;
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     const uint16_t* __restrict__ gate, const uint16_t* __restrict__ mix,
     const uint32_t* __restrict__ mask, int Wm,
     const uint8_t* __restrict__ flag, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, uint8_t* __restrict__ done, int nbps, int nblk) {
+    float* __restrict__ lse, uint8_t* __restrict__ done, int nbps, int nblk, int sets) {
   using C = DenseCfg<D, G>;
   // two K and two V tile buffers (see the pipeline below)
   __shared__ __align__(16) uint16_t ks[2][C::BK * C::KP];
@@ -198,14 +199,18 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   const int tb = nbps - 1 - blk % nbps;  // longest causal range first
   const int i0 = tb * C::BQ;
   const int iend = min(i0 + C::BQ, Tq);
+  // masks, flags and done bytes are per index set ([B][sets][...]): with one
+  // set per key/value head this workgroup reads those of its head g
+  const int sg = sets > 1 ? g : 0;
+  const int64_t srow = (static_cast<int64_t>(b) * sets + sg) * Tq;  // row 0 of this set
 
   // the whole token block must be on this path
   int ok = 1;
   if (threadIdx.x < C::BQ && i0 + static_cast<int>(threadIdx.x) < Tq)
-    ok = flag[static_cast<int64_t>(b) * Tq + i0 + threadIdx.x] != 0;
+    ok = flag[srow + i0 + threadIdx.x] != 0;
   const int all_ok = __syncthreads_and(ok);
   // the gather kernel skips the token blocks this kernel takes
-  if (threadIdx.x == 0) done[static_cast<int64_t>(b) * nbps + tb] = all_ok ? 1 : 0;
+  if (threadIdx.x == 0) done[(static_cast<int64_t>(b) * sets + sg) * nbps + tb] = all_ok ? 1 : 0;
   if (all_ok == 0) return;
 
   const int qo = q_offset[b];
@@ -224,8 +229,8 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   const int h = g * G + r % G;
   const bool rv = i < Tq;
   const int64_t qrow = static_cast<int64_t>(b) * Tq + (rv ? i : 0);
-  const int fl = rv ? flag[qrow] : 0;
-  const uint32_t* mrow = mask + qrow * Wm;
+  const int fl = rv ? flag[srow + i] : 0;
+  const uint32_t* mrow = mask + (srow + (rv ? i : 0)) * Wm;
   // every row of this wave keeps all of 0..p (flag 2): tiles entirely at or
   // below the wave's first position need no mask at all
   const int iw0 = i0 + wv * C::TW;
@@ -504,15 +509,15 @@ int dense_mask_words(const Geom& g) {
 }
 
 // [mask: rows x Wm words][flag: rows bytes][done: one byte per token block
-// (at most one block per row)], each part 256-byte aligned
+// (at most one block per row)], each part 256-byte aligned; rows = B x sets x Tq
 size_t dense_workspace(const Geom& g) {
-  const size_t rows = static_cast<size_t>(g.B) * g.Tq;
+  const size_t rows = static_cast<size_t>(g.B) * g.sets * g.Tq;
   const size_t mbytes = (rows * dense_mask_words(g) * sizeof(uint32_t) + 255) & ~size_t(255);
   return mbytes + 2 * ((rows + 255) & ~size_t(255));
 }
 
 DenseMasks dense_masks(const Geom& g, void* ws) {
-  const size_t rows = static_cast<size_t>(g.B) * g.Tq;
+  const size_t rows = static_cast<size_t>(g.B) * g.sets * g.Tq;
   DenseMasks d;
   d.Wm = dense_mask_words(g);
   d.lim = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
@@ -540,7 +545,7 @@ static hipError_t launch_dense_k(const Geom& g, const uint16_t* q, const uint16_
     hipLaunchKernelGGL((attn_dense_kernel<D, G, EXACT_L, MIX>), dim3(static_cast<uint32_t>(nwg)),
                        dim3(256), 0, st,
                        g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, gate, mix, dm.mask,
-                       dm.Wm, dm.flag, scale * LOG2E, out, lse, dm.done, nbps, nblk);
+                       dm.Wm, dm.flag, scale * LOG2E, out, lse, dm.done, nbps, nblk, g.sets);
   }
   return hipGetLastError();
 }
@@ -579,11 +584,12 @@ hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k
                              float scale, uint16_t* out, float* lse, void* ws, bool masks_ready,
                              hipStream_t st) {
   const DenseMasks dm = dense_masks(g, ws);
-  const size_t rows = static_cast<size_t>(g.B) * g.Tq;
+  const size_t rows = static_cast<size_t>(g.B) * g.sets * g.Tq;
   if (!masks_ready) {
     KernelTimer timer(LCI_KERNEL_IDX_MASK, st);
     hipLaunchKernelGGL(idx_mask_kernel, dim3(static_cast<uint32_t>(rows)), dim3(256), 0, st, g.Tq,
-                       g.Tk, g.K, g.q_offset, g.kv_len, idx, dm.lim, dm.Wm, dm.mask, dm.flag);
+                       g.Tk, g.K, g.sets, g.q_offset, g.kv_len, idx, dm.lim, dm.Wm, dm.mask,
+                       dm.flag);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

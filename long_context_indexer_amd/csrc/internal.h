@@ -27,6 +27,7 @@ struct Geom {
   const int32_t* q_offset;
   const int32_t* kv_len;
   int block;  // selection granularity: 1 = single positions, else blocks of this many
+  int sets;   // index sets per query row: 1, or Hkv (index rows [B][sets][Tq][K])
 };
 
 // ---- indexer scoring
@@ -92,6 +93,12 @@ constexpr int kBlockTopkMaxKeep = 2048;    // K at most (K*block <= 4096, block 
 hipError_t launch_block_topk(const Geom& g, const int32_t* scores, int64_t score_row_stride,
                              int row_begin, int row_count, int32_t* idx, int32_t* sel,
                              const DenseMasks* dm, hipStream_t stream);
+
+// ---- index sets per key/value head: q_idx [B,Tq,H_I,d_I] regrouped into
+// [sets][B][Tq][H_I/sets][d_I], so each set's indexer heads form a contiguous
+// query array for the scoring kernels
+hipError_t launch_regroup_q_idx(const Geom& g, const int8_t* q_idx, int8_t* out,
+                                hipStream_t stream);
 
 // ---- appending rows to the key / value / indexer-key caches
 // Sizes from g: B, Tq (= rows of the new tensors per sequence), Tk (capacity),

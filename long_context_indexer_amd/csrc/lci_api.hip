@@ -29,6 +29,20 @@ constexpr int kMaxK = 4096;
 // Positions per selected unit: 1, or the block size of block-granular selection.
 int sel_block(const lci_geom* g) { return g->block > 1 ? g->block : 1; }
 
+// Index sets per query row: 1 (shared by every head), or Hkv.
+int sel_sets(const lci_geom* g) { return g->sets > 1 ? g->sets : 1; }
+
+// Index sets: 1, or one per key/value head; the indexer heads split evenly.
+// `indexer`: the entry also scores (its indexer heads must split into the sets).
+lci_status check_sets(const lci_geom* g, bool indexer) {
+  if (g->sets < 0) return LCI_ERR_SHAPE;
+  const int ns = sel_sets(g);
+  if (ns == 1) return LCI_OK;
+  if (ns != g->Hkv) return LCI_ERR_SHAPE;
+  if (indexer && (g->H_I % ns != 0 || g->H_I < ns)) return LCI_ERR_SHAPE;
+  return LCI_OK;
+}
+
 // Sizes common to every entry.
 lci_status check_base(const lci_geom* g) {
   if (!g) return LCI_ERR_NULL;
@@ -69,7 +83,7 @@ bool scale_ok(float scale) { return scale > 0.f && scale < INFINITY; }
 
 Geom to_geom(const lci_geom* g) {
   return Geom{g->B, g->Tq, g->Tk, g->Hq, g->Hkv, g->d, g->H_I, g->d_I, g->K, g->q_offset,
-              g->kv_len, sel_block(g)};
+              g->kv_len, sel_block(g), sel_sets(g)};
 }
 
 // The attention kernels' view: index rows of K*block positions.
@@ -97,7 +111,8 @@ int prefill_chunk_rows(const lci_geom* g) {
 }
 
 struct PrefillLayout {
-  size_t idx_off, idx_bytes, score_off, score_bytes, attn_off, attn_bytes, total;
+  size_t idx_off, idx_bytes, score_off, score_bytes, attn_off, attn_bytes, qg_off, qg_bytes,
+      total;
   int chunk_rows, splits;
 };
 
@@ -107,12 +122,17 @@ PrefillLayout prefill_layout(const lci_geom* g) {
   L.chunk_rows = prefill_chunk_rows(g);
   L.splits = lci::sparse_attn_pick_splits(gg);
   L.idx_off = 0;
-  L.idx_bytes = align_up(static_cast<size_t>(g->B) * g->Tq * gg.K * sizeof(int32_t));
+  L.idx_bytes =
+      align_up(static_cast<size_t>(g->B) * sel_sets(g) * g->Tq * gg.K * sizeof(int32_t));
   L.score_off = L.idx_off + L.idx_bytes;
   L.score_bytes = align_up(static_cast<size_t>(g->B) * L.chunk_rows * g->Tk * sizeof(int32_t));
   L.attn_off = L.score_off + L.score_bytes;
   L.attn_bytes = align_up(lci::sparse_attn_workspace(gg, L.splits));
-  L.total = L.attn_off + L.attn_bytes;
+  // the query rows regrouped by index set
+  L.qg_off = L.attn_off + L.attn_bytes;
+  L.qg_bytes =
+      sel_sets(g) > 1 ? align_up(static_cast<size_t>(g->B) * g->Tq * g->H_I * g->d_I) : 0;
+  L.total = L.qg_off + L.qg_bytes;
   return L;
 }
 
@@ -145,17 +165,21 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
     case LCI_ENTRY_TOPK_SELECT:
       return 0;
     case LCI_ENTRY_SPARSE_ATTN: {
-      if (check_attention(g) != LCI_OK) return 0;
+      if (check_attention(g) != LCI_OK || check_sets(g, false) != LCI_OK) return 0;
       const Geom gg = attn_geom(g);
       return lci::sparse_attn_workspace(gg, lci::sparse_attn_pick_splits(gg));
     }
     case LCI_ENTRY_PREFILL:
-      if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK) return 0;
+      if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK ||
+          check_sets(g, true) != LCI_OK)
+        return 0;
       return prefill_layout(g).total;
     case LCI_ENTRY_DECODE:
-      if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK || g->Tq != 1) return 0;
-      // block-granular decode runs the prefill path on its one row
-      if (sel_block(g) > 1) return prefill_layout(g).total;
+      if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK || g->Tq != 1 ||
+          check_sets(g, true) != LCI_OK)
+        return 0;
+      // block-granular or per-head-set decode runs the prefill path on its one row
+      if (sel_block(g) > 1 || sel_sets(g) > 1) return prefill_layout(g).total;
       return lci::decode_layout(to_geom(g)).total;
     default:
       return 0;
@@ -168,6 +192,8 @@ lci_status lci_idx_score(const lci_geom* g, const int8_t* q_idx, const int8_t* k
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if ((s = check_indexer(g)) != LCI_OK) return s;
+  if (g->sets < 0) return LCI_ERR_SHAPE;
+  if (sel_sets(g) > 1) return LCI_ERR_UNSUPPORTED;
   if (!q_idx || !k_idx || !w || !scores) return LCI_ERR_NULL;
   if (w_stride_b < 0 || w_stride_q < 0) return LCI_ERR_SHAPE;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(scores)) return LCI_ERR_ALIGN;
@@ -183,6 +209,8 @@ lci_status lci_topk_select(const lci_geom* g, const int32_t* scores, int32_t* id
   (void)ws_bytes;
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
+  if (g->sets < 0) return LCI_ERR_SHAPE;
+  if (sel_sets(g) > 1) return LCI_ERR_UNSUPPORTED;
   if (!scores || !idx) return LCI_ERR_NULL;
   if (!aligned4(scores) || !aligned4(idx) || (sel_scores && !aligned4(sel_scores)))
     return LCI_ERR_ALIGN;
@@ -201,6 +229,7 @@ lci_status lci_sparse_attn_fwd(const lci_geom* g, const lci_bf16* q, const lci_b
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
+  if ((s = check_sets(g, false)) != LCI_OK) return s;
   if (!q || !k || !v || !idx || !out || (mix && !gate)) return LCI_ERR_NULL;
   if (!scale_ok(softmax_scale)) return LCI_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
@@ -227,6 +256,7 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   if (s != LCI_OK) return s;
   if ((s = check_indexer(g)) != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
+  if ((s = check_sets(g, true)) != LCI_OK) return s;
   if (!q_idx || !k_idx || !w || !q || !k || !v || !out || (mix && !gate)) return LCI_ERR_NULL;
   if (wsb < 0 || wsq < 0 || !scale_ok(scale)) return LCI_ERR_SHAPE;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(k) ||
@@ -247,14 +277,42 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   // for rows short enough for its one-wave form
   const bool masks = L.splits == 1 && (gg.block > 1 || g->Tk <= lci::kWaveTopkMax);
   const lci::DenseMasks dm = masks ? lci::dense_masks(ga, ws + L.attn_off) : lci::DenseMasks{};
+  // index sets per key/value head: set g is scored as an indexer of H_I/sets
+  // heads (its rows of the regrouped query array, its weights) and its index
+  // rows go to [B][sets][Tq][K*block] (the selection kernels address rows as
+  // b*Tq' + row, so Tq' = sets*Tq and an offset of g*Tq rows place them)
+  Geom gs = gg;
+  gs.H_I = g->H_I / gg.sets;
+  Geom gsel = gg;
+  gsel.Tq = g->Tq * gg.sets;
+  const int8_t* qsrc = q_idx;
+  if (gg.sets > 1) {
+    int8_t* qg = reinterpret_cast<int8_t*>(ws + L.qg_off);
+    hipError_t e = lci::launch_regroup_q_idx(gg, q_idx, qg, st);
+    if (e != hipSuccess) return hip_status(e);
+    qsrc = qg;
+  }
+  const size_t qset = static_cast<size_t>(g->B) * g->Tq * gs.H_I * g->d_I;
   for (int r0 = 0; r0 < g->Tq; r0 += L.chunk_rows) {
     const int rc = std::min(L.chunk_rows, g->Tq - r0);
-    hipError_t e = lci::launch_idx_score(gg, q_idx, k_idx, w, wsb, wsq, sc, g->Tk, r0, rc, st);
-    if (e != hipSuccess) return hip_status(e);
-    e = gg.block > 1
-            ? lci::launch_block_topk(gg, sc, g->Tk, r0, rc, idx, nullptr, masks ? &dm : nullptr, st)
-            : lci::launch_topk_rows(gg, sc, g->Tk, r0, rc, idx, nullptr, masks ? &dm : nullptr, st);
-    if (e != hipSuccess) return hip_status(e);
+    for (int set = 0; set < gg.sets; ++set) {
+      hipError_t e = lci::launch_idx_score(gs, qsrc + set * qset, k_idx, w + set * gs.H_I, wsb,
+                                           wsq, sc, g->Tk, r0, rc, st);
+      if (e != hipSuccess) return hip_status(e);
+      int32_t* iset = idx + static_cast<size_t>(set) * g->Tq * ga.K;
+      // this set's masks and flags: rows [B][sets][Tq] like the index rows
+      lci::DenseMasks dms = dm;
+      if (masks) {
+        dms.mask += static_cast<size_t>(set) * g->Tq * dm.Wm;
+        dms.flag += static_cast<size_t>(set) * g->Tq;
+      }
+      e = gg.block > 1
+              ? lci::launch_block_topk(gsel, sc, g->Tk, r0, rc, iset, nullptr,
+                                       masks ? &dms : nullptr, st)
+              : lci::launch_topk_rows(gsel, sc, g->Tk, r0, rc, iset, nullptr,
+                                      masks ? &dms : nullptr, st);
+      if (e != hipSuccess) return hip_status(e);
+    }
   }
   return hip_status(lci::launch_sparse_attn(ga, q, k, v, idx, gate, mix, scale, out, lse,
                                             L.splits, ws + L.attn_off, masks, st));
@@ -279,9 +337,10 @@ lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* 
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if (g->Tq != 1) return LCI_ERR_SHAPE;
-  // block-granular selection: the prefill path on the one row (its selection
-  // works on at most kBlockTopkMaxBlocks blocks, which bounds the history)
-  if (sel_block(g) > 1)
+  // block-granular selection or index sets per key/value head: the prefill path
+  // on the one row (block selection works on at most kBlockTopkMaxBlocks
+  // blocks, which bounds the history)
+  if (sel_block(g) > 1 || sel_sets(g) > 1)
     return fused_forward(g, q_idx, k_idx, w, w_stride_b, w_stride_q, q, k, v, gate, mix,
                          softmax_scale, out, lse, idx_out, workspace, ws_bytes, stream);
   if ((s = check_indexer(g)) != LCI_OK) return s;

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
     const uint16_t* __restrict__ gate, const uint16_t* __restrict__ mix, float scale_log2,
     uint16_t* __restrict__ out,
     float* __restrict__ lse, int splits, int per_split, float* __restrict__ part,
-    const uint8_t* __restrict__ done, int dbq, int64_t nitems) {
+    const uint8_t* __restrict__ done, int dbq, int64_t nitems, int sets) {
   using C = AttnCfg<D>;
   // [Hkv][16][PITCH]; 16-byte aligned wherever the dynamic LDS region starts:
   // its 8-byte writes and transposed reads need aligned rows
@@ -127,16 +127,20 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(
   const int64_t qrow = item / splits;
   const int b = static_cast<int>(qrow / Tq);
   if (done) {
-    // token blocks the tile kernel took are finished already
+    // token blocks the tile kernel took (for this wave's index set) are finished
     const int i = static_cast<int>(qrow % Tq);
     const int nbps = (Tq + dbq - 1) / dbq;
-    if (done[static_cast<int64_t>(b) * nbps + i / dbq]) return;
+    const int sg = sets > 1 ? static_cast<int>(threadIdx.x >> 6) : 0;
+    if (done[(static_cast<int64_t>(b) * sets + sg) * nbps + i / dbq]) return;
   }
   const int kvl0 = kv_len[b];
   const int kvl = kvl0 <= Tk ? kvl0 : 0;  // a history longer than its allocation: no entry is read
   const int e_begin = split * per_split;
   const int nent = max(0, min(per_split, K - e_begin));
-  const int32_t* ip = idx + qrow * K + e_begin;
+  // index rows [B][sets][Tq][K]: with one set per key/value head, wave g reads
+  // the row of its own head
+  const int64_t irow = sets > 1 ? qrow + (static_cast<int64_t>(b) * (sets - 1) + g) * Tq : qrow;
+  const int32_t* ip = idx + irow * K + e_begin;
   uint16_t* vs = vstage + g * 16 * C::PITCH;
 
   const int hl = lane & 15;     // this lane's query-head column
@@ -378,7 +382,7 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
     hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * g.Hkv), lds, st, g.Tq, g.Tk, g.K,
                        g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, mix, scale * LOG2E, out, lse,
                        splits, per_split, static_cast<float*>(ws), done, dense_block_rows(G),
-                       nitems);
+                       nitems, g.sets);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;

@@ -52,11 +52,11 @@ def test_abi_version_and_status_strings(lib):
 
 def geom(**kw):
     base = dict(B=1, Tq=16, Tk=64, Hq=8, Hkv=2, d=128, H_I=8, d_I=64, K=8,
-                q_offset=FAKE, kv_len=FAKE, block=0)
+                q_offset=FAKE, kv_len=FAKE, block=0, sets=0)
     base.update(kw)
     return lci.lci_geom(base["B"], base["Tq"], base["Tk"], base["Hq"], base["Hkv"], base["d"],
                         base["H_I"], base["d_I"], base["K"], base["q_offset"], base["kv_len"],
-                        base["block"])
+                        base["block"], base["sets"])
 
 
 def score(lib, g, q=FAKE, k=FAKE, w=FAKE, out=FAKE, wsb=0, wsq=0):
@@ -128,6 +128,20 @@ def test_block_granularity_limits(lib):
     assert lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g)) >= 16 * 4096 * 4
     gd = geom(Tq=1, block=64, K=32, Tk=1 << 17)
     assert lib.lci_workspace_bytes(lci.ENTRY_DECODE, ctypes.byref(gd)) > 0
+
+
+def test_index_set_limits(lib):
+    # one index set per key/value head: sets = Hkv, indexer heads split evenly
+    assert attn(lib, geom(sets=-1)) == SHAPE
+    assert attn(lib, geom(sets=3)) == SHAPE                   # Hkv = 2
+    assert fused(lib, geom(sets=2, H_I=1, d_I=64)) == SHAPE   # 1 indexer head for 2 sets
+    assert score(lib, geom(sets=2)) == UNSUP                  # scores of one set only
+    assert lib.lci_topk_select(ctypes.byref(geom(sets=2)), FAKE, FAKE, None, None, 0,
+                               None) == UNSUP
+    g = geom(sets=2, Tk=4096, K=64)
+    need = lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g))
+    assert need >= 2 * 16 * 64 * 4 + 16 * 8 * 64         # index rows of both sets + queries
+    assert fused(lib, g, nb=need - 1) == WS
 
 
 def test_softmax_scale_must_be_positive(lib):
