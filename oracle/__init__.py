@@ -66,6 +66,8 @@ def open_library(path: str):
                                    i64, i64, P, P, P, P, P, f64, i64, P, P, P, P, P, P]
     lib.orc_layer_rows.restype = i32
     lib.orc_kv_append.argtypes = [i32, i32, i32, i64, P, P, P, P, P, P]
+    lib.orc_attn_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64,
+                                 P, P, P, P, P]
     lib.orc_num_threads.restype = i32
     return lib
 
@@ -198,6 +200,30 @@ class Oracle:
                                     _p(blk), _p(sel))
         return idx, blk, sel
 
+    def attention_bwd(self, q, k, v, gate, idx, kv_len, scale, dy, mix=None):
+        """Gradients of the gated attention over index rows idx int32 [B,Tq,K] (one
+        set) for the output gradient dy uint16 [B,Tq,Hq,d]. q, gate, mix, dy bf16 bits
+        [B,Tq,Hq,d]; k, v [B,Tk,Hkv,d]. Returns dict(dq, dgate, dmix [B,Tq,Hq,d];
+        dk, dv [B,Tk,Hkv,d]) in float64 (dgate / dmix None without gate / mix)."""
+        q, k, v, dy = (_c(a, np.uint16) for a in (q, k, v, dy))
+        B, Tq, Hq, d = q.shape
+        Tk, Hkv = k.shape[1], k.shape[2]
+        gate = None if gate is None else _c(gate, np.uint16)
+        mix = None if mix is None else _c(mix, np.uint16)
+        if mix is not None and gate is None:
+            raise ValueError("mix needs a gate")
+        idx = _c(idx, np.int32).reshape(B, Tq, -1)
+        K = idx.shape[2]
+        dq = np.empty((B, Tq, Hq, d), np.float64)
+        dk = np.empty((B, Tk, Hkv, d), np.float64)
+        dv = np.empty((B, Tk, Hkv, d), np.float64)
+        dg = np.empty((B, Tq, Hq, d), np.float64) if gate is not None else None
+        dm = np.empty((B, Tq, Hq, d), np.float64) if mix is not None else None
+        self.lib.orc_attn_bwd(B, Tq, Tk, Hq, Hkv, d, K, _p(_c(kv_len, np.int32)), _p(q), _p(k),
+                              _p(v), _p(gate), _p(mix), _p(idx), _p(dy), float(scale), _p(dq),
+                              _p(dk), _p(dv), _p(dg), _p(dm))
+        return dict(dq=dq, dk=dk, dv=dv, dgate=dg, dmix=dm)
+
     def layer(self, inp, K, rows=None, gated=True, block=1, sets=1):
         """The whole layer (score -> Top-K -> attention -> gate) for the listed rows
         of an input dict as produced by ``synth.host_inputs``; an entry "mix" (the
@@ -302,6 +328,10 @@ def layer(*a, **k):
 
 def block_topk(*a, **k):
     return default().block_topk(*a, **k)
+
+
+def attention_bwd(*a, **k):
+    return default().attention_bwd(*a, **k)
 
 
 def kv_append(*a, **k):

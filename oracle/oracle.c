@@ -33,6 +33,8 @@
  *            output): y = o * sigmoid(G), elementwise per head and feature; or,
  *            mixed with the other branch's output x (step 4 and its pseudocode),
  *            y = sigmoid(G) * o + (1 - sigmoid(G)) * x.
+ *   backward the gradients of attention and gate (orc_attn_bwd), by the chain
+ *            rule on the definitions above.
  *   append   same page, section "Engineering and Evaluation Recommendations"
  *            (chunked prefill that reuses the cached scorer inputs): the new
  *            rows' keys, values and indexer keys go into the caches right after
@@ -387,6 +389,109 @@ void orc_kv_append(int B, int Tn, int Tk, int64_t row_bytes, const uint8_t *src,
         if (q_offset_out) q_offset_out[b] = (int32_t)old;
         if (kv_len_out) kv_len_out[b] = (int32_t)(old + n < Tk ? old + n : Tk);
     }
+}
+
+/* Gradients of the gated sparse attention (the training direction of the
+ * layer: "Hybrid Sparse Attention for Long-Context LLMs", section "Engineering
+ * and Evaluation Recommendations", training side; the scorer, trained by
+ * distillation, is not differentiated here). For the forward of orc_attn_row
+ * (one index set) and an output gradient dy, by the chain rule on
+ *   l_t = scale q.k[s_t],  P = softmax(l),  o = sum_t P_t v[s_t],
+ *   y = s*o + (1 - s)*x,   s = sigmoid(G)   (s = 1 and no x when ungated):
+ *   do = s*dy;  dG = dy*(o - x)*s*(1 - s);  dx = (1 - s)*dy;
+ *   dP_t = do.v[s_t];  dl_t = P_t*(dP_t - sum_u P_u dP_u);
+ *   dq = scale * sum_t dl_t k[s_t];  dk[s_t] += scale*dl_t*q;  dv[s_t] += P_t*do,
+ * summed over the query heads that share a key/value head and over every
+ * occurrence of a position in an index row. Rows B x Tq with idx [B][Tq][K];
+ * entries outside 0..kv_len-1 are skipped. All outputs are overwritten (fp64):
+ * dq, dgate, dmix [B][Tq][Hq][d] (dgate, dmix nullable; used only with gate /
+ * mix), dk, dv [B][Tk][Hkv][d]. */
+void orc_attn_bwd(int B, int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t *kv_len,
+                  const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gate,
+                  const uint16_t *mix, const int32_t *idx, const uint16_t *dy, double scale,
+                  double *dq, double *dk, double *dv, double *dgate, double *dmix)
+{
+    int G = Hq / Hkv;
+    memset(dk, 0, (size_t)B * Tk * Hkv * d * sizeof(double));
+    memset(dv, 0, (size_t)B * Tk * Hkv * d * sizeof(double));
+    double *P = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    double *dP = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    double *o = (double *)malloc((size_t)d * sizeof(double));
+    double *dO = (double *)malloc((size_t)d * sizeof(double));
+    for (int b = 0; b < B; ++b) {
+        int64_t kvl = kv_len[b] < Tk ? kv_len[b] : Tk;
+        const uint16_t *kb = k + (int64_t)b * Tk * Hkv * d, *vb = v + (int64_t)b * Tk * Hkv * d;
+        for (int i = 0; i < Tq; ++i) {
+            int64_t row = (int64_t)b * Tq + i;
+            const int32_t *ir = idx + row * K;
+            for (int h = 0; h < Hq; ++h) {
+                int g = h / G;
+                int64_t hb = (row * Hq + h) * d;
+                /* softmax weights over the valid entries */
+                double m = -INFINITY;
+                for (int t = 0; t < K; ++t) {
+                    int64_t st = ir[t];
+                    if (st < 0 || st >= kvl) { P[t] = -INFINITY; continue; }
+                    double dot = 0.0;
+                    for (int j = 0; j < d; ++j)
+                        dot += orc_bf16(q[hb + j]) * orc_bf16(kb[(st * Hkv + g) * d + j]);
+                    P[t] = scale * dot;
+                    if (P[t] > m) m = P[t];
+                }
+                double Z = 0.0;
+                for (int t = 0; t < K; ++t) {
+                    P[t] = (m == -INFINITY || P[t] == -INFINITY) ? 0.0 : exp(P[t] - m);
+                    Z += P[t];
+                }
+                for (int t = 0; t < K; ++t) if (Z > 0.0) P[t] /= Z;
+                for (int j = 0; j < d; ++j) o[j] = 0.0;
+                for (int t = 0; t < K; ++t) {
+                    if (P[t] == 0.0) continue;
+                    int64_t st = ir[t];
+                    for (int j = 0; j < d; ++j) o[j] += P[t] * orc_bf16(vb[(st * Hkv + g) * d + j]);
+                }
+                /* the gate */
+                for (int j = 0; j < d; ++j) {
+                    double gy = orc_bf16(dy[hb + j]);
+                    if (gate) {
+                        double sg = 1.0 / (1.0 + exp(-orc_bf16(gate[hb + j])));
+                        double x = mix ? orc_bf16(mix[hb + j]) : 0.0;
+                        dO[j] = sg * gy;
+                        if (dgate) dgate[hb + j] = gy * (o[j] - x) * sg * (1.0 - sg);
+                        if (dmix && mix) dmix[hb + j] = (1.0 - sg) * gy;
+                    } else {
+                        dO[j] = gy;
+                    }
+                }
+                /* the softmax */
+                double delta = 0.0;
+                for (int t = 0; t < K; ++t) {
+                    dP[t] = 0.0;
+                    int64_t st = ir[t];
+                    if (st < 0 || st >= kvl) continue;
+                    for (int j = 0; j < d; ++j) dP[t] += dO[j] * orc_bf16(vb[(st * Hkv + g) * d + j]);
+                    delta += P[t] * dP[t];
+                }
+                for (int j = 0; j < d; ++j) dq[hb + j] = 0.0;
+                for (int t = 0; t < K; ++t) {
+                    int64_t st = ir[t];
+                    if (st < 0 || st >= kvl) continue;
+                    double dl = P[t] * (dP[t] - delta);
+                    double *dkr = dk + (((int64_t)b * Tk + st) * Hkv + g) * d;
+                    double *dvr = dv + (((int64_t)b * Tk + st) * Hkv + g) * d;
+                    for (int j = 0; j < d; ++j) {
+                        dq[hb + j] += scale * dl * orc_bf16(kb[(st * Hkv + g) * d + j]);
+                        dkr[j] += scale * dl * orc_bf16(q[hb + j]);
+                        dvr[j] += P[t] * dO[j];
+                    }
+                }
+            }
+        }
+    }
+    free(dO);
+    free(o);
+    free(dP);
+    free(P);
 }
 
 int orc_num_threads(void)

@@ -688,4 +688,112 @@ def pin_sets_per_kv_head(orc):
     assert np.array_equal(res["out"], shared["out"])
 
 
+# ------------------------------------------------------------------ backward
+
+def _torch_sparse_forward(q, k, v, G, x, idx, kv_len, scale):
+    """The gated sparse attention written with torch ops on float64 tensors (an
+    independent statement of the forward, for autograd)."""
+    import torch
+    B, Tq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    it = torch.from_numpy(idx.astype(np.int64))                       # [B,Tq,K]
+    valid = (it >= 0) & (it < torch.from_numpy(kv_len.astype(np.int64))[:, None, None])
+    safe = torch.where(valid, it, torch.zeros_like(it))
+    bi = torch.arange(B)[:, None, None]
+    ks = k[bi, safe].repeat_interleave(Hq // Hkv, dim=3)             # [B,Tq,K,Hq,d]
+    vs = v[bi, safe].repeat_interleave(Hq // Hkv, dim=3)
+    logits = (ks * q[:, :, None]).sum(-1) * scale                      # [B,Tq,K,Hq]
+    logits = logits.masked_fill(~valid[..., None], float("-inf"))
+    any_valid = valid.any(-1)[..., None, None]                         # [B,Tq,1,1]
+    P = torch.softmax(torch.where(any_valid, logits, torch.zeros_like(logits)), dim=2)
+    P = torch.where(any_valid & valid[..., None], P, torch.zeros_like(P))
+    o = (P[..., None] * vs).sum(2)                                     # [B,Tq,Hq,d]
+    if G is None:
+        return o
+    s = torch.sigmoid(G)
+    return s * o + (1 - s) * x if x is not None else s * o
+
+
+def _bwd_against_autograd(orc, q, k, v, G, x, idx, kv_len, scale, dy, tol):
+    import torch
+    t = lambda a: torch.from_numpy(bf16_to_f32(a).astype(np.float64)).requires_grad_(True)
+    tq, tk, tv = t(q), t(k), t(v)
+    tg = t(G) if G is not None else None
+    tx = t(x) if x is not None else None
+    y = _torch_sparse_forward(tq, tk, tv, tg, tx, idx, kv_len, scale)
+    (y * torch.from_numpy(bf16_to_f32(dy).astype(np.float64))).sum().backward()
+    res = orc.attention_bwd(q, k, v, G, idx, kv_len, scale, dy, mix=x)
+    pairs = [("dq", tq), ("dk", tk), ("dv", tv)]
+    if G is not None:
+        pairs.append(("dgate", tg))
+    if x is not None:
+        pairs.append(("dmix", tx))
+    for name, leaf in pairs:
+        want = leaf.grad.numpy()
+        assert np.abs(res[name] - want).max() <= tol * max(1.0, np.abs(want).max()), name
+
+
+def pin_bwd_dense_sdpa(orc):
+    """K >= p+1 (every causal position): the gradients equal torch autograd through
+    its SDPA (causal, fp64, GQA by head repetition) with the gate and the mix."""
+    import torch
+    r = np.random.default_rng(50)
+    B, T, Hq, Hkv, d = 2, 20, 4, 2, 16
+    q, k, v = (_rand_bf16(r, (B, T, h, d)) for h in (Hq, Hkv, Hkv))
+    G, x, dy = (_rand_bf16(r, (B, T, Hq, d)) for _ in range(3))
+    scale = 0.35
+    idx = np.full((B, T, T + 2), -1, np.int32)
+    for i in range(T):
+        idx[:, i, :i + 1] = np.arange(i + 1)
+    t = lambda a: torch.from_numpy(bf16_to_f32(a).astype(np.float64)).requires_grad_(True)
+    tq, tk, tv, tg, tx = t(q), t(k), t(v), t(G), t(x)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.transpose(1, 2), tk.repeat_interleave(2, dim=2).transpose(1, 2),
+        tv.repeat_interleave(2, dim=2).transpose(1, 2), is_causal=True, scale=scale).transpose(1, 2)
+    s = torch.sigmoid(tg)
+    y = s * o + (1 - s) * tx
+    (y * torch.from_numpy(bf16_to_f32(dy).astype(np.float64))).sum().backward()
+    res = orc.attention_bwd(q, k, v, G, idx, np.array([T, T]), scale, dy, mix=x)
+    for name, leaf in (("dq", tq), ("dk", tk), ("dv", tv), ("dgate", tg), ("dmix", tx)):
+        assert np.abs(res[name] - leaf.grad.numpy()).max() < 1e-12, name
+
+
+def pin_bwd_sparse_autograd(orc):
+    """Sparse index rows in any order, with -1 padding, a repeated position, a row
+    with no entry and a history shorter than the allocation: the gradients equal
+    torch autograd through an independent torch statement of the forward, gated
+    and mixed, gated only, and ungated."""
+    r = np.random.default_rng(51)
+    B, Tq, Tk, Hq, Hkv, d, K = 2, 5, 30, 4, 1, 8, 9
+    q = _rand_bf16(r, (B, Tq, Hq, d))
+    k, v = (_rand_bf16(r, (B, Tk, Hkv, d)) for _ in range(2))
+    G, x, dy = (_rand_bf16(r, (B, Tq, Hq, d)) for _ in range(3))
+    idx = np.stack([np.stack([r.permutation(Tk)[:K] for _ in range(Tq)]) for _ in range(B)])
+    idx = idx.astype(np.int32)
+    idx[0, 1, 3:] = -1
+    idx[0, 2, 4] = idx[0, 2, 0]            # a repeated position counts twice
+    idx[1, 3, :] = -1                      # no entry at all
+    kv_len = np.array([Tk, 22])            # entries >= 22 of sequence 1 are skipped
+    _bwd_against_autograd(orc, q, k, v, G, x, idx, kv_len, 0.5, dy, 1e-12)
+    _bwd_against_autograd(orc, q, k, v, G, None, idx, kv_len, 0.5, dy, 1e-12)
+    _bwd_against_autograd(orc, q, k, v, None, None, idx, kv_len, 0.5, dy, 1e-12)
+
+
+def pin_bwd_constant_values(orc):
+    """Constant value rows make the output independent of the weights: dq and dk
+    vanish, dv spreads the head's output gradient over the selected rows."""
+    r = np.random.default_rng(52)
+    B, Tq, Tk, Hq, Hkv, d, K = 1, 3, 12, 2, 1, 8, 5
+    q = _rand_bf16(r, (B, Tq, Hq, d))
+    k = _rand_bf16(r, (B, Tk, Hkv, d))
+    v = np.broadcast_to(_rand_bf16(r, (1, 1, 1, d)), (B, Tk, Hkv, d)).copy()
+    dy = _rand_bf16(r, (B, Tq, Hq, d))
+    idx = np.array([[[0, 3, 5, 7, 11], [1, 2, -1, -1, -1], [4, 4, 6, 8, 9]]], np.int32)
+    res = orc.attention_bwd(q, k, v, None, idx, np.array([Tk]), 0.7, dy)
+    assert np.abs(res["dq"]).max() < 1e-14 and np.abs(res["dk"]).max() < 1e-14
+    # dv summed over all rows = sum over rows and heads of dy (softmax weights sum to 1)
+    tot = bf16_to_f32(dy).astype(np.float64).sum(axis=(0, 1, 2))
+    assert np.abs(res["dv"].sum(axis=(0, 1, 2)) - tot).max() < 1e-12
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

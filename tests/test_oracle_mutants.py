@@ -60,6 +60,11 @@ MUTANTS = [
     ("sets_share_group0_weights", "wr + gs * Hg, p + 1, S);", "wr, p + 1, S);"),
     ("heads_read_set0", "const int32_t *ih = idx + (int64_t)(g * sets / Hkv) * K;",
      "const int32_t *ih = idx;"),
+    ("bwd_no_delta", "double dl = P[t] * (dP[t] - delta);", "double dl = P[t] * dP[t];"),
+    ("bwd_gate_derivative", "gy * (o[j] - x) * sg * (1.0 - sg)", "gy * (o[j] - x) * sg * (1.0 + sg)"),
+    ("bwd_dk_unscaled", "dkr[j] += scale * dl * orc_bf16(q[hb + j]);", "dkr[j] += dl * orc_bf16(q[hb + j]);"),
+    ("bwd_dv_ungated", "dvr[j] += P[t] * dO[j];", "dvr[j] += P[t] * orc_bf16(dy[hb + j]);"),
+    ("bwd_dq_from_values", "dq[hb + j] += scale * dl * orc_bf16(kb[", "dq[hb + j] += scale * dl * orc_bf16(vb["),
     ("overflow_unchecked", "if (acc > INT32_MAX) { acc = INT32_MAX; rc = ORC_OVERFLOW; }", ""),
 ]
 
