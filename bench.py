@@ -268,7 +268,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "prefill64k", "decode1m", "blocks",
-                                       "sets"],
+                                       "sets", "backward"],
                     default=None,
                     help="run only one fused step (profiler runs; prefill64k and decode1m are "
                          "the long-context workloads, outside the default run)")
@@ -369,6 +369,44 @@ def main():
                     kernels_us_per_step={k: round(v["ms_per_step"] * 1e3, 2)
                                          for k, v in kern.items()})
 
+    def run_backward(cfg, inp_host):
+        """Gradients of attention + gate for the Prefill-8K index rows (from the
+        fused forward) and a random bf16 output gradient."""
+        torch.cuda.empty_cache()
+        d = {k: dev(v) for k, v in inp_host.items() if isinstance(v, np.ndarray)}
+        _, idx = lci.prefill_fwd(d["q_idx"], d["k_idx"], d["w"], d["q"], d["k"], d["v"],
+                                 d["gate"], cfg.scale, d["q_offset"], d["kv_len"], cfg.K,
+                                 want_idx=True, stream=stream)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(7)
+        dy = torch.randn(d["q"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+        geom = lci.make_geom(cfg.B, cfg.Tq, cfg.Tk, cfg.K, d["q_offset"], d["kv_len"], Hq=cfg.Hq,
+                             Hkv=cfg.Hkv, d=cfg.d)
+        ws = torch.empty(lci.workspace_bytes(lci.ENTRY_SPARSE_ATTN_BWD, geom), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            lci.sparse_attn_bwd(d["q"], d["k"], d["v"], idx, d["gate"], cfg.scale, d["kv_len"],
+                                dy, workspace=ws, stream=stream)
+
+        steps = max(2, args.steps // 4)
+        step()
+        torch.cuda.synchronize()
+        ms_step, ev_ms, kern = timed_region(timer, step, steps, lci)
+        pairs = causal_pairs(cfg)
+        tflops = 10.0 * cfg.d * cfg.Hq * pairs / (ms_step * 1e-3) / 1e12
+        log(f"prefill8k backward: {ms_step:.3f} ms/step, {cfg.Tq / ms_step * 1e3 / 1e6:.2f} M tok/s, "
+            f"{tflops:.1f} TFLOP/s of backward work")
+        for kname, kv in kern.items():
+            log(f"  {kname:12s} {kv['launches_per_step']:.0f} launch(es)/step, "
+                f"{kv['ms_per_step'] * 1e3:8.1f} us/step")
+        return dict(workload="prefill8k", ms_per_step=ms_step, event_ms_per_step=ev_ms,
+                    tok_s=cfg.B * cfg.Tq / (ms_step * 1e-3), steps=steps,
+                    tflops=tflops, note="dq, dk, dv, dgate for the layer's index rows; "
+                    "10*d flops per (query head, selected key); forward recomputed inside",
+                    kernels_us_per_step={k: round(v["ms_per_step"] * 1e3, 2)
+                                         for k, v in kern.items()})
+
     def run_decode(name):
         dcfg = synth.CONFIGS[name]
         dd = synth.device_inputs(dcfg, seed=0)
@@ -442,6 +480,10 @@ def main():
     if args.only in (None, "sets"):
         res["sets"] = run_variant(cfg, inp_host, 1, cfg.K, cfg.Hkv)
 
+    # ------------------------------------------- Prefill 8K gradients (training direction)
+    if args.only in (None, "backward"):
+        res["backward"] = run_backward(cfg, inp_host)
+
     # --------------------------------------------------------------- decode 128K
     if not args.no_decode and args.only in (None, "decode"):
         res["decode"] = run_decode("decode128k")
@@ -486,7 +528,7 @@ def main():
         "kv_append": dict(pre["kv_append"], note="the whole prompt appended as one chunk to "
                           "the key/value/indexer-key caches (copy kernel; lengths kernel apart)"),
     }
-    for name in ("blocks", "sets"):
+    for name in ("blocks", "sets", "backward"):
         if name in res:
             line[name] = res[name]
     if "decode" in res:

@@ -102,7 +102,8 @@ enum {
     LCI_ENTRY_TOPK_SELECT = 1,
     LCI_ENTRY_SPARSE_ATTN = 2,
     LCI_ENTRY_PREFILL = 3,
-    LCI_ENTRY_DECODE = 4
+    LCI_ENTRY_DECODE = 4,
+    LCI_ENTRY_SPARSE_ATTN_BWD = 5
 };
 
 /* Indexer scoring (step 1). "Hybrid Sparse Attention ...", section "Indexer +
@@ -242,6 +243,34 @@ lci_status lci_kv_append(const lci_geom *g, const lci_bf16 *k_new, const lci_bf1
                          lci_bf16 *v_cache, int8_t *kI_cache, int32_t *q_offset_out,
                          int32_t *kv_len_out, void *stream);
 
+/* Gradients of sparse attention + gate (the training direction of steps 3-4;
+ * "Hybrid Sparse Attention ...", section "Engineering and Evaluation
+ * Recommendations", training side). For the forward of lci_sparse_attn_fwd
+ * on the same inputs and an output gradient dy, by the chain rule:
+ *   do = s*dy, dgate = dy*(o - x)*s*(1 - s), dmix = (1 - s)*dy (s = sigmoid(gate),
+ *   s = 1 ungated), dP_t = do.v_t, delta = do.o, dl_t = P_t (dP_t - delta),
+ *   dq = scale sum_t dl_t k_t, dk_t += scale dl_t q, dv_t += P_t do,
+ * summed over the query heads of a key/value head and over every occurrence of
+ * a position in an index row. The scorer (indexer) gets no gradient here.
+ *   q, k, v, idx, gate, mix, softmax_scale: as in lci_sparse_attn_fwd (one index
+ *            set: g->sets > 1 is UNSUPPORTED)
+ *   dy       bf16 [B, Tq, Hq, d]: gradient of out
+ *   dq       fp32 [B, Tq, Hq, d] out
+ *   dk, dv   fp32 [B, Tk, Hkv, d] out: 0 for positions no row selected; sums in
+ *            32.32 fixed point, so they do not depend on the summation order
+ *            (deterministic); each element's sum must stay below 2^31 in size
+ *   dgate    fp32 [B, Tq, Hq, d] out, nullable (only with gate)
+ *   dmix     fp32 [B, Tq, Hq, d] out, nullable (only with mix)
+ *   workspace at least lci_workspace_bytes(LCI_ENTRY_SPARSE_ATTN_BWD): the
+ *            recomputed forward output and lse, do, delta and the transpose of
+ *            the index rows. B*Tq*K*max(1, block) < 2^31 (SHAPE).
+ * Errors: NULL, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN, HIP. */
+lci_status lci_sparse_attn_bwd(const lci_geom *g, const lci_bf16 *q, const lci_bf16 *k,
+                               const lci_bf16 *v, const int32_t *idx, const lci_bf16 *gate,
+                               const lci_bf16 *mix, const lci_bf16 *dy, float softmax_scale,
+                               float *dq, float *dk, float *dv, float *dgate, float *dmix,
+                               void *workspace, size_t ws_bytes, void *stream);
+
 /* Workspace bytes an entry needs for this geometry (host only, reads no device
  * memory). Returns 0 for an invalid geometry or entry id. */
 size_t lci_workspace_bytes(int entry, const lci_geom *g);
@@ -283,7 +312,11 @@ enum {
   LCI_KERNEL_DEC_COMPACT = 10,/* decode: ordered compaction of the selected positions*/
   LCI_KERNEL_KV_APPEND = 11,  /* new rows into the key/value/indexer-key caches     */
   LCI_KERNEL_KV_LENGTHS = 12, /* new cache lengths and first positions after append */
-  LCI_KERNEL_COUNT = 13
+  LCI_KERNEL_BWD_PROLOGUE = 13, /* backward: output gradient through the gate, delta */
+  LCI_KERNEL_BWD_DQ = 14,     /* backward: query gradients                           */
+  LCI_KERNEL_BWD_TRANSPOSE = 15, /* backward: the rows that selected each position  */
+  LCI_KERNEL_BWD_DKDV = 16,   /* backward: key and value gradients                   */
+  LCI_KERNEL_COUNT = 17
 };
 int lci_kernel_timing(int enable);
 int lci_kernel_timing_read(int kernel, double *total_ms, int64_t *launches);

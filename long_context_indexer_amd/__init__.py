@@ -10,6 +10,7 @@ the built library every call raises.
 
 Entry points (same names as the C ABI, without the ``lci_`` prefix):
     idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd, kv_append,
+    sparse_attn_bwd,
     workspace_bytes, kernel_timing, kernel_timing_read, kernel_name
 """
 from __future__ import annotations
@@ -21,19 +22,20 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblci.so")
 
-ENTRY_IDX_SCORE, ENTRY_TOPK_SELECT, ENTRY_SPARSE_ATTN, ENTRY_PREFILL, ENTRY_DECODE = range(5)
+(ENTRY_IDX_SCORE, ENTRY_TOPK_SELECT, ENTRY_SPARSE_ATTN, ENTRY_PREFILL, ENTRY_DECODE,
+ ENTRY_SPARSE_ATTN_BWD) = range(6)
 
 # LCI_ABI_VERSION of the signatures declared below
 ABI_VERSION = 2
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
-           "lci_decode_fwd", "lci_kv_append", "lci_workspace_bytes", "lci_status_str", "lci_last_hip_error",
+           "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_workspace_bytes", "lci_status_str", "lci_last_hip_error",
            "lci_abi_version", "lci_kernel_timing", "lci_kernel_timing_read", "lci_kernel_name")
 
 # kernel kinds of the timing log (LCI_KERNEL_* in lci.h)
 KERNELS = ("idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
            "dec_thresh", "dec_score", "dec_cand", "dec_resolve", "dec_compact", "kv_append",
-           "kv_lengths")
+           "kv_lengths", "bwd_prologue", "bwd_dq", "bwd_transpose", "bwd_dkdv")
 
 
 class LciError(RuntimeError):
@@ -71,6 +73,8 @@ def load_library(path: str = LIB_PATH):
     lib.lci_prefill_fwd.argtypes = fused
     lib.lci_decode_fwd.argtypes = fused
     lib.lci_kv_append.argtypes = [G, P, P, P, P, P, P, P, P, P, P]
+    lib.lci_sparse_attn_bwd.argtypes = [G, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P,
+                                        P, sz, P]
     lib.lci_workspace_bytes.argtypes = [ctypes.c_int, G]
     lib.lci_workspace_bytes.restype = sz
     lib.lci_status_str.argtypes = [ctypes.c_int]
@@ -86,7 +90,7 @@ def load_library(path: str = LIB_PATH):
     lib.lci_kernel_name.argtypes = [ctypes.c_int]
     lib.lci_kernel_name.restype = ctypes.c_char_p
     for fn in ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
-               "lci_decode_fwd", "lci_kv_append", "lci_kernel_timing", "lci_kernel_timing_read"):
+               "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_kernel_timing", "lci_kernel_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -382,3 +386,37 @@ def kv_append(k_new, v_new, kI_new, k_cache, v_cache, kI_cache, kv_len, n_new=No
                                         _ptr(kI_cache), _ptr(q_offset_out), _ptr(kv_len_out),
                                         _stream(stream)))
     return q_offset_out, kv_len_out
+
+
+def sparse_attn_bwd(q, k, v, idx, gate, scale, kv_len, dy, q_offset=None, mix=None,
+                    workspace=None, stream=None):
+    """Gradients of sparse_attn_fwd for the output gradient dy (bf16, the shape of q):
+    returns dict(dq, dk, dv, dgate, dmix) as float32 tensors (dgate / dmix None
+    without gate / mix). idx int32 [B,Tq,K] (one index set)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dy, "dy")):
+        _dev(t, torch.bfloat16, n, 4)
+    _dev(idx, torch.int32, "idx", 3)
+    _dev(gate, torch.bfloat16, "gate", 4)
+    _dev(mix, torch.bfloat16, "mix", 4)
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Tk, Hkv, d) or tuple(v.shape) != tuple(k.shape) or \
+            tuple(dy.shape) != tuple(q.shape) or idx.shape[:2] != (B, Tq):
+        raise ValueError("inconsistent shapes")
+    _gate_args(q, gate, mix)
+    if q_offset is None:
+        q_offset = torch.zeros(B, dtype=torch.int32, device=q.device)
+    g = make_geom(B, Tq, Tk, idx.shape[2], q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(k.shape, **f32)
+    dv = torch.empty(k.shape, **f32)
+    dg = torch.empty(q.shape, **f32) if gate is not None else None
+    dm = torch.empty(q.shape, **f32) if mix is not None else None
+    ws, nb = _workspace(ENTRY_SPARSE_ATTN_BWD, g, workspace, q.device)
+    _check(load_library().lci_sparse_attn_bwd(ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(idx), _ptr(gate), _ptr(mix), _ptr(dy),
+                                              float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                              _ptr(dg), _ptr(dm), _ptr(ws), nb, _stream(stream)))
+    return dict(dq=dq, dk=dk, dv=dv, dgate=dg, dmix=dm)

@@ -100,6 +100,18 @@ hipError_t launch_block_topk(const Geom& g, const int32_t* scores, int64_t score
 hipError_t launch_regroup_q_idx(const Geom& g, const int8_t* q_idx, int8_t* out,
                                 hipStream_t stream);
 
+// ---- gradients of sparse attention + gate (g.K = index row length, one set)
+struct BwdLayout {
+  size_t fwd, o, lse, dO, delta, cnt, off, cursor, tiles, rows, total;
+  int splits, ntiles;
+};
+BwdLayout bwd_layout(const Geom& g);
+hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const int32_t* idx, const uint16_t* gate,
+                                  const uint16_t* mix, const uint16_t* dy, float scale, float* dq,
+                                  float* dk, float* dv, float* dgate, float* dmix,
+                                  void* workspace, hipStream_t stream);
+
 // ---- appending rows to the key / value / indexer-key caches
 // Sizes from g: B, Tq (= rows of the new tensors per sequence), Tk (capacity),
 // Hkv, d, d_I; g.kv_len holds the current lengths.

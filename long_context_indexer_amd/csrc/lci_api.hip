@@ -174,6 +174,10 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
           check_sets(g, true) != LCI_OK)
         return 0;
       return prefill_layout(g).total;
+    case LCI_ENTRY_SPARSE_ATTN_BWD: {
+      if (check_attention(g) != LCI_OK || sel_sets(g) > 1 || g->sets < 0) return 0;
+      return lci::bwd_layout(attn_geom(g)).total;
+    }
     case LCI_ENTRY_DECODE:
       if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK || g->Tq != 1 ||
           check_sets(g, true) != LCI_OK)
@@ -360,6 +364,38 @@ lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* 
   return hip_status(lci::launch_decode(gg, q_idx, k_idx, w, w_stride_b, q, k, v, gate, mix,
                                        softmax_scale, out, lse, idx_out, workspace,
                                        static_cast<hipStream_t>(stream)));
+}
+
+lci_status lci_sparse_attn_bwd(const lci_geom* g, const lci_bf16* q, const lci_bf16* k,
+                               const lci_bf16* v, const int32_t* idx, const lci_bf16* gate,
+                               const lci_bf16* mix, const lci_bf16* dy, float softmax_scale,
+                               float* dq, float* dk, float* dv, float* dgate, float* dmix,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  lci_status s = check_base(g);
+  if (s != LCI_OK) return s;
+  if ((s = check_attention(g)) != LCI_OK) return s;
+  if (g->sets < 0) return LCI_ERR_SHAPE;
+  if (sel_sets(g) > 1) return LCI_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !idx || !dy || !dq || !dk || !dv || (mix && !gate) ||
+      (dgate && !gate) || (dmix && !mix))
+    return LCI_ERR_NULL;
+  if (!scale_ok(softmax_scale)) return LCI_ERR_SHAPE;
+  const Geom ga = attn_geom(g);
+  // the transpose of the index rows addresses entries with int32 offsets
+  if (static_cast<int64_t>(g->B) * g->Tq * ga.K >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(g->B) * g->Tk >= (int64_t(1) << 31))
+    return LCI_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dy) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || (gate && !aligned16(gate)) ||
+      (mix && !aligned16(mix)) || (dgate && !aligned16(dgate)) || (dmix && !aligned16(dmix)) ||
+      !aligned4(idx))
+    return LCI_ERR_ALIGN;
+  const lci::BwdLayout L = lci::bwd_layout(ga);
+  if (!workspace || ws_bytes < L.total) return LCI_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LCI_ERR_ALIGN;
+  return hip_status(lci::launch_sparse_attn_bwd(ga, q, k, v, idx, gate, mix, dy, softmax_scale,
+                                                dq, dk, dv, dgate, dmix, workspace,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 lci_status lci_kv_append(const lci_geom* g, const lci_bf16* k_new, const lci_bf16* v_new,

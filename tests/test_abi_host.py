@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
-              "lci_decode_fwd", "lci_kv_append", "lci_workspace_bytes"):
+              "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_workspace_bytes"):
         assert n in names
 
 
@@ -142,6 +142,23 @@ def test_index_set_limits(lib):
     need = lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g))
     assert need >= 2 * 16 * 64 * 4 + 16 * 8 * 64         # index rows of both sets + queries
     assert fused(lib, g, nb=need - 1) == WS
+
+
+def test_backward_arguments(lib):
+    def bwd(g, dgate=None, dmix=None, gate=None, mix=None, ws=FAKE, nb=None, dq=FAKE):
+        if nb is None:
+            nb = lib.lci_workspace_bytes(lci.ENTRY_SPARSE_ATTN_BWD, ctypes.byref(g))
+        return lib.lci_sparse_attn_bwd(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, gate, mix, FAKE,
+                                       0.1, dq, FAKE, FAKE, dgate, dmix, ws, nb, None)
+    assert bwd(geom(), dq=None) == NULL
+    assert bwd(geom(), dgate=FAKE) == NULL                     # dgate without a gate
+    assert bwd(geom(), gate=FAKE, dmix=FAKE) == NULL          # dmix without a mix
+    assert bwd(geom(sets=2)) == UNSUP
+    assert bwd(geom(), nb=16) == WS
+    assert bwd(geom(), ws=None) == WS
+    assert bwd(geom(), dq=FAKE + 4) == ALIGN
+    g = geom(B=2, Tq=64, Tk=4096, K=64)
+    assert lib.lci_workspace_bytes(lci.ENTRY_SPARSE_ATTN_BWD, ctypes.byref(g)) >= 2 * 64 * 64 * 4
 
 
 def test_softmax_scale_must_be_positive(lib):

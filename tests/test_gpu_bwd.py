@@ -1,0 +1,106 @@
+"""GPU parity of the gradients of sparse attention + gate (lci_sparse_attn_bwd)
+against the oracle's chain rule in fp64.
+
+Tolerance: the kernels recompute the forward output o and round it to bf16
+(2^-9 relative) before it enters delta = do.o and dgate, keep do in bf16 for
+the two passes over the selected pairs (2^-9 relative in dv and dP), and
+accumulate in fp32; dk and dv are summed in 32.32 fixed point (2^-33 per
+contribution). The comparison allows relative L2 1e-2 and max-abs 2e-2 of the
+largest reference value per gradient (measured: at most 3e-3 and 1.2e-2). dq,
+dk and dv must be bit-identical across runs (order-free integer sums)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import dev, host, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+MED = synth.CONFIGS["prefill8k"].replace(Tq=300, Tk=300, K=96, n_needles=4)
+TINY = synth.CONFIGS["tiny"]
+REL_L2 = 1e-2
+MAX_REL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def lci():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_indexer_amd as m
+    m.load_library()
+    return m
+
+
+def _close(got, want, what):
+    got = got.astype(np.float64)
+    diff = got - want
+    scale = max(np.abs(want).max(), 1e-30)
+    rel = np.linalg.norm(diff) / max(np.linalg.norm(want), 1e-30)
+    mx = np.abs(diff).max() / scale
+    log(f"  {what}: rel_l2={rel:.2e} max/ref_max={mx:.2e}")
+    assert rel <= REL_L2 and mx <= MAX_REL, (what, rel, mx)
+
+
+def _case(orc, name):
+    r = np.random.default_rng(60)
+    if name == "med_gate_mix":
+        cfg = MED
+        inp = synth.host_inputs(cfg, seed=60)
+        inp["mix"] = synth.host_mix(cfg, seed=60)
+        idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K)
+        return cfg, inp, idx, True
+    if name == "tiny_scrambled_ungated":
+        cfg = TINY.replace(Tq=40, Tk=120, K=24)
+        inp = synth.host_inputs(cfg, seed=61)
+        inp["kv_len"] = np.array([100], np.int32)      # entries >= 100 are skipped
+        idx = np.stack([r.permutation(cfg.Tk)[:cfg.K] for _ in range(cfg.Tq)]).astype(np.int32)
+        idx[3, 10:] = -1
+        idx[5, :] = -1                                  # a row with no entry
+        idx[7, 2] = idx[7, 1]                           # a repeated position
+        return cfg, inp, idx[None], False
+    if name == "g16_gate":
+        cfg = TINY.replace(Hq=16, Hkv=1, d=128, Tq=64, Tk=64, K=80)
+        inp = synth.host_inputs(cfg, seed=62)
+        idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K)
+        return cfg, inp, idx, True
+    if name == "d64_g2_two_sequences":
+        cfg = TINY.replace(B=2, Hq=4, Hkv=2, Tq=50, Tk=90, K=30)
+        inp = synth.host_inputs(cfg, seed=63)
+        inp["q_offset"] = np.array([40, 0], np.int32)
+        inp["kv_len"] = np.array([90, 45], np.int32)
+        idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K)
+        return cfg, inp, idx, True
+    raise KeyError(name)
+
+
+CASES = ["med_gate_mix", "tiny_scrambled_ungated", "g16_gate", "d64_g2_two_sequences"]
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_sparse_attn_bwd(lci, orc, name):
+    import torch
+    cfg, inp, idx, gated = _case(orc, name)
+    r = np.random.default_rng(64)
+    dy = synth.bf16_bits(r.standard_normal((cfg.B, cfg.Tq, cfg.Hq, cfg.d), dtype=np.float32))
+    gate = inp["gate"] if gated else None
+    mix = inp.get("mix") if gated else None
+    log(f"bwd {name}: B={cfg.B} Tq={cfg.Tq} Tk={cfg.Tk} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} "
+        f"K={idx.shape[2]} gated={gated} mix={mix is not None}")
+    d = to_device(inp)
+    res = lci.sparse_attn_bwd(d["q"], d["k"], d["v"], dev(idx), dev(gate), inp["scale"],
+                              d["kv_len"], dev(dy), mix=dev(mix))
+    torch.cuda.synchronize()
+    want = orc.attention_bwd(inp["q"], inp["k"], inp["v"], gate, idx, inp["kv_len"],
+                             inp["scale"], dy, mix=mix)
+    for key in ("dq", "dk", "dv", "dgate", "dmix"):
+        if want[key] is None:
+            assert res[key] is None
+            continue
+        _close(host(res[key]), want[key], f"{name} {key}")
+    # deterministic: a second call gives the same bits
+    res2 = lci.sparse_attn_bwd(d["q"], d["k"], d["v"], dev(idx), dev(gate), inp["scale"],
+                               d["kv_len"], dev(dy), mix=dev(mix))
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(res[key], res2[key]), key
