@@ -40,8 +40,9 @@ TRAFFIC = {
     "attn_dense": dict(fetch_kib=125491.6, fetch_scale=2.0, write_kib=65872.8, write_scale=1.0,
                        sources=("long_context_indexer_amd/csrc/attn_dense.hip",
                                 "long_context_indexer_amd/csrc/attn_dense.h",
-                                "long_context_indexer_amd/csrc/common.h"),
-                       sha256="0db48af7b1ea734e7c1f18c0b684e92e4988259b3af8d1f5a203e31f25a2c4b8"),
+                                "long_context_indexer_amd/csrc/common.h",
+                                "long_context_indexer_amd/csrc/tile.h"),
+                       sha256="45fc9c45a4d3eae9a5358e73e3237d7295431079bcb32d4cfc35ae5bb2d83d0b"),
 }
 
 
