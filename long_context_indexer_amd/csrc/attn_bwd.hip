@@ -30,6 +30,7 @@
 #include "attn_dense.h"
 #include "common.h"
 #include "internal.h"
+#include "tile.h"
 
 namespace lci {
 
@@ -115,7 +116,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const float* __restrict__ lse, const uint16_t* __restrict__ dO,
-    const float* __restrict__ delta, float scale, float* __restrict__ dq, int64_t nwaves) {
+    const float* __restrict__ delta, float scale, float* __restrict__ dq, int64_t nwaves,
+    const uint8_t* __restrict__ done, int dbq) {
   constexpr int L = 64 / G;  // lanes per head
   constexpr int F = D / L;   // features per lane
   const int64_t wv = blockIdx.x * 4LL + (threadIdx.x >> 6);
@@ -125,6 +127,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   const int g = static_cast<int>(wv % Hkv);
   const int64_t row = wv / Hkv;
   const int b = static_cast<int>(row / Tq);
+  if (done) {
+    // rows of token blocks the tile kernel takes are written there
+    const int i = static_cast<int>(row % Tq);
+    if (done[static_cast<int64_t>(b) * ((Tq + dbq - 1) / dbq) + i / dbq]) return;
+  }
   const int h = g * G + hl;
   const int64_t rh = row * Hq + h;
   const int kvl0 = kv_len[b];
@@ -334,20 +341,227 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   }
 }
 
+// dq on the tile path (token blocks the forward's tile kernel took: every row
+// keeps its selection as a bit mask over 64-key tiles). The forward's tile
+// structure: a workgroup is one key/value head g and a token block of 4 waves
+// x 32 (token, head) rows; per 64-key tile, S^T = K Q^T and dP^T = V dO^T on
+// v_mfma_f32_32x32x16_bf16 (K and V rows from LDS), P = exp(scale S - lse)
+// under the mask, dS = P (dP - delta), and dQ^T += K^T dS^T with K^T read
+// transposed from the K tile (ds_read_b64_tr_b16) and dS^T in the B-operand
+// order the C layout already has. No running max: lse is known.
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void bwd_dq_tile_kernel(
+    int Tq, int Tk, int Hq, int Hkv, const int32_t* __restrict__ q_offset,
+    const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ delta, const uint32_t* __restrict__ mask, int Wm,
+    const uint8_t* __restrict__ flag, const uint8_t* __restrict__ done, float scale_log2,
+    float scale, float* __restrict__ dq, int nbps, int nblk) {
+  using C = DenseCfg<D, G>;
+  __shared__ __align__(16) uint16_t ks[2][C::BK * C::KP];
+  __shared__ __align__(16) uint16_t vsh[2][C::BK * C::KP];
+
+  // the forward's placement: XCD x = blockIdx.x % 8 serves key/value head x / (8/Hkv)
+  const int per = 8 / Hkv;
+  const int xcd = blockIdx.x & 7;
+  const int g = xcd / per;
+  const int blk = (blockIdx.x >> 3) * per + xcd % per;
+  if (blk >= nblk) return;
+  const int b = blk / nbps;
+  const int tb = nbps - 1 - blk % nbps;
+  if (done[static_cast<int64_t>(b) * nbps + tb] == 0) return;  // a gather-path block
+  const int i0 = tb * C::BQ;
+  const int iend = min(i0 + C::BQ, Tq);
+  const int qo = q_offset[b];
+  const int kvl0 = kv_len[b];
+  const int kvl = __builtin_amdgcn_readfirstlane(kvl0 <= Tk ? max(kvl0, 0) : 0);
+  const int64_t p_last = min(static_cast<int64_t>(qo) + iend - 1, static_cast<int64_t>(kvl) - 1);
+  const int nkb = p_last < 0 ? 0 : static_cast<int>(p_last / C::BK) + 1;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int r = lane & 31;
+  const int hf = lane >> 5;
+  const int i = i0 + wv * C::TW + r / G;
+  const int h = g * G + r % G;
+  const bool rv = i < Tq;
+  const int64_t qrow = static_cast<int64_t>(b) * Tq + (rv ? i : 0);
+  const int fl = rv ? flag[qrow] : 0;
+  const uint32_t* mrow = mask + qrow * Wm;
+  const int iw0 = i0 + wv * C::TW;
+  const int p_wave_min = qo + iw0;
+  const bool wave_all = __all(!rv || fl == kRowAll) && iw0 < Tq;
+
+  // Q^T and dO^T as B operands: lane holds row[16*kk + 8*hf .. +7]
+  v8bf qf[C::NKK], df[C::NKK];
+  {
+    const int64_t rb = (qrow * Hq + h) * D + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      v4i z = {0, 0, 0, 0};
+      qf[kk] = __builtin_bit_cast(v8bf, rv ? *reinterpret_cast<const v4i*>(q + rb + 16 * kk) : z);
+      df[kk] = __builtin_bit_cast(v8bf, rv ? *reinterpret_cast<const v4i*>(dO + rb + 16 * kk) : z);
+    }
+  }
+  // a row without entries (lse = -inf) or past the block: P = 2^(x - inf) = 0
+  const float lr = rv ? lse[qrow * Hq + h] : -INFINITY;
+  const float l2 = lr == -INFINITY ? INFINITY : lr * LOG2E;
+  const float dl = rv ? delta[qrow * Hq + h] : 0.f;
+
+  constexpr int UPR = D / 8;
+  constexpr int RPI = 64 / UPR;
+  constexpr int NI = C::BK * UPR / 256;
+  const int rowstep = Hkv * D;
+  const uint16_t* kbase =
+      static_cast<const uint16_t*>(uniform_ptr(k + (static_cast<int64_t>(b) * Tk * Hkv + g) * D));
+  const uint16_t* vbase =
+      static_cast<const uint16_t*>(uniform_ptr(v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D));
+  int voff[NI];
+#pragma unroll
+  for (int c = 0; c < NI; ++c) {
+    const int row = (4 * c + wv) * RPI + lane / UPR;
+    const int lu = (lane % UPR) ^ swz<D>(row);
+    voff[c] = (row * rowstep + 8 * lu) * 2;
+  }
+  auto load_tile = [&](const uint16_t* base, int kb, uint16_t* dst) {
+    const int key0 = kb * C::BK;
+    const int nvalid = min(kvl - key0, C::BK);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base) + static_cast<int64_t>(key0) * rowstep, 0,
+        nvalid * rowstep * 2, kBufferFlags);
+#pragma unroll
+    for (int c = 0; c < NI; ++c)
+      load16_to_lds(rs, (LDS_AS uint16_t*)dst + (4 * c + wv) * 512, voff[c]);
+  };
+  // X^T B of one 64-key tile (two 32-key halves): rows of X from LDS, B per lane
+  auto tile_mm = [&](const uint16_t* x_lds, const v8bf* bf, v16f* st) {
+    const LDS_AS uint16_t* xs = (const LDS_AS uint16_t*)x_lds;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
+      const int krow = 32 * kt + r;
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        const v8bf a = __builtin_bit_cast(
+            v8bf, *(const LDS_AS v4i*)(xs + tile_off<D>(krow, 16 * kk + 8 * hf)));
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[kk], st[kt], 0, 0, 0);
+      }
+    }
+  };
+  const int wlast = Wm - 1;
+
+  v16f acc[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+  if (nkb > 0) {
+    load_tile(kbase, 0, ks[0]);
+    load_tile(vbase, 0, vsh[0]);
+  }
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nkb) {
+      load_tile(kbase, kb + 1, ks[buf ^ 1]);
+      load_tile(vbase, kb + 1, vsh[buf ^ 1]);
+    }
+    uint32_t mw[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint32_t x = mrow[min(2 * kb + kt, wlast)];
+      mw[kt] = 2 * kb + kt <= wlast ? x : 0u;
+    }
+    v16f sc[2], dp[2];
+    tile_mm(ks[buf], qf, sc);
+    tile_mm(vsh[buf], df, dp);
+    const int key0 = kb * C::BK;
+    if (!(wave_all && key0 + C::BK - 1 <= p_wave_min)) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint32_t m = mw[kt] >> (4 * hf);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int sel = __builtin_amdgcn_sbfe(static_cast<int>(m), 8 * (e >> 2) + (e & 3), 1);
+          const int sb = __float_as_int(sc[kt][e]);
+          sc[kt][e] = __int_as_float((sb & sel) | (~sel & kNegInfBits));
+        }
+      }
+    }
+    // dS^T in the B-operand order of the dQ step s (see the forward's P^T)
+    v8bf pb[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(__builtin_fmaf(sc[kt][e], scale_log2, -l2));
+        pb[2 * kt + (e >> 3)][e & 7] = static_cast<__bf16>(p * (dp[kt][e] - dl));
+      }
+    // dQ^T += K^T dS^T over the 64 keys, four 16-key steps
+    const LDS_AS uint16_t* ksl = (const LDS_AS uint16_t*)(ks[buf]);
+    const int gi = lane & 15;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
+        const int k0 = 16 * s2 + 4 * hf;
+        LDS_AS v4bf* a0 = (LDS_AS v4bf*)(ksl + tile_off<D>(k0 + gi / 4, d0 + 4 * (gi % 4)));
+        LDS_AS v4bf* a1 = (LDS_AS v4bf*)(ksl + tile_off<D>(k0 + 8 + gi / 4, d0 + 4 * (gi % 4)));
+        const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0);
+        const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1);
+        const v8bf a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], acc[dt], 0, 0, 0);
+      }
+    }
+    // the barrier waits for the next tile's loads and keeps this tile's
+    // buffers until every wave is done with them
+    __syncthreads();
+  }
+  if (!rv) return;
+  // lane holds dQ^T rows d = 32 dt + 8 (e/4) + 4 hf + e%4 of its (token, head)
+  float* out = dq + (qrow * Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const float4 val = make_float4(scale * acc[dt][4 * ii], scale * acc[dt][4 * ii + 1],
+                                     scale * acc[dt][4 * ii + 2], scale * acc[dt][4 * ii + 3]);
+      *reinterpret_cast<float4*>(out + 32 * dt + 8 * ii + 4 * hf) = val;
+    }
+}
+
 template <int D, int G>
 hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* idx, const float* lse, const uint16_t* dO, const float* dlt,
                          const int32_t* off, const int32_t* rows, float scale, float* dq,
-                         float* dk, float* dv, hipStream_t st) {
+                         float* dk, float* dv, const DenseMasks* dm, hipStream_t st) {
+  using C = DenseCfg<D, G>;
+  hipError_t e;
+  if (dm) {
+    // the tile path: token blocks the forward's tile kernel took
+    const int nbps = (g.Tq + C::BQ - 1) / C::BQ;
+    const int nblk = g.B * nbps;
+    const int per = 8 / g.Hkv;
+    const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
+    KernelTimer timer(LCI_KERNEL_BWD_DQ, st);
+    hipLaunchKernelGGL((bwd_dq_tile_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)), dim3(256), 0,
+                       st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, dO, lse, dlt,
+                       dm->mask, dm->Wm, dm->flag, dm->done, scale * LOG2E, scale, dq, nbps,
+                       nblk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t nrow_w = static_cast<int64_t>(g.B) * g.Tq * g.Hkv;
   {
     KernelTimer timer(LCI_KERNEL_BWD_DQ, st);
     hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(static_cast<uint32_t>((nrow_w + 3) / 4)),
                        dim3(256), 0, st, g.Tq, g.Tk, g.K, g.Hq, g.Hkv, g.kv_len, q, k, v, idx,
-                       lse, dO, dlt, scale, dq, nrow_w);
+                       lse, dO, dlt, scale, dq, nrow_w, dm ? dm->done : nullptr, C::BQ);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nkey_w = static_cast<int64_t>(g.B) * g.Tk * g.Hkv;
   {
     KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
@@ -363,13 +577,13 @@ template <int D>
 hipError_t launch_bwd_d(const Geom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const int32_t* idx, const float* lse, const uint16_t* dO, const float* dlt,
                         const int32_t* off, const int32_t* rows, float scale, float* dq,
-                        float* dk, float* dv, hipStream_t st) {
+                        float* dk, float* dv, const DenseMasks* dm, hipStream_t st) {
   switch (g.Hq / g.Hkv) {
-    case 1: return launch_bwd_dg<D, 1>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, st);
-    case 2: return launch_bwd_dg<D, 2>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, st);
-    case 4: return launch_bwd_dg<D, 4>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, st);
-    case 8: return launch_bwd_dg<D, 8>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, st);
-    case 16: return launch_bwd_dg<D, 16>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, st);
+    case 1: return launch_bwd_dg<D, 1>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
+    case 2: return launch_bwd_dg<D, 2>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
+    case 4: return launch_bwd_dg<D, 4>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
+    case 8: return launch_bwd_dg<D, 8>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
+    case 16: return launch_bwd_dg<D, 16>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -449,9 +663,13 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16
                        idx, nent, off, cursor, rows);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // with one split the forward ran the tile path: its masks, row flags and
+  // done bytes sit in the forward workspace
+  const DenseMasks dmv = dense_masks(g, ws + L.fwd);
+  const DenseMasks* dm = L.splits == 1 ? &dmv : nullptr;
   switch (g.d) {
-    case 64: return launch_bwd_d<64>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, st);
-    case 128: return launch_bwd_d<128>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, st);
+    case 64: return launch_bwd_d<64>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
+    case 128: return launch_bwd_d<128>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
     default: return hipErrorInvalidValue;
   }
 }
