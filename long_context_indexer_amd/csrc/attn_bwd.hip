@@ -39,6 +39,8 @@ namespace {
 constexpr float kFix = 4294967296.0f;  // 2^32: the fixed-point scale of dk, dv
 
 // F consecutive bf16 -> float (16-byte loads where F allows)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 template <int F>
 __device__ __forceinline__ void load_bf16(const uint16_t* p, float (&x)[F]) {
   if constexpr (F >= 8) {
@@ -187,13 +189,22 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, 
   for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += gridDim.x * 256LL) p[i] = v;
 }
 
+// a row of a token block the tile kernels take (done non-null: blocks of dbq tokens)
+__device__ __forceinline__ bool tile_row(int64_t row, int b, int Tq, const uint8_t* done, int dbq) {
+  if (!done) return false;
+  const int i = static_cast<int>(row - static_cast<int64_t>(b) * Tq);
+  return done[static_cast<int64_t>(b) * ((Tq + dbq - 1) / dbq) + i / dbq] != 0;
+}
+
 __global__ __launch_bounds__(256) void bwd_count_kernel(int Tq, int Tk, int K,
                                                         const int32_t* __restrict__ kv_len,
                                                         const int32_t* __restrict__ idx,
-                                                        int64_t nent, int32_t* __restrict__ cnt) {
+                                                        int64_t nent, int32_t* __restrict__ cnt,
+                                                        const uint8_t* __restrict__ done, int dbq) {
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < nent; e += gridDim.x * 256LL) {
     const int64_t row = e / K;
     const int b = static_cast<int>(row / Tq);
+    if (tile_row(row, b, Tq, done, dbq)) continue;
     const int kvl = kv_len[b] <= Tk ? kv_len[b] : 0;
     const int s = idx[e];
     if (s >= 0 && s < kvl) atomicAdd(&cnt[static_cast<int64_t>(b) * Tk + s], 1);
@@ -248,10 +259,12 @@ __global__ __launch_bounds__(256) void bwd_fill_kernel(int Tq, int Tk, int K,
                                                        int64_t nent,
                                                        const int32_t* __restrict__ off,
                                                        int32_t* __restrict__ cursor,
-                                                       int32_t* __restrict__ rows) {
+                                                       int32_t* __restrict__ rows,
+                                                       const uint8_t* __restrict__ done, int dbq) {
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < nent; e += gridDim.x * 256LL) {
     const int64_t row = e / K;
     const int b = static_cast<int>(row / Tq);
+    if (tile_row(row, b, Tq, done, dbq)) continue;
     const int kvl = kv_len[b] <= Tk ? kv_len[b] : 0;
     const int s = idx[e];
     if (s >= 0 && s < kvl) {
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ delta,
     const int32_t* __restrict__ off,
     const int32_t* __restrict__ rows, float scale, float* __restrict__ dk,
-    float* __restrict__ dv, int64_t nwaves) {
+    float* __restrict__ dv, int64_t nwaves, int add) {
   constexpr int L = 64 / G;
   constexpr int F = D / L;
   const int lane = threadIdx.x & 63;
@@ -280,6 +293,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int64_t key = wv / Hkv;  // b*Tk + s: the row of k, v, dk, dv
     const int64_t kvrow = (key * Hkv + g) * D + sl * F;
     const int r0 = off[key], r1 = off[key + 1];
+    // add mode: the tile kernel wrote every key; only keys with listed rows change
+    if (add && r1 == r0) continue;
     long long ak[F], av[F];
 #pragma unroll
     for (int f = 0; f < F; ++f) ak[f] = av[f] = 0;
@@ -334,8 +349,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     if (hl == 0) {
 #pragma unroll
       for (int f = 0; f < F; ++f) {
-        dk[kvrow + f] = static_cast<float>(static_cast<double>(ak[f]) * (1.0 / 4294967296.0));
-        dv[kvrow + f] = static_cast<float>(static_cast<double>(av[f]) * (1.0 / 4294967296.0));
+        const float xk = static_cast<float>(static_cast<double>(ak[f]) * (1.0 / 4294967296.0));
+        const float xv = static_cast<float>(static_cast<double>(av[f]) * (1.0 / 4294967296.0));
+        dk[kvrow + f] = add ? dk[kvrow + f] + xk : xk;
+        dv[kvrow + f] = add ? dv[kvrow + f] + xv : xv;
       }
     }
   }
@@ -534,6 +551,222 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_tile_kernel(
     }
 }
 
+// dk, dv on the tile path, key-major: a workgroup is one key/value head g and
+// a block of 128 keys, 32 per wave (the MFMA N dimension). It walks the row
+// tiles (32 (token, head) rows: TW tokens x G heads) of the token blocks the
+// forward's tile kernel took, from the last down to the first that can see
+// its keys, so that the workgroups of one head read the same Q and dO rows at
+// about the same time. Per row tile: S = Q K^T and dP = dO V^T (Q, dO rows
+// from LDS, K and V held as B operands), P = exp(scale S - lse) under each
+// row's mask, dS = P (dP - delta), then dV^T += dO^T P and dK^T += Q^T dS
+// with dO^T and Q^T read transposed from LDS and P, dS in the B-operand order
+// the C layout already has. A fixed order of row tiles: deterministic sums.
+template <int D, int G>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
+    int Tq, int Tk, int Hq, int Hkv, const int32_t* __restrict__ q_offset,
+    const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ delta, const uint32_t* __restrict__ mask, int Wm,
+    const uint8_t* __restrict__ done, float scale_log2, float scale, float* __restrict__ dk,
+    float* __restrict__ dv, int nkbs, int nblk, int nbps) {
+  using C = DenseCfg<D, G>;
+  constexpr int TW = C::TW;  // tokens per row tile
+  constexpr int KB = 128;    // keys per workgroup
+  __shared__ __align__(16) uint16_t qs[2][32 * D];
+  __shared__ __align__(16) uint16_t os[2][32 * D];
+  __shared__ __align__(16) uint32_t msk[2][4][32];  // [wave][row]: the row's word of the wave's keys
+  __shared__ __align__(16) float l2s[2][32];
+  __shared__ __align__(16) float dls[2][32];
+
+  // XCD x = blockIdx.x % 8 serves key/value head x / (8/Hkv); low key blocks
+  // (the longest walks) start first
+  const int per = 8 / Hkv;
+  const int xcd = blockIdx.x & 7;
+  const int g = xcd / per;
+  const int blk = (blockIdx.x >> 3) * per + xcd % per;
+  if (blk >= nblk) return;
+  const int b = blk / nkbs;
+  const int key0 = (blk % nkbs) * KB;
+  const int qo = q_offset[b];
+  const int kvl0 = kv_len[b];
+  const int kvl = __builtin_amdgcn_readfirstlane(kvl0 <= Tk ? max(kvl0, 0) : 0);
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int r = lane & 31;
+  const int hf = lane >> 5;
+  const int key = key0 + 32 * wv + r;
+
+  // K^T and V^T as B operands: lane holds row[16*kk + 8*hf .. +7] of its key
+  v8bf kf[C::NKK], vf[C::NKK];
+  {
+    const bool kv_ok = key < kvl;
+    const int64_t rb = ((static_cast<int64_t>(b) * Tk + (kv_ok ? key : 0)) * Hkv + g) * D + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      v4i z = {0, 0, 0, 0};
+      kf[kk] = __builtin_bit_cast(v8bf, kv_ok ? *reinterpret_cast<const v4i*>(k + rb + 16 * kk) : z);
+      vf[kk] = __builtin_bit_cast(v8bf, kv_ok ? *reinterpret_cast<const v4i*>(v + rb + 16 * kk) : z);
+    }
+  }
+
+  // row tiles t (tokens t*TW ..): from the first whose last token sees key0
+  // to the last token inside the history
+  const int64_t i_first = max(static_cast<int64_t>(key0) - qo, int64_t(0));
+  const int64_t i_end = min(static_cast<int64_t>(Tq), static_cast<int64_t>(kvl) - qo);
+  const int t_first = static_cast<int>(i_first / TW);
+  const int t_last = i_end > i_first && key0 < kvl ? static_cast<int>((i_end - 1) / TW) : -1;
+  auto prev_tile = [&](int t) {  // the last tile <= t of a tile-path token block
+    while (t >= t_first && done[static_cast<int64_t>(b) * nbps + t * TW / C::BQ] == 0) --t;
+    return t;
+  };
+
+  constexpr int UPR = D / 8;
+  constexpr int RPI = 64 / UPR;
+  constexpr int NI = 32 * UPR / 256;
+  int roff[NI];
+#pragma unroll
+  for (int c = 0; c < NI; ++c) {
+    const int row = (4 * c + wv) * RPI + lane / UPR;
+    const int lu = (lane % UPR) ^ swz<D>(row);
+    roff[c] = (((row / G) * Hq + row % G) * D + 8 * lu) * 2;
+  }
+  auto load_rows = [&](int t, int nb) {
+    const int i0 = t * TW;
+    const int ntok = min(TW, Tq - i0);
+    const int64_t e0 = ((static_cast<int64_t>(b) * Tq + i0) * Hq + g * G) * D;
+    const int bytes = ((ntok - 1) * Hq + G) * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(q + e0), 0, bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(dO + e0), 0, bytes, kBufferFlags);
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      load16_to_lds(rq, (LDS_AS uint16_t*)qs[nb] + (4 * c + wv) * 512, roff[c]);
+      load16_to_lds(ro, (LDS_AS uint16_t*)os[nb] + (4 * c + wv) * 512, roff[c]);
+    }
+  };
+  // per-row values of tile t: threads 0-127 the mask words, 128-159 lse
+  // (as log2, +inf for a row without entries), 160-191 delta
+  const int tid = threadIdx.x;
+  auto stage_load = [&](int t) -> uint32_t {
+    const int R = tid & 31;
+    const int i = t * TW + R / G;
+    if (i >= Tq || tid >= 192) return tid >= 128 && tid < 160 ? __float_as_uint(INFINITY) : 0u;
+    const int64_t tok = static_cast<int64_t>(b) * Tq + i;
+    if (tid < 128) {
+      const int kw = key0 / 32 + (tid >> 5);
+      return kw < Wm ? mask[tok * Wm + kw] : 0u;
+    }
+    const int64_t rh = tok * Hq + g * G + R % G;
+    if (tid < 160) {
+      const float l = lse[rh];
+      return __float_as_uint(l == -INFINITY ? INFINITY : l * LOG2E);
+    }
+    return __float_as_uint(delta[rh]);
+  };
+  auto stage_store = [&](uint32_t x, int nb) {
+    const int R = tid & 31;
+    if (tid < 128) msk[nb][tid >> 5][R] = x;
+    else if (tid < 160) l2s[nb][R] = __uint_as_float(x);
+    else if (tid < 192) dls[nb][R] = __uint_as_float(x);
+  };
+
+  v16f av[C::NDT], ak[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) av[dt][e] = ak[dt][e] = 0.f;
+
+  int t = prev_tile(t_last);
+  if (t >= t_first) {
+    load_rows(t, 0);
+    stage_store(stage_load(t), 0);
+  }
+  __syncthreads();
+  int buf = 0;
+  const int gi = lane & 15;
+  while (t >= t_first) {
+    const int tn = prev_tile(t - 1);
+    uint32_t xn = 0;
+    if (tn >= t_first) {
+      load_rows(tn, buf ^ 1);
+      xn = stage_load(tn);
+    }
+    const LDS_AS uint16_t* qt = (const LDS_AS uint16_t*)qs[buf];
+    const LDS_AS uint16_t* ot = (const LDS_AS uint16_t*)os[buf];
+    // S and dP: rows x the wave's 32 keys
+    v16f sc, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = dp[e] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      const int o = tile_off<D>(r, 16 * kk + 8 * hf);
+      const v8bf aq = __builtin_bit_cast(v8bf, *(const LDS_AS v4i*)(qt + o));
+      const v8bf ao = __builtin_bit_cast(v8bf, *(const LDS_AS v4i*)(ot + o));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], sc, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], dp, 0, 0, 0);
+    }
+    // element e is row 8 (e/4) + 4 hf + e%4 of the tile and key r of the wave
+    v8bf pp[2], pd[2];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int R0 = 8 * ii + 4 * hf;
+      const v4u mw = *(const LDS_AS v4u*)&msk[buf][wv][R0];
+      const v4f l2 = *(const LDS_AS v4f*)&l2s[buf][R0];
+      const v4f dl = *(const LDS_AS v4f*)&dls[buf][R0];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * ii + j;
+        const bool sel = (mw[j] >> r) & 1u;
+        const float p = sel ? fast_exp2(__builtin_fmaf(sc[e], scale_log2, -l2[j])) : 0.f;
+        pp[e >> 3][e & 7] = static_cast<__bf16>(p);
+        pd[e >> 3][e & 7] = static_cast<__bf16>(p * (dp[e] - dl[j]));
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows, two 16-row steps
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
+        const int k0 = 16 * s2 + 4 * hf;
+        const int o0 = tile_off<D>(k0 + gi / 4, d0 + 4 * (gi % 4));
+        const int o1 = tile_off<D>(k0 + 8 + gi / 4, d0 + 4 * (gi % 4));
+        const v4bf olo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4bf*)(ot + o0));
+        const v4bf ohi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4bf*)(ot + o1));
+        const v4bf qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4bf*)(qt + o0));
+        const v4bf qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4bf*)(qt + o1));
+        av[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7), pp[s2], av[dt], 0, 0, 0);
+        ak[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), pd[s2], ak[dt], 0, 0, 0);
+      }
+    }
+    if (tn >= t_first) stage_store(xn, buf ^ 1);
+    // the barrier waits for the next tile's loads and keeps this tile's
+    // buffers until every wave is done with them
+    __syncthreads();
+    t = tn;
+    buf ^= 1;
+  }
+  if (key >= Tk) return;
+  // lane holds dV^T rows d = 32 dt + 8 (e/4) + 4 hf + e%4 of its key
+  const int64_t ob = ((static_cast<int64_t>(b) * Tk + key) * Hkv + g) * D;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int d = 32 * dt + 8 * ii + 4 * hf;
+      *reinterpret_cast<float4*>(dv + ob + d) =
+          make_float4(av[dt][4 * ii], av[dt][4 * ii + 1], av[dt][4 * ii + 2], av[dt][4 * ii + 3]);
+      *reinterpret_cast<float4*>(dk + ob + d) =
+          make_float4(scale * ak[dt][4 * ii], scale * ak[dt][4 * ii + 1],
+                      scale * ak[dt][4 * ii + 2], scale * ak[dt][4 * ii + 3]);
+    }
+}
+
 template <int D, int G>
 hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* idx, const float* lse, const uint16_t* dO, const float* dlt,
@@ -562,13 +795,27 @@ hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, co
                        lse, dO, dlt, scale, dq, nrow_w, dm ? dm->done : nullptr, C::BQ);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (dm) {
+    // every key from the tile-path rows; the gather rows are added below
+    const int nbps = (g.Tq + C::BQ - 1) / C::BQ;
+    const int nkbs = (g.Tk + 127) / 128;
+    const int nblk = g.B * nkbs;
+    const int per = 8 / g.Hkv;
+    const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
+    KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
+    hipLaunchKernelGGL((bwd_dkdv_tile_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)), dim3(256),
+                       0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, dO, lse,
+                       dlt, dm->mask, dm->Wm, dm->done, scale * LOG2E, scale, dk, dv, nkbs, nblk,
+                       nbps);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t nkey_w = static_cast<int64_t>(g.B) * g.Tk * g.Hkv;
   {
     KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>),
                        dim3(static_cast<uint32_t>(std::min<int64_t>((nkey_w + 3) / 4, 1 << 16))),
                        dim3(256), 0, st, g.Hq, g.Hkv, q, k, v, lse, dO, dlt, off, rows,
-                       scale, dk, dv, nkey_w);
+                       scale, dk, dv, nkey_w, dm ? 1 : 0);
   }
   return hipGetLastError();
 }
@@ -644,6 +891,13 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16
                          dim3(256), 0, st, nrh, o, dy, gate, mix, dO, dlt, dgate, dmix);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // with one split the forward ran the tile path: its masks, row flags and
+  // done bytes sit in the forward workspace. The position lists below hold
+  // only the rows of the other token blocks.
+  const DenseMasks dmv = dense_masks(g, ws + L.fwd);
+  const DenseMasks* dm = L.splits == 1 ? &dmv : nullptr;
+  const uint8_t* done = dm ? dm->done : nullptr;
+  const int dbq = dense_block_rows(g.Hq / g.Hkv);
   // the rows that selected each position
   const int64_t keys = static_cast<int64_t>(g.B) * g.Tk;
   const int64_t nent = static_cast<int64_t>(g.B) * g.Tq * g.K;
@@ -654,19 +908,15 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16
     hipLaunchKernelGGL(fill_i32_kernel, dim3(gk), dim3(256), 0, st, cnt, keys, 0);
     hipLaunchKernelGGL(fill_i32_kernel, dim3(gk), dim3(256), 0, st, cursor, keys, 0);
     hipLaunchKernelGGL(bwd_count_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, g.kv_len,
-                       idx, nent, cnt);
+                       idx, nent, cnt, done, dbq);
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<uint32_t>(L.ntiles)), dim3(256), 0, st,
                        cnt, keys, off, tiles);
     hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(1024), 0, st, tiles, L.ntiles);
     hipLaunchKernelGGL(scan_add_kernel, dim3(gk), dim3(256), 0, st, off, keys, tiles, L.ntiles);
     hipLaunchKernelGGL(bwd_fill_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, g.kv_len,
-                       idx, nent, off, cursor, rows);
+                       idx, nent, off, cursor, rows, done, dbq);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // with one split the forward ran the tile path: its masks, row flags and
-  // done bytes sit in the forward workspace
-  const DenseMasks dmv = dense_masks(g, ws + L.fwd);
-  const DenseMasks* dm = L.splits == 1 ? &dmv : nullptr;
   switch (g.d) {
     case 64: return launch_bwd_d<64>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
     case 128: return launch_bwd_d<128>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);

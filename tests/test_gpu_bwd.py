@@ -71,10 +71,20 @@ def _case(orc, name):
         inp["kv_len"] = np.array([90, 45], np.int32)
         idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K)
         return cfg, inp, idx, True
+    if name == "mixed_paths":
+        # rows past 4K (K = 64: p >= 256) and two out-of-order rows go to the
+        # gather kernels, the other token blocks to the tile kernels
+        cfg = MED.replace(Tq=520, Tk=520, K=64)
+        inp = synth.host_inputs(cfg, seed=65)
+        idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K).copy()
+        for i in (10, 130):
+            idx[0, i, :i + 1] = r.permutation(idx[0, i, :i + 1])
+        return cfg, inp, idx, True
     raise KeyError(name)
 
 
-CASES = ["med_gate_mix", "tiny_scrambled_ungated", "g16_gate", "d64_g2_two_sequences"]
+CASES = ["med_gate_mix", "tiny_scrambled_ungated", "g16_gate", "d64_g2_two_sequences",
+         "mixed_paths"]
 
 
 @pytest.mark.parametrize("name", CASES)
