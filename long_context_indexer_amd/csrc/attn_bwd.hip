@@ -41,6 +41,9 @@ constexpr float kFix = 4294967296.0f;  // 2^32: the fixed-point scale of dk, dv
 // F consecutive bf16 -> float (16-byte loads where F allows)
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
+constexpr int kBwdChunks = 4;
+constexpr size_t kBwdPartMax = size_t(1) << 30;
+
 template <int F>
 __device__ __forceinline__ void load_bf16(const uint16_t* p, float (&x)[F]) {
   if constexpr (F >= 8) {
@@ -552,7 +555,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_tile_kernel(
 }
 
 // dk, dv on the tile path, key-major: a workgroup is one key/value head g and
-// a block of 128 keys, 32 per wave (the MFMA N dimension). It walks the row
+// a block of 128 keys; 8 waves, two per 32 keys (the MFMA N dimension), each
+// pair splitting d (both compute the pair's S and dP: the second wave per
+// SIMD hides the latency of one wave's chain of reads, MFMAs and exponentials). It walks the row
 // tiles (32 (token, head) rows: TW tokens x G heads) of the token blocks the
 // forward's tile kernel took, from the last down to the first that can see
 // its keys, so that the workgroups of one head read the same Q and dO rows at
@@ -562,14 +567,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_tile_kernel(
 // with dO^T and Q^T read transposed from LDS and P, dS in the B-operand order
 // the C layout already has. A fixed order of row tiles: deterministic sums.
 template <int D, int G>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
+__global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
     int Tq, int Tk, int Hq, int Hkv, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ delta, const uint32_t* __restrict__ mask, int Wm,
     const uint8_t* __restrict__ done, float scale_log2, float scale, float* __restrict__ dk,
-    float* __restrict__ dv, int nkbs, int nblk, int nbps) {
+    float* __restrict__ dv, int nkbs, int nblk, int nbps, int nch, int ch,
+    float* __restrict__ part) {
   using C = DenseCfg<D, G>;
   constexpr int TW = C::TW;  // tokens per row tile
   constexpr int KB = 128;    // keys per workgroup
@@ -586,8 +592,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
   const int g = xcd / per;
   const int blk = (blockIdx.x >> 3) * per + xcd % per;
   if (blk >= nblk) return;
-  const int b = blk / nkbs;
-  const int key0 = (blk % nkbs) * KB;
+  const int b = blk / (nkbs * nch);
+  const int key0 = (blk / nch % nkbs) * KB;
+  const int c = blk % nch;
   const int qo = q_offset[b];
   const int kvl0 = kv_len[b];
   const int kvl = __builtin_amdgcn_readfirstlane(kvl0 <= Tk ? max(kvl0, 0) : 0);
@@ -596,7 +603,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int r = lane & 31;
   const int hf = lane >> 5;
-  const int key = key0 + 32 * wv + r;
+  const int kq = wv & 3;  // the wave's 32 keys
+  const int dh = wv >> 2;  // the wave's half of d
+  constexpr int NDH = C::NDT / 2;
+  const int key = key0 + 32 * kq + r;
 
   // K^T and V^T as B operands: lane holds row[16*kk + 8*hf .. +7] of its key
   v8bf kf[C::NKK], vf[C::NKK];
@@ -615,24 +625,41 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
   // to the last token inside the history
   const int64_t i_first = max(static_cast<int64_t>(key0) - qo, int64_t(0));
   const int64_t i_end = min(static_cast<int64_t>(Tq), static_cast<int64_t>(kvl) - qo);
-  const int t_first = static_cast<int>(i_first / TW);
-  const int t_last = i_end > i_first && key0 < kvl ? static_cast<int>((i_end - 1) / TW) : -1;
+  int t_first = static_cast<int>(i_first / TW);
+  int t_last = i_end > i_first && key0 < kvl ? static_cast<int>((i_end - 1) / TW) : -1;
+  if (nch > 1) {
+    // chunk c: row tiles [c ch, (c+1) ch); a chunk outside the walk writes
+    // nothing and the sum skips it
+    if (t_last < t_first || t_last / ch < c || t_first / ch > c) return;
+    t_first = max(t_first, c * ch);
+    t_last = min(t_last, (c + 1) * ch - 1);
+  }
+  // done bytes read as aligned words: uniform loads through the scalar cache
+  const uint32_t* done_w = reinterpret_cast<const uint32_t*>(done);
+  auto tile_done = [&](int t) {
+    const int64_t x = static_cast<int64_t>(b) * nbps + t * TW / C::BQ;
+    return ((done_w[x >> 2] >> (8 * (x & 3))) & 0xffu) != 0;
+  };
   auto prev_tile = [&](int t) {  // the last tile <= t of a tile-path token block
-    while (t >= t_first && done[static_cast<int64_t>(b) * nbps + t * TW / C::BQ] == 0) --t;
+    while (t >= t_first && !tile_done(t)) --t;
     return t;
   };
 
+  // a row tile is 32 rows of D/8 16-byte units: thread x < 4 D moves unit
+  // x, to LDS offset 16 x (the unit's place after the swizzle)
   constexpr int UPR = D / 8;
-  constexpr int RPI = 64 / UPR;
-  constexpr int NI = 32 * UPR / 256;
-  int roff[NI];
-#pragma unroll
-  for (int c = 0; c < NI; ++c) {
-    const int row = (4 * c + wv) * RPI + lane / UPR;
-    const int lu = (lane % UPR) ^ swz<D>(row);
-    roff[c] = (((row / G) * Hq + row % G) * D + 8 * lu) * 2;
+  const int tid = threadIdx.x;
+  const bool mover = tid < 32 * UPR;
+  int roff;
+  {
+    const int row = (tid / UPR) & 31;
+    const int lu = (tid % UPR) ^ swz<D>(row);
+    roff = (((row / G) * Hq + row % G) * D + 8 * lu) * 2;
   }
-  auto load_rows = [&](int t, int nb) {
+  // the next tile's rows pass through registers: loads straight into LDS
+  // would make every LDS read of the current tile wait for them
+  auto load_rows = [&](int t, v4i* rg) {
+    if (!mover) return;
     const int i0 = t * TW;
     const int ntok = min(TW, Tq - i0);
     const int64_t e0 = ((static_cast<int64_t>(b) * Tq + i0) * Hq + g * G) * D;
@@ -641,48 +668,53 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
         uniform_ptr(q + e0), 0, bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(dO + e0), 0, bytes, kBufferFlags);
-#pragma unroll
-    for (int c = 0; c < NI; ++c) {
-      load16_to_lds(rq, (LDS_AS uint16_t*)qs[nb] + (4 * c + wv) * 512, roff[c]);
-      load16_to_lds(ro, (LDS_AS uint16_t*)os[nb] + (4 * c + wv) * 512, roff[c]);
-    }
+    rg[0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, roff, 0, 0));
+    rg[1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ro, roff, 0, 0));
   };
-  // per-row values of tile t: threads 0-127 the mask words, 128-159 lse
-  // (as log2, +inf for a row without entries), 160-191 delta
-  const int tid = threadIdx.x;
+  auto store_rows = [&](const v4i* rg, int nb) {
+    if (!mover) return;
+    *(LDS_AS v4i*)((LDS_AS uint16_t*)qs[nb] + 8 * tid) = rg[0];
+    *(LDS_AS v4i*)((LDS_AS uint16_t*)os[nb] + 8 * tid) = rg[1];
+  };
+  // per-row values of tile t: threads 0-127 the mask words, 128-159 lse,
+  // 160-191 delta. One load from a clamped in-range address; the row's
+  // validity and the lse transform (log2, +inf for a row without entries)
+  // wait until the store, after the tile's work.
+  const int kw = key0 / 32 + ((tid >> 5) & 3);
   auto stage_load = [&](int t) -> uint32_t {
     const int R = tid & 31;
-    const int i = t * TW + R / G;
-    if (i >= Tq || tid >= 192) return tid >= 128 && tid < 160 ? __float_as_uint(INFINITY) : 0u;
+    const int i = min(t * TW + R / G, Tq - 1);
     const int64_t tok = static_cast<int64_t>(b) * Tq + i;
-    if (tid < 128) {
-      const int kw = key0 / 32 + (tid >> 5);
-      return kw < Wm ? mask[tok * Wm + kw] : 0u;
-    }
     const int64_t rh = tok * Hq + g * G + R % G;
-    if (tid < 160) {
-      const float l = lse[rh];
-      return __float_as_uint(l == -INFINITY ? INFINITY : l * LOG2E);
-    }
-    return __float_as_uint(delta[rh]);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tid < 160 ? lse : delta) + rh;
+    if (tid < 128 && Wm > 0) src = mask + tok * Wm + min(kw, Wm - 1);
+    return *src;
   };
-  auto stage_store = [&](uint32_t x, int nb) {
+  auto stage_store = [&](uint32_t x, int t, int nb) {
     const int R = tid & 31;
-    if (tid < 128) msk[nb][tid >> 5][R] = x;
-    else if (tid < 160) l2s[nb][R] = __uint_as_float(x);
-    else if (tid < 192) dls[nb][R] = __uint_as_float(x);
+    const bool ok = t * TW + R / G < Tq;
+    if (tid < 128) {
+      msk[nb][tid >> 5][R] = ok && kw < Wm ? x : 0u;
+    } else if (tid < 160) {
+      const float l = __uint_as_float(x);
+      l2s[nb][R] = !ok || l == -INFINITY ? INFINITY : l * LOG2E;
+    } else if (tid < 192) {
+      dls[nb][R] = ok ? __uint_as_float(x) : 0.f;
+    }
   };
 
-  v16f av[C::NDT], ak[C::NDT];
+  v16f av[NDH], ak[NDH];
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt)
+  for (int dt = 0; dt < NDH; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) av[dt][e] = ak[dt][e] = 0.f;
 
   int t = prev_tile(t_last);
+  v4i rg[2];
   if (t >= t_first) {
-    load_rows(t, 0);
-    stage_store(stage_load(t), 0);
+    load_rows(t, rg);
+    store_rows(rg, 0);
+    stage_store(stage_load(t), t, 0);
   }
   __syncthreads();
   int buf = 0;
@@ -691,7 +723,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
     const int tn = prev_tile(t - 1);
     uint32_t xn = 0;
     if (tn >= t_first) {
-      load_rows(tn, buf ^ 1);
+      load_rows(tn, rg);
       xn = stage_load(tn);
     }
     const LDS_AS uint16_t* qt = (const LDS_AS uint16_t*)qs[buf];
@@ -713,7 +745,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int R0 = 8 * ii + 4 * hf;
-      const v4u mw = *(const LDS_AS v4u*)&msk[buf][wv][R0];
+      const v4u mw = *(const LDS_AS v4u*)&msk[buf][kq][R0];
       const v4f l2 = *(const LDS_AS v4f*)&l2s[buf][R0];
       const v4f dl = *(const LDS_AS v4f*)&dls[buf][R0];
 #pragma unroll
@@ -729,8 +761,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
+      for (int dt = 0; dt < NDH; ++dt) {
+        const int d0 = 32 * (NDH * dh + dt) + 16 * ((lane >> 4) & 1);
         const int k0 = 16 * s2 + 4 * hf;
         const int o0 = tile_off<D>(k0 + gi / 4, d0 + 4 * (gi % 4));
         const int o1 = tile_off<D>(k0 + 8 + gi / 4, d0 + 4 * (gi % 4));
@@ -744,7 +776,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
             __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), pd[s2], ak[dt], 0, 0, 0);
       }
     }
-    if (tn >= t_first) stage_store(xn, buf ^ 1);
+    if (tn >= t_first) {
+      store_rows(rg, buf ^ 1);
+      stage_store(xn, tn, buf ^ 1);
+    }
     // the barrier waits for the next tile's loads and keeps this tile's
     // buffers until every wave is done with them
     __syncthreads();
@@ -754,11 +789,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
   if (key >= Tk) return;
   // lane holds dV^T rows d = 32 dt + 8 (e/4) + 4 hf + e%4 of its key
   const int64_t ob = ((static_cast<int64_t>(b) * Tk + key) * Hkv + g) * D;
+  if (nch > 1) {
+    // partials [2][nch][B][Tk][Hkv][D]: dv, then dk
+    const int64_t n = static_cast<int64_t>(nblk / (nkbs * nch)) * Tk * Hkv * D;
+    dv = part + c * n;
+    dk = part + (nch + c) * n;
+  }
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt)
+  for (int dt = 0; dt < NDH; ++dt)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const int d = 32 * dt + 8 * ii + 4 * hf;
+      const int d = 32 * (NDH * dh + dt) + 8 * ii + 4 * hf;
       *reinterpret_cast<float4*>(dv + ob + d) =
           make_float4(av[dt][4 * ii], av[dt][4 * ii + 1], av[dt][4 * ii + 2], av[dt][4 * ii + 3]);
       *reinterpret_cast<float4*>(dk + ob + d) =
@@ -767,11 +808,47 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
     }
 }
 
+// dk, dv = the sum of the chunks' partials, in chunk order (the chunks that
+// the key block's walk touched, as the tile kernel decides them)
+template <int D, int G>
+__global__ __launch_bounds__(256) void bwd_part_sum_kernel(
+    int B, int Tq, int Tk, int Hkv, const int32_t* __restrict__ q_offset,
+    const int32_t* __restrict__ kv_len, const float* __restrict__ part, int nch, int ch,
+    float* __restrict__ dk, float* __restrict__ dv) {
+  constexpr int TW = 32 / G;
+  const int64_t n = static_cast<int64_t>(B) * Tk * Hkv * D;
+  for (int64_t x = (blockIdx.x * 256LL + threadIdx.x) * 4; x < n; x += gridDim.x * 1024LL) {
+    const int64_t krow = x / (static_cast<int64_t>(Hkv) * D);  // b*Tk + key
+    const int b = static_cast<int>(krow / Tk);
+    const int key0 = static_cast<int>(krow % Tk) / 128 * 128;
+    const int qo = q_offset[b];
+    const int kvl0 = kv_len[b];
+    const int kvl = kvl0 <= Tk ? max(kvl0, 0) : 0;
+    const int64_t i_first = max(static_cast<int64_t>(key0) - qo, int64_t(0));
+    const int64_t i_end = min(static_cast<int64_t>(Tq), static_cast<int64_t>(kvl) - qo);
+    const int t_first = static_cast<int>(i_first / TW);
+    const int t_last = i_end > i_first && key0 < kvl ? static_cast<int>((i_end - 1) / TW) : -1;
+    float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+    if (t_last >= t_first) {
+      const int c1 = min(t_last / ch, nch - 1);
+      for (int c = t_first / ch; c <= c1; ++c) {
+        const float4 a = *reinterpret_cast<const float4*>(part + c * n + x);
+        const float4 e = *reinterpret_cast<const float4*>(part + (nch + c) * n + x);
+        sv.x += a.x; sv.y += a.y; sv.z += a.z; sv.w += a.w;
+        sk.x += e.x; sk.y += e.y; sk.z += e.z; sk.w += e.w;
+      }
+    }
+    *reinterpret_cast<float4*>(dv + x) = sv;
+    *reinterpret_cast<float4*>(dk + x) = sk;
+  }
+}
+
 template <int D, int G>
 hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* idx, const float* lse, const uint16_t* dO, const float* dlt,
                          const int32_t* off, const int32_t* rows, float scale, float* dq,
-                         float* dk, float* dv, const DenseMasks* dm, hipStream_t st) {
+                         float* dk, float* dv, const DenseMasks* dm, int nch, float* part,
+                         hipStream_t st) {
   using C = DenseCfg<D, G>;
   hipError_t e;
   if (dm) {
@@ -799,15 +876,25 @@ hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, co
     // every key from the tile-path rows; the gather rows are added below
     const int nbps = (g.Tq + C::BQ - 1) / C::BQ;
     const int nkbs = (g.Tk + 127) / 128;
-    const int nblk = g.B * nkbs;
+    const int nblk = g.B * nkbs * nch;
     const int per = 8 / g.Hkv;
     const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
+    const int ntw = (g.Tq + C::TW - 1) / C::TW;
+    const int ch = (ntw + nch - 1) / nch;
     KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
-    hipLaunchKernelGGL((bwd_dkdv_tile_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)), dim3(256),
-                       0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v, dO, lse,
-                       dlt, dm->mask, dm->Wm, dm->done, scale * LOG2E, scale, dk, dv, nkbs, nblk,
-                       nbps);
+    hipLaunchKernelGGL((bwd_dkdv_tile_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)),
+                       dim3(512), 0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v,
+                       dO, lse, dlt, dm->mask, dm->Wm, dm->done, scale * LOG2E, scale, dk, dv,
+                       nkbs, nblk, nbps, nch, ch, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (nch > 1) {
+      const int64_t n4 = static_cast<int64_t>(g.B) * g.Tk * g.Hkv * D / 4;
+      hipLaunchKernelGGL((bwd_part_sum_kernel<D, G>),
+                         dim3(static_cast<uint32_t>(std::min<int64_t>((n4 + 255) / 256, 8192))),
+                         dim3(256), 0, st, g.B, g.Tq, g.Tk, g.Hkv, g.q_offset, g.kv_len, part,
+                         nch, ch, dk, dv);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   const int64_t nkey_w = static_cast<int64_t>(g.B) * g.Tk * g.Hkv;
   {
@@ -824,13 +911,14 @@ template <int D>
 hipError_t launch_bwd_d(const Geom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const int32_t* idx, const float* lse, const uint16_t* dO, const float* dlt,
                         const int32_t* off, const int32_t* rows, float scale, float* dq,
-                        float* dk, float* dv, const DenseMasks* dm, hipStream_t st) {
+                        float* dk, float* dv, const DenseMasks* dm, int nch, float* part,
+                        hipStream_t st) {
   switch (g.Hq / g.Hkv) {
-    case 1: return launch_bwd_dg<D, 1>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
-    case 2: return launch_bwd_dg<D, 2>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
-    case 4: return launch_bwd_dg<D, 4>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
-    case 8: return launch_bwd_dg<D, 8>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
-    case 16: return launch_bwd_dg<D, 16>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
+    case 1: return launch_bwd_dg<D, 1>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, nch, part, st);
+    case 2: return launch_bwd_dg<D, 2>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, nch, part, st);
+    case 4: return launch_bwd_dg<D, 4>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, nch, part, st);
+    case 8: return launch_bwd_dg<D, 8>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, nch, part, st);
+    case 16: return launch_bwd_dg<D, 16>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, nch, part, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -856,7 +944,14 @@ BwdLayout bwd_layout(const Geom& g) {
   L.tiles = L.cursor + align256(keys * sizeof(int32_t));
   L.ntiles = static_cast<int>((keys + 1023) / 1024);
   L.rows = L.tiles + align256((L.ntiles + 1) * sizeof(int32_t));
-  L.total = L.rows + align256(rows * g.K * sizeof(int32_t));
+  L.part = L.rows + align256(rows * g.K * sizeof(int32_t));
+  // the key-major tile kernel splits each key block's rows into kBwdChunks
+  // chunks (balance: the first key blocks see every row, the last few), each
+  // writing partial dk and dv; above kBwdPartMax bytes of partials one chunk
+  // writes dk, dv directly
+  const size_t pbytes = keys * g.Hkv * g.d * sizeof(float) * 2;
+  L.nch = (L.splits == 1 && kBwdChunks * pbytes <= kBwdPartMax) ? kBwdChunks : 1;
+  L.total = L.part + (L.nch > 1 ? align256(L.nch * pbytes) : 0);
   return L;
 }
 
@@ -876,6 +971,8 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16
   int32_t* cursor = reinterpret_cast<int32_t*>(ws + L.cursor);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
+  float* part = L.nch > 1 ? reinterpret_cast<float*>(ws + L.part) : nullptr;
+  const int nch = L.nch;
   // o and lse of the ungated attention
   hipError_t e = launch_sparse_attn(g, q, k, v, idx, nullptr, nullptr, scale, o, lse, L.splits,
                                     ws + L.fwd, false, st);
@@ -918,8 +1015,8 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (g.d) {
-    case 64: return launch_bwd_d<64>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
-    case 128: return launch_bwd_d<128>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, st);
+    case 64: return launch_bwd_d<64>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, nch, part, st);
+    case 128: return launch_bwd_d<128>(g, q, k, v, idx, lse, dO, dlt, off, rows, scale, dq, dk, dv, dm, nch, part, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -102,8 +102,9 @@ hipError_t launch_regroup_q_idx(const Geom& g, const int8_t* q_idx, int8_t* out,
 
 // ---- gradients of sparse attention + gate (g.K = index row length, one set)
 struct BwdLayout {
-  size_t fwd, o, lse, dO, delta, cnt, off, cursor, tiles, rows, total;
+  size_t fwd, o, lse, dO, delta, cnt, off, cursor, tiles, rows, part, total;
   int splits, ntiles;
+  int nch;  // row chunks of the key-major tile kernel (partials summed in order)
 };
 BwdLayout bwd_layout(const Geom& g);
 hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16_t* k,
