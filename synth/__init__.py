@@ -185,6 +185,28 @@ def host_mix(cfg: Config, seed: int = 0) -> np.ndarray:
     return bf16_bits(m)
 
 
+def index_rows(q_offset: np.ndarray, kv_len: np.ndarray, Tq: int, K: int,
+               seed: int = 0) -> np.ndarray:
+    """Random valid index rows int32 [B,Tq,K]: row i of sequence b (position
+    p = q_offset[b] + i) lists min(K, p+1) distinct positions of 0..p in
+    increasing order, then -1; rows past the history (p >= kv_len[b]) are all
+    -1. An input for the attention and its gradients without running a
+    selection (uniform choice, no scores)."""
+    B = len(q_offset)
+    out = np.full((B, Tq, K), -1, np.int32)
+    r = np.random.default_rng(seed)
+    for b in range(B):
+        for i in range(Tq):
+            p = int(q_offset[b]) + i
+            if p >= int(kv_len[b]):
+                continue
+            if p + 1 <= K:
+                out[b, i, :p + 1] = np.arange(p + 1, dtype=np.int32)
+            else:
+                out[b, i] = np.sort(r.choice(p + 1, K, replace=False)).astype(np.int32)
+    return out
+
+
 def device_inputs(cfg: Config, seed: int = 0, device: str = "cuda") -> dict:
     """All inputs of one configuration as device torch tensors, drawn on the GPU.
 

@@ -114,3 +114,33 @@ def test_sparse_attn_bwd(lci, orc, name):
     torch.cuda.synchronize()
     for key in ("dq", "dk", "dv"):
         assert torch.equal(res[key], res2[key]), key
+
+
+def test_sparse_attn_bwd_prefill8k_sampled(lci, orc):
+    """The gradient call at the full Prefill-8K size of the backward benchmark
+    (8192 rows, Hq = 32 over 4 key/value heads, d = 128, K = 2048, every row on
+    the tile path) on random valid index rows, checked on what the oracle
+    computes from a subset of the rows: dq and dgate of the first 64 and the
+    last 92 rows, and dk, dv of positions 8100.. (only the last 92 rows can
+    select them, so the subset's sums for them are complete)."""
+    import torch
+    cfg = synth.CONFIGS["prefill8k"]
+    inp = synth.host_inputs(cfg, seed=66)
+    idx = synth.index_rows(inp["q_offset"], inp["kv_len"], cfg.Tq, cfg.K, seed=66)
+    r = np.random.default_rng(67)
+    dy = synth.bf16_bits(r.standard_normal((cfg.B, cfg.Tq, cfg.Hq, cfg.d), dtype=np.float32))
+    log("bwd prefill8k sampled: B=1 Tq=Tk=8192 Hq=32 Hkv=4 d=128 K=2048")
+    d = to_device(inp)
+    res = lci.sparse_attn_bwd(d["q"], d["k"], d["v"], dev(idx), d["gate"], inp["scale"],
+                              d["kv_len"], dev(dy))
+    torch.cuda.synchronize()
+    got = {k_: host(res[k_]) for k_ in ("dq", "dk", "dv", "dgate")}
+    s0 = 8100
+    for rows in (slice(0, 64), slice(s0, cfg.Tq)):
+        want = orc.attention_bwd(inp["q"][:, rows], inp["k"], inp["v"], inp["gate"][:, rows],
+                                 idx[:, rows], inp["kv_len"], inp["scale"], dy[:, rows])
+        tag = f"rows {rows.start}-{rows.stop - 1}"
+        _close(got["dq"][:, rows], want["dq"], f"8k {tag} dq")
+        _close(got["dgate"][:, rows], want["dgate"], f"8k {tag} dgate")
+    _close(got["dk"][:, s0:], want["dk"][:, s0:], f"8k keys {s0}.. dk")
+    _close(got["dv"][:, s0:], want["dv"][:, s0:], f"8k keys {s0}.. dv")
