@@ -10,20 +10,25 @@
 //   dq = scale sum_t dl_t k_t, dk_t += scale dl_t q, dv_t += P_t do.
 // Kernels, on the caller's stream:
 //   (forward)        the attention without gate recomputes o (bf16) and lse;
-//   bwd_prologue     per (row, head): do (stored as bf16: the two passes below
-//                    read it once per selected pair), delta (from the fp32 do),
-//                    dgate, dmix;
-//   bwd_dq           one wave per (row, key/value head g): lanes are (query head
-//                    of the group, feature slice), so the dot products of a
-//                    selected key with every head of the group are lane-local
-//                    sums plus a reduction over the lanes of one head; P is
-//                    recomputed from q, k and lse; dq accumulates lane-locally;
-//   key transpose    counts per position (integer atomics), an exclusive scan,
-//                    and a fill of the rows that selected each position;
-//   bwd_dkdv         one wave per (position, key/value head): the rows that
-//                    selected it, in any order, each contributing to dk and dv
-//                    in 32.32 fixed point (int64): integer sums do not depend on
-//                    the order, so dk and dv are deterministic bit for bit.
+//                    with one split it runs the masked-tile kernel, whose row
+//                    masks and per-token-block done bytes route each block of
+//                    rows to the tile kernels below or to the gather kernels;
+//   bwd_prologue     per (row, head): do (stored as bf16), delta (from the fp32
+//                    do), dgate, dmix;
+//   tile path        bwd_dq_tile (query-major, the forward's tile structure) and
+//                    bwd_dkdv_tile (key-major: 128 keys per workgroup walking the
+//                    row tiles that can see them, in chunks summed in order by
+//                    bwd_part_sum): MFMA products over 64-key or 32-row tiles,
+//                    P and dS under each row's selection mask;
+//   gather path      bwd_dq: one wave per (row, key/value head g), lanes (query
+//                    head of the group, feature slice), P recomputed from q, k
+//                    and lse; the key transpose (counts per position, an
+//                    exclusive scan, a fill of the selecting rows) over the
+//                    gather rows only; bwd_dkdv: one wave per (position,
+//                    key/value head) over those rows, in 32.32 fixed point
+//                    (int64), added to the tile path's dk, dv.
+// Every sum runs in a fixed order or in integers: dq, dk, dv are deterministic
+// bit for bit.
 #include <algorithm>
 
 #include "../../include/lci.h"
