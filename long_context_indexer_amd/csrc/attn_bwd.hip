@@ -756,8 +756,11 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = 4 * ii + j;
-        const bool sel = (mw[j] >> r) & 1u;
-        const float p = sel ? fast_exp2(__builtin_fmaf(sc[e], scale_log2, -l2[j])) : 0.f;
+        // bit r of the row's word keeps this key: a one-bit signed extract
+        // gives an all-ones/all-zeros mask for the exponential's bits
+        const int sel = __builtin_amdgcn_sbfe(static_cast<int>(mw[j]), r, 1);
+        const float p = __int_as_float(
+            __float_as_int(fast_exp2(__builtin_fmaf(sc[e], scale_log2, -l2[j]))) & sel);
         pp[e >> 3][e & 7] = static_cast<__bf16>(p);
         pd[e >> 3][e & 7] = static_cast<__bf16>(p * (dp[e] - dl[j]));
       }
