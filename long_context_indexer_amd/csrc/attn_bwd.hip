@@ -16,7 +16,7 @@
 //   bwd_prologue     per (row, head): do (stored as bf16), delta (from the fp32
 //                    do), dgate, dmix;
 //   tile path        bwd_dq_tile (query-major, the forward's tile structure) and
-//                    bwd_dkdv_tile (key-major: 128 keys per workgroup walking the
+//                    bwd_dkdv_tile (key-major: 64 keys per workgroup walking the
 //                    row tiles that can see them, in chunks summed in order by
 //                    bwd_part_sum): MFMA products over 64-key or 32-row tiles,
 //                    P and dS under each row's selection mask;
@@ -47,6 +47,7 @@ constexpr float kFix = 4294967296.0f;  // 2^32: the fixed-point scale of dk, dv
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kBwdChunks = 4;
+constexpr int kDkdvKeys = 64;  // keys per workgroup of the key-major tile kernel
 constexpr size_t kBwdPartMax = size_t(1) << 30;
 
 template <int F>
@@ -560,9 +561,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_tile_kernel(
 }
 
 // dk, dv on the tile path, key-major: a workgroup is one key/value head g and
-// a block of 128 keys; 8 waves, two per 32 keys (the MFMA N dimension), each
-// pair splitting d (both compute the pair's S and dP: the second wave per
-// SIMD hides the latency of one wave's chain of reads, MFMAs and exponentials). It walks the row
+// a block of 64 keys; 4 waves, two per 32 keys (the MFMA N dimension), each
+// pair splitting d (both compute the pair's S and dP). Two workgroups share a
+// compute unit (two waves per SIMD, not in step with each other), which hides
+// the latency of one wave's chain of reads, MFMAs and exponentials. It walks the row
 // tiles (32 (token, head) rows: TW tokens x G heads) of the token blocks the
 // forward's tile kernel took, from the last down to the first that can see
 // its keys, so that the workgroups of one head read the same Q and dO rows at
@@ -572,7 +574,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_tile_kernel(
 // with dO^T and Q^T read transposed from LDS and P, dS in the B-operand order
 // the C layout already has. A fixed order of row tiles: deterministic sums.
 template <int D, int G>
-__global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_tile_kernel(
     int Tq, int Tk, int Hq, int Hkv, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -583,10 +585,10 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
     float* __restrict__ part) {
   using C = DenseCfg<D, G>;
   constexpr int TW = C::TW;  // tokens per row tile
-  constexpr int KB = 128;    // keys per workgroup
+  constexpr int KB = kDkdvKeys;
   __shared__ __align__(16) uint16_t qs[2][32 * D];
   __shared__ __align__(16) uint16_t os[2][32 * D];
-  __shared__ __align__(16) uint32_t msk[2][4][32];  // [wave][row]: the row's word of the wave's keys
+  __shared__ __align__(16) uint32_t msk[2][2][32];  // [wave][row]: the row's word of the wave's keys
   __shared__ __align__(16) float l2s[2][32];
   __shared__ __align__(16) float dls[2][32];
 
@@ -608,8 +610,8 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int r = lane & 31;
   const int hf = lane >> 5;
-  const int kq = wv & 3;  // the wave's 32 keys
-  const int dh = wv >> 2;  // the wave's half of d
+  const int kq = wv & 1;  // the wave's 32 keys
+  const int dh = wv >> 1;  // the wave's half of d
   constexpr int NDH = C::NDT / 2;
   const int key = key0 + 32 * kq + r;
 
@@ -650,21 +652,22 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
     return t;
   };
 
-  // a row tile is 32 rows of D/8 16-byte units: thread x < 4 D moves unit
-  // x, to LDS offset 16 x (the unit's place after the swizzle)
+  // a row tile is 32 rows of D/8 16-byte units: thread x moves units x and
+  // x + 256 (D = 128), to LDS offset 16 x (the unit's place after the swizzle)
   constexpr int UPR = D / 8;
+  constexpr int NU = 32 * UPR / 256;
   const int tid = threadIdx.x;
-  const bool mover = tid < 32 * UPR;
-  int roff;
-  {
-    const int row = (tid / UPR) & 31;
-    const int lu = (tid % UPR) ^ swz<D>(row);
-    roff = (((row / G) * Hq + row % G) * D + 8 * lu) * 2;
+  int roff[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int x = tid + 256 * u;
+    const int row = x / UPR;
+    const int lu = (x % UPR) ^ swz<D>(row);
+    roff[u] = (((row / G) * Hq + row % G) * D + 8 * lu) * 2;
   }
   // the next tile's rows pass through registers: loads straight into LDS
   // would make every LDS read of the current tile wait for them
   auto load_rows = [&](int t, v4i* rg) {
-    if (!mover) return;
     const int i0 = t * TW;
     const int ntok = min(TW, Tq - i0);
     const int64_t e0 = ((static_cast<int64_t>(b) * Tq + i0) * Hq + g * G) * D;
@@ -673,37 +676,42 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
         uniform_ptr(q + e0), 0, bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(dO + e0), 0, bytes, kBufferFlags);
-    rg[0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, roff, 0, 0));
-    rg[1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ro, roff, 0, 0));
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      rg[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, roff[u], 0, 0));
+      rg[NU + u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ro, roff[u], 0, 0));
+    }
   };
   auto store_rows = [&](const v4i* rg, int nb) {
-    if (!mover) return;
-    *(LDS_AS v4i*)((LDS_AS uint16_t*)qs[nb] + 8 * tid) = rg[0];
-    *(LDS_AS v4i*)((LDS_AS uint16_t*)os[nb] + 8 * tid) = rg[1];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      *(LDS_AS v4i*)((LDS_AS uint16_t*)qs[nb] + 8 * (tid + 256 * u)) = rg[u];
+      *(LDS_AS v4i*)((LDS_AS uint16_t*)os[nb] + 8 * (tid + 256 * u)) = rg[NU + u];
+    }
   };
-  // per-row values of tile t: threads 0-127 the mask words, 128-159 lse,
-  // 160-191 delta. One load from a clamped in-range address; the row's
+  // per-row values of tile t: threads 0-63 the mask words, 64-95 lse,
+  // 96-127 delta. One load from a clamped in-range address; the row's
   // validity and the lse transform (log2, +inf for a row without entries)
   // wait until the store, after the tile's work.
-  const int kw = key0 / 32 + ((tid >> 5) & 3);
+  const int kw = key0 / 32 + ((tid >> 5) & 1);
   auto stage_load = [&](int t) -> uint32_t {
     const int R = tid & 31;
     const int i = min(t * TW + R / G, Tq - 1);
     const int64_t tok = static_cast<int64_t>(b) * Tq + i;
     const int64_t rh = tok * Hq + g * G + R % G;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(tid < 160 ? lse : delta) + rh;
-    if (tid < 128 && Wm > 0) src = mask + tok * Wm + min(kw, Wm - 1);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tid < 96 ? lse : delta) + rh;
+    if (tid < 64 && Wm > 0) src = mask + tok * Wm + min(kw, Wm - 1);
     return *src;
   };
   auto stage_store = [&](uint32_t x, int t, int nb) {
     const int R = tid & 31;
     const bool ok = t * TW + R / G < Tq;
-    if (tid < 128) {
+    if (tid < 64) {
       msk[nb][tid >> 5][R] = ok && kw < Wm ? x : 0u;
-    } else if (tid < 160) {
+    } else if (tid < 96) {
       const float l = __uint_as_float(x);
       l2s[nb][R] = !ok || l == -INFINITY ? INFINITY : l * LOG2E;
-    } else if (tid < 192) {
+    } else if (tid < 128) {
       dls[nb][R] = ok ? __uint_as_float(x) : 0.f;
     }
   };
@@ -715,7 +723,7 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_tile_kernel(
     for (int e = 0; e < 16; ++e) av[dt][e] = ak[dt][e] = 0.f;
 
   int t = prev_tile(t_last);
-  v4i rg[2];
+  v4i rg[2 * NU];
   if (t >= t_first) {
     load_rows(t, rg);
     store_rows(rg, 0);
@@ -828,7 +836,7 @@ __global__ __launch_bounds__(256) void bwd_part_sum_kernel(
   for (int64_t x = (blockIdx.x * 256LL + threadIdx.x) * 4; x < n; x += gridDim.x * 1024LL) {
     const int64_t krow = x / (static_cast<int64_t>(Hkv) * D);  // b*Tk + key
     const int b = static_cast<int>(krow / Tk);
-    const int key0 = static_cast<int>(krow % Tk) / 128 * 128;
+    const int key0 = static_cast<int>(krow % Tk) / kDkdvKeys * kDkdvKeys;
     const int qo = q_offset[b];
     const int kvl0 = kv_len[b];
     const int kvl = kvl0 <= Tk ? max(kvl0, 0) : 0;
@@ -883,7 +891,7 @@ hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, co
   if (dm) {
     // every key from the tile-path rows; the gather rows are added below
     const int nbps = (g.Tq + C::BQ - 1) / C::BQ;
-    const int nkbs = (g.Tk + 127) / 128;
+    const int nkbs = (g.Tk + kDkdvKeys - 1) / kDkdvKeys;
     const int nblk = g.B * nkbs * nch;
     const int per = 8 / g.Hkv;
     const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
@@ -891,7 +899,7 @@ hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, co
     const int ch = (ntw + nch - 1) / nch;
     KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
     hipLaunchKernelGGL((bwd_dkdv_tile_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)),
-                       dim3(512), 0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v,
+                       dim3(256), 0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v,
                        dO, lse, dlt, dm->mask, dm->Wm, dm->done, scale * LOG2E, scale, dk, dv,
                        nkbs, nblk, nbps, nch, ch, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
