@@ -47,7 +47,8 @@ constexpr float kFix = 4294967296.0f;  // 2^32: the fixed-point scale of dk, dv
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kBwdChunks = 4;
-constexpr int kDkdvKeys = 64;  // keys per workgroup of the key-major tile kernel
+constexpr int kDkdvKeys = 64;              // keys per workgroup of the key-major tile kernel
+constexpr int kDkdvThreads = 2 * kDkdvKeys * 2;  // two waves per 32 keys
 constexpr size_t kBwdPartMax = size_t(1) << 30;
 
 template <int F>
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_tile_kernel(
 // with dO^T and Q^T read transposed from LDS and P, dS in the B-operand order
 // the C layout already has. A fixed order of row tiles: deterministic sums.
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_tile_kernel(
+__global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_tile_kernel(
     int Tq, int Tk, int Hq, int Hkv, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -588,7 +589,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_tile_kernel(
   constexpr int KB = kDkdvKeys;
   __shared__ __align__(16) uint16_t qs[2][32 * D];
   __shared__ __align__(16) uint16_t os[2][32 * D];
-  __shared__ __align__(16) uint32_t msk[2][2][32];  // [wave][row]: the row's word of the wave's keys
+  constexpr int NKQ = KB / 32;          // 32-key groups
+  constexpr int NT = kDkdvThreads;      // threads
+  __shared__ __align__(16) uint32_t msk[2][NKQ][32];  // [wave][row]: the row's word of the wave's keys
   __shared__ __align__(16) float l2s[2][32];
   __shared__ __align__(16) float dls[2][32];
 
@@ -610,8 +613,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_tile_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int r = lane & 31;
   const int hf = lane >> 5;
-  const int kq = wv & 1;  // the wave's 32 keys
-  const int dh = wv >> 1;  // the wave's half of d
+  const int kq = wv % NKQ;  // the wave's 32 keys
+  const int dh = wv / NKQ;  // the wave's half of d
   constexpr int NDH = C::NDT / 2;
   const int key = key0 + 32 * kq + r;
 
@@ -652,15 +655,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_tile_kernel(
     return t;
   };
 
-  // a row tile is 32 rows of D/8 16-byte units: thread x moves units x and
-  // x + 256 (D = 128), to LDS offset 16 x (the unit's place after the swizzle)
+  // a row tile is 32 rows of D/8 16-byte units: thread x moves units x,
+  // x + NT, ..., to LDS offset 16 x (the unit's place after the swizzle)
   constexpr int UPR = D / 8;
-  constexpr int NU = 32 * UPR / 256;
+  constexpr int NU = 32 * UPR / NT;
   const int tid = threadIdx.x;
   int roff[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int x = tid + 256 * u;
+    const int x = tid + NT * u;
     const int row = x / UPR;
     const int lu = (x % UPR) ^ swz<D>(row);
     roff[u] = (((row / G) * Hq + row % G) * D + 8 * lu) * 2;
@@ -685,33 +688,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_tile_kernel(
   auto store_rows = [&](const v4i* rg, int nb) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      *(LDS_AS v4i*)((LDS_AS uint16_t*)qs[nb] + 8 * (tid + 256 * u)) = rg[u];
-      *(LDS_AS v4i*)((LDS_AS uint16_t*)os[nb] + 8 * (tid + 256 * u)) = rg[NU + u];
+      *(LDS_AS v4i*)((LDS_AS uint16_t*)qs[nb] + 8 * (tid + NT * u)) = rg[u];
+      *(LDS_AS v4i*)((LDS_AS uint16_t*)os[nb] + 8 * (tid + NT * u)) = rg[NU + u];
     }
   };
-  // per-row values of tile t: threads 0-63 the mask words, 64-95 lse,
-  // 96-127 delta. One load from a clamped in-range address; the row's
+  // per-row values of tile t: threads 0 .. 32 NKQ - 1 the mask words (one
+  // per 32-key group), the next 32 lse, the 32 after delta. One load from a clamped in-range address; the row's
   // validity and the lse transform (log2, +inf for a row without entries)
   // wait until the store, after the tile's work.
-  const int kw = key0 / 32 + ((tid >> 5) & 1);
+  constexpr int TL = 32 * NKQ, TD = TL + 32, TE = TD + 32;
+  const int kw = key0 / 32 + min(tid >> 5, NKQ - 1);
   auto stage_load = [&](int t) -> uint32_t {
     const int R = tid & 31;
     const int i = min(t * TW + R / G, Tq - 1);
     const int64_t tok = static_cast<int64_t>(b) * Tq + i;
     const int64_t rh = tok * Hq + g * G + R % G;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(tid < 96 ? lse : delta) + rh;
-    if (tid < 64 && Wm > 0) src = mask + tok * Wm + min(kw, Wm - 1);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tid < TD ? lse : delta) + rh;
+    if (tid < TL && Wm > 0) src = mask + tok * Wm + min(kw, Wm - 1);
     return *src;
   };
   auto stage_store = [&](uint32_t x, int t, int nb) {
     const int R = tid & 31;
     const bool ok = t * TW + R / G < Tq;
-    if (tid < 64) {
+    if (tid < TL) {
       msk[nb][tid >> 5][R] = ok && kw < Wm ? x : 0u;
-    } else if (tid < 96) {
+    } else if (tid < TD) {
       const float l = __uint_as_float(x);
       l2s[nb][R] = !ok || l == -INFINITY ? INFINITY : l * LOG2E;
-    } else if (tid < 128) {
+    } else if (tid < TE) {
       dls[nb][R] = ok ? __uint_as_float(x) : 0.f;
     }
   };
@@ -899,7 +903,7 @@ hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, co
     const int ch = (ntw + nch - 1) / nch;
     KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
     hipLaunchKernelGGL((bwd_dkdv_tile_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)),
-                       dim3(256), 0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v,
+                       dim3(kDkdvThreads), 0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v,
                        dO, lse, dlt, dm->mask, dm->Wm, dm->done, scale * LOG2E, scale, dk, dv,
                        nkbs, nblk, nbps, nch, ch, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
