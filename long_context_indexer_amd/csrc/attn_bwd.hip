@@ -595,16 +595,18 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_tile_kernel(
   __shared__ __align__(16) float l2s[2][32];
   __shared__ __align__(16) float dls[2][32];
 
-  // XCD x = blockIdx.x % 8 serves key/value head x / (8/Hkv); low key blocks
-  // (the longest walks) start first
+  // XCD x = blockIdx.x % 8 serves key/value head x / (8/Hkv)
   const int per = 8 / Hkv;
   const int xcd = blockIdx.x & 7;
   const int g = xcd / per;
   const int blk = (blockIdx.x >> 3) * per + xcd % per;
   if (blk >= nblk) return;
-  const int b = blk / (nkbs * nch);
-  const int key0 = (blk / nch % nkbs) * KB;
-  const int c = blk % nch;
+  // chunk-major, last chunk first: the workgroups running together walk the
+  // same rows (shared in L2), and the last chunk has work for every key block
+  const int nb = nblk / (nkbs * nch);
+  const int key0 = (blk % nkbs) * KB;
+  const int b = blk / nkbs % nb;
+  const int c = nch - 1 - blk / (nkbs * nb);
   const int qo = q_offset[b];
   const int kvl0 = kv_len[b];
   const int kvl = __builtin_amdgcn_readfirstlane(kvl0 <= Tk ? max(kvl0, 0) : 0);
@@ -811,7 +813,7 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_tile_kernel(
   const int64_t ob = ((static_cast<int64_t>(b) * Tk + key) * Hkv + g) * D;
   if (nch > 1) {
     // partials [2][nch][B][Tk][Hkv][D]: dv, then dk
-    const int64_t n = static_cast<int64_t>(nblk / (nkbs * nch)) * Tk * Hkv * D;
+    const int64_t n = static_cast<int64_t>(nb) * Tk * Hkv * D;
     dv = part + c * n;
     dk = part + (nch + c) * n;
   }
