@@ -46,7 +46,7 @@ constexpr float kFix = 4294967296.0f;  // 2^32: the fixed-point scale of dk, dv
 // F consecutive bf16 -> float (16-byte loads where F allows)
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kBwdChunks = 4;
+constexpr int kBwdChunks = 8;
 constexpr int kDkdvKeys = 64;              // keys per workgroup of the key-major tile kernel
 constexpr int kDkdvThreads = 2 * kDkdvKeys * 2;  // two waves per 32 keys
 constexpr size_t kBwdPartMax = size_t(1) << 30;
@@ -967,12 +967,18 @@ BwdLayout bwd_layout(const Geom& g) {
   L.ntiles = static_cast<int>((keys + 1023) / 1024);
   L.rows = L.tiles + align256((L.ntiles + 1) * sizeof(int32_t));
   L.part = L.rows + align256(rows * g.K * sizeof(int32_t));
-  // the key-major tile kernel splits each key block's rows into kBwdChunks
-  // chunks (balance: the first key blocks see every row, the last few), each
-  // writing partial dk and dv; above kBwdPartMax bytes of partials one chunk
-  // writes dk, dv directly
+  // the key-major tile kernel splits each key block's rows into up to
+  // kBwdChunks chunks (balance: the first key blocks see every row, the last
+  // few), each writing partial dk and dv, as many as fit in kBwdPartMax bytes
+  // of partials; with one chunk the kernel writes dk, dv directly
   const size_t pbytes = keys * g.Hkv * g.d * sizeof(float) * 2;
-  L.nch = (L.splits == 1 && kBwdChunks * pbytes <= kBwdPartMax) ? kBwdChunks : 1;
+  L.nch = 1;
+  if (L.splits == 1)
+    for (int n = kBwdChunks; n > 1; n /= 2)
+      if (n * pbytes <= kBwdPartMax) {
+        L.nch = n;
+        break;
+      }
   L.total = L.part + (L.nch > 1 ? align256(L.nch * pbytes) : 0);
   return L;
 }
