@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define LCI_ABI_VERSION 2
+#define LCI_ABI_VERSION 3
 
 typedef uint16_t lci_bf16;
 
@@ -274,6 +274,19 @@ lci_status lci_sparse_attn_bwd(const lci_geom *g, const lci_bf16 *q, const lci_b
 /* Workspace bytes an entry needs for this geometry (host only, reads no device
  * memory). Returns 0 for an invalid geometry or entry id. */
 size_t lci_workspace_bytes(int entry, const lci_geom *g);
+
+/* Query rows of an entry that take the dense-tile attention path (host only,
+ * reads no device memory): a valid row at position p takes it when
+ * p + 1 <= the returned limit, which is 0 when the entry runs no tile path for
+ * this geometry (few rows: split-K; the one-row decode path). The two exact
+ * formulations of the pages ("From Linear Attention to Gated Sparse
+ * Attention", section 2: scores over all causal positions under a selection
+ * mask; "Hybrid Sparse Attention ...", the Indexer + Top-K pseudocode: a
+ * gather of the selected rows) give the same result up to fp32 summation
+ * order; the limit only says which kernel does the work (for per-kernel
+ * accounting). entry: LCI_ENTRY_PREFILL, LCI_ENTRY_SPARSE_ATTN or
+ * LCI_ENTRY_DECODE; any other id, or an invalid geometry, gives 0. */
+int lci_dense_row_limit(int entry, const lci_geom *g);
 
 /* Static text for a status code. */
 const char *lci_status_str(int status);

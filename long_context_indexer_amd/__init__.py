@@ -11,7 +11,7 @@ the built library every call raises.
 Entry points (same names as the C ABI, without the ``lci_`` prefix):
     idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd, kv_append,
     sparse_attn_bwd,
-    workspace_bytes, kernel_timing, kernel_timing_read, kernel_name
+    workspace_bytes, dense_row_limit, kernel_timing, kernel_timing_read, kernel_name
 """
 from __future__ import annotations
 
@@ -26,10 +26,11 @@ LIB_PATH = os.path.join(HERE, "liblci.so")
  ENTRY_SPARSE_ATTN_BWD) = range(6)
 
 # LCI_ABI_VERSION of the signatures declared below
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
-           "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_workspace_bytes", "lci_status_str", "lci_last_hip_error",
+           "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_workspace_bytes",
+           "lci_dense_row_limit", "lci_status_str", "lci_last_hip_error",
            "lci_abi_version", "lci_kernel_timing", "lci_kernel_timing_read", "lci_kernel_name")
 
 # kernel kinds of the timing log (LCI_KERNEL_* in lci.h)
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH):
                                         P, sz, P]
     lib.lci_workspace_bytes.argtypes = [ctypes.c_int, G]
     lib.lci_workspace_bytes.restype = sz
+    lib.lci_dense_row_limit.argtypes = [ctypes.c_int, G]
+    lib.lci_dense_row_limit.restype = ctypes.c_int
     lib.lci_status_str.argtypes = [ctypes.c_int]
     lib.lci_status_str.restype = ctypes.c_char_p
     lib.lci_last_hip_error.restype = ctypes.c_int
@@ -156,6 +159,11 @@ def _w_strides(w, B, Tq, H_I):
 
 def workspace_bytes(entry: int, geom: lci_geom) -> int:
     return int(load_library().lci_workspace_bytes(entry, ctypes.byref(geom)))
+
+
+def dense_row_limit(geom: lci_geom, entry: int = ENTRY_PREFILL) -> int:
+    """Rows with p + 1 <= this limit take the dense-tile attention path (0: none)."""
+    return int(load_library().lci_dense_row_limit(entry, ctypes.byref(geom)))
 
 
 def kernel_timing(enable: bool) -> None:

@@ -456,10 +456,11 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
 
 int dense_block_rows(int G) { return 4 * (32 / G); }
 
-int dense_mask_words(const Geom& g) {
-  const int64_t lim = std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk);
-  return static_cast<int>((lim + 31) / 32);
+int dense_row_limit(const Geom& g) {
+  return static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
 }
+
+int dense_mask_words(const Geom& g) { return (dense_row_limit(g) + 31) / 32; }
 
 // [mask: rows x Wm words][flag: rows bytes][done: one byte per token block
 // (at most one block per row)], each part 256-byte aligned; rows = B x sets x Tq
@@ -473,7 +474,7 @@ DenseMasks dense_masks(const Geom& g, void* ws) {
   const size_t rows = static_cast<size_t>(g.B) * g.sets * g.Tq;
   DenseMasks d;
   d.Wm = dense_mask_words(g);
-  d.lim = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
+  d.lim = dense_row_limit(g);
   char* base = static_cast<char*>(ws);
   const size_t mbytes = (rows * d.Wm * sizeof(uint32_t) + 255) & ~size_t(255);
   d.mask = reinterpret_cast<uint32_t*>(base);

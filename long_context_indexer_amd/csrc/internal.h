@@ -64,6 +64,8 @@ struct DenseMasks {
   int Wm, lim;
 };
 DenseMasks dense_masks(const Geom& g, void* workspace);
+// Rows with p + 1 <= dense_row_limit(g) take the dense-tile path (one split).
+int dense_row_limit(const Geom& g);
 
 // With dm (only when Tk <= kWaveTopkMax), the Top-K kernel also writes the
 // dense-path flags and masks of its rows.

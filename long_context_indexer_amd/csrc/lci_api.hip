@@ -190,6 +190,18 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
   }
 }
 
+int lci_dense_row_limit(int entry, const lci_geom* g) {
+  if (check_base(g) != LCI_OK || check_attention(g) != LCI_OK) return 0;
+  if (entry != LCI_ENTRY_PREFILL && entry != LCI_ENTRY_SPARSE_ATTN &&
+      entry != LCI_ENTRY_DECODE)
+    return 0;
+  // the one-row decode path never takes the tile kernel
+  if (entry == LCI_ENTRY_DECODE && sel_block(g) == 1 && sel_sets(g) == 1) return 0;
+  const Geom ga = attn_geom(g);
+  if (lci::sparse_attn_pick_splits(ga) != 1) return 0;
+  return lci::dense_row_limit(ga);
+}
+
 lci_status lci_idx_score(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
                          const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
                          int32_t* scores, void* stream) {

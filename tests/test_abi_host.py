@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.lci_abi_version() == lci.ABI_VERSION == 2
+    assert lib.lci_abi_version() == lci.ABI_VERSION == 3
     for code in (OK, NULL, SHAPE, UNSUP, OVF, WS, HIP, ALIGN):
         assert lib.lci_status_str(code).decode().startswith("LCI_")
     assert b"unknown" in lib.lci_status_str(123)
@@ -246,3 +246,15 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises((ValueError, RuntimeError)):
         lci.idx_score(z, torch.zeros(1, 4, 32, dtype=torch.int8), torch.ones(2, dtype=torch.int8),
                       torch.zeros(1, dtype=torch.int32), torch.ones(1, dtype=torch.int32))
+
+
+def test_dense_row_limit(lib):
+    def lim(entry, g):
+        return lib.lci_dense_row_limit(entry, ctypes.byref(g))
+    g = geom(B=1, Tq=65536, Tk=65536, Hq=32, Hkv=4, K=2048)
+    assert lim(lci.ENTRY_PREFILL, g) == lim(lci.ENTRY_SPARSE_ATTN, g) == 4 * 2048
+    assert lim(lci.ENTRY_PREFILL, geom(B=1, Tq=4096, Tk=4096, K=2048)) == 4096   # whole history
+    assert lim(lci.ENTRY_DECODE, geom(B=64, Tq=1, Tk=1 << 17, K=2048)) == 0     # split-K decode
+    assert lim(lci.ENTRY_PREFILL, geom(B=2, Tq=8, Tk=4096, K=2048)) == 0        # few rows
+    assert lim(lci.ENTRY_IDX_SCORE, g) == 0
+    assert lim(lci.ENTRY_PREFILL, geom(d=96)) == 0                              # invalid
