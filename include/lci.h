@@ -75,7 +75,9 @@ typedef enum lci_status {
     LCI_ERR_OVERFLOW_RISK = -4, /* H_I*d_I > 1024: an int32 score could overflow        */
     LCI_ERR_WORKSPACE = -5,     /* workspace NULL or smaller than lci_workspace_bytes() */
     LCI_ERR_HIP = -6,           /* a HIP call failed; see lci_last_hip_error()          */
-    LCI_ERR_ALIGN = -7          /* a pointer is not 16-byte aligned                     */
+    LCI_ERR_ALIGN = -7,         /* a pointer is not 16-byte aligned                     */
+    LCI_ERR_SCRATCH = -8        /* lci_decode_fwd_noalloc: the call needs more workspace */
+                                /* than the static scratch array holds                  */
 } lci_status;
 
 /* Geometry shared by every entry point. */
@@ -211,6 +213,30 @@ lci_status lci_decode_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *
                           const lci_bf16 *gate, const lci_bf16 *mix, float softmax_scale,
                           lci_bf16 *out, float *lse, int32_t *idx_out, void *workspace,
                           size_t ws_bytes, void *stream);
+
+/* Allocation-free fused decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, results and errors as lci_decode_fwd, without
+ * the workspace: the call carves its workspace out of a static device array of
+ * LCI_NOALLOC_SCRATCH_MIB MiB (lci_noalloc_scratch_bytes()) that the library's
+ * code object holds; each GPU the library runs on keeps its own copy until the
+ * process ends. The call allocates and frees nothing; its first call on a
+ * device looks up that device's copy (hipGetSymbolAddress). A geometry whose
+ * lci_workspace_bytes(LCI_ENTRY_DECODE) exceeds the array returns
+ * LCI_ERR_SCRATCH and enqueues nothing (Decode 128K, 64 x 131072 positions,
+ * and Decode 1M, 8 x 1048576, both fit: about 14 B per history position plus
+ * the split-K partials). Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be ordered
+ * by the caller. The array keeps the last call's contents; the decode kernels
+ * read no workspace byte they have not written in the same call. */
+#define LCI_NOALLOC_SCRATCH_MIB 128
+size_t lci_noalloc_scratch_bytes(void);
+lci_status lci_decode_fwd_noalloc(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
+                                  const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
+                                  const lci_bf16 *q, const lci_bf16 *k, const lci_bf16 *v,
+                                  const lci_bf16 *gate, const lci_bf16 *mix,
+                                  float softmax_scale, lci_bf16 *out, float *lse,
+                                  int32_t *idx_out, void *stream);
 
 /* Append new rows to the key, value and indexer-key caches ("Hybrid Sparse
  * Attention ...", section "Engineering and Evaluation Recommendations": long

@@ -9,8 +9,8 @@ PyTorch supplies device memory and streams. There is no CPU fallback: without
 the built library every call raises.
 
 Entry points (same names as the C ABI, without the ``lci_`` prefix):
-    idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd, kv_append,
-    sparse_attn_bwd,
+    idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd, decode_fwd_noalloc,
+    kv_append, sparse_attn_bwd,
     workspace_bytes, dense_row_limit, kernel_timing, kernel_timing_read, kernel_name
 """
 from __future__ import annotations
@@ -30,7 +30,8 @@ ABI_VERSION = 3
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
            "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_workspace_bytes",
-           "lci_dense_row_limit", "lci_status_str", "lci_last_hip_error",
+           "lci_dense_row_limit", "lci_decode_fwd_noalloc", "lci_noalloc_scratch_bytes",
+           "lci_status_str", "lci_last_hip_error",
            "lci_abi_version", "lci_kernel_timing", "lci_kernel_timing_read", "lci_kernel_name")
 
 # kernel kinds of the timing log (LCI_KERNEL_* in lci.h)
@@ -73,6 +74,9 @@ def load_library(path: str = LIB_PATH):
     fused = [G, P, P, P, i64, i64, P, P, P, P, P, ctypes.c_float, P, P, P, P, sz, P]
     lib.lci_prefill_fwd.argtypes = fused
     lib.lci_decode_fwd.argtypes = fused
+    lib.lci_decode_fwd_noalloc.argtypes = fused[:-3] + [P]
+    lib.lci_decode_fwd_noalloc.restype = ctypes.c_int
+    lib.lci_noalloc_scratch_bytes.restype = sz
     lib.lci_kv_append.argtypes = [G, P, P, P, P, P, P, P, P, P, P]
     lib.lci_sparse_attn_bwd.argtypes = [G, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P,
                                         P, sz, P]
@@ -292,7 +296,8 @@ def _gate_args(q, gate, mix):
 
 
 def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset, kv_len, K,
-           out, lse, idx_out, want_lse, want_idx, workspace, stream, block=1, sets=1):
+           out, lse, idx_out, want_lse, want_idx, workspace, stream, block=1, sets=1,
+           noalloc=False):
     import torch
     _dev(q_idx, torch.int8, "q_idx", 4)
     _dev(k_idx, torch.int8, "k_idx", 3)
@@ -323,12 +328,13 @@ def _fused(fn_name, entry, q_idx, k_idx, w, q, k, v, gate, mix, scale, q_offset,
     _dev(out, torch.bfloat16, "out", 4)
     _dev(lse, torch.float32, "lse", 3)
     _dev(idx_out, torch.int32, "idx_out", 3 if sets <= 1 else 4)
-    ws, nb = _workspace(entry, g, workspace, q.device)
     lib = load_library()
-    _check(getattr(lib, fn_name)(ctypes.byref(g), _ptr(q_idx), _ptr(k_idx), _ptr(w), wsb, wsq,
-                                 _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(mix), float(scale),
-                                 _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), nb,
-                                 _stream(stream)))
+    args = [ctypes.byref(g), _ptr(q_idx), _ptr(k_idx), _ptr(w), wsb, wsq, _ptr(q), _ptr(k),
+            _ptr(v), _ptr(gate), _ptr(mix), float(scale), _ptr(out), _ptr(lse), _ptr(idx_out)]
+    if not noalloc:
+        ws, nb = _workspace(entry, g, workspace, q.device)
+        args += [_ptr(ws), nb]
+    _check(getattr(lib, fn_name)(*args, _stream(stream)))
     res = [out]
     if idx_out is not None:
         res.append(idx_out)
@@ -357,6 +363,23 @@ def decode_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=N
     return _fused("lci_decode_fwd", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, mix, scale,
                   q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream,
                   block, sets)
+
+
+def decode_fwd_noalloc(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None,
+                       lse=None, idx_out=None, want_lse=False, want_idx=False, stream=None,
+                       mix=None, block=1, sets=1):
+    """``decode_fwd`` without a workspace: the library carves it out of its static
+    per-device scratch array (no device allocation inside the library; the
+    outputs are allocated here only when the caller passes none). Calls that
+    overlap on one GPU race on that array."""
+    return _fused("lci_decode_fwd_noalloc", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, mix,
+                  scale, q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, None,
+                  stream, block, sets, noalloc=True)
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static scratch array behind ``decode_fwd_noalloc``."""
+    return int(load_library().lci_noalloc_scratch_bytes())
 
 
 def kv_append(k_new, v_new, kI_new, k_cache, v_cache, kI_cache, kv_len, n_new=None,

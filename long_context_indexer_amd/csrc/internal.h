@@ -22,6 +22,10 @@ class KernelTimer {
   hipEvent_t start_ = nullptr;
 };
 
+// Records a failed HIP call as this thread's last HIP error (lci_last_hip_error)
+// and returns the library status for it (LCI_OK for hipSuccess).
+int hip_error_status(hipError_t e);
+
 struct Geom {
   int B, Tq, Tk, Hq, Hkv, d, H_I, d_I, K;
   const int32_t* q_offset;

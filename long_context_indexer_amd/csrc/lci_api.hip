@@ -138,6 +138,10 @@ PrefillLayout prefill_layout(const lci_geom* g) {
 
 }  // namespace
 
+namespace lci {
+int hip_error_status(hipError_t e) { return hip_status(e); }
+}  // namespace lci
+
 extern "C" {
 
 int lci_abi_version(void) { return LCI_ABI_VERSION; }
@@ -154,6 +158,9 @@ const char* lci_status_str(int s) {
     case LCI_ERR_WORKSPACE: return "LCI_ERR_WORKSPACE: workspace missing or too small";
     case LCI_ERR_HIP: return "LCI_ERR_HIP: a HIP call failed";
     case LCI_ERR_ALIGN: return "LCI_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case LCI_ERR_SCRATCH:
+      return "LCI_ERR_SCRATCH: the call needs more workspace than the allocation-free entry's "
+             "static scratch array holds";
     default: return "unknown lci status";
   }
 }

@@ -258,3 +258,27 @@ def test_dense_row_limit(lib):
     assert lim(lci.ENTRY_PREFILL, geom(B=2, Tq=8, Tk=4096, K=2048)) == 0        # few rows
     assert lim(lci.ENTRY_IDX_SCORE, g) == 0
     assert lim(lci.ENTRY_PREFILL, geom(d=96)) == 0                              # invalid
+
+
+def test_decode_noalloc_arguments(lib):
+    """The allocation-free decode refuses, before touching any device, a geometry
+    whose workspace exceeds its static scratch array, and passes every other
+    argument error through from the decode entry."""
+    SCRATCH = -8
+    cap = lib.lci_noalloc_scratch_bytes()
+    assert cap == 128 << 20
+
+    def call(g, q=FAKE):
+        return lib.lci_decode_fwd_noalloc(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, q, FAKE, FAKE,
+                                          FAKE, None, 0.1, FAKE, None, None, None)
+    big = geom(B=128, Tq=1, Tk=1 << 17, Hq=32, Hkv=4, K=2048)
+    assert lib.lci_workspace_bytes(lci.ENTRY_DECODE, ctypes.byref(big)) > cap
+    assert call(big) == SCRATCH
+    assert b"scratch" in lib.lci_status_str(SCRATCH)
+    for fits in (geom(B=64, Tq=1, Tk=1 << 17, Hq=32, Hkv=4, K=2048),
+                 geom(B=8, Tq=1, Tk=1 << 20, Hq=32, Hkv=4, K=2048)):
+        assert 0 < lib.lci_workspace_bytes(lci.ENTRY_DECODE, ctypes.byref(fits)) <= cap
+    assert call(geom(Tq=2)) == SHAPE                      # decode takes one row per sequence
+    assert call(geom(Tq=1), q=None) == NULL
+    assert lib.lci_decode_fwd_noalloc(None, FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, None,
+                                      0.1, FAKE, None, None, None) == NULL
