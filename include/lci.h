@@ -355,7 +355,10 @@ enum {
   LCI_KERNEL_BWD_DQ = 14,     /* backward: query gradients                           */
   LCI_KERNEL_BWD_TRANSPOSE = 15, /* backward: the rows that selected each position  */
   LCI_KERNEL_BWD_DKDV = 16,   /* backward: key and value gradients                   */
-  LCI_KERNEL_COUNT = 17
+  LCI_KERNEL_SEL_SCAN = 17,   /* long prefill: scores, sampled threshold, candidates */
+  LCI_KERNEL_SEL_ROWS = 18,   /* long prefill: exact Top-K of each row's candidates  */
+  LCI_KERNEL_SEL_FALLBACK = 19, /* long prefill: rows whose candidates fell short    */
+  LCI_KERNEL_COUNT = 20
 };
 int lci_kernel_timing(int enable);
 int lci_kernel_timing_read(int kernel, double *total_ms, int64_t *launches);

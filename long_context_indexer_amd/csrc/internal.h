@@ -77,6 +77,24 @@ hipError_t launch_topk_rows(const Geom& g, const int32_t* scores, int64_t score_
                             int row_begin, int row_count, int32_t* idx, int32_t* sel,
                             const DenseMasks* dm, hipStream_t stream);
 
+// ---- long-prefill scoring + Top-K without materialised score rows: one wave
+// per 16 query rows samples a threshold, lists the (score, position) pairs at
+// or above it, one workgroup per row selects exactly from its list, and rows
+// whose list cannot hold their Top-K are redone from their whole score row.
+// g: the geometry of one index set (H_I = that set's heads; w shared by every
+// row). Index rows are written at idx + (b*out_tq + i)*K.
+constexpr int kSelMaxTk = 131072;   // histories up to this long (row bit maps in LDS)
+constexpr int kSelMinRows = 8192;   // query rows per call at least
+struct SelLayout {
+  size_t cand, cnt, meta, nfb, fbrows, scratch, total;
+  int cap;
+  int64_t srow;
+};
+bool sel_supported(const Geom& g, int64_t wsb, int64_t wsq);
+SelLayout sel_layout(const Geom& g);
+hipError_t launch_sel(const Geom& g, const int8_t* q_idx, const int8_t* k_idx, const int8_t* w,
+                      int32_t* idx, int out_tq, void* workspace, hipStream_t stream);
+
 // ---- sparse attention over index rows
 size_t sparse_attn_workspace(const Geom& g, int splits);
 int sparse_attn_pick_splits(const Geom& g);

@@ -112,27 +112,41 @@ int prefill_chunk_rows(const lci_geom* g) {
 
 struct PrefillLayout {
   size_t idx_off, idx_bytes, score_off, score_bytes, attn_off, attn_bytes, qg_off, qg_bytes,
-      total;
+      sel_off, sel_bytes, total;
   int chunk_rows, splits;
+  bool sel;  // scores and Top-K by the long-prefill kernels (no score block)
 };
 
-PrefillLayout prefill_layout(const lci_geom* g) {
+// The geometry of one index set's scoring and selection: H_I/sets indexer heads.
+Geom set_geom(const lci_geom* g) {
+  Geom gs = to_geom(g);
+  gs.H_I = g->H_I / gs.sets;
+  return gs;
+}
+
+PrefillLayout prefill_layout(const lci_geom* g, int64_t wsb = 0, int64_t wsq = 0) {
   PrefillLayout L{};
   const Geom gg = attn_geom(g);
+  const Geom gs = set_geom(g);
+  L.sel = lci::sel_supported(gs, wsb, wsq);
   L.chunk_rows = prefill_chunk_rows(g);
   L.splits = lci::sparse_attn_pick_splits(gg);
   L.idx_off = 0;
   L.idx_bytes =
       align_up(static_cast<size_t>(g->B) * sel_sets(g) * g->Tq * gg.K * sizeof(int32_t));
   L.score_off = L.idx_off + L.idx_bytes;
-  L.score_bytes = align_up(static_cast<size_t>(g->B) * L.chunk_rows * g->Tk * sizeof(int32_t));
+  L.score_bytes =
+      L.sel ? 0
+            : align_up(static_cast<size_t>(g->B) * L.chunk_rows * g->Tk * sizeof(int32_t));
   L.attn_off = L.score_off + L.score_bytes;
   L.attn_bytes = align_up(lci::sparse_attn_workspace(gg, L.splits));
   // the query rows regrouped by index set
   L.qg_off = L.attn_off + L.attn_bytes;
   L.qg_bytes =
       sel_sets(g) > 1 ? align_up(static_cast<size_t>(g->B) * g->Tq * g->H_I * g->d_I) : 0;
-  L.total = L.qg_off + L.qg_bytes;
+  L.sel_off = L.qg_off + L.qg_bytes;
+  L.sel_bytes = L.sel ? align_up(lci::sel_layout(gs).total) : 0;
+  L.total = L.sel_off + L.sel_bytes;
   return L;
 }
 
@@ -180,7 +194,8 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
       if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK ||
           check_sets(g, true) != LCI_OK)
         return 0;
-      return prefill_layout(g).total;
+      // the weights' strides are not known here: enough for either scoring path
+      return std::max(prefill_layout(g, 0, 0).total, prefill_layout(g, 1, 1).total);
     case LCI_ENTRY_SPARSE_ATTN_BWD: {
       if (check_attention(g) != LCI_OK || sel_sets(g) > 1 || g->sets < 0) return 0;
       return lci::bwd_layout(attn_geom(g)).total;
@@ -190,7 +205,8 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
           check_sets(g, true) != LCI_OK)
         return 0;
       // block-granular or per-head-set decode runs the prefill path on its one row
-      if (sel_block(g) > 1 || sel_sets(g) > 1) return prefill_layout(g).total;
+      if (sel_block(g) > 1 || sel_sets(g) > 1)
+        return std::max(prefill_layout(g, 0, 0).total, prefill_layout(g, 1, 1).total);
       return lci::decode_layout(to_geom(g)).total;
     default:
       return 0;
@@ -286,7 +302,7 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
       !aligned16(v) || !aligned16(out) || (gate && !aligned16(gate)) ||
       (mix && !aligned16(mix)) || (lse && !aligned4(lse)) || (idx_out && !aligned4(idx_out)))
     return LCI_ERR_ALIGN;
-  const PrefillLayout L = prefill_layout(g);
+  const PrefillLayout L = prefill_layout(g, wsb, wsq);
   if (!workspace || ws_bytes < L.total) return LCI_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LCI_ERR_ALIGN;
   const Geom gg = to_geom(g);
@@ -304,8 +320,7 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   // heads (its rows of the regrouped query array, its weights) and its index
   // rows go to [B][sets][Tq][K*block] (the selection kernels address rows as
   // b*Tq' + row, so Tq' = sets*Tq and an offset of g*Tq rows place them)
-  Geom gs = gg;
-  gs.H_I = g->H_I / gg.sets;
+  const Geom gs = set_geom(g);
   Geom gsel = gg;
   gsel.Tq = g->Tq * gg.sets;
   const int8_t* qsrc = q_idx;
@@ -316,7 +331,16 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
     qsrc = qg;
   }
   const size_t qset = static_cast<size_t>(g->B) * g->Tq * gs.H_I * g->d_I;
-  for (int r0 = 0; r0 < g->Tq; r0 += L.chunk_rows) {
+  if (L.sel) {
+    // long prefill: scores never leave the chip
+    for (int set = 0; set < gg.sets; ++set) {
+      int32_t* iset = idx + static_cast<size_t>(set) * g->Tq * ga.K;
+      hipError_t e = lci::launch_sel(gs, qsrc + set * qset, k_idx, w + set * gs.H_I, iset,
+                                     g->Tq * gg.sets, ws + L.sel_off, st);
+      if (e != hipSuccess) return hip_status(e);
+    }
+  }
+  for (int r0 = 0; !L.sel && r0 < g->Tq; r0 += L.chunk_rows) {
     const int rc = std::min(L.chunk_rows, g->Tq - r0);
     for (int set = 0; set < gg.sets; ++set) {
       hipError_t e = lci::launch_idx_score(gs, qsrc + set * qset, k_idx, w + set * gs.H_I, wsb,
