@@ -9,7 +9,11 @@ namespace lci {
 
 // A query row takes the tile path when its causal history is at most
 // kDenseFactor * K positions long (it then keeps at least 1/kDenseFactor of it).
-constexpr int kDenseFactor = 4;
+// Measured on Prefill 64K (K = 2048): tiles cost about 17 ps per (row, causal
+// key) and a gathered row about 0.5 us, so they break even near 14.5 K causal
+// keys; the attention kernels together took 29.0, 26.9, 25.7, 25.2 and 25.6 ms
+// with factors 4, 8, 12, 16 and 20.
+constexpr int kDenseFactor = 16;
 constexpr int kDenseMaxWords = (kDenseFactor * 4096 + 31) / 32;
 
 int dense_block_rows(int G);

@@ -5,11 +5,11 @@
 // Attention", section 2 pseudocode: build a sparse mask from the Top-K
 // positions, then run attention under that mask) computes the same thing as
 // gathering the selected rows ("Hybrid Sparse Attention for Long-Context LLMs",
-// section "Indexer + Top-K ...", step 3). When a query row keeps a quarter or
-// more of its causal positions (always so for rows with p < K, where every
+// section "Indexer + Top-K ...", step 3). When a query row keeps a sixteenth
+// or more of its causal positions (always so for rows with p < K, where every
 // position is kept), streaming contiguous key/value tiles through LDS and
-// masking is much cheaper than gathering 2 KiB per selected position: each key
-// tile is loaded once for 4*32 query rows instead of once per row.
+// masking is cheaper than gathering 2 KiB per selected position: each key tile
+// is loaded once for 4*32 query rows instead of once per row.
 //
 // Two kernels:
 //   idx_mask_kernel  turns each index row into a bit mask over positions and a

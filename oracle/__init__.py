@@ -15,6 +15,10 @@ Parity status of each function (pins live in tests/test_oracle_pins.py):
   attention  pinned: dense causal attention from torch's SDPA when K >= p+1, K = 1,
              constant values, a two-key closed form, permutation invariance
   gate       pinned: G = 0 halves the output, G -> +inf leaves it, closed form
+  gradients  pinned: torch autograd (fp64) through independent statements of the
+             attention forward and of the indexer's distillation loss; closed
+             forms (constant values; a teacher equal to the scorer's own
+             distribution; one entry)
 """
 from __future__ import annotations
 
@@ -68,6 +72,8 @@ def open_library(path: str):
     lib.orc_kv_append.argtypes = [i32, i32, i32, i64, P, P, P, P, P, P]
     lib.orc_attn_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64,
                                  P, P, P, P, P]
+    lib.orc_indexer_bwd.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, i64, i64, P, P,
+                                    f64, P, P, P, P]
     lib.orc_num_threads.restype = i32
     return lib
 
@@ -224,6 +230,29 @@ class Oracle:
                               _p(dk), _p(dv), _p(dg), _p(dm))
         return dict(dq=dq, dk=dk, dv=dv, dgate=dg, dmix=dm)
 
+    def indexer_bwd(self, q_idx, k_idx, w, q_offset, kv_len, idx, teacher, tau):
+        """Gradients of the indexer's distillation loss over index rows idx int32
+        [B,Tq,K] with the teacher's weights teacher [B,Tq,K] (float) and score
+        scale tau. Returns dict(loss [B,Tq], dq [B,Tq,H_I,d_I], dk [B,Tk,d_I],
+        dw [B,Tq,H_I]) in float64 (dw per row; sum over rows for shared weights)."""
+        q_idx = _c(q_idx, np.int8)
+        k_idx = _c(k_idx, np.int8)
+        B, Tq, H_I, d_I = q_idx.shape
+        Tk = k_idx.shape[1]
+        w = _c(w, np.int8)
+        wsb, wsq = _w_strides(w, B, Tq, H_I)
+        idx = _c(idx, np.int32).reshape(B, Tq, -1)
+        K = idx.shape[2]
+        T = _c(teacher, np.float64).reshape(B, Tq, K)
+        loss = np.empty((B, Tq), np.float64)
+        dq = np.empty((B, Tq, H_I, d_I), np.float64)
+        dk = np.empty((B, Tk, d_I), np.float64)
+        dw = np.empty((B, Tq, H_I), np.float64)
+        self.lib.orc_indexer_bwd(B, Tq, Tk, H_I, d_I, K, _p(_c(q_offset, np.int32)),
+                                 _p(_c(kv_len, np.int32)), _p(q_idx), _p(k_idx), _p(w), wsb, wsq,
+                                 _p(idx), _p(T), float(tau), _p(loss), _p(dq), _p(dk), _p(dw))
+        return dict(loss=loss, dq=dq, dk=dk, dw=dw)
+
     def layer(self, inp, K, rows=None, gated=True, block=1, sets=1):
         """The whole layer (score -> Top-K -> attention -> gate) for the listed rows
         of an input dict as produced by ``synth.host_inputs``; an entry "mix" (the
@@ -336,3 +365,7 @@ def attention_bwd(*a, **k):
 
 def kv_append(*a, **k):
     return default().kv_append(*a, **k)
+
+
+def indexer_bwd(*a, **k):
+    return default().indexer_bwd(*a, **k)

@@ -284,7 +284,8 @@ void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, int sets, cons
     for (int64_t r = 0; r < nrows; ++r) {
         int b = row_b[r], i = row_i[r];
         int64_t qrow = (int64_t)b * Tq + i;
-        int64_t kvl = kv_len[b] < Tk ? kv_len[b] : Tk;
+        /* a history longer than its allocation is not a valid one: no entry is read */
+        int64_t kvl = kv_len[b] <= Tk ? kv_len[b] : 0;
         orc_attn_row(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
                      v + (int64_t)b * Tk * Hkv * d, kvl, idx + r * (int64_t)sets * K, K, sets,
                      gate ? gate + qrow * Hq * d : NULL, mix ? mix + qrow * Hq * d : NULL, scale,
@@ -419,7 +420,8 @@ void orc_attn_bwd(int B, int Tq, int Tk, int Hq, int Hkv, int d, int K, const in
     double *o = (double *)malloc((size_t)d * sizeof(double));
     double *dO = (double *)malloc((size_t)d * sizeof(double));
     for (int b = 0; b < B; ++b) {
-        int64_t kvl = kv_len[b] < Tk ? kv_len[b] : Tk;
+        /* a history longer than its allocation is not a valid one: no entry is read */
+        int64_t kvl = kv_len[b] <= Tk ? kv_len[b] : 0;
         const uint16_t *kb = k + (int64_t)b * Tk * Hkv * d, *vb = v + (int64_t)b * Tk * Hkv * d;
         for (int i = 0; i < Tq; ++i) {
             int64_t row = (int64_t)b * Tq + i;
@@ -492,6 +494,104 @@ void orc_attn_bwd(int B, int Tq, int Tk, int Hq, int Hkv, int d, int K, const in
     free(o);
     free(dP);
     free(P);
+}
+
+/* Gradients of the indexer's distillation loss (the training of the scorer:
+ * "How Fine-Grained Sparse Attention Reshapes Long-Context Architecture in
+ * Large Models", section "How Indexer + Top-K Works at Runtime" -- the
+ * indexer's selection distribution is distilled from a full-attention teacher;
+ * "Hybrid Sparse Attention for Long-Context LLMs", section "Engineering and
+ * Evaluation Recommendations", training side -- the scorer is trained jointly).
+ * The pages give no loss; the reading taken: for query row i with index row
+ * idx[i][0..K) (entries outside 0..p or past the history are skipped), the
+ * scorer's distribution is the softmax over the entries of z_t = tau * S_t,
+ *   S_t = sum_h w_h max(0, d_ht),  d_ht = qI[i,h] . kI[idx_t],
+ * the teacher's weights T_t (>= 0) are given per entry, and the loss is
+ *   L_i = sum_t T_t (log T_t - log p_t)   (0 log 0 = 0),
+ * the Kullback-Leibler divergence when T sums to 1. With q, k and w taken as
+ * real numbers (their int8 values) and the ReLU's derivative 0 at 0:
+ *   g_t = dL/dS_t = tau (p_t sum_u T_u - T_t),
+ *   dw[i,h] = sum_t g_t max(0, d_ht),
+ *   dq[i,h,:] = w_h sum_t g_t [d_ht > 0] kI[idx_t],
+ *   dk[idx_t,:] += g_t sum_h w_h [d_ht > 0] qI[i,h]   (over every row and entry).
+ * q_idx [B][Tq][H_I][d_I], k_idx [B][Tk][d_I], w at b*w_stride_b + i*w_stride_q
+ * (+h), idx and T [B][Tq][K]. Outputs (fp64, overwritten): loss [B][Tq] (NULL
+ * allowed), dq [B][Tq][H_I][d_I], dk [B][Tk][d_I], dw [B][Tq][H_I]. Invalid rows
+ * (p outside 0..kv_len-1, or kv_len > Tk) and rows without a valid entry give
+ * zeros. */
+void orc_indexer_bwd(int B, int Tq, int Tk, int H_I, int d_I, int K, const int32_t *q_offset,
+                     const int32_t *kv_len, const int8_t *q_idx, const int8_t *k_idx,
+                     const int8_t *w, int64_t w_stride_b, int64_t w_stride_q, const int32_t *idx,
+                     const double *T, double tau, double *loss, double *dq, double *dk,
+                     double *dw)
+{
+    memset(dk, 0, (size_t)B * Tk * d_I * sizeof(double));
+    double *z = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    int64_t *dd = (int64_t *)malloc((size_t)(K > 0 ? K : 1) * H_I * sizeof(int64_t));
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < Tq; ++i) {
+            int64_t row = (int64_t)b * Tq + i;
+            int64_t p = (int64_t)q_offset[b] + i;
+            const int8_t *qI = q_idx + row * H_I * d_I;
+            const int8_t *wr = w + b * w_stride_b + (int64_t)i * w_stride_q;
+            const int32_t *ir = idx + row * K;
+            const double *Tr = T + row * K;
+            double *dqr = dq + row * H_I * d_I;
+            double *dwr = dw + row * H_I;
+            for (int j = 0; j < H_I * d_I; ++j) dqr[j] = 0.0;
+            for (int h = 0; h < H_I; ++h) dwr[h] = 0.0;
+            if (loss) loss[row] = 0.0;
+            int valid_row = p >= 0 && p < kv_len[b] && kv_len[b] <= Tk;
+            if (!valid_row) continue;
+            /* scores of the entries (exact, int64) and the softmax of tau*S */
+            double m = -INFINITY;
+            for (int t = 0; t < K; ++t) {
+                int64_t s = ir[t];
+                if (s < 0 || s > p) { z[t] = -INFINITY; continue; }
+                int64_t S = 0;
+                for (int h = 0; h < H_I; ++h) {
+                    int64_t d = 0;
+                    for (int j = 0; j < d_I; ++j)
+                        d += (int64_t)qI[h * d_I + j] * (int64_t)k_idx[((int64_t)b * Tk + s) * d_I + j];
+                    dd[(int64_t)t * H_I + h] = d;
+                    S += (int64_t)wr[h] * (d > 0 ? d : 0);
+                }
+                z[t] = tau * (double)S;
+                if (z[t] > m) m = z[t];
+            }
+            if (m == -INFINITY) continue;   /* no valid entry */
+            double Z = 0.0, Tsum = 0.0;
+            for (int t = 0; t < K; ++t) {
+                if (z[t] == -INFINITY) continue;
+                Z += exp(z[t] - m);
+                Tsum += Tr[t];
+            }
+            double logZ = m + log(Z);
+            double L = 0.0;
+            for (int t = 0; t < K; ++t) {
+                if (z[t] == -INFINITY) continue;
+                double logp = z[t] - logZ;
+                double pt = exp(logp);
+                if (Tr[t] > 0.0) L += Tr[t] * (log(Tr[t]) - logp);
+                double g = tau * (pt * Tsum - Tr[t]);
+                int64_t s = ir[t];
+                const int8_t *kr = k_idx + ((int64_t)b * Tk + s) * d_I;
+                double *dkr = dk + ((int64_t)b * Tk + s) * d_I;
+                for (int h = 0; h < H_I; ++h) {
+                    int64_t d = dd[(int64_t)t * H_I + h];
+                    dwr[h] += g * (double)(d > 0 ? d : 0);
+                    if (d <= 0) continue;
+                    for (int j = 0; j < d_I; ++j) {
+                        dqr[h * d_I + j] += g * (double)wr[h] * (double)kr[j];
+                        dkr[j] += g * (double)wr[h] * (double)qI[h * d_I + j];
+                    }
+                }
+            }
+            if (loss) loss[row] = L;
+        }
+    }
+    free(dd);
+    free(z);
 }
 
 int orc_num_threads(void)

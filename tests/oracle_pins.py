@@ -351,6 +351,39 @@ def pin_attn_permutation_and_padding(orc):
     assert np.abs(l1 - l3).max() < 1e-14
 
 
+def pin_attn_history_past_allocation(orc):
+    """A history length beyond the allocated rows (kv_len > Tk) is not a valid
+    history (the library's validity rule: 0 <= p < kv_len <= Tk): attention over
+    it reads no entry, so the output is 0 (the gate's mix alone with a mix),
+    lse is -inf, and every gradient is 0, while the same rows with kv_len = Tk
+    give ordinary results."""
+    r = np.random.default_rng(36)
+    B, Tq, Tk, Hq, Hkv, d, K = 1, 3, 16, 2, 1, 8, 6
+    q = _rand_bf16(r, (B, Tq, Hq, d))
+    k, v = (_rand_bf16(r, (B, Tk, Hkv, d)) for _ in range(2))
+    G, x, dy = (_rand_bf16(r, (B, Tq, Hq, d)) for _ in range(3))
+    idx = np.stack([np.sort(r.choice(Tk, K, replace=False)) for _ in range(Tq)])[None]
+    idx = idx.astype(np.int32)
+    o, lse = orc.attention(q, k, v, None, idx.reshape(Tq, K), np.array([Tk + 1]), 0.3)
+    assert (o == 0).all() and np.isneginf(lse).all()
+    o_ok, lse_ok = orc.attention(q, k, v, None, idx.reshape(Tq, K), np.array([Tk]), 0.3)
+    assert np.isfinite(lse_ok).all() and np.abs(o_ok).max() > 0
+    om, _ = orc.attention(q, k, v, G, idx.reshape(Tq, K), np.array([Tk + 1]), 0.3, mix=x)
+    from scipy.special import expit
+    want = expit(-bf16_to_f32(G).astype(np.float64)) * bf16_to_f32(x).astype(np.float64)
+    assert np.abs(om - want.reshape(om.shape)).max() < 1e-12
+    g = orc.attention_bwd(q, k, v, G, idx, np.array([Tk + 1]), 0.3, dy, mix=x)
+    for name in ("dq", "dk", "dv"):
+        assert (g[name] == 0).all(), name
+    # o = 0: dgate = dy*(0 - x)*s*(1 - s), dmix = (1 - s)*dy
+    sg = expit(bf16_to_f32(G).astype(np.float64))
+    xf, dyf = (bf16_to_f32(a).astype(np.float64) for a in (x, dy))
+    assert np.abs(g["dgate"] - (-dyf * xf * sg * (1 - sg))).max() < 1e-12
+    assert np.abs(g["dmix"] - (1 - sg) * dyf).max() < 1e-12
+    g_ok = orc.attention_bwd(q, k, v, G, idx, np.array([Tk]), 0.3, dy, mix=x)
+    assert np.abs(g_ok["dq"]).max() > 0
+
+
 def pin_attn_mask_formulation(orc):
     """Page 5's form (scores over the whole cache, a sparse mask, masked softmax via
     torch) equals attention over the gathered rows."""
@@ -794,6 +827,118 @@ def pin_bwd_constant_values(orc):
     # dv summed over all rows = sum over rows and heads of dy (softmax weights sum to 1)
     tot = bf16_to_f32(dy).astype(np.float64).sum(axis=(0, 1, 2))
     assert np.abs(res["dv"].sum(axis=(0, 1, 2)) - tot).max() < 1e-12
+
+
+
+
+# ------------------------------------------------------- indexer gradients
+
+def _torch_indexer_loss(q, k, w, idx, T, q_offset, kv_len, tau):
+    """The distillation loss of the scorer written with torch ops on float64
+    tensors (independent of the oracle, for autograd): per row, log-softmax of
+    tau * sum_h w_h relu(q_h . k_s) over the row's valid entries, and
+    sum_t T_t (log T_t - log p_t)."""
+    import torch
+    B, Tq, H_I, d_I = q.shape
+    K = idx.shape[2]
+    total = torch.zeros((), dtype=torch.float64)
+    losses = torch.zeros((B, Tq), dtype=torch.float64)
+    for b in range(B):
+        for i in range(Tq):
+            p = int(q_offset[b]) + i
+            if not (0 <= p < int(kv_len[b]) <= k.shape[1]):
+                continue
+            ent = [t for t in range(K) if 0 <= int(idx[b, i, t]) <= p]
+            if not ent:
+                continue
+            pos = torch.tensor([int(idx[b, i, t]) for t in ent])
+            kk = k[b, pos]                                       # [n, d_I]
+            wr = w[b, i] if w.dim() == 3 else w
+            d = kk @ q[b, i].T                                   # [n, H_I]
+            S = (torch.relu(d) * wr).sum(-1)
+            logp = torch.log_softmax(tau * S, dim=0)
+            Tt = torch.tensor([float(T[b, i, t]) for t in ent], dtype=torch.float64)
+            logT = torch.where(Tt > 0, torch.log(torch.where(Tt > 0, Tt, torch.ones_like(Tt))),
+                               torch.zeros_like(Tt))
+            L = (Tt * (logT - logp)).sum()
+            losses[b, i] = L.detach()
+            total = total + L
+    return total, losses
+
+
+def pin_indexer_bwd_autograd(orc):
+    """The oracle's gradients of the scorer's distillation loss equal torch
+    autograd (fp64) through an independent statement of the loss: per-row
+    weights with negative values, -1 padding, entries past the row's position,
+    a repeated position, a row with no valid entry, an invalid row, and a
+    teacher that does not sum to 1."""
+    import torch
+    r = np.random.default_rng(80)
+    B, Tq, Tk, H_I, d_I, K = 2, 6, 40, 3, 8, 7
+    q = r.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.int8)
+    k = r.integers(-8, 9, size=(B, Tk, d_I)).astype(np.int8)
+    w = r.integers(-3, 5, size=(B, Tq, H_I)).astype(np.int8)
+    q_offset = np.array([20, 5], np.int32)
+    kv_len = np.array([40, 9], np.int32)               # sequence 1: rows 4, 5 invalid
+    idx = np.stack([np.stack([r.choice(Tk, K, replace=False) for _ in range(Tq)])
+                    for _ in range(B)]).astype(np.int32)
+    idx[0, 1, 4:] = -1
+    idx[0, 2, 3] = idx[0, 2, 0]                         # a repeated position: two entries
+    idx[0, 3, :] = 39                                   # past the row's position: none valid
+    T = r.random((B, Tq, K))
+    T /= T.sum(-1, keepdims=True)
+    T[0, 4] *= 1.7                                      # a teacher row that sums to 1.7
+    T[1, 0, 2] = 0.0                                    # a zero weight (0 log 0 = 0)
+    tau = 0.01
+    tq = torch.tensor(q.astype(np.float64), requires_grad=True)
+    tk = torch.tensor(k.astype(np.float64), requires_grad=True)
+    tw = torch.tensor(w.astype(np.float64), requires_grad=True)
+    total, losses = _torch_indexer_loss(tq, tk, tw, idx, T, q_offset, kv_len, tau)
+    total.backward()
+    res = orc.indexer_bwd(q, k, w, q_offset, kv_len, idx, T, tau)
+    assert np.abs(res["loss"] - losses.numpy()).max() < 1e-10
+    for name, leaf in (("dq", tq), ("dk", tk), ("dw", tw)):
+        want = leaf.grad.numpy()
+        assert np.abs(res[name] - want).max() <= 1e-10 * max(1.0, np.abs(want).max()), name
+
+
+def pin_indexer_bwd_closed_forms(orc):
+    """A teacher equal to the scorer's own distribution (softmax of tau*S from
+    numpy's scores and scipy's logsumexp) gives loss 0 and no gradient; a row
+    whose single entry holds all the teacher's weight likewise; shared [H_I]
+    weights give the same per-row dw as the same weights written out per row."""
+    from scipy.special import logsumexp
+    r = np.random.default_rng(81)
+    B, Tq, Tk, H_I, d_I, K = 1, 4, 30, 2, 8, 6
+    q = r.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.int8)
+    k = r.integers(-8, 9, size=(B, Tk, d_I)).astype(np.int8)
+    w = np.array([2, 3], np.int8)
+    q_offset, kv_len = np.array([25], np.int32), np.array([30], np.int32)
+    idx = np.stack([np.sort(r.choice(26, K, replace=False)) for _ in range(Tq)])[None]
+    idx = idx.astype(np.int32)
+    tau = 0.02
+    kk = k[0][idx[0]].astype(np.int64)                           # [Tq, K, d_I]
+    d = np.einsum("tkj,thj->tkh", kk, q[0].astype(np.int64))
+    S = (np.maximum(d, 0) * w.astype(np.int64)).sum(-1)          # [Tq, K]
+    z = tau * S
+    p = np.exp(z - logsumexp(z, axis=1, keepdims=True))
+    res = orc.indexer_bwd(q, k, w, q_offset, kv_len, idx, p[None], tau)
+    assert np.abs(res["loss"]).max() < 1e-12
+    for name in ("dq", "dk", "dw"):
+        assert np.abs(res[name]).max() < 1e-9, name
+    one = np.full((B, Tq, K), -1, np.int32)
+    one[..., 0] = idx[..., 0]
+    T1 = np.zeros((B, Tq, K))
+    T1[..., 0] = 1.0
+    res1 = orc.indexer_bwd(q, k, w, q_offset, kv_len, one, T1, tau)
+    for name in ("loss", "dq", "dk", "dw"):
+        assert np.abs(res1[name]).max() < 1e-15, name
+    T = r.random((B, Tq, K))
+    shared = orc.indexer_bwd(q, k, w, q_offset, kv_len, idx, T, tau)
+    per_row = orc.indexer_bwd(q, k, np.broadcast_to(w, (B, Tq, H_I)).copy(), q_offset, kv_len,
+                              idx, T, tau)
+    for name in ("loss", "dq", "dk", "dw"):
+        assert np.abs(shared[name] - per_row[name]).max() < 1e-12, name
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

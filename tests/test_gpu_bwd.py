@@ -72,9 +72,9 @@ def _case(orc, name):
         idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K)
         return cfg, inp, idx, True
     if name == "mixed_paths":
-        # rows past 4K (K = 64: p >= 256) and two out-of-order rows go to the
+        # rows past 16K (K = 64: p >= 1024) and two out-of-order rows go to the
         # gather kernels, the other token blocks to the tile kernels
-        cfg = MED.replace(Tq=520, Tk=520, K=64)
+        cfg = MED.replace(Tq=1300, Tk=1300, K=64)
         inp = synth.host_inputs(cfg, seed=65)
         idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K).copy()
         for i in (10, 130):

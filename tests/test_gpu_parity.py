@@ -196,8 +196,9 @@ FUSED_CASES = {
     "invalid_rows": (TINY.replace(B=2, Tq=20, Tk=100, K=8), dict(q_offset=[90, 0],
                                                                   kv_len=[100, 10])),
     # one split: the Top-K kernel writes the tile path's flags and masks; rows
-    # p < 256 keep everything, 256 <= p < 1024 take masked tiles, the rest gather
-    "tile_masks_from_topk": (MED.replace(Tq=2048, Tk=2048, K=256), {}),
+    # p < 64 keep everything, 64 <= p < 1024 take masked tiles (histories of at
+    # most 16 K), the rest gather
+    "tile_masks_from_topk": (MED.replace(Tq=2048, Tk=2048, K=64), {}),
     # histories no longer than 4K: every row, the empty ones included, is written
     # by the tile kernel and the gather kernel is not launched
     # the largest K, on rows that keep 68-72% of their history (tile path)

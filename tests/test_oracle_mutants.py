@@ -65,6 +65,16 @@ MUTANTS = [
     ("bwd_dk_unscaled", "dkr[j] += scale * dl * orc_bf16(q[hb + j]);", "dkr[j] += dl * orc_bf16(q[hb + j]);"),
     ("bwd_dv_ungated", "dvr[j] += P[t] * dO[j];", "dvr[j] += P[t] * orc_bf16(dy[hb + j]);"),
     ("bwd_dq_from_values", "dq[hb + j] += scale * dl * orc_bf16(kb[", "dq[hb + j] += scale * dl * orc_bf16(vb["),
+    ("history_clamped_to_allocation", "kv_len[b] <= Tk ? kv_len[b] : 0", "kv_len[b] < Tk ? kv_len[b] : Tk"),
+    ("ibwd_relu_mask_dropped", "                    if (d <= 0) continue;\n", ""),
+    ("ibwd_no_tau", "double g = tau * (pt * Tsum - Tr[t]);", "double g = (pt * Tsum - Tr[t]);"),
+    ("ibwd_sign", "double g = tau * (pt * Tsum - Tr[t]);", "double g = tau * (Tr[t] - pt * Tsum);"),
+    ("ibwd_teacher_mass_ignored", "double g = tau * (pt * Tsum - Tr[t]);", "double g = tau * (pt - Tr[t]);"),
+    ("ibwd_dk_without_weight", "dkr[j] += g * (double)wr[h] * (double)qI[h * d_I + j];",
+     "dkr[j] += g * (double)qI[h * d_I + j];"),
+    ("ibwd_dw_without_relu", "dwr[h] += g * (double)(d > 0 ? d : 0);", "dwr[h] += g * (double)d;"),
+    ("ibwd_entries_past_p", "if (s < 0 || s > p) { z[t] = -INFINITY; continue; }",
+     "if (s < 0) { z[t] = -INFINITY; continue; }"),
     ("overflow_unchecked", "if (acc > INT32_MAX) { acc = INT32_MAX; rc = ORC_OVERFLOW; }", ""),
 ]
 
