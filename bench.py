@@ -368,7 +368,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["prefill64k", "decode1m", "prefill8k", "decode128k",
-                                       "blocks", "sets", "backward"],
+                                       "blocks", "sets", "backward", "indexer_bwd"],
                     default=None, help="run one leg only (profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 2 GiB device buffer 5 times (HBM counter calibration runs)")
@@ -567,6 +567,39 @@ def main():
                     "10*d flops per (query head, selected key); forward recomputed inside",
                     kernels_us_per_step=us_per_step(kern))
 
+    def run_indexer_bwd(cfg, d):
+        """Gradients of the scorer's distillation loss for the Prefill-8K index rows
+        (from the fused forward) and seeded teacher weights (normalised per row)."""
+        free()
+        _, idx = lci.prefill_fwd(d["q_idx"], d["k_idx"], d["w"], d["q"], d["k"], d["v"],
+                                 d["gate"], cfg.scale, d["q_offset"], d["kv_len"], cfg.K,
+                                 want_idx=True, stream=stream)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(11)
+        T = torch.rand(idx.shape, generator=gen, device="cuda") ** 3
+        T /= T.sum(-1, keepdim=True)
+        geom = lci.make_geom(cfg.B, cfg.Tq, cfg.Tk, cfg.K, d["q_offset"], d["kv_len"],
+                             H_I=cfg.H_I, d_I=cfg.d_I)
+        ws = torch.empty(lci.workspace_bytes(lci.ENTRY_INDEXER_BWD, geom), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            lci.indexer_bwd(d["q_idx"], d["k_idx"], d["w"], idx, T, 0.002, d["q_offset"],
+                            d["kv_len"], workspace=ws, stream=stream)
+
+        steps = max(2, args.steps // 4)
+        step()
+        torch.cuda.synchronize()
+        ms_step, ev_ms, dist, kern = timed_region(timer, step, steps, lci)
+        pairs = pairs_of(cfg, row_positions(cfg))
+        log(f"prefill8k indexer gradients: {ms_step:.3f} ms/step ({pairs} entries)")
+        kernel_log_lines(kern)
+        return dict(workload="prefill8k", ms_per_step=ms_step, event_ms_per_step=ev_ms,
+                    step_ms=dist, steps=steps, entries=pairs,
+                    note="loss, dq_idx, dk_idx, dw of the scorer's distillation loss over the "
+                         "layer's index rows; teacher weights seeded, tau = 0.002",
+                    kernels_us_per_step=us_per_step(kern))
+
     res = {}
     want = (lambda leg: args.only in (None, leg))
     cpu, cpu_dec = None, None
@@ -599,7 +632,7 @@ def main():
 
     # ------------------------------------------------ Prefill 8K and its variants
     cfg8 = synth.CONFIGS["prefill8k"]
-    if any(want(x) for x in ("prefill8k", "blocks", "sets", "backward")):
+    if any(want(x) for x in ("prefill8k", "blocks", "sets", "backward", "indexer_bwd")):
         d8 = {k: dev(v) for k, v in synth.host_inputs(cfg8, seed=0).items()
               if isinstance(v, np.ndarray)}
         d8["scale"] = cfg8.scale
@@ -623,6 +656,8 @@ def main():
             res["sets"] = run_variant(cfg8, d8, 1, cfg8.K, cfg8.Hkv)
         if want("backward"):
             res["backward"] = run_backward(cfg8, d8)
+        if want("indexer_bwd"):
+            res["indexer_bwd"] = run_indexer_bwd(cfg8, d8)
         del d8
         free()
 
@@ -667,7 +702,7 @@ def main():
         "decode_queries_s": res["decode1m"]["queries_s"],
         "workloads": {k: res[k] for k in ("decode1m", "prefill8k", "decode128k") if k in res},
     }
-    for name in ("blocks", "sets", "backward"):
+    for name in ("blocks", "sets", "backward", "indexer_bwd"):
         if name in res:
             line[name] = res[name]
     print(json.dumps(line), flush=True)

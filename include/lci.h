@@ -105,7 +105,8 @@ enum {
     LCI_ENTRY_SPARSE_ATTN = 2,
     LCI_ENTRY_PREFILL = 3,
     LCI_ENTRY_DECODE = 4,
-    LCI_ENTRY_SPARSE_ATTN_BWD = 5
+    LCI_ENTRY_SPARSE_ATTN_BWD = 5,
+    LCI_ENTRY_INDEXER_BWD = 6
 };
 
 /* Indexer scoring (step 1). "Hybrid Sparse Attention ...", section "Indexer +
@@ -297,6 +298,45 @@ lci_status lci_sparse_attn_bwd(const lci_geom *g, const lci_bf16 *q, const lci_b
                                float *dq, float *dk, float *dv, float *dgate, float *dmix,
                                void *workspace, size_t ws_bytes, void *stream);
 
+/* Gradients of the scorer's distillation loss (the training of the indexer:
+ * "How Fine-Grained Sparse Attention Reshapes ...", section "How Indexer + Top-K
+ * Works at Runtime" -- the indexer's selection distribution is distilled from a
+ * full-attention teacher; "Hybrid Sparse Attention ...", section "Engineering
+ * and Evaluation Recommendations", training side). The pages give no loss; the
+ * reading taken: for query row i with index row idx[i] (entries outside 0..p
+ * skipped; each entry counts, a repeated position twice), the scorer's
+ * distribution is p_t = softmax_t(tau * S_t) over the entries, with S the
+ * indexer score of lci_idx_score, and the loss is
+ *   L_i = sum_t T_t (log T_t - log p_t)      (0 log 0 = 0; KL when T sums to 1).
+ * With q_idx, k_idx and w taken as real numbers (their int8 values) and the
+ * ReLU's derivative 0 at 0, g_t = tau (p_t sum_u T_u - T_t) and
+ *   dw[i,h] = sum_t g_t max(0, d_ht),  dq[i,h,:] = w_h sum_t g_t [d_ht > 0] k_idx[idx_t],
+ *   dk[s,:] = sum over entries with idx_t = s of g_t sum_h w_h [d_ht > 0] q_idx[i,h],
+ * d_ht = q_idx[i,h] . k_idx[idx_t].
+ *   q_idx, k_idx, w, strides: as in lci_idx_score (one index set: g->sets > 1 is
+ *            UNSUPPORTED)
+ *   idx      int32 [B, Tq, K*max(1, block)]: the entries (the index rows of the
+ *            forward, or any positions)
+ *   teacher  fp32 [B, Tq, K*max(1, block)]: the teacher's weights, >= 0, aligned
+ *            with idx (they need not sum to 1)
+ *   tau      the score scale of the scorer's softmax (finite, else SHAPE)
+ *   loss     fp32 [B, Tq] out, nullable
+ *   dq_idx   fp32 [B, Tq, H_I, d_I] out;  dk_idx fp32 [B, Tk, d_I] out (0 where no
+ *            entry points); dw fp32 [B, Tq, H_I] out (per row: for weights shared
+ *            by every row, their gradient is the sum over rows)
+ *   workspace at least lci_workspace_bytes(LCI_ENTRY_INDEXER_BWD): the dk
+ *            accumulator, 64-bit integers with 32 fraction bits (sums independent
+ *            of their order: deterministic); each element's sum must stay below
+ *            2^31 in size.
+ * Invalid rows and rows without a valid entry give zeros. Floating-point work is
+ * fp32 (the scores themselves are exact).
+ * Errors: NULL, SHAPE, UNSUPPORTED, OVERFLOW_RISK, WORKSPACE, ALIGN, HIP. */
+lci_status lci_indexer_bwd(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
+                           const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
+                           const int32_t *idx, const float *teacher, float tau, float *loss,
+                           float *dq_idx, float *dk_idx, float *dw, void *workspace,
+                           size_t ws_bytes, void *stream);
+
 /* Workspace bytes an entry needs for this geometry (host only, reads no device
  * memory). Returns 0 for an invalid geometry or entry id. */
 size_t lci_workspace_bytes(int entry, const lci_geom *g);
@@ -358,7 +398,8 @@ enum {
   LCI_KERNEL_SEL_SCAN = 17,   /* long prefill: scores, sampled threshold, candidates */
   LCI_KERNEL_SEL_ROWS = 18,   /* long prefill: exact Top-K of each row's candidates  */
   LCI_KERNEL_SEL_FALLBACK = 19, /* long prefill: rows whose candidates fell short    */
-  LCI_KERNEL_COUNT = 20
+  LCI_KERNEL_IBWD = 20,       /* gradients of the scorer's distillation loss        */
+  LCI_KERNEL_COUNT = 21
 };
 int lci_kernel_timing(int enable);
 int lci_kernel_timing_read(int kernel, double *total_ms, int64_t *launches);

@@ -10,7 +10,7 @@ the built library every call raises.
 
 Entry points (same names as the C ABI, without the ``lci_`` prefix):
     idx_score, topk_select, sparse_attn_fwd, prefill_fwd, decode_fwd, decode_fwd_noalloc,
-    kv_append, sparse_attn_bwd,
+    kv_append, sparse_attn_bwd, indexer_bwd,
     workspace_bytes, dense_row_limit, kernel_timing, kernel_timing_read, kernel_name
 """
 from __future__ import annotations
@@ -23,14 +23,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblci.so")
 
 (ENTRY_IDX_SCORE, ENTRY_TOPK_SELECT, ENTRY_SPARSE_ATTN, ENTRY_PREFILL, ENTRY_DECODE,
- ENTRY_SPARSE_ATTN_BWD) = range(6)
+ ENTRY_SPARSE_ATTN_BWD, ENTRY_INDEXER_BWD) = range(7)
 
 # LCI_ABI_VERSION of the signatures declared below
 ABI_VERSION = 3
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
            "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_workspace_bytes",
-           "lci_dense_row_limit", "lci_decode_fwd_noalloc", "lci_noalloc_scratch_bytes",
+           "lci_dense_row_limit", "lci_indexer_bwd", "lci_decode_fwd_noalloc", "lci_noalloc_scratch_bytes",
            "lci_status_str", "lci_last_hip_error",
            "lci_abi_version", "lci_kernel_timing", "lci_kernel_timing_read", "lci_kernel_name")
 
@@ -38,7 +38,7 @@ EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefi
 KERNELS = ("idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
            "dec_thresh", "dec_score", "dec_cand", "dec_resolve", "dec_compact", "kv_append",
            "kv_lengths", "bwd_prologue", "bwd_dq", "bwd_transpose", "bwd_dkdv", "sel_scan",
-           "sel_rows", "sel_fallback")
+           "sel_rows", "sel_fallback", "indexer_bwd")
 
 
 class LciError(RuntimeError):
@@ -81,6 +81,9 @@ def load_library(path: str = LIB_PATH):
     lib.lci_kv_append.argtypes = [G, P, P, P, P, P, P, P, P, P, P]
     lib.lci_sparse_attn_bwd.argtypes = [G, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P,
                                         P, sz, P]
+    lib.lci_indexer_bwd.argtypes = [G, P, P, P, i64, i64, P, P, ctypes.c_float, P, P, P, P, P,
+                                    sz, P]
+    lib.lci_indexer_bwd.restype = ctypes.c_int
     lib.lci_workspace_bytes.argtypes = [ctypes.c_int, G]
     lib.lci_workspace_bytes.restype = sz
     lib.lci_dense_row_limit.argtypes = [ctypes.c_int, G]
@@ -364,6 +367,38 @@ def decode_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=N
     return _fused("lci_decode_fwd", ENTRY_DECODE, q_idx, k_idx, w, q, k, v, gate, mix, scale,
                   q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream,
                   block, sets)
+
+
+def indexer_bwd(q_idx, k_idx, w, idx, teacher, tau, q_offset, kv_len, loss=True, workspace=None,
+                stream=None):
+    """Gradients of the scorer's distillation loss over index rows idx int32
+    [B,Tq,K] with the teacher's weights teacher fp32 [B,Tq,K] and score scale tau.
+    Returns dict(loss [B,Tq] or None, dq [B,Tq,H_I,d_I], dk [B,Tk,d_I], dw [B,Tq,H_I])."""
+    import torch
+    _dev(q_idx, torch.int8, "q_idx", 4)
+    _dev(k_idx, torch.int8, "k_idx", 3)
+    _dev(w, torch.int8, "w")
+    _dev(idx, torch.int32, "idx", 3)
+    _dev(teacher, torch.float32, "teacher", 3)
+    B, Tq, H_I, d_I = q_idx.shape
+    Tk = k_idx.shape[1]
+    K = idx.shape[2]
+    if tuple(idx.shape[:2]) != (B, Tq) or tuple(teacher.shape) != tuple(idx.shape) or \
+            tuple(k_idx.shape) != (B, Tk, d_I):
+        raise ValueError("inconsistent shapes")
+    wsb, wsq = _w_strides(w, B, Tq, H_I)
+    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, H_I=H_I, d_I=d_I)
+    dev = q_idx.device
+    out_loss = torch.empty((B, Tq), dtype=torch.float32, device=dev) if loss else None
+    dq = torch.empty((B, Tq, H_I, d_I), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, Tk, d_I), dtype=torch.float32, device=dev)
+    dw = torch.empty((B, Tq, H_I), dtype=torch.float32, device=dev)
+    ws, nb = _workspace(ENTRY_INDEXER_BWD, g, workspace, dev)
+    _check(load_library().lci_indexer_bwd(ctypes.byref(g), _ptr(q_idx), _ptr(k_idx), _ptr(w), wsb,
+                                          wsq, _ptr(idx), _ptr(teacher), float(tau),
+                                          _ptr(out_loss), _ptr(dq), _ptr(dk), _ptr(dw), _ptr(ws),
+                                          nb, _stream(stream)))
+    return dict(loss=out_loss, dq=dq, dk=dk, dw=dw)
 
 
 def decode_fwd_noalloc(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=None,

@@ -137,6 +137,13 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16
                                   float* dk, float* dv, float* dgate, float* dmix,
                                   void* workspace, hipStream_t stream);
 
+// ---- gradients of the scorer's distillation loss (g.K = index row length)
+size_t ibwd_workspace(const Geom& g);
+hipError_t launch_indexer_bwd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
+                              const int8_t* w, int64_t wsb, int64_t wsq, const int32_t* idx,
+                              const float* teacher, float tau, float* loss, float* dq, float* dk,
+                              float* dw, void* workspace, hipStream_t stream);
+
 // ---- appending rows to the key / value / indexer-key caches
 // Sizes from g: B, Tq (= rows of the new tensors per sequence), Tk (capacity),
 // Hkv, d, d_I; g.kv_len holds the current lengths.

@@ -200,6 +200,9 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
       if (check_attention(g) != LCI_OK || sel_sets(g) > 1 || g->sets < 0) return 0;
       return lci::bwd_layout(attn_geom(g)).total;
     }
+    case LCI_ENTRY_INDEXER_BWD:
+      if (check_indexer(g) != LCI_OK || sel_sets(g) > 1 || g->sets < 0) return 0;
+      return lci::ibwd_workspace(to_geom(g));
     case LCI_ENTRY_DECODE:
       if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK || g->Tq != 1 ||
           check_sets(g, true) != LCI_OK)
@@ -439,6 +442,34 @@ lci_status lci_sparse_attn_bwd(const lci_geom* g, const lci_bf16* q, const lci_b
   return hip_status(lci::launch_sparse_attn_bwd(ga, q, k, v, idx, gate, mix, dy, softmax_scale,
                                                 dq, dk, dv, dgate, dmix, workspace,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+lci_status lci_indexer_bwd(const lci_geom* g, const int8_t* q_idx, const int8_t* k_idx,
+                           const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
+                           const int32_t* idx, const float* teacher, float tau, float* loss,
+                           float* dq_idx, float* dk_idx, float* dw, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  lci_status s = check_base(g);
+  if (s != LCI_OK) return s;
+  if ((s = check_indexer(g)) != LCI_OK) return s;
+  if (g->sets < 0) return LCI_ERR_SHAPE;
+  if (sel_sets(g) > 1) return LCI_ERR_UNSUPPORTED;
+  if (!q_idx || !k_idx || !w || !idx || !teacher || !dq_idx || !dk_idx || !dw)
+    return LCI_ERR_NULL;
+  if (w_stride_b < 0 || w_stride_q < 0 || !(tau == tau) || tau == INFINITY || tau == -INFINITY)
+    return LCI_ERR_SHAPE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(dq_idx) || !aligned4(idx) ||
+      !aligned4(teacher) || !aligned4(dk_idx) || !aligned4(dw) || (loss && !aligned4(loss)))
+    return LCI_ERR_ALIGN;
+  Geom gg = to_geom(g);
+  gg.K = g->K * gg.block;  // index rows of K*block positions
+  if (static_cast<int64_t>(g->B) * g->Tk * g->d_I >= (int64_t(1) << 40)) return LCI_ERR_SHAPE;
+  const size_t need = lci::ibwd_workspace(gg);
+  if (!workspace || ws_bytes < need) return LCI_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LCI_ERR_ALIGN;
+  return hip_status(lci::launch_indexer_bwd(gg, q_idx, k_idx, w, w_stride_b, w_stride_q, idx,
+                                            teacher, tau, loss, dq_idx, dk_idx, dw, workspace,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 lci_status lci_kv_append(const lci_geom* g, const lci_bf16* k_new, const lci_bf16* v_new,

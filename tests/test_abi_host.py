@@ -252,7 +252,7 @@ def test_dense_row_limit(lib):
     def lim(entry, g):
         return lib.lci_dense_row_limit(entry, ctypes.byref(g))
     g = geom(B=1, Tq=65536, Tk=65536, Hq=32, Hkv=4, K=2048)
-    assert lim(lci.ENTRY_PREFILL, g) == lim(lci.ENTRY_SPARSE_ATTN, g) == 4 * 2048
+    assert lim(lci.ENTRY_PREFILL, g) == lim(lci.ENTRY_SPARSE_ATTN, g) == 16 * 2048
     assert lim(lci.ENTRY_PREFILL, geom(B=1, Tq=4096, Tk=4096, K=2048)) == 4096   # whole history
     assert lim(lci.ENTRY_DECODE, geom(B=64, Tq=1, Tk=1 << 17, K=2048)) == 0     # split-K decode
     assert lim(lci.ENTRY_PREFILL, geom(B=2, Tq=8, Tk=4096, K=2048)) == 0        # few rows
@@ -282,3 +282,22 @@ def test_decode_noalloc_arguments(lib):
     assert call(geom(Tq=1), q=None) == NULL
     assert lib.lci_decode_fwd_noalloc(None, FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, None,
                                       0.1, FAKE, None, None, None) == NULL
+
+
+def test_indexer_bwd_arguments(lib):
+    def call(g, q=FAKE, teacher=FAKE, tau=0.01, ws=FAKE, nb=None, dq=FAKE):
+        if nb is None:
+            nb = lib.lci_workspace_bytes(lci.ENTRY_INDEXER_BWD, ctypes.byref(g))
+        return lib.lci_indexer_bwd(ctypes.byref(g), q, FAKE, FAKE, 0, 0, FAKE, teacher, tau, None,
+                                   dq, FAKE, FAKE, ws, nb, None)
+    g = geom(B=2, Tq=16, Tk=300, H_I=8, d_I=64, K=32)
+    assert lib.lci_workspace_bytes(lci.ENTRY_INDEXER_BWD, ctypes.byref(g)) == 2 * 300 * 64 * 8
+    assert call(g, q=None) == NULL
+    assert call(g, teacher=None) == NULL
+    assert call(g, tau=float("inf")) == SHAPE
+    assert call(g, tau=float("nan")) == SHAPE
+    assert call(geom(H_I=32, d_I=64)) == OVF
+    assert call(geom(sets=2)) == UNSUP
+    assert call(g, nb=8) == WS
+    assert call(g, ws=None) == WS
+    assert call(g, dq=FAKE + 4) == ALIGN
