@@ -324,10 +324,11 @@ lci_status lci_sparse_attn_bwd(const lci_geom *g, const lci_bf16 *q, const lci_b
  *   dq_idx   fp32 [B, Tq, H_I, d_I] out;  dk_idx fp32 [B, Tk, d_I] out (0 where no
  *            entry points); dw fp32 [B, Tq, H_I] out (per row: for weights shared
  *            by every row, their gradient is the sum over rows)
- *   workspace at least lci_workspace_bytes(LCI_ENTRY_INDEXER_BWD): the dk
- *            accumulator, 64-bit integers with 32 fraction bits (sums independent
- *            of their order: deterministic); each element's sum must stay below
- *            2^31 in size.
+ *   workspace at least lci_workspace_bytes(LCI_ENTRY_INDEXER_BWD): g and the
+ *            heads' ReLU masks per entry, and the entries of each position. dk
+ *            sums its products as 64-bit integers with 32 fraction bits (the
+ *            sum does not depend on the order: deterministic); each element's
+ *            sum must stay below 2^31 in size. B*Tq*K < 2^31 (SHAPE).
  * Invalid rows and rows without a valid entry give zeros. Floating-point work is
  * fp32 (the scores themselves are exact).
  * Errors: NULL, SHAPE, UNSUPPORTED, OVERFLOW_RISK, WORKSPACE, ALIGN, HIP. */
@@ -398,8 +399,10 @@ enum {
   LCI_KERNEL_SEL_SCAN = 17,   /* long prefill: scores, sampled threshold, candidates */
   LCI_KERNEL_SEL_ROWS = 18,   /* long prefill: exact Top-K of each row's candidates  */
   LCI_KERNEL_SEL_FALLBACK = 19, /* long prefill: rows whose candidates fell short    */
-  LCI_KERNEL_IBWD = 20,       /* gradients of the scorer's distillation loss        */
-  LCI_KERNEL_COUNT = 21
+  LCI_KERNEL_IBWD = 20,       /* scorer's distillation loss: rows (loss, g, dq, dw)  */
+  LCI_KERNEL_IBWD_TRANSPOSE = 21, /* scorer's gradients: the entries of each position */
+  LCI_KERNEL_IBWD_DK = 22,    /* scorer's gradients: indexer-key gradients           */
+  LCI_KERNEL_COUNT = 23
 };
 int lci_kernel_timing(int enable);
 int lci_kernel_timing_read(int kernel, double *total_ms, int64_t *launches);

@@ -949,6 +949,18 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
+hipError_t launch_exclusive_scan(const int32_t* in, int64_t n, int32_t* out, int32_t* tiles,
+                                 hipStream_t st) {
+  const int ntiles = static_cast<int>((n + 1023) / 1024);
+  const uint32_t gk = static_cast<uint32_t>(std::min<int64_t>((n + 1 + 255) / 256, 8192));
+  hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<uint32_t>(ntiles)), dim3(256), 0, st, in,
+                     n, out, tiles);
+  hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(1024), 0, st, tiles, ntiles);
+  hipLaunchKernelGGL(scan_add_kernel, dim3(gk), dim3(256), 0, st, out, n, tiles, ntiles);
+  return hipGetLastError();
+}
+
+
 // [forward workspace][o bf16][lse][do][delta][counts][offsets (+1)][cursors][tiles (+1)][rows]
 BwdLayout bwd_layout(const Geom& g) {
   BwdLayout L{};

@@ -16,17 +16,21 @@
 //   dq[i,h,:] = w_h sum_t g_t [d_ht > 0] kI[idx_t],
 //   dk[s,:]  += g_t sum_h w_h [d_ht > 0] qI[i,h]   for every entry with idx_t = s.
 //
-//   ibwd_zero_kernel   clears the 32.32 fixed-point accumulator of dk.
 //   ibwd_row_kernel    one workgroup per query row: the entries' scores from the
 //                      int8 rows (v_dot4 over d_I, exact), the softmax of tau*S
-//                      and the loss (workgroup reductions in a fixed order), g;
-//                      dw reduced in a fixed order; dq by threads that each own a
-//                      head and four features and sum the entries in order; dk
-//                      contributions g_t * u_t (u_t = sum_h w_h [d_ht > 0] qI[i,h],
-//                      an exact integer vector) added to the accumulator as
-//                      64-bit integers (32 fraction bits): integer sums do not
-//                      depend on their order, so the result is deterministic.
-//   ibwd_dk_kernel     accumulator -> fp32 dk.
+//                      and the loss (workgroup reductions in a fixed order), g
+//                      and the heads' ReLU masks kept per entry for dk; dw
+//                      reduced in a fixed order; dq by threads that each own a
+//                      head and four features and sum the entries in order, the
+//                      entries' key rows staged in LDS 256 at a time.
+//   ibwd_count/fill    the transpose of the index rows: for each position, the
+//                      entries that point at it (counts, an exclusive scan,
+//                      then the entry numbers in any order).
+//   ibwd_dk_kernel     one wave per position: dk[s, j] (lane j) sums, over its
+//                      entries, g_t u_tj with u_t = sum_h w_h [d_ht > 0] qI[i,h]
+//                      (exact integers), each product rounded to 32 fraction bits
+//                      and added as a 64-bit integer: the sum does not depend
+//                      on the entries' order, so dk is deterministic.
 #include "common.h"
 #include "../../include/lci.h"
 #include "internal.h"
@@ -34,21 +38,7 @@
 namespace lci {
 
 constexpr int IB_NT = 256;
-constexpr double kIbFix = 4294967296.0;  // 2^32: fraction bits of the dk accumulator
-
-__global__ __launch_bounds__(256) void ibwd_zero_kernel(unsigned long long* __restrict__ acc,
-                                                        int64_t n) {
-  for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < n;
-       j += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    acc[j] = 0ull;
-}
-
-__global__ __launch_bounds__(256) void ibwd_dk_kernel(const unsigned long long* __restrict__ acc,
-                                                      float* __restrict__ dk, int64_t n) {
-  for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < n;
-       j += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    dk[j] = static_cast<float>(static_cast<double>(static_cast<long long>(acc[j])) / kIbFix);
-}
+constexpr double kIbFix = 4294967296.0;  // 2^32: fraction bits of the dk sums
 
 // Sum over the workgroup in a fixed order (wave shuffles, then the waves in order).
 __device__ __forceinline__ float ib_block_sum(float v, float* red) {
@@ -85,7 +75,7 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
     const int8_t* __restrict__ k_idx, const int8_t* __restrict__ w, int64_t wsb, int64_t wsq,
     const int32_t* __restrict__ idx, const float* __restrict__ teacher, float tau,
     float* __restrict__ loss, float* __restrict__ dq, float* __restrict__ dw,
-    unsigned long long* __restrict__ dk_acc) {
+    float* __restrict__ g_ent, uint16_t* __restrict__ m_ent) {
   static_assert(D_I % 16 == 0 && H_I * (D_I / 4) <= IB_NT, "thread mapping of dq");
   constexpr int NW = D_I / 4;  // int8 quads of a row
   static_assert(H_I <= 16, "16-bit head masks");
@@ -94,6 +84,7 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
   __shared__ __align__(16) int qrow[H_I * NW];
   __shared__ float red[IB_NT / 64];
   __shared__ float dwp[IB_NT / 64][H_I];
+  __shared__ __align__(16) int kst[IB_NT][NW];  // key rows of 256 entries (dq)
 
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -173,12 +164,13 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
   const float Z = ib_block_sum(zs, red);
   const float Tsum = ib_block_sum(ts, red);
   const float logZ = m + __logf(Z);
-  // 3. loss, g, dw partials and the dk contributions
+  // 3. loss, g and dw partials; g and the masks kept per entry for dk
   float lloc = 0.f;
   float dwl[H_I];
 #pragma unroll
   for (int h = 0; h < H_I; ++h) dwl[h] = 0.f;
-  unsigned long long* accb = dk_acc + static_cast<int64_t>(b) * Tk * D_I;
+  float* gr = g_ent + row * K;
+  uint16_t* mr = m_ent + row * K;
   for (int e = t; e < K; e += IB_NT) {
     const float z = gz[e];
     float g = 0.f;
@@ -188,32 +180,14 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
       const float te = Tr[e];
       if (te > 0.f) lloc += te * (__logf(te) - logp);
       g = tau * (pt * Tsum - te);
-      const int s = ir[e];
       int d[H_I];
-      dots(s, d);
+      dots(ir[e], d);
 #pragma unroll
       for (int h = 0; h < H_I; ++h) dwl[h] += g * static_cast<float>(max(d[h], 0));
-      // u = sum_h w_h [d_h > 0] q_h: exact integers; g*u into the accumulator
-      const uint32_t hm = hmask[e];
-      unsigned long long* ak = accb + static_cast<int64_t>(s) * D_I;
-      const double gf = static_cast<double>(g) * kIbFix;
-#pragma unroll 4
-      for (int j4 = 0; j4 < NW; ++j4) {
-        int u[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int h = 0; h < H_I; ++h) {
-          const int qw = (hm >> h) & 1u ? qrow[h * NW + j4] : 0;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) u[c] += wh[h] * static_cast<int>(static_cast<int8_t>(qw >> (8 * c)));
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (u[c] != 0)
-            atomicAdd(ak + 4 * j4 + c,
-                      static_cast<unsigned long long>(__double2ll_rn(gf * static_cast<double>(u[c]))));
-      }
     }
-    gz[e] = g;  // the same thread reads it back for dq after the barrier
+    gz[e] = g;  // the same thread reads it back below, after a barrier
+    gr[e] = g;
+    mr[e] = hmask[e];
   }
   const float L = ib_block_sum(lloc, red);
   if (loss && t == 0) loss[row] = L;
@@ -232,29 +206,245 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
     for (int wv = 0; wv < IB_NT / 64; ++wv) v += dwp[wv][t];
     dwr[t] = v;
   }
-  // 4. dq: thread (h, j4) of the first H_I*NW sums its head and four features
-  // over the entries in order
-  if (t < H_I * NW) {
-    const int h = t / NW, j4 = t % NW;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int e = 0; e < K; ++e) {
-      if (!((hmask[e] >> h) & 1u)) continue;
-      const float g = gz[e];
-      const int kw = *reinterpret_cast<const int*>(kb + static_cast<int64_t>(ir[e]) * D_I + 4 * j4);
+  // 4. dq: the threads split into SPLIT groups of H_I*NW; thread (h, j4) of
+  // group c sums its head and four features over the entries q = c (mod SPLIT)
+  // of each 256-entry chunk (key rows staged in LDS), in order; the groups'
+  // sums are added in group order at the end
+  constexpr int OWN = H_I * NW;
+  constexpr int SPLIT = IB_NT / OWN;
+  const int grp = t / OWN;
+  const int h = (t % OWN) / NW, j4 = t % NW;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int e0 = 0; e0 < K; e0 += IB_NT) {
+    const int e = e0 + t;
+    __syncthreads();  // the previous chunk is consumed
+    if (e < K && hmask[e] != 0) {
+      const int4* kr = reinterpret_cast<const int4*>(kb + static_cast<int64_t>(ir[e]) * D_I);
+#pragma unroll
+      for (int c = 0; c < NW / 4; ++c) *reinterpret_cast<int4*>(&kst[t][4 * c]) = kr[c];
+    }
+    __syncthreads();
+    const int n = min(IB_NT, K - e0);
+#pragma unroll 4
+    for (int q = grp; q < n; q += SPLIT) {
+      // masked entries contribute 0 (their key row slot may hold stale bytes)
+      const float g = ((hmask[e0 + q] >> h) & 1u) ? gz[e0 + q] : 0.f;
+      const int kw = g != 0.f ? kst[q][j4] : 0;
       a0 += g * static_cast<float>(static_cast<int8_t>(kw));
       a1 += g * static_cast<float>(static_cast<int8_t>(kw >> 8));
       a2 += g * static_cast<float>(static_cast<int8_t>(kw >> 16));
       a3 += g * static_cast<float>(static_cast<int8_t>(kw >> 24));
     }
-    const float wf = static_cast<float>(wh[h]);
-    *reinterpret_cast<float4*>(dqr + h * D_I + 4 * j4) = make_float4(wf * a0, wf * a1, wf * a2, wf * a3);
   }
+  __syncthreads();
+  float4* part = reinterpret_cast<float4*>(kst);  // reused: SPLIT x OWN partial sums
+  part[t] = make_float4(a0, a1, a2, a3);
+  __syncthreads();
+  if (t < OWN) {
+    float4 acc = part[t];
+#pragma unroll
+    for (int c = 1; c < SPLIT; ++c) {
+      const float4 v = part[c * OWN + t];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const float wf = static_cast<float>(wh[h]);
+    *reinterpret_cast<float4*>(dqr + h * D_I + 4 * j4) =
+        make_float4(wf * acc.x, wf * acc.y, wf * acc.z, wf * acc.w);
+  }
+}
+
+// counts of the valid entries per position (key b*Tk + s)
+__global__ __launch_bounds__(256) void ibwd_count_kernel(int Tq, int Tk, int K,
+                                                         const int32_t* __restrict__ q_offset,
+                                                         const int32_t* __restrict__ kv_len,
+                                                         const int32_t* __restrict__ idx,
+                                                         int64_t nent, int32_t* __restrict__ cnt) {
+  for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < nent; e += gridDim.x * 256LL) {
+    const int64_t row = e / K;
+    const int b = static_cast<int>(row / Tq);
+    const int64_t p = static_cast<int64_t>(q_offset[b]) + (row - static_cast<int64_t>(b) * Tq);
+    const int kvl = kv_len[b];
+    const int s = idx[e];
+    if (kvl <= Tk && p >= 0 && p < kvl && s >= 0 && s <= p)
+      atomicAdd(&cnt[static_cast<int64_t>(b) * Tk + s], 1);
+  }
+}
+
+__global__ __launch_bounds__(256) void ibwd_fill_kernel(int Tq, int Tk, int K,
+                                                        const int32_t* __restrict__ q_offset,
+                                                        const int32_t* __restrict__ kv_len,
+                                                        const int32_t* __restrict__ idx,
+                                                        int64_t nent,
+                                                        const int32_t* __restrict__ off,
+                                                        int32_t* __restrict__ cursor,
+                                                        int32_t* __restrict__ ents,
+                                                        int32_t* __restrict__ ekey) {
+  for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < nent; e += gridDim.x * 256LL) {
+    const int64_t row = e / K;
+    const int b = static_cast<int>(row / Tq);
+    const int64_t p = static_cast<int64_t>(q_offset[b]) + (row - static_cast<int64_t>(b) * Tq);
+    const int kvl = kv_len[b];
+    const int s = idx[e];
+    if (kvl <= Tk && p >= 0 && p < kvl && s >= 0 && s <= p) {
+      const int64_t key = static_cast<int64_t>(b) * Tk + s;
+      const int slot = off[key] + atomicAdd(&cursor[key], 1);
+      ents[slot] = static_cast<int32_t>(e);
+      ekey[slot] = static_cast<int32_t>(key);
+    }
+  }
+}
+
+// Entries grouped by position (the transpose), taken 64 at a time: a wave's
+// chunk of the list may span several positions, and a long list spans many
+// chunks. Lane k loads the metadata of entry k of the chunk (one coalesced
+// pass); then lane j (features j, j + 64) walks the chunk's entries in order,
+// EB at a time with every load of the group issued first, adding g_t u_tj
+// rounded to 32 fraction bits (exactly: g's mantissa times u in 64 bits, one
+// rounding shift) as 64-bit integers; when the position changes, and at the
+// end of the chunk, the sums go into the position's accumulator by integer
+// atomics. Integer sums do not depend on their order: deterministic.
+template <int H_I, int D_I>
+__global__ __launch_bounds__(256) void ibwd_dk_kernel(
+    int Tq, int K, const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w, int64_t wsb,
+    int64_t wsq, const int32_t* __restrict__ ents, const int32_t* __restrict__ ekey,
+    const float* __restrict__ g_ent, const uint16_t* __restrict__ m_ent,
+    unsigned long long* __restrict__ acc_dk, const int32_t* __restrict__ total) {
+  constexpr int JL = (D_I + 63) / 64;   // features per lane
+  const int64_t nlist = *total;         // the valid entries (the count total)
+  constexpr int EB = D_I > 64 ? 4 : 8;  // entries per load group
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nw = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  for (int64_t c0 = w0 * 64; c0 < nlist; c0 += nw * 64) {
+    const int n = static_cast<int>(min<int64_t>(64, nlist - c0));
+    // this lane's entry of the chunk
+    int my_row = 0, my_key = -1, my_hm = 0;
+    float my_g = 0.f;
+    if (lane < n) {
+      const int e = ents[c0 + lane];
+      my_row = e / K;
+      my_key = ekey[c0 + lane];
+      my_hm = m_ent[e];
+      my_g = g_ent[e];
+    }
+    long long acc[JL];
+#pragma unroll
+    for (int c = 0; c < JL; ++c) acc[c] = 0;
+    int cur = __shfl(my_key, 0, 64);
+    auto flush = [&](int key) {
+#pragma unroll
+      for (int c = 0; c < JL; ++c) {
+        const int j = lane + 64 * c;
+        if (j < D_I && acc[c] != 0)
+          atomicAdd(acc_dk + static_cast<int64_t>(key) * D_I + j, static_cast<unsigned long long>(acc[c]));
+        acc[c] = 0;
+      }
+    };
+    for (int k0 = 0; k0 < n; k0 += EB) {
+      // the group's entries are the same for every lane: scalar registers
+      int rowv[EB], hmv[EB], keyv[EB];
+      uint32_t gbits[EB];
+#pragma unroll
+      for (int k = 0; k < EB; ++k) {
+        const int src = min(k0 + k, 63);
+        rowv[k] = __builtin_amdgcn_readlane(my_row, src);
+        keyv[k] = k0 + k < n ? __builtin_amdgcn_readlane(my_key, src) : -1;
+        hmv[k] = k0 + k < n ? __builtin_amdgcn_readlane(my_hm, src) : 0;
+        gbits[k] = __builtin_amdgcn_readlane(__float_as_uint(my_g), src);
+      }
+      int8_t qv[EB][JL][H_I];
+#pragma unroll
+      for (int k = 0; k < EB; ++k) {
+        const int8_t* qr = q_idx + static_cast<int64_t>(rowv[k]) * H_I * D_I;
+#pragma unroll
+        for (int c = 0; c < JL; ++c)
+#pragma unroll
+          for (int hh = 0; hh < H_I; ++hh)
+            qv[k][c][hh] = lane + 64 * c < D_I ? qr[hh * D_I + lane + 64 * c] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < EB; ++k) {
+        if (keyv[k] < 0) break;  // past the chunk (uniform)
+        if (keyv[k] != cur) {   // a new position (uniform)
+          flush(cur);
+          cur = keyv[k];
+        }
+        const int row = rowv[k];
+        const int b = row / Tq;
+        const int i = row - b * Tq;
+        const int8_t* wr = w + b * wsb + static_cast<int64_t>(i) * wsq;
+        // weights of the heads whose ReLU passed this entry (uniform)
+        int wm[H_I];
+#pragma unroll
+        for (int hh = 0; hh < H_I; ++hh) wm[hh] = ((hmv[k] >> hh) & 1) ? static_cast<int>(wr[hh]) : 0;
+        // g = mant * 2^(ex - 150) exactly (fp32 bits), so g*u*2^32 is
+        // mant*u (exact in 64 bits) shifted right by 118 - ex, rounded
+        const uint32_t gb = gbits[k];
+        const int ex = static_cast<int>((gb >> 23) & 0xffu);
+        int mant = static_cast<int>(gb & 0x7fffffu) | (ex ? 0x800000 : 0);
+        if (gb >> 31) mant = -mant;
+        const int sh = 118 - (ex ? ex : 1);
+#pragma unroll
+        for (int c = 0; c < JL; ++c) {
+          int u = 0;
+#pragma unroll
+          for (int hh = 0; hh < H_I; ++hh) u += wm[hh] * static_cast<int>(qv[k][c][hh]);
+          const long long prod = static_cast<long long>(mant) * u;
+          long long add;
+          if (sh <= 0) add = prod << (-sh);
+          else if (sh > 62) add = 0;
+          else add = (prod + (1ll << (sh - 1))) >> sh;
+          acc[c] += add;
+        }
+      }
+    }
+    flush(cur);
+  }
+}
+
+__global__ __launch_bounds__(256) void ibwd_zero_u64_kernel(unsigned long long* __restrict__ p,
+                                                            int64_t n) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += gridDim.x * 256LL) p[i] = 0ull;
+}
+
+__global__ __launch_bounds__(256) void ibwd_dk_out_kernel(const unsigned long long* __restrict__ acc,
+                                                          float* __restrict__ dk, int64_t n) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += gridDim.x * 256LL)
+    dk[i] = static_cast<float>(static_cast<double>(static_cast<long long>(acc[i])) / kIbFix);
 }
 
 // ------------------------------------------------------------------ host side
 
-size_t ibwd_workspace(const Geom& g) {
-  return static_cast<size_t>(g.B) * g.Tk * g.d_I * sizeof(unsigned long long);
+struct IbwdLayout {
+  size_t g, m, cnt, off, cursor, tiles, ents, ekey, acc, total;
+};
+
+static IbwdLayout ibwd_layout(const Geom& g) {
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t nent = static_cast<size_t>(g.B) * g.Tq * g.K;
+  const size_t keys = static_cast<size_t>(g.B) * g.Tk;
+  IbwdLayout L{};
+  size_t o = 0;
+  L.g = o;      o += al(nent * sizeof(float));
+  L.m = o;      o += al(nent * sizeof(uint16_t));
+  L.cnt = o;    o += al(keys * sizeof(int32_t));
+  L.off = o;    o += al((keys + 1) * sizeof(int32_t));
+  L.cursor = o; o += al(keys * sizeof(int32_t));
+  L.tiles = o;  o += al(((keys + 1023) / 1024 + 1) * sizeof(int32_t));
+  L.ents = o;   o += al(nent * sizeof(int32_t));
+  L.ekey = o;   o += al(nent * sizeof(int32_t));
+  L.acc = o;    o += al(keys * g.d_I * sizeof(unsigned long long));
+  L.total = o;
+  return L;
+}
+
+size_t ibwd_workspace(const Geom& g) { return ibwd_layout(g).total; }
+
+__global__ __launch_bounds__(256) void ibwd_fill_i32_kernel(int32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += gridDim.x * 256LL) p[i] = 0;
 }
 
 template <int H_I, int D_I>
@@ -262,26 +452,51 @@ static hipError_t ibwd_launch_hd(const Geom& g, const int8_t* q_idx, const int8_
                                  const int8_t* w, int64_t wsb, int64_t wsq, const int32_t* idx,
                                  const float* teacher, float tau, float* loss, float* dq,
                                  float* dk, float* dw, void* ws, hipStream_t st) {
-  unsigned long long* acc = static_cast<unsigned long long*>(ws);
-  const int64_t n = static_cast<int64_t>(g.B) * g.Tk * g.d_I;
-  const int nb = static_cast<int>(std::min<int64_t>((n + 255) / 256, 8192));
-  {
-    KernelTimer timer(LCI_KERNEL_IBWD, st);
-    hipLaunchKernelGGL(ibwd_zero_kernel, dim3(nb), dim3(256), 0, st, acc, n);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const IbwdLayout L = ibwd_layout(g);
+  char* base = static_cast<char*>(ws);
+  float* g_ent = reinterpret_cast<float*>(base + L.g);
+  uint16_t* m_ent = reinterpret_cast<uint16_t*>(base + L.m);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt);
+  int32_t* off = reinterpret_cast<int32_t*>(base + L.off);
+  int32_t* cursor = reinterpret_cast<int32_t*>(base + L.cursor);
+  int32_t* tiles = reinterpret_cast<int32_t*>(base + L.tiles);
+  int32_t* ents = reinterpret_cast<int32_t*>(base + L.ents);
+  int32_t* ekey = reinterpret_cast<int32_t*>(base + L.ekey);
+  unsigned long long* acc = reinterpret_cast<unsigned long long*>(base + L.acc);
+  const int64_t keys = static_cast<int64_t>(g.B) * g.Tk;
+  const int64_t nent = static_cast<int64_t>(g.B) * g.Tq * g.K;
+  const uint32_t gk = static_cast<uint32_t>(std::min<int64_t>((keys + 255) / 256, 8192));
+  const uint32_t ge = static_cast<uint32_t>(std::min<int64_t>((nent + 255) / 256, 8192));
   const size_t lds = static_cast<size_t>(g.K) * (sizeof(float) + sizeof(uint16_t));
+  hipError_t e;
   {
     KernelTimer timer(LCI_KERNEL_IBWD, st);
     hipLaunchKernelGGL((ibwd_row_kernel<H_I, D_I>), dim3(static_cast<uint32_t>(g.B) * g.Tq),
                        dim3(IB_NT), lds, st, g.Tq, g.Tk, g.K, g.q_offset, g.kv_len, q_idx, k_idx,
-                       w, wsb, wsq, idx, teacher, tau, loss, dq, dw, acc);
+                       w, wsb, wsq, idx, teacher, tau, loss, dq, dw, g_ent, m_ent);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
-    KernelTimer timer(LCI_KERNEL_IBWD, st);
-    hipLaunchKernelGGL(ibwd_dk_kernel, dim3(nb), dim3(256), 0, st, acc, dk, n);
+    KernelTimer timer(LCI_KERNEL_IBWD_TRANSPOSE, st);
+    hipLaunchKernelGGL(ibwd_fill_i32_kernel, dim3(gk), dim3(256), 0, st, cnt, keys);
+    hipLaunchKernelGGL(ibwd_fill_i32_kernel, dim3(gk), dim3(256), 0, st, cursor, keys);
+    hipLaunchKernelGGL(ibwd_count_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K,
+                       g.q_offset, g.kv_len, idx, nent, cnt);
+    if ((e = launch_exclusive_scan(cnt, keys, off, tiles, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(ibwd_fill_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, g.q_offset,
+                       g.kv_len, idx, nent, off, cursor, ents, ekey);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    KernelTimer timer(LCI_KERNEL_IBWD_DK, st);
+    const int64_t nacc = keys * g.d_I;
+    const uint32_t ga = static_cast<uint32_t>(std::min<int64_t>((nacc + 255) / 256, 8192));
+    hipLaunchKernelGGL(ibwd_zero_u64_kernel, dim3(ga), dim3(256), 0, st, acc, nacc);
+    // the list holds the valid entries: as many as the count total off[keys]
+    const uint32_t gd = static_cast<uint32_t>(std::min<int64_t>((nent + 255) / 256, 8192));
+    hipLaunchKernelGGL((ibwd_dk_kernel<H_I, D_I>), dim3(gd), dim3(256), 0, st, g.Tq, g.K, q_idx,
+                       w, wsb, wsq, ents, ekey, g_ent, m_ent, acc, off + keys);
+    hipLaunchKernelGGL(ibwd_dk_out_kernel, dim3(ga), dim3(256), 0, st, acc, dk, nacc);
   }
   return hipGetLastError();
 }

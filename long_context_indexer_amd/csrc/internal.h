@@ -137,6 +137,11 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16
                                   float* dk, float* dv, float* dgate, float* dmix,
                                   void* workspace, hipStream_t stream);
 
+// Exclusive scan of n int32 counts: out[0..n) the prefix sums, out[n] the total;
+// tiles holds (n + 1023) / 1024 + 1 words of scratch.
+hipError_t launch_exclusive_scan(const int32_t* in, int64_t n, int32_t* out, int32_t* tiles,
+                                 hipStream_t stream);
+
 // ---- gradients of the scorer's distillation loss (g.K = index row length)
 size_t ibwd_workspace(const Geom& g);
 hipError_t launch_indexer_bwd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,

@@ -463,7 +463,10 @@ lci_status lci_indexer_bwd(const lci_geom* g, const int8_t* q_idx, const int8_t*
     return LCI_ERR_ALIGN;
   Geom gg = to_geom(g);
   gg.K = g->K * gg.block;  // index rows of K*block positions
-  if (static_cast<int64_t>(g->B) * g->Tk * g->d_I >= (int64_t(1) << 40)) return LCI_ERR_SHAPE;
+  // entries are numbered with int32
+  if (static_cast<int64_t>(g->B) * g->Tq * gg.K >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(g->B) * g->Tk >= (int64_t(1) << 31))
+    return LCI_ERR_SHAPE;
   const size_t need = lci::ibwd_workspace(gg);
   if (!workspace || ws_bytes < need) return LCI_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LCI_ERR_ALIGN;
