@@ -582,7 +582,7 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_tile_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ delta, const uint32_t* __restrict__ mask, int Wm,
     const uint8_t* __restrict__ done, float scale_log2, float scale, float* __restrict__ dk,
-    float* __restrict__ dv, int nkbs, int nblk, int nbps, int nch, int ch,
+    float* __restrict__ dv, int nkbs, int nblk, int nbps, int nch, int ch, int lim,
     float* __restrict__ part) {
   using C = DenseCfg<D, G>;
   constexpr int TW = C::TW;  // tokens per row tile
@@ -634,9 +634,11 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_tile_kernel(
   }
 
   // row tiles t (tokens t*TW ..): from the first whose last token sees key0
-  // to the last token inside the history
+  // to the last token inside the history that may take the tile path
+  // (p + 1 <= lim); key blocks at or past lim have no tile rows
   const int64_t i_first = max(static_cast<int64_t>(key0) - qo, int64_t(0));
-  const int64_t i_end = min(static_cast<int64_t>(Tq), static_cast<int64_t>(kvl) - qo);
+  const int64_t i_end = min(min(static_cast<int64_t>(Tq), static_cast<int64_t>(kvl) - qo),
+                            static_cast<int64_t>(lim) - qo);
   int t_first = static_cast<int>(i_first / TW);
   int t_last = i_end > i_first && key0 < kvl ? static_cast<int>((i_end - 1) / TW) : -1;
   if (nch > 1) {
@@ -835,7 +837,7 @@ __global__ __launch_bounds__(kDkdvThreads, 2) void bwd_dkdv_tile_kernel(
 template <int D, int G>
 __global__ __launch_bounds__(256) void bwd_part_sum_kernel(
     int B, int Tq, int Tk, int Hkv, const int32_t* __restrict__ q_offset,
-    const int32_t* __restrict__ kv_len, const float* __restrict__ part, int nch, int ch,
+    const int32_t* __restrict__ kv_len, const float* __restrict__ part, int nch, int ch, int lim,
     float* __restrict__ dk, float* __restrict__ dv) {
   constexpr int TW = 32 / G;
   const int64_t n = static_cast<int64_t>(B) * Tk * Hkv * D;
@@ -847,7 +849,8 @@ __global__ __launch_bounds__(256) void bwd_part_sum_kernel(
     const int kvl0 = kv_len[b];
     const int kvl = kvl0 <= Tk ? max(kvl0, 0) : 0;
     const int64_t i_first = max(static_cast<int64_t>(key0) - qo, int64_t(0));
-    const int64_t i_end = min(static_cast<int64_t>(Tq), static_cast<int64_t>(kvl) - qo);
+    const int64_t i_end = min(min(static_cast<int64_t>(Tq), static_cast<int64_t>(kvl) - qo),
+                              static_cast<int64_t>(lim) - qo);
     const int t_first = static_cast<int>(i_first / TW);
     const int t_last = i_end > i_first && key0 < kvl ? static_cast<int>((i_end - 1) / TW) : -1;
     float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
@@ -903,18 +906,21 @@ hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, co
     const int64_t nwg = static_cast<int64_t>((nblk + per - 1) / per) * 8;
     const int ntw = (g.Tq + C::TW - 1) / C::TW;
     const int ch = (ntw + nch - 1) / nch;
-    KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
-    hipLaunchKernelGGL((bwd_dkdv_tile_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)),
-                       dim3(kDkdvThreads), 0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len, q, k, v,
-                       dO, lse, dlt, dm->mask, dm->Wm, dm->done, scale * LOG2E, scale, dk, dv,
-                       nkbs, nblk, nbps, nch, ch, part);
+    {
+      KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
+      hipLaunchKernelGGL((bwd_dkdv_tile_kernel<D, G>), dim3(static_cast<uint32_t>(nwg)),
+                         dim3(kDkdvThreads), 0, st, g.Tq, g.Tk, g.Hq, g.Hkv, g.q_offset, g.kv_len,
+                         q, k, v, dO, lse, dlt, dm->mask, dm->Wm, dm->done, scale * LOG2E, scale,
+                         dk, dv, nkbs, nblk, nbps, nch, ch, dm->lim, part);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nch > 1) {
       const int64_t n4 = static_cast<int64_t>(g.B) * g.Tk * g.Hkv * D / 4;
+      KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);  // the partial sum
       hipLaunchKernelGGL((bwd_part_sum_kernel<D, G>),
                          dim3(static_cast<uint32_t>(std::min<int64_t>((n4 + 255) / 256, 8192))),
                          dim3(256), 0, st, g.B, g.Tq, g.Tk, g.Hkv, g.q_offset, g.kv_len, part,
-                         nch, ch, dk, dv);
+                         nch, ch, dm->lim, dk, dv);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }

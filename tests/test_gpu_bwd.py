@@ -80,11 +80,42 @@ def _case(orc, name):
         for i in (10, 130):
             idx[0, i, :i + 1] = r.permutation(idx[0, i, :i + 1])
         return cfg, inp, idx, True
+    if name == "g1_d64":
+        # one query head per key/value head
+        cfg = TINY.replace(Hq=4, Hkv=4, d=64, Tq=150, Tk=220, K=40)
+        inp = synth.host_inputs(cfg, seed=67)
+        inp["q_offset"] = np.array([70], np.int32)
+        idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K)
+        return cfg, inp, idx, True
+    if name == "decode_splits":
+        # eight one-row sequences with K >= 128: the forward splits each row's
+        # entries, no row takes the tile path, and the gather kernels write dk,
+        # dv without a tile pass before them
+        cfg = MED.replace(B=8, Tq=1, Tk=4096, K=256, n_needles=0, needles="none")
+        inp = synth.host_inputs(cfg, seed=68)
+        inp["kv_len"] = np.array([4096, 3000, 17, 256, 257, 4000, 1, 2048], np.int32)
+        inp["q_offset"] = inp["kv_len"] - 1
+        idx = synth.index_rows(inp["q_offset"], inp["kv_len"], cfg.Tq, cfg.K, seed=68)
+        return cfg, inp, idx, True
+    if name == "one_chunk_long_history":
+        # partial dk, dv of two or more row chunks would take more than 1 GiB
+        # (B Tk Hkv d = 136001 * 4 * 128 floats, twice, per chunk): one chunk,
+        # the tile kernel writes dk, dv itself, zeros for every key block past
+        # the tile rows; rows 1024.. (p + 1 > 16 K) take the gather kernels
+        cfg = MED.replace(Tq=1100, Tk=136001, K=64, n_needles=0, needles="none")
+        inp = synth.host_inputs(cfg, seed=69)
+        idx = synth.index_rows(inp["q_offset"], inp["kv_len"], cfg.Tq, cfg.K, seed=69)
+        return cfg, inp, idx, True
     raise KeyError(name)
 
 
 CASES = ["med_gate_mix", "tiny_scrambled_ungated", "g16_gate", "d64_g2_two_sequences",
-         "mixed_paths"]
+         "mixed_paths", "g1_d64", "decode_splits", "one_chunk_long_history"]
+
+# launches of (bwd_dq, bwd_dkdv) per call where the case is there to reach a
+# particular arrangement: no tile dq pass (split rows), no partial-sum pass
+# (one chunk)
+LAUNCHES = {"decode_splits": (1, 1), "one_chunk_long_history": (2, 2), "med_gate_mix": (2, 3)}
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -98,9 +129,14 @@ def test_sparse_attn_bwd(lci, orc, name):
     log(f"bwd {name}: B={cfg.B} Tq={cfg.Tq} Tk={cfg.Tk} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} "
         f"K={idx.shape[2]} gated={gated} mix={mix is not None}")
     d = to_device(inp)
+    lci.kernel_timing(True)
     res = lci.sparse_attn_bwd(d["q"], d["k"], d["v"], dev(idx), dev(gate), inp["scale"],
                               d["kv_len"], dev(dy), mix=dev(mix))
     torch.cuda.synchronize()
+    launches = (lci.kernel_timing_read("bwd_dq")[1], lci.kernel_timing_read("bwd_dkdv")[1])
+    lci.kernel_timing(False)
+    if name in LAUNCHES:
+        assert launches == LAUNCHES[name], launches
     want = orc.attention_bwd(inp["q"], inp["k"], inp["v"], gate, idx, inp["kv_len"],
                              inp["scale"], dy, mix=mix)
     for key in ("dq", "dk", "dv", "dgate", "dmix"):
@@ -144,3 +180,36 @@ def test_sparse_attn_bwd_prefill8k_sampled(lci, orc):
         _close(got["dgate"][:, rows], want["dgate"], f"8k {tag} dgate")
     _close(got["dk"][:, s0:], want["dk"][:, s0:], f"8k keys {s0}.. dk")
     _close(got["dv"][:, s0:], want["dv"][:, s0:], f"8k keys {s0}.. dv")
+
+
+def test_sparse_attn_bwd_prefill8k_chunk_seams(lci, orc):
+    """dk and dv summed across the row chunks of the tile kernel at the full
+    Prefill-8K size: keys 64..127 are selected only by 64 rows spread over
+    every chunk (the other rows drop them and pad with -1, still ascending and
+    tile-eligible), so the oracle on those 64 rows gives their whole sums."""
+    import torch
+    cfg = synth.CONFIGS["prefill8k"]
+    inp = synth.host_inputs(cfg, seed=70)
+    idx = synth.index_rows(inp["q_offset"], inp["kv_len"], cfg.Tq, cfg.K, seed=70)
+    lo, hi = 64, 128
+    S = np.linspace(128, cfg.Tq - 1, 64).astype(np.int64)
+    keep = np.zeros(cfg.Tq, bool)
+    keep[S] = True
+    for i in np.flatnonzero(~keep):
+        row = idx[0, i]
+        v = row[(row >= 0) & ((row < lo) | (row >= hi))]
+        row[:] = -1
+        row[:v.size] = v
+    assert all(((idx[0, i] >= lo) & (idx[0, i] < hi)).any() for i in S)
+    r = np.random.default_rng(71)
+    dy = synth.bf16_bits(r.standard_normal((cfg.B, cfg.Tq, cfg.Hq, cfg.d), dtype=np.float32))
+    log("bwd prefill8k chunk seams: keys 64..127 from 64 rows across every chunk")
+    d = to_device(inp)
+    res = lci.sparse_attn_bwd(d["q"], d["k"], d["v"], dev(idx), d["gate"], inp["scale"],
+                              d["kv_len"], dev(dy))
+    torch.cuda.synchronize()
+    want = orc.attention_bwd(inp["q"][:, S], inp["k"], inp["v"], inp["gate"][:, S],
+                             idx[:, S], inp["kv_len"], inp["scale"], dy[:, S])
+    _close(host(res["dq"])[:, S], want["dq"], "8k seam rows dq")
+    _close(host(res["dk"])[:, lo:hi], want["dk"][:, lo:hi], f"8k keys {lo}..{hi - 1} dk")
+    _close(host(res["dv"])[:, lo:hi], want["dv"][:, lo:hi], f"8k keys {lo}..{hi - 1} dv")
