@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define LCI_ABI_VERSION 3
+#define LCI_ABI_VERSION 4
 
 typedef uint16_t lci_bf16;
 
@@ -200,7 +200,9 @@ lci_status lci_prefill_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t 
                            size_t ws_bytes, void *stream);
 
 /* Fused decode: one query row per sequence (Tq == 1) over a long history, with
- * the history split across workgroups for scoring, an exact two-level Top-K
+ * the history split across workgroups for scoring, an exact Top-K taken from
+ * the list of positions at or above a threshold estimated from every 32nd
+ * score (a whole-row selection where that list falls short of K or overflows),
  * and split-K attention combined in a fixed order ("How Fine-Grained Sparse
  * Attention Reshapes ...", section "Engineering Practices": per-step decode
  * work decoupled from context length). Same arguments and results as
@@ -225,7 +227,7 @@ lci_status lci_decode_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *
  * device looks up that device's copy (hipGetSymbolAddress). A geometry whose
  * lci_workspace_bytes(LCI_ENTRY_DECODE) exceeds the array returns
  * LCI_ERR_SCRATCH and enqueues nothing (Decode 128K, 64 x 131072 positions,
- * and Decode 1M, 8 x 1048576, both fit: about 14 B per history position plus
+ * and Decode 1M, 8 x 1048576, both fit: about 12 B per history position plus
  * the split-K partials). Every call on one GPU uses the same array: calls that
  * overlap on one GPU (other streams, other threads) race and must be ordered
  * by the caller. The array keeps the last call's contents; the decode kernels
@@ -385,24 +387,23 @@ enum {
   LCI_KERNEL_ATTN_DENSE = 3,  /* masked attention over contiguous key tiles          */
   LCI_KERNEL_ATTN_GATHER = 4, /* attention over gathered selected keys              */
   LCI_KERNEL_ATTN_COMBINE = 5,/* fixed-order merge of split-K partial results        */
-  LCI_KERNEL_DEC_THRESH = 6,  /* decode: histogram bin of the K-th largest score    */
-  LCI_KERNEL_DEC_SCORE = 7,   /* decode: scores + score histogram per history chunk */
-  LCI_KERNEL_DEC_CAND = 8,    /* decode: candidates at or above the threshold bin   */
-  LCI_KERNEL_DEC_RESOLVE = 9, /* decode: exact K-th score among the candidates      */
-  LCI_KERNEL_DEC_COMPACT = 10,/* decode: ordered compaction of the selected positions*/
-  LCI_KERNEL_KV_APPEND = 11,  /* new rows into the key/value/indexer-key caches     */
-  LCI_KERNEL_KV_LENGTHS = 12, /* new cache lengths and first positions after append */
-  LCI_KERNEL_BWD_PROLOGUE = 13, /* backward: output gradient through the gate, delta */
-  LCI_KERNEL_BWD_DQ = 14,     /* backward: query gradients                           */
-  LCI_KERNEL_BWD_TRANSPOSE = 15, /* backward: the rows that selected each position  */
-  LCI_KERNEL_BWD_DKDV = 16,   /* backward: key and value gradients                   */
-  LCI_KERNEL_SEL_SCAN = 17,   /* long prefill: scores, sampled threshold, candidates */
-  LCI_KERNEL_SEL_ROWS = 18,   /* long prefill: exact Top-K of each row's candidates  */
-  LCI_KERNEL_SEL_FALLBACK = 19, /* long prefill: rows whose candidates fell short    */
-  LCI_KERNEL_IBWD = 20,       /* scorer's distillation loss: rows (loss, g, dq, dw)  */
-  LCI_KERNEL_IBWD_TRANSPOSE = 21, /* scorer's gradients: the entries of each position */
-  LCI_KERNEL_IBWD_DK = 22,    /* scorer's gradients: indexer-key gradients           */
-  LCI_KERNEL_COUNT = 23
+  LCI_KERNEL_DEC_SAMPLE = 6,  /* decode: histogram of every 32nd position's score  */
+  LCI_KERNEL_DEC_THRESH = 7,  /* decode: the candidate threshold from the histogram */
+  LCI_KERNEL_DEC_SCORE = 8,   /* decode: every score; candidates at the threshold   */
+  LCI_KERNEL_DEC_SELECT = 9,  /* decode: exact Top-K of the candidates (or the row) */
+  LCI_KERNEL_KV_APPEND = 10,  /* new rows into the key/value/indexer-key caches     */
+  LCI_KERNEL_KV_LENGTHS = 11, /* new cache lengths and first positions after append */
+  LCI_KERNEL_BWD_PROLOGUE = 12, /* backward: output gradient through the gate, delta */
+  LCI_KERNEL_BWD_DQ = 13,     /* backward: query gradients                           */
+  LCI_KERNEL_BWD_TRANSPOSE = 14, /* backward: the rows that selected each position  */
+  LCI_KERNEL_BWD_DKDV = 15,   /* backward: key and value gradients                   */
+  LCI_KERNEL_SEL_SCAN = 16,   /* long prefill: scores, sampled threshold, candidates */
+  LCI_KERNEL_SEL_ROWS = 17,   /* long prefill: exact Top-K of each row's candidates  */
+  LCI_KERNEL_SEL_FALLBACK = 18, /* long prefill: rows whose candidates fell short    */
+  LCI_KERNEL_IBWD = 19,       /* scorer's distillation loss: rows (loss, g, dq, dw)  */
+  LCI_KERNEL_IBWD_TRANSPOSE = 20, /* scorer's gradients: the entries of each position */
+  LCI_KERNEL_IBWD_DK = 21,    /* scorer's gradients: indexer-key gradients           */
+  LCI_KERNEL_COUNT = 22
 };
 int lci_kernel_timing(int enable);
 int lci_kernel_timing_read(int kernel, double *total_ms, int64_t *launches);

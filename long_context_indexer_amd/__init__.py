@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(HERE, "liblci.so")
  ENTRY_SPARSE_ATTN_BWD, ENTRY_INDEXER_BWD) = range(7)
 
 # LCI_ABI_VERSION of the signatures declared below
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
            "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_workspace_bytes",
@@ -36,7 +36,7 @@ EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefi
 
 # kernel kinds of the timing log (LCI_KERNEL_* in lci.h)
 KERNELS = ("idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
-           "dec_thresh", "dec_score", "dec_cand", "dec_resolve", "dec_compact", "kv_append",
+           "dec_sample", "dec_thresh", "dec_score", "dec_select", "kv_append",
            "kv_lengths", "bwd_prologue", "bwd_dq", "bwd_transpose", "bwd_dkdv", "sel_scan",
            "sel_rows", "sel_fallback", "ibwd_rows", "ibwd_transpose", "ibwd_dk")
 

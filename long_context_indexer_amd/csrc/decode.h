@@ -5,13 +5,14 @@
 
 namespace lci {
 
-constexpr int kDecChunk = 4096;      // history positions per scoring / compaction workgroup
+constexpr int kDecChunk = 4096;      // history positions per scoring workgroup
 constexpr int kDecCap = 8192;        // candidates per sequence resolved in LDS
 constexpr int kDecMaxChunks = 8192;  // history of at most 2^25 positions
 
 struct DecLayout {
-  size_t scores, hist, chist, ncand, cand, ngt, off, thr, bsel, idx, attn, total;
-  int nchunks, splits;
+  size_t scores, fhist, chist, ncand, cand, thr, idx, attn, total;
+  int nchunks, splits, ss;
+  int nsw;  // sample workgroups per sequence
 };
 
 DecLayout decode_layout(const Geom& g);

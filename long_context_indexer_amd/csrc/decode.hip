@@ -8,26 +8,30 @@
 // the decode step is bound by HBM: L*d_I bytes of indexer keys plus K rows of
 // keys and values per query.
 //
-// With one query per sequence the parallelism comes from splitting the history:
-//   dec_score    (chunks x B) int8-MFMA scores of 4096 positions per workgroup,
-//                written to workspace, and the chunk's 2048-bin histogram over a
-//                monotone float-like binning of the int32 score (exponent + 5
-//                mantissa bits, both signs), built in LDS and stored whole;
-//   dec_thresh   (B) sums the chunk histograms, then finds the bin b* holding
-//                the K-th largest score and the count of positions above it;
-//   dec_cand     (chunks x B) every workgroup counts its positions above b*
-//                and writes the (score, position) pairs inside b* to its own
-//                slice of the sequence's candidate list;
-//   dec_resolve  (B) gathers the candidate slices, selects the exact K-th score v* and
-//                the position cut s* that keeps the lowest-position ties, then
-//                turns per-chunk counts into output offsets (a candidate list
-//                that overflows its capacity falls back to the exact one-workgroup
-//                selection over the whole row);
-//   dec_compact  (chunks x B) ordered compaction: keeps S > v* or (S == v* and
-//                s <= s*), writing ascending positions at the chunk's offset.
-// The selected set is exactly the K best positions under (score desc, position
-// asc): every position in a higher bin is kept, every position in a lower bin
-// dropped, and the split inside b* is resolved exactly.
+// With one query per sequence the parallelism comes from splitting the
+// history into chunks of 4096 positions. A sampled threshold lets the full
+// scoring pass keep only a short candidate list, so no score row goes to HBM:
+//   dec_sample   (sample blocks x B) int8-MFMA scores of every ss-th
+//                position, histogrammed per workgroup (score_bin);
+//   dec_thresh   (B) the threshold t from the histograms: the lowest score of
+//                the bin holding the sample that about K/ss + 4 sqrt(K/ss) + 2
+//                samples reach (expected candidates about ss times that, a
+//                few standard deviations above K); histories of at most 8192
+//                positions take every position;
+//   dec_score    (chunks x B) int8-MFMA scores of every position of the chunk,
+//                listing (score, position) of those >= t in position order in
+//                the chunk's own slice of the candidate list;
+//   dec_select   (B) gathers the slices (chunk order = position order), finds
+//                the exact K-th score v* and the position cut s* that keeps the
+//                lowest-position ties, and writes the kept positions in order.
+//                A list shorter than K (t was above the K-th score) or longer
+//                than the LDS capacity sends the sequence to the fallback in
+//                the same workgroup: every score of the row into workspace,
+//                then the exact one-workgroup selection over the whole row.
+// Every position scoring >= t is listed, so when the list holds at least K
+// entries the K-th largest listed score is the row's K-th largest: the
+// selected set is exactly the K best positions under (score desc, position
+// asc), whatever the sample.
 #include "common.h"
 #include "../../include/lci.h"
 #include "internal.h"
@@ -37,7 +41,7 @@
 namespace lci {
 
 constexpr int DEC_BINS = 2048;
-constexpr int DEC_CBINS = DEC_BINS / 32;  // coarse bins: fine bin / 32 (sign and exponent)
+constexpr int DEC_CBINS = DEC_BINS / 32;  // coarse bins: fine bin / 32 (sign and bit length)
 constexpr int DEC_NT = 256;
 
 struct DecRow {
@@ -55,113 +59,26 @@ __device__ __forceinline__ DecRow dec_row(int Tk, const int32_t* q_offset, const
   return r;
 }
 
-// Sum of p[c * stride] over c = c0, c0 + step, ... < nc, eight loads in flight.
-__device__ __forceinline__ uint32_t strided_sum(const uint32_t* __restrict__ p, int c0, int nc,
-                                                int step, int64_t stride) {
-  uint32_t acc = 0;
-  int c = c0;
-  for (; c + 7 * step < nc; c += 8 * step) {
-    uint32_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[static_cast<int64_t>(c + u * step) * stride];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
-  }
-  for (; c < nc; c += step) acc += p[static_cast<int64_t>(c) * stride];
-  return acc;
-}
-
-// One workgroup per sequence: the bin b* holding the K-th largest score and
-// the count of positions in higher bins, read by the candidate and resolve
-// kernels. Two levels over the stored chunk histograms: the 64 coarse bins
-// (sign and exponent) summed over the chunks give the coarse bin holding the
-// K-th score, then only its 32 fine bins are summed (96 words per chunk read
-// instead of 2048).
-__global__ __launch_bounds__(DEC_NT) void dec_thresh_kernel(
-    int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
-    const uint32_t* __restrict__ fhist, const uint32_t* __restrict__ chist, int nchunks,
-    uint32_t* __restrict__ bsel) {
-  __shared__ uint32_t red[DEC_NT];
-  __shared__ uint32_t res[2];
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
-  if (rw.n <= K) return;
-  const int nc = static_cast<int>((rw.n + kDecChunk - 1) / kDecChunk);  // chunks with positions
-  const uint32_t uK = static_cast<uint32_t>(K);
-  // coarse: thread t sums coarse bin t % 64 over chunks t / 64, t / 64 + 4, ...
-  red[t] = strided_sum(chist + static_cast<int64_t>(b) * nchunks * DEC_CBINS + lane, t >> 6, nc,
-                       DEC_NT / 64, DEC_CBINS);
-  __syncthreads();
-  if (t < 64) {
-    // lane l takes coarse bin 63 - l: the inclusive scan runs from the top bin down
-    const int cb = DEC_CBINS - 1 - lane;
-    uint32_t v = 0;
-#pragma unroll
-    for (int g = 0; g < DEC_NT / 64; ++g) v += red[g * 64 + cb];
-    const uint32_t incl = wave_incl_scan(v);
-    if (incl - v < uK && uK <= incl) {
-      res[0] = static_cast<uint32_t>(cb);
-      res[1] = incl - v;
-    }
-  }
-  __syncthreads();
-  const int cbin = static_cast<int>(res[0]);
-  const uint32_t abovec = res[1];
-  // fine: thread t sums fine bin 32 cbin + t % 32 over chunks t / 32, t / 32 + 8, ...
-  red[t] = strided_sum(fhist + static_cast<int64_t>(b) * nchunks * DEC_BINS + 32 * cbin + (t & 31),
-                       t >> 5, nc, DEC_NT / 32, DEC_BINS);
-  __syncthreads();
-  if (t < 64) {
-    const int f = 31 - lane;  // lanes 32..63 carry nothing
-    uint32_t v = 0;
-    if (lane < 32)
-#pragma unroll
-      for (int g = 0; g < DEC_NT / 32; ++g) v += red[g * 32 + f];
-    const uint32_t incl = wave_incl_scan(v);
-    const uint32_t krem = uK - abovec;
-    if (lane < 32 && incl - v < krem && krem <= incl) {
-      bsel[2 * b] = static_cast<uint32_t>(32 * cbin + f);
-      bsel[2 * b + 1] = abovec + incl - v;
-    }
-  }
-}
-
-// Scoring uses v_mfma_i32_16x16x64_i8 with the history positions as the 16
+// Scoring uses v_mfma_i32_16x16x64_i8 with 16 history positions as the
 // columns: lane l loads 16 bytes at offset 16*(l/16) of position l%16, so one
-// load instruction covers 16 consecutive 64-byte indexer keys (1 KiB, fully
-// coalesced) for d_I = 64. MFMA rows are the H_I indexer heads (at most 16) of
-// the single query; lane l holds heads 4*(l/16)+i of position l%16, so the
-// weighted ReLU sum is completed across the lane groups with two xor-shuffles.
-// Loads are unconditional (positions past the end are clamped to a valid row
-// and their scores dropped) and double-buffered in two named register sets, so
-// the compiler can keep the next step's loads in flight during this step's
-// MFMAs; scores are staged in LDS and written out, with the histogram, at the end.
+// load instruction covers 16 64-byte indexer keys (1 KiB, fully coalesced when
+// the positions are consecutive) for d_I = 64. MFMA rows are the H_I indexer
+// heads (at most 16) of the single query; lane l holds heads 4*(l/16)+i of
+// position l%16, so the weighted ReLU sum is completed across the lane groups
+// with two xor-shuffles, and lanes 0..15 end with the 16 scores.
 template <int H_I, int D_I>
-__global__ __launch_bounds__(DEC_NT) void dec_score_kernel(
-    int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
-    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
-    const int8_t* __restrict__ w, int64_t wsb, int32_t* __restrict__ S,
-    uint32_t* __restrict__ fhist, uint32_t* __restrict__ chist) {
-  constexpr int NCH = D_I / 64 > 0 ? D_I / 64 : 1;  // 64-deep MFMA steps
-  constexpr int U = 4;                             // 16-position tiles per step
-  constexpr int STEP = 16 * U;
-  __shared__ uint32_t lh[DEC_BINS];
-  __shared__ int32_t sl[kDecChunk];
-  const int b = blockIdx.y;
-  const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDecChunk;
-  if (rw.n <= K || base >= rw.n) return;  // nothing to select for this chunk
-  for (int j = threadIdx.x; j < DEC_BINS; j += DEC_NT) lh[j] = 0u;
-
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int grp = lane >> 4;
-  // A operand: lane l supplies row (head) l%16, bytes 16*(l/16) of each 64-deep step;
-  // for d_I = 32 the upper 32 bytes of the step are zero in A (B may hold anything)
+struct DecScorer {
+  static constexpr int NCH = D_I / 64 > 0 ? D_I / 64 : 1;  // 64-deep MFMA steps
   v4i a[NCH];
-  {
+  int wh[4];  // weights of the heads this lane holds: 4*grp + i
+  const int8_t* kb;
+
+  __device__ DecScorer(int b, const int8_t* q_idx, const int8_t* k_idx, const int8_t* w,
+                       int64_t wsb, int Tk) {
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4;
+    // A operand: lane l supplies row (head) l%16, bytes 16*(l/16) of each 64-deep
+    // step; for d_I = 32 the upper 32 bytes of the step are zero in A
     const int hh = lane & 15;
     const bool ok = hh < H_I && 16 * grp < D_I;
     const int8_t* src = q_idx + (static_cast<int64_t>(b) * H_I + (ok ? hh : 0)) * D_I + 16 * grp;
@@ -170,44 +87,217 @@ __global__ __launch_bounds__(DEC_NT) void dec_score_kernel(
       v4i z = {0, 0, 0, 0};
       a[c] = ok ? *reinterpret_cast<const v4i*>(src + 64 * c) : z;
     }
-  }
-  int wh[4];  // weights of the heads this lane holds: 4*grp + i
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * grp + i;
-    wh[i] = hh < H_I ? static_cast<int>(w[b * wsb + hh]) : 0;
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * grp + i;
+      wh[i] = h < H_I ? static_cast<int>(w[b * wsb + h]) : 0;
+    }
+    kb = k_idx + static_cast<int64_t>(b) * Tk * D_I + 16 * (grp % (D_I / 16 < 4 ? D_I / 16 : 4));
   }
+  // the key fragments of position `key` (this lane's part); the keys are read
+  // once per call, so they are not kept in the caches
+  __device__ __forceinline__ void load(int64_t key, v4i (&dst)[NCH]) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) dst[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(kb + key * D_I + 64 * c));
+  }
+  // the score of position l%16 of the 16 loaded (valid in lanes 0..15)
+  __device__ __forceinline__ int score(const v4i (&src)[NCH]) const {
+    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[c], src[c], acc, 0, 0, 0);
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += __mul24(wh[i], max(acc[i], 0));
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    return s;
+  }
+};
+
+// Scores of the sampled positions s = ss*j, kDecSampWG of them per
+// workgroup (16 per MFMA group, every group's loads issued before any MFMA),
+// histogrammed by score_bin in LDS; each workgroup stores its fine (2048-bin)
+// and coarse (64-bin: sign and bit length) histograms. Rows that take every
+// position skip the sample.
+constexpr int kDecSampWG = 512;
+
+template <int H_I, int D_I>
+__global__ __launch_bounds__(DEC_NT) void dec_sample_kernel(
+    int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
+    const int8_t* __restrict__ w, int64_t wsb, int ss, uint32_t* __restrict__ fhist,
+    uint32_t* __restrict__ chist) {
+  using SC = DecScorer<H_I, D_I>;
+  constexpr int G = kDecSampWG / 16 / (DEC_NT / 64);  // MFMA groups per wave
+  __shared__ uint32_t lh[DEC_BINS];
+  const int b = blockIdx.y;
+  const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kDecSampWG;  // first sample
+  if (rw.n <= kDecCap || j0 * ss >= rw.n) return;
+  for (int j = threadIdx.x; j < DEC_BINS; j += DEC_NT) lh[j] = 0u;
+  const SC sc(b, q_idx, k_idx, w, wsb, Tk);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  v4i kf[G][SC::NCH];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t s = (j0 + 16 * (G * wv + g) + (lane & 15)) * ss;
+    sc.load(min(s, rw.n - 1), kf[g]);
+  }
+  __syncthreads();  // histogram zeroed
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int v = sc.score(kf[g]);
+    const int64_t s = (j0 + 16 * (G * wv + g) + (lane & 15)) * ss;
+    if (lane < 16 && s < rw.n) atomicAdd(&lh[score_bin(v)], 1u);
+  }
+  __syncthreads();
+  const int64_t wi = static_cast<int64_t>(b) * gridDim.x + blockIdx.x;
+  uint32_t* hb = fhist + wi * DEC_BINS;
+  for (int j = threadIdx.x; j < DEC_BINS; j += DEC_NT) hb[j] = lh[j];
+  if (threadIdx.x < DEC_CBINS) {
+    uint32_t cs = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) cs += lh[32 * threadIdx.x + ((j + threadIdx.x) & 31)];
+    chist[wi * DEC_CBINS + threadIdx.x] = cs;
+  }
+}
+
+// The threshold t of sequence b: the lowest score of the
+// score_bin bin holding the target-th largest sample (target about
+// K/ss + 4 sqrt(K/ss) + 2), so at least target samples score >= t. Two levels
+// over the sample workgroups' histograms: the coarse bins summed give the
+// coarse bin holding it, then only that coarse bin's 32 fine bins are summed.
+// Rows of at most kDecCap positions take every position (t = INT32_MIN).
+// All DEC_NT threads call it; red holds DEC_NT words of LDS, res 2.
+__device__ int32_t dec_threshold(int b, int64_t n, int K, int ss, int nsw,
+                                 const uint32_t* __restrict__ fhist,
+                                 const uint32_t* __restrict__ chist, uint32_t* red,
+                                 uint32_t* res) {
+  if (n <= kDecCap) return INT32_MIN;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int64_t ns = (n + ss - 1) / ss;
+  const int nw = static_cast<int>((ns + kDecSampWG - 1) / kDecSampWG);  // workgroups with samples
+  const float kf = static_cast<float>(K) / ss;
+  const uint32_t target = static_cast<uint32_t>(
+      fminf(static_cast<float>(ns), ceilf(kf + 4.0f * sqrtf(kf) + 2.0f)));
+  // coarse: thread t sums coarse bin t % 64 over workgroups t / 64, t / 64 + 4, ...
+  {
+    const uint32_t* cp = chist + static_cast<int64_t>(b) * nsw * DEC_CBINS + lane;
+    uint32_t acc = 0;
+    for (int wi = t >> 6; wi < nw; wi += DEC_NT / 64) acc += cp[static_cast<int64_t>(wi) * DEC_CBINS];
+    red[t] = acc;
+  }
+  __syncthreads();
+  if (t < 64) {
+    // lane l takes coarse bin 63 - l: the inclusive scan runs from the top bin down
+    const int cb = DEC_CBINS - 1 - lane;
+    uint32_t v = 0;
+#pragma unroll
+    for (int g = 0; g < DEC_NT / 64; ++g) v += red[g * 64 + cb];
+    const uint32_t incl = wave_incl_scan(v);
+    if (incl - v < target && target <= incl) {
+      res[0] = static_cast<uint32_t>(cb);
+      res[1] = incl - v;
+    }
+  }
+  __syncthreads();
+  const int cbin = static_cast<int>(res[0]);
+  const uint32_t abovec = res[1];
+  // fine: thread t sums fine bin 32 cbin + t % 32 over workgroups t / 32, t / 32 + 8, ...
+  {
+    const uint32_t* fp = fhist + static_cast<int64_t>(b) * nsw * DEC_BINS + 32 * cbin + (t & 31);
+    uint32_t acc = 0;
+    for (int wi = t >> 5; wi < nw; wi += DEC_NT / 32) acc += fp[static_cast<int64_t>(wi) * DEC_BINS];
+    __syncthreads();  // every thread has read res
+    red[t] = acc;
+  }
+  __syncthreads();
+  if (t < 64) {
+    const int f = 31 - lane;  // lanes 32..63 carry nothing
+    uint32_t v = 0;
+    if (lane < 32)
+#pragma unroll
+      for (int g = 0; g < DEC_NT / 32; ++g) v += red[g * 32 + f];
+    const uint32_t incl = wave_incl_scan(v);
+    const uint32_t krem = target - abovec;
+    if (lane < 32 && incl - v < krem && krem <= incl) {
+      // the lowest score of fine bin 32 cbin + f (score_bin is monotone)
+      const int bin = 32 * cbin + f;
+      int64_t lo = INT32_MIN, hi = INT32_MAX;
+      while (lo < hi) {
+        const int64_t mid = lo + ((hi - lo) >> 1);
+        if (score_bin(static_cast<int32_t>(mid)) >= bin) hi = mid;
+        else lo = mid + 1;
+      }
+      res[0] = static_cast<uint32_t>(static_cast<int32_t>(lo));
+    }
+  }
+  __syncthreads();
+  return static_cast<int32_t>(res[0]);
+}
+
+// One workgroup per sequence: thr[b] = the threshold (read by every scoring
+// workgroup of the sequence). Rows of at most K positions need none.
+__global__ __launch_bounds__(DEC_NT) void dec_thresh_kernel(
+    int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
+    int ss, int nsw, const uint32_t* __restrict__ fhist, const uint32_t* __restrict__ chist,
+    int32_t* __restrict__ thr) {
+  __shared__ uint32_t red[DEC_NT];
+  __shared__ uint32_t res[2];
+  const int b = blockIdx.x;
+  const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
+  if (rw.n <= K) return;
+  const int32_t t = dec_threshold(b, rw.n, K, ss, nsw, fhist, chist, red, res);
+  if (threadIdx.x == 0) thr[b] = t;
+}
+
+// Every position of the chunk scored (four waves, 1024 positions each, loads
+// double-buffered in two named register sets so the next step's loads stay in
+// flight during this step's MFMAs) into LDS; then the (score, position) pairs
+// with score >= t, in position order, into the chunk's slice of the candidate
+// list, and their count.
+template <int H_I, int D_I>
+__global__ __launch_bounds__(DEC_NT) void dec_score_kernel(
+    int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
+    const int8_t* __restrict__ w, int64_t wsb, const int32_t* __restrict__ thr,
+    uint32_t* __restrict__ ncand, int2* __restrict__ cand, int nchunks) {
+  using SC = DecScorer<H_I, D_I>;
+  constexpr int U = 4;  // 16-position tiles per step
+  constexpr int STEP = 16 * U;
+  constexpr int E = kDecChunk / DEC_NT;
+  constexpr int NW = DEC_NT / 64;
+  __shared__ int32_t sl[kDecChunk];
+  __shared__ uint32_t cnt[E * NW];
+  const int b = blockIdx.y;
+  const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDecChunk;
+  if (rw.n <= K || base >= rw.n) return;  // nothing to select for this chunk
+  const SC sc(b, q_idx, k_idx, w, wsb, Tk);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
 
   const int64_t nend = min(base + kDecChunk, rw.n);
   const int64_t wbeg = base + wv * (kDecChunk / 4);
   const int64_t wend = min(wbeg + kDecChunk / 4, nend);
-  const int8_t* kb = k_idx + static_cast<int64_t>(b) * Tk * D_I + 16 * (grp % (D_I / 16 < 4 ? D_I / 16 : 4));
-
-  auto load = [&](int64_t kt, v4i (&dst)[U][NCH]) {
+  // loads are unconditional: positions past the end are clamped to a valid
+  // row and their scores dropped
+  auto load = [&](int64_t kt, v4i (&dst)[U][SC::NCH]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t key = min(kt + 16 * u + (lane & 15), wend - 1);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) dst[u][c] = *reinterpret_cast<const v4i*>(kb + key * D_I + 64 * c);
-    }
+    for (int u = 0; u < U; ++u) sc.load(min(kt + 16 * u + (lane & 15), wend - 1), dst[u]);
   };
-  auto score = [&](int64_t kt, const v4i (&src)[U][NCH]) {
+  auto score = [&](int64_t kt, const v4i (&src)[U][SC::NCH]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      v4i acc = {0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[c], src[u][c], acc, 0, 0, 0);
-      int s = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s += __mul24(wh[i], max(acc[i], 0));
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
+      const int s = sc.score(src[u]);
       const int64_t key = kt + 16 * u + (lane & 15);
       if (lane < 16 && key < wend) sl[key - base] = s;
     }
   };
   if (wbeg < wend) {
-    v4i bufA[U][NCH], bufB[U][NCH];
+    v4i bufA[U][SC::NCH], bufB[U][SC::NCH];
     load(wbeg, bufA);
     for (int64_t kt = wbeg; kt < wend; kt += 2 * STEP) {
       load(kt + STEP, bufB);
@@ -219,80 +309,35 @@ __global__ __launch_bounds__(DEC_NT) void dec_score_kernel(
     }
   }
   __syncthreads();
-  // write the chunk's scores (coalesced) and histogram them
-  int32_t* Sb = S + static_cast<int64_t>(b) * Tk;
-  const int cnt = static_cast<int>(nend - base);
-  for (int j = threadIdx.x; j < cnt; j += DEC_NT) {
-    const int32_t sv = sl[j];
-    Sb[base + j] = sv;
-    atomicAdd(&lh[score_bin(sv)], 1u);
-  }
-  __syncthreads();
-  // this chunk's histogram, stored whole (no cross-workgroup atomics), and
-  // its coarse form (32 fine bins per coarse bin)
-  const int64_t ci = static_cast<int64_t>(b) * gridDim.x + blockIdx.x;
-  uint32_t* hb = fhist + ci * DEC_BINS;
-  for (int j = threadIdx.x; j < DEC_BINS; j += DEC_NT) hb[j] = lh[j];
-  if (threadIdx.x < DEC_CBINS) {
-    uint32_t cs = 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) cs += lh[32 * threadIdx.x + ((j + threadIdx.x) & 31)];
-    chist[ci * DEC_CBINS + threadIdx.x] = cs;
-  }
-}
-
-__global__ __launch_bounds__(DEC_NT) void dec_cand_kernel(
-    int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ S, const uint32_t* __restrict__ bsel, uint32_t* __restrict__ ncand,
-    int2* __restrict__ cand, uint32_t* __restrict__ ngt, int nchunks) {
-  constexpr int E = kDecChunk / DEC_NT;
-  __shared__ uint32_t scratch[DEC_NT / 64 + 2];
-  const int b = blockIdx.y;
-  const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDecChunk;
-  const int64_t ci = static_cast<int64_t>(b) * nchunks + blockIdx.x;
-  if (rw.n <= K || base >= rw.n) {
-    if (threadIdx.x == 0) {
-      ngt[ci] = 0u;
-      ncand[ci] = 0u;
-    }
-    return;
-  }
-  const int bstar = static_cast<int>(bsel[2 * b]);
-  const int64_t nend = min(base + kDecChunk, rw.n);
-  const int32_t* Sb = S + static_cast<int64_t>(b) * Tk;
-  // element e of this thread: position base + e*DEC_NT + tid (coalesced)
-  int32_t val[E];
-  uint32_t gt = 0, nc = 0, cmask = 0;
-  // every load issued before any is used (clamped to the chunk's last position)
-#pragma unroll
-  for (int e = 0; e < E; ++e) val[e] = Sb[min(base + e * DEC_NT + threadIdx.x, nend - 1)];
+  const int ncnt = static_cast<int>(nend - base);
+  // candidates in position order: element e of this thread is position
+  // base + e*DEC_NT + tid, so position order is (e, wave, lane): a ballot per
+  // e ranks the lanes, LDS counts rank (e, wave)
+  const int32_t t = thr[b];
+  uint64_t km[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int64_t s = base + e * DEC_NT + threadIdx.x;
-    const int bin = s < nend ? score_bin(val[e]) : -1;
-    gt += bin > bstar ? 1u : 0u;
-    if (bin == bstar) {
-      cmask |= 1u << e;
-      ++nc;
-    }
+    const int j = e * DEC_NT + threadIdx.x;
+    km[e] = __ballot(j < ncnt && sl[j] >= t);
+    if (lane == 0) cnt[e * NW + wv] = __popcll(km[e]);
   }
-  uint32_t tot_c;
-  const uint32_t ex = block_excl_scan(nc, scratch, &tot_c);
-  uint32_t tot_g;
-  block_excl_scan(gt, scratch, &tot_g);
-  if (threadIdx.x == 0) {
-    ncand[ci] = tot_c;
-    ngt[ci] = tot_g;
+  __syncthreads();
+  const int64_t ci = static_cast<int64_t>(b) * nchunks + blockIdx.x;
+  if (threadIdx.x < 64) {
+    // exclusive prefix over the E*NW = 64 counts, one per lane
+    const uint32_t c = cnt[threadIdx.x];
+    const uint32_t incl = wave_incl_scan(c);
+    cnt[threadIdx.x] = incl - c;
+    if (threadIdx.x == 63) ncand[ci] = incl;
   }
-  // this chunk's candidates, in its own slice of the list (at most kDecChunk)
-  uint32_t slot = ex;
+  __syncthreads();
   int2* cb = cand + ci * kDecChunk;
+  const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    if (cmask & (1u << e)) {
-      cb[slot] = make_int2(val[e], static_cast<int>(base + e * DEC_NT + threadIdx.x));
-      ++slot;
+    if ((km[e] >> lane) & 1ull) {
+      const int j = e * DEC_NT + threadIdx.x;
+      cb[cnt[e * NW + wv] + __popcll(km[e] & below)] = make_int2(sl[j], static_cast<int>(base + j));
     }
 }
 
@@ -357,12 +402,24 @@ __device__ uint32_t lds_kth_largest(int n, uint32_t k, F keyf, uint32_t* hist, u
   return prefix;
 }
 
-__global__ __launch_bounds__(TOPK_NT) void dec_resolve_kernel(
+constexpr int kSelList = 512;  // entries ranked pairwise in dec_select
+
+// One workgroup per sequence: the exact selection from the candidate list.
+// The chunks' slices are merged in chunk order, which is position order; the
+// K-th largest listed score v* and the tie cut s* (the r-th smallest position
+// among the scores equal to v*, r = K - (count above v*)) come from two LDS
+// radix selects, and an ordered compaction writes the kept positions in
+// ascending order. A list shorter than K (the sampled threshold was above the
+// K-th score) or longer than kDecCap sends the row to the fallback: this
+// workgroup scores the whole row into workspace and runs the exact
+// one-workgroup selection over it (slow, but only for such rows).
+template <int H_I, int D_I>
+__global__ __launch_bounds__(TOPK_NT) void dec_select_kernel(
     int Tk, int K, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ S, const uint32_t* __restrict__ bsel,
-    const uint32_t* __restrict__ ncand, const int2* __restrict__ cand,
-    const uint32_t* __restrict__ ngt, uint32_t* __restrict__ off, int nchunks,
-    int32_t* __restrict__ thr, int32_t* __restrict__ idx) {
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
+    const int8_t* __restrict__ w, int64_t wsb, const uint32_t* __restrict__ ncand,
+    const int2* __restrict__ cand, int nchunks, int32_t* __restrict__ S,
+    int32_t* __restrict__ idx) {
   __shared__ SelectLds sm;
   __shared__ int cval[kDecCap];
   __shared__ int cpos[kDecCap];
@@ -370,35 +427,45 @@ __global__ __launch_bounds__(TOPK_NT) void dec_resolve_kernel(
   const int b = blockIdx.x;
   const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
   int32_t* out = idx + static_cast<int64_t>(b) * K;
-  int32_t* th = thr + 4 * b;
   if (rw.n <= K) {  // every candidate is kept (or the row is invalid)
     for (int j = threadIdx.x; j < K; j += TOPK_NT) out[j] = j < rw.n ? j : -1;
-    if (threadIdx.x == 0) th[0] = 0;
     return;
   }
   // per-chunk candidate counts -> where each chunk's candidates go in LDS
   const int nch = static_cast<int>((rw.n + kDecChunk - 1) / kDecChunk);
   const uint32_t* cn = ncand + static_cast<int64_t>(b) * nchunks;
-  for (int c = threadIdx.x; c < nch; c += TOPK_NT) ccount[c] = cn[c];
-  __syncthreads();
   uint32_t nc = 0;
   for (int c0 = 0; c0 < nch; c0 += TOPK_NT) {
     const int c = c0 + threadIdx.x;
-    const uint32_t v = c < nch ? ccount[c] : 0u;
+    const uint32_t v = c < nch ? cn[c] : 0u;
     uint32_t tot;
     const uint32_t ex = block_excl_scan(v, sm.scratch, &tot);
     if (c < nch) ccount[c] = nc + ex;  // exclusive start of chunk c
     nc += tot;
   }
-  __syncthreads();
-  if (nc > static_cast<uint32_t>(kDecCap)) {
-    // too many equal-bin candidates for LDS: exact selection over the whole row
-    select_row(S + static_cast<int64_t>(b) * Tk, rw.n, K, out, nullptr, sm);
-    if (threadIdx.x == 0) th[0] = 0;
+  if (nc < static_cast<uint32_t>(K) || nc > static_cast<uint32_t>(kDecCap)) {
+    // the fallback: every score of the row (each wave 64 positions a step,
+    // four 16-position MFMA groups, loads clamped to the last position)
+    using SC = DecScorer<H_I, D_I>;
+    const SC sc(b, q_idx, k_idx, w, wsb, Tk);
+    const int lane = threadIdx.x & 63;
+    int32_t* Sb = S + static_cast<int64_t>(b) * Tk;
+    for (int64_t kt = 64 * (threadIdx.x >> 6); kt < rw.n; kt += 64 * (TOPK_NT / 64)) {
+      v4i kf[4][SC::NCH];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sc.load(min(kt + 16 * u + (lane & 15), rw.n - 1), kf[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = sc.score(kf[u]);
+        const int64_t key = kt + 16 * u + (lane & 15);
+        if (lane < 16 && key < rw.n) Sb[key] = v;
+      }
+    }
+    __syncthreads();
+    select_row(Sb, rw.n, K, out, nullptr, sm);
     return;
   }
-  // positions in bins above the candidate bin are all kept
-  const uint32_t krem = static_cast<uint32_t>(K) - bsel[2 * b + 1];
+  __syncthreads();
   // gather the chunks' lists: entry j of the merged list comes from the last
   // chunk whose start is <= j (empty chunks share their successor's start);
   // eight loads in flight per thread
@@ -408,8 +475,7 @@ __global__ __launch_bounds__(TOPK_NT) void dec_resolve_kernel(
       int2 cv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        // nc >= 1 here (at least K - (count above b*) candidates); entries
-        // past nc read the last one and are not stored
+        // entries past nc read the last one and are not stored
         const uint32_t j = min(j0 + u * TOPK_NT + threadIdx.x, nc - 1);
         int lo = 0, hi = nch - 1;  // largest c with ccount[c] <= j
         while (lo < hi) {
@@ -431,155 +497,225 @@ __global__ __launch_bounds__(TOPK_NT) void dec_resolve_kernel(
   }
   __syncthreads();
   const int n = static_cast<int>(nc);
-  // exact K-th score among the candidates
-  const uint32_t vkey = lds_kth_largest(
-      n, krem,
-      [&](int i, uint32_t& u) {
-        u = score_key(cval[i]);
-        return true;
-      },
-      sm.hist, sm.scratch, sm.red, sm.found);
-  const int32_t vstar = key_score(vkey);
-  uint32_t ngt2 = 0;
-  for (int j = threadIdx.x; j < n; j += TOPK_NT) ngt2 += cval[j] > vstar ? 1u : 0u;
-  ngt2 = wave_sum(ngt2);
-  if ((threadIdx.x & 63) == 0) sm.red[threadIdx.x >> 6] = ngt2;
+  constexpr int NT = TOPK_NT;
+  // the bin of score_bin holding the K-th largest listed score ...
+  for (int j = threadIdx.x; j < DEC_BINS; j += NT) sm.hist[j] = 0u;
   __syncthreads();
-  uint32_t cgt = 0;
-  for (int w2 = 0; w2 < TOPK_NT / 64; ++w2) cgt += sm.red[w2];
+  for (int j = threadIdx.x; j < n; j += NT) atomicAdd(&sm.hist[score_bin(cval[j])], 1u);
   __syncthreads();
-  const uint32_t r = krem - cgt;  // ties at v* to keep, lowest positions first
-  // r-th smallest position among the ties = r-th largest of the complemented positions
-  const uint32_t ckey = lds_kth_largest(
-      n, r,
-      [&](int i, uint32_t& u) {
-        u = ~static_cast<uint32_t>(cpos[i]);
-        return cval[i] == vstar;
-      },
-      sm.hist, sm.scratch, sm.red, sm.found);
-  const int32_t scut = static_cast<int32_t>(~ckey);
-  // per-chunk selected counts (LDS) -> exclusive offsets
-  uint32_t* ob = off + static_cast<int64_t>(b) * nchunks;
-  const uint32_t* gb = ngt + static_cast<int64_t>(b) * nchunks;
-  for (int c = threadIdx.x; c < nchunks; c += TOPK_NT) ccount[c] = gb[c];
-  __syncthreads();
-  for (int j = threadIdx.x; j < n; j += TOPK_NT) {
-    const int v = cval[j], s = cpos[j];
-    if (v > vstar || (v == vstar && s <= scut)) atomicAdd(&ccount[s / kDecChunk], 1u);
-  }
-  __syncthreads();
-  uint32_t carry = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += TOPK_NT) {
-    const int c = c0 + threadIdx.x;
-    const uint32_t v = c < nchunks ? ccount[c] : 0u;
+  __shared__ uint32_t res[3];
+  __shared__ int32_t lst[kSelList];
+  {
+    constexpr int BPT = DEC_BINS / NT;  // thread t owns bins 2047 - BPT t - (0 .. BPT-1)
+    uint32_t c[BPT], sum = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      c[e] = sm.hist[DEC_BINS - 1 - BPT * static_cast<int>(threadIdx.x) - e];
+      sum += c[e];
+    }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan(v, sm.scratch, &tot);
-    if (c < nchunks) ob[c] = carry + ex;
-    carry += tot;
-  }
-  if (threadIdx.x == 0) {
-    th[0] = 1;
-    th[1] = vstar;
-    th[2] = scut;
-  }
-}
-
-__global__ __launch_bounds__(DEC_NT) void dec_compact_kernel(
-    int Tk, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ S, const int32_t* __restrict__ thr,
-    const uint32_t* __restrict__ off, int nchunks, int K, int32_t* __restrict__ idx) {
-  constexpr int E = kDecChunk / DEC_NT;
-  constexpr int NW = DEC_NT / 64;
-  __shared__ uint32_t cnt[E * NW];
-  const int b = blockIdx.y;
-  const int32_t* th = thr + 4 * b;
-  if (th[0] != 1) return;
-  const DecRow rw = dec_row(Tk, q_offset, kv_len, b);
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDecChunk;
-  if (base >= rw.n) return;
-  const int32_t vstar = th[1], scut = th[2];
-  const int32_t* Sb = S + static_cast<int64_t>(b) * Tk;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  // position of element e of this thread: base + e*DEC_NT + tid, i.e. position
-  // order is (e, wave, lane): a ballot per e ranks lanes, LDS counts rank (e, wave)
-  uint64_t km[E];
-  int32_t vals[E];  // every load issued before any is used
+    uint32_t above = block_excl_scan(sum, sm.scratch, &tot);
 #pragma unroll
-  for (int e = 0; e < E; ++e) vals[e] = Sb[min(base + e * DEC_NT + threadIdx.x, rw.n - 1)];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int64_t s = base + e * DEC_NT + threadIdx.x;
-    const int32_t v = vals[e];
-    const bool keep = s < rw.n && (v > vstar || (v == vstar && s <= scut));
-    km[e] = __ballot(keep);
-    if (lane == 0) cnt[e * NW + wv] = __popcll(km[e]);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = off[static_cast<int64_t>(b) * nchunks + blockIdx.x];
-    for (int j = 0; j < E * NW; ++j) {
-      const uint32_t c = cnt[j];
-      cnt[j] = run;
-      run += c;
+    for (int e = 0; e < BPT; ++e) {
+      if (above < static_cast<uint32_t>(K) && static_cast<uint32_t>(K) <= above + c[e]) {
+        res[0] = static_cast<uint32_t>(DEC_BINS - 1 - BPT * static_cast<int>(threadIdx.x) - e);
+        res[1] = static_cast<uint32_t>(K) - above;
+      }
+      above += c[e];
     }
   }
   __syncthreads();
-  int32_t* out = idx + static_cast<int64_t>(b) * K;
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if ((km[e] >> lane) & 1ull) {
-      const uint32_t pos = cnt[e * NW + wv] + __popcll(km[e] & below);
-      if (pos < static_cast<uint32_t>(K)) out[pos] = static_cast<int32_t>(base + e * DEC_NT + threadIdx.x);
+  const int kbin = static_cast<int>(res[0]);
+  const uint32_t krank = res[1];  // rank of v* among the bin's scores
+  const uint32_t nkbin = sm.hist[kbin];
+  // ... then the exact score within it: when the bin's listed scores span
+  // fewer than DEC_BINS values (always below 2^17 in magnitude), a histogram
+  // of (key - the lowest key) gives it exactly; wider spans take the radix
+  // select
+  int32_t vstar;
+  uint32_t blo = 0xffffffffu, bhi = 0u;
+  for (int j = threadIdx.x; j < n; j += NT)
+    if (score_bin(cval[j]) == kbin) {
+      const uint32_t u = score_key(cval[j]);
+      blo = min(blo, u);
+      bhi = max(bhi, u);
     }
+  block_minmax(blo, bhi, sm.red);
+  if (bhi - blo < static_cast<uint32_t>(DEC_BINS)) {
+    for (int j = threadIdx.x; j < DEC_BINS; j += NT) sm.hist[j] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n; j += NT)
+      if (score_bin(cval[j]) == kbin) atomicAdd(&sm.hist[score_key(cval[j]) - blo], 1u);
+    __syncthreads();
+    constexpr int BPT = DEC_BINS / NT;  // thread t owns offsets 2047 - BPT t - (0 .. BPT-1)
+    uint32_t c[BPT], sum = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      c[e] = sm.hist[DEC_BINS - 1 - BPT * static_cast<int>(threadIdx.x) - e];
+      sum += c[e];
+    }
+    uint32_t tot;
+    uint32_t above = block_excl_scan(sum, sm.scratch, &tot);
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      if (above < krank && krank <= above + c[e])
+        res[0] = blo + static_cast<uint32_t>(DEC_BINS - 1 - BPT * static_cast<int>(threadIdx.x) - e);
+      above += c[e];
+    }
+    __syncthreads();
+    vstar = key_score(res[0]);
+    __syncthreads();
+  } else {
+    vstar = key_score(lds_kth_largest(
+        n, krank,
+        [&](int i, uint32_t& u) {
+          u = score_key(cval[i]);
+          return score_bin(cval[i]) == kbin;
+        },
+        sm.hist, sm.scratch, sm.red, sm.found));
+  }
+  // counts above and at v*: r = K - above ties are kept, lowest positions first
+  uint32_t ngt = 0, neq = 0;
+  for (int j = threadIdx.x; j < n; j += NT) {
+    ngt += cval[j] > vstar ? 1u : 0u;
+    neq += cval[j] == vstar ? 1u : 0u;
+  }
+  ngt = wave_sum(ngt);
+  neq = wave_sum(neq);
+  if ((threadIdx.x & 63) == 0) {
+    sm.red[2 * (threadIdx.x >> 6)] = ngt;
+    sm.red[2 * (threadIdx.x >> 6) + 1] = neq;
+  }
+  __syncthreads();
+  uint32_t cgt = 0, ceq = 0;
+  for (int w2 = 0; w2 < NT / 64; ++w2) {
+    cgt += sm.red[2 * w2];
+    ceq += sm.red[2 * w2 + 1];
+  }
+  __syncthreads();
+  const uint32_t r = static_cast<uint32_t>(K) - cgt;
+  int32_t scut = INT32_MAX;  // every tie kept
+  if (r < ceq && ceq <= static_cast<uint32_t>(kSelList)) {
+    // the r-th smallest position among the ties, from a short list (the
+    // positions are distinct: each entry counts those below it)
+    if (threadIdx.x == 0) res[2] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n; j += NT)
+      if (cval[j] == vstar) lst[atomicAdd(&res[2], 1u)] = cpos[j];
+    __syncthreads();
+    for (int i = threadIdx.x; i < static_cast<int>(ceq); i += NT) {
+      const int32_t p = lst[i];
+      uint32_t below = 0;
+      for (int j = 0; j < static_cast<int>(ceq); ++j) below += lst[j] < p ? 1u : 0u;
+      if (below + 1 == r) res[0] = static_cast<uint32_t>(p);
+    }
+    __syncthreads();
+    scut = static_cast<int32_t>(res[0]);
+  } else if (r < ceq) {
+    // r-th smallest position among the ties = r-th largest complemented position
+    const uint32_t ckey = lds_kth_largest(
+        n, r,
+        [&](int i, uint32_t& u) {
+          u = ~static_cast<uint32_t>(cpos[i]);
+          return cval[i] == vstar;
+        },
+        sm.hist, sm.scratch, sm.red, sm.found);
+    scut = static_cast<int32_t>(~ckey);
+  }
+  // ordered compaction of the merged list (ascending positions): thread t
+  // takes entries [C t, C t + C), one block-wide scan of the kept counts
+  const int C = (n + NT - 1) / NT;
+  const int j0 = C * static_cast<int>(threadIdx.x);
+  uint32_t kc = 0;
+  for (int j = j0; j < min(j0 + C, n); ++j)
+    kc += (cval[j] > vstar || (cval[j] == vstar && cpos[j] <= scut)) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t pos = block_excl_scan(kc, sm.scratch, &tot);
+  for (int j = j0; j < min(j0 + C, n); ++j)
+    if (cval[j] > vstar || (cval[j] == vstar && cpos[j] <= scut)) out[pos++] = cpos[j];
 }
 
 // ---------------------------------------------------------------- host side
+
+// Sampling stride: every 32nd position (the threshold's target is then about
+// 64 samples at K = 2048, so the list falls short of K only when a Poisson(64)
+// count exceeds its mean by four standard deviations).
+constexpr int kDecSampleStride = 32;
 
 DecLayout decode_layout(const Geom& g) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   DecLayout L{};
   L.nchunks = static_cast<int>((static_cast<int64_t>(g.Tk) + kDecChunk - 1) / kDecChunk);
+  L.ss = kDecSampleStride;
+  L.nsw = static_cast<int>((static_cast<int64_t>(g.Tk) / L.ss + kDecSampWG) / kDecSampWG);
   size_t o = 0;
   L.scores = o;  o += al(static_cast<size_t>(g.B) * g.Tk * sizeof(int32_t));
-  L.hist = o;    o += al(static_cast<size_t>(g.B) * L.nchunks * DEC_BINS * sizeof(uint32_t));
+  L.fhist = o;   o += al(static_cast<size_t>(g.B) * L.nsw * DEC_BINS * sizeof(uint32_t));
+  L.chist = o;   o += al(static_cast<size_t>(g.B) * L.nsw * DEC_CBINS * sizeof(uint32_t));
   L.ncand = o;   o += al(static_cast<size_t>(g.B) * L.nchunks * sizeof(uint32_t));
   L.cand = o;    o += al(static_cast<size_t>(g.B) * L.nchunks * kDecChunk * sizeof(int2));
-  L.ngt = o;     o += al(static_cast<size_t>(g.B) * L.nchunks * sizeof(uint32_t));
-  L.off = o;     o += al(static_cast<size_t>(g.B) * L.nchunks * sizeof(uint32_t));
-  L.thr = o;     o += al(static_cast<size_t>(g.B) * 4 * sizeof(int32_t));
-  L.bsel = o;    o += al(static_cast<size_t>(g.B) * 2 * sizeof(uint32_t));
+  L.thr = o;     o += al(static_cast<size_t>(g.B) * sizeof(int32_t));
   L.idx = o;     o += al(static_cast<size_t>(g.B) * g.K * sizeof(int32_t));
   L.attn = o;
   L.splits = sparse_attn_pick_splits(g);
   o += al(sparse_attn_workspace(g, L.splits));
-  L.chist = o;   o += al(static_cast<size_t>(g.B) * L.nchunks * DEC_CBINS * sizeof(uint32_t));
   L.total = o;
   return L;
 }
 
+struct DecPtrs {
+  int32_t* S;
+  uint32_t* fhist;
+  uint32_t* chist;
+  uint32_t* ncand;
+  int2* cand;
+  int32_t* thr;
+};
+
 template <int H_I, int D_I>
-static hipError_t launch_score_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
-                                  const int8_t* w, int64_t wsb, int32_t* S, uint32_t* hist,
-                                  uint32_t* chist, int nchunks, hipStream_t st) {
+static hipError_t launch_select_hd(const Geom& g, const DecLayout& L, const int8_t* q_idx,
+                                   const int8_t* k_idx, const int8_t* w, int64_t wsb,
+                                   const DecPtrs& P, int32_t* idx, hipStream_t st) {
+  hipError_t e;
+  const dim3 grid(L.nchunks, g.B);
+  {
+    KernelTimer timer(LCI_KERNEL_DEC_SAMPLE, st);
+    hipLaunchKernelGGL((dec_sample_kernel<H_I, D_I>), dim3(L.nsw, g.B), dim3(DEC_NT), 0, st, g.Tk,
+                       g.K, g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, L.ss, P.fhist, P.chist);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    KernelTimer timer(LCI_KERNEL_DEC_THRESH, st);
+    hipLaunchKernelGGL(dec_thresh_kernel, dim3(g.B), dim3(DEC_NT), 0, st, g.Tk, g.K, g.q_offset,
+                       g.kv_len, L.ss, L.nsw, P.fhist, P.chist, P.thr);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     KernelTimer timer(LCI_KERNEL_DEC_SCORE, st);
-    hipLaunchKernelGGL((dec_score_kernel<H_I, D_I>), dim3(nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk,
-                       g.K, g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, S, hist, chist);
+    hipLaunchKernelGGL((dec_score_kernel<H_I, D_I>), grid, dim3(DEC_NT), 0, st, g.Tk, g.K,
+                       g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, P.thr, P.ncand, P.cand,
+                       L.nchunks);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    KernelTimer timer(LCI_KERNEL_DEC_SELECT, st);
+    hipLaunchKernelGGL((dec_select_kernel<H_I, D_I>), dim3(g.B), dim3(TOPK_NT), 0, st, g.Tk, g.K,
+                       g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, P.ncand, P.cand, L.nchunks,
+                       P.S, idx);
   }
   return hipGetLastError();
 }
 
 template <int H_I>
-static hipError_t launch_score_h(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
-                                 const int8_t* w, int64_t wsb, int32_t* S, uint32_t* hist,
-                                 uint32_t* chist, int nchunks, hipStream_t st) {
+static hipError_t launch_select_h(const Geom& g, const DecLayout& L, const int8_t* q_idx,
+                                  const int8_t* k_idx, const int8_t* w, int64_t wsb,
+                                  const DecPtrs& P, int32_t* idx, hipStream_t st) {
   switch (g.d_I) {
-    case 32: return launch_score_hd<H_I, 32>(g, q_idx, k_idx, w, wsb, S, hist, chist, nchunks, st);
-    case 64: return launch_score_hd<H_I, 64>(g, q_idx, k_idx, w, wsb, S, hist, chist, nchunks, st);
+    case 32: return launch_select_hd<H_I, 32>(g, L, q_idx, k_idx, w, wsb, P, idx, st);
+    case 64: return launch_select_hd<H_I, 64>(g, L, q_idx, k_idx, w, wsb, P, idx, st);
     case 128:
       if constexpr (H_I * 128 <= 1024)
-        return launch_score_hd<H_I, 128>(g, q_idx, k_idx, w, wsb, S, hist, chist, nchunks, st);
+        return launch_select_hd<H_I, 128>(g, L, q_idx, k_idx, w, wsb, P, idx, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -592,54 +728,27 @@ hipError_t launch_decode(const Geom& g, const int8_t* q_idx, const int8_t* k_idx
                          float* lse, int32_t* idx_out, void* workspace, hipStream_t st) {
   const DecLayout L = decode_layout(g);
   char* ws = static_cast<char*>(workspace);
-  int32_t* S = reinterpret_cast<int32_t*>(ws + L.scores);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
-  uint32_t* chist = reinterpret_cast<uint32_t*>(ws + L.chist);
-  uint32_t* ncand = reinterpret_cast<uint32_t*>(ws + L.ncand);
-  int2* cand = reinterpret_cast<int2*>(ws + L.cand);
-  uint32_t* ngt = reinterpret_cast<uint32_t*>(ws + L.ngt);
-  uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
-  int32_t* thr = reinterpret_cast<int32_t*>(ws + L.thr);
-  uint32_t* bsel = reinterpret_cast<uint32_t*>(ws + L.bsel);
+  DecPtrs P;
+  P.S = reinterpret_cast<int32_t*>(ws + L.scores);
+  P.fhist = reinterpret_cast<uint32_t*>(ws + L.fhist);
+  P.chist = reinterpret_cast<uint32_t*>(ws + L.chist);
+  P.ncand = reinterpret_cast<uint32_t*>(ws + L.ncand);
+  P.cand = reinterpret_cast<int2*>(ws + L.cand);
+  P.thr = reinterpret_cast<int32_t*>(ws + L.thr);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
 
   hipError_t e = hipSuccess;
   switch (g.H_I) {
-    case 1: e = launch_score_h<1>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
-    case 2: e = launch_score_h<2>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
-    case 4: e = launch_score_h<4>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
-    case 8: e = launch_score_h<8>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
-    case 16: e = launch_score_h<16>(g, q_idx, k_idx, w, wsb, S, hist, chist, L.nchunks, st); break;
+    case 1: e = launch_select_h<1>(g, L, q_idx, k_idx, w, wsb, P, idx, st); break;
+    case 2: e = launch_select_h<2>(g, L, q_idx, k_idx, w, wsb, P, idx, st); break;
+    case 4: e = launch_select_h<4>(g, L, q_idx, k_idx, w, wsb, P, idx, st); break;
+    case 8: e = launch_select_h<8>(g, L, q_idx, k_idx, w, wsb, P, idx, st); break;
+    case 16: e = launch_select_h<16>(g, L, q_idx, k_idx, w, wsb, P, idx, st); break;
     default: e = hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  {
-    KernelTimer timer(LCI_KERNEL_DEC_THRESH, st);
-    hipLaunchKernelGGL(dec_thresh_kernel, dim3(g.B), dim3(DEC_NT), 0, st, g.Tk, g.K, g.q_offset,
-                       g.kv_len, hist, chist, L.nchunks, bsel);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    KernelTimer timer(LCI_KERNEL_DEC_CAND, st);
-    hipLaunchKernelGGL(dec_cand_kernel, dim3(L.nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk, g.K,
-                       g.q_offset, g.kv_len, S, bsel, ncand, cand, ngt, L.nchunks);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    KernelTimer timer(LCI_KERNEL_DEC_RESOLVE, st);
-    hipLaunchKernelGGL(dec_resolve_kernel, dim3(g.B), dim3(TOPK_NT), 0, st, g.Tk, g.K, g.q_offset,
-                       g.kv_len, S, bsel, ncand, cand, ngt, off, L.nchunks, thr, idx);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    KernelTimer timer(LCI_KERNEL_DEC_COMPACT, st);
-    hipLaunchKernelGGL(dec_compact_kernel, dim3(L.nchunks, g.B), dim3(DEC_NT), 0, st, g.Tk,
-                       g.q_offset, g.kv_len, S, thr, off, L.nchunks, g.K, idx);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_sparse_attn(g, q, k, v, idx, gate, mix, scale, out, lse, L.splits, ws + L.attn,
-                            false,
-                            st);
+                            false, st);
 }
 
 }  // namespace lci

@@ -75,7 +75,7 @@ void clear(Log& l) {
 
 const char* const kNames[LCI_KERNEL_COUNT] = {
     "idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
-    "dec_thresh", "dec_score", "dec_cand", "dec_resolve", "dec_compact", "kv_append",
+    "dec_sample", "dec_thresh", "dec_score", "dec_select", "kv_append",
     "kv_lengths", "bwd_prologue", "bwd_dq", "bwd_transpose", "bwd_dkdv", "sel_scan",
     "sel_rows", "sel_fallback", "ibwd_rows", "ibwd_transpose", "ibwd_dk"};
 

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.lci_abi_version() == lci.ABI_VERSION == 3
+    assert lib.lci_abi_version() == lci.ABI_VERSION == 4
     for code in (OK, NULL, SHAPE, UNSUP, OVF, WS, HIP, ALIGN):
         assert lib.lci_status_str(code).decode().startswith("LCI_")
     assert b"unknown" in lib.lci_status_str(123)

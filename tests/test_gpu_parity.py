@@ -251,6 +251,22 @@ def test_decode_fused_edges(lci, orc, name):
     _fused_check(lci, orc, cfg, inp, cfg.K, entry="decode")
 
 
+def test_decode_sample_too_high(lci, orc):
+    """Every 32nd position (each sampled one) scores far above the rest and
+    there are fewer of them than K: the threshold from the sample sits above
+    the K-th score, the candidate list falls short of K, and the row is
+    selected again from its whole score row. One sequence stays on the list
+    path (unplanted) beside it, one takes every position."""
+    L = 40000
+    cfg = MED.replace(B=3, Tq=1, Tk=L, decode=True, K=2048, needles="none")
+    inp = make(cfg, seed=9, kv_len=[L, L - 5, 3000], q_offset=[L - 1, L - 6, 2999],
+               w=[1] * cfg.H_I)
+    inp["q_idx"][0] = 1
+    inp["k_idx"][0, ::32, :] = 8
+    log(f"decode sample too high: L={L} K={cfg.K} (1250 planted positions < K)")
+    _fused_check(lci, orc, cfg, inp, cfg.K, entry="decode")
+
+
 def test_deterministic(lci):
     import torch
     cfg = MED.replace(Tq=256, Tk=256, K=64)
