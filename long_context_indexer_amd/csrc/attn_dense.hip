@@ -39,6 +39,8 @@
 // free of bank conflicts. Workgroups are placed so that each XCD (its own L2)
 // serves one key/value head (blockIdx.x % 8 picks the XCD), and the longest
 // causal tiles start first.
+#include <type_traits>
+
 #include "attn_dense.h"
 #include "common.h"
 #include "../../include/lci.h"
@@ -288,8 +290,10 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   tile_scores(ks[0], sc);
   __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
+  // one step per tile; the steps of even and odd tiles are separate copies
+  // so each has its buffer addresses as constants
+  auto tile_step = [&](int kb, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     if (kb + 1 < nkb) load_tile(vbase, kb + 1, vsh[buf ^ 1]);
     if (kb + 2 < nkb) load_tile(kbase, kb + 2, ks[buf]);
     uint32_t mwn[2];
@@ -391,6 +395,10 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     // visible; it also guarantees every wave is done with the buffers the
     // next step's loads overwrite
     __syncthreads();
+  };
+  for (int kb = 0; kb < nkb; kb += 2) {
+    tile_step(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < nkb) tile_step(kb + 1, std::integral_constant<int, 1>{});
   }
 
   lsum = sum_xor32(lsum);
