@@ -139,6 +139,14 @@ __device__ __forceinline__ uint32_t sel_hbin(uint32_t key, uint32_t hb, int hsh)
   return key < hb ? 0u : min((key - hb) >> hsh, static_cast<uint32_t>(SEL_FB - 1));
 }
 
+// a * b + c for 24-bit signed a, b (one v_mad_i32_i24: the compiler would
+// otherwise pair the products into v_add3, three operations per two terms)
+__device__ __forceinline__ int mad_i24(int a, int b, int c) {
+  int d;
+  asm volatile("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
 
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
 #pragma unroll
       for (int h = 0; h < H_I; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[u][e] += __mul24(wh[h], max(acc[h][e], 0));
+        for (int e = 0; e < 4; ++e) sacc[u][e] = mad_i24(wh[h], max(acc[h][e], 0), sacc[u][e]);
     }
   };
   // f(position, score) over this lane's causal positions of a strided sweep
@@ -354,6 +362,11 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
   const uint32_t hb = sm.hb[r];
   const int hsh = sm.hsh[r];
   const int plist = listed ? p : -1;  // causal limit of the listed positions
+  // steps wholly at or below every listed row's limit need no position test
+  int pmin = listed ? p : INT32_MAX;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) pmin = min(pmin, __shfl_xor(pmin, off, 64));
+  pmin = __builtin_amdgcn_readfirstlane(pmin);
   int2* crow = cand + (static_cast<int64_t>(b) * Tq + (i < Tq ? i : 0)) * cap;
   v4i ka[U][NCH];
   load_keys(0, 1, ka);
@@ -390,13 +403,21 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
     v4i sacc[U];
     score(ka, sacc);
     uint32_t m = 0u;
+    if (pos0 + 31 <= pmin) {  // uniform
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pos = pos0 + 16 * u + 4 * g4 + e;
-        m |= static_cast<uint32_t>((sacc[u][e] >= thr) & (pos <= plist)) << (4 * u + e);
-      }
+        for (int e = 0; e < 4; ++e) m |= static_cast<uint32_t>(sacc[u][e] >= thr) << (4 * u + e);
+      m = listed ? m : 0u;
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pos = pos0 + 16 * u + 4 * g4 + e;
+          m |= static_cast<uint32_t>((sacc[u][e] >= thr) & (pos <= plist)) << (4 * u + e);
+        }
+    }
     pm = m;
     ps[0] = sacc[0];
     ps[1] = sacc[1];
