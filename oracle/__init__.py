@@ -13,7 +13,9 @@ Parity status of each function (pins live in tests/test_oracle_pins.py):
              linearity, a hand-worked example (tests/golden/indexer_hand.json)
   topk       pinned: O(n^2) rank definition, closed forms (monotone and constant rows)
   attention  pinned: dense causal attention from torch's SDPA when K >= p+1, K = 1,
-             constant values, a two-key closed form, permutation invariance
+             constant values, a two-key closed form, permutation invariance;
+             its fp32-source form (attention_f32): the same SDPA pin on fp32
+             inputs, and equality with the bf16 form on bf16-exact values
   gate       pinned: G = 0 halves the output, G -> +inf leaves it, closed form
   gradients  pinned: torch autograd (fp64) through independent statements of the
              attention forward and of the indexer's distillation loss; closed
@@ -65,6 +67,8 @@ def open_library(path: str):
     lib.orc_topk_rows.argtypes = [i64, P, i64, P, i32, P, P]
     lib.orc_attn_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, i64,
                                   P, P, P, P, P]
+    lib.orc_attn_rows_f32.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, f64, i64,
+                                      P, P, P, P, P]
     lib.orc_block_topk_rows.argtypes = [i64, P, i64, P, i32, i32, P, P, P]
     lib.orc_layer_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                    i64, i64, P, P, P, P, P, f64, i64, P, P, P, P, P, P]
@@ -186,6 +190,32 @@ class Oracle:
         self.lib.orc_attn_rows(Tq, Tk, Hq, Hkv, d, K, sets, _p(_c(kv_len, np.int32)), _p(q), _p(k),
                               _p(v), _p(gate), _p(mix), float(scale), len(rb), _p(rb), _p(ri),
                               _p(idx), _p(out), _p(lse))
+        return out, lse
+
+    def attention_f32(self, q, k, v, gate, idx, kv_len, scale, rows=None):
+        """``attention`` on fp32 sources (float32 q, gate [B,Tq,Hq,d], k, v
+        [B,Tk,Hkv,d]; gate may be None), no mix: the same fp64 arithmetic on
+        the fp32 values, for configurations whose inputs are drawn in fp32."""
+        q = _c(q, np.float32)
+        k = _c(k, np.float32)
+        v = _c(v, np.float32)
+        B, Tq, Hq, d = q.shape
+        Tk, Hkv = k.shape[1], k.shape[2]
+        gate = None if gate is None else _c(gate, np.float32)
+        if gate is not None and gate.shape != q.shape:
+            raise ValueError("gate has the shape of q")
+        rb, ri = _rows(rows, B, Tq)
+        idx = _c(idx, np.int32)
+        sets = idx.shape[1] if idx.ndim == 3 else 1
+        if sets not in (1, Hkv):
+            raise ValueError("one index set per row or one per key/value head")
+        idx = idx.reshape(len(rb), sets, -1)
+        K = idx.shape[2]
+        out = np.empty((len(rb), Hq, d), np.float64)
+        lse = np.empty((len(rb), Hq), np.float64)
+        self.lib.orc_attn_rows_f32(Tq, Tk, Hq, Hkv, d, K, sets, _p(_c(kv_len, np.int32)), _p(q),
+                                   _p(k), _p(v), _p(gate), float(scale), len(rb), _p(rb), _p(ri),
+                                   _p(idx), _p(out), _p(lse))
         return out, lse
 
     def block_topk(self, S, n, K, block):

@@ -142,10 +142,17 @@ static double orc_gate(double o, double G, const uint16_t *mix, int64_t j)
  * lse [Hq] (natural log of the softmax denominator, including the running
  * max); a row with no valid entry has o = 0 (so out = 0 without mixing) and
  * lse = -inf. */
-void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
-                  const uint16_t *v, int64_t kv_len, const int32_t *idx, int K, int sets,
-                  const uint16_t *gate, const uint16_t *mix, double scale, double *out,
-                  double *lse)
+/* Element i of a bf16 or an fp32 array, widened exactly to double. */
+typedef double (*orc_load)(const void *p, int64_t i);
+static double orc_ld_bf16(const void *p, int64_t i) { return orc_bf16(((const uint16_t *)p)[i]); }
+static double orc_ld_f32(const void *p, int64_t i) { return (double)((const float *)p)[i]; }
+
+/* The row's attention with q, k, v and gate read through ld (bf16 or fp32
+ * elements; mix is always bf16). */
+static void orc_attn_row_ld(int Hq, int Hkv, int d, const void *q, const void *k, const void *v,
+                            int64_t kv_len, const int32_t *idx, int K, int sets, const void *gate,
+                            const uint16_t *mix, double scale, double *out, double *lse,
+                            orc_load ld)
 {
     int G = Hq / Hkv;
     double *logit = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
@@ -158,7 +165,7 @@ void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
             if (s < 0 || s >= kv_len) { logit[t] = -INFINITY; continue; }
             double dot = 0.0;
             for (int j = 0; j < d; ++j)
-                dot += orc_bf16(q[h * d + j]) * orc_bf16(k[(s * Hkv + g) * d + j]);
+                dot += ld(q, (int64_t)h * d + j) * ld(k, (s * Hkv + g) * d + j);
             logit[t] = scale * dot;
             if (logit[t] > m) m = logit[t];
         }
@@ -173,16 +180,25 @@ void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
                 if (s < 0 || s >= kv_len) continue;
                 double e = exp(logit[t] - m);
                 Z += e;
-                for (int j = 0; j < d; ++j) o[j] += e * orc_bf16(v[(s * Hkv + g) * d + j]);
+                for (int j = 0; j < d; ++j) o[j] += e * ld(v, (s * Hkv + g) * d + j);
             }
             for (int j = 0; j < d; ++j) o[j] /= Z;
             if (lse) lse[h] = m + log(Z);
         }
         if (gate)
             for (int j = 0; j < d; ++j)
-                o[j] = orc_gate(o[j], orc_bf16(gate[h * d + j]), mix ? mix + (size_t)h * d : NULL, j);
+                o[j] = orc_gate(o[j], ld(gate, (int64_t)h * d + j), mix ? mix + (size_t)h * d : NULL, j);
     }
     free(logit);
+}
+
+void orc_attn_row(int Hq, int Hkv, int d, const uint16_t *q, const uint16_t *k,
+                  const uint16_t *v, int64_t kv_len, const int32_t *idx, int K, int sets,
+                  const uint16_t *gate, const uint16_t *mix, double scale, double *out,
+                  double *lse)
+{
+    orc_attn_row_ld(Hq, Hkv, d, q, k, v, kv_len, idx, K, sets, gate, mix, scale, out, lse,
+                    orc_ld_bf16);
 }
 
 /* ----------------------------------------------------------- whole rows */
@@ -290,6 +306,26 @@ void orc_attn_rows(int Tq, int Tk, int Hq, int Hkv, int d, int K, int sets, cons
                      v + (int64_t)b * Tk * Hkv * d, kvl, idx + r * (int64_t)sets * K, K, sets,
                      gate ? gate + qrow * Hq * d : NULL, mix ? mix + qrow * Hq * d : NULL, scale,
                      out + r * (int64_t)Hq * d, lse ? lse + r * (int64_t)Hq : NULL);
+    }
+}
+
+/* orc_attn_rows with fp32 q, k, v and gate (sources drawn in fp32, such as the
+ * Tiny configuration's), no mix; the same arithmetic in fp64. */
+void orc_attn_rows_f32(int Tq, int Tk, int Hq, int Hkv, int d, int K, int sets,
+                       const int32_t *kv_len, const float *q, const float *k, const float *v,
+                       const float *gate, double scale, int64_t nrows, const int32_t *row_b,
+                       const int32_t *row_i, const int32_t *idx, double *out, double *lse)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int b = row_b[r], i = row_i[r];
+        int64_t qrow = (int64_t)b * Tq + i;
+        int64_t kvl = kv_len[b] <= Tk ? kv_len[b] : 0;
+        orc_attn_row_ld(Hq, Hkv, d, q + qrow * Hq * d, k + (int64_t)b * Tk * Hkv * d,
+                        v + (int64_t)b * Tk * Hkv * d, kvl, idx + r * (int64_t)sets * K, K, sets,
+                        gate ? gate + qrow * Hq * d : NULL, NULL, scale,
+                        out + r * (int64_t)Hq * d, lse ? lse + r * (int64_t)Hq : NULL,
+                        orc_ld_f32);
     }
 }
 

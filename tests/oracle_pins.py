@@ -289,6 +289,52 @@ def pin_attn_dense_equivalence(orc):
     assert np.abs(lse.reshape(B, T, Hq) - ref_lse).max() < 1e-12
 
 
+def pin_attn_f32_dense_equivalence(orc):
+    """The fp32-source form: K >= p+1 on fp32 inputs (not bf16-representable)
+    is dense causal attention, from torch's SDPA in fp64 on the same fp32
+    values; with the gate, sigmoid(G) times it (scipy expit)."""
+    import torch
+    from scipy.special import expit
+    r = np.random.default_rng(36)
+    B, T, Hq, Hkv, d = 2, 20, 4, 1, 16
+    q = r.standard_normal((B, T, Hq, d)).astype(np.float32)
+    k = r.standard_normal((B, T, Hkv, d)).astype(np.float32)
+    v = r.standard_normal((B, T, Hkv, d)).astype(np.float32)
+    g = r.standard_normal((B, T, Hq, d)).astype(np.float32)
+    scale = 0.125
+    idx = np.full((B * T, T), -1, np.int32)
+    for b in range(B):
+        for i in range(T):
+            idx[b * T + i, :i + 1] = np.arange(i + 1)
+    out, lse = orc.attention_f32(q, k, v, g, idx, np.array([T, T]), scale)
+    qf = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)
+    kf = torch.from_numpy(k.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, 1)
+    vf = torch.from_numpy(v.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, is_causal=True, scale=scale)
+    ref = ref.permute(0, 2, 1, 3).numpy() * expit(g.astype(np.float64))
+    assert np.abs(out.reshape(B, T, Hq, d) - ref).max() < 1e-12
+    assert np.isfinite(lse).all()
+
+
+def pin_attn_f32_matches_bf16_form(orc):
+    """On values that bf16 represents exactly, the fp32-source form and the bf16
+    form read the same numbers and must agree bit for bit (ragged index rows,
+    padding, an entry past the history, two index sets)."""
+    r = np.random.default_rng(37)
+    B, Tq, Tk, Hq, Hkv, d, K = 2, 6, 30, 4, 2, 8, 7
+    q, gate = _rand_bf16(r, (B, Tq, Hq, d)), _rand_bf16(r, (B, Tq, Hq, d))
+    k, v = _rand_bf16(r, (B, Tk, Hkv, d)), _rand_bf16(r, (B, Tk, Hkv, d))
+    kv_len = np.array([30, 21], np.int32)
+    idx = r.integers(-1, 30, size=(B * Tq, Hkv, K)).astype(np.int32)
+    a, la = orc.attention(q, k, v, gate, idx, kv_len, 0.3)
+    f = [bf16_to_f32(x).astype(np.float32) for x in (q, k, v, gate)]
+    b, lb = orc.attention_f32(f[0], f[1], f[2], f[3], idx, kv_len, 0.3)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    a, _ = orc.attention(q, k, v, None, idx[:, 0], kv_len, 0.3)
+    b, _ = orc.attention_f32(f[0], f[1], f[2], None, idx[:, 0], kv_len, 0.3)
+    assert np.array_equal(a, b)
+
+
 def pin_attn_single_key(orc):
     """K = 1: softmax of one logit is 1, so y = sigmoid(G) * V[s] (scipy expit)."""
     from scipy.special import expit
