@@ -30,7 +30,7 @@ MUTANTS = [
      "rc |= orc_score_row(H_I, d_I, qI, kI, wr, p, S + r * (int64_t)Tk);"),
     ("no_softmax_scale", "logit[t] = scale * dot;", "logit[t] = dot;"),
     ("gqa_modulo", "int g = h / G;", "int g = h % Hkv;"),
-    ("keys_as_values", "o[j] += e * orc_bf16(v[", "o[j] += e * orc_bf16(k["),
+    ("keys_as_values", "o[j] += e * ld(v, ", "o[j] += e * ld(k, "),
     ("no_normalisation", "o[j] /= Z;", ""),
     ("gate_sign", "exp(-G)", "exp(G)"),
     ("gate_dropped", "return s * o + ", "return o + "),
