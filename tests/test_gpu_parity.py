@@ -188,6 +188,37 @@ def _fused_check(lci, orc, cfg, inp, K, rows=None, entry="prefill"):
     assert np.abs(lse[sel][fin] - res["lse"][fin]).max() < LSE_TOL
 
 
+def test_tiny_fp32_source(lci, orc):
+    """The Tiny configuration draws Q, K, V and the gate logits in fp32. The
+    library computes from their bf16 roundings (to nearest even): parity is
+    judged against the oracle on those bf16 inputs, and the same output is also
+    reported against the oracle on the fp32 sources (the rounding of the inputs
+    shows there, at about 3e-3 relative L2), within the same bounds."""
+    import torch
+    from gpu_util import attn_errors
+    cfg = TINY
+    inp = synth.host_inputs(cfg, seed=0)
+    assert "q_f32" in inp
+    d = to_device(inp)
+    out, idx = lci.prefill_fwd(d["q_idx"], d["k_idx"], d["w"], d["q"], d["k"], d["v"], d["gate"],
+                               inp["scale"], d["q_offset"], d["kv_len"], cfg.K, want_idx=True)
+    torch.cuda.synchronize()
+    res = orc.layer(inp, cfg.K)
+    out = host(out).reshape(cfg.Tq, cfg.Hq, cfg.d)
+    assert (host(idx).reshape(cfg.Tq, cfg.K) == res["idx"]).all()
+    ref32, _ = orc.attention_f32(inp["q_f32"], inp["k_f32"], inp["v_f32"], inp["gate_f32"],
+                                 res["idx"], inp["kv_len"], inp["scale"])
+    a16 = attn_errors(out, res["out"])
+    a32 = attn_errors(out, ref32)
+    o16 = np.abs(res["out"] - ref32)
+    log(f"tiny: GPU vs bf16-input oracle max_abs={a16[0]:.3e} rel_l2={a16[1]:.3e}; "
+        f"GPU vs fp32-source oracle max_abs={a32[0]:.3e} rel_l2={a32[1]:.3e}; "
+        f"bf16-input oracle vs fp32-source oracle max_abs={o16.max():.3e} "
+        f"rel_l2={np.linalg.norm(o16) / np.linalg.norm(ref32):.3e}")
+    assert_attn_close(out, res["out"], "tiny fp32 source, bf16 parity")
+    assert_attn_close(out, ref32, "tiny fp32 source, against the fp32 sources")
+
+
 FUSED_CASES = {
     "tiny": (TINY, {}),
     "med_needles": (MED, {}),
