@@ -227,8 +227,8 @@ lci_status lci_decode_fwd(const lci_geom *g, const int8_t *q_idx, const int8_t *
  * device looks up that device's copy (hipGetSymbolAddress). A geometry whose
  * lci_workspace_bytes(LCI_ENTRY_DECODE) exceeds the array returns
  * LCI_ERR_SCRATCH and enqueues nothing (Decode 128K, 64 x 131072 positions,
- * and Decode 1M, 8 x 1048576, both fit: about 12 B per history position plus
- * the split-K partials). Every call on one GPU uses the same array: calls that
+ * and Decode 1M, 8 x 1048576, both fit: about 13 B per history position, the
+ * split-K partials included). Every call on one GPU uses the same array: calls that
  * overlap on one GPU (other streams, other threads) race and must be ordered
  * by the caller. The array keeps the last call's contents; the decode kernels
  * read no workspace byte they have not written in the same call. */

@@ -12,12 +12,12 @@ compared rows):
     scores each whole history and selects on the host; the attention is then
     recomputed on the key/value rows the oracle itself selected (copied out of
     device memory by position: attention does not depend on where a row sits).
-  * Prefill 64K: two whole 4096-row score blocks (rows 4096..12287: the
-    fused entry scores and selects the sequence in blocks of 4096 rows, and
-    these two hold the last rows the dense-tile path takes and the first the
-    gather path takes, so the block seam and the path seam are both inside),
-    plus 32 rows of every other block (its first and last rows and 30 drawn
-    at random), 8640 rows in all.
+  * Prefill 64K: two whole blocks of 4096 rows (rows 4096..12287: rows the
+    long-prefill selection finishes from their candidate lists, sampled and
+    listed-whole rows alike), plus 32 rows of every other block (its first
+    and last rows and 30 drawn at random), 8640 rows in all. The first and
+    last rows of the blocks include rows 32767 and 32768, the last row the
+    dense-tile path takes (p + 1 <= 16 K) and the first the gather path takes.
 
 Planted needle recall is reported."""
 import numpy as np
