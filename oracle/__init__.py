@@ -166,8 +166,10 @@ class Oracle:
         """Gated attention over given index rows. q, gate, mix uint16 [B,Tq,Hq,d] (gate
         may be None: ungated; mix may be None: the gate only scales, else
         out = s*o + (1-s)*mix); k, v uint16 [B,Tk,Hkv,d]; idx int32 [nrows, K] (one
-        set per row) or [nrows, Hkv, K] (one per key/value head) for the listed
-        rows. Returns (out float64 [nrows,Hq,d], lse float64 [nrows,Hq])."""
+        set per row) or [nrows, sets, K] for the listed rows, where query head h
+        reads set h // (Hq // sets) (one set per key/value head with sets = Hkv,
+        per query head with sets = Hq). Returns (out float64 [nrows,Hq,d], lse
+        float64 [nrows,Hq])."""
         q = _c(q, np.uint16)
         k = _c(k, np.uint16)
         v = _c(v, np.uint16)
@@ -181,8 +183,8 @@ class Oracle:
         rb, ri = _rows(rows, B, Tq)
         idx = _c(idx, np.int32)
         sets = idx.shape[1] if idx.ndim == 3 else 1
-        if sets not in (1, Hkv):
-            raise ValueError("one index set per row or one per key/value head")
+        if Hq % sets:
+            raise ValueError("the index sets divide the query heads")
         idx = idx.reshape(len(rb), sets, -1)
         K = idx.shape[2]
         out = np.empty((len(rb), Hq, d), np.float64)
@@ -207,8 +209,8 @@ class Oracle:
         rb, ri = _rows(rows, B, Tq)
         idx = _c(idx, np.int32)
         sets = idx.shape[1] if idx.ndim == 3 else 1
-        if sets not in (1, Hkv):
-            raise ValueError("one index set per row or one per key/value head")
+        if Hq % sets:
+            raise ValueError("the index sets divide the query heads")
         idx = idx.reshape(len(rb), sets, -1)
         K = idx.shape[2]
         out = np.empty((len(rb), Hq, d), np.float64)
@@ -288,9 +290,11 @@ class Oracle:
         of an input dict as produced by ``synth.host_inputs``; an entry "mix" (the
         other branch's output, uint16 [B,Tq,Hq,d]) is mixed in by the gate. With
         block > 1 the selection keeps K blocks of `block` positions: idx holds
-        K*block positions per row and sel the K kept blocks' scores. With sets =
-        Hkv every key/value head has its own index set, scored by its group of
-        H_I/Hkv indexer heads: idx [nrows, Hkv, K or K*block], sel [nrows, Hkv, K].
+        K*block positions per row and sel the K kept blocks' scores. With sets > 1
+        (dividing Hq and H_I) query head h attends over index set h // (Hq // sets),
+        scored by indexer heads g*H_I/sets .. (g+1)*H_I/sets - 1 of set g: sets =
+        Hkv gives one set per key/value head, sets = Hq one per query head;
+        idx [nrows, sets, K or K*block], sel [nrows, sets, K].
         Returns dict(idx, sel, out, lse) with out float64 [nrows,Hq,d]."""
         q_idx = _c(inp["q_idx"], np.int8)
         k_idx = _c(inp["k_idx"], np.int8)
@@ -311,8 +315,8 @@ class Oracle:
         nr = len(rb)
         bl = max(int(block), 1)
         ns = max(int(sets), 1)
-        if ns not in (1, Hkv) or H_I % ns:
-            raise ValueError("sets is 1 or Hkv, and divides H_I")
+        if Hq % ns or H_I % ns:
+            raise ValueError("sets divides Hq and H_I")
         idx = np.empty((nr, ns, K * bl), np.int32)
         sel = np.empty((nr, ns, K), np.int32)
         out = np.empty((nr, Hq, d), np.float64)

@@ -135,8 +135,9 @@ static double orc_gate(double o, double G, const uint16_t *mix, int64_t j)
 
 /* Gated attention of one query row over the listed positions.
  * q, gate, mix [Hq][d]; k, v [kv_rows][Hkv][d] (one sequence); idx [sets][K]:
- * one index set shared by every head (sets = 1), or one per key/value head
- * (sets = Hkv: query head h reads the set of its key/value head h / (Hq/Hkv)).
+ * sets divides Hq, and query head h reads set h / (Hq/sets): one set shared by
+ * every head (sets = 1), one per key/value head (sets = Hkv), one per query
+ * head (sets = Hq).
  * Entries outside 0..kv_len-1 (the -1 padding) are skipped. gate may be NULL
  * (ungated; then mix is ignored), mix may be NULL (no mixing). out [Hq][d],
  * lse [Hq] (natural log of the softmax denominator, including the running
@@ -155,10 +156,11 @@ static void orc_attn_row_ld(int Hq, int Hkv, int d, const void *q, const void *k
                             orc_load ld)
 {
     int G = Hq / Hkv;
+    int hps = Hq / (sets > 1 ? sets : 1);   /* query heads per index set */
     double *logit = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
     for (int h = 0; h < Hq; ++h) {
         int g = h / G;
-        const int32_t *ih = idx + (int64_t)(g * sets / Hkv) * K;   /* this head's index set */
+        const int32_t *ih = idx + (int64_t)(h / hps) * K;   /* this head's index set */
         double m = -INFINITY;
         for (int t = 0; t < K; ++t) {
             int64_t s = ih[t];
@@ -333,13 +335,14 @@ void orc_attn_rows_f32(int Tq, int Tk, int Hq, int Hkv, int d, int K, int sets,
  * With block > 1 the selection keeps K blocks of that many positions
  * (orc_block_topk_row): index rows of K*block positions, sel the K kept
  * blocks' scores; with block <= 1 single positions (K of each).
- * Index sets: sets = 1, one set per query row shared by every head; sets =
- * Hkv, one per key/value head ("Hybrid Sparse Attention for Long-Context
- * LLMs", the pseudocode of the Indexer + Top-K section keeps indices per head;
- * "How Fine-Grained Sparse Attention Reshapes ...", the runtime section's
- * pseudocode likewise). Reading taken for the per-set scorer: the H_I indexer
- * heads are split into sets consecutive groups of H_I/sets heads, and set g is
- * scored by group g alone (its heads and their weights).
+ * Index sets: sets divides Hq and H_I; sets = 1, one set per query row shared
+ * by every head; sets = Hkv, one per key/value head; sets = Hq, one per query
+ * head ("Hybrid Sparse Attention for Long-Context LLMs", the pseudocode of the
+ * Indexer + Top-K section keeps indices per head; "How Fine-Grained Sparse
+ * Attention Reshapes ...", the runtime section's pseudocode likewise). Query
+ * head h attends over set h / (Hq/sets). Reading taken for the per-set scorer:
+ * the H_I indexer heads are split into sets consecutive groups of H_I/sets
+ * heads, and set g is scored by group g alone (its heads and their weights).
  * idx [nrows][sets][K or K*block], sel [nrows][sets][K], out [nrows][Hq][d],
  * lse [nrows][Hq]. Invalid rows give
  * idx = -1, sel = INT32_MIN, an attention output of 0 (out = 0 unless mixed)

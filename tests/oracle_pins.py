@@ -729,42 +729,71 @@ def pin_layer_block_dense_and_composition(orc):
 
 # ------------------------------------------------------------ index sets
 
-def pin_sets_per_kv_head(orc):
-    """One index set per key/value head equals, head by head, the shared-set
-    layer run on that head's own sub-problem: its group of indexer heads and
-    their weights, its query heads, its keys and values (sliced with numpy).
-    Identical indexer groups give every head the shared-set selection."""
+def _set_sub_problem(inp, sets, s):
+    """Set s's own shared-set problem, sliced with numpy: its group of indexer
+    heads and their weights, its query heads (and gates), and the key/value
+    heads those query heads read."""
+    Hq, Hkv, H_I = inp["q"].shape[2], inp["k"].shape[2], inp["q_idx"].shape[2]
+    hps, Hg, G = Hq // sets, H_I // sets, Hq // Hkv
+    k0, k1 = s * hps // G, ((s + 1) * hps - 1) // G + 1
+    sub = dict(inp)
+    sub["q_idx"] = np.ascontiguousarray(inp["q_idx"][:, :, s * Hg:(s + 1) * Hg])
+    sub["w"] = np.ascontiguousarray(inp["w"][s * Hg:(s + 1) * Hg])
+    for n in ("q", "gate"):
+        sub[n] = np.ascontiguousarray(inp[n][:, :, s * hps:(s + 1) * hps])
+    for n in ("k", "v"):
+        sub[n] = np.ascontiguousarray(inp[n][:, :, k0:k1])
+    return sub
+
+
+def pin_sets_sub_problems(orc):
+    """Index sets (query head h reads set h // (Hq/sets), set g scored by its
+    group of indexer heads) equal, set by set, the shared-set layer run on that
+    set's own sub-problem: one set per key/value head, one per query head (two
+    query heads on one key/value head then read different sets), and two sets
+    over four key/value heads. Identical indexer groups give every head the
+    shared-set selection."""
     import synth
-    cfg = synth.CONFIGS["tiny"].replace(B=2, Tq=12, Tk=60, Hq=4, Hkv=2, H_I=4, K=7, decode=False)
+    base = synth.CONFIGS["tiny"].replace(B=2, Tq=12, Tk=60, K=7, decode=False)
+    cases = [  # (Hq, Hkv, H_I, sets)
+        (4, 2, 4, 2),    # one set per key/value head
+        (4, 2, 4, 4),    # one set per query head
+        (8, 4, 4, 2),    # a set spans two key/value heads
+    ]
+    for Hq, Hkv, H_I, sets in cases:
+        cfg = base.replace(Hq=Hq, Hkv=Hkv, H_I=H_I)
+        inp = synth.host_inputs(cfg, seed=15)
+        inp["w"] = np.array([1, 3, 4, 2], np.int8)[:H_I]
+        inp["q_offset"] = np.array([40, 50], np.int32)
+        inp["kv_len"] = np.array([52, 55], np.int32)   # sequence 1 ends in invalid rows
+        hps = Hq // sets
+        for block in (1, 4):
+            K = 3 if block > 1 else cfg.K
+            res = orc.layer(inp, K=K, block=block, sets=sets)
+            for g in range(sets):
+                one = orc.layer(_set_sub_problem(inp, sets, g), K=K, block=block)
+                assert (res["idx"][:, g] == one["idx"]).all()
+                assert (res["sel"][:, g] == one["sel"]).all()
+                assert np.array_equal(res["out"][:, g * hps:(g + 1) * hps], one["out"])
+                assert np.array_equal(res["lse"][:, g * hps:(g + 1) * hps], one["lse"])
+            assert not (res["idx"][:, 0] == res["idx"][:, 1]).all()
+    # every group a copy of group 0: every head keeps the shared-set selection
+    cfg = base.replace(Hq=4, Hkv=2, H_I=4)
     inp = synth.host_inputs(cfg, seed=15)
-    inp["w"] = np.array([1, 3, 4, 2], np.int8)
     inp["q_offset"] = np.array([40, 50], np.int32)
-    inp["kv_len"] = np.array([52, 55], np.int32)   # sequence 1 ends in invalid rows
-    for block in (1, 4):
-        res = orc.layer(inp, K=3 if block > 1 else cfg.K, block=block, sets=2)
-        for g in range(2):
-            sub = dict(inp)
-            sub["q_idx"] = np.ascontiguousarray(inp["q_idx"][:, :, 2 * g:2 * g + 2])
-            sub["w"] = np.ascontiguousarray(inp["w"][2 * g:2 * g + 2])
-            for n in ("q", "gate"):
-                sub[n] = np.ascontiguousarray(inp[n][:, :, 2 * g:2 * g + 2])
-            for n in ("k", "v"):
-                sub[n] = np.ascontiguousarray(inp[n][:, :, g:g + 1])
-            one = orc.layer(sub, K=3 if block > 1 else cfg.K, block=block)
-            assert (res["idx"][:, g] == one["idx"]).all() and (res["sel"][:, g] == one["sel"]).all()
-            assert np.array_equal(res["out"][:, 2 * g:2 * g + 2], one["out"])
-            assert np.array_equal(res["lse"][:, 2 * g:2 * g + 2], one["lse"])
-        assert not (res["idx"][:, 0] == res["idx"][:, 1]).all()
-    # both groups a copy of group 0: every head keeps the shared-set selection
-    dup = dict(inp)
-    dup["q_idx"] = np.ascontiguousarray(np.concatenate([inp["q_idx"][:, :, :2]] * 2, axis=2))
-    dup["w"] = np.array([1, 3, 1, 3], np.int8)
-    res = orc.layer(dup, K=cfg.K, sets=2)
-    base = dict(dup, q_idx=np.ascontiguousarray(inp["q_idx"][:, :, :2]), w=np.array([1, 3], np.int8))
-    shared = orc.layer(base, K=cfg.K)
-    for g in range(2):
-        assert (res["idx"][:, g] == shared["idx"]).all()
-    assert np.array_equal(res["out"], shared["out"])
+    inp["kv_len"] = np.array([52, 55], np.int32)
+    for sets in (2, 4):
+        Hg = 4 // sets
+        dup = dict(inp)
+        dup["q_idx"] = np.ascontiguousarray(np.concatenate([inp["q_idx"][:, :, :Hg]] * sets, axis=2))
+        dup["w"] = np.tile(np.array([1, 3], np.int8)[:Hg], sets)
+        res = orc.layer(dup, K=cfg.K, sets=sets)
+        one = dict(dup, q_idx=np.ascontiguousarray(inp["q_idx"][:, :, :Hg]),
+                   w=np.array([1, 3], np.int8)[:Hg])
+        shared = orc.layer(one, K=cfg.K)
+        for g in range(sets):
+            assert (res["idx"][:, g] == shared["idx"]).all()
+        assert np.array_equal(res["out"], shared["out"])
 
 
 # ------------------------------------------------------------------ backward

@@ -58,8 +58,12 @@ MUTANTS = [
     ("sets_share_group0_heads", "const int8_t *qI = q_idx + (((int64_t)b * Tq + i) * H_I + (int64_t)gs * Hg) * d_I;",
      "const int8_t *qI = q_idx + ((int64_t)b * Tq + i) * H_I * d_I;"),
     ("sets_share_group0_weights", "wr + gs * Hg, p + 1, S);", "wr, p + 1, S);"),
-    ("heads_read_set0", "const int32_t *ih = idx + (int64_t)(g * sets / Hkv) * K;",
+    ("heads_read_set0", "const int32_t *ih = idx + (int64_t)(h / hps) * K;",
      "const int32_t *ih = idx;"),
+    ("sets_by_kv_head", "const int32_t *ih = idx + (int64_t)(h / hps) * K;",
+     "const int32_t *ih = idx + (int64_t)(g * sets / Hkv < sets ? g * sets / Hkv : 0) * K;"),
+    ("sets_by_head_modulo", "const int32_t *ih = idx + (int64_t)(h / hps) * K;",
+     "const int32_t *ih = idx + (int64_t)(h % sets) * K;"),
     ("bwd_no_delta", "double dl = P[t] * (dP[t] - delta);", "double dl = P[t] * dP[t];"),
     ("bwd_gate_derivative", "gy * (o[j] - x) * sg * (1.0 - sg)", "gy * (o[j] - x) * sg * (1.0 + sg)"),
     ("bwd_dk_unscaled", "dkr[j] += scale * dl * orc_bf16(q[hb + j]);", "dkr[j] += dl * orc_bf16(q[hb + j]);"),
