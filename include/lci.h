@@ -94,8 +94,9 @@ typedef struct lci_geom {
                                /* power of two 2..256 = blocks of that many positions,   */
                                /* K then counts blocks (see lci_topk_select)             */
     int32_t sets;              /* index sets per query row: 0 or 1 = one set shared by   */
-                               /* every head; Hkv = one per key/value head (fused        */
-                               /* entries and lci_sparse_attn_fwd only; see below)       */
+                               /* every head; S > 1 = S sets, query head h reading set   */
+                               /* h / (Hq/S): Hkv = one per key/value head, Hq = one per */
+                               /* query head (see below)                                 */
 } lci_geom;
 
 /* Entry ids for lci_workspace_bytes. */
@@ -118,7 +119,9 @@ enum {
  *   w      int8, element (b, i, h) at w[b*w_stride_b + i*w_stride_q + h];
  *          strides in elements, 0 broadcasts (a [H_I] vector uses 0, 0)
  *   scores int32 [B, Tq, Tk] out: S[b,i,s] for s <= p of every valid row; all
- *          other elements are left unwritten.
+ *          other elements are left unwritten. With g->sets = S > 1 (S must
+ *          divide H_I, else SHAPE) set j is scored by indexer heads j*H_I/S ..
+ *          (j+1)*H_I/S - 1 alone and scores is int32 [B, S, Tq, Tk].
  * Errors: NULL, SHAPE, UNSUPPORTED, OVERFLOW_RISK, HIP. Workspace: none. */
 lci_status lci_idx_score(const lci_geom *g, const int8_t *q_idx, const int8_t *k_idx,
                          const int8_t *w, int64_t w_stride_b, int64_t w_stride_q,
@@ -131,6 +134,9 @@ lci_status lci_idx_score(const lci_geom *g, const int8_t *q_idx, const int8_t *k
  *   idx        int32 [B, Tq, K] out: selected positions ascending, -1 padded
  *   sel_scores int32 [B, Tq, K] out, nullable: the score of each idx entry,
  *              INT32_MIN in the padding
+ * With g->sets = S > 1 every array gains a set axis after B (scores
+ * [B, S, Tq, Tk], idx [B, S, Tq, ...], sel_scores [B, S, Tq, K]) and each
+ * set's rows are selected like those of one set.
  * Block-granular selection (g->block = b > 1; same steps: the scorer rates
  * positions or blocks and the top K positions or blocks are kept): block j
  * holds positions j*b .. j*b + b - 1 and rates as its best causal position;
@@ -172,17 +178,18 @@ lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_b
                                const lci_bf16 *mix, float softmax_scale, lci_bf16 *out,
                                float *lse, void *workspace, size_t ws_bytes, void *stream);
 
-/* Index sets per key/value head (g->sets = Hkv > 1). The pages' pseudocode keeps
- * one index row per head ("Hybrid Sparse Attention ...", the pseudocode of the
- * Indexer + Top-K section; "How Fine-Grained Sparse Attention Reshapes ...",
- * section "How Indexer + Top-K Works at Runtime"). The H_I indexer heads split
- * into Hkv consecutive groups of H_I/Hkv heads (H_I must be a multiple of Hkv,
- * else SHAPE); set g is scored by group g alone, with its heads' weights, and
- * selected like a shared set; query head h attends over the set of its
- * key/value head h / (Hq/Hkv). Index rows are then int32 [B, Hkv, Tq, K*max(1,
- * block)] (idx_out of the fused entries, idx of lci_sparse_attn_fwd). These
- * rows take the gather attention kernel. lci_idx_score and lci_topk_select work
- * on one set (sets > 1: UNSUPPORTED). */
+/* Index sets (g->sets = S > 1). The pages' pseudocode keeps one index row per
+ * head ("Hybrid Sparse Attention ...", the pseudocode of the Indexer + Top-K
+ * section, index shape [B, H, Lq, top_k]; "How Fine-Grained Sparse Attention
+ * Reshapes ...", section "How Indexer + Top-K Works at Runtime", index shape
+ * [B, Hq, K]). Query head h attends over set h / (Hq/S): S = Hkv gives one set
+ * per key/value head, S = Hq one per query head (S must divide Hq, else SHAPE).
+ * The H_I indexer heads split into S consecutive groups of H_I/S heads (S must
+ * divide H_I, else SHAPE); set j is scored by group j alone, with its heads'
+ * weights, and selected like a shared set. Index rows are then int32 [B, S,
+ * Tq, K*max(1, block)] (idx_out of the fused entries, idx of
+ * lci_sparse_attn_fwd); lci_idx_score and lci_topk_select take the same set
+ * axis. The gradient entries work on one set (S > 1: UNSUPPORTED). */
 
 /* Fused prefill: steps 1-4 for many query rows per sequence in one call
  * ("Hybrid Sparse Attention ...", section "Engineering and Evaluation

@@ -202,8 +202,10 @@ def _workspace(entry, geom, workspace, device):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def idx_score(q_idx, k_idx, w, q_offset, kv_len, scores=None, stream=None):
-    """Indexer scores int32 [B,Tq,Tk]; only s <= p of each valid row is written."""
+def idx_score(q_idx, k_idx, w, q_offset, kv_len, scores=None, stream=None, sets=1):
+    """Indexer scores int32 [B,Tq,Tk]; only s <= p of each valid row is written.
+    With sets > 1 the indexer heads split into `sets` groups, each scoring its
+    own set: scores [B,sets,Tq,Tk]."""
     import torch
     _dev(q_idx, torch.int8, "q_idx", 4)
     _dev(k_idx, torch.int8, "k_idx", 3)
@@ -213,10 +215,13 @@ def idx_score(q_idx, k_idx, w, q_offset, kv_len, scores=None, stream=None):
     if k_idx.shape[0] != B or k_idx.shape[2] != d_I:
         raise ValueError("k_idx must be [B,Tk,d_I]")
     wsb, wsq = _w_strides(w, B, Tq, H_I)
-    g = make_geom(B, Tq, Tk, 1, q_offset, kv_len, H_I=H_I, d_I=d_I)
+    g = make_geom(B, Tq, Tk, 1, q_offset, kv_len, H_I=H_I, d_I=d_I, sets=sets)
+    shape = (B, Tq, Tk) if sets <= 1 else (B, sets, Tq, Tk)
     if scores is None:
-        scores = torch.empty((B, Tq, Tk), dtype=torch.int32, device=q_idx.device)
-    _dev(scores, torch.int32, "scores", 3)
+        scores = torch.empty(shape, dtype=torch.int32, device=q_idx.device)
+    _dev(scores, torch.int32, "scores", len(shape))
+    if tuple(scores.shape) != shape:
+        raise ValueError(f"scores must be {list(shape)}")
     lib = load_library()
     _check(lib.lci_idx_score(ctypes.byref(g), _ptr(q_idx), _ptr(k_idx), _ptr(w), wsb, wsq,
                              _ptr(scores), _stream(stream)))
@@ -227,17 +232,27 @@ def topk_select(scores, K, q_offset, kv_len, idx=None, sel_scores=None, want_sco
                 workspace=None, stream=None, block=1):
     """Top-K positions int32 [B,Tq,K] (ascending, -1 padded) and optional scores.
     With block > 1, the K best blocks of `block` positions: idx [B,Tq,K*block]
-    holds their positions, sel_scores [B,Tq,K] the blocks' scores."""
+    holds their positions, sel_scores [B,Tq,K] the blocks' scores. Scores of
+    several index sets, [B,sets,Tq,Tk], give idx [B,sets,Tq,K*block] and
+    sel_scores [B,sets,Tq,K]."""
     import torch
-    _dev(scores, torch.int32, "scores", 3)
-    B, Tq, Tk = scores.shape
-    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, block=block)
+    if scores is not None and scores.dim() == 4:
+        _dev(scores, torch.int32, "scores", 4)
+        B, sets, Tq, Tk = scores.shape
+    else:
+        _dev(scores, torch.int32, "scores", 3)
+        (B, Tq, Tk), sets = scores.shape, 1
+    lead = (B, Tq) if scores.dim() == 3 else (B, sets, Tq)
+    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, block=block, sets=sets)
     if idx is None:
-        idx = torch.empty((B, Tq, K * max(block, 1)), dtype=torch.int32, device=scores.device)
+        idx = torch.empty(lead + (K * max(block, 1),), dtype=torch.int32, device=scores.device)
     if want_scores and sel_scores is None:
-        sel_scores = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
-    _dev(idx, torch.int32, "idx", 3)
-    _dev(sel_scores, torch.int32, "sel_scores", 3)
+        sel_scores = torch.empty(lead + (K,), dtype=torch.int32, device=scores.device)
+    _dev(idx, torch.int32, "idx", len(lead) + 1)
+    _dev(sel_scores, torch.int32, "sel_scores", len(lead) + 1)
+    if tuple(idx.shape) != lead + (K * max(block, 1),) or \
+            (sel_scores is not None and tuple(sel_scores.shape) != lead + (K,)):
+        raise ValueError("idx / sel_scores do not match the score rows")
     ws, nb = _workspace(ENTRY_TOPK_SELECT, g, workspace, scores.device)
     lib = load_library()
     _check(lib.lci_topk_select(ctypes.byref(g), _ptr(scores), _ptr(idx), _ptr(sel_scores),
@@ -248,8 +263,10 @@ def topk_select(scores, K, q_offset, kv_len, idx=None, sel_scores=None, want_sco
 def sparse_attn_fwd(q, k, v, idx, gate, scale, kv_len, q_offset=None, out=None, lse=None,
                     want_lse=False, workspace=None, stream=None, mix=None):
     """Gated attention over the listed positions: out bf16 [B,Tq,Hq,d] (and lse).
-    idx int32 [B,Tq,K] (one index set per row) or [B,Hkv,Tq,K] (one per key/value
-    head). With ``mix`` (bf16, the shape of q) the gate mixes: s*o + (1-s)*mix."""
+    idx int32 [B,Tq,K] (one index set per row) or [B,sets,Tq,K] with sets
+    dividing Hq: query head h attends over set h // (Hq // sets) (sets = Hkv:
+    one per key/value head; sets = Hq: one per query head). With ``mix`` (bf16,
+    the shape of q) the gate mixes: s*o + (1-s)*mix."""
     import torch
     _dev(q, torch.bfloat16, "q", 4)
     _dev(k, torch.bfloat16, "k", 4)
@@ -258,8 +275,8 @@ def sparse_attn_fwd(q, k, v, idx, gate, scale, kv_len, q_offset=None, out=None, 
     if idx is not None and idx.dim() == 4:
         sets = idx.shape[1]
         _dev(idx, torch.int32, "idx", 4)
-        if idx.shape[0] != q.shape[0] or idx.shape[2] != q.shape[1] or sets != k.shape[2]:
-            raise ValueError("per-head index rows must be [B,Hkv,Tq,K]")
+        if idx.shape[0] != q.shape[0] or idx.shape[2] != q.shape[1] or q.shape[2] % sets:
+            raise ValueError("per-head index rows must be [B,sets,Tq,K], sets dividing Hq")
         idx3 = idx.view(idx.shape[0], sets * idx.shape[2], idx.shape[3])
     else:
         _dev(idx, torch.int32, "idx", 3)
@@ -352,8 +369,10 @@ def prefill_fwd(q_idx, k_idx, w, q, k, v, gate, scale, q_offset, kv_len, K, out=
                 mix=None, block=1, sets=1):
     """Fused layer for many query rows: returns out (and idx, lse when asked).
     ``mix`` as in ``sparse_attn_fwd``; with block > 1 the selection keeps K blocks
-    of `block` positions and idx rows hold K*block positions; with sets = Hkv
-    every key/value head has its own index set (idx [B,Hkv,Tq,K*block])."""
+    of `block` positions and idx rows hold K*block positions; with sets > 1
+    (dividing Hq and H_I) query head h attends over index set h // (Hq // sets),
+    scored by the set's group of H_I // sets indexer heads (sets = Hkv: one per
+    key/value head; sets = Hq: one per query head; idx [B,sets,Tq,K*block])."""
     return _fused("lci_prefill_fwd", ENTRY_PREFILL, q_idx, k_idx, w, q, k, v, gate, mix, scale,
                   q_offset, kv_len, K, out, lse, idx_out, want_lse, want_idx, workspace, stream,
                   block, sets)

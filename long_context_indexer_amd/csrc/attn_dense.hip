@@ -154,18 +154,26 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   const int tb = nbps - 1 - blk % nbps;  // longest causal range first
   const int i0 = tb * C::BQ;
   const int iend = min(i0 + C::BQ, Tq);
-  // masks, flags and done bytes are per index set ([B][sets][...]): with one
-  // set per key/value head this workgroup reads those of its head g
-  const int sg = sets > 1 ? g : 0;
-  const int64_t srow = (static_cast<int64_t>(b) * sets + sg) * Tq;  // row 0 of this set
+  // masks, flags and done bytes are per index set ([B][sets][...]); query head
+  // h reads set h / hps, so this workgroup's heads g*G .. g*G + G - 1 read
+  // sets s0 .. s0 + nsg - 1
+  const int hps = Hq / sets;
+  const int s0 = g * G / hps;
+  const int nsg = G > hps ? G / hps : 1;
 
-  // the whole token block must be on this path
+  // the whole token block must be on this path, in every set its heads read
+  // (BQ * nsg <= BQ * G = 128 rows)
   int ok = 1;
-  if (threadIdx.x < C::BQ && i0 + static_cast<int>(threadIdx.x) < Tq)
-    ok = flag[srow + i0 + threadIdx.x] != 0;
+  {
+    const int t = threadIdx.x;
+    const int it = i0 + t / nsg;
+    if (t < C::BQ * nsg && it < Tq)
+      ok = flag[(static_cast<int64_t>(b) * sets + s0 + t % nsg) * Tq + it] != 0;
+  }
   const int all_ok = __syncthreads_and(ok);
   // the gather kernel skips the token blocks this kernel takes
-  if (threadIdx.x == 0) done[(static_cast<int64_t>(b) * sets + sg) * nbps + tb] = all_ok ? 1 : 0;
+  if (static_cast<int>(threadIdx.x) < nsg)
+    done[(static_cast<int64_t>(b) * sets + s0 + threadIdx.x) * nbps + tb] = all_ok ? 1 : 0;
   if (all_ok == 0) return;
 
   const int qo = q_offset[b];
@@ -184,6 +192,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   const int h = g * G + r % G;
   const bool rv = i < Tq;
   const int64_t qrow = static_cast<int64_t>(b) * Tq + (rv ? i : 0);
+  const int64_t srow = (static_cast<int64_t>(b) * sets + h / hps) * Tq;  // row 0 of h's set
   const int fl = rv ? flag[srow + i] : 0;
   const uint32_t* mrow = mask + (srow + (rv ? i : 0)) * Wm;
   // every row of this wave keeps all of 0..p (flag 2): tiles entirely at or

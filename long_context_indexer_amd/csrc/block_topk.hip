@@ -110,8 +110,8 @@ __device__ void select_blocks_radix(const uint32_t* key, int nb, int K, int32_t*
 __global__ __launch_bounds__(BT_NT) void block_topk_kernel(
     int Tq, int Tk, int K, int lb, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ scores, int64_t stride,
-    int row_begin, int row_count, int32_t* __restrict__ idx, int32_t* __restrict__ sel,
-    uint32_t* __restrict__ dmask, uint8_t* __restrict__ dflag, int Wm, int lim) {
+    int64_t batch_rows, int row_begin, int row_count, int32_t* __restrict__ idx,
+    int32_t* __restrict__ sel, uint32_t* __restrict__ dmask, uint8_t* __restrict__ dflag, int Wm, int lim) {
   __shared__ __align__(16) uint32_t key[kBlockTopkMaxBlocks];
   __shared__ int32_t blist[kBlockTopkMaxKeep];
   __shared__ uint32_t kept[kBlockTopkMaxBlocks / 32];  // bit j: block j is kept
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(BT_NT) void block_topk_kernel(
   const bool valid = kvl <= Tk && p >= 0 && p < kvl;
   const int n = valid ? static_cast<int>(p + 1) : 0;
   const int nb = (n + block - 1) >> lb;
-  const int32_t* S = scores + (static_cast<int64_t>(b) * row_count + rr) * stride;
+  const int32_t* S = scores + (static_cast<int64_t>(b) * batch_rows + rr) * stride;
 
   // 1. block maxima
   for (int j = t; j < (nb + 31) / 32; j += BT_NT) kept[j] = 0u;
@@ -251,15 +251,15 @@ __global__ __launch_bounds__(BT_NT) void block_topk_kernel(
 
 }  // namespace
 
-hipError_t launch_block_topk(const Geom& g, const int32_t* scores, int64_t stride, int row_begin,
-                             int row_count, int32_t* idx, int32_t* sel, const DenseMasks* dm,
-                             hipStream_t st) {
+hipError_t launch_block_topk(const Geom& g, const int32_t* scores, int64_t stride,
+                             int64_t batch_rows, int row_begin, int row_count, int32_t* idx,
+                             int32_t* sel, const DenseMasks* dm, hipStream_t st) {
   const int lb = __builtin_ctz(static_cast<unsigned>(g.block));
   dim3 grid(static_cast<uint32_t>(row_count), static_cast<uint32_t>(g.B));
   {
     KernelTimer timer(LCI_KERNEL_TOPK, st);
     hipLaunchKernelGGL(block_topk_kernel, grid, dim3(BT_NT), 0, st, g.Tq, g.Tk, g.K, lb,
-                       g.q_offset, g.kv_len, scores, stride, row_begin, row_count, idx, sel,
+                       g.q_offset, g.kv_len, scores, stride, batch_rows, row_begin, row_count, idx, sel,
                        dm ? dm->mask : nullptr, dm ? dm->flag : nullptr, dm ? dm->Wm : 0,
                        dm ? dm->lim : 0);
   }

@@ -16,6 +16,8 @@
 // lane half hf; slot k holds query hf*(16/H_I) + k/H_I, head k%H_I. The output
 // element v of lane l is row 8*(v/4) + 4*(l/32) + v%4, i.e. slot v of half l/32,
 // for column (history position) l%32.
+#include <type_traits>
+
 #include "common.h"
 #include "../../include/lci.h"
 #include "internal.h"
@@ -27,7 +29,8 @@ __global__ __launch_bounds__(256) void idx_score_kernel(
     int Tq, int Tk, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
     const int8_t* __restrict__ w, int64_t wsb, int64_t wsq, int32_t* __restrict__ scores,
-    int64_t row_stride, int row_begin, int row_count, int keys_per_wg) {
+    int64_t row_stride, int64_t batch_rows, int q_heads, int row_begin, int row_count,
+    int keys_per_wg) {
   constexpr int QW = 32 / H_I;   // query rows per wave tile
   constexpr int QH = 16 / H_I;   // query rows per lane half
   constexpr int NCH = D_I / 32;  // 32-deep MFMA steps over d_I
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(
     // unconditional loads (rows past the end read row begin, then zeroed), so
     // they are all in flight together
     const int lrc = ok ? lr : 0;
-    const int8_t* src = q_idx + ((static_cast<int64_t>(b) * Tq + row_begin + lrc) * H_I + ha) * D_I +
+    const int8_t* src = q_idx + ((static_cast<int64_t>(b) * Tq + row_begin + lrc) * q_heads + ha) * D_I +
                         16 * (lane >> 5);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(
     const bool ok = lr < row_count && row < Tq;
     const int64_t p = static_cast<int64_t>(qoff) + row;
     prow[qq] = (ok && p >= 0 && p < kvl) ? static_cast<int>(p) : -1;
-    orow[qq] = (static_cast<int64_t>(b) * row_count + lr) * row_stride;
+    orow[qq] = (static_cast<int64_t>(b) * batch_rows + lr) * row_stride;
     const int64_t wrow = b * wsb + static_cast<int64_t>(ok ? row : row_begin) * wsq;
 #pragma unroll
     for (int h = 0; h < H_I; ++h) {
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256, 5) void idx_score_q16_kernel(
     int Tq, int Tk, const int32_t* __restrict__ q_offset, const int32_t* __restrict__ kv_len,
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx,
     const int8_t* __restrict__ w, int32_t* __restrict__ scores, int64_t row_stride,
-    int row_begin, int row_count, int keys_per_wg) {
+    int64_t batch_rows, int q_heads, int row_begin, int row_count, int keys_per_wg) {
   constexpr int NCH = D_I / 64;  // 64-deep MFMA steps over d_I
   constexpr int U = 2;           // 16-position tiles per step
   const int lane = threadIdx.x & 63;
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(256, 5) void idx_score_q16_kernel(
   v4i bq[H_I][NCH];
   {
     const int lrc = rok ? lr : r0;  // rows past the end read a valid row, then zeroed
-    const int8_t* src = q_idx + (static_cast<int64_t>(b) * Tq + row_begin + lrc) * H_I * D_I +
+    const int8_t* src = q_idx + (static_cast<int64_t>(b) * Tq + row_begin + lrc) * q_heads * D_I +
                         16 * (lane >> 4);
 #pragma unroll
     for (int h = 0; h < H_I; ++h)
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(256, 5) void idx_score_q16_kernel(
   // this lane's row and its causal limit (-1: the row has no position)
   const int64_t p64 = static_cast<int64_t>(qoff) + row_begin + lr;
   const int plim = (rok && p64 >= 0 && p64 < kvl) ? static_cast<int>(p64) : -1;
-  int32_t* orow = scores + (static_cast<int64_t>(b) * row_count + (rok ? lr : r0)) * row_stride;
+  int32_t* orow = scores + (static_cast<int64_t>(b) * batch_rows + (rok ? lr : r0)) * row_stride;
   const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && (row_stride & 3) == 0;
 
   const int8_t* kbase = k_idx + static_cast<int64_t>(b) * Tk * D_I + 16 * (lane >> 4);
@@ -223,7 +226,8 @@ __global__ __launch_bounds__(256, 5) void idx_score_q16_kernel(
 template <int H_I, int D_I>
 static hipError_t launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                             const int8_t* w, int64_t wsb, int64_t wsq, int32_t* scores,
-                            int64_t stride, int row_begin, int row_count, hipStream_t st) {
+                            int64_t stride, int64_t brows, int qh, int row_begin, int row_count,
+                            hipStream_t st) {
   constexpr int QW = 32 / H_I;
   if constexpr (D_I >= 64 && H_I * D_I <= 512) {
     if (wsb == 0 && wsq == 0 && row_count >= 64) {
@@ -234,8 +238,8 @@ static hipError_t launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_
       dim3 grid((g.Tk + keys - 1) / keys, (row_count + 63) / 64, g.B);
       KernelTimer timer(LCI_KERNEL_IDX_SCORE, st);
       hipLaunchKernelGGL((idx_score_q16_kernel<H_I, D_I>), grid, dim3(256), 0, st, g.Tq, g.Tk,
-                         g.q_offset, g.kv_len, q_idx, k_idx, w, scores, stride, row_begin,
-                         row_count, keys);
+                         g.q_offset, g.kv_len, q_idx, k_idx, w, scores, stride, brows, qh,
+                         row_begin, row_count, keys);
       return hipGetLastError();
     }
   }
@@ -247,7 +251,7 @@ static hipError_t launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_
       KernelTimer timer(LCI_KERNEL_IDX_SCORE, st);
       hipLaunchKernelGGL((idx_score_kernel<H_I, D_I, 4>), grid, dim3(256), 0, st, g.Tq, g.Tk,
                          g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, wsq, scores, stride,
-                         row_begin, row_count, keys);
+                         brows, qh, row_begin, row_count, keys);
     }
   } else {
     // few query rows (decode): the 4 waves split the history
@@ -257,7 +261,7 @@ static hipError_t launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_
       KernelTimer timer(LCI_KERNEL_IDX_SCORE, st);
       hipLaunchKernelGGL((idx_score_kernel<H_I, D_I, 1>), grid, dim3(256), 0, st, g.Tq, g.Tk,
                          g.q_offset, g.kv_len, q_idx, k_idx, w, wsb, wsq, scores, stride,
-                         row_begin, row_count, keys);
+                         brows, qh, row_begin, row_count, keys);
     }
   }
   return hipGetLastError();
@@ -266,27 +270,33 @@ static hipError_t launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_
 template <int H_I>
 static hipError_t launch_h(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                            const int8_t* w, int64_t wsb, int64_t wsq, int32_t* scores,
-                           int64_t stride, int row_begin, int row_count, hipStream_t st) {
+                           int64_t stride, int64_t brows, int qh, int row_begin, int row_count,
+                           hipStream_t st) {
   switch (g.d_I) {
-    case 32: return launch_hd<H_I, 32>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
-    case 64: return launch_hd<H_I, 64>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    case 32: return launch_hd<H_I, 32>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, brows, qh, row_begin, row_count, st);
+    case 64: return launch_hd<H_I, 64>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, brows, qh, row_begin, row_count, st);
     case 128:
       if constexpr (H_I * 128 <= 1024)
-        return launch_hd<H_I, 128>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+        return launch_hd<H_I, 128>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, brows, qh, row_begin, row_count, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_idx_score(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
-                            const int8_t* w, int64_t wsb, int64_t wsq, int32_t* scores,
-                            int64_t stride, int row_begin, int row_count, hipStream_t st) {
+hipError_t launch_idx_score(const Geom& g, const int8_t* q_idx, int q_heads,
+                            const int8_t* k_idx, const int8_t* w, int64_t wsb, int64_t wsq,
+                            int32_t* scores, int64_t stride, int64_t batch_rows, int row_begin,
+                            int row_count, hipStream_t st) {
+  auto go = [&](auto heads) {
+    return launch_h<decltype(heads)::value>(g, q_idx, k_idx, w, wsb, wsq, scores, stride,
+                                            batch_rows, q_heads, row_begin, row_count, st);
+  };
   switch (g.H_I) {
-    case 1: return launch_h<1>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
-    case 2: return launch_h<2>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
-    case 4: return launch_h<4>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
-    case 8: return launch_h<8>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
-    case 16: return launch_h<16>(g, q_idx, k_idx, w, wsb, wsq, scores, stride, row_begin, row_count, st);
+    case 1: return go(std::integral_constant<int, 1>{});
+    case 2: return go(std::integral_constant<int, 2>{});
+    case 4: return go(std::integral_constant<int, 4>{});
+    case 8: return go(std::integral_constant<int, 8>{});
+    case 16: return go(std::integral_constant<int, 16>{});
     default: return hipErrorInvalidValue;
   }
 }

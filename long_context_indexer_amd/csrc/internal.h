@@ -31,19 +31,26 @@ struct Geom {
   const int32_t* q_offset;
   const int32_t* kv_len;
   int block;  // selection granularity: 1 = single positions, else blocks of this many
-  int sets;   // index sets per query row: 1, or Hkv (index rows [B][sets][Tq][K])
+  int sets;   // index sets per query row (index rows [B][sets][Tq][K]): a divisor of
+              // Hq; query head h reads set h / (Hq/sets)
 };
 
-// ---- indexer scoring
-hipError_t launch_idx_score(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
-                            const int8_t* w, int64_t w_stride_b, int64_t w_stride_q,
-                            int32_t* scores, int64_t score_row_stride, int row_begin,
-                            int row_count, hipStream_t stream);
+// ---- indexer scoring of query rows [row_begin, row_begin + row_count) of every
+// sequence with g.H_I indexer heads: query row (b, i) holds q_heads >= g.H_I
+// heads of d_I bytes, the first g.H_I of them scored (a set's heads are read in
+// place); the score row of (b, row_begin + r) is written at
+// scores + (b*batch_rows + r)*score_row_stride.
+hipError_t launch_idx_score(const Geom& g, const int8_t* q_idx, int q_heads,
+                            const int8_t* k_idx, const int8_t* w, int64_t w_stride_b,
+                            int64_t w_stride_q, int32_t* scores, int64_t score_row_stride,
+                            int64_t batch_rows, int row_begin, int row_count,
+                            hipStream_t stream);
 
 // ---- Top-K over materialised score rows.
 // Both launchers work on query rows [row_begin, row_begin+row_count) of every
-// sequence; the score row of (b, row_begin + r) is at scores + (b*row_count + r)*stride.
-// idx/sel are always the full [B, Tq, K] arrays.
+// sequence; the score row of (b, row_begin + r) is at
+// scores + (b*batch_rows + r)*stride. idx/sel rows are [B, g.Tq, K]: row
+// (b, row_begin + r) at (b*g.Tq + row_begin + r)*K.
 // Rows of histories up to kWaveTopkMax positions (Tk <= kWaveTopkMax) run one
 // wave per row with the row in registers; longer ones one workgroup per row.
 constexpr int kWaveTopkMax = 8192;
@@ -74,8 +81,8 @@ int dense_row_limit(const Geom& g);
 // With dm (only when Tk <= kWaveTopkMax), the Top-K kernel also writes the
 // dense-path flags and masks of its rows.
 hipError_t launch_topk_rows(const Geom& g, const int32_t* scores, int64_t score_row_stride,
-                            int row_begin, int row_count, int32_t* idx, int32_t* sel,
-                            const DenseMasks* dm, hipStream_t stream);
+                            int64_t batch_rows, int row_begin, int row_count, int32_t* idx,
+                            int32_t* sel, const DenseMasks* dm, hipStream_t stream);
 
 // ---- long-prefill scoring + Top-K without materialised score rows: one wave
 // per 16 query rows samples a threshold, lists the (score, position) pairs at
@@ -115,10 +122,10 @@ hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* 
 constexpr int kBlockTopkMaxBlocks = 8192;  // ceil(Tk / block) at most
 constexpr int kBlockTopkMaxKeep = 2048;    // K at most (K*block <= 4096, block >= 2)
 hipError_t launch_block_topk(const Geom& g, const int32_t* scores, int64_t score_row_stride,
-                             int row_begin, int row_count, int32_t* idx, int32_t* sel,
-                             const DenseMasks* dm, hipStream_t stream);
+                             int64_t batch_rows, int row_begin, int row_count, int32_t* idx,
+                             int32_t* sel, const DenseMasks* dm, hipStream_t stream);
 
-// ---- index sets per key/value head: q_idx [B,Tq,H_I,d_I] regrouped into
+// ---- index sets: q_idx [B,Tq,H_I,d_I] regrouped into
 // [sets][B][Tq][H_I/sets][d_I], so each set's indexer heads form a contiguous
 // query array for the scoring kernels
 hipError_t launch_regroup_q_idx(const Geom& g, const int8_t* q_idx, int8_t* out,

@@ -29,17 +29,17 @@ constexpr int kMaxK = 4096;
 // Positions per selected unit: 1, or the block size of block-granular selection.
 int sel_block(const lci_geom* g) { return g->block > 1 ? g->block : 1; }
 
-// Index sets per query row: 1 (shared by every head), or Hkv.
+// Index sets per query row: 1 (shared by every head), or g->sets.
 int sel_sets(const lci_geom* g) { return g->sets > 1 ? g->sets : 1; }
 
-// Index sets: 1, or one per key/value head; the indexer heads split evenly.
-// `indexer`: the entry also scores (its indexer heads must split into the sets).
-lci_status check_sets(const lci_geom* g, bool indexer) {
+// Index sets: query head h reads set h / (Hq/sets), so with attention the sets
+// divide Hq; with scoring the indexer heads split evenly into them.
+lci_status check_sets(const lci_geom* g, bool indexer, bool attention) {
   if (g->sets < 0) return LCI_ERR_SHAPE;
   const int ns = sel_sets(g);
   if (ns == 1) return LCI_OK;
-  if (ns != g->Hkv) return LCI_ERR_SHAPE;
-  if (indexer && (g->H_I % ns != 0 || g->H_I < ns)) return LCI_ERR_SHAPE;
+  if (attention && g->Hq % ns != 0) return LCI_ERR_SHAPE;
+  if (indexer && g->H_I % ns != 0) return LCI_ERR_SHAPE;
   return LCI_OK;
 }
 
@@ -140,10 +140,12 @@ PrefillLayout prefill_layout(const lci_geom* g, int64_t wsb = 0, int64_t wsq = 0
             : align_up(static_cast<size_t>(g->B) * L.chunk_rows * g->Tk * sizeof(int32_t));
   L.attn_off = L.score_off + L.score_bytes;
   L.attn_bytes = align_up(lci::sparse_attn_workspace(gg, L.splits));
-  // the query rows regrouped by index set
+  // the query rows regrouped by index set (for the long-prefill kernels; the
+  // scoring kernel reads a set's heads in place)
   L.qg_off = L.attn_off + L.attn_bytes;
-  L.qg_bytes =
-      sel_sets(g) > 1 ? align_up(static_cast<size_t>(g->B) * g->Tq * g->H_I * g->d_I) : 0;
+  L.qg_bytes = L.sel && sel_sets(g) > 1
+                   ? align_up(static_cast<size_t>(g->B) * g->Tq * g->H_I * g->d_I)
+                   : 0;
   L.sel_off = L.qg_off + L.qg_bytes;
   L.sel_bytes = L.sel ? align_up(lci::sel_layout(gs).total) : 0;
   L.total = L.sel_off + L.sel_bytes;
@@ -186,13 +188,13 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
     case LCI_ENTRY_TOPK_SELECT:
       return 0;
     case LCI_ENTRY_SPARSE_ATTN: {
-      if (check_attention(g) != LCI_OK || check_sets(g, false) != LCI_OK) return 0;
+      if (check_attention(g) != LCI_OK || check_sets(g, false, true) != LCI_OK) return 0;
       const Geom gg = attn_geom(g);
       return lci::sparse_attn_workspace(gg, lci::sparse_attn_pick_splits(gg));
     }
     case LCI_ENTRY_PREFILL:
       if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK ||
-          check_sets(g, true) != LCI_OK)
+          check_sets(g, true, true) != LCI_OK)
         return 0;
       // the weights' strides are not known here: enough for either scoring path
       return std::max(prefill_layout(g, 0, 0).total, prefill_layout(g, 1, 1).total);
@@ -205,7 +207,7 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
       return lci::ibwd_workspace(to_geom(g));
     case LCI_ENTRY_DECODE:
       if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK || g->Tq != 1 ||
-          check_sets(g, true) != LCI_OK)
+          check_sets(g, true, true) != LCI_OK)
         return 0;
       // block-granular or per-head-set decode runs the prefill path on its one row
       if (sel_block(g) > 1 || sel_sets(g) > 1)
@@ -234,14 +236,22 @@ lci_status lci_idx_score(const lci_geom* g, const int8_t* q_idx, const int8_t* k
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if ((s = check_indexer(g)) != LCI_OK) return s;
-  if (g->sets < 0) return LCI_ERR_SHAPE;
-  if (sel_sets(g) > 1) return LCI_ERR_UNSUPPORTED;
+  if ((s = check_sets(g, true, false)) != LCI_OK) return s;
   if (!q_idx || !k_idx || !w || !scores) return LCI_ERR_NULL;
   if (w_stride_b < 0 || w_stride_q < 0) return LCI_ERR_SHAPE;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(scores)) return LCI_ERR_ALIGN;
-  const Geom gg = to_geom(g);
-  return hip_status(lci::launch_idx_score(gg, q_idx, k_idx, w, w_stride_b, w_stride_q, scores,
-                                          g->Tk, 0, g->Tq, static_cast<hipStream_t>(stream)));
+  // set g: indexer heads g*Hg .. g*Hg + Hg - 1 read in place from the query
+  // rows, their weights, score rows [B][sets][Tq][Tk]
+  const Geom gs = set_geom(g);
+  const int ns = gs.sets;
+  for (int set = 0; set < ns; ++set) {
+    hipError_t e = lci::launch_idx_score(
+        gs, q_idx + static_cast<size_t>(set) * gs.H_I * g->d_I, g->H_I, k_idx,
+        w + set * gs.H_I, w_stride_b, w_stride_q, scores + static_cast<size_t>(set) * g->Tq * g->Tk,
+        g->Tk, static_cast<int64_t>(ns) * g->Tq, 0, g->Tq, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return LCI_OK;
 }
 
 lci_status lci_topk_select(const lci_geom* g, const int32_t* scores, int32_t* idx,
@@ -251,17 +261,29 @@ lci_status lci_topk_select(const lci_geom* g, const int32_t* scores, int32_t* id
   (void)ws_bytes;
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
-  if (g->sets < 0) return LCI_ERR_SHAPE;
-  if (sel_sets(g) > 1) return LCI_ERR_UNSUPPORTED;
+  if ((s = check_sets(g, false, false)) != LCI_OK) return s;
   if (!scores || !idx) return LCI_ERR_NULL;
   if (!aligned4(scores) || !aligned4(idx) || (sel_scores && !aligned4(sel_scores)))
     return LCI_ERR_ALIGN;
-  const Geom gg = to_geom(g);
-  if (gg.block > 1)
-    return hip_status(lci::launch_block_topk(gg, scores, g->Tk, 0, g->Tq, idx, sel_scores,
-                                             nullptr, static_cast<hipStream_t>(stream)));
-  return hip_status(lci::launch_topk_rows(gg, scores, g->Tk, 0, g->Tq, idx, sel_scores, nullptr,
-                                          static_cast<hipStream_t>(stream)));
+  // rows [B][sets][Tq]: the kernels address index rows as b*Tq' + row with
+  // Tq' = sets*Tq, and set g's rows start g*Tq rows in
+  const int ns = sel_sets(g);
+  Geom gsel = to_geom(g);
+  gsel.Tq = g->Tq * ns;
+  const int KI = g->K * gsel.block;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int set = 0; set < ns; ++set) {
+    const size_t r0 = static_cast<size_t>(set) * g->Tq;
+    const int32_t* sc = scores + r0 * g->Tk;
+    int32_t* is = idx + r0 * KI;
+    int32_t* ss = sel_scores ? sel_scores + r0 * g->K : nullptr;
+    const int64_t brows = static_cast<int64_t>(ns) * g->Tq;
+    hipError_t e = gsel.block > 1
+                       ? lci::launch_block_topk(gsel, sc, g->Tk, brows, 0, g->Tq, is, ss, nullptr, st)
+                       : lci::launch_topk_rows(gsel, sc, g->Tk, brows, 0, g->Tq, is, ss, nullptr, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return LCI_OK;
 }
 
 lci_status lci_sparse_attn_fwd(const lci_geom* g, const lci_bf16* q, const lci_bf16* k,
@@ -271,7 +293,7 @@ lci_status lci_sparse_attn_fwd(const lci_geom* g, const lci_bf16* q, const lci_b
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
-  if ((s = check_sets(g, false)) != LCI_OK) return s;
+  if ((s = check_sets(g, false, true)) != LCI_OK) return s;
   if (!q || !k || !v || !idx || !out || (mix && !gate)) return LCI_ERR_NULL;
   if (!scale_ok(softmax_scale)) return LCI_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
@@ -298,7 +320,7 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   if (s != LCI_OK) return s;
   if ((s = check_indexer(g)) != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
-  if ((s = check_sets(g, true)) != LCI_OK) return s;
+  if ((s = check_sets(g, true, true)) != LCI_OK) return s;
   if (!q_idx || !k_idx || !w || !q || !k || !v || !out || (mix && !gate)) return LCI_ERR_NULL;
   if (wsb < 0 || wsq < 0 || !scale_ok(scale)) return LCI_ERR_SHAPE;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(k) ||
@@ -319,23 +341,24 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   // for rows short enough for its one-wave form
   const bool masks = L.splits == 1 && (gg.block > 1 || g->Tk <= lci::kWaveTopkMax);
   const lci::DenseMasks dm = masks ? lci::dense_masks(ga, ws + L.attn_off) : lci::DenseMasks{};
-  // index sets per key/value head: set g is scored as an indexer of H_I/sets
-  // heads (its rows of the regrouped query array, its weights) and its index
-  // rows go to [B][sets][Tq][K*block] (the selection kernels address rows as
+  // index sets: set g is scored as an indexer of H_I/sets heads (heads
+  // g*Hg .. g*Hg + Hg - 1 of the query rows, their weights) and its index rows
+  // go to [B][sets][Tq][K*block] (the selection kernels address rows as
   // b*Tq' + row, so Tq' = sets*Tq and an offset of g*Tq rows place them)
   const Geom gs = set_geom(g);
   Geom gsel = gg;
   gsel.Tq = g->Tq * gg.sets;
-  const int8_t* qsrc = q_idx;
-  if (gg.sets > 1) {
-    int8_t* qg = reinterpret_cast<int8_t*>(ws + L.qg_off);
-    hipError_t e = lci::launch_regroup_q_idx(gg, q_idx, qg, st);
-    if (e != hipSuccess) return hip_status(e);
-    qsrc = qg;
-  }
-  const size_t qset = static_cast<size_t>(g->B) * g->Tq * gs.H_I * g->d_I;
   if (L.sel) {
-    // long prefill: scores never leave the chip
+    // long prefill: scores never leave the chip; its kernels take each set's
+    // query heads as a contiguous array
+    const int8_t* qsrc = q_idx;
+    if (gg.sets > 1) {
+      int8_t* qg = reinterpret_cast<int8_t*>(ws + L.qg_off);
+      hipError_t e = lci::launch_regroup_q_idx(gg, q_idx, qg, st);
+      if (e != hipSuccess) return hip_status(e);
+      qsrc = qg;
+    }
+    const size_t qset = static_cast<size_t>(g->B) * g->Tq * gs.H_I * g->d_I;
     for (int set = 0; set < gg.sets; ++set) {
       int32_t* iset = idx + static_cast<size_t>(set) * g->Tq * ga.K;
       hipError_t e = lci::launch_sel(gs, qsrc + set * qset, k_idx, w + set * gs.H_I, iset,
@@ -346,8 +369,9 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   for (int r0 = 0; !L.sel && r0 < g->Tq; r0 += L.chunk_rows) {
     const int rc = std::min(L.chunk_rows, g->Tq - r0);
     for (int set = 0; set < gg.sets; ++set) {
-      hipError_t e = lci::launch_idx_score(gs, qsrc + set * qset, k_idx, w + set * gs.H_I, wsb,
-                                           wsq, sc, g->Tk, r0, rc, st);
+      hipError_t e = lci::launch_idx_score(
+          gs, q_idx + static_cast<size_t>(set) * gs.H_I * g->d_I, g->H_I, k_idx,
+          w + set * gs.H_I, wsb, wsq, sc, g->Tk, rc, r0, rc, st);
       if (e != hipSuccess) return hip_status(e);
       int32_t* iset = idx + static_cast<size_t>(set) * g->Tq * ga.K;
       // this set's masks and flags: rows [B][sets][Tq] like the index rows
@@ -357,9 +381,9 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
         dms.flag += static_cast<size_t>(set) * g->Tq;
       }
       e = gg.block > 1
-              ? lci::launch_block_topk(gsel, sc, g->Tk, r0, rc, iset, nullptr,
+              ? lci::launch_block_topk(gsel, sc, g->Tk, rc, r0, rc, iset, nullptr,
                                        masks ? &dms : nullptr, st)
-              : lci::launch_topk_rows(gsel, sc, g->Tk, r0, rc, iset, nullptr,
+              : lci::launch_topk_rows(gsel, sc, g->Tk, rc, r0, rc, iset, nullptr,
                                       masks ? &dms : nullptr, st);
       if (e != hipSuccess) return hip_status(e);
     }
@@ -387,7 +411,7 @@ lci_status lci_decode_fwd(const lci_geom* g, const int8_t* q_idx, const int8_t* 
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if (g->Tq != 1) return LCI_ERR_SHAPE;
-  // block-granular selection or index sets per key/value head: the prefill path
+  // block-granular selection or several index sets: the prefill path
   // on the one row (block selection works on at most kBlockTopkMaxBlocks
   // blocks, which bounds the history)
   if (sel_block(g) > 1 || sel_sets(g) > 1)

@@ -6,13 +6,16 @@
 // that modulates the output per head and feature; "From Linear Attention to
 // Gated Sparse Attention", section 2 (the gate multiplies the attention output).
 //
-// One workgroup per (query row, split of its index list); one wave per key/value
-// head g, which serves that head's G = Hq/Hkv query heads (grouped-query
-// attention). Per chunk of 16 listed positions a wave
+// One workgroup per (query row, split of its index list, group of up to 8
+// waves); each wave serves a unit of Gu query heads that read one key/value
+// head and one index set: with one index set per row or per key/value head the
+// unit is a key/value head's G = Hq/Hkv query heads (grouped-query attention),
+// with more sets than key/value heads it is one set's Hq/sets query heads.
+// Per chunk of 16 positions of its index set a wave
 //   - gathers the 16 key rows of head g straight into MFMA A-operand registers
 //     (each lane loads 16 contiguous bytes of one row),
 //   - computes S^T = K_sel . Q^T on v_mfma_f32_16x16x32_bf16 (rows = keys,
-//     columns = the G query heads), so lane l holds keys 4*(l/16)+i of head l%16,
+//     columns = the Gu query heads), so lane l holds keys 4*(l/16)+i of head l%16,
 //   - updates an online softmax in base 2 (logits pre-scaled by scale*log2 e),
 //   - rounds P to bf16; its register layout is already the B operand of
 //     O^T += V^T . P on v_mfma_f32_16x16x16bf16_1k,
@@ -106,47 +109,53 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(int Hq, int splits,
 
 template <int D>
 __global__ __launch_bounds__(512) void sparse_attn_kernel(
-    int Tq, int Tk, int K, int Hq, int Hkv, int G, const int32_t* __restrict__ kv_len,
+    int Tq, int Tk, int K, int Hq, int Hkv, int G, int sets, int Gu, int nck,
+    const int32_t* __restrict__ kv_len,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ gate, const uint16_t* __restrict__ mix, float scale_log2,
     uint16_t* __restrict__ out,
     float* __restrict__ lse, int splits, int per_split, float* __restrict__ part,
-    const uint8_t* __restrict__ done, int dbq, int64_t nitems, int sets) {
+    const uint8_t* __restrict__ done, int dbq, int64_t nitems) {
   using C = AttnCfg<D>;
-  // [Hkv][16][PITCH]; 16-byte aligned wherever the dynamic LDS region starts:
+  // [waves][16][PITCH]; 16-byte aligned wherever the dynamic LDS region starts:
   // its 8-byte writes and transposed reads need aligned rows
   extern __shared__ __align__(16) uint16_t vstage[];
   const int lane = threadIdx.x & 63;
-  const int g = threadIdx.x >> 6;
-  // work items (b*Tq + row)*splits + split, strided over the grid; the waves
-  // of a workgroup share no LDS and no barrier, so an item ends by returning
-  // from the per-item body
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  // work items ((b*Tq + row)*splits + split)*nck + chunk of units, strided over
+  // the grid; the waves of a workgroup share no LDS and no barrier, so an item
+  // ends by returning from the per-item body
   for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) [&] {
-  const int split = static_cast<int>(item % splits);
-  const int64_t qrow = item / splits;
+  const int64_t rs = item / nck;
+  const int split = static_cast<int>(rs % splits);
+  const int64_t qrow = rs / splits;
   const int b = static_cast<int>(qrow / Tq);
+  // this wave's unit: query heads h0 .. h0 + Gu - 1, of key/value head g and
+  // index set sg (query head h reads set h / (Hq/sets))
+  const int h0 = (static_cast<int>(item % nck) * nw + wv) * Gu;
+  const int g = h0 / G;
+  const int sg = h0 / (Hq / sets);
   if (done) {
     // token blocks the tile kernel took (for this wave's index set) are finished
     const int i = static_cast<int>(qrow % Tq);
     const int nbps = (Tq + dbq - 1) / dbq;
-    const int sg = sets > 1 ? static_cast<int>(threadIdx.x >> 6) : 0;
     if (done[(static_cast<int64_t>(b) * sets + sg) * nbps + i / dbq]) return;
   }
   const int kvl0 = kv_len[b];
   const int kvl = kvl0 <= Tk ? kvl0 : 0;  // a history longer than its allocation: no entry is read
   const int e_begin = split * per_split;
   const int nent = max(0, min(per_split, K - e_begin));
-  // index rows [B][sets][Tq][K]: with one set per key/value head, wave g reads
-  // the row of its own head
-  const int64_t irow = sets > 1 ? qrow + (static_cast<int64_t>(b) * (sets - 1) + g) * Tq : qrow;
+  // index rows [B][sets][Tq][K]: the wave reads the row of its own set
+  const int64_t irow = qrow + (static_cast<int64_t>(b) * (sets - 1) + sg) * Tq;
   const int32_t* ip = idx + irow * K + e_begin;
-  uint16_t* vs = vstage + g * 16 * C::PITCH;
+  uint16_t* vs = vstage + wv * 16 * C::PITCH;
 
   const int hl = lane & 15;     // this lane's query-head column
   const int grp = lane >> 4;    // lane group 0..3
-  const bool hok = hl < G;
-  const int h = g * G + hl;
+  const bool hok = hl < Gu;
+  const int h = h0 + hl;
 
   v8bf qf[C::NCH];
   {
@@ -372,17 +381,23 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
     if (masks_ready && g.Tk <= dm.lim) return hipSuccess;
     done = dm.done;
   }
-  // a grid of up to 8192 waves strides over the items (rows x splits), so
-  // items the tile kernel finished cost one byte read each
-  const int64_t nitems = static_cast<int64_t>(g.B) * g.Tq * splits;
-  dim3 grid(static_cast<uint32_t>(std::min<int64_t>(nitems, 8192 / g.Hkv)));
-  const size_t lds = static_cast<size_t>(g.Hkv) * 16 * C::PITCH * sizeof(uint16_t);
+  // wave units of a row: the key/value heads, or the index sets when there are
+  // more sets than key/value heads; up to 8 of them per workgroup
+  const int units = std::max(g.sets, g.Hkv);
+  const int Gu = g.Hq / units;
+  const int nw = std::min(units, 8);
+  const int nck = units / nw;
+  // a grid of up to 8192 waves strides over the items (rows x splits x unit
+  // chunks), so items the tile kernel finished cost one byte read each
+  const int64_t nitems = static_cast<int64_t>(g.B) * g.Tq * splits * nck;
+  dim3 grid(static_cast<uint32_t>(std::min<int64_t>(nitems, 8192 / nw)));
+  const size_t lds = static_cast<size_t>(nw) * 16 * C::PITCH * sizeof(uint16_t);
   {
     KernelTimer timer(LCI_KERNEL_ATTN_GATHER, st);
-    hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * g.Hkv), lds, st, g.Tq, g.Tk, g.K,
-                       g.Hq, g.Hkv, G, g.kv_len, q, k, v, idx, gate, mix, scale * LOG2E, out, lse,
-                       splits, per_split, static_cast<float*>(ws), done, dense_block_rows(G),
-                       nitems, g.sets);
+    hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * nw), lds, st, g.Tq, g.Tk, g.K,
+                       g.Hq, g.Hkv, G, g.sets, Gu, nck, g.kv_len, q, k, v, idx, gate, mix,
+                       scale * LOG2E, out, lse, splits, per_split, static_cast<float*>(ws), done,
+                       dense_block_rows(G), nitems);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;

@@ -32,7 +32,7 @@ namespace lci {
 __global__ __launch_bounds__(TOPK_NT) void topk_rows_kernel(
     int Tq, int Tk, int K, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ scores, int64_t stride,
-    int row_begin, int row_count, int32_t* __restrict__ idx, int32_t* __restrict__ sel) {
+    int64_t batch_rows, int row_begin, int row_count, int32_t* __restrict__ idx, int32_t* __restrict__ sel) {
   __shared__ union {
     SelectLds radix;
     Select2Lds mask2;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(TOPK_NT) void topk_rows_kernel(
   const int64_t p = static_cast<int64_t>(q_offset[b]) + row;
   const bool valid = kvl <= Tk && p >= 0 && p < kvl;
   const int64_t n = valid ? p + 1 : 0;
-  const int32_t* S = scores + (static_cast<int64_t>(b) * row_count + rr) * stride;
+  const int32_t* S = scores + (static_cast<int64_t>(b) * batch_rows + rr) * stride;
 
   if (n <= K) {  // every candidate is kept (dense-equivalent row) or the row is invalid
     for (int j = threadIdx.x; j < K; j += TOPK_NT) {
@@ -142,7 +142,7 @@ __device__ __forceinline__ uint32_t scan_b4(uint32_t v, int wv, uint32_t* red, u
 __global__ __launch_bounds__(B4_NT, 6) void topk_b4_kernel(
     int Tq, int Tk, int K, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ scores, int64_t stride,
-    int row_begin, int row_count, int32_t* __restrict__ idx, int32_t* __restrict__ sel,
+    int64_t batch_rows, int row_begin, int row_count, int32_t* __restrict__ idx, int32_t* __restrict__ sel,
     uint32_t* __restrict__ dmask, uint8_t* __restrict__ dflag, int Wm, int lim) {
   // histogram (+ one dummy word per thread), staged output row (+ dummies)
   __shared__ __align__(16) uint32_t hist[TOPK_BINS + B4_NT];
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(B4_NT, 6) void topk_b4_kernel(
   const int64_t p = static_cast<int64_t>(q_offset[b]) + row;
   const bool valid = kvl <= Tk && p >= 0 && p < kvl;
   const int n = valid ? static_cast<int>(p + 1) : 0;  // n <= Tk <= kWaveTopkMax
-  const int32_t* S = scores + (static_cast<int64_t>(b) * row_count + rr) * stride;
+  const int32_t* S = scores + (static_cast<int64_t>(b) * batch_rows + rr) * stride;
 
   if (n <= K) {  // every candidate is kept (dense-equivalent row) or the row is invalid
     for (int j = t; j < K; j += B4_NT) {
@@ -377,13 +377,14 @@ __global__ __launch_bounds__(B4_NT, 6) void topk_b4_kernel(
 }
 
 hipError_t launch_topk_rows(const Geom& g, const int32_t* scores, int64_t stride,
-                            int row_begin, int row_count, int32_t* idx, int32_t* sel,
+                            int64_t batch_rows, int row_begin, int row_count, int32_t* idx,
+                            int32_t* sel,
                             const DenseMasks* dm, hipStream_t st) {
   if (g.Tk <= kWaveTopkMax) {
     dim3 grid(row_count, g.B);
     KernelTimer timer(LCI_KERNEL_TOPK, st);
     hipLaunchKernelGGL(topk_b4_kernel, grid, dim3(B4_NT), 0, st, g.Tq, g.Tk, g.K, g.q_offset,
-                       g.kv_len, scores, stride, row_begin, row_count, idx, sel,
+                       g.kv_len, scores, stride, batch_rows, row_begin, row_count, idx, sel,
                        dm ? dm->mask : nullptr, dm ? dm->flag : nullptr, dm ? dm->Wm : 0,
                        dm ? dm->lim : 0);
     return hipGetLastError();
@@ -393,7 +394,7 @@ hipError_t launch_topk_rows(const Geom& g, const int32_t* scores, int64_t stride
   {
     KernelTimer timer(LCI_KERNEL_TOPK, st);
     hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(TOPK_NT), 0, st, g.Tq, g.Tk, g.K,
-                       g.q_offset, g.kv_len, scores, stride, row_begin, row_count, idx, sel);
+                       g.q_offset, g.kv_len, scores, stride, batch_rows, row_begin, row_count, idx, sel);
   }
   return hipGetLastError();
 }

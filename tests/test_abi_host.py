@@ -131,17 +131,23 @@ def test_block_granularity_limits(lib):
 
 
 def test_index_set_limits(lib):
-    # one index set per key/value head: sets = Hkv, indexer heads split evenly
+    # query head h reads set h / (Hq/sets): the sets divide Hq (8); the indexer
+    # heads (8) split evenly into them
     assert attn(lib, geom(sets=-1)) == SHAPE
-    assert attn(lib, geom(sets=3)) == SHAPE                   # Hkv = 2
+    assert attn(lib, geom(sets=3)) == SHAPE                   # does not divide Hq
+    assert attn(lib, geom(sets=16)) == SHAPE                  # more sets than query heads
     assert fused(lib, geom(sets=2, H_I=1, d_I=64)) == SHAPE   # 1 indexer head for 2 sets
-    assert score(lib, geom(sets=2)) == UNSUP                  # scores of one set only
-    assert lib.lci_topk_select(ctypes.byref(geom(sets=2)), FAKE, FAKE, None, None, 0,
-                               None) == UNSUP
-    g = geom(sets=2, Tk=4096, K=64)
-    need = lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g))
-    assert need >= 2 * 16 * 64 * 4 + 16 * 8 * 64         # index rows of both sets + queries
-    assert fused(lib, g, nb=need - 1) == WS
+    assert fused(lib, geom(sets=8, H_I=4, d_I=64)) == SHAPE   # 4 indexer heads for 8 sets
+    assert score(lib, geom(sets=3)) == SHAPE
+    assert score(lib, geom(sets=16)) == SHAPE
+    assert lib.lci_topk_select(ctypes.byref(geom(sets=-1)), FAKE, FAKE, None, None, 0,
+                               None) == SHAPE
+    for sets in (2, 4, 8):   # per key/value head, between, per query head
+        g = geom(sets=sets, Tk=4096, K=64)
+        need = lib.lci_workspace_bytes(lci.ENTRY_PREFILL, ctypes.byref(g))
+        assert need >= sets * 16 * 64 * 4                     # index rows of every set
+        assert lib.lci_workspace_bytes(lci.ENTRY_SPARSE_ATTN, ctypes.byref(g)) > 0
+        assert fused(lib, g, nb=need - 1) == WS
 
 
 def test_backward_arguments(lib):

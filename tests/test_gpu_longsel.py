@@ -9,7 +9,7 @@ finished from their list, and rows the list cannot finish (every score equal:
 the list overflows; a planted pattern that makes the sampled threshold too
 high: the list holds fewer than K) redone from their whole score row. Also:
 ties at the K-th score, ragged and invalid rows, continuation rows, index sets
-per key/value head, both indexer widths, K = 64 and K = 4096, one indexer
+per key/value head and per query head, both indexer widths, K = 64 and K = 4096, one indexer
 head, and the gate mix."""
 import numpy as np
 import pytest
@@ -59,6 +59,9 @@ CASES = {
     # the sample sees only the planted high scores: lists shorter than K (redo)
     "sample_too_high": (BASE, dict(q_offset=[3807]), plant_stride_pattern),
     "sets_per_kv_head": (BASE.replace(Hq=4, Hkv=2, H_I=8), dict(q_offset=[3807], sets=2), None),
+    # one set per query head (two query heads per key/value head, one indexer head each)
+    "sets_per_query_head": (BASE.replace(Hq=4, Hkv=2, H_I=4), dict(q_offset=[3807], sets=4),
+                            None),
     "h4_d128": (BASE.replace(H_I=4, d_I=128), dict(q_offset=[3807]), None),
     "k64": (BASE.replace(K=64), dict(q_offset=[3807]), None),
     "k4096": (BASE.replace(K=4096, Tk=20000), dict(q_offset=[11807]), None),
