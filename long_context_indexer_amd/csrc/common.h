@@ -108,4 +108,17 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
   return res;
 }
 
+// dword 3 of a raw buffer resource on gfx9-class parts: 32-bit data format.
+// Loads past the resource's size read zero; stores past it are dropped.
+constexpr int kBufferFlags = 0x00020000;
+
+// A workgroup-uniform pointer, moved to scalar registers (buffer resources must
+// live there; without this the compiler may loop over lanes to build them).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 }  // namespace lci

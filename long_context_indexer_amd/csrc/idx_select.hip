@@ -9,32 +9,37 @@
 // back twice for every row it is 17 GB of traffic. Here the scores stay in
 // registers:
 //
-//   sel_scan_kernel   one wave per 16 consecutive query rows of a sequence. For
-//                     rows with more than `cap` candidates, two sampled passes
-//                     set a per-row threshold t: every 32nd position fills a
-//                     64-bin histogram (sign and bit length of the score), which
-//                     names the coarse bin holding the estimated K-th score;
-//                     every 8th position then fills 256 linear sub-bins of that
-//                     bin. t is the lowest score of the sub-bin where the count
-//                     of sampled scores at or above it first reaches
-//                     K*f + 4*sqrt(K*f) + 2 (f: the sampled fraction of the row),
-//                     so that about K + 4 standard deviations of the row's
-//                     positions score at least t. One full pass then scores every
-//                     causal position (int8 MFMA 16x16x64, positions as MFMA rows,
-//                     one indexer head per MFMA, as in the scoring kernel) and
-//                     appends each (score, position) with score >= t to the row's
-//                     candidate list (LDS counters, at most cap stored). Rows
-//                     with at most cap candidates take every position.
+//   sel_scan_kernel   one workgroup of four waves per 16 consecutive query rows
+//                     of a sequence, each wave taking every fourth step of each
+//                     sweep. For rows with more than `cap` candidates, two
+//                     sampled passes set a per-row threshold t: every 32nd
+//                     position fills a 64-bin histogram (sign and bit length of
+//                     the score), which names the coarse bin holding the
+//                     estimated K-th score; every 8th position then fills 256
+//                     linear sub-bins of that bin. t is the lowest score of the
+//                     sub-bin where the count of sampled scores at or above it
+//                     first reaches K*f + 4*sqrt(K*f) + 2 (f: the sampled
+//                     fraction of the row), so that about K + 4 standard
+//                     deviations of the row's positions score at least t. One
+//                     full pass then scores every causal position (int8 MFMA
+//                     16x16x64, positions as MFMA rows, one indexer head per
+//                     MFMA, as in the scoring kernel) and appends each (score,
+//                     position) with score >= t to the scanning lane's part of
+//                     the row's candidate list (16 parts of cap/16 entries, one
+//                     per wave and lane of the row, each counted in a
+//                     register). Rows with few positions may list every one.
 //   sel_rows_kernel   one workgroup per row. When the list holds every position
-//                     whose score is >= t and at least K of them (count in
-//                     [K, cap]), the row's Top-K is the Top-K of the list: an
-//                     exact radix select of the K-th key under (score desc,
-//                     position asc) over the list in LDS, the kept positions set
-//                     in an LDS bit map of the row (ties at the K-th score: the
-//                     lowest positions), and an ordered compaction of the map
-//                     writes the ascending index row. Any other count (the
-//                     threshold missed: too few or too many scores >= t) puts the
-//                     row on the fallback list.
+//                     whose score is >= t and at least K of them (no part past
+//                     its capacity, K or more in all), the row's Top-K is the
+//                     Top-K of the list: a histogram of the listed keys names
+//                     the bin of the K-th key under (score desc, position asc),
+//                     keys above it are kept and the bin's own entries ranked by
+//                     direct count in LDS, the kept positions set in an LDS bit
+//                     map of the row (ties at the K-th score: the lowest
+//                     positions), and an ordered compaction of the map writes
+//                     the ascending index row. Any other count (the threshold
+//                     missed: too few or too many scores >= t) puts the row on
+//                     the fallback list.
 //   sel_fallback_kernel  the listed rows, exactly as the materialised path does
 //                     them: the row's scores into a scratch row, then the same
 //                     one-workgroup selection (select_row_2pass, or the radix
@@ -56,6 +61,10 @@ constexpr int SEL_CB = 64;     // coarse bins
 constexpr int SEL_FB = 256;    // fine bins inside one coarse bin
 constexpr int SEL_NT = 256;    // threads of the per-row selection
 constexpr int SEL_FB_GRID = 64;  // workgroups of the fallback kernel
+// Waves of a scan workgroup, each taking every SEL_NW-th step of every sweep,
+// and parts of a row's candidate list (one per wave and lane of the row).
+constexpr int SEL_NW = 4;
+constexpr int SEL_PARTS = 4 * SEL_NW;
 
 // Candidate list capacity for K: the expected count plus seven standard
 // deviations of the sampled estimate, and a margin for the sub-bin width.
@@ -64,6 +73,15 @@ int sel_cap(int K) {
   const double expect = kf + 4.0 * sqrt(kf * SEL_SS2) + 2.0 * SEL_SS2;
   const double c = expect + 7.0 * sqrt(SEL_SS2 * expect) + 64.0;
   return (static_cast<int>(c) + 255) / 256 * 256;
+}
+
+// Capacity of each of the SEL_PARTS parts of a list: an even share of the
+// list's capacity plus a quarter for the parts' own spread (a row listing
+// cap candidates fills its fullest part past the even share: on Prefill 64K
+// one row in about 800 overflowed the even share), a multiple of 16.
+int sel_part_cap(int K) {
+  const int share = sel_cap(K) / SEL_PARTS;
+  return (share + share / 4 + 15) / 16 * 16;
 }
 
 // Coarse bin of a score: monotone, 64 bins by sign and bit length
@@ -116,23 +134,21 @@ __device__ __forceinline__ int sel_target(int K, int ns, int n) {
 // count carries into its neighbour.
 static_assert(kSelMaxTk / SEL_SS2 < 65536, "16-bit histogram counters");
 struct SelScanLds {
-  uint32_t hist[16][SEL_FB / 2];   // coarse (first SEL_CB / 2 words of a row), fine, then
-                                   // the candidates' histogram
-  uint32_t cnt[16];                // candidates of each row
+  uint32_t hist[16][SEL_FB / 2];   // coarse (first SEL_CB / 2 words of a row), then fine
+  uint32_t above[16];              // fine-sampled scores above the coarse bin, per row
+  uint32_t kmin[16], kmax[16];     // range of the fine-sampled keys, per row
   int32_t thr[16];                 // threshold of each row
   int32_t cb[16];                  // coarse bin of each row
   uint32_t hb[16];                 // key at the bottom of the candidates' histogram
   int32_t hsh[16];                 // its bin width, log2
 };
 
-// Per-row summary the scan leaves for the row kernel: the candidates'
-// histogram is 256 bins of width 2^hsh over keys from hb up (keys below hb in
-// bin 0, keys past the top in bin 255); kbin is the bin holding the K-th
-// largest listed key and above the count of listed keys in higher bins.
+// Per-row summary the scan leaves for the row kernel: the range of the
+// sampled keys from the threshold up, as 256 histogram bins of width 2^hsh
+// over keys from hb up (keys below hb in bin 0, keys past the top in bin 255).
 struct SelMeta {
   uint32_t hb;
-  int32_t hsh, kbin;
-  uint32_t above;
+  int32_t hsh;
 };
 
 __device__ __forceinline__ uint32_t sel_hbin(uint32_t key, uint32_t hb, int hsh) {
@@ -147,28 +163,32 @@ __device__ __forceinline__ int mad_i24(int a, int b, int c) {
   return d;
 }
 
-// s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
-constexpr int kWaitVm0 = 0x0F70;
-
-// One wave: 16 query rows rb*16 .. rb*16+15 of sequence b (a set's rows).
+// One workgroup of SEL_NW waves: 16 query rows rb*16 .. rb*16+15 of sequence b
+// (a set's rows). Wave v takes the steps s = v, v + SEL_NW, ... of each sweep,
+// so the waves see the same mix of positions and finish together, and the
+// many workgroups, longest rows first, keep every SIMD busy to the end.
 // q_idx [B, Tq, H_I, D_I] (this set's heads), k_idx [B, Tk, D_I], w [H_I]
-// shared by every row. cand [B*Tq][cap] int2 (score, position), cnt [B*Tq]
-// (the true count, possibly above cap), meta [B*Tq]. nfb: the fallback list's
-// length, zeroed here for the row kernel that follows.
+// shared by every row. cand [B*Tq][SEL_PARTS][cap/SEL_PARTS] int2 (score,
+// position), cnt [B*Tq][SEL_PARTS] (each part's true count, possibly above its
+// capacity), meta [B*Tq]. nfb: the fallback list's length, zeroed here for the
+// row kernel that follows.
 template <int H_I, int D_I>
-__global__ __launch_bounds__(64, 3) void sel_scan_kernel(
-    int Tq, int Tk, int K, int cap, const int32_t* __restrict__ q_offset,
+__global__ __launch_bounds__(64 * SEL_NW, 4) void sel_scan_kernel(
+    int Tq, int Tk, int K, int cap, int capp, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int8_t* __restrict__ q_idx,
     const int8_t* __restrict__ k_idx, const int8_t* __restrict__ w, int2* __restrict__ cand,
     uint32_t* __restrict__ cnt, SelMeta* __restrict__ meta, uint32_t* __restrict__ nfb) {
   constexpr int NCH = D_I / 64;  // 64-deep MFMA steps over d_I
   constexpr int U = 2;           // 16-position tiles per step
   __shared__ SelScanLds sm;
-  const int lane = threadIdx.x;
+  const int lrow = SEL_PARTS * capp;  // entries of a row's list
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nrb = (Tq + 15) / 16;
   const int rb = nrb - 1 - static_cast<int>(blockIdx.x);  // longest rows first
   const int b = blockIdx.y;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && lane == 0) *nfb = 0u;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *nfb = 0u;
   const int r = lane & 15;
   const int g4 = lane >> 4;
   const int i = rb * 16 + r;
@@ -181,11 +201,15 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
   // a row that keeps everything (n <= K) needs no list; the others sample a
   // threshold (rows with at most cap positions may end up listing all)
   const bool listed = n > K;
-  if (lane < 16) {
-    sm.cnt[r] = 0u;
+  if (tid < 16) {
     sm.thr[r] = INT32_MIN;
+    sm.above[r] = 0u;
+    sm.kmin[r] = 0xffffffffu;
+    sm.kmax[r] = 0u;
   }
-  for (int j = lane; j < 16 * (SEL_CB / 2); j += 64) sm.hist[j / (SEL_CB / 2)][j % (SEL_CB / 2)] = 0u;
+  for (int j = tid; j < 16 * (SEL_CB / 2); j += 64 * SEL_NW)
+    sm.hist[j / (SEL_CB / 2)][j % (SEL_CB / 2)] = 0u;
+  // every wave holds the same rows: these are uniform over the workgroup
   int pmax = p;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) pmax = max(pmax, __shfl_xor(pmax, off, 64));
@@ -244,14 +268,15 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
         for (int e = 0; e < 4; ++e) sacc[u][e] = mad_i24(wh[h], max(acc[h][e], 0), sacc[u][e]);
     }
   };
-  // f(position, score) over this lane's causal positions of a strided sweep
+  // f(position, score) over this lane's causal positions of this wave's steps
+  // of a strided sweep
   auto sweep = [&](int stride, int last, auto&& f) {
     const int span = 32 * stride;  // positions covered by one step
     v4i ka[U][NCH];
-    load_keys(0, stride, ka);
-    for (int pos0 = 0; pos0 <= last; pos0 += span) {
+    load_keys(wv * span, stride, ka);
+    for (int pos0 = wv * span; pos0 <= last; pos0 += SEL_NW * span) {
       v4i kn[U][NCH];
-      load_keys(pos0 + span, stride, kn);
+      load_keys(pos0 + SEL_NW * span, stride, kn);
       v4i sacc[U];
       score(ka, sacc);
 #pragma unroll
@@ -277,7 +302,7 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
     }
   });
   __syncthreads();
-  if (lane < 16 && listed) {
+  if (tid < 16 && listed) {
     const int ns = p / SEL_SS1 + 1;
     const uint32_t tgt = static_cast<uint32_t>(sel_target(K, ns, n));
     uint32_t cum = 0;
@@ -292,7 +317,8 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
     sm.cb[r] = cb;
   }
   __syncthreads();
-  for (int j = lane; j < 16 * (SEL_FB / 2); j += 64) sm.hist[j / (SEL_FB / 2)][j % (SEL_FB / 2)] = 0u;
+  for (int j = tid; j < 16 * (SEL_FB / 2); j += 64 * SEL_NW)
+    sm.hist[j / (SEL_FB / 2)][j % (SEL_FB / 2)] = 0u;
   __syncthreads();
   // 2. fine sample inside the coarse bin; the count above it; the sampled range
   uint32_t ulo = 0, uhi = 0;
@@ -316,23 +342,29 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
       atomicAdd(&sm.hist[r][fb >> 1], 1u << (16 * (fb & 1)));
     }
   });
-  // the row's four lanes combine their counts and ranges
+  // the row's lanes of every wave combine their counts and ranges
   above += __shfl_xor(above, 16, 64);
   above += __shfl_xor(above, 32, 64);
   kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), 16, 64)));
   kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), 32, 64)));
   kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), 16, 64)));
   kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), 32, 64)));
-  __syncthreads();
   if (lane < 16 && listed) {
+    atomicAdd(&sm.above[r], above);
+    atomicMin(&sm.kmin[r], kmin);
+    atomicMax(&sm.kmax[r], kmax);
+  }
+  __syncthreads();
+  if (tid < 16 && listed) {
     const int ns = p / SEL_SS2 + 1;
     const uint32_t tgt = static_cast<uint32_t>(sel_target(K, ns, n));
+    const uint32_t ab = sm.above[r];
     uint32_t t;
-    if (above >= tgt) {
+    if (ab >= tgt) {
       // the coarse sample put the bin too low: everything above it
       t = uhi + 1u;
     } else {
-      uint32_t cum = above;
+      uint32_t cum = ab;
       t = ulo;  // the whole bin when even it falls short
       for (int fb = SEL_FB - 1; fb >= 0; --fb) {
         cum += (sm.hist[r][fb >> 1] >> (16 * (fb & 1))) & 0xffffu;
@@ -341,133 +373,123 @@ __global__ __launch_bounds__(64, 3) void sel_scan_kernel(
           break;
         }
       }
-      // too few samples to reach the target: every position is a candidate
-      if (cum < tgt) t = 0u;
+      // too few samples to reach the target: a row of at most cap positions
+      // lists all of them; a longer one keeps the whole coarse bin (exact
+      // either way: a list short of K sends the row to the fallback)
+      if (cum < tgt && n <= cap) t = 0u;
     }
     sm.thr[r] = key_score(t);
     // the candidates' histogram spans the sampled keys from the threshold up
-    const uint32_t hb = max(t, kmin);
+    const uint32_t hb = max(t, sm.kmin[r]);
+    const uint32_t km = sm.kmax[r];
     sm.hb[r] = hb;
-    sm.hsh[r] = kmax > hb ? sel_fshift(hb, kmax) : 0;
+    sm.hsh[r] = km > hb ? sel_fshift(hb, km) : 0;
   }
-  for (int j = lane; j < 16 * (SEL_FB / 2); j += 64) sm.hist[j / (SEL_FB / 2)][j % (SEL_FB / 2)] = 0u;
   __syncthreads();
 
-  // 3. full pass: every causal position at or above the row's threshold. Each
-  // step first stores the previous step's candidates (their slots came from one
-  // LDS atomic per lane, issued a step earlier), then issues the next step's
-  // key loads, then scores this step: the stores are older than every load a
-  // later wait covers.
-  const int32_t thr = sm.thr[r];
-  const uint32_t hb = sm.hb[r];
-  const int hsh = sm.hsh[r];
+  // 3. full pass: every causal position at or above the row's threshold goes
+  // to its own part of the row's list (part 4*v + g4 for lane g4 of the row in
+  // wave v, which sees positions 16u + 4*g4 + e of its 32-position steps), of
+  // capp entries, counted in a register: no slot is shared. Rows that keep
+  // every position list nothing: no score reaches INT32_MAX (|S| <= 2^30 with
+  // H_I*d_I <= 512).
+  const int32_t thr = listed ? sm.thr[r] : INT32_MAX;
   const int plist = listed ? p : -1;  // causal limit of the listed positions
   // steps wholly at or below every listed row's limit need no position test
   int pmin = listed ? p : INT32_MAX;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) pmin = min(pmin, __shfl_xor(pmin, off, 64));
   pmin = __builtin_amdgcn_readfirstlane(pmin);
-  int2* crow = cand + (static_cast<int64_t>(b) * Tq + (i < Tq ? i : 0)) * cap;
-  v4i ka[U][NCH];
-  load_keys(0, 1, ka);
-  uint32_t pm = 0u, pslot = 0u;
+  // The workgroup's rows' lists as one buffer: every step issues the same
+  // eight stores, a position that is no candidate with an offset past the
+  // buffer, which the range check drops. The code is then straight-line, so
+  // the wait for a step's keys leaves the younger stores in flight.
+  const int wrows = min(16, Tq - rb * 16);
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(cand + (static_cast<int64_t>(b) * Tq + rb * 16) * lrow), 0,
+      wrows * lrow * static_cast<int>(sizeof(int2)), kBufferFlags);
+  const int lbase = (r * SEL_PARTS + 4 * wv + g4) * capp * static_cast<int>(sizeof(int2));
+  const int llast = lbase + (capp - 1) * static_cast<int>(sizeof(int2));
+  constexpr int kDrop = INT32_MIN;  // byte offset 2^31, past the buffer
+  // byte offset of this part's next entry (past llast: the part is full, and
+  // further entries overwrite its last one, as the row is redone anyway)
+  int noff = lbase;
+  // the previous step's scores ps, at positions pb + 16u + e (pb = its first
+  // position + 4*g4), candidates when >= thr and at or below plim
+  auto put = [&](const v4i (&sc4)[U], int pb, int plim) {
+#pragma unroll
+    for (int k = 0; k < 4 * U; ++k) {
+      const int32_t sc = sc4[k >> 2][k & 3];
+      const int pos = pb + 16 * (k >> 2) + (k & 3);
+      const bool c = (sc >= thr) & (pos <= plim);
+      __builtin_amdgcn_raw_buffer_store_b64(v2i{sc, pos}, crs, c ? min(noff, llast) : kDrop, 0, 0);
+      noff += c ? static_cast<int>(sizeof(int2)) : 0;
+    }
+  };
+  // one step: the previous step's candidates, the next step's key loads, this
+  // step's scores; the two key buffers alternate, so no register with a load
+  // in flight is ever copied. The first step's "previous" positions lie past
+  // every row's limit, so it stores nothing.
+  constexpr int kStep = 32 * SEL_NW;  // positions between a wave's steps
   v4i ps[U] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-  int ppos = 0;
-  for (int pos0 = 0; pos0 <= pmax + 32; pos0 += 32) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  int ppos = INT32_MAX - 64;  // first position of the previous step
+  int pplim = -1;             // position limit of the previous step
+  auto step = [&](int pos0, const v4i (&kc)[U][NCH], v4i (&kx)[U][NCH]) {
+    put(ps, ppos + 4 * g4, pplim);
     __builtin_amdgcn_sched_barrier(0);
-    // the previous step's candidates
-    if (pm != 0u) {
-      uint32_t mm = pm, slot = pslot;
-      while (mm != 0u) {
-        const int k = __ffs(static_cast<int>(mm)) - 1;  // bit 4u + e: position 16u + 4*g4 + e
-        mm &= mm - 1u;
-        const bool hi = (k & 4) != 0, b1 = (k & 2) != 0, b0 = (k & 1) != 0;
-        const int32_t a0 = hi ? ps[1][0] : ps[0][0], a1 = hi ? ps[1][1] : ps[0][1];
-        const int32_t a2 = hi ? ps[1][2] : ps[0][2], a3 = hi ? ps[1][3] : ps[0][3];
-        const int32_t c0 = b1 ? a2 : a0, c1 = b1 ? a3 : a1;
-        const int32_t sc = b0 ? c1 : c0;
-        if (slot < static_cast<uint32_t>(cap)) {
-          crow[slot] = make_int2(sc, ppos + 4 * (k & 4) + 4 * g4 + (k & 3));
-          const uint32_t hbin = sel_hbin(score_key(sc), hb, hsh);
-          atomicAdd(&sm.hist[r][hbin >> 1], 1u << (16 * (hbin & 1)));
-        }
-        ++slot;
-      }
-    }
+    load_keys(pos0 + kStep, 1, kx);
     __builtin_amdgcn_sched_barrier(0);
-    if (pos0 > pmax) break;
-    v4i kn[U][NCH];
-    load_keys(pos0 + 32, 1, kn);
-    __builtin_amdgcn_sched_barrier(0);
-    v4i sacc[U];
-    score(ka, sacc);
-    uint32_t m = 0u;
-    if (pos0 + 31 <= pmin) {  // uniform
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m |= static_cast<uint32_t>(sacc[u][e] >= thr) << (4 * u + e);
-      m = listed ? m : 0u;
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int pos = pos0 + 16 * u + 4 * g4 + e;
-          m |= static_cast<uint32_t>((sacc[u][e] >= thr) & (pos <= plist)) << (4 * u + e);
-        }
-    }
-    pm = m;
-    ps[0] = sacc[0];
-    ps[1] = sacc[1];
+    score(kc, ps);
     ppos = pos0;
-    if (m != 0u) pslot = atomicAdd(&sm.cnt[r], static_cast<uint32_t>(__popc(m)));
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) ka[u][c] = kn[u][c];
+    // steps wholly at or below every listed row's limit need no position test
+    pplim = pos0 + 31 <= pmin ? INT32_MAX : plist;
+  };
+  v4i ka[U][NCH], kb[U][NCH];
+  int pos0 = 32 * wv;
+  load_keys(pos0, 1, ka);
+  for (; pos0 + kStep <= pmax; pos0 += 2 * kStep) {
+    step(pos0, ka, kb);
+    step(pos0 + kStep, kb, ka);
   }
-  __syncthreads();
-  if (lane < 16 && i < Tq) {
-    const uint32_t c = sm.cnt[r];
-    cnt[static_cast<int64_t>(b) * Tq + i] = c;
-    SelMeta mt{hb, hsh, -1, 0u};
-    if (listed && c >= static_cast<uint32_t>(K) && c <= static_cast<uint32_t>(cap)) {
-      uint32_t cum = 0;
-      for (int bb = SEL_FB - 1; bb >= 0; --bb) {
-        const uint32_t h = (sm.hist[r][bb >> 1] >> (16 * (bb & 1))) & 0xffffu;
-        if (cum + h >= static_cast<uint32_t>(K)) {
-          mt.kbin = bb;
-          mt.above = cum;
-          break;
-        }
-        cum += h;
-      }
-    }
-    meta[static_cast<int64_t>(b) * Tq + i] = mt;
-  }
+  if (pos0 <= pmax) step(pos0, ka, kb);
+  put(ps, ppos + 4 * g4, pplim);  // the last step's (if any ran)
+  const uint32_t nlist = static_cast<uint32_t>(noff - lbase) / sizeof(int2);
+  if (i < Tq) cnt[(static_cast<int64_t>(b) * Tq + i) * SEL_PARTS + 4 * wv + g4] = nlist;
+  if (tid < 16 && i < Tq) meta[static_cast<int64_t>(b) * Tq + i] = SelMeta{sm.hb[r], sm.hsh[r]};
 }
 
 constexpr int SEL_SMALL = 1024;  // list entries in the K-th score's bin resolved in LDS
+// Entries per thread of the row kernel for the largest part capacity
+// (K = 4096: parts of 512 entries, 16 threads each).
+constexpr int kSelRowsMaxE = 32;
 
-// One workgroup per (row, sequence). The list of row (b, i) holds cnt entries
-// (at most cap stored) and its histogram summary meta. The row's Top-K is every
-// listed key in a bin above meta.kbin plus the (K - meta.above) best of the
-// entries in that bin (ranked by direct count), set in an LDS bit map of the
-// row and compacted in position order. idx rows at idx + (b*out_tq + i)*K.
-// Rows whose list cannot give their Top-K (count outside [K, cap], or more
-// than SEL_SMALL entries in the K-th bin) go to the fallback list.
+// One workgroup per (row, sequence). The list of row (b, i) is SEL_PARTS parts
+// of cap/SEL_PARTS entries (one per scanning wave and lane), with their counts
+// (all counted, at most cap/SEL_PARTS stored each) and the row's histogram
+// range meta. The kernel histograms the listed keys, finds the bin holding the
+// K-th largest; the row's Top-K is every listed key in a higher bin plus the
+// best of the entries in that bin (ranked by direct count), set in an LDS bit
+// map of the row and compacted in position order. idx rows at
+// idx + (b*out_tq + i)*K. Rows whose list cannot give their Top-K (fewer than
+// K entries, a part past its capacity, or more than SEL_SMALL entries in the
+// K-th bin) go to the fallback list.
+// E: entries of a part each thread holds in registers between the two passes
+// (at least capp / 16).
+template <int E>
 __global__ __launch_bounds__(SEL_NT) void sel_rows_kernel(
-    int Tq, int Tk, int K, int cap, const int32_t* __restrict__ q_offset,
+    int Tq, int Tk, int K, int capp, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int2* __restrict__ cand,
     const uint32_t* __restrict__ cnt, const SelMeta* __restrict__ meta,
     int32_t* __restrict__ idx, int out_tq, uint32_t* __restrict__ nfb,
     int32_t* __restrict__ fb_rows) {
   extern __shared__ __align__(16) uint32_t keep[];  // ceil(Tk/32) words
   __shared__ int2 small[SEL_SMALL];
+  __shared__ uint32_t hist[SEL_FB];
+  __shared__ uint32_t pc[SEL_PARTS];
   __shared__ uint32_t scratch[SEL_NT / 64 + 2];
-  __shared__ uint32_t nsmall;
+  __shared__ uint32_t nsmall, kbin, above;
+  static_assert(SEL_NT == SEL_FB, "one thread per histogram bin");
+  static_assert(SEL_NT == 16 * SEL_PARTS, "16 threads per part of a list");
 
   const int t = threadIdx.x;
   const int i = blockIdx.x;
@@ -483,21 +505,59 @@ __global__ __launch_bounds__(SEL_NT) void sel_rows_kernel(
     return;
   }
   const int64_t row = static_cast<int64_t>(b) * Tq + i;
-  const uint32_t c = cnt[row];
-  const SelMeta mt = meta[row];
-  if (mt.kbin < 0) {  // count outside [K, cap]: the threshold missed
+  if (t < SEL_PARTS) pc[t] = cnt[row * SEL_PARTS + t];
+  hist[t] = 0u;
+  __syncthreads();
+  uint32_t listed = 0, cmax = 0;
+#pragma unroll
+  for (int g = 0; g < SEL_PARTS; ++g) {
+    listed += pc[g];
+    cmax = max(cmax, pc[g]);
+  }
+  if (cmax > static_cast<uint32_t>(capp) || listed < static_cast<uint32_t>(K)) {
+    // the threshold missed (uniform: every thread read the same counts)
     if (t == 0) fb_rows[atomicAdd(nfb, 1u)] = static_cast<int32_t>(row);
     return;
   }
-  const int nc = static_cast<int>(c);
+  const SelMeta mt = meta[row];
+  // 16 threads per part: thread t reads entries t % 16, t % 16 + 16, ... of
+  // part t / 16
+  const int2* cpart = cand + (row * SEL_PARTS + (t >> 4)) * capp;
+  const int npart = static_cast<int>(pc[t >> 4]);
+  // the thread's entries, all loads in flight together; kept in registers for
+  // both passes
+  int2 ent[E];
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    const int j = (t & 15) + 16 * q;
+    ent[q] = j < npart ? cpart[j] : make_int2(0, 0);
+  }
+  // 1. the listed keys' histogram; the bin of the K-th largest
+#pragma unroll
+  for (int q = 0; q < E; ++q)
+    if ((t & 15) + 16 * q < npart)
+      atomicAdd(&hist[sel_hbin(score_key(ent[q].x), mt.hb, mt.hsh)], 1u);
+  __syncthreads();
+  {
+    // thread t takes bin 255 - t: the count above it is the scan of the bins before
+    const uint32_t h = hist[SEL_FB - 1 - t];
+    uint32_t htot;
+    const uint32_t ab = block_excl_scan(h, scratch, &htot);
+    if (ab < static_cast<uint32_t>(K) && static_cast<uint32_t>(K) <= ab + h) {
+      kbin = static_cast<uint32_t>(SEL_FB - 1 - t);
+      above = ab;
+    }
+  }
   const int nw = (n + 31) / 32;
   for (int j = t; j < nw; j += SEL_NT) keep[j] = 0u;
   if (t == 0) nsmall = 0u;
   __syncthreads();
-  const int2* crow = cand + row * cap;
-  const uint32_t kb = static_cast<uint32_t>(mt.kbin);
-  for (int j = t; j < nc; j += SEL_NT) {
-    const int2 e = crow[j];
+  // 2. keys above the K-th bin are kept; the bin's own entries are gathered
+  const uint32_t kb = kbin;
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    if ((t & 15) + 16 * q >= npart) break;
+    const int2 e = ent[q];
     const uint32_t hbin = sel_hbin(score_key(e.x), mt.hb, mt.hsh);
     if (hbin > kb) {
       atomicOr(&keep[e.y >> 5], 1u << (e.y & 31));
@@ -514,7 +574,7 @@ __global__ __launch_bounds__(SEL_NT) void sel_rows_kernel(
   }
   // the bin's entries: kept when fewer than K - above of them precede it under
   // (score desc, position asc)
-  const uint32_t need = static_cast<uint32_t>(K) - mt.above;
+  const uint32_t need = static_cast<uint32_t>(K) - above;
   for (int j = t; j < ns; j += SEL_NT) {
     const int2 ej = small[j];
     uint32_t rank = 0;
@@ -606,7 +666,7 @@ bool sel_supported(const Geom& g, int64_t wsb, int64_t wsq) {
   return g.block <= 1 && wsb == 0 && wsq == 0 && (g.d_I == 64 || g.d_I == 128) &&
          g.H_I <= 8 && g.H_I * g.d_I <= 512 && g.Tk > kWaveTopkMax && g.Tk <= kSelMaxTk &&
          static_cast<int64_t>(g.B) * g.Tq >= kSelMinRows && g.K <= 4096 &&
-         sel_rows_lds(g.Tk) <= 32768;
+         sel_part_cap(g.K) <= 16 * kSelRowsMaxE && sel_rows_lds(g.Tk) <= 32768;
 }
 
 SelLayout sel_layout(const Geom& g) {
@@ -616,8 +676,9 @@ SelLayout sel_layout(const Geom& g) {
   const size_t rows = static_cast<size_t>(g.B) * g.Tq;
   L.srow = (static_cast<int64_t>(g.Tk) + 3) / 4 * 4;
   size_t o = 0;
-  L.cand = o;  o += al(rows * L.cap * sizeof(int2));
-  L.cnt = o;   o += al(rows * sizeof(uint32_t));
+  L.capp = sel_part_cap(g.K);
+  L.cand = o;  o += al(rows * SEL_PARTS * L.capp * sizeof(int2));
+  L.cnt = o;   o += al(rows * SEL_PARTS * sizeof(uint32_t));  // one count per part of a list
   L.meta = o;  o += al(rows * sizeof(SelMeta));
   L.nfb = o;   o += al(sizeof(uint32_t));
   L.fbrows = o; o += al(rows * sizeof(int32_t));
@@ -640,8 +701,8 @@ static hipError_t launch_sel_hd(const Geom& g, const int8_t* q_idx, const int8_t
   int32_t* scratch = reinterpret_cast<int32_t*>(base + L.scratch);
   {
     KernelTimer timer(LCI_KERNEL_SEL_SCAN, st);
-    hipLaunchKernelGGL((sel_scan_kernel<H_I, D_I>), dim3((g.Tq + 15) / 16, g.B), dim3(64), 0,
-                       st, g.Tq, g.Tk, g.K, L.cap, g.q_offset, g.kv_len, q_idx, k_idx, w, cand,
+    hipLaunchKernelGGL((sel_scan_kernel<H_I, D_I>), dim3((g.Tq + 15) / 16, g.B), dim3(64 * SEL_NW), 0,
+                       st, g.Tq, g.Tk, g.K, L.cap, L.capp, g.q_offset, g.kv_len, q_idx, k_idx, w, cand,
                        cnt, meta, nfb);
   }
   hipError_t e = hipGetLastError();
@@ -649,8 +710,18 @@ static hipError_t launch_sel_hd(const Geom& g, const int8_t* q_idx, const int8_t
   const size_t lds = sel_rows_lds(g.Tk);
   {
     KernelTimer timer(LCI_KERNEL_SEL_ROWS, st);
-    hipLaunchKernelGGL(sel_rows_kernel, dim3(g.Tq, g.B), dim3(SEL_NT), lds, st, g.Tq, g.Tk, g.K,
-                       L.cap, g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb, fbrows);
+    const int e = (L.capp + 15) / 16;  // entries per thread
+    const dim3 grid(g.Tq, g.B);
+    if (e <= 8)
+      hipLaunchKernelGGL(sel_rows_kernel<8>, grid, dim3(SEL_NT), lds, st, g.Tq, g.Tk, g.K, L.capp,
+                         g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb, fbrows);
+    else if (e <= 20)
+      hipLaunchKernelGGL(sel_rows_kernel<20>, grid, dim3(SEL_NT), lds, st, g.Tq, g.Tk, g.K, L.capp,
+                         g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb, fbrows);
+    else
+      hipLaunchKernelGGL(sel_rows_kernel<kSelRowsMaxE>, grid, dim3(SEL_NT), lds, st, g.Tq, g.Tk,
+                         g.K, L.capp, g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb,
+                         fbrows);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {

@@ -94,7 +94,8 @@ constexpr int kSelMaxTk = 131072;   // histories up to this long (row bit maps i
 constexpr int kSelMinRows = 8192;   // query rows per call at least
 struct SelLayout {
   size_t cand, cnt, meta, nfb, fbrows, scratch, total;
-  int cap;
+  int cap;   // candidates a row lists at most by design (rows with fewer positions list all)
+  int capp;  // entries of each part of a row's list
   int64_t srow;
 };
 bool sel_supported(const Geom& g, int64_t wsb, int64_t wsq);

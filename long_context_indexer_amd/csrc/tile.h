@@ -38,18 +38,7 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
 }
 
-// dword 3 of a raw buffer resource on gfx9-class parts: 32-bit data format
-constexpr int kBufferFlags = 0x00020000;
 constexpr int kNegInfBits = static_cast<int>(0xff800000u);
-
-// A workgroup-uniform pointer, moved to scalar registers (buffer resources must
-// live there; without this the compiler may loop over lanes to build them).
-__device__ __forceinline__ void* uniform_ptr(const void* p) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
 // dst + 16 l (dst is wave-uniform); offsets outside the buffer read as zero.
