@@ -42,29 +42,29 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # were taken on: any change to them turns the figure into null.
 TRAFFIC = {
     ("prefill64k", "attn_gather"): dict(
-        fetch_kib=59633428.8, write_kib=263201.8, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=59446964.3, write_kib=263154.8, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/sparse_attn.hip", "long_context_indexer_amd/csrc/common.h"],
-        sha256="0177dfa71d629fab09846f0e0d8bf749e02cd1df2eb6e65d725cf06bce5be449"),
+        sha256="4311449b841043ce2e6b14fd54b686a3617f295e73bbf5e23b193de17e049ef5"),
     ("prefill64k", "attn_dense"): dict(
-        fetch_kib=1458918.7, write_kib=262181.7, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=1459692.3, write_kib=262180.4, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/attn_dense.hip", "long_context_indexer_amd/csrc/attn_dense.h", "long_context_indexer_amd/csrc/tile.h", "long_context_indexer_amd/csrc/common.h"],
-        sha256="f022ab9829bcdd6153988b3659e5228f9fb330933fa48b199469b5051d438107"),
+        sha256="9c4f27d6134a0471d759e9ccd2fbdd529421a18313ffa9a97a910ec524f99e43"),
     ("prefill64k", "sel_scan"): dict(
-        fetch_kib=94288.0, write_kib=1610903.8, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=225150.2, write_kib=4112108.6, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/idx_select.hip", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
-        sha256="0ce1229f72b5747fffb14dc2f5ad71d15c8b55ad95c73b7048b74e2b993c2de3"),
+        sha256="0f04192ab4187b5d31d4cfd8fd0a3f04f224afad7e92f9be97fa8cc5f9d7727e"),
     ("prefill8k", "attn_dense"): dict(
-        fetch_kib=123642.5, write_kib=66431.0, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=123682.6, write_kib=66504.3, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/attn_dense.hip", "long_context_indexer_amd/csrc/attn_dense.h", "long_context_indexer_amd/csrc/tile.h", "long_context_indexer_amd/csrc/common.h"],
-        sha256="f022ab9829bcdd6153988b3659e5228f9fb330933fa48b199469b5051d438107"),
+        sha256="9c4f27d6134a0471d759e9ccd2fbdd529421a18313ffa9a97a910ec524f99e43"),
     ("decode1m", "dec_score"): dict(
-        fetch_kib=262420.4, write_kib=322.5, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=262422.7, write_kib=322.4, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/decode.hip", "long_context_indexer_amd/csrc/decode.h", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
-        sha256="b9e3e798068a10d7def08ad45c0a0c626f235c46d74b2e8967347cd6c029cde8"),
+        sha256="cb608208a9e2d07bbf891fb0919459e6991e4d0dab02beba46098bbb6c295c5e"),
     ("decode128k", "dec_score"): dict(
-        fetch_kib=262542.3, write_kib=1775.3, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=262540.9, write_kib=1775.4, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/decode.hip", "long_context_indexer_amd/csrc/decode.h", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
-        sha256="b9e3e798068a10d7def08ad45c0a0c626f235c46d74b2e8967347cd6c029cde8"),
+        sha256="cb608208a9e2d07bbf891fb0919459e6991e4d0dab02beba46098bbb6c295c5e"),
 }
 
 
