@@ -74,8 +74,8 @@ def open_library(path: str):
                                    i64, i64, P, P, P, P, P, f64, i64, P, P, P, P, P, P]
     lib.orc_layer_rows.restype = i32
     lib.orc_kv_append.argtypes = [i32, i32, i32, i64, P, P, P, P, P, P]
-    lib.orc_attn_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64,
-                                 P, P, P, P, P]
+    lib.orc_attn_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
+                                 f64, P, P, P, P, P]
     lib.orc_indexer_bwd.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, i64, i64, P, P,
                                     f64, P, P, P, P]
     lib.orc_num_threads.restype = i32
@@ -240,7 +240,8 @@ class Oracle:
 
     def attention_bwd(self, q, k, v, gate, idx, kv_len, scale, dy, mix=None):
         """Gradients of the gated attention over index rows idx int32 [B,Tq,K] (one
-        set) for the output gradient dy uint16 [B,Tq,Hq,d]. q, gate, mix, dy bf16 bits
+        set) or [B,Tq,sets,K] (query head h reads set h // (Hq // sets)) for the
+        output gradient dy uint16 [B,Tq,Hq,d]. q, gate, mix, dy bf16 bits
         [B,Tq,Hq,d]; k, v [B,Tk,Hkv,d]. Returns dict(dq, dgate, dmix [B,Tq,Hq,d];
         dk, dv [B,Tk,Hkv,d]) in float64 (dgate / dmix None without gate / mix)."""
         q, k, v, dy = (_c(a, np.uint16) for a in (q, k, v, dy))
@@ -250,14 +251,18 @@ class Oracle:
         mix = None if mix is None else _c(mix, np.uint16)
         if mix is not None and gate is None:
             raise ValueError("mix needs a gate")
-        idx = _c(idx, np.int32).reshape(B, Tq, -1)
-        K = idx.shape[2]
+        idx = _c(idx, np.int32)
+        sets = idx.shape[2] if idx.ndim == 4 else 1
+        if Hq % sets:
+            raise ValueError("the index sets divide the query heads")
+        idx = idx.reshape(B, Tq, sets, -1)
+        K = idx.shape[3]
         dq = np.empty((B, Tq, Hq, d), np.float64)
         dk = np.empty((B, Tk, Hkv, d), np.float64)
         dv = np.empty((B, Tk, Hkv, d), np.float64)
         dg = np.empty((B, Tq, Hq, d), np.float64) if gate is not None else None
         dm = np.empty((B, Tq, Hq, d), np.float64) if mix is not None else None
-        self.lib.orc_attn_bwd(B, Tq, Tk, Hq, Hkv, d, K, _p(_c(kv_len, np.int32)), _p(q), _p(k),
+        self.lib.orc_attn_bwd(B, Tq, Tk, Hq, Hkv, d, K, sets, _p(_c(kv_len, np.int32)), _p(q), _p(k),
                               _p(v), _p(gate), _p(mix), _p(idx), _p(dy), float(scale), _p(dq),
                               _p(dk), _p(dv), _p(dg), _p(dm))
         return dict(dq=dq, dk=dk, dv=dv, dgate=dg, dmix=dm)

@@ -442,16 +442,20 @@ void orc_kv_append(int B, int Tn, int Tk, int64_t row_bytes, const uint8_t *src,
  *   dP_t = do.v[s_t];  dl_t = P_t*(dP_t - sum_u P_u dP_u);
  *   dq = scale * sum_t dl_t k[s_t];  dk[s_t] += scale*dl_t*q;  dv[s_t] += P_t*do,
  * summed over the query heads that share a key/value head and over every
- * occurrence of a position in an index row. Rows B x Tq with idx [B][Tq][K];
- * entries outside 0..kv_len-1 are skipped. All outputs are overwritten (fp64):
+ * occurrence of a position in an index row. Rows B x Tq with idx
+ * [B][Tq][sets][K] (sets as in orc_attn_row: query head h reads set
+ * h / (Hq/sets)); entries outside 0..kv_len-1 are skipped. All outputs are overwritten (fp64):
  * dq, dgate, dmix [B][Tq][Hq][d] (dgate, dmix nullable; used only with gate /
  * mix), dk, dv [B][Tk][Hkv][d]. */
-void orc_attn_bwd(int B, int Tq, int Tk, int Hq, int Hkv, int d, int K, const int32_t *kv_len,
+void orc_attn_bwd(int B, int Tq, int Tk, int Hq, int Hkv, int d, int K, int sets,
+                  const int32_t *kv_len,
                   const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gate,
                   const uint16_t *mix, const int32_t *idx, const uint16_t *dy, double scale,
                   double *dq, double *dk, double *dv, double *dgate, double *dmix)
 {
     int G = Hq / Hkv;
+    int ns = sets > 1 ? sets : 1;
+    int hps = Hq / ns;   /* query heads per index set */
     memset(dk, 0, (size_t)B * Tk * Hkv * d * sizeof(double));
     memset(dv, 0, (size_t)B * Tk * Hkv * d * sizeof(double));
     double *P = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
@@ -464,9 +468,9 @@ void orc_attn_bwd(int B, int Tq, int Tk, int Hq, int Hkv, int d, int K, const in
         const uint16_t *kb = k + (int64_t)b * Tk * Hkv * d, *vb = v + (int64_t)b * Tk * Hkv * d;
         for (int i = 0; i < Tq; ++i) {
             int64_t row = (int64_t)b * Tq + i;
-            const int32_t *ir = idx + row * K;
             for (int h = 0; h < Hq; ++h) {
                 int g = h / G;
+                const int32_t *ir = idx + (row * ns + h / hps) * K;   /* this head's index set */
                 int64_t hb = (row * Hq + h) * d;
                 /* softmax weights over the valid entries */
                 double m = -INFINITY;

@@ -841,6 +841,63 @@ def _bwd_against_autograd(orc, q, k, v, G, x, idx, kv_len, scale, dy, tol):
         assert np.abs(res[name] - want).max() <= tol * max(1.0, np.abs(want).max()), name
 
 
+def _torch_sparse_forward_sets(q, k, v, G, x, idx, kv_len, scale):
+    """The gated sparse attention with index sets, written with torch ops on
+    float64 tensors (an independent statement of the forward, for autograd):
+    idx [B,Tq,S,K]; query head h attends over set h // (Hq // S) and reads
+    key/value head h // (Hq // Hkv)."""
+    import torch
+    B, Tq, Hq, d = q.shape
+    Hkv, S = k.shape[2], idx.shape[2]
+    it = torch.from_numpy(idx.astype(np.int64)).repeat_interleave(Hq // S, dim=2)  # [B,Tq,Hq,K]
+    valid = (it >= 0) & (it < torch.from_numpy(kv_len.astype(np.int64))[:, None, None, None])
+    safe = torch.where(valid, it, torch.zeros_like(it))
+    bi = torch.arange(B)[:, None, None, None]
+    hk = (torch.arange(Hq) // (Hq // Hkv))[None, None, :, None]
+    ks, vs = k[bi, safe, hk], v[bi, safe, hk]                          # [B,Tq,Hq,K,d]
+    logits = (ks * q[:, :, :, None]).sum(-1) * scale                   # [B,Tq,Hq,K]
+    logits = logits.masked_fill(~valid, float("-inf"))
+    any_valid = valid.any(-1, keepdim=True)
+    P = torch.softmax(torch.where(any_valid, logits, torch.zeros_like(logits)), dim=-1)
+    P = torch.where(any_valid & valid, P, torch.zeros_like(P))
+    o = (P[..., None] * vs).sum(3)                                     # [B,Tq,Hq,d]
+    if G is None:
+        return o
+    s = torch.sigmoid(G)
+    return s * o + (1 - s) * x if x is not None else s * o
+
+
+def pin_bwd_sets_autograd(orc):
+    """Index sets (query head h reads set h // (Hq/S)): one per key/value head, one
+    per query head, two over four key/value heads; sparse rows in any order with
+    -1 padding, a repeated position, a row without entries and a short history:
+    the oracle's gradients equal torch autograd through a per-head gather
+    written independently, gated with the mix and ungated."""
+    import torch
+    r = np.random.default_rng(57)
+    for Hq, Hkv, S, gated in ((4, 2, 2, True), (4, 2, 4, True), (8, 4, 2, False)):
+        B, Tq, Tk, d, K = 2, 5, 30, 16, 9
+        q = _rand_bf16(r, (B, Tq, Hq, d))
+        k, v = (_rand_bf16(r, (B, Tk, Hkv, d)) for _ in range(2))
+        G, x, dy = (_rand_bf16(r, (B, Tq, Hq, d)) for _ in range(3))
+        idx = r.integers(0, Tk, size=(B, Tq, S, K)).astype(np.int32)
+        idx[0, 0, :, 0] = idx[0, 0, :, 1]          # a repeated position
+        idx[:, :, :, -2:] = -1                       # padding
+        idx[1, 3, 0] = -1                            # a row (set 0) without entries
+        kv_len = np.array([Tk, 20], np.int32)        # sequence 1: entries past 20 dropped
+        t = lambda a: torch.from_numpy(bf16_to_f32(a).astype(np.float64)).requires_grad_(True)
+        tq, tk, tv = t(q), t(k), t(v)
+        tg, tx = (t(G), t(x)) if gated else (None, None)
+        y = _torch_sparse_forward_sets(tq, tk, tv, tg, tx, idx, kv_len, 0.3)
+        (y * torch.from_numpy(bf16_to_f32(dy).astype(np.float64))).sum().backward()
+        res = orc.attention_bwd(q, k, v, G if gated else None, idx, kv_len, 0.3, dy,
+                                mix=x if gated else None)
+        pairs = [("dq", tq), ("dk", tk), ("dv", tv)] + ([("dgate", tg), ("dmix", tx)] if gated else [])
+        for name, leaf in pairs:
+            want = leaf.grad.numpy()
+            assert np.abs(res[name] - want).max() <= 1e-10 * max(1.0, np.abs(want).max()), (Hq, S, name)
+
+
 def pin_bwd_dense_sdpa(orc):
     """K >= p+1 (every causal position): the gradients equal torch autograd through
     its SDPA (causal, fp64, GQA by head repetition) with the gate and the mix."""

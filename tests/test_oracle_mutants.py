@@ -65,6 +65,8 @@ MUTANTS = [
     ("sets_by_head_modulo", "const int32_t *ih = idx + (int64_t)(h / hps) * K;",
      "const int32_t *ih = idx + (int64_t)(h % sets) * K;"),
     ("bwd_no_delta", "double dl = P[t] * (dP[t] - delta);", "double dl = P[t] * dP[t];"),
+    ("bwd_heads_read_set0", "const int32_t *ir = idx + (row * ns + h / hps) * K;",
+     "const int32_t *ir = idx + row * ns * K;"),
     ("bwd_gate_derivative", "gy * (o[j] - x) * sg * (1.0 - sg)", "gy * (o[j] - x) * sg * (1.0 + sg)"),
     ("bwd_dk_unscaled", "dkr[j] += scale * dl * orc_bf16(q[hb + j]);", "dkr[j] += dl * orc_bf16(q[hb + j]);"),
     ("bwd_dv_ungated", "dvr[j] += P[t] * dO[j];", "dvr[j] += P[t] * orc_bf16(dy[hb + j]);"),
