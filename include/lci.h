@@ -188,8 +188,9 @@ lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_b
  * divide H_I, else SHAPE); set j is scored by group j alone, with its heads'
  * weights, and selected like a shared set. Index rows are then int32 [B, S,
  * Tq, K*max(1, block)] (idx_out of the fused entries, idx of
- * lci_sparse_attn_fwd); lci_idx_score and lci_topk_select take the same set
- * axis. The gradient entries work on one set (S > 1: UNSUPPORTED). */
+ * lci_sparse_attn_fwd, lci_sparse_attn_bwd); lci_idx_score and lci_topk_select
+ * take the same set axis. lci_indexer_bwd works on one set (S > 1:
+ * UNSUPPORTED). */
 
 /* Fused prefill: steps 1-4 for many query rows per sequence in one call
  * ("Hybrid Sparse Attention ...", section "Engineering and Evaluation
@@ -288,8 +289,8 @@ lci_status lci_kv_append(const lci_geom *g, const lci_bf16 *k_new, const lci_bf1
  *   dq = scale sum_t dl_t k_t, dk_t += scale dl_t q, dv_t += P_t do,
  * summed over the query heads of a key/value head and over every occurrence of
  * a position in an index row. The scorer (indexer) gets no gradient here.
- *   q, k, v, idx, gate, mix, softmax_scale: as in lci_sparse_attn_fwd (one index
- *            set: g->sets > 1 is UNSUPPORTED)
+ *   q, k, v, idx, gate, mix, softmax_scale: as in lci_sparse_attn_fwd, index
+ *            sets included (g->sets > 1: idx [B, sets, Tq, K*max(1, block)])
  *   dy       bf16 [B, Tq, Hq, d]: gradient of out
  *   dq       fp32 [B, Tq, Hq, d] out
  *   dk, dv   fp32 [B, Tk, Hkv, d] out: 0 for positions no row selected; sums in
@@ -299,7 +300,7 @@ lci_status lci_kv_append(const lci_geom *g, const lci_bf16 *k_new, const lci_bf1
  *   dmix     fp32 [B, Tq, Hq, d] out, nullable (only with mix)
  *   workspace at least lci_workspace_bytes(LCI_ENTRY_SPARSE_ATTN_BWD): the
  *            recomputed forward output and lse, do, delta and the transpose of
- *            the index rows. B*Tq*K*max(1, block) < 2^31 (SHAPE).
+ *            the index rows. B*sets*Tq*K*max(1, block) < 2^31 (SHAPE).
  * Errors: NULL, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN, HIP. */
 lci_status lci_sparse_attn_bwd(const lci_geom *g, const lci_bf16 *q, const lci_bf16 *k,
                                const lci_bf16 *v, const int32_t *idx, const lci_bf16 *gate,

@@ -478,22 +478,32 @@ def sparse_attn_bwd(q, k, v, idx, gate, scale, kv_len, dy, q_offset=None, mix=No
                     workspace=None, stream=None):
     """Gradients of sparse_attn_fwd for the output gradient dy (bf16, the shape of q):
     returns dict(dq, dk, dv, dgate, dmix) as float32 tensors (dgate / dmix None
-    without gate / mix). idx int32 [B,Tq,K] (one index set)."""
+    without gate / mix). idx int32 [B,Tq,K] (one index set) or [B,sets,Tq,K]
+    (query head h reads set h // (Hq // sets)), as in sparse_attn_fwd."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dy, "dy")):
         _dev(t, torch.bfloat16, n, 4)
-    _dev(idx, torch.int32, "idx", 3)
+    B, Tq, Hq, d = q.shape
+    sets = 1
+    if idx is not None and idx.dim() == 4:
+        _dev(idx, torch.int32, "idx", 4)
+        sets = idx.shape[1]
+        if idx.shape[0] != B or idx.shape[2] != Tq or Hq % sets:
+            raise ValueError("per-head index rows must be [B,sets,Tq,K], sets dividing Hq")
+    else:
+        _dev(idx, torch.int32, "idx", 3)
+        if idx.shape[:2] != (B, Tq):
+            raise ValueError("idx must be [B,Tq,K]")
     _dev(gate, torch.bfloat16, "gate", 4)
     _dev(mix, torch.bfloat16, "mix", 4)
-    B, Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, Tk, Hkv, d) or tuple(v.shape) != tuple(k.shape) or \
-            tuple(dy.shape) != tuple(q.shape) or idx.shape[:2] != (B, Tq):
+            tuple(dy.shape) != tuple(q.shape):
         raise ValueError("inconsistent shapes")
     _gate_args(q, gate, mix)
     if q_offset is None:
         q_offset = torch.zeros(B, dtype=torch.int32, device=q.device)
-    g = make_geom(B, Tq, Tk, idx.shape[2], q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d)
+    g = make_geom(B, Tq, Tk, idx.shape[-1], q_offset, kv_len, Hq=Hq, Hkv=Hkv, d=d, sets=sets)
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty(q.shape, **f32)
     dk = torch.empty(k.shape, **f32)

@@ -13,8 +13,8 @@
 //                    with one split it runs the masked-tile kernel, whose row
 //                    masks and per-token-block done bytes route each block of
 //                    rows to the tile kernels below or to the gather kernels;
-//   bwd_prologue     per (row, head): do (stored as bf16), delta (from the fp32
-//                    do), dgate, dmix;
+//   bwd_prologue     per (row, head): do (stored as bf16), delta (from that bf16
+//                    do, as dP below), dgate, dmix;
 //   tile path        bwd_dq_tile (query-major, the forward's tile structure) and
 //                    bwd_dkdv_tile (key-major: 64 keys per workgroup walking the
 //                    row tiles that can see them, in chunks summed in order by
@@ -27,6 +27,9 @@
 //                    gather rows only; bwd_dkdv: one wave per (position,
 //                    key/value head) over those rows, in 32.32 fixed point
 //                    (int64), added to the tile path's dk, dv.
+// With several index sets (query head h reads set h / (Hq/sets)) every row
+// takes the gather kernels, the position lists are per set, and a dk/dv wave
+// walks the lists of every set its key/value head's query heads read.
 // Every sum runs in a fixed order or in integers: dq, dk, dv are deterministic
 // bit for bit.
 #include <algorithm>
@@ -113,18 +116,26 @@ __global__ __launch_bounds__(256) void bwd_prologue_kernel(
       if (dgate) dgate[base + f] = gy[f] * (ov[f] - x) * s * (1.f - s);
       if (dmix) dmix[base + f] = (1.f - s) * gy[f];
     }
-    dO[base + f] = f32_to_bf16(d_o);
-    acc += d_o * ov[f];
+    // delta from the bf16 do the passes below use for dP = do.v, so that
+    // sum_t P_t (dP_t - delta) stays at the rounding of o: a row with one
+    // entry (P = 1, o = v) then gets dq = 0, as it should
+    const uint16_t dob = f32_to_bf16(d_o);
+    dO[base + f] = dob;
+    acc += bf16_to_f32(dob) * ov[f];
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (lane == 0) delta[rh] = acc;
 }
 
-// dq: one wave per (row, key/value head g); lane = (head hl of the group, slice sl)
+// dq: one wave per (row, unit of G query heads that read one key/value head and
+// one index set: a key/value head's heads, or an index set's when there are
+// more sets than key/value heads); lane = (head hl of the unit, slice sl).
+// Gkv: query heads per key/value head; S: index sets (rows [B][S][Tq][K]).
 template <int D, int G>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(
-    int Tq, int Tk, int K, int Hq, int Hkv, const int32_t* __restrict__ kv_len,
+    int Tq, int Tk, int K, int Hq, int Hkv, int Gkv, int units, int S,
+    const int32_t* __restrict__ kv_len,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const float* __restrict__ lse, const uint16_t* __restrict__ dO,
@@ -136,15 +147,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   if (wv >= nwaves) return;
   const int lane = threadIdx.x & 63;
   const int hl = lane / L, sl = lane % L;
-  const int g = static_cast<int>(wv % Hkv);
-  const int64_t row = wv / Hkv;
+  const int h0 = static_cast<int>(wv % units) * G;  // the unit's first query head
+  const int g = h0 / Gkv;                           // its key/value head
+  const int sg = h0 / (Hq / S);                     // its index set
+  const int64_t row = wv / units;
   const int b = static_cast<int>(row / Tq);
+  const int i = static_cast<int>(row % Tq);
   if (done) {
     // rows of token blocks the tile kernel takes are written there
-    const int i = static_cast<int>(row % Tq);
-    if (done[static_cast<int64_t>(b) * ((Tq + dbq - 1) / dbq) + i / dbq]) return;
+    if (done[(static_cast<int64_t>(b) * S + sg) * ((Tq + dbq - 1) / dbq) + i / dbq]) return;
   }
-  const int h = g * G + hl;
+  const int h = h0 + hl;
   const int64_t rh = row * Hq + h;
   const int kvl0 = kv_len[b];
   const int kvl = kvl0 <= Tk ? kvl0 : 0;
@@ -156,7 +169,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   const float l2 = lse[rh] * LOG2E;  // -inf for a row without entries: no entry is valid then
   const float dlt = delta[rh];
   const float sl2 = scale * LOG2E;
-  const int32_t* ir = idx + row * K;
+  const int32_t* ir = idx + ((static_cast<int64_t>(b) * S + sg) * Tq + i) * K;
   const int64_t rowstep = static_cast<int64_t>(Hkv) * D;
   const uint16_t* kb = k + (static_cast<int64_t>(b) * Tk * Hkv + g) * D + sl * F;
   const uint16_t* vb = v + (static_cast<int64_t>(b) * Tk * Hkv + g) * D + sl * F;
@@ -206,18 +219,20 @@ __device__ __forceinline__ bool tile_row(int64_t row, int b, int Tq, const uint8
   return done[static_cast<int64_t>(b) * ((Tq + dbq - 1) / dbq) + i / dbq] != 0;
 }
 
-__global__ __launch_bounds__(256) void bwd_count_kernel(int Tq, int Tk, int K,
+// index rows [B][S][Tq][K]; the lists are per (sequence, set, position):
+// list (b*S + set)*Tk + s holds query rows b*Tq + i (done bytes only with S = 1)
+__global__ __launch_bounds__(256) void bwd_count_kernel(int Tq, int Tk, int K, int S,
                                                         const int32_t* __restrict__ kv_len,
                                                         const int32_t* __restrict__ idx,
                                                         int64_t nent, int32_t* __restrict__ cnt,
                                                         const uint8_t* __restrict__ done, int dbq) {
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < nent; e += gridDim.x * 256LL) {
-    const int64_t row = e / K;
-    const int b = static_cast<int>(row / Tq);
-    if (tile_row(row, b, Tq, done, dbq)) continue;
+    const int64_t vr = e / K;  // (b*S + set)*Tq + i
+    const int b = static_cast<int>(vr / (static_cast<int64_t>(S) * Tq));
+    if (tile_row(vr, b, Tq, done, dbq)) continue;
     const int kvl = kv_len[b] <= Tk ? kv_len[b] : 0;
     const int s = idx[e];
-    if (s >= 0 && s < kvl) atomicAdd(&cnt[static_cast<int64_t>(b) * Tk + s], 1);
+    if (s >= 0 && s < kvl) atomicAdd(&cnt[(vr / Tq) * Tk + s], 1);
   }
 }
 
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(256) void scan_add_kernel(int32_t* __restrict__ out
     out[i] = i < n ? out[i] + tiles[i / 1024] : tiles[ntiles];
 }
 
-__global__ __launch_bounds__(256) void bwd_fill_kernel(int Tq, int Tk, int K,
+__global__ __launch_bounds__(256) void bwd_fill_kernel(int Tq, int Tk, int K, int S,
                                                        const int32_t* __restrict__ kv_len,
                                                        const int32_t* __restrict__ idx,
                                                        int64_t nent,
@@ -272,25 +287,29 @@ __global__ __launch_bounds__(256) void bwd_fill_kernel(int Tq, int Tk, int K,
                                                        int32_t* __restrict__ rows,
                                                        const uint8_t* __restrict__ done, int dbq) {
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < nent; e += gridDim.x * 256LL) {
-    const int64_t row = e / K;
-    const int b = static_cast<int>(row / Tq);
-    if (tile_row(row, b, Tq, done, dbq)) continue;
+    const int64_t vr = e / K;  // (b*S + set)*Tq + i
+    const int b = static_cast<int>(vr / (static_cast<int64_t>(S) * Tq));
+    if (tile_row(vr, b, Tq, done, dbq)) continue;
     const int kvl = kv_len[b] <= Tk ? kv_len[b] : 0;
     const int s = idx[e];
     if (s >= 0 && s < kvl) {
-      const int64_t key = static_cast<int64_t>(b) * Tk + s;
-      rows[off[key] + atomicAdd(&cursor[key], 1)] = static_cast<int32_t>(row);
+      const int64_t key = (vr / Tq) * Tk + s;
+      rows[off[key] + atomicAdd(&cursor[key], 1)] =
+          static_cast<int32_t>(static_cast<int64_t>(b) * Tq + vr % Tq);
     }
   }
 }
 
-// dk, dv: one wave per (position, key/value head g); lane = (head hl, slice sl)
+// dk, dv: one wave per (position, key/value head g); lane = (head hl, slice sl).
+// The G heads of g read index sets s0 .. s0 + nsg - 1 (query head h reads set
+// h / (Hq/S)); the wave walks each set's list of rows in set order, a lane
+// counting the rows of its own head's set.
 template <int D, int G>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
-    int Hq, int Hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ lse,
-    const uint16_t* __restrict__ dO, const float* __restrict__ delta,
-    const int32_t* __restrict__ off,
+    int Tk, int Hq, int Hkv, int S, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ lse, const uint16_t* __restrict__ dO,
+    const float* __restrict__ delta, const int32_t* __restrict__ off,
     const int32_t* __restrict__ rows, float scale, float* __restrict__ dk,
     float* __restrict__ dv, int64_t nwaves, int add) {
   constexpr int L = 64 / G;
@@ -298,51 +317,66 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   const int lane = threadIdx.x & 63;
   const int hl = lane / L, sl = lane % L;
   const float sl2 = scale * LOG2E;
+  const int hps = Hq / S;  // query heads per index set
   for (int64_t wv = blockIdx.x * 4LL + (threadIdx.x >> 6); wv < nwaves; wv += gridDim.x * 4LL) {
     const int g = static_cast<int>(wv % Hkv);
     const int64_t key = wv / Hkv;  // b*Tk + s: the row of k, v, dk, dv
     const int64_t kvrow = (key * Hkv + g) * D + sl * F;
-    const int r0 = off[key], r1 = off[key + 1];
+    const int64_t b = key / Tk;
+    const int64_t spos = key - b * Tk;
+    const int s0 = g * G / hps;
+    const int nsg = G > hps ? G / hps : 1;
+    const int hset = (g * G + hl) / hps;  // this lane's head's set
+    int nrows = 0;
+    for (int j = 0; j < nsg; ++j) {
+      const int64_t lk = (b * S + s0 + j) * Tk + spos;
+      nrows += off[lk + 1] - off[lk];
+    }
     // add mode: the tile kernel wrote every key; only keys with listed rows change
-    if (add && r1 == r0) continue;
+    if (add && nrows == 0) continue;
     long long ak[F], av[F];
 #pragma unroll
     for (int f = 0; f < F; ++f) ak[f] = av[f] = 0;
-    if (r1 > r0) {
+    if (nrows > 0) {
       float kx[F], vx[F];
       load_bf16<F>(k + kvrow, kx);
       load_bf16<F>(v + kvrow, vx);
-      constexpr int U = 2;  // rows in flight
-      for (int j0 = r0; j0 < r1; j0 += U) {
-        float qx[U][F], dx[U][F], l2[U], dl[U];
-        bool ok[U];
+      for (int j = 0; j < nsg; ++j) {
+        const int64_t lk = (b * S + s0 + j) * Tk + spos;
+        const int r0 = off[lk], r1 = off[lk + 1];
+        const bool mine = hset == s0 + j;
+        constexpr int U = 2;  // rows in flight
+        for (int j0 = r0; j0 < r1; j0 += U) {
+          float qx[U][F], dx[U][F], l2[U], dl[U];
+          bool ok[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          ok[u] = j0 + u < r1;
-          const int64_t row = rows[ok[u] ? j0 + u : r0];
-          const int64_t rh = row * Hq + g * G + hl;
-          load_bf16<F>(q + rh * D + sl * F, qx[u]);
-          load_bf16<F>(dO + rh * D + sl * F, dx[u]);
-          l2[u] = lse[rh] * LOG2E;
-          dl[u] = delta[rh];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float sdot = 0.f, pdot = 0.f;
-#pragma unroll
-          for (int f = 0; f < F; ++f) {
-            sdot += qx[u][f] * kx[f];
-            pdot += dx[u][f] * vx[f];
+          for (int u = 0; u < U; ++u) {
+            ok[u] = j0 + u < r1 && mine;
+            const int64_t row = rows[j0 + u < r1 ? j0 + u : r0];
+            const int64_t rh = row * Hq + g * G + hl;
+            load_bf16<F>(q + rh * D + sl * F, qx[u]);
+            load_bf16<F>(dO + rh * D + sl * F, dx[u]);
+            l2[u] = lse[rh] * LOG2E;
+            dl[u] = delta[rh];
           }
-          sdot = head_sum<L>(sdot);
-          pdot = head_sum<L>(pdot);
-          if (!ok[u]) continue;
-          const float p = fast_exp2(sdot * sl2 - l2[u]);
-          const float ds = scale * p * (pdot - dl[u]);
 #pragma unroll
-          for (int f = 0; f < F; ++f) {
-            av[f] += __float2ll_rn(p * dx[u][f] * kFix);
-            ak[f] += __float2ll_rn(ds * qx[u][f] * kFix);
+          for (int u = 0; u < U; ++u) {
+            float sdot = 0.f, pdot = 0.f;
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+              sdot += qx[u][f] * kx[f];
+              pdot += dx[u][f] * vx[f];
+            }
+            sdot = head_sum<L>(sdot);
+            pdot = head_sum<L>(pdot);
+            if (!ok[u]) continue;
+            const float p = fast_exp2(sdot * sl2 - l2[u]);
+            const float ds = scale * p * (pdot - dl[u]);
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+              av[f] += __float2ll_rn(p * dx[u][f] * kFix);
+              ak[f] += __float2ll_rn(ds * qx[u][f] * kFix);
+            }
           }
         }
       }
@@ -868,6 +902,34 @@ __global__ __launch_bounds__(256) void bwd_part_sum_kernel(
   }
 }
 
+// dq of the gather rows: one wave per (row, unit); a unit is a key/value head's
+// query heads, or an index set's when there are more sets than key/value heads
+template <int D>
+hipError_t launch_dq_gather(const Geom& g, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const int32_t* idx, const float* lse,
+                            const uint16_t* dO, const float* dlt, float scale, float* dq,
+                            const uint8_t* done, int dbq, hipStream_t st) {
+  const int units = std::max(g.sets, g.Hkv);
+  const int gu = g.Hq / units;  // query heads per wave
+  const int64_t nw = static_cast<int64_t>(g.B) * g.Tq * units;
+  const dim3 grid(static_cast<uint32_t>((nw + 3) / 4));
+  KernelTimer timer(LCI_KERNEL_BWD_DQ, st);
+#define LCI_DQ_GATHER(GU)                                                                         \
+  hipLaunchKernelGGL((bwd_dq_kernel<D, GU>), grid, dim3(256), 0, st, g.Tq, g.Tk, g.K, g.Hq, g.Hkv, \
+                     g.Hq / g.Hkv, units, g.sets, g.kv_len, q, k, v, idx, lse, dO, dlt, scale, dq, \
+                     nw, done, dbq)
+  switch (gu) {
+    case 1: LCI_DQ_GATHER(1); break;
+    case 2: LCI_DQ_GATHER(2); break;
+    case 4: LCI_DQ_GATHER(4); break;
+    case 8: LCI_DQ_GATHER(8); break;
+    case 16: LCI_DQ_GATHER(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LCI_DQ_GATHER
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* idx, const float* lse, const uint16_t* dO, const float* dlt,
@@ -889,14 +951,9 @@ hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, co
                        nblk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int64_t nrow_w = static_cast<int64_t>(g.B) * g.Tq * g.Hkv;
-  {
-    KernelTimer timer(LCI_KERNEL_BWD_DQ, st);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(static_cast<uint32_t>((nrow_w + 3) / 4)),
-                       dim3(256), 0, st, g.Tq, g.Tk, g.K, g.Hq, g.Hkv, g.kv_len, q, k, v, idx,
-                       lse, dO, dlt, scale, dq, nrow_w, dm ? dm->done : nullptr, C::BQ);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_dq_gather<D>(g, q, k, v, idx, lse, dO, dlt, scale, dq, dm ? dm->done : nullptr,
+                               C::BQ, st)) != hipSuccess)
+    return e;
   if (dm) {
     // every key from the tile-path rows; the gather rows are added below
     const int nbps = (g.Tq + C::BQ - 1) / C::BQ;
@@ -929,8 +986,8 @@ hipError_t launch_bwd_dg(const Geom& g, const uint16_t* q, const uint16_t* k, co
     KernelTimer timer(LCI_KERNEL_BWD_DKDV, st);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>),
                        dim3(static_cast<uint32_t>(std::min<int64_t>((nkey_w + 3) / 4, 1 << 16))),
-                       dim3(256), 0, st, g.Hq, g.Hkv, q, k, v, lse, dO, dlt, off, rows,
-                       scale, dk, dv, nkey_w, dm ? 1 : 0);
+                       dim3(256), 0, st, g.Tk, g.Hq, g.Hkv, g.sets, q, k, v, lse, dO, dlt, off,
+                       rows, scale, dk, dv, nkey_w, dm ? 1 : 0);
   }
   return hipGetLastError();
 }
@@ -968,10 +1025,11 @@ hipError_t launch_exclusive_scan(const int32_t* in, int64_t n, int32_t* out, int
 
 
 // [forward workspace][o bf16][lse][do][delta][counts][offsets (+1)][cursors][tiles (+1)][rows]
+// with the position lists per (sequence, index set, position)
 BwdLayout bwd_layout(const Geom& g) {
   BwdLayout L{};
   const size_t rows = static_cast<size_t>(g.B) * g.Tq;
-  const size_t keys = static_cast<size_t>(g.B) * g.Tk;
+  const size_t keys = static_cast<size_t>(g.B) * g.sets * g.Tk;
   L.splits = sparse_attn_pick_splits(g);
   L.fwd = 0;
   L.o = L.fwd + align256(sparse_attn_workspace(g, L.splits));
@@ -984,14 +1042,14 @@ BwdLayout bwd_layout(const Geom& g) {
   L.tiles = L.cursor + align256(keys * sizeof(int32_t));
   L.ntiles = static_cast<int>((keys + 1023) / 1024);
   L.rows = L.tiles + align256((L.ntiles + 1) * sizeof(int32_t));
-  L.part = L.rows + align256(rows * g.K * sizeof(int32_t));
+  L.part = L.rows + align256(rows * g.sets * g.K * sizeof(int32_t));
   // the key-major tile kernel splits each key block's rows into up to
   // kBwdChunks chunks (balance: the first key blocks see every row, the last
   // few), each writing partial dk and dv, as many as fit in kBwdPartMax bytes
   // of partials; with one chunk the kernel writes dk, dv directly
-  const size_t pbytes = keys * g.Hkv * g.d * sizeof(float) * 2;
+  const size_t pbytes = static_cast<size_t>(g.B) * g.Tk * g.Hkv * g.d * sizeof(float) * 2;
   L.nch = 1;
-  if (L.splits == 1)
+  if (L.splits == 1 && g.sets == 1)
     for (int n = kBwdChunks; n > 1; n /= 2)
       if (n * pbytes <= kBwdPartMax) {
         L.nch = n;
@@ -1036,28 +1094,29 @@ hipError_t launch_sparse_attn_bwd(const Geom& g, const uint16_t* q, const uint16
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // with one split the forward ran the tile path: its masks, row flags and
   // done bytes sit in the forward workspace. The position lists below hold
-  // only the rows of the other token blocks.
+  // only the rows of the other token blocks. With several index sets every
+  // row takes the gather kernels.
   const DenseMasks dmv = dense_masks(g, ws + L.fwd);
-  const DenseMasks* dm = L.splits == 1 ? &dmv : nullptr;
+  const DenseMasks* dm = L.splits == 1 && g.sets == 1 ? &dmv : nullptr;
   const uint8_t* done = dm ? dm->done : nullptr;
   const int dbq = dense_block_rows(g.Hq / g.Hkv);
-  // the rows that selected each position
-  const int64_t keys = static_cast<int64_t>(g.B) * g.Tk;
-  const int64_t nent = static_cast<int64_t>(g.B) * g.Tq * g.K;
+  // the rows that selected each position, per index set
+  const int64_t keys = static_cast<int64_t>(g.B) * g.sets * g.Tk;
+  const int64_t nent = static_cast<int64_t>(g.B) * g.sets * g.Tq * g.K;
   const uint32_t gk = static_cast<uint32_t>(std::min<int64_t>((keys + 255) / 256, 8192));
   const uint32_t ge = static_cast<uint32_t>(std::min<int64_t>((nent + 255) / 256, 8192));
   {
     KernelTimer timer(LCI_KERNEL_BWD_TRANSPOSE, st);
     hipLaunchKernelGGL(fill_i32_kernel, dim3(gk), dim3(256), 0, st, cnt, keys, 0);
     hipLaunchKernelGGL(fill_i32_kernel, dim3(gk), dim3(256), 0, st, cursor, keys, 0);
-    hipLaunchKernelGGL(bwd_count_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, g.kv_len,
-                       idx, nent, cnt, done, dbq);
+    hipLaunchKernelGGL(bwd_count_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, g.sets,
+                       g.kv_len, idx, nent, cnt, done, dbq);
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<uint32_t>(L.ntiles)), dim3(256), 0, st,
                        cnt, keys, off, tiles);
     hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(1024), 0, st, tiles, L.ntiles);
     hipLaunchKernelGGL(scan_add_kernel, dim3(gk), dim3(256), 0, st, off, keys, tiles, L.ntiles);
-    hipLaunchKernelGGL(bwd_fill_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, g.kv_len,
-                       idx, nent, off, cursor, rows, done, dbq);
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, g.sets,
+                       g.kv_len, idx, nent, off, cursor, rows, done, dbq);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (g.d) {

@@ -132,7 +132,8 @@ hipError_t launch_block_topk(const Geom& g, const int32_t* scores, int64_t score
 hipError_t launch_regroup_q_idx(const Geom& g, const int8_t* q_idx, int8_t* out,
                                 hipStream_t stream);
 
-// ---- gradients of sparse attention + gate (g.K = index row length, one set)
+// ---- gradients of sparse attention + gate (g.K = index row length; index rows
+// [B][g.sets][Tq][K])
 struct BwdLayout {
   size_t fwd, o, lse, dO, delta, cnt, off, cursor, tiles, rows, part, total;
   int splits, ntiles;

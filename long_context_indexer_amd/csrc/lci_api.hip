@@ -199,7 +199,7 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
       // the weights' strides are not known here: enough for either scoring path
       return std::max(prefill_layout(g, 0, 0).total, prefill_layout(g, 1, 1).total);
     case LCI_ENTRY_SPARSE_ATTN_BWD: {
-      if (check_attention(g) != LCI_OK || sel_sets(g) > 1 || g->sets < 0) return 0;
+      if (check_attention(g) != LCI_OK || check_sets(g, false, true) != LCI_OK) return 0;
       return lci::bwd_layout(attn_geom(g)).total;
     }
     case LCI_ENTRY_INDEXER_BWD:
@@ -444,16 +444,15 @@ lci_status lci_sparse_attn_bwd(const lci_geom* g, const lci_bf16* q, const lci_b
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if ((s = check_attention(g)) != LCI_OK) return s;
-  if (g->sets < 0) return LCI_ERR_SHAPE;
-  if (sel_sets(g) > 1) return LCI_ERR_UNSUPPORTED;
+  if ((s = check_sets(g, false, true)) != LCI_OK) return s;
   if (!q || !k || !v || !idx || !dy || !dq || !dk || !dv || (mix && !gate) ||
       (dgate && !gate) || (dmix && !mix))
     return LCI_ERR_NULL;
   if (!scale_ok(softmax_scale)) return LCI_ERR_SHAPE;
   const Geom ga = attn_geom(g);
   // the transpose of the index rows addresses entries with int32 offsets
-  if (static_cast<int64_t>(g->B) * g->Tq * ga.K >= (int64_t(1) << 31) ||
-      static_cast<int64_t>(g->B) * g->Tk >= (int64_t(1) << 31))
+  if (static_cast<int64_t>(g->B) * ga.sets * g->Tq * ga.K >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(g->B) * ga.sets * g->Tk >= (int64_t(1) << 31))
     return LCI_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dy) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || (gate && !aligned16(gate)) ||

@@ -159,7 +159,11 @@ def test_backward_arguments(lib):
     assert bwd(geom(), dq=None) == NULL
     assert bwd(geom(), dgate=FAKE) == NULL                     # dgate without a gate
     assert bwd(geom(), gate=FAKE, dmix=FAKE) == NULL          # dmix without a mix
-    assert bwd(geom(sets=2)) == UNSUP
+    assert bwd(geom(sets=3)) == SHAPE                         # does not divide Hq
+    assert bwd(geom(sets=16)) == SHAPE                        # more sets than query heads
+    two = lib.lci_workspace_bytes(lci.ENTRY_SPARSE_ATTN_BWD, ctypes.byref(geom(sets=2)))
+    per_head = lib.lci_workspace_bytes(lci.ENTRY_SPARSE_ATTN_BWD, ctypes.byref(geom(sets=8)))
+    assert per_head > two > 0                                 # position lists per set
     assert bwd(geom(), nb=16) == WS
     assert bwd(geom(), ws=None) == WS
     assert bwd(geom(), dq=FAKE + 4) == ALIGN

@@ -3,8 +3,9 @@ against the oracle's chain rule in fp64.
 
 Tolerance: the kernels recompute the forward output o and round it to bf16
 (2^-9 relative) before it enters delta = do.o and dgate, keep do in bf16 for
-the two passes over the selected pairs (2^-9 relative in dv and dP), and
-accumulate in fp32; dk and dv are summed in 32.32 fixed point (2^-33 per
+delta and the two passes over the selected pairs (2^-9 relative in dv and dP;
+the same rounded do in delta and dP keeps sum_t dl_t at the rounding of o),
+and accumulate in fp32; dk and dv are summed in 32.32 fixed point (2^-33 per
 contribution). The comparison allows relative L2 1e-2 and max-abs 2e-2 of the
 largest reference value per gradient (measured: at most 3e-3 and 1.2e-2). dq,
 dk and dv must be bit-identical across runs (order-free integer sums)."""
@@ -213,3 +214,82 @@ def test_sparse_attn_bwd_prefill8k_chunk_seams(lci, orc):
     _close(host(res["dq"])[:, S], want["dq"], "8k seam rows dq")
     _close(host(res["dk"])[:, lo:hi], want["dk"][:, lo:hi], f"8k keys {lo}..{hi - 1} dk")
     _close(host(res["dv"])[:, lo:hi], want["dv"][:, lo:hi], f"8k keys {lo}..{hi - 1} dv")
+
+
+def _random_set_rows(cfg, inp, sets, seed):
+    """Random valid index rows per set: int32 [B, Tq, sets, K]."""
+    return np.stack([synth.index_rows(inp["q_offset"], inp["kv_len"], cfg.Tq, cfg.K,
+                                      seed=seed + j) for j in range(sets)], axis=2)
+
+
+def _sets_case(orc, name):
+    """(config, inputs, index rows [B, Tq, sets, K], gated) of the set cases."""
+    if name == "per_kv_head_mix":
+        cfg = MED.replace(Tq=200, Tk=200, K=48)
+        inp = synth.host_inputs(cfg, seed=80)
+        inp["mix"] = synth.host_mix(cfg, seed=80)
+        idx = orc.layer(inp, cfg.K, sets=cfg.Hkv)["idx"].reshape(cfg.B, cfg.Tq, cfg.Hkv, cfg.K)
+        return cfg, inp, idx, True
+    if name == "per_query_head_two_sequences":
+        cfg = MED.replace(B=2, Hq=8, Hkv=2, H_I=8, Tq=90, Tk=260, K=40)
+        inp = synth.host_inputs(cfg, seed=81)
+        inp["q_offset"] = np.array([170, 0], np.int32)
+        inp["kv_len"] = np.array([260, 70], np.int32)   # sequence 1: rows past 69 are empty
+        idx = orc.layer(inp, cfg.K, sets=cfg.Hq)["idx"].reshape(cfg.B, cfg.Tq, cfg.Hq, cfg.K)
+        return cfg, inp, idx, True
+    if name == "sets2_over_kv4_ungated":
+        cfg = MED.replace(Tq=160, Tk=160, K=40)
+        inp = synth.host_inputs(cfg, seed=82)
+        idx = _random_set_rows(cfg, inp, 2, 82)
+        return cfg, inp, idx, False
+    if name == "per_query_head_splits":
+        # one-row sequences with long lists: the forward recompute splits them
+        cfg = MED.replace(B=4, Hq=8, Hkv=2, Tq=1, Tk=3000, K=512, n_needles=0, needles="none")
+        inp = synth.host_inputs(cfg, seed=83)
+        inp["kv_len"] = np.array([3000, 900, 1, 2048], np.int32)
+        inp["q_offset"] = inp["kv_len"] - 1
+        idx = _random_set_rows(cfg, inp, cfg.Hq, 83)
+        return cfg, inp, idx, True
+    if name == "per_query_head_g16_d64":
+        cfg = TINY.replace(Hq=16, Hkv=1, d=64, Tq=70, Tk=150, K=30)
+        inp = synth.host_inputs(cfg, seed=84)
+        inp["q_offset"] = np.array([80], np.int32)
+        idx = _random_set_rows(cfg, inp, cfg.Hq, 84)
+        return cfg, inp, idx, True
+    raise KeyError(name)
+
+
+SET_CASES = ["per_kv_head_mix", "per_query_head_two_sequences", "sets2_over_kv4_ungated",
+             "per_query_head_splits", "per_query_head_g16_d64"]
+
+
+@pytest.mark.parametrize("name", SET_CASES)
+def test_sparse_attn_bwd_sets(lci, orc, name):
+    """Gradients over index sets (query head h reads set h // (Hq // sets)):
+    every row takes the gather kernels, dk and dv walk each set's list of rows;
+    against the oracle's chain rule, and bit-identical across two calls."""
+    import torch
+    cfg, inp, idx, gated = _sets_case(orc, name)
+    sets = idx.shape[2]
+    r = np.random.default_rng(85)
+    dy = synth.bf16_bits(r.standard_normal((cfg.B, cfg.Tq, cfg.Hq, cfg.d), dtype=np.float32))
+    gate = inp["gate"] if gated else None
+    mix = inp.get("mix") if gated else None
+    log(f"bwd sets {name}: B={cfg.B} Tq={cfg.Tq} Tk={cfg.Tk} Hq={cfg.Hq} Hkv={cfg.Hkv} "
+        f"d={cfg.d} K={cfg.K} sets={sets} gated={gated}")
+    d = to_device(inp)
+    idx4 = np.ascontiguousarray(idx.transpose(0, 2, 1, 3))   # [B, sets, Tq, K]
+    args = (d["q"], d["k"], d["v"], dev(idx4), dev(gate), inp["scale"], d["kv_len"], dev(dy))
+    res = lci.sparse_attn_bwd(*args, q_offset=d["q_offset"], mix=dev(mix))
+    torch.cuda.synchronize()
+    want = orc.attention_bwd(inp["q"], inp["k"], inp["v"], gate, idx, inp["kv_len"],
+                             inp["scale"], dy, mix=mix)
+    for key in ("dq", "dk", "dv", "dgate", "dmix"):
+        if want[key] is None:
+            assert res[key] is None
+            continue
+        _close(host(res[key]), want[key], f"{name} {key}")
+    res2 = lci.sparse_attn_bwd(*args, q_offset=d["q_offset"], mix=dev(mix))
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(res[key], res2[key]), key
