@@ -312,6 +312,67 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
 
 
+def probe_peaks():
+    """Peaks reachable on this GPU, reported beside the vendor ones: a 2 GiB
+    device-to-device copy (HBM read + write bytes over time), a sum over 8 GiB
+    (read bytes over time; the HBM reference is the faster of the two), and bf16 and int8
+    GEMMs of 8192 x 8192 x 8192 through the installed BLAS library (the matrix
+    cores' rate a tuned library reaches). Torch's own kernels on its current
+    stream, timed with torch events; None where a probe is not available."""
+    import torch
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    out = {}
+    n = 2 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    out["hbm_copy_gbs"] = round(2 * n / timed(lambda: dst.copy_(src), 10) / 1e9, 1)
+    del src, dst
+    x = torch.ones(n, dtype=torch.float32, device="cuda")  # 8 GiB, read once per sum
+    out["hbm_read_gbs"] = round(4 * n / timed(lambda: x.sum(), 5) / 1e9, 1)
+    del x
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    out["bf16_gemm_tflops"] = round(2 * m ** 3 / timed(lambda: torch.matmul(a, b), 10) / 1e12, 1)
+    del a, b
+    try:
+        a8 = torch.randint(-8, 8, (m, m), dtype=torch.int8, device="cuda")
+        b8 = torch.randint(-8, 8, (m, m), dtype=torch.int8, device="cuda")
+        out["int8_gemm_tops"] = round(2 * m ** 3 / timed(lambda: torch._int_mm(a8, b8), 10) / 1e12, 1)
+        del a8, b8
+    except (RuntimeError, AttributeError):
+        out["int8_gemm_tops"] = None
+    torch.cuda.empty_cache()
+    out["note"] = ("reachable rates measured here (copy kernel, library GEMMs); rooflines "
+                   "give frac against the vendor peak and frac_probe against these")
+    return out
+
+
+def add_probe_fracs(node, probes):
+    """frac_probe beside frac in every roofline dict under node (in place)."""
+    hbm = max(probes.get("hbm_copy_gbs") or 0.0, probes.get("hbm_read_gbs") or 0.0) or None
+    ref = {"GB/s": hbm, "TFLOP/s": probes.get("bf16_gemm_tflops"),
+           "TOP/s": probes.get("int8_gemm_tops")}
+    if isinstance(node, dict):
+        if "frac" in node and "achieved" in node and node.get("unit") in ref:
+            pk = ref[node["unit"]]
+            node["frac_probe"] = round(node["achieved"] / pk, 4) if pk and node["achieved"] else None
+        for v in node.values():
+            add_probe_fracs(v, probes)
+
+
 def host(t):
     """Host numpy copy of a device tensor (bf16 as its uint16 bit pattern)."""
     import torch
@@ -736,6 +797,11 @@ def main():
     for name in ("blocks", "sets", "backward", "indexer_bwd"):
         if name in res:
             line[name] = res[name]
+    probes = probe_peaks()
+    log(f"probe peaks: HBM copy {probes['hbm_copy_gbs']} GB/s, read {probes['hbm_read_gbs']} GB/s, bf16 GEMM "
+        f"{probes['bf16_gemm_tflops']} TFLOP/s, int8 GEMM {probes['int8_gemm_tops']} TOP/s")
+    line["probe_peaks"] = probes
+    add_probe_fracs(line, probes)
     print(json.dumps(line), flush=True)
 
 
