@@ -335,7 +335,8 @@ lci_status lci_sparse_attn_bwd(const lci_geom *g, const lci_bf16 *q, const lci_b
  *            entry points); dw fp32 [B, Tq, H_I] out (per row: for weights shared
  *            by every row, their gradient is the sum over rows)
  *   workspace at least lci_workspace_bytes(LCI_ENTRY_INDEXER_BWD): g and the
- *            heads' ReLU masks per entry, and the entries of each position. dk
+ *            heads' ReLU masks per entry, the entries of each position, and
+ *            the query rows with each feature's heads side by side. dk
  *            sums its products as 64-bit integers with 32 fraction bits (the
  *            sum does not depend on the order: deterministic); each element's
  *            sum must stay below 2^31 in size. B*Tq*K < 2^31 (SHAPE).

@@ -26,9 +26,12 @@
 //   ibwd_count/fill    the transpose of the index rows: for each position, the
 //                      entries that point at it (counts, an exclusive scan,
 //                      then the entry numbers in any order).
-//   ibwd_dk_kernel     one wave per position: dk[s, j] (lane j) sums, over its
-//                      entries, g_t u_tj with u_t = sum_h w_h [d_ht > 0] qI[i,h]
-//                      (exact integers), each product rounded to 32 fraction bits
+//   ibwd_dk_kernel     one wave per 256 entries of the position-ordered list:
+//                      dk[s, j] (lane j) sums, over the entries of s, g_t u_tj
+//                      with u_t = sum_h w_h [d_ht > 0] qI[i,h] (exact: v_dot4
+//                      of the row's heads of feature j, read from a transposed
+//                      copy of the query rows, with the entry's masked
+//                      weights), each product rounded to 32 fraction bits
 //                      and added as a 64-bit integer: the sum does not depend
 //                      on the entries' order, so dk is deterministic.
 #include "common.h"
@@ -306,34 +309,52 @@ __global__ __launch_bounds__(256) void ibwd_fill_kernel(int Tq, int Tk, int K,
 // rounding shift) as 64-bit integers; when the position changes, and at the
 // end of the chunk, the sums go into the position's accumulator by integer
 // atomics. Integer sums do not depend on their order: deterministic.
+// Query rows with each feature's heads side by side: qT[row][j] holds
+// qI[row, h, j] for h = 0 .. H_I-1 as int8 in (H_I + 3) / 4 words (zero padded),
+// so the dk kernel reads one feature's heads with one or two dword loads and
+// sums them with v_dot4. One thread per (row, feature).
+template <int H_I, int D_I>
+__global__ __launch_bounds__(256) void ibwd_qt_kernel(int64_t rows, const int8_t* __restrict__ q_idx,
+                                                      uint32_t* __restrict__ qT) {
+  constexpr int NW = (H_I + 3) / 4;
+  for (int64_t x = blockIdx.x * 256LL + threadIdx.x; x < rows * D_I; x += gridDim.x * 256LL) {
+    const int64_t row = x / D_I;
+    const int j = static_cast<int>(x - row * D_I);
+    const int8_t* qr = q_idx + row * H_I * D_I + j;
+#pragma unroll
+    for (int n = 0; n < NW; ++n) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (4 * n + b < H_I) word |= static_cast<uint32_t>(static_cast<uint8_t>(qr[(4 * n + b) * D_I])) << (8 * b);
+      qT[x * NW + n] = word;
+    }
+  }
+}
+
 template <int H_I, int D_I>
 __global__ __launch_bounds__(256) void ibwd_dk_kernel(
-    int Tq, int K, const int8_t* __restrict__ q_idx, const int8_t* __restrict__ w, int64_t wsb,
+    int Tq, int K, const uint32_t* __restrict__ qT, const int8_t* __restrict__ w, int64_t wsb,
     int64_t wsq, const int32_t* __restrict__ ents, const int32_t* __restrict__ ekey,
     const float* __restrict__ g_ent, const uint16_t* __restrict__ m_ent,
     unsigned long long* __restrict__ acc_dk, const int32_t* __restrict__ total) {
   constexpr int JL = (D_I + 63) / 64;   // features per lane
+  constexpr int NW = (H_I + 3) / 4;     // words of one feature's heads
   const int64_t nlist = *total;         // the valid entries (the count total)
   constexpr int EB = D_I > 64 ? 4 : 8;  // entries per load group
   const int lane = threadIdx.x & 63;
   const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nw = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-  for (int64_t c0 = w0 * 64; c0 < nlist; c0 += nw * 64) {
-    const int n = static_cast<int>(min<int64_t>(64, nlist - c0));
-    // this lane's entry of the chunk
-    int my_row = 0, my_key = -1, my_hm = 0;
-    float my_g = 0.f;
-    if (lane < n) {
-      const int e = ents[c0 + lane];
-      my_row = e / K;
-      my_key = ekey[c0 + lane];
-      my_hm = m_ent[e];
-      my_g = g_ent[e];
-    }
+  // each wave takes SC consecutive entries of the list (64 at a time) and
+  // keeps its sums across them: a position's entries are flushed once per
+  // wave that holds them, not once per 64
+  constexpr int SC = 256;
+  for (int64_t s0 = w0 * SC; s0 < nlist; s0 += nw * SC) {
+    const int64_t s1 = min<int64_t>(s0 + SC, nlist);
     long long acc[JL];
 #pragma unroll
     for (int c = 0; c < JL; ++c) acc[c] = 0;
-    int cur = __shfl(my_key, 0, 64);
+    int cur = ekey[s0];
     auto flush = [&](int key) {
 #pragma unroll
       for (int c = 0; c < JL; ++c) {
@@ -343,61 +364,89 @@ __global__ __launch_bounds__(256) void ibwd_dk_kernel(
         acc[c] = 0;
       }
     };
-    for (int k0 = 0; k0 < n; k0 += EB) {
-      // the group's entries are the same for every lane: scalar registers
-      int rowv[EB], hmv[EB], keyv[EB];
-      uint32_t gbits[EB];
+    for (int64_t c0 = s0; c0 < s1; c0 += 64) {
+      const int n = static_cast<int>(min<int64_t>(64, s1 - c0));
+      // this lane's entry of the chunk: its query row, position, the weights of
+      // the heads whose ReLU passed it packed like qT's words, and g split as
+      // g = mant * 2^(ex - 150) exactly (fp32 bits), so that g*u*2^32 is mant*u
+      // (exact in 64 bits) shifted right by 118 - ex, rounded
+      int my_row = 0, my_key = -1, my_mant = 0, my_sh = 63;
+      uint32_t my_wm[NW];
 #pragma unroll
-      for (int k = 0; k < EB; ++k) {
-        const int src = min(k0 + k, 63);
-        rowv[k] = __builtin_amdgcn_readlane(my_row, src);
-        keyv[k] = k0 + k < n ? __builtin_amdgcn_readlane(my_key, src) : -1;
-        hmv[k] = k0 + k < n ? __builtin_amdgcn_readlane(my_hm, src) : 0;
-        gbits[k] = __builtin_amdgcn_readlane(__float_as_uint(my_g), src);
-      }
-      int8_t qv[EB][JL][H_I];
-#pragma unroll
-      for (int k = 0; k < EB; ++k) {
-        const int8_t* qr = q_idx + static_cast<int64_t>(rowv[k]) * H_I * D_I;
-#pragma unroll
-        for (int c = 0; c < JL; ++c)
-#pragma unroll
-          for (int hh = 0; hh < H_I; ++hh)
-            qv[k][c][hh] = lane + 64 * c < D_I ? qr[hh * D_I + lane + 64 * c] : 0;
-      }
-#pragma unroll
-      for (int k = 0; k < EB; ++k) {
-        if (keyv[k] < 0) break;  // past the chunk (uniform)
-        if (keyv[k] != cur) {   // a new position (uniform)
-          flush(cur);
-          cur = keyv[k];
-        }
-        const int row = rowv[k];
-        const int b = row / Tq;
-        const int i = row - b * Tq;
+      for (int m = 0; m < NW; ++m) my_wm[m] = 0u;
+      if (lane < n) {
+        const int e = ents[c0 + lane];
+        my_row = e / K;
+        my_key = ekey[c0 + lane];
+        const int hm = m_ent[e];
+        const int b = my_row / Tq;
+        const int i = my_row - b * Tq;
         const int8_t* wr = w + b * wsb + static_cast<int64_t>(i) * wsq;
-        // weights of the heads whose ReLU passed this entry (uniform)
-        int wm[H_I];
 #pragma unroll
-        for (int hh = 0; hh < H_I; ++hh) wm[hh] = ((hmv[k] >> hh) & 1) ? static_cast<int>(wr[hh]) : 0;
-        // g = mant * 2^(ex - 150) exactly (fp32 bits), so g*u*2^32 is
-        // mant*u (exact in 64 bits) shifted right by 118 - ex, rounded
-        const uint32_t gb = gbits[k];
+        for (int m = 0; m < NW; ++m) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int hh = 4 * m + bb;
+            if (hh < H_I && ((hm >> hh) & 1))
+              word |= static_cast<uint32_t>(static_cast<uint8_t>(wr[hh])) << (8 * bb);
+          }
+          my_wm[m] = word;
+        }
+        const uint32_t gb = __float_as_uint(g_ent[e]);
         const int ex = static_cast<int>((gb >> 23) & 0xffu);
-        int mant = static_cast<int>(gb & 0x7fffffu) | (ex ? 0x800000 : 0);
-        if (gb >> 31) mant = -mant;
-        const int sh = 118 - (ex ? ex : 1);
+        my_mant = static_cast<int>(gb & 0x7fffffu) | (ex ? 0x800000 : 0);
+        if (gb >> 31) my_mant = -my_mant;
+        my_sh = 118 - (ex ? ex : 1);
+      }
+      for (int k0 = 0; k0 < n; k0 += EB) {
+        // the group's entries are the same for every lane: scalar registers
+        int rowv[EB], keyv[EB];
 #pragma unroll
-        for (int c = 0; c < JL; ++c) {
-          int u = 0;
+        for (int k = 0; k < EB; ++k) {
+          const int src = min(k0 + k, 63);
+          rowv[k] = __builtin_amdgcn_readlane(my_row, src);
+          keyv[k] = k0 + k < n ? __builtin_amdgcn_readlane(my_key, src) : -1;
+        }
+        // feature j's heads of each entry's query row (all loads in flight together)
+        uint32_t qv[EB][JL][NW];
 #pragma unroll
-          for (int hh = 0; hh < H_I; ++hh) u += wm[hh] * static_cast<int>(qv[k][c][hh]);
-          const long long prod = static_cast<long long>(mant) * u;
-          long long add;
-          if (sh <= 0) add = prod << (-sh);
-          else if (sh > 62) add = 0;
-          else add = (prod + (1ll << (sh - 1))) >> sh;
-          acc[c] += add;
+        for (int k = 0; k < EB; ++k) {
+          const uint32_t* qr = qT + static_cast<int64_t>(rowv[k]) * D_I * NW;
+#pragma unroll
+          for (int c = 0; c < JL; ++c)
+#pragma unroll
+            for (int m = 0; m < NW; ++m)
+              qv[k][c][m] = lane + 64 * c < D_I ? qr[(lane + 64 * c) * NW + m] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < EB; ++k) {
+          if (keyv[k] < 0) break;  // past the chunk (uniform)
+          if (keyv[k] != cur) {   // a new position (uniform)
+            flush(cur);
+            cur = keyv[k];
+          }
+          const int src = k0 + k;
+          int wm[NW];
+#pragma unroll
+          for (int m = 0; m < NW; ++m)
+            wm[m] = __builtin_amdgcn_readlane(static_cast<int>(my_wm[m]), src);
+          const int mant = __builtin_amdgcn_readlane(my_mant, src);
+          const int sh = __builtin_amdgcn_readlane(my_sh, src);
+#pragma unroll
+          for (int c = 0; c < JL; ++c) {
+            // u = sum_h w_h [d_h > 0] qI[h, j]: exact int8 dot products
+            int u = 0;
+#pragma unroll
+            for (int m = 0; m < NW; ++m)
+              u = __builtin_amdgcn_sdot4(static_cast<int>(qv[k][c][m]), wm[m], u, false);
+            const long long prod = static_cast<long long>(mant) * u;
+            long long add;
+            if (sh <= 0) add = prod << (-sh);
+            else if (sh > 62) add = 0;
+            else add = (prod + (1ll << (sh - 1))) >> sh;
+            acc[c] += add;
+          }
         }
       }
     }
@@ -419,7 +468,7 @@ __global__ __launch_bounds__(256) void ibwd_dk_out_kernel(const unsigned long lo
 // ------------------------------------------------------------------ host side
 
 struct IbwdLayout {
-  size_t g, m, cnt, off, cursor, tiles, ents, ekey, acc, total;
+  size_t g, m, cnt, off, cursor, tiles, ents, ekey, acc, qt, total;
 };
 
 static IbwdLayout ibwd_layout(const Geom& g) {
@@ -437,6 +486,7 @@ static IbwdLayout ibwd_layout(const Geom& g) {
   L.ents = o;   o += al(nent * sizeof(int32_t));
   L.ekey = o;   o += al(nent * sizeof(int32_t));
   L.acc = o;    o += al(keys * g.d_I * sizeof(unsigned long long));
+  L.qt = o;     o += al(static_cast<size_t>(g.B) * g.Tq * g.d_I * ((g.H_I + 3) / 4) * sizeof(uint32_t));
   L.total = o;
   return L;
 }
@@ -463,6 +513,7 @@ static hipError_t ibwd_launch_hd(const Geom& g, const int8_t* q_idx, const int8_
   int32_t* ents = reinterpret_cast<int32_t*>(base + L.ents);
   int32_t* ekey = reinterpret_cast<int32_t*>(base + L.ekey);
   unsigned long long* acc = reinterpret_cast<unsigned long long*>(base + L.acc);
+  uint32_t* qt = reinterpret_cast<uint32_t*>(base + L.qt);
   const int64_t keys = static_cast<int64_t>(g.B) * g.Tk;
   const int64_t nent = static_cast<int64_t>(g.B) * g.Tq * g.K;
   const uint32_t gk = static_cast<uint32_t>(std::min<int64_t>((keys + 255) / 256, 8192));
@@ -492,9 +543,13 @@ static hipError_t ibwd_launch_hd(const Geom& g, const int8_t* q_idx, const int8_
     const int64_t nacc = keys * g.d_I;
     const uint32_t ga = static_cast<uint32_t>(std::min<int64_t>((nacc + 255) / 256, 8192));
     hipLaunchKernelGGL(ibwd_zero_u64_kernel, dim3(ga), dim3(256), 0, st, acc, nacc);
+    const int64_t rows = static_cast<int64_t>(g.B) * g.Tq;
+    const uint32_t gq = static_cast<uint32_t>(std::min<int64_t>((rows * D_I + 255) / 256, 8192));
+    hipLaunchKernelGGL((ibwd_qt_kernel<H_I, D_I>), dim3(gq), dim3(256), 0, st, rows, q_idx, qt);
     // the list holds the valid entries: as many as the count total off[keys]
-    const uint32_t gd = static_cast<uint32_t>(std::min<int64_t>((nent + 255) / 256, 8192));
-    hipLaunchKernelGGL((ibwd_dk_kernel<H_I, D_I>), dim3(gd), dim3(256), 0, st, g.Tq, g.K, q_idx,
+    // four waves of 256 entries per workgroup
+    const uint32_t gd = static_cast<uint32_t>(std::min<int64_t>((nent + 1023) / 1024, 8192));
+    hipLaunchKernelGGL((ibwd_dk_kernel<H_I, D_I>), dim3(gd), dim3(256), 0, st, g.Tq, g.K, qt,
                        w, wsb, wsq, ents, ekey, g_ent, m_ent, acc, off + keys);
     hipLaunchKernelGGL(ibwd_dk_out_kernel, dim3(ga), dim3(256), 0, st, acc, dk, nacc);
   }
