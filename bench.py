@@ -354,20 +354,64 @@ def probe_peaks():
         del a8, b8
     except (RuntimeError, AttributeError):
         out["int8_gemm_tops"] = None
+    out.update(gather_probes(timed))
     torch.cuda.empty_cache()
-    out["note"] = ("reachable rates measured here (copy kernel, library GEMMs); rooflines "
-                   "give frac against the vendor peak and frac_probe against these")
+    out["note"] = ("reachable rates measured here (copy kernel, library GEMMs, random-row "
+                   "gathers); rooflines give frac against the vendor peak and frac_probe "
+                   "against these (the gather kernel against the faster gather probe)")
     return out
+
+
+def gather_probes(timed):
+    """Random-row gather rate from a 128 MiB table (the key/value cache of the
+    Prefill-64K workload: 65536 positions x 4 heads x 128 x bf16, keys and
+    values), rows of 256 B (one head's key row) and 1 KiB (a position's four
+    heads), by the measurement kernel in bench_probe.hip: 4 GiB gathered per
+    launch from seeded uniform row numbers. None where the probe is not built."""
+    import ctypes
+    import torch
+
+    path = os.path.join(ROOT, "bench_probe.so")
+    if not os.path.exists(path):
+        return {"gather_128mib_256b_gbs": None, "gather_128mib_1kib_gbs": None}
+    fn = ctypes.CDLL(path).bench_gather_probe
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    table_bytes = 128 << 20
+    table = torch.ones(table_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    res = {}
+    for rb, key in ((256, "gather_128mib_256b_gbs"), (1024, "gather_128mib_1kib_gbs")):
+        n = (4 << 30) // rb
+        idx = torch.randint(0, table_bytes // rb, (n,), generator=gen, dtype=torch.int32,
+                            device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def go():
+            rc = fn(table.data_ptr(), rb, idx.data_ptr(), n, sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"bench_gather_probe failed with HIP error {rc}")
+
+        res[key] = round(n * rb / timed(go, 5) / 1e9, 1)
+        del idx
+    return res
 
 
 def add_probe_fracs(node, probes):
     """frac_probe beside frac in every roofline dict under node (in place)."""
     hbm = max(probes.get("hbm_copy_gbs") or 0.0, probes.get("hbm_read_gbs") or 0.0) or None
+    gather = max(probes.get("gather_128mib_256b_gbs") or 0.0,
+                 probes.get("gather_128mib_1kib_gbs") or 0.0) or None
     ref = {"GB/s": hbm, "TFLOP/s": probes.get("bf16_gemm_tflops"),
            "TOP/s": probes.get("int8_gemm_tops")}
     if isinstance(node, dict):
         if "frac" in node and "achieved" in node and node.get("unit") in ref:
             pk = ref[node["unit"]]
+            if node.get("kernel") == "attn_gather" and gather:
+                pk = gather
             node["frac_probe"] = round(node["achieved"] / pk, 4) if pk and node["achieved"] else None
         for v in node.values():
             add_probe_fracs(v, probes)
@@ -799,7 +843,9 @@ def main():
             line[name] = res[name]
     probes = probe_peaks()
     log(f"probe peaks: HBM copy {probes['hbm_copy_gbs']} GB/s, read {probes['hbm_read_gbs']} GB/s, bf16 GEMM "
-        f"{probes['bf16_gemm_tflops']} TFLOP/s, int8 GEMM {probes['int8_gemm_tops']} TOP/s")
+        f"{probes['bf16_gemm_tflops']} TFLOP/s, int8 GEMM {probes['int8_gemm_tops']} TOP/s, gather from "
+        f"128 MiB {probes['gather_128mib_256b_gbs']} GB/s (256 B rows), "
+        f"{probes['gather_128mib_1kib_gbs']} GB/s (1 KiB rows)")
     line["probe_peaks"] = probes
     add_probe_fracs(line, probes)
     print(json.dumps(line), flush=True)

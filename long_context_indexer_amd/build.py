@@ -58,6 +58,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile bench.py's measurement kernel (bench_probe.hip) into bench_probe.so."""
+    tmp = PROBE_LIB + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, "-shared", "-Wl,--no-undefined", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
     sys.exit(0)

@@ -26,7 +26,10 @@
 //                    barrier per tile), then
 //                      S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (lane l owns
 //                            query row l%32, keys 8i+4*(l/32)+j of each 32-key half),
-//                      mask + online softmax in base 2 (max on raw scores,
+//                      the row's selection applied by the accumulators'
+//                            start values (0 for a kept key, -FLT_MAX for a
+//                            dropped one, four keys per LDS table entry),
+//                      online softmax in base 2 (max on raw scores,
 //                            the scale folded into one FMA per exponent, the
 //                            offset moved only when a row's max grows by 2^8),
 //                            all lane-local except one exchange with lane l^32,
@@ -124,6 +127,12 @@ __device__ __forceinline__ float sum_xor32(float v) {
 // is skipped for the whole wave unless some row needs it.
 constexpr float kRescaleLog2 = 8.0f;
 
+// A dropped key's score starts from -FLT_MAX: adding the QK products of finite
+// bf16 rows leaves it at or below -2^127, under any kept score, and its
+// exponential underflows to 0. A tile whose maximum is that low kept nothing.
+constexpr uint32_t kDroppedBits = 0xff7fffffu;
+constexpr float kDroppedMax = -0x1p127f;
+
 // EXACT_L: the softmax denominator sums the fp32 probabilities (needed for the
 // log-sum-exp output). Otherwise it sums the bf16-rounded ones that enter the
 // PV product, two per dot-product instruction.
@@ -143,6 +152,18 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   // two K and two V tile buffers (see the pipeline below)
   __shared__ __align__(16) uint16_t ks[2][C::BK * C::KP];
   __shared__ __align__(16) uint16_t vsh[2][C::BK * C::KP];
+  uint16_t* const ks0 = ks[0];
+  uint16_t* const ks1 = ks[1];
+  uint16_t* const vs0 = vsh[0];
+  uint16_t* const vs1 = vsh[1];
+  // score accumulator start values of four consecutive keys under a 4-bit
+  // selection nibble: 0 where the bit keeps the key, the most negative finite
+  // float where it drops it (the QK products then leave it far below any score)
+  __shared__ __align__(16) uint32_t mlut[16][4];
+  if (threadIdx.x < 64) {
+    const int nib = threadIdx.x >> 2, bit = threadIdx.x & 3;
+    mlut[nib][bit] = ((nib >> bit) & 1) ? 0u : kDroppedBits;
+  }
 
   // XCD-aware placement: XCD x = blockIdx.x % 8 serves key/value head x / (8/Hkv)
   const int per = 8 / Hkv;
@@ -195,11 +216,6 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   const int64_t srow = (static_cast<int64_t>(b) * sets + h / hps) * Tq;  // row 0 of h's set
   const int fl = rv ? flag[srow + i] : 0;
   const uint32_t* mrow = mask + (srow + (rv ? i : 0)) * Wm;
-  // every row of this wave keeps all of 0..p (flag 2): tiles entirely at or
-  // below the wave's first position need no mask at all
-  const int iw0 = i0 + wv * C::TW;
-  const int p_wave_min = qo + iw0;
-  const bool wave_all = __all(!rv || fl == kRowAll) && iw0 < Tq;
 
   // Q^T as the B operand: lane holds Q[row][16*kk + 8*hf .. +7]
   v8bf qf[C::NKK];
@@ -249,13 +265,20 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
       load16_to_lds(rs, (LDS_AS uint16_t*)dst + (4 * c + wv) * 512, voff[c]);
   };
 
-  // S^T of one 64-key tile (two 32-key halves) from the K tile in LDS
-  auto tile_scores = [&](const uint16_t* kt_lds, v16f* st) {
+  // S^T of one 64-key tile (two 32-key halves) from the K tile in LDS, the
+  // selection applied by the accumulator's start values: element e of half kt
+  // (key 32kt + 8(e/4) + 4hf + e%4) starts from the LUT entry of its nibble
+  auto tile_scores = [&](const uint16_t* kt_lds, const uint32_t* mw2, v16f* st) {
     const LDS_AS uint16_t* ksl = (const LDS_AS uint16_t*)kt_lds;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      const uint32_t mw = mw2[kt] >> (4 * hf);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
+      for (int jn = 0; jn < 4; ++jn) {
+        const v4i z = *(const LDS_AS v4i*)(&mlut[(mw >> (8 * jn)) & 15u][0]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) st[kt][4 * jn + c] = __int_as_float(z[c]);
+      }
       const int krow = 32 * kt + r;
 #pragma unroll
       for (int kk = 0; kk < C::NKK; ++kk) {
@@ -266,15 +289,16 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     }
   };
 
-  // selection words of the next tile, loaded one tile ahead (rows not on the
-  // mask path read a valid but unused word)
+  // selection words of a tile, loaded two tiles ahead of its softmax, so they
+  // are in registers (the step's barrier waited for them) when its scores are
+  // computed. Rows hold an even number of words, two per 64-key tile up to the
+  // row limit, so every tile of the block has its words; the index is clamped
+  // only for the tiles past the last, whose scores are never used (rows not on
+  // the mask path read a valid but unused word too).
   const int wlast = Wm - 1;
   auto mask_words = [&](int kb, uint32_t* w) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const uint32_t x = mrow[min(2 * kb + kt, wlast)];
-      w[kt] = 2 * kb + kt <= wlast ? x : 0u;  // past the mask row: nothing kept
-    }
+    for (int kt = 0; kt < 2; ++kt) w[kt] = mrow[min(2 * kb + kt, wlast)];
   };
 
   float m = -INFINITY;  // softmax offset of this row, raw score units (a running max)
@@ -288,49 +312,41 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
   // pipeline: while tile kb is in softmax, the scores of tile kb+1 are computed
   // (their K is already in LDS) and V of kb+1 and K of kb+2 are in flight
   if (nkb > 0) {
-    load_tile(kbase, 0, ks[0]);
-    load_tile(vbase, 0, vsh[0]);
+    load_tile(kbase, 0, ks0);
+    load_tile(vbase, 0, vs0);
   }
-  if (nkb > 1) load_tile(kbase, 1, ks[1]);
-  uint32_t mwc[2];
-  mask_words(0, mwc);
+  if (nkb > 1) load_tile(kbase, 1, ks1);
+  uint32_t mw0[2], mwn[2];  // words of tiles 0 and (the next tile) 1
+  mask_words(0, mw0);
+  mask_words(1, mwn);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // every load done (see the step's end)
   __syncthreads();
   v16f sc[2];
-  tile_scores(ks[0], sc);
+  tile_scores(ks0, mw0, sc);
   __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
 
   // one step per tile; the steps of even and odd tiles are separate copies
   // so each has its buffer addresses as constants
   auto tile_step = [&](int kb, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
-    if (kb + 1 < nkb) load_tile(vbase, kb + 1, vsh[buf ^ 1]);
-    if (kb + 2 < nkb) load_tile(kbase, kb + 2, ks[buf]);
-    uint32_t mwn[2];
-    mask_words(kb + 1, mwn);
+    uint16_t* const kcur = buf ? ks1 : ks0;  // K of tile kb (scored), refilled with kb+2
+    uint16_t* const knxt = buf ? ks0 : ks1;  // K of tile kb+1
+    uint16_t* const vcur = buf ? vs1 : vs0;  // V of tile kb
+    uint16_t* const vnxt = buf ? vs0 : vs1;  // filled with V of tile kb+1
+    if (kb + 1 < nkb) load_tile(vbase, kb + 1, vnxt);
+    if (kb + 2 < nkb) load_tile(kbase, kb + 2, kcur);
+    uint32_t mwa[2];  // words of tile kb + 2
+    mask_words(kb + 2, mwa);
 
-    // mask: the row's selection bits (all of 0..p for rows that keep everything)
-    const int key0 = kb * C::BK;
-    if (!(wave_all && key0 + C::BK - 1 <= p_wave_min)) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        // bit kofs(e) = 8(e/4) + 4hf + e%4 of the word keeps element e: a
-        // one-bit signed extract gives an all-ones/all-zeros select mask
-        const uint32_t mw = mwc[kt] >> (4 * hf);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int sel = __builtin_amdgcn_sbfe(static_cast<int>(mw), 8 * (e >> 2) + (e & 3), 1);
-          const int sb = __float_as_int(sc[kt][e]);
-          sc[kt][e] = __int_as_float((sb & sel) | (~sel & kNegInfBits));
-        }
-      }
-    }
-    // scores are finite or -inf: IEEE maximum (no NaN quieting) folds into v_maximum3
+    // scores are finite (dropped keys near -FLT_MAX): IEEE maximum (no NaN
+    // quieting) folds into v_maximum3
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) mx = max3f(mx, sc[kt][e], sc[kt][e + 1]);
     mx = max_xor32(mx);
+    if (mx < kDroppedMax) mx = -INFINITY;  // no key of this tile kept
     // lazy offset update: only rows whose max grew by kRescaleLog2 or more move
     // their offset (all rows start at -inf, so every row moves on its first
     // kept score); the rescale of O and l runs only if some row of the wave moved
@@ -351,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     // scores of the next tile (independent MFMA work beside the exponentials;
     // past the last tile the result is unused)
     v16f sn[2];
-    tile_scores(ks[buf ^ 1], sn);
+    tile_scores(knxt, mwn, sn);
 
     // P^T as the B operand of the PV step s: e<4 -> half-row i=2(s%2), e>=4 -> i=2(s%2)+1
     v8bf pb[4];
@@ -380,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     lsum += psum;
 
     // O^T += V^T P^T over the 64 keys, four 16-key steps
-    const LDS_AS uint16_t* vsl = (const LDS_AS uint16_t*)(vsh[buf]);
+    const LDS_AS uint16_t* vsl = (const LDS_AS uint16_t*)(vcur);
     const int gi = lane & 15;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
@@ -398,11 +414,14 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
     }
     sc[0] = sn[0];
     sc[1] = sn[1];
-    mwc[0] = mwn[0];
-    mwc[1] = mwn[1];
+    mwn[0] = mwa[0];
+    mwn[1] = mwa[1];
     // the barrier waits for this step's tile loads (vmcnt) and makes them
     // visible; it also guarantees every wave is done with the buffers the
-    // next step's loads overwrite
+    // next step's loads overwrite. The selection words loaded this step are
+    // waited for here too (vmcnt 0, other counters untouched): waiting for
+    // them later, behind the next step's tile loads, would wait for those.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   };
   for (int kb = 0; kb < nkb; kb += 2) {
@@ -477,7 +496,8 @@ int dense_row_limit(const Geom& g) {
   return static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
 }
 
-int dense_mask_words(const Geom& g) { return (dense_row_limit(g) + 31) / 32; }
+// two words per 64-key tile: the tile kernel reads a tile's words as a pair
+int dense_mask_words(const Geom& g) { return 2 * ((dense_row_limit(g) + 63) / 64); }
 
 // [mask: rows x Wm words][flag: rows bytes][done: one byte per token block
 // (at most one block per row)], each part 256-byte aligned; rows = B x sets x Tq

@@ -233,7 +233,9 @@ __global__ __launch_bounds__(BT_NT) void block_topk_kernel(
   for (int w = t; w < Wm; w += BT_NT) {
     const int p0 = 32 * w;
     uint32_t word = 0u;
-    if (lb >= 5) {
+    if (p0 >= n) {
+      // past the row's history (the row's trailing words): nothing kept
+    } else if (lb >= 5) {
       const int j = p0 >> lb;  // one block covers the word
       if (j < nb && ((kept[j >> 5] >> (j & 31)) & 1u)) word = 0xffffffffu;
     } else {
