@@ -76,8 +76,8 @@ def open_library(path: str):
     lib.orc_kv_append.argtypes = [i32, i32, i32, i64, P, P, P, P, P, P]
     lib.orc_attn_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                  f64, P, P, P, P, P]
-    lib.orc_indexer_bwd.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, i64, i64, P, P,
-                                    f64, P, P, P, P]
+    lib.orc_indexer_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, i64, i64, P,
+                                    P, f64, P, P, P, P]
     lib.orc_num_threads.restype = i32
     return lib
 
@@ -271,24 +271,30 @@ class Oracle:
         """Gradients of the indexer's distillation loss over index rows idx int32
         [B,Tq,K] with the teacher's weights teacher [B,Tq,K] (float) and score
         scale tau. Returns dict(loss [B,Tq], dq [B,Tq,H_I,d_I], dk [B,Tk,d_I],
-        dw [B,Tq,H_I]) in float64 (dw per row; sum over rows for shared weights)."""
+        dw [B,Tq,H_I]) in float64 (dw per row; sum over rows for shared weights).
+        With index sets, idx and teacher are [B,S,Tq,K] (S dividing H_I; set g
+        scored by indexer heads g*H_I/S .. (g+1)*H_I/S - 1) and loss [B,S,Tq]."""
         q_idx = _c(q_idx, np.int8)
         k_idx = _c(k_idx, np.int8)
         B, Tq, H_I, d_I = q_idx.shape
         Tk = k_idx.shape[1]
         w = _c(w, np.int8)
         wsb, wsq = _w_strides(w, B, Tq, H_I)
-        idx = _c(idx, np.int32).reshape(B, Tq, -1)
-        K = idx.shape[2]
-        T = _c(teacher, np.float64).reshape(B, Tq, K)
-        loss = np.empty((B, Tq), np.float64)
+        idx = _c(idx, np.int32)
+        sets = idx.shape[1] if idx.ndim == 4 else 1
+        if H_I % sets:
+            raise ValueError("sets must divide H_I")
+        idx = idx.reshape(B, sets, Tq, -1)
+        K = idx.shape[3]
+        T = _c(teacher, np.float64).reshape(B, sets, Tq, K)
+        loss = np.empty((B, sets, Tq), np.float64)
         dq = np.empty((B, Tq, H_I, d_I), np.float64)
         dk = np.empty((B, Tk, d_I), np.float64)
         dw = np.empty((B, Tq, H_I), np.float64)
-        self.lib.orc_indexer_bwd(B, Tq, Tk, H_I, d_I, K, _p(_c(q_offset, np.int32)),
+        self.lib.orc_indexer_bwd(B, Tq, Tk, H_I, d_I, K, sets, _p(_c(q_offset, np.int32)),
                                  _p(_c(kv_len, np.int32)), _p(q_idx), _p(k_idx), _p(w), wsb, wsq,
                                  _p(idx), _p(T), float(tau), _p(loss), _p(dq), _p(dk), _p(dw))
-        return dict(loss=loss, dq=dq, dk=dk, dw=dw)
+        return dict(loss=loss if sets > 1 else loss[:, 0], dq=dq, dk=dk, dw=dw)
 
     def layer(self, inp, K, rows=None, gated=True, block=1, sets=1):
         """The whole layer (score -> Top-K -> attention -> gate) for the listed rows

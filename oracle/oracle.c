@@ -557,33 +557,42 @@ void orc_attn_bwd(int B, int Tq, int Tk, int Hq, int Hkv, int d, int K, int sets
  *   dw[i,h] = sum_t g_t max(0, d_ht),
  *   dq[i,h,:] = w_h sum_t g_t [d_ht > 0] kI[idx_t],
  *   dk[idx_t,:] += g_t sum_h w_h [d_ht > 0] qI[i,h]   (over every row and entry).
+ * With sets > 1 index sets (a divisor of H_I; the reading of the forward's
+ * per-head sets carried over) set g is the scorer of indexer heads
+ * g*H_I/sets .. (g+1)*H_I/sets - 1 (their weights included) over its own index
+ * rows and teacher: each set's loss is the one above with H_I/sets heads, dq
+ * and dw of a head come from its set alone, and dk sums over every set.
  * q_idx [B][Tq][H_I][d_I], k_idx [B][Tk][d_I], w at b*w_stride_b + i*w_stride_q
- * (+h), idx and T [B][Tq][K]. Outputs (fp64, overwritten): loss [B][Tq] (NULL
- * allowed), dq [B][Tq][H_I][d_I], dk [B][Tk][d_I], dw [B][Tq][H_I]. Invalid rows
- * (p outside 0..kv_len-1, or kv_len > Tk) and rows without a valid entry give
- * zeros. */
-void orc_indexer_bwd(int B, int Tq, int Tk, int H_I, int d_I, int K, const int32_t *q_offset,
-                     const int32_t *kv_len, const int8_t *q_idx, const int8_t *k_idx,
-                     const int8_t *w, int64_t w_stride_b, int64_t w_stride_q, const int32_t *idx,
-                     const double *T, double tau, double *loss, double *dq, double *dk,
-                     double *dw)
+ * (+h), idx and T [B][sets][Tq][K]. Outputs (fp64, overwritten): loss
+ * [B][sets][Tq] (NULL allowed), dq [B][Tq][H_I][d_I], dk [B][Tk][d_I], dw
+ * [B][Tq][H_I]. Invalid rows (p outside 0..kv_len-1, or kv_len > Tk) and rows
+ * without a valid entry give zeros. */
+void orc_indexer_bwd(int B, int Tq, int Tk, int H_I, int d_I, int K, int sets,
+                     const int32_t *q_offset, const int32_t *kv_len, const int8_t *q_idx,
+                     const int8_t *k_idx, const int8_t *w, int64_t w_stride_b,
+                     int64_t w_stride_q, const int32_t *idx, const double *T, double tau,
+                     double *loss, double *dq, double *dk, double *dw)
 {
+    int ns = sets > 1 ? sets : 1;
+    int Hs = H_I / ns;  /* indexer heads of one set */
     memset(dk, 0, (size_t)B * Tk * d_I * sizeof(double));
     double *z = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
     int64_t *dd = (int64_t *)malloc((size_t)(K > 0 ? K : 1) * H_I * sizeof(int64_t));
     for (int b = 0; b < B; ++b) {
+        for (int gs = 0; gs < ns; ++gs)
         for (int i = 0; i < Tq; ++i) {
             int64_t row = (int64_t)b * Tq + i;
+            int64_t srow = ((int64_t)b * ns + gs) * Tq + i;  /* the set's index row */
             int64_t p = (int64_t)q_offset[b] + i;
-            const int8_t *qI = q_idx + row * H_I * d_I;
-            const int8_t *wr = w + b * w_stride_b + (int64_t)i * w_stride_q;
-            const int32_t *ir = idx + row * K;
-            const double *Tr = T + row * K;
-            double *dqr = dq + row * H_I * d_I;
-            double *dwr = dw + row * H_I;
-            for (int j = 0; j < H_I * d_I; ++j) dqr[j] = 0.0;
-            for (int h = 0; h < H_I; ++h) dwr[h] = 0.0;
-            if (loss) loss[row] = 0.0;
+            const int8_t *qI = q_idx + (row * H_I + (int64_t)gs * Hs) * d_I;
+            const int8_t *wr = w + b * w_stride_b + (int64_t)i * w_stride_q + gs * Hs;
+            const int32_t *ir = idx + srow * K;
+            const double *Tr = T + srow * K;
+            double *dqr = dq + (row * H_I + (int64_t)gs * Hs) * d_I;
+            double *dwr = dw + row * H_I + gs * Hs;
+            for (int j = 0; j < Hs * d_I; ++j) dqr[j] = 0.0;
+            for (int h = 0; h < Hs; ++h) dwr[h] = 0.0;
+            if (loss) loss[srow] = 0.0;
             int valid_row = p >= 0 && p < kv_len[b] && kv_len[b] <= Tk;
             if (!valid_row) continue;
             /* scores of the entries (exact, int64) and the softmax of tau*S */
@@ -592,11 +601,11 @@ void orc_indexer_bwd(int B, int Tq, int Tk, int H_I, int d_I, int K, const int32
                 int64_t s = ir[t];
                 if (s < 0 || s > p) { z[t] = -INFINITY; continue; }
                 int64_t S = 0;
-                for (int h = 0; h < H_I; ++h) {
+                for (int h = 0; h < Hs; ++h) {
                     int64_t d = 0;
                     for (int j = 0; j < d_I; ++j)
                         d += (int64_t)qI[h * d_I + j] * (int64_t)k_idx[((int64_t)b * Tk + s) * d_I + j];
-                    dd[(int64_t)t * H_I + h] = d;
+                    dd[(int64_t)t * Hs + h] = d;
                     S += (int64_t)wr[h] * (d > 0 ? d : 0);
                 }
                 z[t] = tau * (double)S;
@@ -620,8 +629,8 @@ void orc_indexer_bwd(int B, int Tq, int Tk, int H_I, int d_I, int K, const int32
                 int64_t s = ir[t];
                 const int8_t *kr = k_idx + ((int64_t)b * Tk + s) * d_I;
                 double *dkr = dk + ((int64_t)b * Tk + s) * d_I;
-                for (int h = 0; h < H_I; ++h) {
-                    int64_t d = dd[(int64_t)t * H_I + h];
+                for (int h = 0; h < Hs; ++h) {
+                    int64_t d = dd[(int64_t)t * Hs + h];
                     dwr[h] += g * (double)(d > 0 ? d : 0);
                     if (d <= 0) continue;
                     for (int j = 0; j < d_I; ++j) {
@@ -630,7 +639,7 @@ void orc_indexer_bwd(int B, int Tq, int Tk, int H_I, int d_I, int K, const int32
                     }
                 }
             }
-            if (loss) loss[row] = L;
+            if (loss) loss[srow] = L;
         }
     }
     free(dd);

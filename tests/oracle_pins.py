@@ -1073,4 +1073,71 @@ def pin_indexer_bwd_closed_forms(orc):
         assert np.abs(shared[name] - per_row[name]).max() < 1e-12, name
 
 
+def _ibwd_sets_problem(seed):
+    r = np.random.default_rng(seed)
+    B, Tq, Tk, H_I, d_I, K, S = 2, 5, 36, 6, 8, 6, 3
+    q = r.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.int8)
+    k = r.integers(-8, 9, size=(B, Tk, d_I)).astype(np.int8)
+    w = r.integers(-3, 5, size=(B, Tq, H_I)).astype(np.int8)
+    q_offset = np.array([30, 2], np.int32)
+    kv_len = np.array([36, 6], np.int32)                # sequence 1: rows 4 invalid
+    idx = np.stack([np.stack([np.stack([r.choice(Tk, K, replace=False) for _ in range(Tq)])
+                              for _ in range(S)]) for _ in range(B)]).astype(np.int32)
+    idx[0, 1, 2, 3:] = -1
+    idx[1, 2, 0, :] = 35                                # past the row's position: none valid
+    T = r.random((B, S, Tq, K))
+    T /= T.sum(-1, keepdims=True)
+    return q, k, w, q_offset, kv_len, idx, T, S
+
+
+def pin_indexer_bwd_sets_autograd(orc):
+    """With three index sets of two indexer heads each, the oracle's loss per
+    set and its gradients equal torch autograd (fp64) of the sum of the sets'
+    losses, each stated independently on its heads, weights, index rows and
+    teacher (dk summed over the sets)."""
+    import torch
+    q, k, w, q_offset, kv_len, idx, T, S = _ibwd_sets_problem(82)
+    Hs = q.shape[2] // S
+    tau = 0.015
+    tq = torch.tensor(q.astype(np.float64), requires_grad=True)
+    tk = torch.tensor(k.astype(np.float64), requires_grad=True)
+    tw = torch.tensor(w.astype(np.float64), requires_grad=True)
+    total = torch.zeros((), dtype=torch.float64)
+    losses = []
+    for g in range(S):
+        hs = slice(g * Hs, (g + 1) * Hs)
+        t, l = _torch_indexer_loss(tq[:, :, hs], tk, tw[:, :, hs], idx[:, g], T[:, g], q_offset,
+                                   kv_len, tau)
+        total = total + t
+        losses.append(l.numpy())
+    total.backward()
+    res = orc.indexer_bwd(q, k, w, q_offset, kv_len, idx, T, tau)
+    assert res["loss"].shape == (q.shape[0], S, q.shape[1])
+    assert np.abs(res["loss"] - np.stack(losses, axis=1)).max() < 1e-10
+    for name, leaf in (("dq", tq), ("dk", tk), ("dw", tw)):
+        want = leaf.grad.numpy()
+        assert np.abs(res[name] - want).max() <= 1e-10 * max(1.0, np.abs(want).max()), name
+
+
+def pin_indexer_bwd_sets_sub_problems(orc):
+    """Each index set's gradients are those of its own one-set problem (its
+    heads' slice of q_idx and w, its index rows and teacher): dq and dw of the
+    set's heads equal that problem's, and dk is the sum of the problems' dk."""
+    q, k, w, q_offset, kv_len, idx, T, S = _ibwd_sets_problem(83)
+    Hs = q.shape[2] // S
+    tau = 0.02
+    res = orc.indexer_bwd(q, k, w, q_offset, kv_len, idx, T, tau)
+    dk = np.zeros_like(res["dk"])
+    for g in range(S):
+        hs = slice(g * Hs, (g + 1) * Hs)
+        one = orc.indexer_bwd(np.ascontiguousarray(q[:, :, hs]), k, np.ascontiguousarray(w[:, :, hs]),
+                              q_offset, kv_len, np.ascontiguousarray(idx[:, g]),
+                              np.ascontiguousarray(T[:, g]), tau)
+        assert np.array_equal(res["loss"][:, g], one["loss"])
+        assert np.array_equal(res["dq"][:, :, hs], one["dq"])
+        assert np.array_equal(res["dw"][:, :, hs], one["dw"])
+        dk += one["dk"]
+    assert np.abs(res["dk"] - dk).max() <= 1e-12 * max(1.0, np.abs(dk).max())
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -74,6 +74,11 @@ MUTANTS = [
     ("history_clamped_to_allocation", "kv_len[b] <= Tk ? kv_len[b] : 0", "kv_len[b] < Tk ? kv_len[b] : Tk"),
     ("ibwd_relu_mask_dropped", "                    if (d <= 0) continue;\n", ""),
     ("ibwd_no_tau", "double g = tau * (pt * Tsum - Tr[t]);", "double g = (pt * Tsum - Tr[t]);"),
+    ("ibwd_sets_heads_of_group0", "const int8_t *qI = q_idx + (row * H_I + (int64_t)gs * Hs) * d_I;",
+     "const int8_t *qI = q_idx + row * H_I * d_I;"),
+    ("ibwd_sets_weights_of_group0", "(int64_t)i * w_stride_q + gs * Hs;", "(int64_t)i * w_stride_q;"),
+    ("ibwd_sets_rows_of_set0", "int64_t srow = ((int64_t)b * ns + gs) * Tq + i;",
+     "int64_t srow = (int64_t)b * ns * Tq + i;"),
     ("ibwd_sign", "double g = tau * (pt * Tsum - Tr[t]);", "double g = tau * (Tr[t] - pt * Tsum);"),
     ("ibwd_teacher_mass_ignored", "double g = tau * (pt * Tsum - Tr[t]);", "double g = tau * (pt - Tr[t]);"),
     ("ibwd_dk_without_weight", "dkr[j] += g * (double)wr[h] * (double)qI[h * d_I + j];",
