@@ -188,9 +188,8 @@ lci_status lci_sparse_attn_fwd(const lci_geom *g, const lci_bf16 *q, const lci_b
  * divide H_I, else SHAPE); set j is scored by group j alone, with its heads'
  * weights, and selected like a shared set. Index rows are then int32 [B, S,
  * Tq, K*max(1, block)] (idx_out of the fused entries, idx of
- * lci_sparse_attn_fwd, lci_sparse_attn_bwd); lci_idx_score and lci_topk_select
- * take the same set axis. lci_indexer_bwd works on one set (S > 1:
- * UNSUPPORTED). */
+ * lci_sparse_attn_fwd, lci_sparse_attn_bwd); lci_idx_score, lci_topk_select and
+ * lci_indexer_bwd take the same set axis. */
 
 /* Fused prefill: steps 1-4 for many query rows per sequence in one call
  * ("Hybrid Sparse Attention ...", section "Engineering and Evaluation
@@ -322,15 +321,18 @@ lci_status lci_sparse_attn_bwd(const lci_geom *g, const lci_bf16 *q, const lci_b
  * ReLU's derivative 0 at 0, g_t = tau (p_t sum_u T_u - T_t) and
  *   dw[i,h] = sum_t g_t max(0, d_ht),  dq[i,h,:] = w_h sum_t g_t [d_ht > 0] k_idx[idx_t],
  *   dk[s,:] = sum over entries with idx_t = s of g_t sum_h w_h [d_ht > 0] q_idx[i,h],
- * d_ht = q_idx[i,h] . k_idx[idx_t].
- *   q_idx, k_idx, w, strides: as in lci_idx_score (one index set: g->sets > 1 is
- *            UNSUPPORTED)
- *   idx      int32 [B, Tq, K*max(1, block)]: the entries (the index rows of the
- *            forward, or any positions)
- *   teacher  fp32 [B, Tq, K*max(1, block)]: the teacher's weights, >= 0, aligned
- *            with idx (they need not sum to 1)
+ * d_ht = q_idx[i,h] . k_idx[idx_t]. With S = g->sets > 1 index sets (S divides
+ * H_I, else SHAPE), set j is the scorer of indexer heads j*H_I/S ..
+ * (j+1)*H_I/S - 1 (their weights included) over its own index rows and teacher:
+ * each set has the loss above on its heads, dq and dw of a head come from its
+ * set, and dk sums over the sets.
+ *   q_idx, k_idx, w, strides: as in lci_idx_score
+ *   idx      int32 [B, S, Tq, K*max(1, block)] (S = 1 without sets): the entries
+ *            (the index rows of the forward, or any positions)
+ *   teacher  fp32 [B, S, Tq, K*max(1, block)]: the teacher's weights, >= 0,
+ *            aligned with idx (they need not sum to 1)
  *   tau      the score scale of the scorer's softmax (finite, else SHAPE)
- *   loss     fp32 [B, Tq] out, nullable
+ *   loss     fp32 [B, S, Tq] out, nullable
  *   dq_idx   fp32 [B, Tq, H_I, d_I] out;  dk_idx fp32 [B, Tk, d_I] out (0 where no
  *            entry points); dw fp32 [B, Tq, H_I] out (per row: for weights shared
  *            by every row, their gradient is the sum over rows)
@@ -339,7 +341,9 @@ lci_status lci_sparse_attn_bwd(const lci_geom *g, const lci_bf16 *q, const lci_b
  *            the query rows with each feature's heads side by side. dk
  *            sums its products as 64-bit integers with 32 fraction bits (the
  *            sum does not depend on the order: deterministic); each element's
- *            sum must stay below 2^31 in size. B*Tq*K < 2^31 (SHAPE).
+ *            sum must stay below 2^31 in size. B*Tq*K < 2^31 (SHAPE). The sets
+ *            run one after another and share the workspace (its size does
+ *            not grow with S).
  * Invalid rows and rows without a valid entry give zeros. Floating-point work is
  * fp32 (the scores themselves are exact).
  * Errors: NULL, SHAPE, UNSUPPORTED, OVERFLOW_RISK, WORKSPACE, ALIGN, HIP. */

@@ -392,23 +392,32 @@ def indexer_bwd(q_idx, k_idx, w, idx, teacher, tau, q_offset, kv_len, loss=True,
                 stream=None):
     """Gradients of the scorer's distillation loss over index rows idx int32
     [B,Tq,K] with the teacher's weights teacher fp32 [B,Tq,K] and score scale tau.
+    With index sets, idx and teacher are [B,S,Tq,K] (S dividing H_I; set j is
+    scored by indexer heads j*H_I/S .. (j+1)*H_I/S - 1) and loss [B,S,Tq].
     Returns dict(loss [B,Tq] or None, dq [B,Tq,H_I,d_I], dk [B,Tk,d_I], dw [B,Tq,H_I])."""
     import torch
     _dev(q_idx, torch.int8, "q_idx", 4)
     _dev(k_idx, torch.int8, "k_idx", 3)
     _dev(w, torch.int8, "w")
-    _dev(idx, torch.int32, "idx", 3)
-    _dev(teacher, torch.float32, "teacher", 3)
+    _dev(idx, torch.int32, "idx")
+    _dev(teacher, torch.float32, "teacher")
     B, Tq, H_I, d_I = q_idx.shape
     Tk = k_idx.shape[1]
-    K = idx.shape[2]
-    if tuple(idx.shape[:2]) != (B, Tq) or tuple(teacher.shape) != tuple(idx.shape) or \
-            tuple(k_idx.shape) != (B, Tk, d_I):
+    if idx.dim() not in (3, 4):
+        raise ValueError("idx must be [B,Tq,K] or [B,S,Tq,K]")
+    sets = idx.shape[1] if idx.dim() == 4 else 1
+    K = idx.shape[-1]
+    want = (B, sets, Tq, K) if idx.dim() == 4 else (B, Tq, K)
+    if tuple(idx.shape) != want or tuple(teacher.shape) != want or \
+            tuple(k_idx.shape) != (B, Tk, d_I) or H_I % sets:
         raise ValueError("inconsistent shapes")
     wsb, wsq = _w_strides(w, B, Tq, H_I)
-    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, H_I=H_I, d_I=d_I)
+    g = make_geom(B, Tq, Tk, K, q_offset, kv_len, H_I=H_I, d_I=d_I, sets=sets)
     dev = q_idx.device
-    out_loss = torch.empty((B, Tq), dtype=torch.float32, device=dev) if loss else None
+    out_loss = None
+    if loss:
+        out_loss = torch.empty((B, sets, Tq) if idx.dim() == 4 else (B, Tq), dtype=torch.float32,
+                               device=dev)
     dq = torch.empty((B, Tq, H_I, d_I), dtype=torch.float32, device=dev)
     dk = torch.empty((B, Tk, d_I), dtype=torch.float32, device=dev)
     dw = torch.empty((B, Tq, H_I), dtype=torch.float32, device=dev)

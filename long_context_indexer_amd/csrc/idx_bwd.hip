@@ -15,6 +15,11 @@
 //   dw[i,h]   = sum_t g_t max(0, d_ht),
 //   dq[i,h,:] = w_h sum_t g_t [d_ht > 0] kI[idx_t],
 //   dk[s,:]  += g_t sum_h w_h [d_ht > 0] qI[i,h]   for every entry with idx_t = s.
+// With index sets (per-head index rows, as in the runtime pseudocode of the
+// first page and the Indexer + Top-K pseudocode of the second), set g is the
+// scorer of its group of H_I/sets heads over its own index rows and teacher:
+// each set has the loss above on its heads, and dk sums over the sets. The sets
+// run one after another; their dk sums meet in one fixed-point accumulator.
 //
 //   ibwd_row_kernel    one workgroup per query row: the entries' scores from the
 //                      int8 rows (v_dot4 over d_I, exact), the softmax of tau*S
@@ -69,11 +74,14 @@ __device__ __forceinline__ float ib_block_max(float v, float* red) {
   return s;
 }
 
-// One workgroup per query row (blockIdx.x = b*Tq + i). Dynamic LDS: K floats of
-// g (z first), K 16-bit head masks (bit h: d_ht > 0; 0 for skipped entries).
+// One workgroup per query row (blockIdx.x = b*Tq + i) and one index set: H_I is
+// the set's heads, the first of them at q_idx, dq and dw (rows of q_heads
+// heads); the set's index row, teacher row and loss of (b, i) are row
+// b*brow + i of idx, teacher and loss. Dynamic LDS: K floats of g (z first),
+// K 16-bit head masks (bit h: d_ht > 0; 0 for skipped entries).
 template <int H_I, int D_I>
 __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
-    int Tq, int Tk, int K, const int32_t* __restrict__ q_offset,
+    int Tq, int Tk, int K, int q_heads, int64_t brow, const int32_t* __restrict__ q_offset,
     const int32_t* __restrict__ kv_len, const int8_t* __restrict__ q_idx,
     const int8_t* __restrict__ k_idx, const int8_t* __restrict__ w, int64_t wsb, int64_t wsq,
     const int32_t* __restrict__ idx, const float* __restrict__ teacher, float tau,
@@ -96,21 +104,22 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
   const int kvl0 = kv_len[b];
   const int64_t p = static_cast<int64_t>(q_offset[b]) + i;
   const bool rok = kvl0 <= Tk && p >= 0 && p < kvl0;
-  float* dqr = dq + row * H_I * D_I;
-  float* dwr = dw + row * H_I;
+  const int64_t irow = static_cast<int64_t>(b) * brow + i;  // the set's index row
+  float* dqr = dq + row * q_heads * D_I;
+  float* dwr = dw + row * q_heads;
   for (int j = t; j < H_I * D_I; j += IB_NT) dqr[j] = 0.f;
   if (t < H_I) dwr[t] = 0.f;
-  if (loss && t == 0) loss[row] = 0.f;
+  if (loss && t == 0) loss[irow] = 0.f;
   if (!rok) return;
-  const int* qsrc = reinterpret_cast<const int*>(q_idx + row * H_I * D_I);
+  const int* qsrc = reinterpret_cast<const int*>(q_idx + row * q_heads * D_I);
   for (int j = t; j < H_I * NW; j += IB_NT) qrow[j] = qsrc[j];
   int wh[H_I];
   const int8_t* wr = w + b * wsb + static_cast<int64_t>(i) * wsq;
 #pragma unroll
   for (int h = 0; h < H_I; ++h) wh[h] = static_cast<int>(wr[h]);
   __syncthreads();
-  const int32_t* ir = idx + row * K;
-  const float* Tr = teacher + row * K;
+  const int32_t* ir = idx + irow * K;
+  const float* Tr = teacher + irow * K;
   const int8_t* kb = k_idx + static_cast<int64_t>(b) * Tk * D_I;
 
   // the entry's head dot products, exact
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
     mr[e] = hmask[e];
   }
   const float L = ib_block_sum(lloc, red);
-  if (loss && t == 0) loss[row] = L;
+  if (loss && t == 0) loss[irow] = L;
   // dw: per-wave sums, then the waves in order
 #pragma unroll
   for (int h = 0; h < H_I; ++h) {
@@ -259,8 +268,9 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
   }
 }
 
-// counts of the valid entries per position (key b*Tk + s)
-__global__ __launch_bounds__(256) void ibwd_count_kernel(int Tq, int Tk, int K,
+// counts of the valid entries per position (key b*Tk + s); entry e = row*K + t
+// of the set is its index rows' entry (b*brow + i)*K + t
+__global__ __launch_bounds__(256) void ibwd_count_kernel(int Tq, int Tk, int K, int64_t brow,
                                                          const int32_t* __restrict__ q_offset,
                                                          const int32_t* __restrict__ kv_len,
                                                          const int32_t* __restrict__ idx,
@@ -268,15 +278,16 @@ __global__ __launch_bounds__(256) void ibwd_count_kernel(int Tq, int Tk, int K,
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < nent; e += gridDim.x * 256LL) {
     const int64_t row = e / K;
     const int b = static_cast<int>(row / Tq);
-    const int64_t p = static_cast<int64_t>(q_offset[b]) + (row - static_cast<int64_t>(b) * Tq);
+    const int64_t i = row - static_cast<int64_t>(b) * Tq;
+    const int64_t p = static_cast<int64_t>(q_offset[b]) + i;
     const int kvl = kv_len[b];
-    const int s = idx[e];
+    const int s = idx[(b * brow + i) * K + (e - row * K)];
     if (kvl <= Tk && p >= 0 && p < kvl && s >= 0 && s <= p)
       atomicAdd(&cnt[static_cast<int64_t>(b) * Tk + s], 1);
   }
 }
 
-__global__ __launch_bounds__(256) void ibwd_fill_kernel(int Tq, int Tk, int K,
+__global__ __launch_bounds__(256) void ibwd_fill_kernel(int Tq, int Tk, int K, int64_t brow,
                                                         const int32_t* __restrict__ q_offset,
                                                         const int32_t* __restrict__ kv_len,
                                                         const int32_t* __restrict__ idx,
@@ -288,9 +299,10 @@ __global__ __launch_bounds__(256) void ibwd_fill_kernel(int Tq, int Tk, int K,
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < nent; e += gridDim.x * 256LL) {
     const int64_t row = e / K;
     const int b = static_cast<int>(row / Tq);
-    const int64_t p = static_cast<int64_t>(q_offset[b]) + (row - static_cast<int64_t>(b) * Tq);
+    const int64_t i = row - static_cast<int64_t>(b) * Tq;
+    const int64_t p = static_cast<int64_t>(q_offset[b]) + i;
     const int kvl = kv_len[b];
-    const int s = idx[e];
+    const int s = idx[(b * brow + i) * K + (e - row * K)];
     if (kvl <= Tk && p >= 0 && p < kvl && s >= 0 && s <= p) {
       const int64_t key = static_cast<int64_t>(b) * Tk + s;
       const int slot = off[key] + atomicAdd(&cursor[key], 1);
@@ -310,17 +322,19 @@ __global__ __launch_bounds__(256) void ibwd_fill_kernel(int Tq, int Tk, int K,
 // end of the chunk, the sums go into the position's accumulator by integer
 // atomics. Integer sums do not depend on their order: deterministic.
 // Query rows with each feature's heads side by side: qT[row][j] holds
-// qI[row, h, j] for h = 0 .. H_I-1 as int8 in (H_I + 3) / 4 words (zero padded),
+// qI[row, h, j] for the set's heads h = 0 .. H_I-1 (the first at q_idx, rows of
+// q_heads heads) as int8 in (H_I + 3) / 4 words (zero padded),
 // so the dk kernel reads one feature's heads with one or two dword loads and
 // sums them with v_dot4. One thread per (row, feature).
 template <int H_I, int D_I>
-__global__ __launch_bounds__(256) void ibwd_qt_kernel(int64_t rows, const int8_t* __restrict__ q_idx,
+__global__ __launch_bounds__(256) void ibwd_qt_kernel(int64_t rows, int q_heads,
+                                                      const int8_t* __restrict__ q_idx,
                                                       uint32_t* __restrict__ qT) {
   constexpr int NW = (H_I + 3) / 4;
   for (int64_t x = blockIdx.x * 256LL + threadIdx.x; x < rows * D_I; x += gridDim.x * 256LL) {
     const int64_t row = x / D_I;
     const int j = static_cast<int>(x - row * D_I);
-    const int8_t* qr = q_idx + row * H_I * D_I + j;
+    const int8_t* qr = q_idx + row * q_heads * D_I + j;
 #pragma unroll
     for (int n = 0; n < NW; ++n) {
       uint32_t word = 0;
@@ -471,6 +485,8 @@ struct IbwdLayout {
   size_t g, m, cnt, off, cursor, tiles, ents, ekey, acc, qt, total;
 };
 
+// g.H_I: the heads of one index set (the sets run one after another and share
+// the workspace)
 static IbwdLayout ibwd_layout(const Geom& g) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t nent = static_cast<size_t>(g.B) * g.Tq * g.K;
@@ -491,12 +507,22 @@ static IbwdLayout ibwd_layout(const Geom& g) {
   return L;
 }
 
-size_t ibwd_workspace(const Geom& g) { return ibwd_layout(g).total; }
+static Geom ibwd_set_geom(const Geom& g) {
+  Geom s = g;
+  s.H_I = g.H_I / (g.sets > 1 ? g.sets : 1);
+  return s;
+}
+
+size_t ibwd_workspace(const Geom& g) { return ibwd_layout(ibwd_set_geom(g)).total; }
 
 __global__ __launch_bounds__(256) void ibwd_fill_i32_kernel(int32_t* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += gridDim.x * 256LL) p[i] = 0;
 }
 
+// g: the geometry of one index set (g.H_I its heads, g.sets the set count);
+// set s reads heads s*H_I .. s*H_I + H_I - 1 of rows of H_I*sets heads and
+// index rows [B][sets][Tq][K]. The sets run one after another on the stream,
+// sharing the workspace; their dk sums meet in one fixed-point accumulator.
 template <int H_I, int D_I>
 static hipError_t ibwd_launch_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                                  const int8_t* w, int64_t wsb, int64_t wsq, const int32_t* idx,
@@ -514,46 +540,63 @@ static hipError_t ibwd_launch_hd(const Geom& g, const int8_t* q_idx, const int8_
   int32_t* ekey = reinterpret_cast<int32_t*>(base + L.ekey);
   unsigned long long* acc = reinterpret_cast<unsigned long long*>(base + L.acc);
   uint32_t* qt = reinterpret_cast<uint32_t*>(base + L.qt);
+  const int ns = g.sets > 1 ? g.sets : 1;
+  const int q_heads = H_I * ns;
+  const int64_t brow = static_cast<int64_t>(ns) * g.Tq;  // index rows per sequence
   const int64_t keys = static_cast<int64_t>(g.B) * g.Tk;
-  const int64_t nent = static_cast<int64_t>(g.B) * g.Tq * g.K;
+  const int64_t nent = static_cast<int64_t>(g.B) * g.Tq * g.K;  // entries of one set
+  const int64_t rows = static_cast<int64_t>(g.B) * g.Tq;
+  const int64_t nacc = keys * g.d_I;
   const uint32_t gk = static_cast<uint32_t>(std::min<int64_t>((keys + 255) / 256, 8192));
   const uint32_t ge = static_cast<uint32_t>(std::min<int64_t>((nent + 255) / 256, 8192));
+  const uint32_t ga = static_cast<uint32_t>(std::min<int64_t>((nacc + 255) / 256, 8192));
+  const uint32_t gq = static_cast<uint32_t>(std::min<int64_t>((rows * D_I + 255) / 256, 8192));
+  // the list holds the valid entries: as many as the count total off[keys];
+  // four waves of 256 entries per workgroup
+  const uint32_t gd = static_cast<uint32_t>(std::min<int64_t>((nent + 1023) / 1024, 8192));
   const size_t lds = static_cast<size_t>(g.K) * (sizeof(float) + sizeof(uint16_t));
   hipError_t e;
-  {
-    KernelTimer timer(LCI_KERNEL_IBWD, st);
-    hipLaunchKernelGGL((ibwd_row_kernel<H_I, D_I>), dim3(static_cast<uint32_t>(g.B) * g.Tq),
-                       dim3(IB_NT), lds, st, g.Tq, g.Tk, g.K, g.q_offset, g.kv_len, q_idx, k_idx,
-                       w, wsb, wsq, idx, teacher, tau, loss, dq, dw, g_ent, m_ent);
+  for (int set = 0; set < ns; ++set) {
+    const int8_t* qs = q_idx + static_cast<int64_t>(set) * H_I * D_I;
+    const int8_t* ws_ = w + set * H_I;
+    const int32_t* is = idx + static_cast<int64_t>(set) * g.Tq * g.K;
+    const float* ts = teacher + static_cast<int64_t>(set) * g.Tq * g.K;
+    float* ls = loss ? loss + static_cast<int64_t>(set) * g.Tq : nullptr;
+    float* dqs = dq + static_cast<int64_t>(set) * H_I * D_I;
+    float* dws = dw + set * H_I;
+    {
+      KernelTimer timer(LCI_KERNEL_IBWD, st);
+      hipLaunchKernelGGL((ibwd_row_kernel<H_I, D_I>), dim3(static_cast<uint32_t>(rows)),
+                         dim3(IB_NT), lds, st, g.Tq, g.Tk, g.K, q_heads, brow, g.q_offset,
+                         g.kv_len, qs, k_idx, ws_, wsb, wsq, is, ts, tau, ls, dqs, dws, g_ent,
+                         m_ent);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+      KernelTimer timer(LCI_KERNEL_IBWD_TRANSPOSE, st);
+      hipLaunchKernelGGL(ibwd_fill_i32_kernel, dim3(gk), dim3(256), 0, st, cnt, keys);
+      hipLaunchKernelGGL(ibwd_fill_i32_kernel, dim3(gk), dim3(256), 0, st, cursor, keys);
+      hipLaunchKernelGGL(ibwd_count_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, brow,
+                         g.q_offset, g.kv_len, is, nent, cnt);
+      if ((e = launch_exclusive_scan(cnt, keys, off, tiles, st)) != hipSuccess) return e;
+      hipLaunchKernelGGL(ibwd_fill_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, brow,
+                         g.q_offset, g.kv_len, is, nent, off, cursor, ents, ekey);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+      KernelTimer timer(LCI_KERNEL_IBWD_DK, st);
+      if (set == 0)
+        hipLaunchKernelGGL(ibwd_zero_u64_kernel, dim3(ga), dim3(256), 0, st, acc, nacc);
+      hipLaunchKernelGGL((ibwd_qt_kernel<H_I, D_I>), dim3(gq), dim3(256), 0, st, rows, q_heads,
+                         qs, qt);
+      hipLaunchKernelGGL((ibwd_dk_kernel<H_I, D_I>), dim3(gd), dim3(256), 0, st, g.Tq, g.K, qt,
+                         ws_, wsb, wsq, ents, ekey, g_ent, m_ent, acc, off + keys);
+      if (set == ns - 1)
+        hipLaunchKernelGGL(ibwd_dk_out_kernel, dim3(ga), dim3(256), 0, st, acc, dk, nacc);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    KernelTimer timer(LCI_KERNEL_IBWD_TRANSPOSE, st);
-    hipLaunchKernelGGL(ibwd_fill_i32_kernel, dim3(gk), dim3(256), 0, st, cnt, keys);
-    hipLaunchKernelGGL(ibwd_fill_i32_kernel, dim3(gk), dim3(256), 0, st, cursor, keys);
-    hipLaunchKernelGGL(ibwd_count_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K,
-                       g.q_offset, g.kv_len, idx, nent, cnt);
-    if ((e = launch_exclusive_scan(cnt, keys, off, tiles, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(ibwd_fill_kernel, dim3(ge), dim3(256), 0, st, g.Tq, g.Tk, g.K, g.q_offset,
-                       g.kv_len, idx, nent, off, cursor, ents, ekey);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    KernelTimer timer(LCI_KERNEL_IBWD_DK, st);
-    const int64_t nacc = keys * g.d_I;
-    const uint32_t ga = static_cast<uint32_t>(std::min<int64_t>((nacc + 255) / 256, 8192));
-    hipLaunchKernelGGL(ibwd_zero_u64_kernel, dim3(ga), dim3(256), 0, st, acc, nacc);
-    const int64_t rows = static_cast<int64_t>(g.B) * g.Tq;
-    const uint32_t gq = static_cast<uint32_t>(std::min<int64_t>((rows * D_I + 255) / 256, 8192));
-    hipLaunchKernelGGL((ibwd_qt_kernel<H_I, D_I>), dim3(gq), dim3(256), 0, st, rows, q_idx, qt);
-    // the list holds the valid entries: as many as the count total off[keys]
-    // four waves of 256 entries per workgroup
-    const uint32_t gd = static_cast<uint32_t>(std::min<int64_t>((nent + 1023) / 1024, 8192));
-    hipLaunchKernelGGL((ibwd_dk_kernel<H_I, D_I>), dim3(gd), dim3(256), 0, st, g.Tq, g.K, qt,
-                       w, wsb, wsq, ents, ekey, g_ent, m_ent, acc, off + keys);
-    hipLaunchKernelGGL(ibwd_dk_out_kernel, dim3(ga), dim3(256), 0, st, acc, dk, nacc);
-  }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <int H_I>
@@ -572,10 +615,11 @@ static hipError_t ibwd_launch_h(const Geom& g, const int8_t* q_idx, const int8_t
   }
 }
 
-hipError_t launch_indexer_bwd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
+hipError_t launch_indexer_bwd(const Geom& gall, const int8_t* q_idx, const int8_t* k_idx,
                               const int8_t* w, int64_t wsb, int64_t wsq, const int32_t* idx,
                               const float* teacher, float tau, float* loss, float* dq, float* dk,
                               float* dw, void* ws, hipStream_t st) {
+  const Geom g = ibwd_set_geom(gall);
   switch (g.H_I) {
     case 1: return ibwd_launch_h<1>(g, q_idx, k_idx, w, wsb, wsq, idx, teacher, tau, loss, dq, dk, dw, ws, st);
     case 2: return ibwd_launch_h<2>(g, q_idx, k_idx, w, wsb, wsq, idx, teacher, tau, loss, dq, dk, dw, ws, st);

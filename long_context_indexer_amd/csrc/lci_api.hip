@@ -203,8 +203,8 @@ size_t lci_workspace_bytes(int entry, const lci_geom* g) {
       return lci::bwd_layout(attn_geom(g)).total;
     }
     case LCI_ENTRY_INDEXER_BWD:
-      if (check_indexer(g) != LCI_OK || sel_sets(g) > 1 || g->sets < 0) return 0;
-      return lci::ibwd_workspace(to_geom(g));
+      if (check_indexer(g) != LCI_OK || check_sets(g, true, false) != LCI_OK) return 0;
+      return lci::ibwd_workspace(attn_geom(g));  // index rows of K*block positions
     case LCI_ENTRY_DECODE:
       if (check_attention(g) != LCI_OK || check_indexer(g) != LCI_OK || g->Tq != 1 ||
           check_sets(g, true, true) != LCI_OK)
@@ -475,8 +475,7 @@ lci_status lci_indexer_bwd(const lci_geom* g, const int8_t* q_idx, const int8_t*
   lci_status s = check_base(g);
   if (s != LCI_OK) return s;
   if ((s = check_indexer(g)) != LCI_OK) return s;
-  if (g->sets < 0) return LCI_ERR_SHAPE;
-  if (sel_sets(g) > 1) return LCI_ERR_UNSUPPORTED;
+  if ((s = check_sets(g, true, false)) != LCI_OK) return s;
   if (!q_idx || !k_idx || !w || !idx || !teacher || !dq_idx || !dk_idx || !dw)
     return LCI_ERR_NULL;
   if (w_stride_b < 0 || w_stride_q < 0 || !(tau == tau) || tau == INFINITY || tau == -INFINITY)

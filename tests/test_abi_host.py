@@ -310,7 +310,15 @@ def test_indexer_bwd_arguments(lib):
     assert call(g, tau=float("inf")) == SHAPE
     assert call(g, tau=float("nan")) == SHAPE
     assert call(geom(H_I=32, d_I=64)) == OVF
-    assert call(geom(sets=2)) == UNSUP
+    # index sets: S must divide H_I; the sets share one workspace (no larger than
+    # one set's), so validation is all a host test can call
+    g8 = dict(B=2, Tq=16, Tk=300, H_I=8, d_I=64, K=32)
+    assert call(geom(**g8, sets=3)) == SHAPE
+    assert call(geom(**g8, sets=-1)) == SHAPE
+    one = lib.lci_workspace_bytes(lci.ENTRY_INDEXER_BWD, ctypes.byref(geom(**g8)))
+    two = lib.lci_workspace_bytes(lci.ENTRY_INDEXER_BWD, ctypes.byref(geom(**g8, sets=2)))
+    assert 0 < two <= one
+    assert lib.lci_workspace_bytes(lci.ENTRY_INDEXER_BWD, ctypes.byref(geom(**g8, sets=3))) == 0
     assert call(g, nb=8) == WS
     assert call(g, ws=None) == WS
     assert call(g, dq=FAKE + 4) == ALIGN

@@ -122,6 +122,69 @@ def test_indexer_bwd(lci, orc, name):
         assert torch.equal(res[key], res2[key]), key
 
 
+def _sets_case(orc, name):
+    """(cfg, inp, idx [B,S,Tq,K], teacher, tau): index rows from the oracle's own
+    per-set selection, or scrambled rows."""
+    r = np.random.default_rng(97)
+    if name == "sets2_h8d64":
+        cfg, S = TINY.replace(Tq=64, Tk=256, H_I=8, d_I=64), 2
+        inp = synth.host_inputs(cfg, seed=97)
+        inp["q_offset"] = np.array([192], np.int32)
+        tau = 0.01
+    elif name == "sets4_rowweights_ragged":
+        cfg, S = MED.replace(B=2, H_I=8), 4
+        inp = synth.host_inputs(cfg, seed=98)
+        inp["q_offset"] = np.array([0, 450], np.int32)
+        inp["kv_len"] = np.array([700, 640], np.int32)
+        inp["w"] = r.integers(-4, 6, size=(cfg.B, cfg.Tq, cfg.H_I)).astype(np.int8)
+        tau = 0.004
+    elif name == "sets8_one_head_each":
+        cfg, S = TINY.replace(Tq=48, Tk=160, K=32, Hq=8, H_I=8, d_I=32), 8
+        inp = synth.host_inputs(cfg, seed=99)
+        inp["q_offset"] = np.array([112], np.int32)
+        tau = 0.05
+    elif name == "sets2_h16d64_scrambled":
+        cfg, S = TINY.replace(Tq=40, Tk=120, K=24, H_I=16, d_I=64), 2
+        inp = synth.host_inputs(cfg, seed=100)
+        inp["q_offset"] = np.array([70], np.int32)
+        inp["kv_len"] = np.array([105], np.int32)          # rows 35.. are invalid
+        idx = np.stack([np.stack([r.permutation(111)[:cfg.K] for _ in range(cfg.Tq)])
+                        for _ in range(S)]).astype(np.int32)[None]
+        idx[0, 1, 3, 10:] = -1
+        idx[0, 0, 5, :] = 110                               # past every row's position
+        T = _teacher(r, idx.shape, normalised=False)
+        return cfg, inp, idx, T, 0.002
+    else:
+        raise KeyError(name)
+    lay = orc.layer(inp, cfg.K, sets=S)["idx"].reshape(cfg.B, cfg.Tq, S, cfg.K)
+    idx = np.ascontiguousarray(lay.transpose(0, 2, 1, 3))
+    return cfg, inp, idx, _teacher(r, idx.shape), tau
+
+
+SETS_CASES = ["sets2_h8d64", "sets4_rowweights_ragged", "sets8_one_head_each",
+              "sets2_h16d64_scrambled"]
+
+
+@pytest.mark.parametrize("name", SETS_CASES)
+def test_indexer_bwd_sets(lci, orc, name):
+    """Index sets: set j is the scorer of its group of H_I/S indexer heads over
+    its own index rows and teacher; loss per set, dq and dw per head, dk summed
+    over the sets, against the oracle; repeat calls bit-identical."""
+    import torch
+    cfg, inp, idx, T, tau = _sets_case(orc, name)
+    log(f"indexer bwd {name}: B={cfg.B} Tq={cfg.Tq} Tk={cfg.Tk} H_I={cfg.H_I} d_I={cfg.d_I} "
+        f"sets={idx.shape[1]} K={idx.shape[3]} tau={tau}")
+    res = _run(lci, inp, idx, T, tau)
+    want = orc.indexer_bwd(inp["q_idx"], inp["k_idx"], inp["w"], inp["q_offset"], inp["kv_len"],
+                           idx, T, tau)
+    assert tuple(res["loss"].shape) == want["loss"].shape
+    for key in ("loss", "dq", "dk", "dw"):
+        _close(host(res[key]), want[key], f"{name} {key}")
+    res2 = _run(lci, inp, idx, T, tau)
+    for key in ("dq", "dk", "dw", "loss"):
+        assert torch.equal(res[key], res2[key]), key
+
+
 def test_indexer_bwd_prefill8k_sampled(lci, orc):
     """The full Prefill-8K size (8192 rows, 8 indexer heads of 64, K = 2048) on
     random valid index rows: loss, dq and dw of rows 0-63 and 8100-8191 against
