@@ -42,21 +42,21 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # were taken on: any change to them turns the figure into null.
 TRAFFIC = {
     ("prefill64k", "attn_gather"): dict(
-        fetch_kib=59446964.3, write_kib=263154.8, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=59431076.1, write_kib=263145.3, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/sparse_attn.hip", "long_context_indexer_amd/csrc/common.h"],
         sha256="4311449b841043ce2e6b14fd54b686a3617f295e73bbf5e23b193de17e049ef5"),
     ("prefill64k", "attn_dense"): dict(
-        fetch_kib=1459692.3, write_kib=262180.4, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=1435990.1, write_kib=262179.4, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/attn_dense.hip", "long_context_indexer_amd/csrc/attn_dense.h", "long_context_indexer_amd/csrc/tile.h", "long_context_indexer_amd/csrc/common.h"],
-        sha256="9c4f27d6134a0471d759e9ccd2fbdd529421a18313ffa9a97a910ec524f99e43"),
+        sha256="8db3ccbd72ab2ccec9bad96735122e9383b74934c15531a7869b9bafcc9a9da8"),
     ("prefill64k", "sel_scan"): dict(
-        fetch_kib=225150.2, write_kib=4112108.6, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=226867.1, write_kib=4112361.1, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/idx_select.hip", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
         sha256="0f04192ab4187b5d31d4cfd8fd0a3f04f224afad7e92f9be97fa8cc5f9d7727e"),
     ("prefill8k", "attn_dense"): dict(
-        fetch_kib=123682.6, write_kib=66504.3, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=121629.4, write_kib=65935.9, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/attn_dense.hip", "long_context_indexer_amd/csrc/attn_dense.h", "long_context_indexer_amd/csrc/tile.h", "long_context_indexer_amd/csrc/common.h"],
-        sha256="9c4f27d6134a0471d759e9ccd2fbdd529421a18313ffa9a97a910ec524f99e43"),
+        sha256="8db3ccbd72ab2ccec9bad96735122e9383b74934c15531a7869b9bafcc9a9da8"),
     ("decode1m", "dec_score"): dict(
         fetch_kib=262422.7, write_kib=322.4, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/decode.hip", "long_context_indexer_amd/csrc/decode.h", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
@@ -400,8 +400,9 @@ def gather_probes(timed):
     return res
 
 
-def add_probe_fracs(node, probes):
-    """frac_probe beside frac in every roofline dict under node (in place)."""
+def add_probe_fracs(node, probes, kname=None):
+    """frac_probe beside frac in every roofline dict under node (in place);
+    kname: the kernel a roofline dict is keyed by when it names none itself."""
     hbm = max(probes.get("hbm_copy_gbs") or 0.0, probes.get("hbm_read_gbs") or 0.0) or None
     gather = max(probes.get("gather_128mib_256b_gbs") or 0.0,
                  probes.get("gather_128mib_1kib_gbs") or 0.0) or None
@@ -410,11 +411,11 @@ def add_probe_fracs(node, probes):
     if isinstance(node, dict):
         if "frac" in node and "achieved" in node and node.get("unit") in ref:
             pk = ref[node["unit"]]
-            if node.get("kernel") == "attn_gather" and gather:
+            if node.get("kernel", kname) == "attn_gather" and gather:
                 pk = gather
             node["frac_probe"] = round(node["achieved"] / pk, 4) if pk and node["achieved"] else None
-        for v in node.values():
-            add_probe_fracs(v, probes)
+        for k, v in node.items():
+            add_probe_fracs(v, probes, k)
 
 
 def host(t):
