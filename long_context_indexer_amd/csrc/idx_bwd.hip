@@ -25,9 +25,9 @@
 //                      int8 rows (v_dot4 over d_I, exact), the softmax of tau*S
 //                      and the loss (workgroup reductions in a fixed order), g
 //                      and the heads' ReLU masks kept per entry for dk; dw
-//                      reduced in a fixed order; dq by threads that each own a
-//                      head and four features and sum the entries in order, the
-//                      entries' key rows staged in LDS 256 at a time.
+//                      reduced in a fixed order; dq on bf16 MFMA from the
+//                      entries' key rows staged in LDS 128 at a time, with g
+//                      split exactly into three bf16 parts.
 //   ibwd_count/fill    the transpose of the index rows: for each position, the
 //                      entries that point at it (counts, an exclusive scan,
 //                      then the entry numbers in any order).
@@ -95,7 +95,16 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
   __shared__ __align__(16) int qrow[H_I * NW];
   __shared__ float red[IB_NT / 64];
   __shared__ float dwp[IB_NT / 64][H_I];
-  __shared__ __align__(16) int kst[IB_NT][NW];  // key rows of 256 entries (dq)
+  // dq on MFMA: key rows of KCH entries as bf16, one row of KTS per feature
+  // (padded so a 16-byte read by 16 lanes of 16 features touches every bank
+  // once); afterwards the waves' partial sums
+  constexpr int KCH = 128;
+  constexpr int KTS = KCH + 8;
+  constexpr int KMT = (H_I + 7) / 8;  // MFMA row tiles (8 heads x 3 parts each)
+  constexpr int KNT = D_I / 32;       // MFMA column tiles (32 features each)
+  static_assert(D_I % 32 == 0 && KCH == 2 * IB_NT / 4 && 16 * H_I <= 2 * KTS,
+                "dq staging and the partial sums' room");
+  __shared__ __align__(16) uint16_t kT[D_I * KTS];
 
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -218,53 +227,108 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
     for (int wv = 0; wv < IB_NT / 64; ++wv) v += dwp[wv][t];
     dwr[t] = v;
   }
-  // 4. dq: the threads split into SPLIT groups of H_I*NW; thread (h, j4) of
-  // group c sums its head and four features over the entries q = c (mod SPLIT)
-  // of each 256-entry chunk (key rows staged in LDS), in order; the groups'
-  // sums are added in group order at the end
-  constexpr int OWN = H_I * NW;
-  constexpr int SPLIT = IB_NT / OWN;
-  const int grp = t / OWN;
-  const int h = (t % OWN) / NW, j4 = t % NW;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int e0 = 0; e0 < K; e0 += IB_NT) {
-    const int e = e0 + t;
-    __syncthreads();  // the previous chunk is consumed
-    if (e < K && hmask[e] != 0) {
-      const int4* kr = reinterpret_cast<const int4*>(kb + static_cast<int64_t>(ir[e]) * D_I);
+  // 4. dq[h, :] = w_h sum_t G[h, t] kI[idx_t] with G[h, t] = g_t [d_ht > 0]: a
+  // product [heads x entries] x [entries x features] on bf16 MFMA. Per chunk of
+  // KCH entries the key rows go to LDS as bf16 (exact for int8), feature-major;
+  // wave wv multiplies entries 32 wv .. 32 wv + 31 of the chunk. G enters split
+  // exactly into three bf16 parts (g = hi + mid + lo to 24 bits; each product
+  // with an int8 value is exact in fp32): A-operand row m = 8 part + h % 8 of
+  // tile h / 8, so a lane's accumulators hold the three parts of the same heads
+  // (elements c, 4 + c, 8 + c) and add them itself. The waves' sums meet in LDS,
+  // added in wave order: deterministic.
+  {
+    const int lane = t & 63, wv = t >> 6;
+    const int ln = lane & 31, hf = lane >> 5;
+    const int part = ln >> 3;  // 0 hi, 1 mid, 2 lo, 3 unused rows
+    v16f acc[KMT][KNT];
 #pragma unroll
-      for (int c = 0; c < NW / 4; ++c) *reinterpret_cast<int4*>(&kst[t][4 * c]) = kr[c];
+    for (int mt = 0; mt < KMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < KNT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.f;
+    for (int c0 = 0; c0 < K; c0 += KCH) {
+      __syncthreads();  // the previous chunk is consumed (the first: g and masks visible)
+      {
+        // thread t stages entries c0 + 2 pr and c0 + 2 pr + 1, features q FPT .. + FPT - 1:
+        // bf16 pairs, one dword per feature (zeros for entries without a passing head)
+        constexpr int FPT = D_I / 4;
+        const int pr = t >> 2, q = t & 3;
+        uint32_t kw[2][FPT / 4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = c0 + 2 * pr + u;
+          const bool on = e < K && hmask[e] != 0;
+          const int* kr = reinterpret_cast<const int*>(
+              kb + static_cast<int64_t>(on ? ir[e] : 0) * D_I + q * FPT);
+#pragma unroll
+          for (int c = 0; c < FPT / 4; ++c) kw[u][c] = on ? static_cast<uint32_t>(kr[c]) : 0u;
+        }
+#pragma unroll
+        for (int f = 0; f < FPT; ++f) {
+          // an int8 value as bf16: the top half of its exact fp32 bits
+          const int sh = 8 * (f & 3);
+          const float x0 = static_cast<float>(static_cast<int8_t>(kw[0][f >> 2] >> sh));
+          const float x1 = static_cast<float>(static_cast<int8_t>(kw[1][f >> 2] >> sh));
+          *reinterpret_cast<uint32_t*>(&kT[(q * FPT + f) * KTS + 2 * pr]) =
+              (__float_as_uint(x0) >> 16) | (__float_as_uint(x1) & 0xffff0000u);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int el = 32 * wv + 16 * s + 8 * hf;  // this lane's 8 entries (chunk-local)
+        v8bf bk[KNT];
+#pragma unroll
+        for (int nt = 0; nt < KNT; ++nt)
+          bk[nt] = *reinterpret_cast<const v8bf*>(&kT[(ln + 32 * nt) * KTS + el]);
+        float gv[8];
+        uint32_t hm[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int e = c0 + el + j;
+          gv[j] = e < K ? gz[e] : 0.f;
+          hm[j] = e < K ? hmask[e] : 0u;
+        }
+#pragma unroll
+        for (int mt = 0; mt < KMT; ++mt) {
+          const int h = 8 * mt + (ln & 7);
+          v8bf a;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float v = (part < 3 && h < H_I && ((hm[j] >> h) & 1u)) ? gv[j] : 0.f;
+            const __bf16 hi = static_cast<__bf16>(v);
+            const float r1 = v - static_cast<float>(hi);
+            const __bf16 mid = static_cast<__bf16>(r1);
+            const __bf16 lo = static_cast<__bf16>(r1 - static_cast<float>(mid));
+            a[j] = part == 0 ? hi : (part == 1 ? mid : lo);
+          }
+#pragma unroll
+          for (int nt = 0; nt < KNT; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk[nt], acc[mt][nt], 0, 0, 0);
+        }
+      }
     }
+    __syncthreads();  // every wave is done with the key rows: the area holds the sums
+    float* ps = reinterpret_cast<float*>(kT);  // [4 waves][H_I][D_I]
+#pragma unroll
+    for (int mt = 0; mt < KMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < KNT; ++nt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int h = 8 * mt + 4 * hf + c;
+          if (h < H_I)
+            ps[(wv * H_I + h) * D_I + ln + 32 * nt] =
+                (acc[mt][nt][c] + acc[mt][nt][4 + c]) + acc[mt][nt][8 + c];
+        }
     __syncthreads();
-    const int n = min(IB_NT, K - e0);
-#pragma unroll 4
-    for (int q = grp; q < n; q += SPLIT) {
-      // masked entries contribute 0 (their key row slot may hold stale bytes)
-      const float g = ((hmask[e0 + q] >> h) & 1u) ? gz[e0 + q] : 0.f;
-      const int kw = g != 0.f ? kst[q][j4] : 0;
-      a0 += g * static_cast<float>(static_cast<int8_t>(kw));
-      a1 += g * static_cast<float>(static_cast<int8_t>(kw >> 8));
-      a2 += g * static_cast<float>(static_cast<int8_t>(kw >> 16));
-      a3 += g * static_cast<float>(static_cast<int8_t>(kw >> 24));
-    }
-  }
-  __syncthreads();
-  float4* part = reinterpret_cast<float4*>(kst);  // reused: SPLIT x OWN partial sums
-  part[t] = make_float4(a0, a1, a2, a3);
-  __syncthreads();
-  if (t < OWN) {
-    float4 acc = part[t];
+    for (int x = t; x < H_I * D_I; x += IB_NT) {
+      float v = ps[x];
 #pragma unroll
-    for (int c = 1; c < SPLIT; ++c) {
-      const float4 v = part[c * OWN + t];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+      for (int w2 = 1; w2 < IB_NT / 64; ++w2) v += ps[w2 * H_I * D_I + x];
+      dqr[x] = static_cast<float>(wh[x / D_I]) * v;
     }
-    const float wf = static_cast<float>(wh[h]);
-    *reinterpret_cast<float4*>(dqr + h * D_I + 4 * j4) =
-        make_float4(wf * acc.x, wf * acc.y, wf * acc.z, wf * acc.w);
   }
 }
 
