@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define LCI_ABI_VERSION 4
+#define LCI_ABI_VERSION 5
 
 typedef uint16_t lci_bf16;
 
@@ -421,6 +421,35 @@ enum {
 int lci_kernel_timing(int enable);
 int lci_kernel_timing_read(int kernel, double *total_ms, int64_t *launches);
 const char *lci_kernel_name(int kernel);
+
+/* Concurrent attention paths (a schedule, not part of the computation: the
+ * results are bit-identical either way). When the rows of a call split between
+ * the tile path and the gather path ("Hybrid Sparse Attention ...", section
+ * "Indexer + Top-K", step 3, run two exact ways; see lci_dense_row_limit), the
+ * two kernels can run at once on two library-owned streams whose compute-unit
+ * masks split every XCD (the gather gets k of each XCD's 32 CUs, the tile
+ * kernel t of them, a few possibly shared): the gather is bound by the rate rows arrive from the
+ * last-level cache and saturates on part of the chip, the tile kernel by its
+ * MFMA and softmax work. The caller's stream forks to them and joins back
+ * through events, so the call stays ordered on that stream. The library
+ * creates a pair of streams (default priority) and three events per device and
+ * split used (four splits at most) on first use and keeps them until the
+ * process ends; under graph capture, or on a device without 256 CUs, calls run
+ * on the caller's stream alone. Calls from several host threads on one device
+ * share the streams (their work is serialised there; the fork and join are
+ * guarded by a mutex).
+ *   LCI_OVERLAP_AUTO  (default) only for a whole prompt (Tq == Tk) when a cost
+ *                     model of the two kernels (measured on Prefill 64K) picks
+ *                     a split that beats running them one after the other
+ *   LCI_OVERLAP_OFF   never
+ *   LCI_OVERLAP_ON    for every call with gather rows possible (gather on 20
+ *                     CUs of each XCD, tile kernel on 16: 4 shared)
+ * lci_attn_overlap(mode) sets the process-wide mode: LCI_OK, or SHAPE for an
+ * unknown mode. lci_attn_overlap_forks() counts the calls so far (process-wide)
+ * that ran the two kernels on the library streams. */
+enum { LCI_OVERLAP_AUTO = 0, LCI_OVERLAP_OFF = 1, LCI_OVERLAP_ON = 2 };
+int lci_attn_overlap(int mode);
+long long lci_attn_overlap_forks(void);
 
 #ifdef __cplusplus
 }

@@ -26,13 +26,17 @@ LIB_PATH = os.path.join(HERE, "liblci.so")
  ENTRY_SPARSE_ATTN_BWD, ENTRY_INDEXER_BWD) = range(7)
 
 # LCI_ABI_VERSION of the signatures declared below
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTS = ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
            "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_workspace_bytes",
            "lci_dense_row_limit", "lci_indexer_bwd", "lci_decode_fwd_noalloc", "lci_noalloc_scratch_bytes",
            "lci_status_str", "lci_last_hip_error",
-           "lci_abi_version", "lci_kernel_timing", "lci_kernel_timing_read", "lci_kernel_name")
+           "lci_abi_version", "lci_kernel_timing", "lci_kernel_timing_read", "lci_kernel_name",
+           "lci_attn_overlap", "lci_attn_overlap_forks")
+
+# schedules of lci_attn_overlap (LCI_OVERLAP_* in lci.h)
+OVERLAP_AUTO, OVERLAP_OFF, OVERLAP_ON = range(3)
 
 # kernel kinds of the timing log (LCI_KERNEL_* in lci.h)
 KERNELS = ("idx_score", "topk", "idx_mask", "attn_dense", "attn_gather", "attn_combine",
@@ -99,6 +103,9 @@ def load_library(path: str = LIB_PATH):
     lib.lci_kernel_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_int64)]
     lib.lci_kernel_name.argtypes = [ctypes.c_int]
+    lib.lci_attn_overlap.argtypes = [ctypes.c_int]
+    lib.lci_attn_overlap.restype = ctypes.c_int
+    lib.lci_attn_overlap_forks.restype = ctypes.c_longlong
     lib.lci_kernel_name.restype = ctypes.c_char_p
     for fn in ("lci_idx_score", "lci_topk_select", "lci_sparse_attn_fwd", "lci_prefill_fwd",
                "lci_decode_fwd", "lci_kv_append", "lci_sparse_attn_bwd", "lci_kernel_timing", "lci_kernel_timing_read"):
@@ -172,6 +179,17 @@ def workspace_bytes(entry: int, geom: lci_geom) -> int:
 def dense_row_limit(geom: lci_geom, entry: int = ENTRY_PREFILL) -> int:
     """Rows with p + 1 <= this limit take the dense-tile attention path (0: none)."""
     return int(load_library().lci_dense_row_limit(entry, ctypes.byref(geom)))
+
+
+def attn_overlap(mode: int) -> None:
+    """Process-wide schedule of the tile and gather attention kernels:
+    OVERLAP_AUTO (default), OVERLAP_OFF or OVERLAP_ON (results identical)."""
+    _check(load_library().lci_attn_overlap(int(mode)))
+
+
+def attn_overlap_forks() -> int:
+    """Calls so far that ran the tile and gather kernels at once on the library streams."""
+    return int(load_library().lci_attn_overlap_forks())
 
 
 def kernel_timing(enable: bool) -> None:

@@ -492,6 +492,27 @@ __global__ __launch_bounds__(256, 2) void attn_dense_kernel(
 
 int dense_block_rows(int G) { return 4 * (32 / G); }
 
+// The done bytes the tile kernel writes, from the row flags alone: token block
+// tb of set s is the tile kernel's when every row of it, in every set the
+// workgroup's query heads read (nsg consecutive sets), is a tile row.
+__global__ __launch_bounds__(256) void dense_done_kernel(int Tq, int sets, int nsg, int BQ,
+                                                         int nbps,
+                                                         const uint8_t* __restrict__ flag,
+                                                         uint8_t* __restrict__ done, int64_t n) {
+  for (int64_t x = blockIdx.x * 256LL + threadIdx.x; x < n; x += gridDim.x * 256LL) {
+    const int64_t bs = x / nbps;  // b * sets + s
+    const int tb = static_cast<int>(x - bs * nbps);
+    const int s = static_cast<int>(bs % sets);
+    const int64_t b = bs / sets;
+    const int sg0 = s - s % nsg;
+    const int i1 = min(tb * BQ + BQ, Tq);
+    int ok = 1;
+    for (int s2 = sg0; s2 < sg0 + nsg; ++s2)
+      for (int i = tb * BQ; i < i1; ++i) ok &= flag[(b * sets + s2) * Tq + i] != 0;
+    done[x] = ok ? 1 : 0;
+  }
+}
+
 int dense_row_limit(const Geom& g) {
   return static_cast<int>(std::min<int64_t>(static_cast<int64_t>(kDenseFactor) * g.K, g.Tk));
 }
@@ -569,20 +590,37 @@ static hipError_t launch_dense_d(const Geom& g, const uint16_t* q, const uint16_
   }
 }
 
+hipError_t launch_dense_masks(const Geom& g, const int32_t* idx, void* ws, hipStream_t st) {
+  const DenseMasks dm = dense_masks(g, ws);
+  const size_t rows = static_cast<size_t>(g.B) * g.sets * g.Tq;
+  KernelTimer timer(LCI_KERNEL_IDX_MASK, st);
+  hipLaunchKernelGGL(idx_mask_kernel, dim3(static_cast<uint32_t>(rows)), dim3(256), 0, st, g.Tq,
+                     g.Tk, g.K, g.sets, g.q_offset, g.kv_len, idx, dm.lim, dm.Wm, dm.mask,
+                     dm.flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_done(const Geom& g, void* ws, hipStream_t st) {
+  const DenseMasks dm = dense_masks(g, ws);
+  const int G = g.Hq / g.Hkv;
+  const int BQ = dense_block_rows(G);
+  const int nbps = (g.Tq + BQ - 1) / BQ;
+  const int hps = g.Hq / g.sets;
+  const int nsg = G > hps ? G / hps : 1;
+  const int64_t n = static_cast<int64_t>(g.B) * g.sets * nbps;
+  hipLaunchKernelGGL(dense_done_kernel,
+                     dim3(static_cast<uint32_t>(std::min<int64_t>((n + 255) / 256, 4096))),
+                     dim3(256), 0, st, g.Tq, g.sets, nsg, BQ, nbps, dm.flag, dm.done, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_dense_attn(const Geom& g, const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const int32_t* idx, const uint16_t* gate,
                              const uint16_t* mix,
                              float scale, uint16_t* out, float* lse, void* ws, bool masks_ready,
                              hipStream_t st) {
   const DenseMasks dm = dense_masks(g, ws);
-  const size_t rows = static_cast<size_t>(g.B) * g.sets * g.Tq;
-  if (!masks_ready) {
-    KernelTimer timer(LCI_KERNEL_IDX_MASK, st);
-    hipLaunchKernelGGL(idx_mask_kernel, dim3(static_cast<uint32_t>(rows)), dim3(256), 0, st, g.Tq,
-                       g.Tk, g.K, g.sets, g.q_offset, g.kv_len, idx, dm.lim, dm.Wm, dm.mask,
-                       dm.flag);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e = masks_ready ? hipGetLastError() : launch_dense_masks(g, idx, ws, st);
   if (e != hipSuccess) return e;
   switch (g.d) {
     case 64: return launch_dense_d<64>(g, q, k, v, gate, mix, scale, out, lse, dm, st);

@@ -115,6 +115,27 @@ hipError_t launch_sparse_attn(const Geom& g, const uint16_t* q, const uint16_t* 
                               float scale, uint16_t* out, float* lse, int splits,
                               void* workspace, bool masks_ready, hipStream_t stream);
 
+// ---- tile and gather attention at once on disjoint compute units
+// The compute-unit split (an index into the library's table of splits) for a
+// call whose rows split between the two paths (lim: the tile path's row
+// limit; gather_work: some rows may take the gather path), or -1 to run them
+// one after the other on the caller's stream.
+int pick_overlap_split(const Geom& g, int lim, bool gather_work);
+struct OverlapStreams {
+  hipStream_t tile, gather;
+  hipEvent_t tile_done, gather_done;
+};
+// Fork: both library streams of the split wait for the caller's stream's work so
+// far (hipErrorNotSupported: no streams here, e.g. under graph capture: run on
+// the caller's stream). Join: the caller's stream waits for both.
+hipError_t overlap_fork(int split, hipStream_t caller, OverlapStreams* out);
+hipError_t overlap_join(const OverlapStreams& s, hipStream_t caller);
+// The tile path's per-row masks and flags from index rows (idx_mask_kernel),
+// and its per-token-block done bytes from the flags (what the tile kernel would
+// write), so that the gather kernel can start beside the tile kernel.
+hipError_t launch_dense_masks(const Geom& g, const int32_t* idx, void* ws, hipStream_t st);
+hipError_t launch_dense_done(const Geom& g, void* ws, hipStream_t st);
+
 // ---- block-granular Top-K: K blocks of g.block positions (a power of two,
 // at least 2) per row, the row's blocks in LDS. idx rows hold K*block positions,
 // sel (nullable) the K kept blocks' scores. With dm (masks of the attention

@@ -371,14 +371,39 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   int per_split = (g.K + splits - 1) / splits;
   per_split = (per_split + 15) / 16 * 16;
   const uint8_t* done = nullptr;
+  hipStream_t gst = st;  // the gather kernel's stream
+  bool forked = false;
+  OverlapStreams ov{};
   if (splits == 1) {
-    hipError_t e0 =
-        launch_dense_attn(g, q, k, v, idx, gate, mix, scale, out, lse, ws, masks_ready, st);
-    if (e0 != hipSuccess) return e0;
     const DenseMasks dm = dense_masks(g, ws);
     // masks from the Top-K kernel and histories no longer than lim: every row
     // is a tile-kernel row (valid ones qualify, empty ones are written there)
-    if (masks_ready && g.Tk <= dm.lim) return hipSuccess;
+    const bool gather_work = !(masks_ready && g.Tk <= dm.lim);
+    const int split = pick_overlap_split(g, dm.lim, gather_work);
+    if (split >= 0) {
+      // the tile path's flags and done bytes first, then the two kernels at
+      // once on disjoint CUs (the tile kernel rewrites the same done bytes)
+      hipError_t e0 = masks_ready ? hipSuccess : launch_dense_masks(g, idx, ws, st);
+      if (e0 == hipSuccess) e0 = launch_dense_done(g, ws, st);
+      if (e0 != hipSuccess) return e0;
+      e0 = overlap_fork(split, st, &ov);
+      if (e0 == hipSuccess) {
+        forked = true;
+        gst = ov.gather;
+        e0 = launch_dense_attn(g, q, k, v, idx, gate, mix, scale, out, lse, ws, true, ov.tile);
+      } else if (e0 == hipErrorNotSupported) {  // no library streams: one after the other
+        e0 = launch_dense_attn(g, q, k, v, idx, gate, mix, scale, out, lse, ws, true, st);
+      }
+      if (e0 != hipSuccess) {
+        if (forked) overlap_join(ov, st);
+        return e0;
+      }
+    } else {
+      hipError_t e0 =
+          launch_dense_attn(g, q, k, v, idx, gate, mix, scale, out, lse, ws, masks_ready, st);
+      if (e0 != hipSuccess) return e0;
+      if (!gather_work) return hipSuccess;
+    }
     done = dm.done;
   }
   // wave units of a row: the key/value heads, or the index sets when there are
@@ -393,13 +418,17 @@ static hipError_t launch_d(const Geom& g, const uint16_t* q, const uint16_t* k,
   dim3 grid(static_cast<uint32_t>(std::min<int64_t>(nitems, 8192 / nw)));
   const size_t lds = static_cast<size_t>(nw) * 16 * C::PITCH * sizeof(uint16_t);
   {
-    KernelTimer timer(LCI_KERNEL_ATTN_GATHER, st);
-    hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * nw), lds, st, g.Tq, g.Tk, g.K,
+    KernelTimer timer(LCI_KERNEL_ATTN_GATHER, gst);
+    hipLaunchKernelGGL((sparse_attn_kernel<D>), grid, dim3(64 * nw), lds, gst, g.Tq, g.Tk, g.K,
                        g.Hq, g.Hkv, G, g.sets, Gu, nck, g.kv_len, q, k, v, idx, gate, mix,
                        scale * LOG2E, out, lse, splits, per_split, static_cast<float*>(ws), done,
                        dense_block_rows(G), nitems);
   }
   hipError_t e = hipGetLastError();
+  if (forked) {
+    const hipError_t ej = overlap_join(ov, st);
+    if (e == hipSuccess) e = ej;
+  }
   if (e != hipSuccess || splits == 1) return e;
   dim3 cgrid(static_cast<uint32_t>(static_cast<int64_t>(g.B) * g.Tq), (g.Hq * (D / 2) + 255) / 256);
   {

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.lci_abi_version() == lci.ABI_VERSION == 4
+    assert lib.lci_abi_version() == lci.ABI_VERSION == 5
     for code in (OK, NULL, SHAPE, UNSUP, OVF, WS, HIP, ALIGN):
         assert lib.lci_status_str(code).decode().startswith("LCI_")
     assert b"unknown" in lib.lci_status_str(123)
@@ -248,6 +248,15 @@ def test_kernel_timing_log_on_the_host(lib):
     assert lib.lci_kernel_timing_read(99, ctypes.byref(ms), ctypes.byref(n)) == SHAPE
     assert lib.lci_kernel_timing_read(0, None, ctypes.byref(n)) == NULL
     assert lib.lci_kernel_timing(0) == OK
+
+
+def test_attn_overlap_modes(lib):
+    """The schedule switch takes the three modes and refuses others (it only
+    sets a process-wide value: no stream or device is touched here)."""
+    for m in (lci.OVERLAP_OFF, lci.OVERLAP_ON, lci.OVERLAP_AUTO):
+        assert lib.lci_attn_overlap(m) == 0
+    assert lib.lci_attn_overlap(3) == SHAPE
+    assert lib.lci_attn_overlap(-1) == SHAPE
 
 
 def test_binding_refuses_cpu_tensors():
