@@ -42,21 +42,21 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # were taken on: any change to them turns the figure into null.
 TRAFFIC = {
     ("prefill64k", "attn_gather"): dict(
-        fetch_kib=59431076.1, write_kib=263145.3, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=60698896.4, write_kib=262190.7, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/sparse_attn.hip", "long_context_indexer_amd/csrc/common.h"],
-        sha256="4311449b841043ce2e6b14fd54b686a3617f295e73bbf5e23b193de17e049ef5"),
+        sha256="9d1e44aa4e1c05578d0ce0df95e035332296c77f2401efe0829f0c6c5eb64a92"),
     ("prefill64k", "attn_dense"): dict(
-        fetch_kib=1435990.1, write_kib=262179.4, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=2436313.1, write_kib=262178.7, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/attn_dense.hip", "long_context_indexer_amd/csrc/attn_dense.h", "long_context_indexer_amd/csrc/tile.h", "long_context_indexer_amd/csrc/common.h"],
-        sha256="8db3ccbd72ab2ccec9bad96735122e9383b74934c15531a7869b9bafcc9a9da8"),
+        sha256="7b605c37ae27f08f2199cd7a9bfb116bbcc24e858955a4ee0f314501a9973b8c"),
     ("prefill64k", "sel_scan"): dict(
-        fetch_kib=226867.1, write_kib=4112361.1, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=224014.6, write_kib=4107806.6, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/idx_select.hip", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
         sha256="0f04192ab4187b5d31d4cfd8fd0a3f04f224afad7e92f9be97fa8cc5f9d7727e"),
     ("prefill8k", "attn_dense"): dict(
-        fetch_kib=121629.4, write_kib=65935.9, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=121627.7, write_kib=65956.5, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/attn_dense.hip", "long_context_indexer_amd/csrc/attn_dense.h", "long_context_indexer_amd/csrc/tile.h", "long_context_indexer_amd/csrc/common.h"],
-        sha256="8db3ccbd72ab2ccec9bad96735122e9383b74934c15531a7869b9bafcc9a9da8"),
+        sha256="7b605c37ae27f08f2199cd7a9bfb116bbcc24e858955a4ee0f314501a9973b8c"),
     ("decode1m", "dec_score"): dict(
         fetch_kib=262422.7, write_kib=322.4, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/decode.hip", "long_context_indexer_amd/csrc/decode.h", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
@@ -156,12 +156,15 @@ def kernel_work(cfg, kname, lim):
     return None
 
 
-def roofline(cfg, kern, lim, workload):
-    """Roofline of the kernel that takes the most time per step. achieved = the
-    algorithmic work that kernel does per step / its summed launch durations per
-    step (event-timed average launch time x launches per step)."""
+def roofline(cfg, kern, lim, workload, prefer=None):
+    """Roofline of the kernel that takes the most time per step (or `prefer`,
+    when given and timed). achieved = the algorithmic work that kernel does per
+    step / its summed launch durations per step (event-timed average launch
+    time x launches per step)."""
     ranked = sorted(kern, key=lambda k: -kern[k]["ms_per_step"])
     dom = next((k for k in ranked if kernel_work(cfg, k, lim) is not None), ranked[0])
+    if prefer in kern and kernel_work(cfg, prefer, lim) is not None:
+        dom = prefer
     kw = kernel_work(cfg, dom, lim)
     ms = kern[dom]["ms_per_step"]
     if kw is None:
@@ -557,9 +560,12 @@ def main():
         ms_step, ev_ms, dist, kern = timed_region(timer, step, args.steps, lci)
         forked = lci.attn_overlap_forks() > forks0
         tok_s = cfg.B * cfg.Tq / (ms_step * 1e-3)
+        # with the two attention kernels at once (about equally long by the
+        # split's choice), the headline is the gather: it moves the step's bytes
         res = dict(workload=name, ms_per_step=ms_step, event_ms_per_step=ev_ms, step_ms=dist,
                    tok_s=tok_s, dense_row_limit=lim,
-                   roofline=roofline(cfg, kern, lim, name),
+                   roofline=roofline(cfg, kern, lim, name,
+                                     prefer="attn_gather" if forked else None),
                    kernel_rooflines=kernel_rooflines(cfg, kern, lim),
                    kernels_us_per_step=us_per_step(kern))
         if forked:

@@ -21,6 +21,7 @@
 // ms split 20 / 16.
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <mutex>
 
 #include "../../include/lci.h"
@@ -57,6 +58,28 @@ struct DeviceStreams {
 
 std::mutex g_mu;  // guards the table and each fork/join sequence
 DeviceStreams g_dev[kMaxDevices][kNumSplits];  // per device and split
+bool g_exit_hook = false;
+
+// At process exit (before the runtime's own teardown, whose exit hooks were
+// registered earlier): wait for the library streams and release them, so no
+// masked queue outlives the code that made it.
+void release_streams() {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (int dev = 0; dev < kMaxDevices; ++dev)
+    for (int si = 0; si < kNumSplits; ++si) {
+      DeviceStreams& d = g_dev[dev][si];
+      if (!d.ok) continue;
+      if (hipSetDevice(dev) != hipSuccess) continue;
+      hipStreamSynchronize(d.tile);
+      hipStreamSynchronize(d.gather);
+      hipStreamDestroy(d.tile);
+      hipStreamDestroy(d.gather);
+      hipEventDestroy(d.fork);
+      hipEventDestroy(d.tile_done);
+      hipEventDestroy(d.gather_done);
+      d.ok = false;
+    }
+}
 std::atomic<int> g_mode{LCI_OVERLAP_AUTO};
 std::atomic<long long> g_forks{0};  // calls that ran the two kernels on the library streams
 
@@ -94,6 +117,10 @@ DeviceStreams* device_streams(int si, hipStream_t caller) {
   if (d.ok) return &d;
   if (d.tried) return nullptr;
   d.tried = true;
+  if (!g_exit_hook) {
+    g_exit_hook = true;
+    std::atexit(release_streams);
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess ||
       prop.multiProcessorCount != kXcds * kCusPerXcd)
