@@ -517,7 +517,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for {args.gpus}); the "
+        print(f"bench.py: the library runs on one GPU (asked for {args.gpus}); the "
               "multi-GPU split of the path is a design note, not a runnable mode", file=sys.stderr)
         sys.exit(2)
 

@@ -191,7 +191,7 @@ def _fused_check(lci, orc, cfg, inp, K, rows=None, entry="prefill"):
 def test_tiny_fp32_source(lci, orc):
     """The Tiny configuration draws Q, K, V and the gate logits in fp32. The
     library computes from their bf16 roundings (to nearest even): parity is
-    judged against the oracle on those bf16 inputs, and the same output is also
+    checked against the oracle on those bf16 inputs, and the same output is also
     reported against the oracle on the fp32 sources (the rounding of the inputs
     shows there, at about 3e-3 relative L2), within the same bounds."""
     import torch
