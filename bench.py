@@ -569,6 +569,8 @@ def main():
                    kernel_rooflines=kernel_rooflines(cfg, kern, lim),
                    kernels_us_per_step=us_per_step(kern))
         if forked:
+            res["roofline"]["schedule"] = ("at once with attn_dense, each on its own share of "
+                                           "every XCD's compute units (lci_attn_overlap)")
             both = [kern[k]["ms_per_step"] for k in ("attn_dense", "attn_gather") if k in kern]
             res["attention_overlap"] = dict(
                 concurrent=True, attention_ms=max(both) if both else None,
