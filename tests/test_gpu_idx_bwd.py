@@ -90,11 +90,22 @@ def _case(orc, name):
         inp["q_offset"] = np.array([120], np.int32)
         idx = orc.layer(inp, cfg.K)["idx"].reshape(cfg.B, cfg.Tq, cfg.K)
         return cfg, inp, idx, _teacher(r, idx.shape), 1e-7
+    if name == "long_history_global_counts":
+        # more positions than the transpose keeps per-block counters for in LDS
+        # (16384): the per-entry atomic count and fill
+        cfg = TINY.replace(Tq=48, Tk=20000, K=64, H_I=4, d_I=64)
+        inp = synth.host_inputs(cfg, seed=98)
+        inp["q_offset"] = np.array([19900], np.int32)
+        inp["kv_len"] = np.array([19948], np.int32)
+        idx = np.stack([r.choice(19900 + i + 1, cfg.K, replace=False) for i in range(cfg.Tq)])
+        idx = idx.astype(np.int32)[None]
+        idx[0, :, 0] = 7                                     # a position every row points at
+        return cfg, inp, idx, _teacher(r, idx.shape), 0.01
     raise KeyError(name)
 
 
 CASES = ["tiny_topk", "med_rowweights_ragged", "scrambled_padding", "h16d64",
-         "h8d128_int8_extremes"]
+         "h8d128_int8_extremes", "long_history_global_counts"]
 
 
 def _run(lci, inp, idx, T, tau):
