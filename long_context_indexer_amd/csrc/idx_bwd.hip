@@ -78,7 +78,7 @@ __device__ __forceinline__ float ib_block_max(float v, float* red) {
 // the set's heads, the first of them at q_idx, dq and dw (rows of q_heads
 // heads); the set's index row, teacher row and loss of (b, i) are row
 // b*brow + i of idx, teacher and loss. Dynamic LDS: K floats of g (z first),
-// K 16-bit head masks (bit h: d_ht > 0; 0 for skipped entries).
+// the K positions, K 16-bit head masks (bit h: d_ht > 0; 0 for skipped entries).
 template <int H_I, int D_I>
 __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
     int Tq, int Tk, int K, int q_heads, int64_t brow, const int32_t* __restrict__ q_offset,
@@ -90,11 +90,11 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
   static_assert(D_I % 16 == 0 && H_I * (D_I / 4) <= IB_NT, "thread mapping of dq");
   constexpr int NW = D_I / 4;  // int8 quads of a row
   static_assert(H_I <= 16, "16-bit head masks");
-  extern __shared__ __align__(16) float gz[];  // K floats, then K 16-bit masks
-  uint16_t* hmask = reinterpret_cast<uint16_t*>(gz + K);
+  extern __shared__ __align__(16) float gz[];  // K floats, K positions, K 16-bit masks
+  int* sidx = reinterpret_cast<int*>(gz + K);
+  uint16_t* hmask = reinterpret_cast<uint16_t*>(sidx + K);
   __shared__ __align__(16) int qrow[H_I * NW];
   __shared__ float red[IB_NT / 64];
-  __shared__ float dwp[IB_NT / 64][H_I];
   // dq on MFMA: key rows of KCH entries as bf16, one row of KTS per feature
   // (padded so a 16-byte read by 16 lanes of 16 features touches every bank
   // once); afterwards the waves' partial sums
@@ -131,46 +131,67 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
   const float* Tr = teacher + irow * K;
   const int8_t* kb = k_idx + static_cast<int64_t>(b) * Tk * D_I;
 
-  // the entry's head dot products, exact
-  auto dots = [&](int s, int (&d)[H_I]) {
-    const int4* kr = reinterpret_cast<const int4*>(kb + static_cast<int64_t>(s) * D_I);
-    int4 kq[NW / 4];
+  // 1. z_t = tau * S_t for the valid entries (-inf for the others), max
+  // A thread takes its entries e0 + u IB_NT (u < EB) together: the positions,
+  // then the key rows, every load issued before any is used (one memory
+  // latency per EB entries); then head by head, the head's query quads read
+  // once from LDS for all EB rows (a compiler barrier per head keeps the
+  // query row out of registers). Entries past K or outside 0..p read row 0
+  // and are not used.
+  constexpr int KQ = NW / 4;  // 16-byte pieces of a row
+  constexpr int EB = 2;
+  float mloc = -INFINITY;
+  for (int e0 = t; e0 < K; e0 += EB * IB_NT) {
+    int sv[EB];
 #pragma unroll
-    for (int c = 0; c < NW / 4; ++c) kq[c] = kr[c];
+    for (int u = 0; u < EB; ++u) {
+      const int e = e0 + u * IB_NT;
+      sv[u] = e < K ? ir[e] : -1;
+    }
+    int4 kq[EB][KQ];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      const int s = sv[u] >= 0 && sv[u] <= p ? sv[u] : 0;
+      const int4* kr = reinterpret_cast<const int4*>(kb + static_cast<int64_t>(s) * D_I);
+#pragma unroll
+      for (int c = 0; c < KQ; ++c) kq[u][c] = kr[c];
+    }
+    int S[EB];
+    uint32_t hm[EB];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) S[u] = 0, hm[u] = 0u;
 #pragma unroll
     for (int h = 0; h < H_I; ++h) {
-      int acc = 0;
 #pragma unroll
-      for (int c = 0; c < NW / 4; ++c) {
-        acc = __builtin_amdgcn_sdot4(qrow[h * NW + 4 * c], kq[c].x, acc, false);
-        acc = __builtin_amdgcn_sdot4(qrow[h * NW + 4 * c + 1], kq[c].y, acc, false);
-        acc = __builtin_amdgcn_sdot4(qrow[h * NW + 4 * c + 2], kq[c].z, acc, false);
-        acc = __builtin_amdgcn_sdot4(qrow[h * NW + 4 * c + 3], kq[c].w, acc, false);
-      }
-      d[h] = acc;
-    }
-  };
-
-  // 1. z_t = tau * S_t for the valid entries (-inf for the others), max
-  float mloc = -INFINITY;
-  for (int e = t; e < K; e += IB_NT) {
-    const int s = ir[e];
-    float z = -INFINITY;
-    uint32_t hm = 0;
-    if (s >= 0 && s <= p) {
-      int d[H_I];
-      dots(s, d);
-      int S = 0;
+      for (int u = 0; u < EB; ++u) asm volatile("" : "+v"(S[u]) : : "memory");
+      int4 qq[KQ];
 #pragma unroll
-      for (int h = 0; h < H_I; ++h) {
-        S += wh[h] * max(d[h], 0);
-        hm |= (d[h] > 0 ? 1u : 0u) << h;
+      for (int c = 0; c < KQ; ++c) qq[c] = reinterpret_cast<const int4*>(qrow + h * NW)[c];
+#pragma unroll
+      for (int u = 0; u < EB; ++u) {
+        int acc = 0;
+#pragma unroll
+        for (int c = 0; c < KQ; ++c) {
+          acc = __builtin_amdgcn_sdot4(qq[c].x, kq[u][c].x, acc, false);
+          acc = __builtin_amdgcn_sdot4(qq[c].y, kq[u][c].y, acc, false);
+          acc = __builtin_amdgcn_sdot4(qq[c].z, kq[u][c].z, acc, false);
+          acc = __builtin_amdgcn_sdot4(qq[c].w, kq[u][c].w, acc, false);
+        }
+        S[u] += wh[h] * max(acc, 0);
+        hm[u] |= (acc > 0 ? 1u : 0u) << h;
       }
-      z = tau * static_cast<float>(S);
     }
-    gz[e] = z;
-    hmask[e] = static_cast<uint16_t>(hm);
-    mloc = fmaxf(mloc, z);
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      const int e = e0 + u * IB_NT;
+      if (e >= K) break;
+      const bool ok = sv[u] >= 0 && sv[u] <= p;
+      const float z = ok ? tau * static_cast<float>(S[u]) : -INFINITY;
+      gz[e] = z;
+      sidx[e] = sv[u];
+      hmask[e] = static_cast<uint16_t>(ok ? hm[u] : 0u);
+      mloc = fmaxf(mloc, z);
+    }
   }
   const float m = ib_block_max(mloc, red);
   if (m == -INFINITY) return;  // no valid entry: zeros (written above)
@@ -185,11 +206,8 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
   const float Z = ib_block_sum(zs, red);
   const float Tsum = ib_block_sum(ts, red);
   const float logZ = m + __logf(Z);
-  // 3. loss, g and dw partials; g and the masks kept per entry for dk
+  // 3. loss and g; g and the masks kept per entry for dk
   float lloc = 0.f;
-  float dwl[H_I];
-#pragma unroll
-  for (int h = 0; h < H_I; ++h) dwl[h] = 0.f;
   float* gr = g_ent + row * K;
   uint16_t* mr = m_ent + row * K;
   for (int e = t; e < K; e += IB_NT) {
@@ -201,32 +219,13 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
       const float te = Tr[e];
       if (te > 0.f) lloc += te * (__logf(te) - logp);
       g = tau * (pt * Tsum - te);
-      int d[H_I];
-      dots(ir[e], d);
-#pragma unroll
-      for (int h = 0; h < H_I; ++h) dwl[h] += g * static_cast<float>(max(d[h], 0));
     }
     gz[e] = g;  // the same thread reads it back below, after a barrier
     gr[e] = g;
     mr[e] = hmask[e];
   }
-  const float L = ib_block_sum(lloc, red);
+  const float L = ib_block_sum(lloc, red);  // its barriers publish g and the masks
   if (loss && t == 0) loss[irow] = L;
-  // dw: per-wave sums, then the waves in order
-#pragma unroll
-  for (int h = 0; h < H_I; ++h) {
-    float v = dwl[h];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if ((t & 63) == 0) dwp[t >> 6][h] = v;
-  }
-  __syncthreads();  // g, masks and the dw partials are visible
-  if (t < H_I) {
-    float v = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < IB_NT / 64; ++wv) v += dwp[wv][t];
-    dwr[t] = v;
-  }
   // 4. dq[h, :] = w_h sum_t G[h, t] kI[idx_t] with G[h, t] = g_t [d_ht > 0]: a
   // product [heads x entries] x [entries x features] on bf16 MFMA. Per chunk of
   // KCH entries the key rows go to LDS as bf16 (exact for int8), feature-major;
@@ -247,23 +246,27 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
       for (int nt = 0; nt < KNT; ++nt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.f;
+    // thread t stages entries c0 + 2 pr and c0 + 2 pr + 1, features q FPT .. + FPT - 1,
+    // as bf16 pairs, one dword per feature (zeros for entries without a passing
+    // head); the next chunk's key bytes are loaded while this chunk multiplies
+    constexpr int FPT = D_I / 4;
+    const int pr = t >> 2, q = t & 3;
+    uint32_t kw[2][FPT / 4];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = c0 + 2 * pr + u;
+        const bool on = e < K && hmask[e] != 0;
+        const int* kr = reinterpret_cast<const int*>(
+            kb + static_cast<int64_t>(on ? sidx[e] : 0) * D_I + q * FPT);
+#pragma unroll
+        for (int c = 0; c < FPT / 4; ++c) kw[u][c] = on ? static_cast<uint32_t>(kr[c]) : 0u;
+      }
+    };
+    load_chunk(0);  // g, positions and masks are visible (the loss sum's barriers)
     for (int c0 = 0; c0 < K; c0 += KCH) {
-      __syncthreads();  // the previous chunk is consumed (the first: g and masks visible)
+      __syncthreads();  // the previous chunk is consumed
       {
-        // thread t stages entries c0 + 2 pr and c0 + 2 pr + 1, features q FPT .. + FPT - 1:
-        // bf16 pairs, one dword per feature (zeros for entries without a passing head)
-        constexpr int FPT = D_I / 4;
-        const int pr = t >> 2, q = t & 3;
-        uint32_t kw[2][FPT / 4];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int e = c0 + 2 * pr + u;
-          const bool on = e < K && hmask[e] != 0;
-          const int* kr = reinterpret_cast<const int*>(
-              kb + static_cast<int64_t>(on ? ir[e] : 0) * D_I + q * FPT);
-#pragma unroll
-          for (int c = 0; c < FPT / 4; ++c) kw[u][c] = on ? static_cast<uint32_t>(kr[c]) : 0u;
-        }
 #pragma unroll
         for (int f = 0; f < FPT; ++f) {
           // an int8 value as bf16: the top half of its exact fp32 bits
@@ -275,6 +278,7 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
         }
       }
       __syncthreads();
+      if (c0 + KCH < K) load_chunk(c0 + KCH);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int el = 32 * wv + 16 * s + 8 * hf;  // this lane's 8 entries (chunk-local)
@@ -327,7 +331,21 @@ __global__ __launch_bounds__(IB_NT) void ibwd_row_kernel(
       float v = ps[x];
 #pragma unroll
       for (int w2 = 1; w2 < IB_NT / 64; ++w2) v += ps[w2 * H_I * D_I + x];
+      ps[x] = v;  // the sum G kI, kept for dw
       dqr[x] = static_cast<float>(wh[x / D_I]) * v;
+    }
+    __syncthreads();
+    // dw_h = sum_t g_t relu(d_ht) = sum_t G[h, t] d_ht = q_h . (G kI)[h, :]: the
+    // same sum read through the unscaled dq row; wave wv takes heads wv, wv + 4,
+    // ..., a lane features lane, lane + 64, ..., added in a fixed order
+    const int8_t* q8 = reinterpret_cast<const int8_t*>(qrow);
+    for (int h = wv; h < H_I; h += IB_NT / 64) {
+      float v = 0.f;
+      for (int f = lane; f < D_I; f += 64)
+        v += static_cast<float>(q8[h * D_I + f]) * ps[h * D_I + f];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0) dwr[h] = v;
     }
   }
 }
@@ -667,7 +685,7 @@ static hipError_t ibwd_launch_hd(const Geom& g, const int8_t* q_idx, const int8_
   // the list holds the valid entries: as many as the count total off[keys];
   // four waves of 256 entries per workgroup
   const uint32_t gd = static_cast<uint32_t>(std::min<int64_t>((nent + 1023) / 1024, 8192));
-  const size_t lds = static_cast<size_t>(g.K) * (sizeof(float) + sizeof(uint16_t));
+  const size_t lds = static_cast<size_t>(g.K) * (sizeof(float) + sizeof(int) + sizeof(uint16_t));
   hipError_t e;
   for (int set = 0; set < ns; ++set) {
     const int8_t* qs = q_idx + static_cast<int64_t>(set) * H_I * D_I;
