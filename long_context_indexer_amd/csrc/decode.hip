@@ -163,6 +163,27 @@ __global__ __launch_bounds__(DEC_NT) void dec_sample_kernel(
   }
 }
 
+// Sum of p[wi * stride] over wi = w0, w0 + STEP, ... below nw, sixteen loads
+// issued before the first add (the histograms were written by other
+// workgroups, so each load is a trip to the far caches; a plain loop waits for
+// each one in turn).
+template <int STEP>
+__device__ __forceinline__ uint32_t strided_sum(const uint32_t* __restrict__ p, int stride,
+                                                int w0, int nw) {
+  uint32_t acc = 0;
+  for (int wb = w0; wb < nw; wb += 16 * STEP) {
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int wi = wb + u * STEP;
+      v[u] = wi < nw ? p[static_cast<int64_t>(wi) * stride] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += v[u];
+  }
+  return acc;
+}
+
 // The threshold t of sequence b: the lowest score of the
 // score_bin bin holding the target-th largest sample (target about
 // K/ss + 4 sqrt(K/ss) + 2), so at least target samples score >= t. Two levels
@@ -185,9 +206,7 @@ __device__ int32_t dec_threshold(int b, int64_t n, int K, int ss, int nsw,
   // coarse: thread t sums coarse bin t % 64 over workgroups t / 64, t / 64 + 4, ...
   {
     const uint32_t* cp = chist + static_cast<int64_t>(b) * nsw * DEC_CBINS + lane;
-    uint32_t acc = 0;
-    for (int wi = t >> 6; wi < nw; wi += DEC_NT / 64) acc += cp[static_cast<int64_t>(wi) * DEC_CBINS];
-    red[t] = acc;
+    red[t] = strided_sum<DEC_NT / 64>(cp, DEC_CBINS, t >> 6, nw);
   }
   __syncthreads();
   if (t < 64) {
@@ -208,8 +227,7 @@ __device__ int32_t dec_threshold(int b, int64_t n, int K, int ss, int nsw,
   // fine: thread t sums fine bin 32 cbin + t % 32 over workgroups t / 32, t / 32 + 8, ...
   {
     const uint32_t* fp = fhist + static_cast<int64_t>(b) * nsw * DEC_BINS + 32 * cbin + (t & 31);
-    uint32_t acc = 0;
-    for (int wi = t >> 5; wi < nw; wi += DEC_NT / 32) acc += fp[static_cast<int64_t>(wi) * DEC_BINS];
+    const uint32_t acc = strided_sum<DEC_NT / 32>(fp, DEC_BINS, t >> 5, nw);
     __syncthreads();  // every thread has read res
     red[t] = acc;
   }
