@@ -593,6 +593,11 @@ __global__ __launch_bounds__(SEL_NT) void sel_rows_kernel(
     if (w0 + j < nw) mine += static_cast<uint32_t>(__popc(keep[w0 + j]));
   uint32_t tot;
   uint32_t slot = block_excl_scan(mine, scratch, &tot);
+  // the index row is built in LDS (the bin entries' array, free after the
+  // ranking) and stored by consecutive lanes: each thread's own run of slots
+  // written straight to memory would touch a separate cache line per lane
+  int32_t* const ostage = reinterpret_cast<int32_t*>(small);
+  const bool staged = K <= 2 * SEL_SMALL;  // uniform
   for (int j = 0; j < wpt; ++j) {
     const int wj = w0 + j;
     if (wj >= nw) break;
@@ -600,9 +605,17 @@ __global__ __launch_bounds__(SEL_NT) void sel_rows_kernel(
     while (word != 0u) {
       const int bit = __ffs(static_cast<int>(word)) - 1;
       word &= word - 1u;
-      if (slot < static_cast<uint32_t>(K)) out[slot] = 32 * wj + bit;
+      if (slot < static_cast<uint32_t>(K)) {
+        if (staged) ostage[slot] = 32 * wj + bit;
+        else out[slot] = 32 * wj + bit;
+      }
       ++slot;
     }
+  }
+  if (staged) {
+    __syncthreads();
+    const int nout = static_cast<int>(min(tot, static_cast<uint32_t>(K)));
+    for (int j = t; j < nout; j += SEL_NT) out[j] = ostage[j];
   }
 }
 
