@@ -481,7 +481,7 @@ __global__ __launch_bounds__(SEL_NT) void sel_rows_kernel(
     const int32_t* __restrict__ kv_len, const int2* __restrict__ cand,
     const uint32_t* __restrict__ cnt, const SelMeta* __restrict__ meta,
     int32_t* __restrict__ idx, int out_tq, uint32_t* __restrict__ nfb,
-    int32_t* __restrict__ fb_rows) {
+    int32_t* __restrict__ fb_rows, DenseMasks dm) {
   extern __shared__ __align__(16) uint32_t keep[];  // ceil(Tk/32) words
   __shared__ int2 small[SEL_SMALL];
   __shared__ uint32_t hist[SEL_FB];
@@ -499,9 +499,23 @@ __global__ __launch_bounds__(SEL_NT) void sel_rows_kernel(
   const int64_t p64 = static_cast<int64_t>(q_offset[b]) + i;
   const bool rok = p64 >= 0 && p64 < kvl;
   const int n = rok ? static_cast<int>(p64) + 1 : 0;
-  int32_t* out = idx + (static_cast<int64_t>(b) * out_tq + i) * K;
+  const int64_t orow = static_cast<int64_t>(b) * out_tq + i;
+  int32_t* out = idx + orow * K;
+  // the tile path's row flag and mask (dm.mask set): rows with p + 1 <= lim
+  // take the tile kernel, under a bit mask of their kept positions; an
+  // invalid row (n = 0) is the tile kernel's empty row
+  const bool tile = dm.mask != nullptr && n <= dm.lim;
+  if (dm.mask != nullptr && !tile && t == 0) dm.flag[orow] = kRowGather;
   if (n <= K) {  // every position kept, or an invalid row
     for (int j = t; j < K; j += SEL_NT) out[j] = j < n ? j : -1;
+    if (tile) {
+      uint32_t* mrow = dm.mask + orow * dm.Wm;
+      for (int wd = t; wd < dm.Wm; wd += SEL_NT) {
+        const int lo = 32 * wd;
+        mrow[wd] = n >= lo + 32 ? 0xffffffffu : (n > lo ? (1u << (n - lo)) - 1u : 0u);
+      }
+      if (t == 0) dm.flag[orow] = rok ? kRowAll : kRowEmpty;
+    }
     return;
   }
   const int64_t row = static_cast<int64_t>(b) * Tq + i;
@@ -585,6 +599,11 @@ __global__ __launch_bounds__(SEL_NT) void sel_rows_kernel(
     if (rank < need) atomicOr(&keep[ej.y >> 5], 1u << (ej.y & 31));
   }
   __syncthreads();
+  if (tile) {  // the kept map is final: it is the row's mask (zero past p)
+    uint32_t* mrow = dm.mask + orow * dm.Wm;
+    for (int wd = t; wd < dm.Wm; wd += SEL_NT) mrow[wd] = wd < nw ? keep[wd] : 0u;
+    if (t == 0) dm.flag[orow] = kRowMasked;
+  }
   // ordered compaction: thread t takes words [t*wpt, (t+1)*wpt)
   const int wpt = (nw + SEL_NT - 1) / SEL_NT;
   const int w0 = t * wpt;
@@ -627,7 +646,8 @@ __global__ __launch_bounds__(TOPK_NT) void sel_fallback_kernel(
     const int32_t* __restrict__ kv_len, const int8_t* __restrict__ q_idx,
     const int8_t* __restrict__ k_idx, const int8_t* __restrict__ w,
     const uint32_t* __restrict__ nfb, const int32_t* __restrict__ fb_rows,
-    int32_t* __restrict__ scratch, int64_t srow_stride, int32_t* __restrict__ idx, int out_tq) {
+    int32_t* __restrict__ scratch, int64_t srow_stride, int32_t* __restrict__ idx, int out_tq,
+    DenseMasks dm) {
   __shared__ union {
     SelectLds radix;
     Select2Lds mask2;
@@ -659,12 +679,26 @@ __global__ __launch_bounds__(TOPK_NT) void sel_fallback_kernel(
       S[s] = acc;
     }
     __syncthreads();
-    int32_t* out = idx + (static_cast<int64_t>(b) * out_tq + i) * K;
+    const int64_t orow = static_cast<int64_t>(b) * out_tq + i;
+    int32_t* out = idx + orow * K;
     if (!(n <= kSel2MaxN && select_row_2pass(S, n, K, out, nullptr, sm.mask2))) {
       __syncthreads();
       select_row(S, n, K, out, nullptr, sm.radix);
     }
     __syncthreads();  // the next row reuses qrow, S and the LDS
+    if (dm.mask != nullptr && n <= dm.lim) {
+      // the tile path's mask from the finished index row (rare rows: global
+      // atomics on the zeroed mask row)
+      uint32_t* mrow = dm.mask + orow * dm.Wm;
+      for (int wd = threadIdx.x; wd < dm.Wm; wd += TOPK_NT) mrow[wd] = 0u;
+      __threadfence();
+      __syncthreads();
+      for (int j = threadIdx.x; j < K; j += TOPK_NT) {
+        const int32_t sp = out[j];
+        if (sp >= 0) atomicOr(&mrow[sp >> 5], 1u << (sp & 31));
+      }
+      if (threadIdx.x == 0) dm.flag[orow] = kRowMasked;
+    }
   }
 }
 
@@ -703,7 +737,7 @@ SelLayout sel_layout(const Geom& g) {
 template <int H_I, int D_I>
 static hipError_t launch_sel_hd(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                                 const int8_t* w, int32_t* idx, int out_tq, void* ws,
-                                hipStream_t st) {
+                                const DenseMasks& dm, hipStream_t st) {
   const SelLayout L = sel_layout(g);
   char* base = static_cast<char*>(ws);
   int2* cand = reinterpret_cast<int2*>(base + L.cand);
@@ -727,21 +761,21 @@ static hipError_t launch_sel_hd(const Geom& g, const int8_t* q_idx, const int8_t
     const dim3 grid(g.Tq, g.B);
     if (e <= 8)
       hipLaunchKernelGGL(sel_rows_kernel<8>, grid, dim3(SEL_NT), lds, st, g.Tq, g.Tk, g.K, L.capp,
-                         g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb, fbrows);
+                         g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb, fbrows, dm);
     else if (e <= 20)
       hipLaunchKernelGGL(sel_rows_kernel<20>, grid, dim3(SEL_NT), lds, st, g.Tq, g.Tk, g.K, L.capp,
-                         g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb, fbrows);
+                         g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb, fbrows, dm);
     else
       hipLaunchKernelGGL(sel_rows_kernel<kSelRowsMaxE>, grid, dim3(SEL_NT), lds, st, g.Tq, g.Tk,
                          g.K, L.capp, g.q_offset, g.kv_len, cand, cnt, meta, idx, out_tq, nfb,
-                         fbrows);
+                         fbrows, dm);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     KernelTimer timer(LCI_KERNEL_SEL_FALLBACK, st);
     hipLaunchKernelGGL((sel_fallback_kernel<H_I, D_I>), dim3(SEL_FB_GRID), dim3(TOPK_NT), 0, st,
                        g.Tq, g.Tk, g.K, g.q_offset, g.kv_len, q_idx, k_idx, w, nfb, fbrows,
-                       scratch, L.srow, idx, out_tq);
+                       scratch, L.srow, idx, out_tq, dm);
   }
   return hipGetLastError();
 }
@@ -749,23 +783,25 @@ static hipError_t launch_sel_hd(const Geom& g, const int8_t* q_idx, const int8_t
 template <int H_I>
 static hipError_t launch_sel_h(const Geom& g, const int8_t* q_idx, const int8_t* k_idx,
                                const int8_t* w, int32_t* idx, int out_tq, void* ws,
-                               hipStream_t st) {
+                               const DenseMasks& dm, hipStream_t st) {
   if constexpr (H_I * 64 <= 512) {
-    if (g.d_I == 64) return launch_sel_hd<H_I, 64>(g, q_idx, k_idx, w, idx, out_tq, ws, st);
+    if (g.d_I == 64) return launch_sel_hd<H_I, 64>(g, q_idx, k_idx, w, idx, out_tq, ws, dm, st);
   }
   if constexpr (H_I * 128 <= 512) {
-    if (g.d_I == 128) return launch_sel_hd<H_I, 128>(g, q_idx, k_idx, w, idx, out_tq, ws, st);
+    if (g.d_I == 128) return launch_sel_hd<H_I, 128>(g, q_idx, k_idx, w, idx, out_tq, ws, dm, st);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_sel(const Geom& g, const int8_t* q_idx, const int8_t* k_idx, const int8_t* w,
-                      int32_t* idx, int out_tq, void* ws, hipStream_t st) {
+                      int32_t* idx, int out_tq, void* ws, const DenseMasks* masks,
+                      hipStream_t st) {
+  const DenseMasks dm = masks ? *masks : DenseMasks{};
   switch (g.H_I) {
-    case 1: return launch_sel_h<1>(g, q_idx, k_idx, w, idx, out_tq, ws, st);
-    case 2: return launch_sel_h<2>(g, q_idx, k_idx, w, idx, out_tq, ws, st);
-    case 4: return launch_sel_h<4>(g, q_idx, k_idx, w, idx, out_tq, ws, st);
-    case 8: return launch_sel_h<8>(g, q_idx, k_idx, w, idx, out_tq, ws, st);
+    case 1: return launch_sel_h<1>(g, q_idx, k_idx, w, idx, out_tq, ws, dm, st);
+    case 2: return launch_sel_h<2>(g, q_idx, k_idx, w, idx, out_tq, ws, dm, st);
+    case 4: return launch_sel_h<4>(g, q_idx, k_idx, w, idx, out_tq, ws, dm, st);
+    case 8: return launch_sel_h<8>(g, q_idx, k_idx, w, idx, out_tq, ws, dm, st);
     default: return hipErrorInvalidValue;
   }
 }

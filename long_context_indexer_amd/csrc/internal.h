@@ -100,8 +100,11 @@ struct SelLayout {
 };
 bool sel_supported(const Geom& g, int64_t wsb, int64_t wsq);
 SelLayout sel_layout(const Geom& g);
+// With masks, the selection also writes the dense-path flags and masks of its
+// rows (rows [B][out_tq], like the index rows).
 hipError_t launch_sel(const Geom& g, const int8_t* q_idx, const int8_t* k_idx, const int8_t* w,
-                      int32_t* idx, int out_tq, void* workspace, hipStream_t stream);
+                      int32_t* idx, int out_tq, void* workspace, const DenseMasks* masks,
+                      hipStream_t stream);
 
 // ---- sparse attention over index rows
 size_t sparse_attn_workspace(const Geom& g, int splits);

@@ -338,8 +338,9 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
   int32_t* sc = reinterpret_cast<int32_t*>(ws + L.score_off);
   // with the dense-tile path on (one split), the selection kernel writes the
   // tile path's masks and flags: the block kernel always, the position kernel
-  // for rows short enough for its one-wave form
-  const bool masks = L.splits == 1 && (gg.block > 1 || g->Tk <= lci::kWaveTopkMax);
+  // for rows short enough for its one-wave form, the long-prefill selection
+  // always
+  const bool masks = L.splits == 1 && (gg.block > 1 || g->Tk <= lci::kWaveTopkMax || L.sel);
   const lci::DenseMasks dm = masks ? lci::dense_masks(ga, ws + L.attn_off) : lci::DenseMasks{};
   // index sets: set g is scored as an indexer of H_I/sets heads (heads
   // g*Hg .. g*Hg + Hg - 1 of the query rows, their weights) and its index rows
@@ -361,8 +362,14 @@ static lci_status fused_forward(const lci_geom* g, const int8_t* q_idx, const in
     const size_t qset = static_cast<size_t>(g->B) * g->Tq * gs.H_I * g->d_I;
     for (int set = 0; set < gg.sets; ++set) {
       int32_t* iset = idx + static_cast<size_t>(set) * g->Tq * ga.K;
+      // this set's masks and flags: rows [B][sets][Tq] like the index rows
+      lci::DenseMasks dms = dm;
+      if (masks) {
+        dms.mask += static_cast<size_t>(set) * g->Tq * dm.Wm;
+        dms.flag += static_cast<size_t>(set) * g->Tq;
+      }
       hipError_t e = lci::launch_sel(gs, qsrc + set * qset, k_idx, w + set * gs.H_I, iset,
-                                     g->Tq * gg.sets, ws + L.sel_off, st);
+                                     g->Tq * gg.sets, ws + L.sel_off, masks ? &dms : nullptr, st);
       if (e != hipSuccess) return hip_status(e);
     }
   }
