@@ -50,21 +50,21 @@ TRAFFIC = {
         sources=["long_context_indexer_amd/csrc/attn_dense.hip", "long_context_indexer_amd/csrc/attn_dense.h", "long_context_indexer_amd/csrc/tile.h", "long_context_indexer_amd/csrc/common.h"],
         sha256="7b605c37ae27f08f2199cd7a9bfb116bbcc24e858955a4ee0f314501a9973b8c"),
     ("prefill64k", "sel_scan"): dict(
-        fetch_kib=224014.6, write_kib=4107806.6, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=226100.5, write_kib=4113768.9, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/idx_select.hip", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
-        sha256="0f04192ab4187b5d31d4cfd8fd0a3f04f224afad7e92f9be97fa8cc5f9d7727e"),
+        sha256="3f4c7c7272a3e7855316ae942f4ac0fc96a99088780e996f37d7eb792e11a64a"),
     ("prefill8k", "attn_dense"): dict(
         fetch_kib=121627.7, write_kib=65956.5, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/attn_dense.hip", "long_context_indexer_amd/csrc/attn_dense.h", "long_context_indexer_amd/csrc/tile.h", "long_context_indexer_amd/csrc/common.h"],
         sha256="7b605c37ae27f08f2199cd7a9bfb116bbcc24e858955a4ee0f314501a9973b8c"),
     ("decode1m", "dec_score"): dict(
-        fetch_kib=262422.7, write_kib=322.4, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=262428.3, write_kib=322.6, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/decode.hip", "long_context_indexer_amd/csrc/decode.h", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
-        sha256="cb608208a9e2d07bbf891fb0919459e6991e4d0dab02beba46098bbb6c295c5e"),
+        sha256="2dfeebdc7868aba4644b25b1ba2c4621237a458b430ca9121201a5716cf8daa9"),
     ("decode128k", "dec_score"): dict(
-        fetch_kib=262540.9, write_kib=1775.4, fetch_scale=2.0, write_scale=1.0,
+        fetch_kib=262549.1, write_kib=1775.4, fetch_scale=2.0, write_scale=1.0,
         sources=["long_context_indexer_amd/csrc/decode.hip", "long_context_indexer_amd/csrc/decode.h", "long_context_indexer_amd/csrc/common.h", "long_context_indexer_amd/csrc/select_row.h"],
-        sha256="cb608208a9e2d07bbf891fb0919459e6991e4d0dab02beba46098bbb6c295c5e"),
+        sha256="2dfeebdc7868aba4644b25b1ba2c4621237a458b430ca9121201a5716cf8daa9"),
 }
 
 
